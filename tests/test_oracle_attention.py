@@ -1,0 +1,234 @@
+"""Pins for the oracle's attention (CPU only).
+
+When the top-k list covers the whole context the method is dense softmax
+attention over the dequantized cache, so the oracle is checked against a
+float64 numpy brute force and against torch's scaled_dot_product_attention
+(CPU, float64).  The sink is checked as one extra key with score = sink and a
+zero value.  Masking, order, closed forms and the probability sum cover what
+the dense case cannot.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_top_mla_smla_amd import workloads as W
+
+from helpers import dense_attention, np_dequant, oracle_pool, q_f64
+
+FMTS = [W.FMT_BF16, W.FMT_FP8, W.FMT_INT8]
+
+
+def full_ctx_case(fmt, seed=0, ctx=192, T=3, H=4, with_sink=False):
+    # topk = ctx, non-causal: every token's list is a permutation of all slots
+    return W.make_case("full", config_id=101, seed=seed, fmt=fmt, T=T, H=H, n_seqs=1, ctx=ctx,
+                       topk=ctx, causal=False, with_sink=with_sink)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("with_sink", [False, True])
+def test_dense_brute_force(fmt, with_sink):
+    c = full_ctx_case(fmt, seed=fmt, with_sink=with_sink)
+    pool = oracle_pool(c)
+    out, lse, of, lf = oracle.prefill(c.q, pool, c.indices, sink=c.sink, sm_scale=c.sm_scale)
+    K = np_dequant(pool, c.slots)               # all rows of the context
+    q = q_f64(c)
+    for h in range(c.H):
+        o_ref, l_ref = dense_attention(q[:, h], K, float(c.sm_scale),
+                                       None if c.sink is None else float(c.sink[h]))
+        assert np.allclose(of[:, h], o_ref, rtol=0, atol=1e-12)
+        assert np.allclose(lf[:, h], l_ref, rtol=0, atol=1e-12)
+    # BF16 output is the nearest BF16 of the float64 value
+    ref_bits = torch.tensor(of).float().to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.mean(out == ref_bits) > 0.999
+    assert np.array_equal(lse, lf.astype(np.float32))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_dense_vs_torch_sdpa(fmt):
+    c = full_ctx_case(fmt, seed=10 + fmt, T=5, H=3)
+    pool = oracle_pool(c)
+    _, _, of, _ = oracle.prefill(c.q, pool, c.indices, sm_scale=c.sm_scale)
+    K = torch.tensor(np_dequant(pool, c.slots))
+    q = torch.tensor(q_f64(c)).permute(1, 0, 2).unsqueeze(0)     # [1,H,T,576]
+    k = K.unsqueeze(0).unsqueeze(0).expand(1, c.H, -1, -1)
+    v = K[:, :512].unsqueeze(0).unsqueeze(0).expand(1, c.H, -1, -1)
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, scale=float(c.sm_scale))
+    assert np.allclose(of, ref[0].permute(1, 0, 2).numpy(), rtol=0, atol=1e-12)
+
+
+def sparse_case(fmt, seed=0, T=6, H=4, ctx=320, topk=96, **kw):
+    return W.make_case("sparse", config_id=102, seed=seed, fmt=fmt, T=T, H=H, n_seqs=1, ctx=ctx,
+                       topk=topk, causal=True, **kw)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_sparse_equals_dense_over_selected_rows(fmt):
+    c = sparse_case(fmt, seed=3, tail_neg=5, with_sink=True)
+    pool = oracle_pool(c)
+    _, _, of, lf = oracle.prefill(c.q, pool, c.indices, sink=c.sink, sm_scale=c.sm_scale)
+    q = q_f64(c)
+    for t in range(c.T):
+        sel = c.indices[t][c.indices[t] >= 0]
+        K = np_dequant(pool, sel)
+        for h in range(c.H):
+            o_ref, l_ref = dense_attention(q[t:t + 1, h], K, float(c.sm_scale), float(c.sink[h]))
+            assert np.allclose(of[t, h], o_ref[0], atol=1e-12, rtol=0)
+            assert abs(lf[t, h] - l_ref[0]) < 1e-12
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_masked_entries_bit_exact_invariance(fmt):
+    c = sparse_case(fmt, seed=4, with_topk_length=True, with_sink=True)
+    pool = oracle_pool(c)
+    base = oracle.prefill(c.q, pool, c.indices, topk_length=c.topk_length, sink=c.sink,
+                          sm_scale=c.sm_scale)
+    rng = np.random.default_rng(0)
+    idx = c.indices.copy()
+    nslots = c.num_blocks * 64
+    for t in range(c.T):
+        L = c.topk_length[t]
+        tail = c.topk - L
+        # beyond L: arbitrary garbage, including valid slots and huge values
+        idx[t, L:] = rng.choice([0x7FFFFFFF, -5, nslots, 3], size=tail)
+        idx[t, L:L + tail // 2] = rng.integers(0, nslots, size=tail // 2)
+        # inside L: replace some -1 by other out-of-range ids
+        inside = np.nonzero(idx[t, :L] == -1)[0]
+        idx[t, inside] = rng.choice([-2, nslots, 0x7FFFFFFF], size=inside.shape[0])
+    other = oracle.prefill(c.q, pool, idx, topk_length=c.topk_length, sink=c.sink,
+                           sm_scale=c.sm_scale)
+    assert np.array_equal(base[0], other[0])
+    assert np.array_equal(base[1], other[1])
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_permutation_invariance(fmt):
+    c = sparse_case(fmt, seed=5, tail_neg=7)
+    pool = oracle_pool(c)
+    _, _, of, lf = oracle.prefill(c.q, pool, c.indices, sm_scale=c.sm_scale)
+    rng = np.random.default_rng(1)
+    idx = np.ascontiguousarray(c.indices[:, rng.permutation(c.topk)])
+    _, _, of2, lf2 = oracle.prefill(c.q, pool, idx, sm_scale=c.sm_scale)
+    assert np.allclose(of, of2, atol=1e-13, rtol=0)
+    assert np.allclose(lf, lf2, atol=1e-13, rtol=0)
+
+
+def tiny_pool(fmt, seed=0):
+    c = W.make_case("tiny", config_id=103, seed=seed, fmt=fmt, T=2, H=3, n_seqs=1, ctx=64, topk=8,
+                    causal=False, with_sink=True)
+    return c, oracle_pool(c)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_closed_forms(fmt):
+    c, pool = tiny_pool(fmt, seed=fmt)
+    q = q_f64(c)
+    K = np_dequant(pool, np.arange(64))
+    s = float(c.sm_scale)
+    a, b = 7, 42
+    # one candidate: out = V, lse = its score
+    idx = np.full((2, 8), -1, np.int32)
+    idx[:, 3] = a
+    _, _, of, lf = oracle.prefill(c.q, pool, idx, sm_scale=c.sm_scale)
+    for t in range(2):
+        for h in range(3):
+            assert np.allclose(of[t, h], K[a, :512], atol=1e-12, rtol=0)
+            assert abs(lf[t, h] - s * q[t, h] @ K[a]) < 1e-12
+    # one candidate with a sink: out = V * sigmoid(score - sink)
+    _, _, of, _ = oracle.prefill(c.q, pool, idx, sink=c.sink, sm_scale=c.sm_scale)
+    for t in range(2):
+        for h in range(3):
+            z = s * q[t, h] @ K[a] - float(c.sink[h])
+            assert np.allclose(of[t, h], K[a, :512] / (1 + np.exp(-z)), atol=1e-12, rtol=0)
+    # two candidates: weights sigmoid(s_a - s_b), sigmoid(s_b - s_a)
+    idx[:, 5] = b
+    _, _, of, lf = oracle.prefill(c.q, pool, idx, sm_scale=c.sm_scale)
+    for t in range(2):
+        for h in range(3):
+            sa, sb = s * q[t, h] @ K[a], s * q[t, h] @ K[b]
+            pa = 1 / (1 + np.exp(sb - sa))
+            assert np.allclose(of[t, h], pa * K[a, :512] + (1 - pa) * K[b, :512], atol=1e-12, rtol=0)
+            assert abs(lf[t, h] - np.logaddexp(sa, sb)) < 1e-12
+    # n copies of one slot: out = V, lse = s + ln n
+    idx = np.full((2, 8), a, np.int32)
+    idx[:, 6:] = -1
+    _, _, of, lf = oracle.prefill(c.q, pool, idx, sm_scale=c.sm_scale)
+    for t in range(2):
+        for h in range(3):
+            assert np.allclose(of[t, h], K[a, :512], atol=1e-12, rtol=0)
+            assert abs(lf[t, h] - (s * q[t, h] @ K[a] + np.log(6))) < 1e-12
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_empty_set(fmt):
+    c, pool = tiny_pool(fmt, seed=20 + fmt)
+    idx = np.full((2, 8), -1, np.int32)
+    idx[1, :] = 5
+    tl = np.array([8, 0], np.int32)        # token 1 truncated to nothing
+    for sink in (None, c.sink):
+        out, lse, of, lf = oracle.prefill(c.q, pool, idx, topk_length=tl, sink=sink,
+                                          sm_scale=c.sm_scale)
+        assert np.all(out == 0) and np.all(of == 0)
+        assert np.all(np.isneginf(lse)) and np.all(np.isneginf(lf))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_probabilities_sum_to_one(fmt):
+    c = sparse_case(fmt, seed=6, with_topk_length=True, with_sink=True)
+    pool = oracle_pool(c)
+    _, _, of, lf = oracle.prefill(c.q, pool, c.indices, topk_length=c.topk_length, sink=c.sink,
+                                  sm_scale=c.sm_scale)
+    for t in (0, 3, 5):
+        for h in (0, 2):
+            p, ps = oracle.probs(c.q, pool, c.indices, t, h, topk_length=c.topk_length,
+                                 sink=c.sink, sm_scale=c.sm_scale)
+            assert abs(p.sum() + ps - 1.0) < 1e-12
+            L = c.topk_length[t]
+            assert np.all(p[L:] == 0)
+            valid = (np.arange(c.topk) < L) & (c.indices[t] >= 0)
+            assert np.all(p[~valid] == 0)
+            K = np_dequant(pool, np.where(valid, c.indices[t], 0))
+            assert np.allclose(p @ K[:, :512], of[t, h], atol=1e-12, rtol=0)
+            # the sink's share equals 1 / (1 + exp(lse - sink))
+            assert abs(ps - 1 / (1 + np.exp(lf[t, h] - c.sink[h]))) < 1e-12
+
+
+def test_query_scaling_invariance():
+    # doubling q (exact in BF16) and halving sm_scale leaves every score unchanged
+    c = sparse_case(W.FMT_FP8, seed=8)
+    pool = oracle_pool(c)
+    _, _, of, lf = oracle.prefill(c.q, pool, c.indices, sm_scale=c.sm_scale)
+    q2 = W.f32_to_bf16_bits(W.bf16_bits_to_f32(c.q) * 2)
+    _, _, of2, lf2 = oracle.prefill(q2, pool, c.indices, sm_scale=np.float32(c.sm_scale / 2))
+    assert np.allclose(of, of2, atol=1e-13, rtol=0) and np.allclose(lf, lf2, atol=1e-13, rtol=0)
+
+
+def test_strided_views_match_packed():
+    # q as a [:, :H] view of a wider head buffer, indices as a narrowed view
+    c = W.make_case("views", config_id=104, seed=2, fmt=W.FMT_FP8, T=4, H=3, hbuf=8, n_seqs=1,
+                    ctx=256, topk=64, idx_ld=96, pad_fill=W.PAD_SENTINEL)
+    pool = oracle_pool(c)
+    a = oracle.prefill(c.q, pool, c.indices, sm_scale=c.sm_scale)
+    b = oracle.prefill(np.ascontiguousarray(c.q), pool, np.ascontiguousarray(c.indices),
+                       sm_scale=c.sm_scale)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_token_subset_matches_full():
+    c = sparse_case(W.FMT_INT8, seed=9, with_sink=True)
+    pool = oracle_pool(c)
+    full = oracle.prefill(c.q, pool, c.indices, sink=c.sink, sm_scale=c.sm_scale)
+    sub = oracle.prefill(c.q, pool, c.indices, sink=c.sink, sm_scale=c.sm_scale, tokens=[1, 4])
+    for x, y in zip(full, sub):
+        assert np.array_equal(x[[1, 4]], y[[1, 4]])
+
+
+def test_padded_block_stride_and_row_placement():
+    # a pool with padding between blocks gives the same result as a packed pool
+    c = sparse_case(W.FMT_FP8, seed=12)
+    p1 = oracle_pool(c)
+    p2 = oracle_pool(c, block_stride=64 * 656 + 256, fill=0xFF)
+    a = oracle.prefill(c.q, p1, c.indices, sm_scale=c.sm_scale)
+    b = oracle.prefill(c.q, p2, c.indices, sm_scale=c.sm_scale)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
