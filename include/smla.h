@@ -1,0 +1,160 @@
+/*
+ * smla.h -- C ABI of libsmla, sparse MLA attention over a paged, quantized
+ * latent KV cache for AMD MI355X (gfx950).
+ *
+ * What is computed (sources: FlashInfer PR #4802 "Refactor Sparse MLA SM120"
+ * -- review of decode_dsv3_2_kernel.cuh for the 656-byte row, PR description
+ * "Runtime envelopes"/"Dispatch"/"Runner and CUDA graphs" for page block 64,
+ * strided index rows, row-strided LSE, topk_length, sinks and the decode
+ * split-K scratch; AppMana flash-mla-ampere-dsv4 releases "decode H6" for the
+ * log-sum-exp merge and "native int8_ds_mla entry" for the INT8 cache; vLLM
+ * PR #57673 "Test Result" for d=512, combined top-k lists, attn_sink and
+ * topk_length with non-contiguous q/out head views):
+ *
+ *   For each query token t and head h, the candidates are the list entries
+ *   j < L_t (L_t = clamp(topk_length[t], 0, topk), or topk when no lengths
+ *   are given) whose index is a slot of the pool, i.e. in [0, num_blocks*64);
+ *   every other entry (-1 padding included) contributes nothing.  With K the
+ *   dequantized 576-element latent row (512 "nope" + 64 "rope") and V its
+ *   first 512 elements:
+ *     s_j  = sm_scale * <q[t,h,:], K_j>
+ *     lse  = ln sum_j exp(s_j)                (natural log, sink excluded)
+ *     out  = sum_j exp(s_j) V_j / (sum_j exp(s_j) + exp(sink_h))
+ *   (the sink term only when a sink array is given; it is one extra logit
+ *   per head in scaled-score units and carries no value).  An empty
+ *   candidate set gives out = 0 and lse = -inf.  out is BF16 (round to
+ *   nearest even), lse FP32.
+ *
+ * Conventions for every entry point:
+ *  - All data pointers are DEVICE pointers; `stream` is a hipStream_t (NULL
+ *    = the default stream).  Work is enqueued asynchronously on `stream`.
+ *  - The caller owns every buffer.  The library allocates and frees nothing,
+ *    never synchronizes, and keeps no pointer after returning; calls on
+ *    different streams may run concurrently.
+ *  - Strides are in ELEMENTS of the pointed-to type; the last dimension of
+ *    every tensor is contiguous.
+ *  - Arguments are validated on the host before any launch; on a failed
+ *    check nothing is launched and a non-zero status is returned, with a
+ *    message naming the mismatch in smla_last_error().
+ *  - Device-side data (indices, slots, lengths) is not validated on the
+ *    host; the kernels treat out-of-range slots as padding, so no access
+ *    ever leaves the pool.
+ *  - T == 0 (or n == 0) returns SMLA_OK without launching anything.
+ */
+#ifndef SMLA_H
+#define SMLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SMLA_OK = 0,
+  SMLA_ERR_NULL = 1,        /* a required pointer is NULL */
+  SMLA_ERR_SHAPE = 2,       /* a size is out of range (negative T, H < 1, topk < 1, ...) */
+  SMLA_ERR_STRIDE = 3,      /* a stride or address is smaller than its row, or misaligned */
+  SMLA_ERR_UNSUPPORTED = 4, /* a well-formed request outside what is built (page block != 64, H > 128, ...) */
+  SMLA_ERR_HIP = 5          /* the HIP runtime reported an error when launching */
+} smla_status;
+
+/* Latent-cache row formats.  Row layout (FlashInfer PR #4802 review of the
+ * DSv3.2 decode kernel): FP8 row = 656 bytes: [0,512) e4m3 codes of the 512
+ * nope values, [512,528) four FP32 scales (one per 128-element tile),
+ * [528,656) 64 BF16 rope values.  INT8 uses the same layout with int8 codes.
+ * BF16 row = 576 BF16 values (1152 bytes). */
+typedef enum {
+  SMLA_KV_BF16 = 0,
+  SMLA_KV_FP8_E4M3 = 1,
+  SMLA_KV_INT8 = 2
+} smla_kv_format;
+
+/* A paged latent pool.  Slot s (a flat pool position) lives in block s/64 at
+ * row s%64: byte address base + (s/64)*block_stride_bytes + (s%64)*row_bytes.
+ * base must be 16-byte aligned; block_stride_bytes a multiple of 16 and at
+ * least 64*row_bytes; page_block must be 64 (PR #4802: the kernels are
+ * compiled for page block 64 and launchers reject anything else). */
+typedef struct {
+  void* base;
+  int64_t num_blocks;
+  int64_t block_stride_bytes;
+  int32_t page_block;
+  int32_t format; /* smla_kv_format */
+} smla_kv_pool;
+
+/* Bytes of one cache row: 1152 (BF16), 656 (FP8, INT8); -1 for an unknown format. */
+int32_t smla_row_bytes(int32_t format);
+
+/* Width of one decode split: 64 * ceil(ceil(topk / num_splits) / 64).  Split
+ * s covers list positions [s*w, min((s+1)*w, topk)); trailing splits may be
+ * empty.  (PR #4802: decode splits the candidate list into 64-wide chunks.)
+ * Returns -1 when topk < 1 or num_splits < 1. */
+int32_t smla_split_width(int32_t topk, int32_t num_splits);
+
+/* Write n latent rows into the pool.
+ *   kv     BF16 [n, >=576], row i at kv + i*kv_stride (kv_stride >= 576,
+ *          multiple of 8, kv 16-byte aligned)
+ *   slots  int32 [n]: destination slot of row i; slots outside
+ *          [0, num_blocks*64) (-1 included) are skipped.
+ * FP8: per 128-element tile of the nope part, amax = max |x|; scale = 1 when
+ * amax = 0, else the power of two 2^ceil(log2(amax/448)) (the page's
+ * "power-of-2 FP32 scales"); codes = e4m3(x / scale), round to nearest even,
+ * sign kept.  INT8: scale = amax/127 (1 when amax = 0), codes =
+ * clamp(rne(x/scale), -127, 127).  BF16: a copy.  Rope values are copied
+ * bit for bit.  Two slots that are equal race (last writer wins). */
+smla_status smla_quantize_kv(const void* kv, int64_t n, int64_t kv_stride, const int32_t* slots,
+                             smla_kv_pool pool, void* stream);
+
+/* Prefill form: attention for T query tokens, written straight to out/lse.
+ *   q            BF16 [T, H, 576] with strides (q_stride_t, q_stride_h):
+ *                both multiples of 8, q 16-byte aligned (views such as
+ *                q[:, :8] of a wider head buffer are allowed)
+ *   indices      int32 [T, >=topk], row stride idx_stride_t >= topk: flat
+ *                slot ids (a narrowed view of a wider buffer is allowed)
+ *   topk_length  int32 [T] or NULL
+ *   sink         FP32 [H] or NULL
+ *   out          BF16 [T, H, 512] with strides (out_stride_t, out_stride_h),
+ *                multiples of 8, 16-byte aligned; written in place
+ *   lse          FP32 [T, H] with row stride lse_stride_t >= H
+ * H in [1, 128]. */
+smla_status smla_prefill(const void* q, int64_t T, int32_t H, int64_t q_stride_t, int64_t q_stride_h,
+                         smla_kv_pool kv, const int32_t* indices, int32_t topk, int64_t idx_stride_t,
+                         const int32_t* topk_length, const float* sink, float sm_scale,
+                         void* out, int64_t out_stride_t, int64_t out_stride_h,
+                         float* lse, int64_t lse_stride_t, void* stream);
+
+/* Decode split form: per split s (smla_split_width) of each token's list,
+ * the partial result over that split's candidates, with no sink:
+ *   part_lse[t,s,h] = ln sum_{j in split} exp(s_j)   (-inf when empty)
+ *   part_out[t,s,h,:] = sum exp(s_j) V_j / sum exp(s_j)  (0 when empty)
+ * part_out FP32 [T, num_splits, H, 512] and part_lse FP32 [T, num_splits, H]
+ * are caller-owned, contiguous, 16-byte aligned.  Other arguments as in
+ * smla_prefill.  num_splits in [1, 64]. */
+smla_status smla_decode(const void* q, int64_t T, int32_t H, int64_t q_stride_t, int64_t q_stride_h,
+                        smla_kv_pool kv, const int32_t* indices, int32_t topk, int64_t idx_stride_t,
+                        const int32_t* topk_length, float sm_scale, int32_t num_splits,
+                        float* part_out, float* part_lse, void* stream);
+
+/* Log-sum-exp merge of decode splits (AppMana "decode H6" combine): with
+ * M = max_s part_lse, w_s = exp(part_lse_s - M) and W = sum w_s,
+ *   lse = M + ln W,  o = sum_s (w_s / W) part_out_s,
+ *   and with a sink o *= 1 / (1 + exp(sink_h - lse));  out = bf16(o).
+ * All splits empty (M = -inf): out = 0, lse = -inf.  Buffers as in
+ * smla_decode / smla_prefill. */
+smla_status smla_combine(const float* part_out, const float* part_lse, int64_t T, int32_t num_splits,
+                         int32_t H, const float* sink, void* out, int64_t out_stride_t,
+                         int64_t out_stride_h, float* lse, int64_t lse_stride_t, void* stream);
+
+/* Message describing the last failed call on this thread ("" if none). */
+const char* smla_last_error(void);
+
+/* Library version string. */
+const char* smla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SMLA_H */

@@ -1,0 +1,211 @@
+"""Python binding of libsmla -- sparse MLA attention for AMD MI355X.
+
+A thin ctypes layer over the C ABI in include/smla.h: it only checks dtypes
+and devices, reads pointers and strides off torch tensors, allocates outputs
+when the caller passes none, and calls the library on the current HIP
+stream.  Every step of the computation runs in the HIP kernels of
+libsmla.so; there is no fallback, and a missing library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = ["KVPool", "quantize_kv", "prefill", "decode", "combine", "split_width", "row_bytes",
+           "library_path", "SmlaError", "FMT_BF16", "FMT_FP8", "FMT_INT8"]
+
+FMT_BF16, FMT_FP8, FMT_INT8 = 0, 1, 2
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libsmla.so")
+_lib = None
+
+
+class SmlaError(RuntimeError):
+    pass
+
+
+class _Pool(ctypes.Structure):
+    _fields_ = [("base", ctypes.c_void_p), ("num_blocks", ctypes.c_int64),
+                ("block_stride_bytes", ctypes.c_int64), ("page_block", ctypes.c_int32),
+                ("format", ctypes.c_int32)]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise SmlaError(f"{_LIB_PATH} is missing: build it with "
+                        "`python -m sparse_top_mla_smla_amd.build` (hipcc, gfx950)")
+    L = ctypes.CDLL(_LIB_PATH)
+    P, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
+    L.smla_row_bytes.argtypes, L.smla_row_bytes.restype = [i32], i32
+    L.smla_split_width.argtypes, L.smla_split_width.restype = [i32, i32], i32
+    L.smla_last_error.argtypes, L.smla_last_error.restype = [], ctypes.c_char_p
+    L.smla_version.argtypes, L.smla_version.restype = [], ctypes.c_char_p
+    L.smla_quantize_kv.argtypes = [P, i64, i64, P, _Pool, P]
+    L.smla_prefill.argtypes = [P, i64, i32, i64, i64, _Pool, P, i32, i64, P, P, f32, P, i64, i64,
+                               P, i64, P]
+    L.smla_decode.argtypes = [P, i64, i32, i64, i64, _Pool, P, i32, i64, P, f32, i32, P, P, P]
+    L.smla_combine.argtypes = [P, P, i64, i32, i32, P, P, i64, i64, P, i64, P]
+    for fn in (L.smla_quantize_kv, L.smla_prefill, L.smla_decode, L.smla_combine):
+        fn.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        msg = _load().smla_last_error().decode()
+        raise SmlaError(f"{what}: status {status}: {msg}")
+
+
+def row_bytes(fmt: int) -> int:
+    return int(_load().smla_row_bytes(fmt))
+
+
+def split_width(topk: int, num_splits: int) -> int:
+    return int(_load().smla_split_width(topk, num_splits))
+
+
+def version() -> str:
+    return _load().smla_version().decode()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, name: str, dtype, last_contig: bool = True):
+    if t.dtype != dtype:
+        raise SmlaError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise SmlaError(f"{name} must be a GPU tensor")
+    if last_contig and t.dim() > 0 and t.shape[-1] > 1 and t.stride(-1) != 1:
+        raise SmlaError(f"{name}: the last dimension must be contiguous")
+
+
+class KVPool:
+    """A paged latent pool: a uint8 device tensor [num_blocks, block_stride]
+    (block_stride >= 64 * row_bytes, multiple of 16) in format fmt."""
+
+    def __init__(self, data: torch.Tensor, fmt: int, page_block: int = 64):
+        _need(data, "pool", torch.uint8)
+        if data.dim() != 2:
+            raise SmlaError("pool must be 2-D [num_blocks, block_stride_bytes]")
+        self.data, self.fmt, self.page_block = data, fmt, page_block
+
+    @classmethod
+    def empty(cls, num_blocks: int, fmt: int, device="cuda", block_stride: int = 0) -> "KVPool":
+        bs = block_stride or 64 * row_bytes(fmt)
+        return cls(torch.zeros((num_blocks, bs), dtype=torch.uint8, device=device), fmt)
+
+    @property
+    def num_blocks(self) -> int:
+        return self.data.shape[0]
+
+    def c(self) -> _Pool:
+        return _Pool(self.data.data_ptr(), self.data.shape[0], self.data.stride(0), self.page_block,
+                     self.fmt)
+
+
+def quantize_kv(kv: torch.Tensor, slots: torch.Tensor, pool: KVPool, stream=None) -> None:
+    """Write BF16 latent rows kv [n, >=576] into pool slots (see smla_quantize_kv)."""
+    _need(kv, "kv", torch.bfloat16)
+    _need(slots, "slots", torch.int32)
+    n = kv.shape[0]
+    _check(_load().smla_quantize_kv(_ptr(kv), n, kv.stride(0) if n else 576, _ptr(slots), pool.c(),
+                                    _stream(stream)), "smla_quantize_kv")
+
+
+def _idx_args(indices: torch.Tensor, topk: Optional[int]):
+    _need(indices, "indices", torch.int32)
+    topk = indices.shape[1] if topk is None else topk
+    return topk, indices.stride(0)
+
+
+def prefill(q: torch.Tensor, pool: KVPool, indices: torch.Tensor, topk: Optional[int] = None,
+            topk_length: Optional[torch.Tensor] = None, sink: Optional[torch.Tensor] = None,
+            sm_scale: float = 1.0 / 24.0, out: Optional[torch.Tensor] = None,
+            lse: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Sparse MLA prefill (see smla_prefill).  q [T,H,576] bf16 (strided views
+    allowed), indices [T, >=topk] int32.  Returns (out [T,H,512] bf16, lse [T,H] f32)."""
+    _need(q, "q", torch.bfloat16)
+    T, H, _ = q.shape
+    topk, ist = _idx_args(indices, topk)
+    if topk_length is not None:
+        _need(topk_length, "topk_length", torch.int32)
+    if sink is not None:
+        _need(sink, "sink", torch.float32)
+    if out is None:
+        out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.bfloat16)
+    _need(lse, "lse", torch.float32)
+    _check(_load().smla_prefill(_ptr(q), T, H, q.stride(0), q.stride(1), pool.c(), _ptr(indices), topk,
+                                ist, _ptr(topk_length), _ptr(sink), float(sm_scale), _ptr(out),
+                                out.stride(0), out.stride(1), _ptr(lse), lse.stride(0),
+                                _stream(stream)), "smla_prefill")
+    return out, lse
+
+
+def decode(q: torch.Tensor, pool: KVPool, indices: torch.Tensor, num_splits: int,
+           topk: Optional[int] = None, topk_length: Optional[torch.Tensor] = None,
+           sm_scale: float = 1.0 / 24.0, part_out: Optional[torch.Tensor] = None,
+           part_lse: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Split-KV decode partials (see smla_decode).  Returns part_out
+    [T,S,H,512] f32 and part_lse [T,S,H] f32."""
+    _need(q, "q", torch.bfloat16)
+    T, H, _ = q.shape
+    topk, ist = _idx_args(indices, topk)
+    if topk_length is not None:
+        _need(topk_length, "topk_length", torch.int32)
+    if part_out is None:
+        part_out = torch.empty((T, num_splits, H, 512), dtype=torch.float32, device=q.device)
+    if part_lse is None:
+        part_lse = torch.empty((T, num_splits, H), dtype=torch.float32, device=q.device)
+    _need(part_out, "part_out", torch.float32)
+    _need(part_lse, "part_lse", torch.float32)
+    if not (part_out.is_contiguous() and part_lse.is_contiguous()):
+        raise SmlaError("part_out / part_lse must be contiguous")
+    _check(_load().smla_decode(_ptr(q), T, H, q.stride(0), q.stride(1), pool.c(), _ptr(indices), topk,
+                               ist, _ptr(topk_length), float(sm_scale), num_splits, _ptr(part_out),
+                               _ptr(part_lse), _stream(stream)), "smla_decode")
+    return part_out, part_lse
+
+
+def combine(part_out: torch.Tensor, part_lse: torch.Tensor, sink: Optional[torch.Tensor] = None,
+            out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+            stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """LSE combine of decode splits (see smla_combine)."""
+    _need(part_out, "part_out", torch.float32)
+    _need(part_lse, "part_lse", torch.float32)
+    if not (part_out.is_contiguous() and part_lse.is_contiguous()):
+        raise SmlaError("part_out / part_lse must be contiguous")
+    T, S, H, _ = part_out.shape
+    if sink is not None:
+        _need(sink, "sink", torch.float32)
+    if out is None:
+        out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=part_out.device)
+    if lse is None:
+        lse = torch.empty((T, H), dtype=torch.float32, device=part_out.device)
+    _need(out, "out", torch.bfloat16)
+    _need(lse, "lse", torch.float32)
+    _check(_load().smla_combine(_ptr(part_out), _ptr(part_lse), T, S, H, _ptr(sink), _ptr(out),
+                                out.stride(0), out.stride(1), _ptr(lse), lse.stride(0),
+                                _stream(stream)), "smla_combine")
+    return out, lse

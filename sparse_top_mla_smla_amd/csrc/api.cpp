@@ -1,0 +1,237 @@
+// api.cpp -- the C entry points declared in include/smla.h: argument
+// validation (everything is checked on the host before any launch) and
+// dispatch to the kernels.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/smla.h"
+#include "launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+smla_status fail(smla_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+smla_status ok() {
+  g_err[0] = '\0';
+  return SMLA_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+smla_status check_pool(const smla_kv_pool& kv) {
+  if (!kv.base) return fail(SMLA_ERR_NULL, "kv pool base is NULL");
+  if (kv.page_block != 64)
+    return fail(SMLA_ERR_UNSUPPORTED, "page_block %d is not supported (supported: 64)", kv.page_block);
+  int32_t rb = smla_row_bytes(kv.format);
+  if (rb < 0)
+    return fail(SMLA_ERR_UNSUPPORTED, "kv format %d is not supported (supported: 0 = BF16, 1 = FP8_E4M3, 2 = INT8)",
+                kv.format);
+  if (kv.num_blocks < 1) return fail(SMLA_ERR_SHAPE, "num_blocks %lld must be >= 1", (long long)kv.num_blocks);
+  if (kv.num_blocks > (int64_t)(INT32_MAX / 64) + 1)
+    return fail(SMLA_ERR_SHAPE, "num_blocks %lld exceeds the int32 slot range", (long long)kv.num_blocks);
+  if (kv.block_stride_bytes < 64LL * rb)
+    return fail(SMLA_ERR_STRIDE, "block_stride_bytes %lld is smaller than 64 rows of %d bytes",
+                (long long)kv.block_stride_bytes, rb);
+  if (kv.block_stride_bytes % 16 != 0)
+    return fail(SMLA_ERR_STRIDE, "block_stride_bytes %lld is not a multiple of 16", (long long)kv.block_stride_bytes);
+  if (!aligned(kv.base, 16)) return fail(SMLA_ERR_STRIDE, "kv pool base is not 16-byte aligned");
+  return SMLA_OK;
+}
+
+smla_status check_attn_common(const void* q, int64_t T, int32_t H, int64_t q_st, int64_t q_sh,
+                              const smla_kv_pool& kv, const int32_t* indices, int32_t topk,
+                              int64_t idx_st) {
+  if (T < 0) return fail(SMLA_ERR_SHAPE, "T = %lld must be >= 0", (long long)T);
+  if (T > INT32_MAX) return fail(SMLA_ERR_SHAPE, "T = %lld exceeds 2^31-1", (long long)T);
+  if (T == 0) return SMLA_OK;  // nothing is read or launched
+  if (H < 1 || H > 128) return fail(SMLA_ERR_UNSUPPORTED, "H = %d is not supported (supported: 1..128)", H);
+  if (topk < 1) return fail(SMLA_ERR_SHAPE, "topk = %d must be >= 1", topk);
+  if (!q) return fail(SMLA_ERR_NULL, "q is NULL");
+  if (!indices) return fail(SMLA_ERR_NULL, "indices is NULL");
+  smla_status st = check_pool(kv);
+  if (st != SMLA_OK) return st;
+  if (!aligned(q, 16)) return fail(SMLA_ERR_STRIDE, "q is not 16-byte aligned");
+  if (q_sh < 576 || q_sh % 8 != 0)
+    return fail(SMLA_ERR_STRIDE, "q_stride_h = %lld must be >= 576 and a multiple of 8", (long long)q_sh);
+  if (q_st % 8 != 0 || q_st < 0)
+    return fail(SMLA_ERR_STRIDE, "q_stride_t = %lld must be a non-negative multiple of 8", (long long)q_st);
+  if (idx_st < topk) return fail(SMLA_ERR_STRIDE, "idx_stride_t = %lld is smaller than topk = %d", (long long)idx_st, topk);
+  if (!aligned(indices, 4)) return fail(SMLA_ERR_STRIDE, "indices is not 4-byte aligned");
+  return SMLA_OK;
+}
+
+smla_status check_out(const void* out, int64_t out_st, int64_t out_sh, int32_t H, const float* lse,
+                      int64_t lse_st) {
+  if (!out) return fail(SMLA_ERR_NULL, "out is NULL");
+  if (!lse) return fail(SMLA_ERR_NULL, "lse is NULL");
+  if (!aligned(out, 16)) return fail(SMLA_ERR_STRIDE, "out is not 16-byte aligned");
+  if (out_sh < 512 || out_sh % 8 != 0)
+    return fail(SMLA_ERR_STRIDE, "out_stride_h = %lld must be >= 512 and a multiple of 8", (long long)out_sh);
+  if (out_st % 8 != 0 || out_st < 0)
+    return fail(SMLA_ERR_STRIDE, "out_stride_t = %lld must be a non-negative multiple of 8", (long long)out_st);
+  if (lse_st < H) return fail(SMLA_ERR_STRIDE, "lse_stride_t = %lld is smaller than H = %d", (long long)lse_st, H);
+  if (!aligned(lse, 4)) return fail(SMLA_ERR_STRIDE, "lse is not 4-byte aligned");
+  return SMLA_OK;
+}
+
+smla_status launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(SMLA_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t smla_row_bytes(int32_t format) {
+  switch (format) {
+    case SMLA_KV_BF16: return 1152;
+    case SMLA_KV_FP8_E4M3: return 656;
+    case SMLA_KV_INT8: return 656;
+    default: return -1;
+  }
+}
+
+int32_t smla_split_width(int32_t topk, int32_t num_splits) {
+  if (topk < 1 || num_splits < 1) return -1;
+  int32_t per = (topk + num_splits - 1) / num_splits;
+  return ((per + 63) / 64) * 64;
+}
+
+const char* smla_last_error(void) { return g_err; }
+
+const char* smla_version(void) { return "smla 0.1.0 (gfx950)"; }
+
+smla_status smla_quantize_kv(const void* kv, int64_t n, int64_t kv_stride, const int32_t* slots,
+                             smla_kv_pool pool, void* stream) {
+  if (n < 0) return fail(SMLA_ERR_SHAPE, "n = %lld must be >= 0", (long long)n);
+  if (n == 0) return ok();
+  if (!kv) return fail(SMLA_ERR_NULL, "kv is NULL");
+  if (!slots) return fail(SMLA_ERR_NULL, "slots is NULL");
+  smla_status st = check_pool(pool);
+  if (st != SMLA_OK) return st;
+  if (kv_stride < 576 || kv_stride % 8 != 0)
+    return fail(SMLA_ERR_STRIDE, "kv_stride = %lld must be >= 576 and a multiple of 8", (long long)kv_stride);
+  if (!aligned(kv, 16)) return fail(SMLA_ERR_STRIDE, "kv is not 16-byte aligned");
+  if (!aligned(slots, 4)) return fail(SMLA_ERR_STRIDE, "slots is not 4-byte aligned");
+  if ((n + 3) / 4 > (int64_t)UINT32_MAX) return fail(SMLA_ERR_SHAPE, "n = %lld is too large", (long long)n);
+  smla::QuantParams p;
+  p.kv = static_cast<const uint16_t*>(kv);
+  p.n = n;
+  p.kv_stride = kv_stride;
+  p.slots = slots;
+  p.pool = static_cast<uint8_t*>(pool.base);
+  p.nslots = pool.num_blocks * 64;
+  p.block_stride = pool.block_stride_bytes;
+  return launched(smla::launch_quantize(p, pool.format, static_cast<hipStream_t>(stream)), "quantize");
+}
+
+static void fill_attn(smla::AttnParams& p, const void* q, int64_t T, int32_t H, int64_t q_st, int64_t q_sh,
+                      const smla_kv_pool& kv, const int32_t* indices, int32_t topk, int64_t idx_st,
+                      const int32_t* topk_length, float sm_scale) {
+  std::memset(&p, 0, sizeof p);
+  p.q = static_cast<const uint16_t*>(q);
+  p.q_st = q_st;
+  p.q_sh = q_sh;
+  p.T = T;
+  p.H = H;
+  p.pool = static_cast<const uint8_t*>(kv.base);
+  p.block_stride = kv.block_stride_bytes;
+  p.nslots = kv.num_blocks * 64;
+  p.idx = indices;
+  p.idx_st = idx_st;
+  p.topk = topk;
+  p.topk_length = topk_length;
+  p.scale_log2 = sm_scale * 1.4426950408889634f;
+}
+
+smla_status smla_prefill(const void* q, int64_t T, int32_t H, int64_t q_stride_t, int64_t q_stride_h,
+                         smla_kv_pool kv, const int32_t* indices, int32_t topk, int64_t idx_stride_t,
+                         const int32_t* topk_length, const float* sink, float sm_scale, void* out,
+                         int64_t out_stride_t, int64_t out_stride_h, float* lse, int64_t lse_stride_t,
+                         void* stream) {
+  smla_status st = check_attn_common(q, T, H, q_stride_t, q_stride_h, kv, indices, topk, idx_stride_t);
+  if (st != SMLA_OK) return st;
+  if (T == 0) return ok();
+  st = check_out(out, out_stride_t, out_stride_h, H, lse, lse_stride_t);
+  if (st != SMLA_OK) return st;
+  if (!std::isfinite(sm_scale)) return fail(SMLA_ERR_SHAPE, "sm_scale must be finite");
+  if (T == 0) return ok();
+  smla::AttnParams p;
+  fill_attn(p, q, T, H, q_stride_t, q_stride_h, kv, indices, topk, idx_stride_t, topk_length, sm_scale);
+  p.sink = sink;
+  p.out = static_cast<uint16_t*>(out);
+  p.out_st = out_stride_t;
+  p.out_sh = out_stride_h;
+  p.lse = lse;
+  p.lse_st = lse_stride_t;
+  return launched(smla::launch_attention(p, kv.format, false, static_cast<hipStream_t>(stream)), "prefill");
+}
+
+smla_status smla_decode(const void* q, int64_t T, int32_t H, int64_t q_stride_t, int64_t q_stride_h,
+                        smla_kv_pool kv, const int32_t* indices, int32_t topk, int64_t idx_stride_t,
+                        const int32_t* topk_length, float sm_scale, int32_t num_splits, float* part_out,
+                        float* part_lse, void* stream) {
+  smla_status st = check_attn_common(q, T, H, q_stride_t, q_stride_h, kv, indices, topk, idx_stride_t);
+  if (st != SMLA_OK) return st;
+  if (T == 0) return ok();
+  if (num_splits < 1 || num_splits > 64)
+    return fail(SMLA_ERR_UNSUPPORTED, "num_splits = %d is not supported (supported: 1..64)", num_splits);
+  if (!part_out) return fail(SMLA_ERR_NULL, "part_out is NULL");
+  if (!part_lse) return fail(SMLA_ERR_NULL, "part_lse is NULL");
+  if (!aligned(part_out, 16)) return fail(SMLA_ERR_STRIDE, "part_out is not 16-byte aligned");
+  if (!aligned(part_lse, 4)) return fail(SMLA_ERR_STRIDE, "part_lse is not 4-byte aligned");
+  if (!std::isfinite(sm_scale)) return fail(SMLA_ERR_SHAPE, "sm_scale must be finite");
+  if (T == 0) return ok();
+  smla::AttnParams p;
+  fill_attn(p, q, T, H, q_stride_t, q_stride_h, kv, indices, topk, idx_stride_t, topk_length, sm_scale);
+  p.part_out = part_out;
+  p.part_lse = part_lse;
+  p.num_splits = num_splits;
+  p.split_w = smla_split_width(topk, num_splits);
+  return launched(smla::launch_attention(p, kv.format, true, static_cast<hipStream_t>(stream)), "decode");
+}
+
+smla_status smla_combine(const float* part_out, const float* part_lse, int64_t T, int32_t num_splits,
+                         int32_t H, const float* sink, void* out, int64_t out_stride_t,
+                         int64_t out_stride_h, float* lse, int64_t lse_stride_t, void* stream) {
+  if (T < 0) return fail(SMLA_ERR_SHAPE, "T = %lld must be >= 0", (long long)T);
+  if (T == 0) return ok();  // nothing is read or launched
+  if (H < 1 || H > 128) return fail(SMLA_ERR_UNSUPPORTED, "H = %d is not supported (supported: 1..128)", H);
+  if (num_splits < 1 || num_splits > 64)
+    return fail(SMLA_ERR_UNSUPPORTED, "num_splits = %d is not supported (supported: 1..64)", num_splits);
+  if (!part_out) return fail(SMLA_ERR_NULL, "part_out is NULL");
+  if (!part_lse) return fail(SMLA_ERR_NULL, "part_lse is NULL");
+  if (!aligned(part_out, 16)) return fail(SMLA_ERR_STRIDE, "part_out is not 16-byte aligned");
+  smla_status st = check_out(out, out_stride_t, out_stride_h, H, lse, lse_stride_t);
+  if (st != SMLA_OK) return st;
+  if (T == 0) return ok();
+  if ((T * H + 3) / 4 > (int64_t)UINT32_MAX) return fail(SMLA_ERR_SHAPE, "T*H is too large");
+  smla::CombineParams p;
+  p.part_out = part_out;
+  p.part_lse = part_lse;
+  p.T = T;
+  p.S = num_splits;
+  p.H = H;
+  p.sink = sink;
+  p.out = static_cast<uint16_t*>(out);
+  p.out_st = out_stride_t;
+  p.out_sh = out_stride_h;
+  p.lse = lse;
+  p.lse_st = lse_stride_t;
+  return launched(smla::launch_combine(p, static_cast<hipStream_t>(stream)), "combine");
+}
+
+}  // extern "C"

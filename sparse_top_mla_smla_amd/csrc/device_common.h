@@ -1,0 +1,108 @@
+// device_common.h -- gfx950 device helpers shared by the smla kernels:
+// vector types, MFMA wrappers, FP8/INT8 -> BF16 converters and the cache
+// row geometry.  Lane layouts used below were checked on gfx950:
+//  * v_mfma_f32_16x16x32_bf16: lane l holds A[m = l%16][k = 8(l/16)+i] and
+//    B[k = 8(l/16)+i][n = l%16] (i < 8); D[m = 4(l/16)+i][n = l%16] (i < 4).
+//  * v_mfma_f32_16x16x16_bf16: same with k = 4(l/16)+i (i < 4).
+//  * ds_read_b64_tr_b16: within each 16-lane group, lane 4r+b supplies the
+//    address of row r, columns 4b..4b+3 of a 4x16 block of 16-bit values and
+//    receives column (lane%16) of rows 0..3.
+//  * ds_read_b64_tr_b8: lane 2r+b supplies row r, byte columns 8b..8b+7 of
+//    an 8x16 byte block and receives byte column (lane%16) of rows 0..7.
+//  * v_cvt_pk_f32_fp8 decodes OCP E4M3 exactly.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace smla {
+
+constexpr int D_NOPE = 512;
+constexpr int D_ROPE = 64;
+constexpr int D_QK = 576;
+constexpr int D_V = 512;
+constexpr int PAGE = 64;
+constexpr int QTILE = 128;  // quantization tile along the nope part
+
+enum : int { FMT_BF16 = 0, FMT_FP8 = 1, FMT_INT8 = 2 };
+
+template <int FMT>
+struct RowGeom {
+  // bytes of one cache row and its sections
+  static constexpr int BYTES = (FMT == FMT_BF16) ? 2 * D_QK : D_NOPE + 16 + 2 * D_ROPE;
+  static constexpr int SCALE_OFF = D_NOPE;        // FP8/INT8: 4 x fp32
+  static constexpr int ROPE_OFF = (FMT == FMT_BF16) ? 2 * D_NOPE : D_NOPE + 16;
+  static constexpr int CHUNKS = BYTES / 16;       // 16-byte pieces per row
+};
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x4 mfma_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_16x16x16(i16x4 a, i16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+// two floats -> packed BF16 pair (round to nearest even)
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  bf16x2 v;
+  v[0] = (__bf16)lo;
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __builtin_bit_cast(float, (uint32_t)b << 16);
+}
+
+// four E4M3 codes (one dword) -> four BF16 values (exact)
+__device__ __forceinline__ uint2 fp8x4_to_bf16x4(uint32_t v) {
+  f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(v, false);
+  f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(v, true);
+  return make_uint2(pack_bf16(lo[0], lo[1]), pack_bf16(hi[0], hi[1]));
+}
+
+// four int8 codes (one dword) -> four BF16 values (exact: |code| <= 127)
+__device__ __forceinline__ uint2 int8x4_to_bf16x4(uint32_t v) {
+  float a = (float)(int8_t)(v & 0xFF);
+  float b = (float)(int8_t)((v >> 8) & 0xFF);
+  float c = (float)(int8_t)((v >> 16) & 0xFF);
+  float d = (float)(int8_t)(v >> 24);
+  return make_uint2(pack_bf16(a, b), pack_bf16(c, d));
+}
+
+template <int FMT>
+__device__ __forceinline__ uint2 codes4_to_bf16x4(uint32_t v) {
+  if constexpr (FMT == FMT_FP8) return fp8x4_to_bf16x4(v);
+  else return int8x4_to_bf16x4(v);
+}
+
+__device__ __forceinline__ i32x2 lds_read_tr8(const void* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(p));
+}
+__device__ __forceinline__ i16x4 lds_read_tr16(const void* p) {
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  bf16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(p));
+  return __builtin_bit_cast(i16x4, r);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+}  // namespace smla

@@ -1,0 +1,62 @@
+// launch.h -- kernel parameter blocks and host launchers behind the C ABI.
+// Everything here is called only after the C entry points have validated
+// their arguments (see api.cpp).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace smla {
+
+struct QuantParams {
+  const uint16_t* kv;   // bf16 [n, kv_stride]
+  int64_t n;
+  int64_t kv_stride;    // elements
+  const int32_t* slots; // [n]
+  uint8_t* pool;
+  int64_t nslots;       // num_blocks * 64
+  int64_t block_stride; // bytes
+};
+
+struct AttnParams {
+  const uint16_t* q;    // bf16
+  int64_t q_st, q_sh;   // elements
+  int64_t T;
+  int32_t H;
+  const uint8_t* pool;
+  int64_t block_stride; // bytes
+  int64_t nslots;
+  const int32_t* idx;
+  int64_t idx_st;       // elements
+  int32_t topk;
+  const int32_t* topk_length;  // may be null
+  const float* sink;           // may be null (prefill only)
+  float scale_log2;            // sm_scale * log2(e)
+  // prefill outputs
+  uint16_t* out;
+  int64_t out_st, out_sh;
+  float* lse;
+  int64_t lse_st;
+  // decode outputs
+  float* part_out;      // [T, S, H, 512]
+  float* part_lse;      // [T, S, H]
+  int32_t num_splits;
+  int32_t split_w;
+};
+
+struct CombineParams {
+  const float* part_out;
+  const float* part_lse;
+  int64_t T;
+  int32_t S, H;
+  const float* sink;
+  uint16_t* out;
+  int64_t out_st, out_sh;
+  float* lse;
+  int64_t lse_st;
+};
+
+hipError_t launch_quantize(const QuantParams& p, int fmt, hipStream_t s);
+hipError_t launch_attention(const AttnParams& p, int fmt, bool decode, hipStream_t s);
+hipError_t launch_combine(const CombineParams& p, hipStream_t s);
+
+}  // namespace smla

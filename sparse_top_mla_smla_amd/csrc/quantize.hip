@@ -1,0 +1,125 @@
+// quantize.hip -- cache writer: BF16 latent rows -> pool rows.
+//
+// Row layout from the FlashInfer PR #4802 review of the DSv3.2 decode kernel:
+// 512 e4m3 codes, four FP32 per-128 scales, 64 BF16 rope values (656 bytes);
+// the page states DSv3.2 stores power-of-two scales.  INT8 rows reuse the
+// layout with int8 codes and amax/127 scales; BF16 rows are a copy.
+//
+// One wave per row.  Lane l owns nope elements [8l, 8l+8): the 16 lanes of
+// a lane group cover one 128-element scale tile, so the tile amax is a
+// 16-lane max.  All scale and code arithmetic is IEEE float32 (correctly
+// rounded division), which is what fixes the integer codes.
+#include "device_common.h"
+#include "launch.h"
+
+namespace smla {
+
+// Nearest E4M3 code to a float32 y with |y| <= 448 (larger magnitudes
+// saturate to 448), ties to the even mantissa, sign kept.  Works on the
+// float32 bit pattern.
+__device__ __forceinline__ uint32_t e4m3_from_f32(float y) {
+  uint32_t u = __builtin_bit_cast(uint32_t, y);
+  uint32_t sign = (u >> 24) & 0x80u;
+  uint32_t a = u & 0x7FFFFFFFu;
+  if (a >= 0x43E00000u) return sign | 0x7Eu;          // >= 448 (and inf/nan)
+  if (a < 0x3C800000u) {                              // < 2^-6: quantum 2^-9
+    float t = __builtin_bit_cast(float, a) * 512.0f;  // exact scaling
+    uint32_t m = (uint32_t)__builtin_rintf(t);        // 0..8, ties to even
+    return sign | m;                                  // 8 -> 0x08 = 2^-6
+  }
+  int32_t e = (int32_t)(a >> 23) - 127;               // -6..8
+  uint32_t mant = a & 0x7FFFFFu;
+  uint32_t keep = mant >> 20, rest = mant & 0xFFFFFu;
+  if (rest > 0x80000u || (rest == 0x80000u && (keep & 1u))) keep += 1;
+  if (keep == 8u) { keep = 0; e += 1; }
+  uint32_t code = (uint32_t)((e + 7) << 3) | keep;
+  if (code > 0x7Eu) code = 0x7Eu;
+  return sign | code;
+}
+
+// 2^ceil(log2(amax/448)) from the bits of r = amax / 448 (float32, r > 0).
+__device__ __forceinline__ float fp8_tile_scale(float amax) {
+  if (amax == 0.0f) return 1.0f;
+  float r = __fdiv_rn(amax, 448.0f);
+  uint32_t rb = __builtin_bit_cast(uint32_t, r);
+  int e;
+  if (rb >= 0x00800000u) {
+    e = (int)(rb >> 23) - 127 + ((rb & 0x7FFFFFu) != 0u);
+  } else {  // subnormal r = rb * 2^-149
+    e = (32 - __clz((int)(rb - 1u))) - 149;
+  }
+  uint32_t sb = (e >= -126) ? (uint32_t)(e + 127) << 23 : 1u << (e + 149);
+  return __builtin_bit_cast(float, sb);
+}
+
+template <int FMT>
+__global__ __launch_bounds__(256) void quantize_kernel(QuantParams p) {
+  using G = RowGeom<FMT>;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= p.n) return;
+  const int64_t slot = p.slots[row];
+  if (slot < 0 || slot >= p.nslots) return;
+  const uint16_t* src = p.kv + row * p.kv_stride;
+  uint8_t* dst = p.pool + (slot / PAGE) * p.block_stride + (slot % PAGE) * G::BYTES;
+
+  if constexpr (FMT == FMT_BF16) {
+    const uint4* s4 = reinterpret_cast<const uint4*>(src);
+    uint4* d4 = reinterpret_cast<uint4*>(dst);
+    d4[lane] = s4[lane];
+    if (lane < G::CHUNKS - 64) d4[64 + lane] = s4[64 + lane];
+    return;
+  } else {
+    const uint4 raw = reinterpret_cast<const uint4*>(src)[lane];  // 8 bf16
+    float x[8];
+    uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __builtin_bit_cast(float, w[i] << 16);
+      x[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xFFFF0000u);
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+
+    uint32_t code[8];
+    float scale;
+    if constexpr (FMT == FMT_FP8) {
+      scale = fp8_tile_scale(amax);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) code[i] = e4m3_from_f32(__fdiv_rn(x[i], scale));
+    } else {
+      scale = (amax == 0.0f) ? 1.0f : __fdiv_rn(amax, 127.0f);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float qv = __builtin_rintf(__fdiv_rn(x[i], scale));
+        qv = fminf(fmaxf(qv, -127.0f), 127.0f);
+        code[i] = (uint32_t)(int32_t)qv & 0xFFu;
+      }
+    }
+    uint2 packed;
+    packed.x = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
+    packed.y = code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24);
+    reinterpret_cast<uint2*>(dst)[lane] = packed;
+    if ((lane & 15) == 0) reinterpret_cast<float*>(dst + G::SCALE_OFF)[lane >> 4] = scale;
+    if (lane < 16) {
+      const uint2* rs = reinterpret_cast<const uint2*>(src + D_NOPE);
+      reinterpret_cast<uint2*>(dst + G::ROPE_OFF)[lane] = rs[lane];
+    }
+  }
+}
+
+hipError_t launch_quantize(const QuantParams& p, int fmt, hipStream_t s) {
+  dim3 grid((unsigned)((p.n + 3) / 4)), block(256);
+  switch (fmt) {
+    case FMT_BF16: hipLaunchKernelGGL(quantize_kernel<FMT_BF16>, grid, block, 0, s, p); break;
+    case FMT_FP8: hipLaunchKernelGGL(quantize_kernel<FMT_FP8>, grid, block, 0, s, p); break;
+    case FMT_INT8: hipLaunchKernelGGL(quantize_kernel<FMT_INT8>, grid, block, 0, s, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace smla
