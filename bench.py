@@ -1,0 +1,261 @@
+#!/usr/bin/env python3
+"""Benchmark of sparse MLA attention on one MI355X.
+
+Workload (the metric's configuration): FP8 fused prefill at the 16k
+footprint -- one sequence of 16384 tokens in a shuffled 64-row paged pool,
+T = 1024 queries at its last positions, H = 64 heads, causal top-k width
+1024, BF16 q ~ N(0,1).  One step = writing the batch's 1024 new latent rows
+into the cache (smla_quantize_kv) + the prefill over the T tokens
+(smla_prefill).  Inputs are resident in HBM before the timed region.
+
+Also measured in the same run (reported under "decode"): the split-KV
+decode batch -- 64 sequences x 1 query, ctx 16384 each (656 MiB FP8 pool),
+H = 64, top-k 2048, 8 splits, decode + combine.
+
+Prints one JSON line on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense BF16 matrix peak
+PAGE_A5000_US_PER_TOKEN = 5.258e3 / 1024  # AppMana release note: fp8 width 1024 on RTX A5000
+D_QK, D_V = 576, 512
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--width", type=int, default=1024, help="prefill index width (512 or 1024)")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=256)
+    return ap.parse_args()
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sparse_top_mla_smla_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(sha: str):
+    """HBM traffic per prefill launch from committed rocprofv3 --pmc runs,
+    only while the kernel sources are the ones the counters were taken on."""
+    path = os.path.join(ROOT, "profiles", "traffic_prefill_c3.json")
+    try:
+        with open(path) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_sha") != sha:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(this library has no multi-GPU path; see DESIGN.md for how it would shard)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import sparse_top_mla_smla_amd as smla
+    from sparse_top_mla_smla_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    smla.row_bytes(W.FMT_FP8)  # raises if libsmla.so is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    # ---------------- prefill workload ----------------
+    t0 = time.time()
+    case = W.c3_prefill(width=args.width)
+    T, H = case.T, case.H
+    q = bf16(case.q_buf)
+    kv = bf16(case.kv)
+    slots = torch.from_numpy(case.slots).to(dev)
+    idx = torch.from_numpy(case.idx_buf).to(dev)
+    pool = smla.KVPool.empty(case.num_blocks, W.FMT_FP8, device=dev)
+    n_ctx = case.ctx - T
+    smla.quantize_kv(kv[:n_ctx], slots[:n_ctx], pool)            # context written once
+    new_kv, new_slots = kv[n_ctx:], slots[n_ctx:]                 # the batch's own rows
+    out = torch.empty((T, H, D_V), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    setup_s = time.time() - t0
+
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        smla.quantize_kv(new_kv, new_slots, pool)
+        if ev is not None:
+            ev[0].record(stream)
+        smla.prefill(q, pool, idx, sm_scale=float(case.sm_scale), out=out, lse=lse)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    ms_per_step = elapsed * 1e3 / args.steps
+    kern_ms = [a.elapsed_time(b) for a, b in evs]
+    prefill_ms = float(np.mean(kern_ms))
+
+    rows = case.gathered_rows()
+    kv_bytes = rows * W.ROW_BYTES[W.FMT_FP8]
+    io_bytes = T * H * (D_QK * 2 + D_V * 2 + 4) + T * case.topk * 4
+    alg_bytes = kv_bytes + io_bytes
+    flops = 2.0 * H * (D_QK + D_V) * rows
+    achieved = alg_bytes / (prefill_ms * 1e-3) / 1e9
+    us_per_token = ms_per_step * 1e3 / T
+    sha = kernel_source_sha()
+    traffic = load_traffic(sha)
+
+    result = {
+        "metric": "sparse-MLA prefill µs/token & gathered-KV GB/s, T=1024 ctx16k H=64 topk1024",
+        "value": round(us_per_token, 5),
+        "unit": "us/token",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": round(us_per_token / PAGE_A5000_US_PER_TOKEN, 6) if args.width == 1024 else None,
+        "dtype": "fp8_e4m3 cache / bf16 mfma / f32 softmax",
+        "data": "synthetic (seeded N(0,1) latent and q, uniform causal top-k over a shuffled paged pool)",
+        "config": {"workload": f"fp8 sparse-MLA prefill T={T} ctx={case.ctx} H={H} topk={case.topk} "
+                               f"page_block=64 (cache write of the batch's {T} rows + prefill)",
+                   "T": T, "ctx": case.ctx, "H": H, "topk": case.topk, "kv_format": "fp8_e4m3_656B"},
+        "gathered_kv_GBps": round(kv_bytes / (prefill_ms * 1e-3) / 1e9, 2),
+        "prefill_kernel_us": round(prefill_ms * 1e3, 3),
+        "prefill_us_per_token_kernel": round(prefill_ms * 1e3 / T, 5),
+        "mfma_util": round(flops / (prefill_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic,
+                     "kernel": "attn_kernel<FP8, prefill>",
+                     "algorithmic_bytes_per_launch": alg_bytes},
+        "kernel_source_sha": sha,
+    }
+    print(f"[bench] prefill setup {setup_s:.1f}s, step {ms_per_step:.3f} ms, kernel {prefill_ms:.3f} ms",
+          file=sys.stderr, flush=True)
+
+    # ---------------- decode workload ----------------
+    if not args.no_decode:
+        del kv
+        dc = W.c2_decode()
+        dq = bf16(dc.q_buf)
+        dkv = bf16(dc.kv)
+        dslots = torch.from_numpy(dc.slots).to(dev)
+        didx = torch.from_numpy(dc.idx_buf).to(dev)
+        dpool = smla.KVPool.empty(dc.num_blocks, W.FMT_FP8, device=dev)
+        smla.quantize_kv(dkv, dslots, dpool)
+        del dkv
+        S = dc.num_splits
+        po = torch.empty((dc.T, S, dc.H, D_V), dtype=torch.float32, device=dev)
+        pl = torch.empty((dc.T, S, dc.H), dtype=torch.float32, device=dev)
+        dout = torch.empty((dc.T, dc.H, D_V), dtype=torch.bfloat16, device=dev)
+        dlse = torch.empty((dc.T, dc.H), dtype=torch.float32, device=dev)
+        # rotate over independent index sets so no call finds its rows cache-warm
+        rng = np.random.default_rng(7)
+        idx_sets = [didx]
+        for k in range(2):
+            perm = rng.permutation(dc.num_blocks).astype(np.int32)
+            remap = torch.from_numpy(perm).to(dev)
+            # same positions, different blocks: a fresh permutation of the block ids
+            moved = remap[(didx.clamp(min=0) // 64).long()] * 64 + didx.clamp(min=0) % 64
+            idx_sets.append(torch.where(didx >= 0, moved, didx).to(torch.int32))
+        torch.cuda.synchronize()
+        dsteps = max(args.steps, 20)
+
+        def dstep(i, ev=None):
+            ix = idx_sets[i % len(idx_sets)]
+            if ev is not None:
+                ev[0].record(stream)
+            smla.decode(dq, dpool, ix, S, sm_scale=float(dc.sm_scale), part_out=po, part_lse=pl)
+            if ev is not None:
+                ev[1].record(stream)
+            smla.combine(po, pl, out=dout, lse=dlse)
+            if ev is not None:
+                ev[2].record(stream)
+
+        for i in range(args.warmup):
+            dstep(i)
+        devs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(dsteps)]
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for i in range(dsteps):
+            dstep(i, devs[i])
+        torch.cuda.synchronize()
+        d_elapsed = (time.perf_counter() - t1) * 1e6 / dsteps
+        dec_us = float(np.mean([a.elapsed_time(b) for a, b, _ in devs])) * 1e3
+        comb_us = float(np.mean([b.elapsed_time(c) for _, b, c in devs])) * 1e3
+        drows = dc.gathered_rows()
+        dbytes = drows * W.ROW_BYTES[W.FMT_FP8]
+        result["decode"] = {
+            "workload": f"fp8 split-KV decode {dc.T} seqs x 1 query, ctx {dc.ctx}, H={dc.H}, "
+                        f"topk={dc.topk}, splits={S} (decode + combine)",
+            "us_per_call": round(d_elapsed, 3),
+            "decode_kernel_us": round(dec_us, 3),
+            "combine_kernel_us": round(comb_us, 3),
+            "gathered_kv_bytes": dbytes,
+            "gathered_kv_GBps_decode_kernel": round(dbytes / (dec_us * 1e-6) / 1e9, 2),
+            "gathered_kv_GBps_end_to_end": round(dbytes / ((dec_us + comb_us) * 1e-6) / 1e9, 2),
+            "hbm_frac_end_to_end": round(dbytes / ((dec_us + comb_us) * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+        }
+        print(f"[bench] decode {dec_us:.2f} us + combine {comb_us:.2f} us", file=sys.stderr, flush=True)
+
+    # ---------------- CPU baseline: the oracle on a bounded sample ----------------
+    if not args.no_cpu:
+        import oracle
+        ncores = min(16, os.cpu_count() or 1)
+        pool_h = oracle.Pool(np.zeros((case.num_blocks, 64 * 656), np.uint8), W.FMT_FP8, 64 * 656)
+        oracle.quantize_kv(case.kv, case.slots, pool_h)
+        n = min(args.cpu_tokens, T)
+        tokens = np.linspace(0, T - 1, n).astype(np.int64)
+        tc = time.perf_counter()
+        oracle.prefill(case.q, pool_h, case.indices, sm_scale=case.sm_scale, tokens=tokens, nthreads=ncores)
+        cpu_s = time.perf_counter() - tc
+        result["cpu_baseline"] = {
+            "value": round(cpu_s * 1e6 / n, 3), "unit": "us/token", "cores": ncores, "kind": "oracle",
+            "sample": f"{n} of the {T} tokens of the same prefill workload (float64 C oracle, "
+                      f"OpenMP over tokens), {cpu_s:.2f} s wall"}
+        print(f"[bench] cpu oracle {cpu_s:.2f}s for {n} tokens on {ncores} threads", file=sys.stderr, flush=True)
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,401 @@
+// attention_wide.hip -- sparse MLA attention for many heads (H > 16) over an
+// FP8 or INT8 paged latent cache, prefill form and split-KV decode partials.
+//
+// What is computed is stated in include/smla.h.  This kernel serves the
+// shapes of the AppMana release note's fused prefill (T=1024, ctx 16384,
+// H=64, widths 512/1024, FP8 and INT8 caches) and the decode batch: one
+// workgroup owns one token (and split) for 64 heads, so every selected row
+// is gathered from the pool once per token, not once per head group.
+//
+// All products use v_mfma_f32_32x32x16_bf16 (full matrix rate on gfx950).
+// Eight waves (two per SIMD); wave w = g + 4hh works on latent group g and
+// head half hh.  Per 64-candidate tile:
+//  1. QK^T, split over the latent dimension: wave (g, hh) multiplies the
+//     tile's K rows restricted to nope columns [128g, 128g+128) -- exactly
+//     one 128-wide scale tile -- by its slice of Q (kept in registers for
+//     the whole token).  Result: unscaled partial S^T, 64 candidates x 32
+//     heads.
+//  2. Reduce-scatter of the partials through LDS: four owner waves (one
+//     per SIMD) each own a 32x32 score tile, receive the other three
+//     groups' partials for it and form S = sum_g scale[c][g] * N_g + R,
+//     where R is the 64-wide rope product of the tile.
+//  3. Online softmax on the owned 32x32 tile; the two waves that own the
+//     same heads exchange their row maxima, so every head has one running
+//     max.  The max moves lazily (only when exceeded by 2^8), so O is
+//     rarely rescaled.  P goes to LDS in FP32.
+//  4. PV, split over output columns and heads: wave (g, hh) accumulates
+//     O^T for columns [128g, 128g+128) of its 32 heads.  V^T comes from the raw FP8/INT8
+//     codes with ds_read_b64_tr_b8 and is converted to BF16 exactly; the
+//     row scale of column group w is folded into P.
+// The raw tiles are double-buffered in LDS and filled straight from global
+// memory with global_load_lds_dwordx4 (lane l of a wave lands at base+16l;
+// no staging registers), one tile ahead; the index lists run two tiles
+// ahead.  Rows that are never loaded (masked entries) keep finite stale
+// data from earlier valid rows or the initial zero fill, and contribute
+// nothing because their probabilities are exactly 0.
+#include "device_common.h"
+#include "launch.h"
+
+namespace smla {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int FMT>
+__device__ __forceinline__ bf16x8 codes8_to_bf16x8(uint2 c8) {
+  const uint2 lo = codes4_to_bf16x4<FMT>(c8.x), hi = codes4_to_bf16x4<FMT>(c8.y);
+  return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+
+__device__ __forceinline__ void global_to_lds_16(const void* src, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                   (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
+
+namespace wide {
+constexpr int NT = 512;                      // 8 waves, 2 per SIMD
+constexpr int TC = 64;                       // candidates per tile
+constexpr int RB = 656;                      // FP8/INT8 row bytes
+constexpr int RS = 672;                      // LDS row stride
+constexpr int CHUNKS = RB / 16;              // 41 used chunk slots per row
+constexpr int SLOTS = RS / 16;               // 42 chunk slots per LDS row
+constexpr int ROUNDS = (TC * SLOTS + NT - 1) / NT;  // 6 direct-load rounds per tile
+constexpr int OFF_RAW = 0;                   // [2][64][RS]
+constexpr int OFF_RECV = 2 * TC * RS;        // [4 score tiles][3 senders][64 lanes][16] f32
+constexpr int OFF_PL = OFF_RECV + 4 * 3 * 64 * 16 * 4;
+constexpr int PLS = 68;                      // P row stride (floats): [64 heads][PLS]
+constexpr int OFF_MAX = OFF_PL + 64 * PLS * 4;   // [2][64] f32
+constexpr int OFF_ALPHA = OFF_MAX + 2 * 64 * 4;  // [64] f32
+constexpr int OFF_SCT = OFF_ALPHA + 64 * 4;      // [4 groups][64 rows] f32
+constexpr int OFF_IDX = OFF_SCT + 4 * TC * 4;    // [4][64] int32
+constexpr int LDS_BYTES = OFF_IDX + 4 * TC * 4;
+constexpr float TAU = 8.0f;
+}  // namespace wide
+
+// Wave w = g + 4*hh works on latent group g (nope columns [128g, 128g+128),
+// output columns likewise) for head half hh (heads [32hh, 32hh+32)).  Score
+// tile (c2, hh) -- candidates [32c2, +32) x heads [32hh, +32) -- is owned by
+// wave c2 + 6hh (waves 0, 1, 6, 7: one owner per SIMD).
+template <int FMT, bool DECODE>
+__global__ __launch_bounds__(wide::NT, 1) void attn_wide_kernel(AttnParams p) {
+  using namespace wide;
+  static_assert(FMT == FMT_FP8 || FMT == FMT_INT8, "wide kernel serves quantized caches");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[LDS_BYTES];
+  float* recv = reinterpret_cast<float*>(smem + OFF_RECV);
+  float* pl = reinterpret_cast<float*>(smem + OFF_PL);
+  float* maxb = reinterpret_cast<float*>(smem + OFF_MAX);
+  float* alpha_l = reinterpret_cast<float*>(smem + OFF_ALPHA);
+  float* sct = reinterpret_cast<float*>(smem + OFF_SCT);
+  int32_t* idxl = reinterpret_cast<int32_t*>(smem + OFF_IDX);
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int g = w & 3, hh = w >> 2;
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+  const bool owner = (w == 0 || w == 1 || w == 6 || w == 7);
+  const int oc2 = owner ? (w & 1) : 0;  // candidate half of the owned score tile
+
+  const int64_t t = blockIdx.x;
+  const int h0 = blockIdx.y * 64;
+  const int split = DECODE ? (int)blockIdx.z : 0;
+
+  int64_t L = p.topk;
+  if (p.topk_length) {
+    const int64_t v = p.topk_length[t];
+    L = v < 0 ? 0 : (v > p.topk ? p.topk : v);
+  }
+  int64_t j_begin = 0, j_end = p.topk;
+  if (DECODE) {
+    j_begin = (int64_t)split * p.split_w;
+    j_end = j_begin + p.split_w;
+    if (j_end > p.topk) j_end = p.topk;
+  }
+  if (j_end > L) j_end = L;
+  const int n_tiles = j_end > j_begin ? (int)((j_end - j_begin + TC - 1) / TC) : 0;
+
+  // Q as the B operand of S^T = K Q^T for head h0 + 32hh + l32: qn holds nope
+  // columns 128g + 16ks + 8hi + i, qr rope columns 16ks + 8hi + i (owners).
+  bf16x8 qn[8], qr[4];
+  {
+    const int h = h0 + 32 * hh + l32;
+    const bool hv = h < p.H;
+    const uint16_t* qrow = p.q + t * p.q_st + (int64_t)(hv ? h : 0) * p.q_sh;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      uint4 v = *reinterpret_cast<const uint4*>(qrow + 128 * g + 16 * ks + 8 * hi);
+      qn[ks] = __builtin_bit_cast(bf16x8, hv ? v : make_uint4(0, 0, 0, 0));
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      uint4 v = *reinterpret_cast<const uint4*>(qrow + D_NOPE + 16 * ks + 8 * hi);
+      qr[ks] = __builtin_bit_cast(bf16x8, hv ? v : make_uint4(0, 0, 0, 0));
+    }
+  }
+
+  const int32_t* idx_row = p.idx + t * p.idx_st;
+  auto load_idx = [&](int k) -> int32_t {
+    const int64_t j = j_begin + (int64_t)k * TC + tid;
+    int32_t v = -1;
+    if (j < j_end) {
+      const int32_t x = idx_row[j];
+      if (x >= 0 && (int64_t)x < p.nslots) v = x;
+    }
+    return v;
+  };
+  // gather tile k into raw buffer k&1: chunk slot q = (r*8 + w)*64 + lane,
+  // row q / 42, 16-byte chunk q % 42 (chunk 41 is row padding)
+  auto issue_tile = [&](int k) {
+    const int32_t* il = idxl + (k & 3) * TC;
+    uint8_t* raw = smem + OFF_RAW + (k & 1) * TC * RS;
+    int q = w * 64 + lane;
+    int row = q / SLOTS, ck = q % SLOTS;
+#pragma unroll 1
+    for (int r = 0; r < ROUNDS; ++r) {
+      if (row < TC && ck < CHUNKS) {
+        const int32_t slot = il[row];
+        if (slot >= 0) {
+          const uint8_t* src = p.pool + (int64_t)(slot / PAGE) * p.block_stride + (int64_t)(slot % PAGE) * RB + 16 * ck;
+          global_to_lds_16(src, raw + 16 * (r * 8 + w) * 64);
+        }
+      }
+      // advance q by 512 = 12 * 42 + 8
+      row += 12;
+      ck += 8;
+      if (ck >= SLOTS) {
+        ck -= SLOTS;
+        row += 1;
+      }
+    }
+  };
+
+  // running softmax state of an owned score tile (heads 32hh + l32)
+  float m_run = -INFINITY;
+  float l_part = 0.0f;
+  // O^T accumulators: columns [128g + 32dt, +32) x heads [32hh, +32)
+  f32x16 O[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) O[dt][i] = 0.0f;
+
+  if (n_tiles > 0) {
+    for (int i = tid; i < 2 * TC * RS / 16; i += NT) reinterpret_cast<uint4*>(smem + OFF_RAW)[i] = make_uint4(0, 0, 0, 0);
+    if (tid < TC) {
+      idxl[0 * TC + tid] = load_idx(0);
+      idxl[1 * TC + tid] = n_tiles > 1 ? load_idx(1) : -1;
+    }
+    __syncthreads();
+    issue_tile(0);
+  }
+
+  for (int k = 0; k < n_tiles; ++k) {
+    const uint8_t* raw = smem + OFF_RAW + (k & 1) * TC * RS;
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's part of tile k has landed
+    __syncthreads();                // B0: all of tile k is in LDS
+    int32_t pend = -1;
+    if (k + 2 < n_tiles && tid < TC) pend = load_idx(k + 2);
+
+    // ---- 1./2. unscaled partial S^T over nope columns [128g, 128g+128)
+    // for heads 32hh..; the tile (c2, hh) goes to its owner c2 + 6hh ----
+    f32x16 own;
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+      f32x16 acc;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+      const uint8_t* rowA = raw + (32 * c2 + l32) * RS + 128 * g + 8 * hi;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        acc = mfma_32x32x16(codes8_to_bf16x8<FMT>(*reinterpret_cast<const uint2*>(rowA + 16 * ks)), qn[ks], acc);
+      const int ow = c2 + 6 * hh;
+      if (ow == w) {
+        own = acc;
+      } else {
+        const int og = c2 + 2 * hh;             // latent group of the owner
+        const int slot = g < og ? g : g - 1;
+        f32x4* dst = reinterpret_cast<f32x4*>(recv + (((c2 + 2 * hh) * 3 + slot) * 64 + lane) * 16);
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) dst[q4] = f32x4{acc[4 * q4], acc[4 * q4 + 1], acc[4 * q4 + 2], acc[4 * q4 + 3]};
+      }
+    }
+    // rope product of the owned tile (all 64 rope columns)
+    f32x16 s;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[i] = 0.0f;
+    if (owner) {
+      const uint8_t* rowR = raw + (32 * oc2 + l32) * RS + D_NOPE + 16 + 16 * hi;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        s = mfma_32x32x16(__builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(rowR + 32 * ks)), qr[ks], s);
+    }
+    __syncthreads();  // B1: partials visible; every wave is past PV(k-1)
+
+    if (k + 1 < n_tiles) issue_tile(k + 1);
+    if (k + 2 < n_tiles && tid < TC) idxl[((k + 2) & 3) * TC + tid] = pend;
+
+    if (owner) {
+      // S = sum_g scale[c][g] * N_g + rope over the owned rows
+      // c = 32oc2 + 8q4 + 4hi + r, one 4-row block at a time
+      const int tile_id = oc2 + 2 * hh;
+      const f32x4* rsrc = reinterpret_cast<const f32x4*>(recv + (tile_id * 3 * 64 + lane) * 16);
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        f32x4 sc4[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          sc4[r] = *reinterpret_cast<const f32x4*>(raw + (32 * oc2 + 8 * q4 + 4 * hi + r) * RS + D_NOPE);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s[4 * q4 + r] += sc4[r][g] * own[4 * q4 + r];
+#pragma unroll
+        for (int slot = 0; slot < 3; ++slot) {
+          const int gs = slot < g ? slot : slot + 1;
+          const f32x4 v = rsrc[slot * 64 * 4 + q4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) s[4 * q4 + r] += sc4[r][gs] * v[r];
+        }
+      }
+      const int32_t* il = idxl + (k & 3) * TC + 32 * oc2 + 4 * hi;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 4 * q4 + r;
+          s[i] = il[8 * q4 + r] >= 0 ? s[i] * p.scale_log2 : -INFINITY;
+          mx = fmaxf(mx, s[i]);
+        }
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      if (hi == 0) maxb[oc2 * 64 + 32 * hh + l32] = mx;
+    } else {
+      // the four other waves transpose the tile's scales for PV:
+      // sct[gg][row] = scale of row `row`, 128-column group gg
+      const int e = (w - 2) * 64 + lane;  // waves 2..5 -> 0..255
+      const int row = e >> 2, gg = e & 3;
+      sct[gg * TC + row] = *reinterpret_cast<const float*>(raw + row * RS + D_NOPE + 4 * gg);
+    }
+    __syncthreads();  // B2
+    if (owner) {
+      const float mx = fmaxf(maxb[32 * hh + l32], maxb[64 + 32 * hh + l32]);
+      const bool need = mx > m_run + TAU;
+      const float alpha = need ? ((m_run == -INFINITY) ? 0.0f : exp2f(m_run - mx)) : 1.0f;
+      m_run = need ? mx : m_run;
+      float psum = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        s[i] = (s[i] == -INFINITY) ? 0.0f : exp2f(s[i] - m_run);
+        psum += s[i];
+      }
+      l_part = l_part * alpha + psum;
+      float* prow = pl + (32 * hh + l32) * PLS + 32 * oc2 + 4 * hi;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *reinterpret_cast<f32x4*>(prow + 8 * q4) = f32x4{s[4 * q4], s[4 * q4 + 1], s[4 * q4 + 2], s[4 * q4 + 3]};
+      if (oc2 == 0 && hi == 0) alpha_l[32 * hh + l32] = alpha;
+    }
+    __syncthreads();  // B3
+
+    // ---- 4. O^T += V^T P'^T over columns [128g, 128g + 128), heads 32hh.. ----
+    {
+      const float a = alpha_l[32 * hh + l32];
+      if (__any(a != 1.0f)) {
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) O[dt] *= a;
+      }
+    }
+    const int g16 = (lane >> 4) & 1;  // which 16 columns of the 32-column tile this lane group reads
+    const int jr = (lane & 15) >> 1;   // row of the 8-row transpose block this lane addresses
+    const int jb = lane & 1;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const f32x4 sa = *reinterpret_cast<const f32x4*>(sct + g * TC + 16 * ks + 8 * hi);
+      const f32x4 sb = *reinterpret_cast<const f32x4*>(sct + g * TC + 16 * ks + 8 * hi + 4);
+      const float* prow = pl + (32 * hh + l32) * PLS + 16 * ks + 8 * hi;
+      const f32x4 x0 = *reinterpret_cast<const f32x4*>(prow);
+      const f32x4 x1 = *reinterpret_cast<const f32x4*>(prow + 4);
+      const bf16x8 pb = __builtin_bit_cast(
+          bf16x8, make_uint4(pack_bf16(x0[0] * sa[0], x0[1] * sa[1]), pack_bf16(x0[2] * sa[2], x0[3] * sa[3]),
+                             pack_bf16(x1[0] * sb[0], x1[1] * sb[1]), pack_bf16(x1[2] * sb[2], x1[3] * sb[3])));
+      const uint8_t* vrow = raw + (16 * ks + 8 * hi + jr) * RS + 128 * g + 16 * g16 + 8 * jb;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const i32x2 v8 = lds_read_tr8(vrow + 32 * dt);
+        O[dt] = mfma_32x32x16(codes8_to_bf16x8<FMT>(make_uint2((uint32_t)v8[0], (uint32_t)v8[1])), pb, O[dt]);
+      }
+    }
+  }
+
+  // ---- epilogue: per-head max and sum, normalize, store ----
+  float* lsum = maxb;     // [2][64]
+  float* mfin = alpha_l;  // [64]
+  __syncthreads();
+  if (owner) {
+    const float lt = l_part + __shfl_xor(l_part, 32);
+    if (hi == 0) {
+      lsum[oc2 * 64 + 32 * hh + l32] = lt;
+      if (oc2 == 0) mfin[32 * hh + l32] = m_run;
+    }
+  }
+  __syncthreads();
+  const int hl = 32 * hh + l32;
+  const int h = h0 + hl;
+  const float Ls = lsum[hl] + lsum[64 + hl];
+  const float M = mfin[hl];
+  const bool empty = !(Ls > 0.0f);
+  const float lse_v = empty ? -INFINITY : (M + __log2f(Ls)) * LN2;
+  if (h >= p.H) return;
+  if constexpr (DECODE) {
+    const float inv = empty ? 0.0f : 1.0f / Ls;
+    float* po = p.part_out + ((t * p.num_splits + split) * p.H + h) * (int64_t)D_V + 128 * g + 4 * hi;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *reinterpret_cast<f32x4*>(po + 32 * dt + 8 * q4) =
+            f32x4{O[dt][4 * q4] * inv, O[dt][4 * q4 + 1] * inv, O[dt][4 * q4 + 2] * inv, O[dt][4 * q4 + 3] * inv};
+    if (g == 0 && hi == 0) p.part_lse[(t * p.num_splits + split) * p.H + h] = lse_v;
+  } else {
+    float factor;
+    if (empty) {
+      factor = 0.0f;
+    } else if (p.sink) {
+      const float s2 = p.sink[h] * LOG2E;
+      const float ms = fmaxf(M, s2);
+      const float a = exp2f(M - ms);
+      factor = a / (Ls * a + exp2f(s2 - ms));
+    } else {
+      factor = 1.0f / Ls;
+    }
+    uint16_t* orow = p.out + t * p.out_st + (int64_t)h * p.out_sh + 128 * g + 4 * hi;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * q4) =
+            make_uint2(pack_bf16(O[dt][4 * q4] * factor, O[dt][4 * q4 + 1] * factor),
+                       pack_bf16(O[dt][4 * q4 + 2] * factor, O[dt][4 * q4 + 3] * factor));
+    if (g == 0 && hi == 0) p.lse[t * p.lse_st + h] = lse_v;
+  }
+}
+
+hipError_t launch_attention_wide(const AttnParams& p, int fmt, bool decode, hipStream_t s) {
+  dim3 block(wide::NT);
+  dim3 grid((unsigned)p.T, (unsigned)((p.H + 63) / 64), decode ? (unsigned)p.num_splits : 1u);
+  if (fmt == FMT_FP8) {
+    if (decode) hipLaunchKernelGGL((attn_wide_kernel<FMT_FP8, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((attn_wide_kernel<FMT_FP8, false>), grid, block, 0, s, p);
+  } else if (fmt == FMT_INT8) {
+    if (decode) hipLaunchKernelGGL((attn_wide_kernel<FMT_INT8, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((attn_wide_kernel<FMT_INT8, false>), grid, block, 0, s, p);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace smla
