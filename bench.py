@@ -42,7 +42,9 @@ def parse():
     ap.add_argument("--width", type=int, default=1024, help="prefill index width (512 or 1024)")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=256)
+    ap.add_argument("--cpu-tokens", type=int, default=512)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="also run one plain device-to-device copy of MIB MiB (reference for HBM counters)")
     return ap.parse_args()
 
 
@@ -236,6 +238,16 @@ def main():
             "hbm_frac_end_to_end": round(dbytes / ((dec_us + comb_us) * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
         }
         print(f"[bench] decode {dec_us:.2f} us + combine {comb_us:.2f} us", file=sys.stderr, flush=True)
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes"] = n
+        del src, dst
 
     # ---------------- CPU baseline: the oracle on a bounded sample ----------------
     if not args.no_cpu:
