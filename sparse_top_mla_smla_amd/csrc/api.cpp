@@ -8,7 +8,7 @@
 #include <cstdio>
 #include <cstring>
 
-#include "../../include/smla.h"
+#include "smla.h"
 #include "launch.h"
 
 namespace {

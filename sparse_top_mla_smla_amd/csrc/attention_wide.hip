@@ -59,10 +59,9 @@ namespace wide {
 constexpr int NT = 512;                      // 8 waves, 2 per SIMD
 constexpr int TC = 64;                       // candidates per tile
 constexpr int RB = 656;                      // FP8/INT8 row bytes
-constexpr int RS = 672;                      // LDS row stride
-constexpr int CHUNKS = RB / 16;              // 41 used chunk slots per row
-constexpr int SLOTS = RS / 16;               // 42 chunk slots per LDS row
-constexpr int ROUNDS = (TC * SLOTS + NT - 1) / NT;  // 6 direct-load rounds per tile
+constexpr int RS = RB;                       // LDS row stride (41 x 16 B: 2-way worst-case
+                                             // bank conflicts on the 32-row operand reads)
+constexpr int CHUNKS = RB / 16;              // 41 chunks per row
 constexpr int OFF_RAW = 0;                   // [2][64][RS]
 constexpr int OFF_RECV = 2 * TC * RS;        // [4 score tiles][3 senders][64 lanes][16] f32
 constexpr int OFF_PL = OFF_RECV + 4 * 3 * 64 * 16 * 4;
@@ -70,8 +69,9 @@ constexpr int PLS = 68;                      // P row stride (floats): [64 heads
 constexpr int OFF_MAX = OFF_PL + 64 * PLS * 4;   // [2][64] f32
 constexpr int OFF_ALPHA = OFF_MAX + 2 * 64 * 4;  // [64] f32
 constexpr int OFF_SCT = OFF_ALPHA + 64 * 4;      // [4 groups][64 rows] f32
-constexpr int OFF_IDX = OFF_SCT + 4 * TC * 4;    // [4][64] int32
-constexpr int LDS_BYTES = OFF_IDX + 4 * TC * 4;
+constexpr int OFF_IDX = OFF_SCT + 4 * TC * 4;    // [4][64] int64 row byte offsets (-1: masked)
+constexpr int LDS_BYTES = OFF_IDX + 4 * TC * 8;
+constexpr int GROUNDS = (TC * CHUNKS + 255) / 256;  // 11 gather rounds for the 4 issuing waves
 constexpr float TAU = 8.0f;
 }  // namespace wide
 
@@ -89,7 +89,7 @@ __global__ __launch_bounds__(wide::NT, 1) void attn_wide_kernel(AttnParams p) {
   float* maxb = reinterpret_cast<float*>(smem + OFF_MAX);
   float* alpha_l = reinterpret_cast<float*>(smem + OFF_ALPHA);
   float* sct = reinterpret_cast<float*>(smem + OFF_SCT);
-  int32_t* idxl = reinterpret_cast<int32_t*>(smem + OFF_IDX);
+  int64_t* idxl = reinterpret_cast<int64_t*>(smem + OFF_IDX);
 
   const int tid = threadIdx.x;
   const int w = tid >> 6;
@@ -138,36 +138,37 @@ __global__ __launch_bounds__(wide::NT, 1) void attn_wide_kernel(AttnParams p) {
   }
 
   const int32_t* idx_row = p.idx + t * p.idx_st;
-  auto load_idx = [&](int k) -> int32_t {
+  // list entry k*64 + tid of this workgroup's range -> byte offset of its
+  // pool row, or -1 when the entry is masked or not a slot of the pool
+  auto load_idx = [&](int k) -> int64_t {
     const int64_t j = j_begin + (int64_t)k * TC + tid;
-    int32_t v = -1;
+    int64_t v = -1;
     if (j < j_end) {
       const int32_t x = idx_row[j];
-      if (x >= 0 && (int64_t)x < p.nslots) v = x;
+      if (x >= 0 && (int64_t)x < p.nslots) v = (int64_t)(x / PAGE) * p.block_stride + (int64_t)(x % PAGE) * RB;
     }
     return v;
   };
-  // gather tile k into raw buffer k&1: chunk slot q = (r*8 + w)*64 + lane,
-  // row q / 42, 16-byte chunk q % 42 (chunk 41 is row padding)
+  // gather tile k into raw buffer k&1, issued by the four non-owner waves
+  // (nw = w - 2): chunk q = (r*4 + nw)*64 + lane is row q / 41, 16-byte
+  // piece q % 41, and lands at LDS byte 16q
   auto issue_tile = [&](int k) {
-    const int32_t* il = idxl + (k & 3) * TC;
+    const int64_t* il = idxl + (k & 3) * TC;
     uint8_t* raw = smem + OFF_RAW + (k & 1) * TC * RS;
-    int q = w * 64 + lane;
-    int row = q / SLOTS, ck = q % SLOTS;
-#pragma unroll 1
-    for (int r = 0; r < ROUNDS; ++r) {
-      if (row < TC && ck < CHUNKS) {
-        const int32_t slot = il[row];
-        if (slot >= 0) {
-          const uint8_t* src = p.pool + (int64_t)(slot / PAGE) * p.block_stride + (int64_t)(slot % PAGE) * RB + 16 * ck;
-          global_to_lds_16(src, raw + 16 * (r * 8 + w) * 64);
-        }
+    const int nw = w - 2;
+    int q = nw * 64 + lane;
+    int row = q / CHUNKS, ck = q % CHUNKS;
+#pragma unroll 4
+    for (int r = 0; r < GROUNDS; ++r) {
+      if (row < TC) {
+        const int64_t off = il[row];
+        if (off >= 0) global_to_lds_16(p.pool + off + 16 * ck, raw + 16 * (r * 4 + nw) * 64);
       }
-      // advance q by 512 = 12 * 42 + 8
-      row += 12;
-      ck += 8;
-      if (ck >= SLOTS) {
-        ck -= SLOTS;
+      // advance q by 256 = 6 * 41 + 10
+      row += 6;
+      ck += 10;
+      if (ck >= CHUNKS) {
+        ck -= CHUNKS;
         row += 1;
       }
     }
@@ -190,15 +191,22 @@ __global__ __launch_bounds__(wide::NT, 1) void attn_wide_kernel(AttnParams p) {
       idxl[1 * TC + tid] = n_tiles > 1 ? load_idx(1) : -1;
     }
     __syncthreads();
-    issue_tile(0);
+    if (!owner) issue_tile(0);
   }
 
   for (int k = 0; k < n_tiles; ++k) {
     const uint8_t* raw = smem + OFF_RAW + (k & 1) * TC * RS;
     __builtin_amdgcn_s_waitcnt(0);  // this wave's part of tile k has landed
     __syncthreads();                // B0: all of tile k is in LDS
-    int32_t pend = -1;
+    int64_t pend = -1;
     if (k + 2 < n_tiles && tid < TC) pend = load_idx(k + 2);
+    if (!owner) {
+      // the four non-owner waves transpose the tile's scales:
+      // sct[gg][row] = scale of row `row`, 128-column group gg
+      const int e = (w - 2) * 64 + lane;  // waves 2..5 -> 0..255
+      const int row = e >> 2, gg = e & 3;
+      sct[gg * TC + row] = *reinterpret_cast<const float*>(raw + row * RS + D_NOPE + 4 * gg);
+    }
 
     // ---- 1./2. unscaled partial S^T over nope columns [128g, 128g+128)
     // for heads 32hh..; the tile (c2, hh) goes to its owner c2 + 6hh ----
@@ -235,31 +243,31 @@ __global__ __launch_bounds__(wide::NT, 1) void attn_wide_kernel(AttnParams p) {
     }
     __syncthreads();  // B1: partials visible; every wave is past PV(k-1)
 
-    if (k + 1 < n_tiles) issue_tile(k + 1);
+    if (!owner && k + 1 < n_tiles) issue_tile(k + 1);
     if (k + 2 < n_tiles && tid < TC) idxl[((k + 2) & 3) * TC + tid] = pend;
 
     if (owner) {
       // S = sum_g scale[c][g] * N_g + rope over the owned rows
-      // c = 32oc2 + 8q4 + 4hi + r, one 4-row block at a time
+      // c = 32oc2 + 8q4 + 4hi + r; scales come from the transposed table,
+      // four rows of one group per read
       const int tile_id = oc2 + 2 * hh;
       const f32x4* rsrc = reinterpret_cast<const f32x4*>(recv + (tile_id * 3 * 64 + lane) * 16);
+      const float* srow = sct + 32 * oc2 + 4 * hi;
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        f32x4 sc4[4];
+        const f32x4 so = *reinterpret_cast<const f32x4*>(srow + g * TC + 8 * q4);
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          sc4[r] = *reinterpret_cast<const f32x4*>(raw + (32 * oc2 + 8 * q4 + 4 * hi + r) * RS + D_NOPE);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) s[4 * q4 + r] += sc4[r][g] * own[4 * q4 + r];
+        for (int r = 0; r < 4; ++r) s[4 * q4 + r] += so[r] * own[4 * q4 + r];
 #pragma unroll
         for (int slot = 0; slot < 3; ++slot) {
           const int gs = slot < g ? slot : slot + 1;
+          const f32x4 sc = *reinterpret_cast<const f32x4*>(srow + gs * TC + 8 * q4);
           const f32x4 v = rsrc[slot * 64 * 4 + q4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) s[4 * q4 + r] += sc4[r][gs] * v[r];
+          for (int r = 0; r < 4; ++r) s[4 * q4 + r] += sc[r] * v[r];
         }
       }
-      const int32_t* il = idxl + (k & 3) * TC + 32 * oc2 + 4 * hi;
+      const int64_t* il = idxl + (k & 3) * TC + 32 * oc2 + 4 * hi;
       float mx = -INFINITY;
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
@@ -272,23 +280,17 @@ __global__ __launch_bounds__(wide::NT, 1) void attn_wide_kernel(AttnParams p) {
       }
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       if (hi == 0) maxb[oc2 * 64 + 32 * hh + l32] = mx;
-    } else {
-      // the four other waves transpose the tile's scales for PV:
-      // sct[gg][row] = scale of row `row`, 128-column group gg
-      const int e = (w - 2) * 64 + lane;  // waves 2..5 -> 0..255
-      const int row = e >> 2, gg = e & 3;
-      sct[gg * TC + row] = *reinterpret_cast<const float*>(raw + row * RS + D_NOPE + 4 * gg);
     }
     __syncthreads();  // B2
     if (owner) {
       const float mx = fmaxf(maxb[32 * hh + l32], maxb[64 + 32 * hh + l32]);
       const bool need = mx > m_run + TAU;
-      const float alpha = need ? ((m_run == -INFINITY) ? 0.0f : exp2f(m_run - mx)) : 1.0f;
+      const float alpha = need ? ((m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run - mx)) : 1.0f;
       m_run = need ? mx : m_run;
       float psum = 0.0f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        s[i] = (s[i] == -INFINITY) ? 0.0f : exp2f(s[i] - m_run);
+        s[i] = (s[i] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(s[i] - m_run);
         psum += s[i];
       }
       l_part = l_part * alpha + psum;
