@@ -27,12 +27,16 @@
 //     O^T for columns [128g, 128g+128) of its 32 heads.  V^T comes from the raw FP8/INT8
 //     codes with ds_read_b64_tr_b8 and is converted to BF16 exactly; the
 //     row scale of column group w is folded into P.
-// The raw tiles are double-buffered in LDS and filled straight from global
-// memory with global_load_lds_dwordx4 (lane l of a wave lands at base+16l;
-// no staging registers), one tile ahead; the index lists run two tiles
-// ahead.  Rows that are never loaded (masked entries) keep finite stale
-// data from earlier valid rows or the initial zero fill, and contribute
-// nothing because their probabilities are exactly 0.
+// The raw tiles are double-buffered in LDS, chunk-major: 16-byte piece ck
+// (0..40) of tile row r (0..63) sits at byte ck*1024 + r*16.  The four
+// non-owner waves fill the next tile straight from global memory with
+// global_load_lds_dwordx4: one instruction moves piece ck of all 64 rows
+// (lane = row, landing at base + 16*lane), so a lane needs only its own
+// row's address.  The same layout makes the 32-row operand reads of QK and
+// the transposed V reads contiguous in LDS.  Rows that are never loaded
+// (masked entries) keep finite stale data from earlier rows or the initial
+// zero fill, and contribute nothing because their probabilities are
+// exactly 0.
 #include "device_common.h"
 #include "launch.h"
 
@@ -45,8 +49,8 @@ __device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
 }
 
 template <int FMT>
-__device__ __forceinline__ bf16x8 codes8_to_bf16x8(uint2 c8) {
-  const uint2 lo = codes4_to_bf16x4<FMT>(c8.x), hi = codes4_to_bf16x4<FMT>(c8.y);
+__device__ __forceinline__ bf16x8 codes8_to_bf16x8(uint32_t c0, uint32_t c1) {
+  const uint2 lo = codes4_to_bf16x4<FMT>(c0), hi = codes4_to_bf16x4<FMT>(c1);
   return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
 }
 
@@ -59,26 +63,28 @@ namespace wide {
 constexpr int NT = 512;                      // 8 waves, 2 per SIMD
 constexpr int TC = 64;                       // candidates per tile
 constexpr int RB = 656;                      // FP8/INT8 row bytes
-constexpr int RS = RB;                       // LDS row stride (41 x 16 B: 2-way worst-case
-                                             // bank conflicts on the 32-row operand reads)
-constexpr int CHUNKS = RB / 16;              // 41 chunks per row
-constexpr int OFF_RAW = 0;                   // [2][64][RS]
-constexpr int OFF_RECV = 2 * TC * RS;        // [4 score tiles][3 senders][64 lanes][16] f32
+constexpr int CHUNKS = RB / 16;              // 41 pieces of 16 bytes per row
+constexpr int CS = TC * 16;                  // bytes of one piece column (64 rows)
+constexpr int TILE = CHUNKS * CS;            // 41,984 bytes per tile
+constexpr int CK_SCALE = D_NOPE / 16;        // piece 32 holds the four scales
+constexpr int CK_ROPE = CK_SCALE + 1;        // pieces 33..40 hold the rope
+constexpr int GROUNDS = (CHUNKS + 3) / 4;    // pieces per gather wave (11, last one partial)
+constexpr int OFF_RAW = 0;                   // [2][TILE]
+constexpr int OFF_RECV = 2 * TILE;           // [4 score tiles][3 senders][64 lanes][16] f32
 constexpr int OFF_PL = OFF_RECV + 4 * 3 * 64 * 16 * 4;
 constexpr int PLS = 68;                      // P row stride (floats): [64 heads][PLS]
 constexpr int OFF_MAX = OFF_PL + 64 * PLS * 4;   // [2][64] f32
 constexpr int OFF_ALPHA = OFF_MAX + 2 * 64 * 4;  // [64] f32
 constexpr int OFF_SCT = OFF_ALPHA + 64 * 4;      // [4 groups][64 rows] f32
-constexpr int OFF_IDX = OFF_SCT + 4 * TC * 4;    // [4][64] int64 row byte offsets (-1: masked)
-constexpr int LDS_BYTES = OFF_IDX + 4 * TC * 8;
-constexpr int GROUNDS = (TC * CHUNKS + 255) / 256;  // 11 gather rounds for the 4 issuing waves
+constexpr int OFF_VALID = OFF_SCT + 4 * TC * 4;  // [2][64] int32: row was loaded
+constexpr int LDS_BYTES = OFF_VALID + 2 * TC * 4;
 constexpr float TAU = 8.0f;
 }  // namespace wide
 
 // Wave w = g + 4*hh works on latent group g (nope columns [128g, 128g+128),
 // output columns likewise) for head half hh (heads [32hh, 32hh+32)).  Score
 // tile (c2, hh) -- candidates [32c2, +32) x heads [32hh, +32) -- is owned by
-// wave c2 + 6hh (waves 0, 1, 6, 7: one owner per SIMD).
+// wave c2 + 6hh (waves 0, 1, 6, 7: one owner per SIMD); waves 2..5 gather.
 template <int FMT, bool DECODE>
 __global__ __launch_bounds__(wide::NT, 1) void attn_wide_kernel(AttnParams p) {
   using namespace wide;
@@ -89,16 +95,17 @@ __global__ __launch_bounds__(wide::NT, 1) void attn_wide_kernel(AttnParams p) {
   float* maxb = reinterpret_cast<float*>(smem + OFF_MAX);
   float* alpha_l = reinterpret_cast<float*>(smem + OFF_ALPHA);
   float* sct = reinterpret_cast<float*>(smem + OFF_SCT);
-  int64_t* idxl = reinterpret_cast<int64_t*>(smem + OFF_IDX);
+  int32_t* valid = reinterpret_cast<int32_t*>(smem + OFF_VALID);
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in SGPRs
   const int g = w & 3, hh = w >> 2;
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
   const bool owner = (w == 0 || w == 1 || w == 6 || w == 7);
   const int oc2 = owner ? (w & 1) : 0;  // candidate half of the owned score tile
+  const int nw = w - 2;                 // gather wave 0..3 (waves 2..5)
 
   const int64_t t = blockIdx.x;
   const int h0 = blockIdx.y * 64;
@@ -118,18 +125,22 @@ __global__ __launch_bounds__(wide::NT, 1) void attn_wide_kernel(AttnParams p) {
   if (j_end > L) j_end = L;
   const int n_tiles = j_end > j_begin ? (int)((j_end - j_begin + TC - 1) / TC) : 0;
 
-  // Q as the B operand of S^T = K Q^T for head h0 + 32hh + l32: qn holds nope
-  // columns 128g + 16ks + 8hi + i, qr rope columns 16ks + 8hi + i (owners).
+  // Q as the B operand of S^T = K Q^T for head h0 + 32hh + l32.  A K lane
+  // reads one 16-byte piece (8g + 2j + hi) that feeds MFMA steps 2j and
+  // 2j+1, so qn[2j + b] holds nope columns 128g + 32j + 16hi + 8b + i; qr
+  // holds rope columns 16ks + 8hi + i (owners).
   bf16x8 qn[8], qr[4];
   {
     const int h = h0 + 32 * hh + l32;
     const bool hv = h < p.H;
     const uint16_t* qrow = p.q + t * p.q_st + (int64_t)(hv ? h : 0) * p.q_sh;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      uint4 v = *reinterpret_cast<const uint4*>(qrow + 128 * g + 16 * ks + 8 * hi);
-      qn[ks] = __builtin_bit_cast(bf16x8, hv ? v : make_uint4(0, 0, 0, 0));
-    }
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        uint4 v = *reinterpret_cast<const uint4*>(qrow + 128 * g + 32 * j + 16 * hi + 8 * b);
+        qn[2 * j + b] = __builtin_bit_cast(bf16x8, hv ? v : make_uint4(0, 0, 0, 0));
+      }
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       uint4 v = *reinterpret_cast<const uint4*>(qrow + D_NOPE + 16 * ks + 8 * hi);
@@ -138,10 +149,10 @@ __global__ __launch_bounds__(wide::NT, 1) void attn_wide_kernel(AttnParams p) {
   }
 
   const int32_t* idx_row = p.idx + t * p.idx_st;
-  // list entry k*64 + tid of this workgroup's range -> byte offset of its
-  // pool row, or -1 when the entry is masked or not a slot of the pool
-  auto load_idx = [&](int k) -> int64_t {
-    const int64_t j = j_begin + (int64_t)k * TC + tid;
+  // byte offset in the pool of the row of list entry k*64 + lane of this
+  // workgroup's range, or -1 when the entry is masked or not a pool slot
+  auto row_offset = [&](int k) -> int64_t {
+    const int64_t j = j_begin + (int64_t)k * TC + lane;
     int64_t v = -1;
     if (j < j_end) {
       const int32_t x = idx_row[j];
@@ -149,29 +160,19 @@ __global__ __launch_bounds__(wide::NT, 1) void attn_wide_kernel(AttnParams p) {
     }
     return v;
   };
-  // gather tile k into raw buffer k&1, issued by the four non-owner waves
-  // (nw = w - 2): chunk q = (r*4 + nw)*64 + lane is row q / 41, 16-byte
-  // piece q % 41, and lands at LDS byte 16q
-  auto issue_tile = [&](int k) {
-    const int64_t* il = idxl + (k & 3) * TC;
-    uint8_t* raw = smem + OFF_RAW + (k & 1) * TC * RS;
-    const int nw = w - 2;
-    int q = nw * 64 + lane;
-    int row = q / CHUNKS, ck = q % CHUNKS;
-#pragma unroll 4
-    for (int r = 0; r < GROUNDS; ++r) {
-      if (row < TC) {
-        const int64_t off = il[row];
-        if (off >= 0) global_to_lds_16(p.pool + off + 16 * ck, raw + 16 * (r * 4 + nw) * 64);
-      }
-      // advance q by 256 = 6 * 41 + 10
-      row += 6;
-      ck += 10;
-      if (ck >= CHUNKS) {
-        ck -= CHUNKS;
-        row += 1;
+  // gather wave nw moves pieces nw, nw + 4, ... of all 64 rows of tile k
+  // (lane = row) into raw buffer k&1, and wave 2 records which rows exist
+  auto issue_tile = [&](int k, int64_t off) {
+    uint8_t* raw = smem + OFF_RAW + (k & 1) * TILE;
+    if (off >= 0) {
+      const uint8_t* src = p.pool + off;
+#pragma unroll
+      for (int r = 0; r < GROUNDS; ++r) {
+        const int ck = nw + 4 * r;
+        if (r + 1 < GROUNDS || ck < CHUNKS) global_to_lds_16(src + 16 * ck, raw + ck * CS);
       }
     }
+    if (nw == 0) valid[(k & 1) * TC + lane] = off >= 0;
   };
 
   // running softmax state of an owned score tile (heads 32hh + l32)
@@ -185,27 +186,24 @@ __global__ __launch_bounds__(wide::NT, 1) void attn_wide_kernel(AttnParams p) {
     for (int i = 0; i < 16; ++i) O[dt][i] = 0.0f;
 
   if (n_tiles > 0) {
-    for (int i = tid; i < 2 * TC * RS / 16; i += NT) reinterpret_cast<uint4*>(smem + OFF_RAW)[i] = make_uint4(0, 0, 0, 0);
-    if (tid < TC) {
-      idxl[0 * TC + tid] = load_idx(0);
-      idxl[1 * TC + tid] = n_tiles > 1 ? load_idx(1) : -1;
-    }
+    for (int i = tid; i < 2 * TILE / 16; i += NT) reinterpret_cast<uint4*>(smem + OFF_RAW)[i] = make_uint4(0, 0, 0, 0);
+    const int64_t off0 = owner ? -1 : row_offset(0);
     __syncthreads();
-    if (!owner) issue_tile(0);
+    if (!owner) issue_tile(0, off0);
   }
 
   for (int k = 0; k < n_tiles; ++k) {
-    const uint8_t* raw = smem + OFF_RAW + (k & 1) * TC * RS;
+    const uint8_t* raw = smem + OFF_RAW + (k & 1) * TILE;
     __builtin_amdgcn_s_waitcnt(0);  // this wave's part of tile k has landed
     __syncthreads();                // B0: all of tile k is in LDS
     int64_t pend = -1;
-    if (k + 2 < n_tiles && tid < TC) pend = load_idx(k + 2);
     if (!owner) {
-      // the four non-owner waves transpose the tile's scales:
+      if (k + 1 < n_tiles) pend = row_offset(k + 1);
+      // the gather waves transpose the tile's scales:
       // sct[gg][row] = scale of row `row`, 128-column group gg
-      const int e = (w - 2) * 64 + lane;  // waves 2..5 -> 0..255
+      const int e = nw * 64 + lane;
       const int row = e >> 2, gg = e & 3;
-      sct[gg * TC + row] = *reinterpret_cast<const float*>(raw + row * RS + D_NOPE + 4 * gg);
+      sct[gg * TC + row] = *reinterpret_cast<const float*>(raw + CK_SCALE * CS + row * 16 + 4 * gg);
     }
 
     // ---- 1./2. unscaled partial S^T over nope columns [128g, 128g+128)
@@ -216,10 +214,13 @@ __global__ __launch_bounds__(wide::NT, 1) void attn_wide_kernel(AttnParams p) {
       f32x16 acc;
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
-      const uint8_t* rowA = raw + (32 * c2 + l32) * RS + 128 * g + 8 * hi;
+      const uint8_t* kp = raw + (8 * g + hi) * CS + (32 * c2 + l32) * 16;
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
-        acc = mfma_32x32x16(codes8_to_bf16x8<FMT>(*reinterpret_cast<const uint2*>(rowA + 16 * ks)), qn[ks], acc);
+      for (int j = 0; j < 4; ++j) {
+        const uint4 c16 = *reinterpret_cast<const uint4*>(kp + 2 * j * CS);
+        acc = mfma_32x32x16(codes8_to_bf16x8<FMT>(c16.x, c16.y), qn[2 * j], acc);
+        acc = mfma_32x32x16(codes8_to_bf16x8<FMT>(c16.z, c16.w), qn[2 * j + 1], acc);
+      }
       const int ow = c2 + 6 * hh;
       if (ow == w) {
         own = acc;
@@ -236,15 +237,14 @@ __global__ __launch_bounds__(wide::NT, 1) void attn_wide_kernel(AttnParams p) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) s[i] = 0.0f;
     if (owner) {
-      const uint8_t* rowR = raw + (32 * oc2 + l32) * RS + D_NOPE + 16 + 16 * hi;
+      const uint8_t* rp = raw + (CK_ROPE + hi) * CS + (32 * oc2 + l32) * 16;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
-        s = mfma_32x32x16(__builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(rowR + 32 * ks)), qr[ks], s);
+        s = mfma_32x32x16(__builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(rp + 2 * ks * CS)), qr[ks], s);
     }
     __syncthreads();  // B1: partials visible; every wave is past PV(k-1)
 
-    if (!owner && k + 1 < n_tiles) issue_tile(k + 1);
-    if (k + 2 < n_tiles && tid < TC) idxl[((k + 2) & 3) * TC + tid] = pend;
+    if (!owner && k + 1 < n_tiles) issue_tile(k + 1, pend);
 
     if (owner) {
       // S = sum_g scale[c][g] * N_g + rope over the owned rows
@@ -267,14 +267,14 @@ __global__ __launch_bounds__(wide::NT, 1) void attn_wide_kernel(AttnParams p) {
           for (int r = 0; r < 4; ++r) s[4 * q4 + r] += sc[r] * v[r];
         }
       }
-      const int64_t* il = idxl + (k & 3) * TC + 32 * oc2 + 4 * hi;
+      const int32_t* vl = valid + (k & 1) * TC + 32 * oc2 + 4 * hi;
       float mx = -INFINITY;
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int i = 4 * q4 + r;
-          s[i] = il[8 * q4 + r] >= 0 ? s[i] * p.scale_log2 : -INFINITY;
+          s[i] = vl[8 * q4 + r] ? s[i] * p.scale_log2 : -INFINITY;
           mx = fmaxf(mx, s[i]);
         }
       }
@@ -310,9 +310,12 @@ __global__ __launch_bounds__(wide::NT, 1) void attn_wide_kernel(AttnParams p) {
         for (int dt = 0; dt < 4; ++dt) O[dt] *= a;
       }
     }
+    // ds_read_b64_tr_b8: in each 16-lane group, lane 2r + b addresses row r
+    // of an 8-row block, bytes 8b..8b+7 of a 16-column piece
     const int g16 = (lane >> 4) & 1;  // which 16 columns of the 32-column tile this lane group reads
-    const int jr = (lane & 15) >> 1;   // row of the 8-row transpose block this lane addresses
+    const int jr = (lane & 15) >> 1;
     const int jb = lane & 1;
+    const uint8_t* vbase = raw + (8 * g + g16) * CS + (8 * hi + jr) * 16 + 8 * jb;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const f32x4 sa = *reinterpret_cast<const f32x4*>(sct + g * TC + 16 * ks + 8 * hi);
@@ -323,11 +326,10 @@ __global__ __launch_bounds__(wide::NT, 1) void attn_wide_kernel(AttnParams p) {
       const bf16x8 pb = __builtin_bit_cast(
           bf16x8, make_uint4(pack_bf16(x0[0] * sa[0], x0[1] * sa[1]), pack_bf16(x0[2] * sa[2], x0[3] * sa[3]),
                              pack_bf16(x1[0] * sb[0], x1[1] * sb[1]), pack_bf16(x1[2] * sb[2], x1[3] * sb[3])));
-      const uint8_t* vrow = raw + (16 * ks + 8 * hi + jr) * RS + 128 * g + 16 * g16 + 8 * jb;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-        const i32x2 v8 = lds_read_tr8(vrow + 32 * dt);
-        O[dt] = mfma_32x32x16(codes8_to_bf16x8<FMT>(make_uint2((uint32_t)v8[0], (uint32_t)v8[1])), pb, O[dt]);
+        const i32x2 v8 = lds_read_tr8(vbase + 2 * dt * CS + 16 * ks * 16);
+        O[dt] = mfma_32x32x16(codes8_to_bf16x8<FMT>((uint32_t)v8[0], (uint32_t)v8[1]), pb, O[dt]);
       }
     }
   }
