@@ -63,7 +63,11 @@ typedef enum {
 /* Latent-cache row formats.  Row layout (FlashInfer PR #4802 review of the
  * DSv3.2 decode kernel): FP8 row = 656 bytes: [0,512) e4m3 codes of the 512
  * nope values, [512,528) four FP32 scales (one per 128-element tile),
- * [528,656) 64 BF16 rope values.  INT8 uses the same layout with int8 codes.
+ * [528,656) 64 BF16 rope values.  DSv3.2 stores power-of-two scales, and
+ * the attention entry points require FP8 scales of loaded rows to be
+ * positive normal powers of two (smla_quantize_kv writes only those); with
+ * H > 16 a loaded row with any other scale makes its token's output NaN.
+ * INT8 uses the same layout with int8 codes and any positive FP32 scale.
  * BF16 row = 576 BF16 values (1152 bytes). */
 typedef enum {
   SMLA_KV_BF16 = 0,

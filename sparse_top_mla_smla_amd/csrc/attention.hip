@@ -365,7 +365,8 @@ static hipError_t launch_fmt(const AttnParams& p, bool decode, hipStream_t s) {
 
 hipError_t launch_attention(const AttnParams& p, int fmt, bool decode, hipStream_t s) {
   // many heads over a quantized cache: one workgroup per token for 64 heads
-  if (fmt != FMT_BF16 && p.H > 16) return launch_attention_wide(p, fmt, decode, s);
+  if (fmt == FMT_FP8 && p.H > 16) return launch_attention_fp8(p, decode, s);
+  if (fmt == FMT_INT8 && p.H > 16) return launch_attention_wide(p, fmt, decode, s);
   switch (fmt) {
     case FMT_BF16: return launch_fmt<FMT_BF16>(p, decode, s);
     case FMT_FP8: return launch_fmt<FMT_FP8>(p, decode, s);

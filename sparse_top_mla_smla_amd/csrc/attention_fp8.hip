@@ -1,0 +1,498 @@
+// attention_fp8.hip -- sparse MLA attention for many heads (H > 16) over the
+// FP8 paged latent cache (656-byte rows with power-of-two per-128 scales),
+// prefill form and split-KV decode partials.
+//
+// What is computed is stated in include/smla.h.  This kernel serves the
+// shapes of the AppMana release note's fused prefill (T=1024, ctx 16384,
+// H=64, widths 512/1024) and the decode batch: one workgroup owns one token
+// (and split) for 64 heads, so each selected row is gathered from the pool
+// once per token.
+//
+// DSv3.2 rows (FlashInfer #4802, KV layout of the decode kernel review) hold
+// power-of-two FP32 scales.  Then code * scale is exact in BF16, and gfx950
+// converts two e4m3 codes to BF16 with a power-of-two scale in a single
+// v_cvt_scalef32_pk_bf16_fp8.  K is therefore dequantized exactly while it
+// is converted, and the nope and rope parts of a score accumulate in one
+// MFMA accumulator.  A valid row whose scale is not a positive power of two
+// turns its token's output into NaN instead of a silently wrong result.
+//
+// All products use v_mfma_f32_32x32x16_bf16.  Eight waves; wave w = g + 4hh
+// works on latent group g (0..3) and head half hh (heads [32hh, 32hh+32)).
+// Per 64-candidate tile:
+//  1. QK^T, split over the latent dimension: wave (g, hh) forms the partial
+//     S^T of all 64 candidates x its 32 heads over nope columns
+//     [128g, 128g+128) and rope columns [16g, 16g+16), with its slice of Q
+//     in registers for the whole token.
+//  2. Reduce-scatter through LDS: wave (g, hh) owns candidates
+//     [16g, 16g+16) of its heads and receives the three other groups'
+//     partials for them.
+//  3. Online softmax on the owned 16 x 32 block in the exp2 domain.  The
+//     four waves of a head half exchange their block maxima, so they all
+//     hold the same running max per head; it moves lazily (only when
+//     exceeded by 2^8), so O is rarely rescaled.  P goes to LDS in FP32.
+//  4. PV, split over output columns: wave (g, hh) accumulates O^T for
+//     columns [128g, 128g+128) of its heads.  V^T is read from the raw codes
+//     with ds_read_b64_tr_b8 and converted with scale 1; the row scale of
+//     column group g (a per-candidate factor) is folded into P.
+// Raw tiles are double-buffered in LDS, chunk-major: 16-byte piece ck
+// (0..40) of tile row r (0..63) sits at byte ck*1024 + r*16.  All eight
+// waves gather the next tile straight from global memory with
+// global_load_lds_dwordx4, one instruction per piece for all 64 rows
+// (lane = row, landing at base + 16*lane), issued as soon as the tile
+// before it is consumed; the index list runs one tile further ahead.  Rows
+// that are never loaded (masked entries) keep stale rows of the same
+// buffer or the initial zero fill and contribute nothing, because their
+// probabilities are exactly 0 (this needs the pool's codes and rope values
+// to be finite, as the cache writer produces them).
+#include "device_common.h"
+#include "launch.h"
+
+namespace smla {
+
+namespace f8 {
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// eight e4m3 codes (bytes of c0 then c1, in order) times a power-of-two scale
+__device__ __forceinline__ bf16x8 cvt8(uint32_t c0, uint32_t c1, float scale) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c0, scale, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c0, scale, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c1, scale, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c1, scale, true);
+  return __builtin_bit_cast(bf16x8, make_uint4(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+                                               __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d)));
+}
+
+__device__ __forceinline__ void global_to_lds_16(const void* src, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                   (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
+
+__device__ __forceinline__ void global_to_lds_4(const void* src, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                   (__attribute__((address_space(3))) void*)lds_wave_base, 4, 0, 0);
+}
+
+// Workgroup barrier for LDS traffic only: this wave's LDS reads and writes
+// are complete, and no LDS access moves across it.  Unlike __syncthreads it
+// does not wait for outstanding global loads, so the direct-to-LDS gather
+// of the next tile stays in flight (that buffer is not touched until the
+// full barrier at the top of the next tile).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// 32-bit LDS address of a pointer into __shared__ memory
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// ds_read_b64_tr_b8 issued through asm.  The builtin's memory operand has
+// no alias information, so the compiler would make it wait for every
+// outstanding direct-to-LDS gather; here the caller waits explicitly
+// (lgkm_wait) before the results are used.  LDS operations complete in
+// order, so the compiler's own lgkmcnt waits stay correct around these.
+template <int OFF>
+__device__ __forceinline__ i32x2 tr8_issue(uint32_t addr) {
+  i32x2 r;
+  asm volatile("ds_read_b64_tr_b8 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+// ds_write_b64 through asm, for the same reason; the LDS barrier that
+// follows waits for its completion
+template <int OFF>
+__device__ __forceinline__ void b64_store(uint32_t addr, u32x2 v) {
+  asm volatile("ds_write_b64 %0, %1 offset:%2" : : "v"(addr), "v"(v), "i"(OFF));
+}
+template <int OFF>
+__device__ __forceinline__ u32x4 b128_issue(uint32_t addr) {
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+
+// a positive, finite, normal power of two
+__device__ __forceinline__ bool is_pow2_scale(float s) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, s);
+  const uint32_t e = b >> 23;
+  return (b & 0x007FFFFFu) == 0 && e != 0 && e < 255;
+}
+
+constexpr int NT = 512;                      // 8 waves, 2 per SIMD
+constexpr int TC = 64;                       // candidates per tile
+constexpr int RB = 656;                      // row bytes
+constexpr int CHUNKS = RB / 16;              // 41 pieces of 16 bytes per row
+constexpr int CS = TC * 16;                  // bytes of one piece column (64 rows)
+constexpr int TILE = CHUNKS * CS;            // 41,984 bytes per tile
+constexpr int CK_SCALE = D_NOPE / 16;        // piece 32 holds the four scales
+constexpr int CK_ROPE = CK_SCALE + 1;        // pieces 33..40 hold the rope
+constexpr int GROUNDS = (CHUNKS + 7) / 8;    // pieces per wave (6, the last for wave 0 only)
+constexpr int GPARTS = 3;                    // the pieces are issued in three parts per tile
+constexpr int RECV_FLOATS = 8 * 3 * 2 * 64 * 4;  // [8 owners][3 senders][2][64 lanes][4] f32
+constexpr int PS = 72;                       // P' row stride (bf16): [4 groups][64 heads][PS], aliases recv
+static_assert(4 * 64 * PS * 2 <= RECV_FLOATS * 4, "P' must fit in the partial-exchange buffer");
+constexpr float TAU = 8.0f;
+
+template <int V>
+struct Buf {
+  static constexpr int value = V;
+};
+}  // namespace f8
+
+template <bool DECODE>
+__global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
+  using namespace f8;
+  // Separate LDS objects, and a loop unrolled by two so that every access
+  // names its raw buffer at compile time: the compiler then sees that reads
+  // of one buffer (and of the other arrays) do not alias the direct-to-LDS
+  // gather into the other buffer, and does not wait for that gather.
+  __shared__ __attribute__((aligned(16))) uint8_t raw0[TILE];
+  __shared__ __attribute__((aligned(16))) uint8_t raw1[TILE];
+  __shared__ __attribute__((aligned(16))) float recv[RECV_FLOATS];
+  __shared__ __attribute__((aligned(16))) float maxb[4 * 64];   // [4 groups][64 heads]
+  __shared__ __attribute__((aligned(16))) int32_t valid[2 * TC];  // [buffer][row]: row was loaded
+  __shared__ __attribute__((aligned(16))) int32_t idx0[TC];       // index list of even tiles
+  __shared__ __attribute__((aligned(16))) int32_t idx1[TC];       // index list of odd tiles
+  uint16_t* pq = reinterpret_cast<uint16_t*>(recv);              // P' (bf16), after the reduce
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in SGPRs
+  const int g = w & 3, hh = w >> 2;
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  const int64_t t = blockIdx.x;
+  const int h0 = blockIdx.y * 64;
+  const int split = DECODE ? (int)blockIdx.z : 0;
+
+  int64_t L = p.topk;
+  if (p.topk_length) {
+    const int64_t v = p.topk_length[t];
+    L = v < 0 ? 0 : (v > p.topk ? p.topk : v);
+  }
+  int64_t j_begin = 0, j_end = p.topk;
+  if (DECODE) {
+    j_begin = (int64_t)split * p.split_w;
+    j_end = j_begin + p.split_w;
+    if (j_end > p.topk) j_end = p.topk;
+  }
+  if (j_end > L) j_end = L;
+  const int n_tiles = j_end > j_begin ? (int)((j_end - j_begin + TC - 1) / TC) : 0;
+
+  // Q as the B operand of S^T = K Q^T for head h0 + 32hh + l32.  A K lane
+  // reads one 16-byte piece (8g + 2j + hi) that feeds MFMA steps 2j and
+  // 2j+1, so qn[2j + b] holds nope columns 128g + 32j + 16hi + 8b + i; qr
+  // holds rope columns 16g + 8hi + i.
+  bf16x8 qn[8], qr;
+  {
+    const int h = h0 + 32 * hh + l32;
+    const bool hv = h < p.H;
+    const uint16_t* qrow = p.q + t * p.q_st + (int64_t)(hv ? h : 0) * p.q_sh;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        uint4 v = *reinterpret_cast<const uint4*>(qrow + 128 * g + 32 * j + 16 * hi + 8 * b);
+        qn[2 * j + b] = __builtin_bit_cast(bf16x8, hv ? v : make_uint4(0, 0, 0, 0));
+      }
+    uint4 v = *reinterpret_cast<const uint4*>(qrow + D_NOPE + 16 * g + 8 * hi);
+    qr = __builtin_bit_cast(bf16x8, hv ? v : make_uint4(0, 0, 0, 0));
+  }
+
+  // list entry k*64 + lane of this workgroup's range: its index value, and
+  // the byte offset in the pool of its row (-1: masked or not a pool slot)
+  const int32_t* idx_row = p.idx + t * p.idx_st;
+  auto load_entry = [&](int k) -> int32_t {
+    const int64_t j = j_begin + (int64_t)k * TC + lane;
+    return j < j_end ? idx_row[j] : -1;
+  };
+  auto row_offset = [&](int32_t x) -> int64_t {
+    return (x >= 0 && (int64_t)x < p.nslots) ? (int64_t)(x / PAGE) * p.block_stride + (int64_t)(x % PAGE) * RB
+                                             : (int64_t)-1;
+  };
+  // wave 0 moves the index list entries of tile k into index buffer B
+  // (entries past the range are not loaded; readers check the range)
+  auto issue_idx = [&](auto buf, int k) {
+    constexpr int B = decltype(buf)::value;
+    const int64_t j = j_begin + (int64_t)k * TC + lane;
+    if (j < j_end) global_to_lds_4(idx_row + j, B ? idx1 : idx0);
+  };
+  // wave w moves pieces w, w + 8, ... of all 64 rows of a tile (lane = row)
+  // into raw buffer B, in part P (0..2) the pieces of rounds 2P and 2P + 1.
+  // Spreading the issue over the tile keeps the address unit's queue short,
+  // so no wave stalls long at issue.  Wave 0 records which rows exist.
+  auto issue_part = [&](auto buf, auto part, int64_t off) {
+    constexpr int B = decltype(buf)::value;
+    constexpr int P = decltype(part)::value;
+    uint8_t* raw = B ? raw1 : raw0;
+    if (off >= 0) {
+      const uint8_t* src = p.pool + off;
+#pragma unroll
+      for (int r = 2 * P; r < 2 * P + 2; ++r) {
+        const int ck = w + 8 * r;
+        if (r + 1 < GROUNDS || ck < CHUNKS) global_to_lds_16(src + 16 * ck, raw + ck * CS);
+      }
+    }
+    if (P == 0 && w == 0) valid[B * TC + lane] = off >= 0;
+  };
+  static_assert(2 * GPARTS == GROUNDS, "three parts of two rounds");
+
+  // softmax state for heads 32hh + l32 (identical in the four waves of hh)
+  float m_run = -INFINITY;
+  float l_part = 0.0f;  // this wave's share: candidates 16g.. of every tile
+  // O^T accumulators: columns [128g + 32dt, +32) x heads [32hh, +32)
+  f32x16 O[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) O[dt][i] = 0.0f;
+
+  if (n_tiles > 0) {
+    for (int i = tid; i < TILE / 16; i += NT) {
+      reinterpret_cast<uint4*>(raw0)[i] = make_uint4(0, 0, 0, 0);
+      reinterpret_cast<uint4*>(raw1)[i] = make_uint4(0, 0, 0, 0);
+    }
+    const int64_t off0 = row_offset(load_entry(0));
+    __syncthreads();
+    issue_part(Buf<0>{}, Buf<0>{}, off0);
+    issue_part(Buf<0>{}, Buf<1>{}, off0);
+    issue_part(Buf<0>{}, Buf<2>{}, off0);
+    if (w == 0 && n_tiles > 1) issue_idx(Buf<1>{}, 1);
+  }
+
+  // one tile; tile k sits in raw buffer B = k & 1
+  auto step = [&](auto buf, int k) {
+    constexpr int B = decltype(buf)::value;
+    const uint8_t* raw = B ? raw1 : raw0;
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's part of tile k has landed
+    __syncthreads();                // B0: all of tile k is in LDS; tile k-1 is consumed
+    // gather of the next tile (its index list arrived before B0), then the
+    // index list one tile further ahead, read after the next B0
+    const bool more = k + 1 < n_tiles;
+    int64_t off_next = -1;
+    if (more) {
+      const int64_t j = j_begin + (int64_t)(k + 1) * TC + lane;
+      const int32_t x = j < j_end ? (B ? idx0 : idx1)[lane] : -1;
+      off_next = row_offset(x);
+      issue_part(Buf<1 - B>{}, Buf<0>{}, off_next);
+    }
+    if (w == 0 && k + 2 < n_tiles) issue_idx(Buf<B>{}, k + 2);
+    // ---- 1. partial S^T (exact dequantized K) for candidates 32c2 + m ----
+    f32x16 acc[2];
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[c2][i] = 0.0f;
+      const int row = 32 * c2 + l32;
+      const float sc = *reinterpret_cast<const float*>(raw + CK_SCALE * CS + row * 16 + 4 * g);
+      // a scale that is not a positive power of two makes this row's rope
+      // operand NaN: the row's scores become NaN for every head (rows that
+      // are not loaded are masked out by selection later)
+      const bool bad = !is_pow2_scale(sc);
+      const uint8_t* kp = raw + (8 * g + hi) * CS + row * 16;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint4 c16 = *reinterpret_cast<const uint4*>(kp + 2 * j * CS);
+        acc[c2] = mfma_32x32x16(cvt8(c16.x, c16.y, sc), qn[2 * j], acc[c2]);
+        acc[c2] = mfma_32x32x16(cvt8(c16.z, c16.w, sc), qn[2 * j + 1], acc[c2]);
+      }
+      uint4 r16 = *reinterpret_cast<const uint4*>(raw + (CK_ROPE + 2 * g + hi) * CS + row * 16);
+      if (bad) r16 = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
+      acc[c2] = mfma_32x32x16(__builtin_bit_cast(bf16x8, r16), qr, acc[c2]);
+    }
+    // ---- 2. reduce-scatter: accumulator elements [8hf, 8hf+8) of tile c2
+    // are candidates 32c2 + 16hf + 8(i/4) + 4hi + i%4, owned by wave
+    // (2c2 + hf, hh) ----
+    f32x4 s0, s1;  // own candidates 16g + 4hi + r and 16g + 8 + 4hi + r
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int og = 2 * c2 + hf;
+        const f32x4 a = f32x4{acc[c2][8 * hf + 0], acc[c2][8 * hf + 1], acc[c2][8 * hf + 2], acc[c2][8 * hf + 3]};
+        const f32x4 b = f32x4{acc[c2][8 * hf + 4], acc[c2][8 * hf + 5], acc[c2][8 * hf + 6], acc[c2][8 * hf + 7]};
+        if (og == g) {
+          s0 = a;
+          s1 = b;
+        } else {
+          const int slot = g < og ? g : g - 1;
+          f32x4* dst = reinterpret_cast<f32x4*>(recv) + ((og + 4 * hh) * 3 + slot) * 128 + lane;
+          dst[0] = a;
+          dst[64] = b;
+        }
+      }
+    lds_barrier();  // B1: partials visible
+    if (more) issue_part(Buf<1 - B>{}, Buf<1>{}, off_next);
+
+    {
+      const f32x4* src = reinterpret_cast<const f32x4*>(recv) + w * 3 * 128 + lane;
+#pragma unroll
+      for (int slot = 0; slot < 3; ++slot) {
+        s0 += src[slot * 128];
+        s1 += src[slot * 128 + 64];
+      }
+      const int32_t* vl = valid + B * TC + 16 * g + 4 * hi;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        s0[r] = vl[r] ? s0[r] * p.scale_log2 : -INFINITY;
+        s1[r] = vl[8 + r] ? s1[r] * p.scale_log2 : -INFINITY;
+        mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      if (hi == 0) maxb[g * 64 + 32 * hh + l32] = mx;
+    }
+    lds_barrier();  // B2: block maxima visible; every partial has been read
+    if (more) issue_part(Buf<1 - B>{}, Buf<2>{}, off_next);
+
+    float alpha;
+    {
+      const int hl = 32 * hh + l32;
+      const float mx = fmaxf(fmaxf(maxb[hl], maxb[64 + hl]), fmaxf(maxb[128 + hl], maxb[192 + hl]));
+      const bool need = mx > m_run + TAU;
+      alpha = need ? ((m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run - mx)) : 1.0f;
+      m_run = need ? mx : m_run;
+      float psum = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        s0[r] = (s0[r] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(s0[r] - m_run);
+        s1[r] = (s1[r] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(s1[r] - m_run);
+        psum += s0[r] + s1[r];
+      }
+      l_part = l_part * alpha + psum;
+      // P'_gg = P x (row scale of column group gg), BF16, for the PV of
+      // every group; the four scales of a row are one 16-byte piece
+      const uint8_t* scp = raw + CK_SCALE * CS + (16 * g + 4 * hi) * 16;
+      f32x4 sc0[4], sc1[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sc0[r] = *reinterpret_cast<const f32x4*>(scp + r * 16);
+        sc1[r] = *reinterpret_cast<const f32x4*>(scp + (8 + r) * 16);
+      }
+      u32x2 w0[4], w1[4];
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) {
+        w0[gg] = u32x2{pack_bf16(s0[0] * sc0[0][gg], s0[1] * sc0[1][gg]), pack_bf16(s0[2] * sc0[2][gg], s0[3] * sc0[3][gg])};
+        w1[gg] = u32x2{pack_bf16(s1[0] * sc1[0][gg], s1[1] * sc1[1][gg]), pack_bf16(s1[2] * sc1[2][gg], s1[3] * sc1[3][gg])};
+      }
+      const uint32_t pw = lds_addr(pq + hl * PS + 16 * g + 4 * hi);
+      constexpr int GS = 64 * PS * 2;  // bytes per group
+      b64_store<0>(pw, w0[0]);
+      b64_store<16>(pw, w1[0]);
+      b64_store<GS>(pw, w0[1]);
+      b64_store<GS + 16>(pw, w1[1]);
+      b64_store<2 * GS>(pw, w0[2]);
+      b64_store<2 * GS + 16>(pw, w1[2]);
+      b64_store<3 * GS>(pw, w0[3]);
+      b64_store<3 * GS + 16>(pw, w1[3]);
+    }
+    if (__any(alpha != 1.0f)) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) O[dt] *= alpha;
+    }
+    lds_barrier();  // B3: P visible
+
+    // ---- 4. O^T += V^T P'^T over columns [128g, 128g + 128), heads 32hh.. ----
+    // ds_read_b64_tr_b8: in each 16-lane group, lane 2r + b addresses row r
+    // of an 8-row block, bytes 8b..8b+7 of a 16-column piece.  All sixteen
+    // V^T operands of the tile are read first.
+    const int g16 = (lane >> 4) & 1;
+    const int jr = (lane & 15) >> 1;
+    const int jb = lane & 1;
+    const uint32_t va = lds_addr(raw + (8 * g + g16) * CS + (8 * hi + jr) * 16 + 8 * jb);
+    i32x2 v8[4][4];  // [ks][dt]: candidates 16ks.., columns 128g + 32dt..
+#define SMLA_TR8(ks, dt) v8[ks][dt] = tr8_issue<2 * (dt) * CS + 256 * (ks)>(va)
+    SMLA_TR8(0, 0); SMLA_TR8(0, 1); SMLA_TR8(0, 2); SMLA_TR8(0, 3);
+    SMLA_TR8(1, 0); SMLA_TR8(1, 1); SMLA_TR8(1, 2); SMLA_TR8(1, 3);
+    SMLA_TR8(2, 0); SMLA_TR8(2, 1); SMLA_TR8(2, 2); SMLA_TR8(2, 3);
+    SMLA_TR8(3, 0); SMLA_TR8(3, 1); SMLA_TR8(3, 2); SMLA_TR8(3, 3);
+#undef SMLA_TR8
+    // P'_g for heads 32hh + l32, candidates 16ks + 8hi + i: the B operands
+    const uint32_t pa = lds_addr(pq + (g * 64 + 32 * hh + l32) * PS + 8 * hi);
+    u32x4 pb[4];
+    pb[0] = b128_issue<0>(pa);
+    pb[1] = b128_issue<32>(pa);
+    pb[2] = b128_issue<64>(pa);
+    pb[3] = b128_issue<96>(pa);
+    // one wait for all twenty reads; the empty statement after it (volatile
+    // statements keep their order) carries the dependency to the rest
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(v8[0][0]), "+v"(v8[0][1]), "+v"(v8[0][2]), "+v"(v8[0][3]), "+v"(v8[1][0]), "+v"(v8[1][1]),
+                   "+v"(v8[1][2]), "+v"(v8[1][3]), "+v"(pb[0]), "+v"(pb[1]), "+v"(pb[2]), "+v"(pb[3]));
+    asm volatile(""
+                 : "+v"(v8[2][0]), "+v"(v8[2][1]), "+v"(v8[2][2]), "+v"(v8[2][3]), "+v"(v8[3][0]), "+v"(v8[3][1]),
+                   "+v"(v8[3][2]), "+v"(v8[3][3]));
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+        O[dt] = mfma_32x32x16(cvt8((uint32_t)v8[ks][dt][0], (uint32_t)v8[ks][dt][1], 1.0f),
+                              __builtin_bit_cast(bf16x8, pb[ks]), O[dt]);
+  };
+  for (int k = 0; k < n_tiles; k += 2) {
+    step(Buf<0>{}, k);
+    if (k + 1 < n_tiles) step(Buf<1>{}, k + 1);
+  }
+
+  // ---- epilogue: per-head sum over the four groups, normalize, store ----
+  float* lsum = maxb;  // [4][64]
+  __syncthreads();
+  {
+    const float lt = l_part + __shfl_xor(l_part, 32);
+    if (hi == 0) lsum[g * 64 + 32 * hh + l32] = lt;
+  }
+  __syncthreads();
+  const int hl = 32 * hh + l32;
+  const int h = h0 + hl;
+  const float Ls = (lsum[hl] + lsum[64 + hl]) + (lsum[128 + hl] + lsum[192 + hl]);
+  const float M = m_run;
+  const bool empty = !(Ls > 0.0f);
+  const float lse_v = empty ? -INFINITY : (M + __log2f(Ls)) * LN2;
+  if (h >= p.H) return;
+  if constexpr (DECODE) {
+    const float inv = empty ? 0.0f : 1.0f / Ls;
+    float* po = p.part_out + ((t * p.num_splits + split) * p.H + h) * (int64_t)D_V + 128 * g + 4 * hi;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *reinterpret_cast<f32x4*>(po + 32 * dt + 8 * q4) =
+            f32x4{O[dt][4 * q4] * inv, O[dt][4 * q4 + 1] * inv, O[dt][4 * q4 + 2] * inv, O[dt][4 * q4 + 3] * inv};
+    if (g == 0 && hi == 0) p.part_lse[(t * p.num_splits + split) * p.H + h] = lse_v;
+  } else {
+    float factor;
+    if (empty) {
+      factor = 0.0f;
+    } else if (p.sink) {
+      const float s2 = p.sink[h] * LOG2E;
+      const float ms = fmaxf(M, s2);
+      const float a = exp2f(M - ms);
+      factor = a / (Ls * a + exp2f(s2 - ms));
+    } else {
+      factor = 1.0f / Ls;
+    }
+    uint16_t* orow = p.out + t * p.out_st + (int64_t)h * p.out_sh + 128 * g + 4 * hi;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * q4) =
+            make_uint2(pack_bf16(O[dt][4 * q4] * factor, O[dt][4 * q4 + 1] * factor),
+                       pack_bf16(O[dt][4 * q4 + 2] * factor, O[dt][4 * q4 + 3] * factor));
+    if (g == 0 && hi == 0) p.lse[t * p.lse_st + h] = lse_v;
+  }
+}
+
+hipError_t launch_attention_fp8(const AttnParams& p, bool decode, hipStream_t s) {
+  dim3 block(f8::NT);
+  dim3 grid((unsigned)p.T, (unsigned)((p.H + 63) / 64), decode ? (unsigned)p.num_splits : 1u);
+  if (decode) hipLaunchKernelGGL((attn_fp8_kernel<true>), grid, block, 0, s, p);
+  else hipLaunchKernelGGL((attn_fp8_kernel<false>), grid, block, 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace smla

@@ -1,11 +1,13 @@
-// attention_wide.hip -- sparse MLA attention for many heads (H > 16) over an
-// FP8 or INT8 paged latent cache, prefill form and split-KV decode partials.
+// attention_wide.hip -- sparse MLA attention for many heads (H > 16) over
+// the INT8 paged latent cache, prefill form and split-KV decode partials.
 //
-// What is computed is stated in include/smla.h.  This kernel serves the
-// shapes of the AppMana release note's fused prefill (T=1024, ctx 16384,
-// H=64, widths 512/1024, FP8 and INT8 caches) and the decode batch: one
-// workgroup owns one token (and split) for 64 heads, so every selected row
-// is gathered from the pool once per token, not once per head group.
+// What is computed is stated in include/smla.h.  INT8 rows carry arbitrary
+// FP32 scales (amax/127), so code * scale is not exact in BF16: the codes
+// are converted exactly and the scales are applied to FP32 partial scores
+// and folded into P.  (The FP8 cache, whose scales are powers of two, has
+// its own kernel that dequantizes while converting.)  One workgroup owns
+// one token (and split) for 64 heads, so every selected row is gathered
+// from the pool once per token, not once per head group.
 //
 // All products use v_mfma_f32_32x32x16_bf16 (full matrix rate on gfx950).
 // Eight waves (two per SIMD); wave w = g + 4hh works on latent group g and
@@ -390,10 +392,7 @@ __global__ __launch_bounds__(wide::NT, 1) void attn_wide_kernel(AttnParams p) {
 hipError_t launch_attention_wide(const AttnParams& p, int fmt, bool decode, hipStream_t s) {
   dim3 block(wide::NT);
   dim3 grid((unsigned)p.T, (unsigned)((p.H + 63) / 64), decode ? (unsigned)p.num_splits : 1u);
-  if (fmt == FMT_FP8) {
-    if (decode) hipLaunchKernelGGL((attn_wide_kernel<FMT_FP8, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((attn_wide_kernel<FMT_FP8, false>), grid, block, 0, s, p);
-  } else if (fmt == FMT_INT8) {
+  if (fmt == FMT_INT8) {
     if (decode) hipLaunchKernelGGL((attn_wide_kernel<FMT_INT8, true>), grid, block, 0, s, p);
     else hipLaunchKernelGGL((attn_wide_kernel<FMT_INT8, false>), grid, block, 0, s, p);
   } else {

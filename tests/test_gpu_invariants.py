@@ -146,6 +146,27 @@ def test_constant_column_gives_one_minus_sink_share():
     assert torch.allclose(o[:, :, 0].float(), share, atol=4e-3, rtol=0)
 
 
+
+def test_fp8_non_power_of_two_scale_gives_nan():
+    # FP8 scales must be powers of two; with H > 16 a selected row whose
+    # scale for columns [128, 256) is 3.0 makes its token's output NaN, and
+    # tokens that do not select the row are unchanged
+    c = case(W.FMT_FP8, H=64, topk=256)
+    d = Dev(c)
+    o1, l1 = pre(d)
+    slot = int(c.indices[0, 0])
+    assert slot >= 0
+    rb = W.ROW_BYTES[W.FMT_FP8]
+    flat = d.pool.data.view(-1)
+    at = (slot // 64) * d.pool.data.stride(0) + (slot % 64) * rb + 512 + 4
+    flat[at:at + 4] = torch.from_numpy(np.frombuffer(np.float32(3.0).tobytes(), np.uint8).copy()).cuda()
+    o2, l2 = pre(d)
+    sel = torch.from_numpy((c.indices == slot).any(axis=1)).cuda()
+    assert sel[0]
+    of = o2.float()
+    assert torch.isnan(of[sel]).all()
+    assert torch.equal(o2[~sel], o1[~sel]) and torch.equal(l2[~sel], l1[~sel])
+
 def test_decode_split_invariance():
     # any split count merges to the prefill result (within tolerance)
     c = case(W.FMT_FP8, H=16, topk=1000, ctx=2048, with_sink=True, with_topk_length=True)
