@@ -60,7 +60,7 @@ def kernel_source_sha() -> str:
 def load_traffic(sha: str):
     """HBM traffic per prefill launch from committed rocprofv3 --pmc runs,
     only while the kernel sources are the ones the counters were taken on."""
-    path = os.path.join(ROOT, "profiles", "traffic_prefill_c3.json")
+    path = os.path.join(ROOT, "profiles", "traffic_attn_fp8_prefill.json")
     try:
         with open(path) as f:
             d = json.load(f)
@@ -167,7 +167,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,
-                     "kernel": "attn_kernel<FP8, prefill>",
+                     "kernel": "attn_fp8_kernel<prefill> (smla::attn_fp8_kernel<false>)",
                      "algorithmic_bytes_per_launch": alg_bytes},
         "kernel_source_sha": sha,
     }
