@@ -97,6 +97,15 @@ int32_t smla_row_bytes(int32_t format);
  * Returns -1 when topk < 1 or num_splits < 1. */
 int32_t smla_split_width(int32_t topk, int32_t num_splits);
 
+/* Scratch smla_decode needs, for callers that carve it from one buffer:
+ * *bytes_out = T*num_splits*H*512*4 (part_out) + T*num_splits*H*4
+ * (part_lse).  part_out may start at the buffer and part_lse at byte offset
+ * T*num_splits*H*2048, which keeps both 16-byte aligned.  (PR #4802 makes
+ * decode scratch caller-owned and sized by the library so that a graph can
+ * hold it.)  T >= 0, H in [1, 128], num_splits in [1, 64]; SMLA_ERR_NULL
+ * when bytes_out is NULL, SMLA_ERR_SHAPE otherwise out of range. */
+smla_status smla_decode_workspace_size(int64_t T, int32_t H, int32_t num_splits, size_t* bytes_out);
+
 /* Write n latent rows into the pool.
  *   kv     BF16 [n, >=576], row i at kv + i*kv_stride (kv_stride >= 576,
  *          multiple of 8, kv 16-byte aligned)

@@ -48,6 +48,8 @@ def _load():
     P, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
     L.smla_row_bytes.argtypes, L.smla_row_bytes.restype = [i32], i32
     L.smla_split_width.argtypes, L.smla_split_width.restype = [i32, i32], i32
+    L.smla_decode_workspace_size.argtypes = [i64, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
+    L.smla_decode_workspace_size.restype = ctypes.c_int
     L.smla_last_error.argtypes, L.smla_last_error.restype = [], ctypes.c_char_p
     L.smla_version.argtypes, L.smla_version.restype = [], ctypes.c_char_p
     L.smla_quantize_kv.argtypes = [P, i64, i64, P, _Pool, P]
@@ -73,6 +75,13 @@ def row_bytes(fmt: int) -> int:
 
 def split_width(topk: int, num_splits: int) -> int:
     return int(_load().smla_split_width(topk, num_splits))
+
+
+def decode_workspace_size(T: int, H: int, num_splits: int) -> int:
+    """Bytes of decode scratch (part_out then part_lse) for T tokens."""
+    n = ctypes.c_size_t(0)
+    _check(_load().smla_decode_workspace_size(T, H, num_splits, ctypes.byref(n)), "smla_decode_workspace_size")
+    return int(n.value)
 
 
 def version() -> str:

@@ -56,7 +56,8 @@ smla_status check_attn_common(const void* q, int64_t T, int32_t H, int64_t q_st,
   if (T < 0) return fail(SMLA_ERR_SHAPE, "T = %lld must be >= 0", (long long)T);
   if (T > INT32_MAX) return fail(SMLA_ERR_SHAPE, "T = %lld exceeds 2^31-1", (long long)T);
   if (T == 0) return SMLA_OK;  // nothing is read or launched
-  if (H < 1 || H > 128) return fail(SMLA_ERR_UNSUPPORTED, "H = %d is not supported (supported: 1..128)", H);
+  if (H < 1) return fail(SMLA_ERR_SHAPE, "H = %d must be >= 1", H);
+  if (H > 128) return fail(SMLA_ERR_UNSUPPORTED, "H = %d is not supported (supported: 1..128)", H);
   if (topk < 1) return fail(SMLA_ERR_SHAPE, "topk = %d must be >= 1", topk);
   if (!q) return fail(SMLA_ERR_NULL, "q is NULL");
   if (!indices) return fail(SMLA_ERR_NULL, "indices is NULL");
@@ -108,6 +109,17 @@ int32_t smla_split_width(int32_t topk, int32_t num_splits) {
   if (topk < 1 || num_splits < 1) return -1;
   int32_t per = (topk + num_splits - 1) / num_splits;
   return ((per + 63) / 64) * 64;
+}
+
+smla_status smla_decode_workspace_size(int64_t T, int32_t H, int32_t num_splits, size_t* bytes_out) {
+  if (!bytes_out) return fail(SMLA_ERR_NULL, "bytes_out is NULL");
+  if (T < 0) return fail(SMLA_ERR_SHAPE, "T = %lld must be >= 0", (long long)T);
+  if (H < 1 || H > 128) return fail(SMLA_ERR_SHAPE, "H = %d is outside [1, 128]", H);
+  if (num_splits < 1 || num_splits > 64)
+    return fail(SMLA_ERR_SHAPE, "num_splits = %d is outside [1, 64]", num_splits);
+  const size_t rows = (size_t)T * (size_t)num_splits * (size_t)H;
+  *bytes_out = rows * 512 * sizeof(float) + rows * sizeof(float);
+  return ok();
 }
 
 const char* smla_last_error(void) { return g_err; }
@@ -209,7 +221,8 @@ smla_status smla_combine(const float* part_out, const float* part_lse, int64_t T
                          int64_t out_stride_h, float* lse, int64_t lse_stride_t, void* stream) {
   if (T < 0) return fail(SMLA_ERR_SHAPE, "T = %lld must be >= 0", (long long)T);
   if (T == 0) return ok();  // nothing is read or launched
-  if (H < 1 || H > 128) return fail(SMLA_ERR_UNSUPPORTED, "H = %d is not supported (supported: 1..128)", H);
+  if (H < 1) return fail(SMLA_ERR_SHAPE, "H = %d must be >= 1", H);
+  if (H > 128) return fail(SMLA_ERR_UNSUPPORTED, "H = %d is not supported (supported: 1..128)", H);
   if (num_splits < 1 || num_splits > 64)
     return fail(SMLA_ERR_UNSUPPORTED, "num_splits = %d is not supported (supported: 1..64)", num_splits);
   if (!part_out) return fail(SMLA_ERR_NULL, "part_out is NULL");
