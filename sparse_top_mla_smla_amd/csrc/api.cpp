@@ -181,7 +181,7 @@ smla_status smla_prefill(const void* q, int64_t T, int32_t H, int64_t q_stride_t
   if (st != SMLA_OK) return st;
   if (!std::isfinite(sm_scale)) return fail(SMLA_ERR_SHAPE, "sm_scale must be finite");
   if (T == 0) return ok();
-  smla::AttnParams p;
+  smla::AttnParams p{};
   fill_attn(p, q, T, H, q_stride_t, q_stride_h, kv, indices, topk, idx_stride_t, topk_length, sm_scale);
   p.sink = sink;
   p.out = static_cast<uint16_t*>(out);
@@ -207,12 +207,13 @@ smla_status smla_decode(const void* q, int64_t T, int32_t H, int64_t q_stride_t,
   if (!aligned(part_lse, 4)) return fail(SMLA_ERR_STRIDE, "part_lse is not 4-byte aligned");
   if (!std::isfinite(sm_scale)) return fail(SMLA_ERR_SHAPE, "sm_scale must be finite");
   if (T == 0) return ok();
-  smla::AttnParams p;
+  smla::AttnParams p{};
   fill_attn(p, q, T, H, q_stride_t, q_stride_h, kv, indices, topk, idx_stride_t, topk_length, sm_scale);
   p.part_out = part_out;
   p.part_lse = part_lse;
   p.num_splits = num_splits;
   p.split_w = smla_split_width(topk, num_splits);
+  p.splits_per_block = 1;
   return launched(smla::launch_attention(p, kv.format, true, static_cast<hipStream_t>(stream)), "decode");
 }
 

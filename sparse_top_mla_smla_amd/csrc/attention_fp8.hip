@@ -167,7 +167,10 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
 
   const int64_t t = blockIdx.x;
   const int h0 = blockIdx.y * 64;
-  const int split = DECODE ? (int)blockIdx.z : 0;
+  // decode: this workgroup covers splits [sp0, sp_end) as one list, with a
+  // partial result at the end of each split
+  const int sp0 = DECODE ? (int)blockIdx.z * p.splits_per_block : 0;
+  const int sp_end = DECODE ? min(sp0 + p.splits_per_block, p.num_splits) : 1;
 
   int64_t L = p.topk;
   if (p.topk_length) {
@@ -176,8 +179,8 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
   }
   int64_t j_begin = 0, j_end = p.topk;
   if (DECODE) {
-    j_begin = (int64_t)split * p.split_w;
-    j_end = j_begin + p.split_w;
+    j_begin = (int64_t)sp0 * p.split_w;
+    j_end = (int64_t)sp_end * p.split_w;
     if (j_end > p.topk) j_end = p.topk;
   }
   if (j_end > L) j_end = L;
@@ -433,65 +436,114 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
         O[dt] = mfma_32x32x16(cvt8((uint32_t)v8[ks][dt][0], (uint32_t)v8[ks][dt][1], 1.0f),
                               __builtin_bit_cast(bf16x8, pb[ks]), O[dt]);
   };
+  // ---- end of a split (decode) or of the list: per-head sum over the four
+  // groups, normalize, store; then start over with empty state ----
+  float* lsum = maxb;  // [4][64]; free once every wave is past the softmax of the tile
+  auto finish = [&](int sp) {
+    {
+      const float lt = l_part + __shfl_xor(l_part, 32);
+      if (hi == 0) lsum[g * 64 + 32 * hh + l32] = lt;
+    }
+    lds_barrier();
+    const int hl = 32 * hh + l32;
+    const int h = h0 + hl;
+    const float Ls = (lsum[hl] + lsum[64 + hl]) + (lsum[128 + hl] + lsum[192 + hl]);
+    const float M = m_run;
+    const bool empty = !(Ls > 0.0f);
+    const float lse_v = empty ? -INFINITY : (M + __log2f(Ls)) * LN2;
+    if (h < p.H) {
+      if constexpr (DECODE) {
+        const float inv = empty ? 0.0f : 1.0f / Ls;
+        float* po = p.part_out + ((t * p.num_splits + sp) * p.H + h) * (int64_t)D_V + 128 * g + 4 * hi;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4)
+            *reinterpret_cast<f32x4*>(po + 32 * dt + 8 * q4) = f32x4{O[dt][4 * q4] * inv, O[dt][4 * q4 + 1] * inv,
+                                                                     O[dt][4 * q4 + 2] * inv, O[dt][4 * q4 + 3] * inv};
+        if (g == 0 && hi == 0) p.part_lse[(t * p.num_splits + sp) * p.H + h] = lse_v;
+      } else {
+        float factor;
+        if (empty) {
+          factor = 0.0f;
+        } else if (p.sink) {
+          const float s2 = p.sink[h] * LOG2E;
+          const float ms = fmaxf(M, s2);
+          const float a = exp2f(M - ms);
+          factor = a / (Ls * a + exp2f(s2 - ms));
+        } else {
+          factor = 1.0f / Ls;
+        }
+        uint16_t* orow = p.out + t * p.out_st + (int64_t)h * p.out_sh + 128 * g + 4 * hi;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4)
+            *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * q4) =
+                make_uint2(pack_bf16(O[dt][4 * q4] * factor, O[dt][4 * q4 + 1] * factor),
+                           pack_bf16(O[dt][4 * q4 + 2] * factor, O[dt][4 * q4 + 3] * factor));
+        if (g == 0 && hi == 0) p.lse[t * p.lse_st + h] = lse_v;
+      }
+    }
+    // every wave has read lsum before anyone writes it again
+    lds_barrier();
+    m_run = -INFINITY;
+    l_part = 0.0f;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) O[dt][i] = 0.0f;
+  };
+  // tiles per split; a split ends after its last tile
+  const int tps = DECODE ? p.split_w / TC : 0;
+  int sp_next = sp0;  // next split to finish
   for (int k = 0; k < n_tiles; k += 2) {
     step(Buf<0>{}, k);
-    if (k + 1 < n_tiles) step(Buf<1>{}, k + 1);
-  }
-
-  // ---- epilogue: per-head sum over the four groups, normalize, store ----
-  float* lsum = maxb;  // [4][64]
-  __syncthreads();
-  {
-    const float lt = l_part + __shfl_xor(l_part, 32);
-    if (hi == 0) lsum[g * 64 + 32 * hh + l32] = lt;
-  }
-  __syncthreads();
-  const int hl = 32 * hh + l32;
-  const int h = h0 + hl;
-  const float Ls = (lsum[hl] + lsum[64 + hl]) + (lsum[128 + hl] + lsum[192 + hl]);
-  const float M = m_run;
-  const bool empty = !(Ls > 0.0f);
-  const float lse_v = empty ? -INFINITY : (M + __log2f(Ls)) * LN2;
-  if (h >= p.H) return;
-  if constexpr (DECODE) {
-    const float inv = empty ? 0.0f : 1.0f / Ls;
-    float* po = p.part_out + ((t * p.num_splits + split) * p.H + h) * (int64_t)D_V + 128 * g + 4 * hi;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        *reinterpret_cast<f32x4*>(po + 32 * dt + 8 * q4) =
-            f32x4{O[dt][4 * q4] * inv, O[dt][4 * q4 + 1] * inv, O[dt][4 * q4 + 2] * inv, O[dt][4 * q4 + 3] * inv};
-    if (g == 0 && hi == 0) p.part_lse[(t * p.num_splits + split) * p.H + h] = lse_v;
-  } else {
-    float factor;
-    if (empty) {
-      factor = 0.0f;
-    } else if (p.sink) {
-      const float s2 = p.sink[h] * LOG2E;
-      const float ms = fmaxf(M, s2);
-      const float a = exp2f(M - ms);
-      factor = a / (Ls * a + exp2f(s2 - ms));
-    } else {
-      factor = 1.0f / Ls;
+    if (DECODE && ((k + 1) % tps == 0 || k + 1 == n_tiles)) finish(sp_next++);
+    if (k + 1 < n_tiles) {
+      step(Buf<1>{}, k + 1);
+      if (DECODE && ((k + 2) % tps == 0 || k + 2 == n_tiles)) finish(sp_next++);
     }
-    uint16_t* orow = p.out + t * p.out_st + (int64_t)h * p.out_sh + 128 * g + 4 * hi;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * q4) =
-            make_uint2(pack_bf16(O[dt][4 * q4] * factor, O[dt][4 * q4 + 1] * factor),
-                       pack_bf16(O[dt][4 * q4 + 2] * factor, O[dt][4 * q4 + 3] * factor));
-    if (g == 0 && hi == 0) p.lse[t * p.lse_st + h] = lse_v;
+  }
+  // the rest of the list: prefill's only result, or decode splits left empty
+  // by the list length
+  if (DECODE) {
+    while (sp_next < sp_end) finish(sp_next++);
+  } else {
+    finish(0);
   }
 }
 
+// compute units of the current device, looked up once per device
+static int compute_units() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 hipError_t launch_attention_fp8(const AttnParams& p, bool decode, hipStream_t s) {
+  AttnParams q = p;
+  q.splits_per_block = 1;
+  if (decode) {
+    // One workgroup takes several consecutive splits of a token when there
+    // are more (token, split) pairs than compute units: the gather pipeline
+    // and Q carry across the split boundary, and the grid fills the chip
+    // about once instead of leaving a ragged second wave.
+    const int64_t pairs = p.T * (int64_t)((p.H + 63) / 64) * p.num_splits;
+    int64_t g = pairs / compute_units();
+    q.splits_per_block = (int)(g < 1 ? 1 : (g > p.num_splits ? p.num_splits : g));
+  }
   dim3 block(f8::NT);
-  dim3 grid((unsigned)p.T, (unsigned)((p.H + 63) / 64), decode ? (unsigned)p.num_splits : 1u);
-  if (decode) hipLaunchKernelGGL((attn_fp8_kernel<true>), grid, block, 0, s, p);
-  else hipLaunchKernelGGL((attn_fp8_kernel<false>), grid, block, 0, s, p);
+  dim3 grid((unsigned)q.T, (unsigned)((q.H + 63) / 64),
+            decode ? (unsigned)((q.num_splits + q.splits_per_block - 1) / q.splits_per_block) : 1u);
+  if (decode) hipLaunchKernelGGL((attn_fp8_kernel<true>), grid, block, 0, s, q);
+  else hipLaunchKernelGGL((attn_fp8_kernel<false>), grid, block, 0, s, q);
   return hipGetLastError();
 }
 

@@ -41,6 +41,7 @@ struct AttnParams {
   float* part_lse;      // [T, S, H]
   int32_t num_splits;
   int32_t split_w;
+  int32_t splits_per_block;  // decode: consecutive splits one workgroup runs (FP8 many-head kernel)
 };
 
 struct CombineParams {
