@@ -8,9 +8,15 @@ T = 1024 queries at its last positions, H = 64 heads, causal top-k width
 into the cache (smla_quantize_kv) + the prefill over the T tokens
 (smla_prefill).  Inputs are resident in HBM before the timed region.
 
-Also measured in the same run (reported under "decode"): the split-KV
-decode batch -- 64 sequences x 1 query, ctx 16384 each (656 MiB FP8 pool),
-H = 64, top-k 2048, 8 splits, decode + combine.
+Also measured in the same run:
+- "decode": the split-KV decode batch -- 64 sequences x 1 query, ctx 16384
+  each (656 MiB FP8 pool), H = 64, top-k 2048, 8 splits, decode + combine;
+- "fewhead": 8192 tokens, 8 native heads read as a view of a 64-head BF16 q
+  buffer, ctx 32768 BF16 pool, top-k 640 with per-token lengths and a sink,
+  written in place; beside it the same inputs with all 64 heads;
+- "int8": T = 1024, H = 128, ctx 65536 INT8 pool, top-k 2048 as a view of a
+  4096-wide index buffer, with a sink.
+Kernel times come from HIP events on the launch stream (median, p10, p90).
 
 Prints one JSON line on stdout.
 """
@@ -43,9 +49,38 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=512)
+    ap.add_argument("--no-extra", action="store_true", help="skip the few-head and INT8 workloads")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="also run one plain device-to-device copy of MIB MiB (reference for HBM counters)")
     return ap.parse_args()
+
+
+def pct(xs):
+    """median, p10, p90 of a list of times"""
+    a = np.asarray(xs, dtype=np.float64)
+    return float(np.median(a)), float(np.percentile(a, 10)), float(np.percentile(a, 90))
+
+
+def event_times_us(torch, fn, iters, stream):
+    """Per-call times (us) of fn() between HIP events recorded on `stream`."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) * 1e3 for a, b in evs]
+
+
+def host_cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def kernel_source_sha() -> str:
@@ -133,6 +168,7 @@ def main():
     ms_per_step = elapsed * 1e3 / args.steps
     kern_ms = [a.elapsed_time(b) for a, b in evs]
     prefill_ms = float(np.mean(kern_ms))
+    p_med, p_p10, p_p90 = pct([x * 1e3 for x in kern_ms])
 
     rows = case.gathered_rows()
     kv_bytes = rows * W.ROW_BYTES[W.FMT_FP8]
@@ -162,6 +198,7 @@ def main():
                    "T": T, "ctx": case.ctx, "H": H, "topk": case.topk, "kv_format": "fp8_e4m3_656B"},
         "gathered_kv_GBps": round(kv_bytes / (prefill_ms * 1e-3) / 1e9, 2),
         "prefill_kernel_us": round(prefill_ms * 1e3, 3),
+        "prefill_kernel_us_median_p10_p90": [round(p_med, 3), round(p_p10, 3), round(p_p90, 3)],
         "prefill_us_per_token_kernel": round(prefill_ms * 1e3 / T, 5),
         "mfma_util": round(flops / (prefill_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
@@ -171,6 +208,11 @@ def main():
                      "algorithmic_bytes_per_launch": alg_bytes},
         "kernel_source_sha": sha,
     }
+    props = torch.cuda.get_device_properties(dev)
+    result["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+                        "compute_units": props.multi_processor_count,
+                        "memory_GiB": round(props.total_memory / 2**30, 1),
+                        "spec_hbm_GBps": HBM_PEAK_GBPS, "spec_bf16_mfma_TFLOPs": BF16_MFMA_PEAK_TFLOPS}
     print(f"[bench] prefill setup {setup_s:.1f}s, step {ms_per_step:.3f} ms, kernel {prefill_ms:.3f} ms",
           file=sys.stderr, flush=True)
 
@@ -222,8 +264,10 @@ def main():
             dstep(i, devs[i])
         torch.cuda.synchronize()
         d_elapsed = (time.perf_counter() - t1) * 1e6 / dsteps
-        dec_us = float(np.mean([a.elapsed_time(b) for a, b, _ in devs])) * 1e3
-        comb_us = float(np.mean([b.elapsed_time(c) for _, b, c in devs])) * 1e3
+        dec_list = [a.elapsed_time(b) * 1e3 for a, b, _ in devs]
+        comb_list = [b.elapsed_time(c) * 1e3 for _, b, c in devs]
+        dec_us = float(np.mean(dec_list))
+        comb_us = float(np.mean(comb_list))
         drows = dc.gathered_rows()
         dbytes = drows * W.ROW_BYTES[W.FMT_FP8]
         result["decode"] = {
@@ -231,13 +275,92 @@ def main():
                         f"topk={dc.topk}, splits={S} (decode + combine)",
             "us_per_call": round(d_elapsed, 3),
             "decode_kernel_us": round(dec_us, 3),
+            "decode_kernel_us_median_p10_p90": [round(v, 3) for v in pct(dec_list)],
             "combine_kernel_us": round(comb_us, 3),
+            "combine_kernel_us_median_p10_p90": [round(v, 3) for v in pct(comb_list)],
             "gathered_kv_bytes": dbytes,
             "gathered_kv_GBps_decode_kernel": round(dbytes / (dec_us * 1e-6) / 1e9, 2),
             "gathered_kv_GBps_end_to_end": round(dbytes / ((dec_us + comb_us) * 1e-6) / 1e9, 2),
             "hbm_frac_end_to_end": round(dbytes / ((dec_us + comb_us) * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
         }
         print(f"[bench] decode {dec_us:.2f} us + combine {comb_us:.2f} us", file=sys.stderr, flush=True)
+        del dpool, po, pl, dq, didx, idx_sets, dout, dlse
+        torch.cuda.empty_cache()
+
+    # ---------------- few-head BF16 and INT8 prefill ----------------
+    if not args.no_extra:
+        iters = 10
+        # few heads: q[:, :8] of a 64-head buffer, out written in place
+        fc = W.c4_fewhead()
+        fq = bf16(fc.q_buf)
+        fkv = bf16(fc.kv)
+        fpool = smla.KVPool.empty(fc.num_blocks, W.FMT_BF16, device=dev)
+        smla.quantize_kv(fkv, torch.from_numpy(fc.slots).to(dev), fpool)
+        del fkv
+        fidx = torch.from_numpy(fc.idx_buf).to(dev)[:, : fc.topk]
+        ftl = torch.from_numpy(fc.topk_length).to(dev)
+        fsink64 = torch.from_numpy(np.concatenate([fc.sink, np.zeros(64 - fc.H, np.float32)])).to(dev)
+        fout = torch.zeros((fc.T, fc.out_hbuf, D_V), dtype=torch.bfloat16, device=dev)
+        flse = torch.empty((fc.T, 64), dtype=torch.float32, device=dev)
+
+        def few(hq):
+            return lambda: smla.prefill(fq[:, :hq], fpool, fidx, topk_length=ftl, sink=fsink64[:hq],
+                                        sm_scale=float(fc.sm_scale), out=fout[:, :hq], lse=flse[:, :hq])
+
+        few(fc.H)()
+        few(64)()
+        t8 = event_times_us(torch, few(fc.H), iters, stream)
+        t64 = event_times_us(torch, few(64), iters, stream)
+        frows = fc.gathered_rows()
+        fbytes = frows * W.ROW_BYTES[W.FMT_BF16]
+        f_med = pct(t8)
+        result["fewhead"] = {
+            "workload": f"bf16 few-head prefill T={fc.T} H={fc.H} (view of a 64-head q buffer), ctx {fc.ctx}, "
+                        f"topk {fc.topk} with topk_length and sink, out in place",
+            "kernel_us_median_p10_p90": [round(v, 3) for v in f_med],
+            "us_per_token": round(f_med[0] / fc.T, 5),
+            "gathered_kv_bytes": fbytes,
+            "gathered_kv_GBps": round(fbytes / (f_med[0] * 1e-6) / 1e9, 2),
+            "hbm_frac": round(fbytes / (f_med[0] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            "same_inputs_all_64_heads_us_median": round(pct(t64)[0], 3),
+            "speedup_vs_64_heads": round(pct(t64)[0] / f_med[0], 3),
+        }
+        print(f"[bench] fewhead {f_med[0]:.1f} us (64 heads: {pct(t64)[0]:.1f} us)", file=sys.stderr, flush=True)
+        del fq, fpool, fidx, ftl, fout, flse
+        torch.cuda.empty_cache()
+        # INT8, 128 heads, narrowed index view
+        ic = W.c5_int8()
+        iq = bf16(ic.q_buf)
+        ikv = bf16(ic.kv)
+        ipool = smla.KVPool.empty(ic.num_blocks, W.FMT_INT8, device=dev)
+        smla.quantize_kv(ikv, torch.from_numpy(ic.slots).to(dev), ipool)
+        del ikv
+        iidx = torch.from_numpy(ic.idx_buf).to(dev)[:, : ic.topk]
+        isink = torch.from_numpy(ic.sink).to(dev)
+        iout = torch.empty((ic.T, ic.H, D_V), dtype=torch.bfloat16, device=dev)
+        ilse = torch.empty((ic.T, ic.H), dtype=torch.float32, device=dev)
+
+        def i8():
+            smla.prefill(iq[:, : ic.H], ipool, iidx, sink=isink, sm_scale=float(ic.sm_scale), out=iout, lse=ilse)
+
+        i8()
+        ti = event_times_us(torch, i8, iters, stream)
+        irows = ic.gathered_rows()
+        ibytes = irows * W.ROW_BYTES[W.FMT_INT8]
+        iflops = 2.0 * ic.H * (D_QK + D_V) * irows
+        i_med = pct(ti)
+        result["int8"] = {
+            "workload": f"int8 prefill T={ic.T} H={ic.H} ctx {ic.ctx} topk {ic.topk} (index view of stride "
+                        f"{ic.idx_buf.shape[1]}), sink",
+            "kernel_us_median_p10_p90": [round(v, 3) for v in i_med],
+            "us_per_token": round(i_med[0] / ic.T, 5),
+            "gathered_kv_bytes": ibytes,
+            "gathered_kv_GBps": round(ibytes / (i_med[0] * 1e-6) / 1e9, 2),
+            "mfma_util": round(iflops / (i_med[0] * 1e-6) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+        }
+        print(f"[bench] int8 {i_med[0]:.1f} us", file=sys.stderr, flush=True)
+        del iq, ipool, iidx, iout, ilse
+        torch.cuda.empty_cache()
 
     if args.calibrate_copy:
         n = args.calibrate_copy << 20
@@ -262,6 +385,7 @@ def main():
         cpu_s = time.perf_counter() - tc
         result["cpu_baseline"] = {
             "value": round(cpu_s * 1e6 / n, 3), "unit": "us/token", "cores": ncores, "kind": "oracle",
+            "host": {"cpu_model": host_cpu_model(), "visible_cpus": os.cpu_count()},
             "sample": f"{n} of the {T} tokens of the same prefill workload (float64 C oracle, "
                       f"OpenMP over tokens), {cpu_s:.2f} s wall"}
         print(f"[bench] cpu oracle {cpu_s:.2f}s for {n} tokens on {ncores} threads", file=sys.stderr, flush=True)
