@@ -186,26 +186,6 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
   if (j_end > L) j_end = L;
   const int n_tiles = j_end > j_begin ? (int)((j_end - j_begin + TC - 1) / TC) : 0;
 
-  // Q as the B operand of S^T = K Q^T for head h0 + 32hh + l32.  A K lane
-  // reads one 16-byte piece (8g + 2j + hi) that feeds MFMA steps 2j and
-  // 2j+1, so qn[2j + b] holds nope columns 128g + 32j + 16hi + 8b + i; qr
-  // holds rope columns 16g + 8hi + i.
-  bf16x8 qn[8], qr;
-  {
-    const int h = h0 + 32 * hh + l32;
-    const bool hv = h < p.H;
-    const uint16_t* qrow = p.q + t * p.q_st + (int64_t)(hv ? h : 0) * p.q_sh;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        uint4 v = *reinterpret_cast<const uint4*>(qrow + 128 * g + 32 * j + 16 * hi + 8 * b);
-        qn[2 * j + b] = __builtin_bit_cast(bf16x8, hv ? v : make_uint4(0, 0, 0, 0));
-      }
-    uint4 v = *reinterpret_cast<const uint4*>(qrow + D_NOPE + 16 * g + 8 * hi);
-    qr = __builtin_bit_cast(bf16x8, hv ? v : make_uint4(0, 0, 0, 0));
-  }
-
   // list entry k*64 + lane of this workgroup's range: its index value, and
   // the byte offset in the pool of its row (-1: masked or not a pool slot)
   const int32_t* idx_row = p.idx + t * p.idx_st;
@@ -244,6 +224,38 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
   };
   static_assert(2 * GPARTS == GROUNDS, "three parts of two rounds");
 
+  // the first index entry is loaded before Q, so the first gather waits
+  // only for it
+  // (an unconditional load of an entry inside the range, selected after)
+  int32_t entry0 = -1;
+  if (n_tiles > 0) {
+    const int64_t j = j_begin + lane;
+    const int32_t x = idx_row[j < j_end ? j : j_end - 1];
+    entry0 = j < j_end ? x : -1;
+  }
+
+  // Q as the B operand of S^T = K Q^T for head h0 + 32hh + l32.  A K lane
+  // reads one 16-byte piece (8g + 2j + hi) that feeds MFMA steps 2j and
+  // 2j+1, so qn[2j + b] holds nope columns 128g + 32j + 16hi + 8b + i; qr
+  // holds rope columns 16g + 8hi + i.
+  bf16x8 qn[8], qr;
+  {
+    const int h = h0 + 32 * hh + l32;
+    const bool hv = h < p.H;
+    const uint16_t* qrow = p.q + t * p.q_st + (int64_t)(hv ? h : 0) * p.q_sh;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        // loaded for every lane (row 0 stands in for heads past H) and
+        // zeroed after, so the loads are unconditional
+        const uint4 v = *reinterpret_cast<const uint4*>(qrow + 128 * g + 32 * j + 16 * hi + 8 * b);
+        qn[2 * j + b] = __builtin_bit_cast(bf16x8, hv ? v : make_uint4(0, 0, 0, 0));
+      }
+    const uint4 v = *reinterpret_cast<const uint4*>(qrow + D_NOPE + 16 * g + 8 * hi);
+    qr = __builtin_bit_cast(bf16x8, hv ? v : make_uint4(0, 0, 0, 0));
+  }
+
   // softmax state for heads 32hh + l32 (identical in the four waves of hh)
   float m_run = -INFINITY;
   float l_part = 0.0f;  // this wave's share: candidates 16g.. of every tile
@@ -259,13 +271,35 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
       reinterpret_cast<uint4*>(raw0)[i] = make_uint4(0, 0, 0, 0);
       reinterpret_cast<uint4*>(raw1)[i] = make_uint4(0, 0, 0, 0);
     }
-    const int64_t off0 = row_offset(load_entry(0));
-    __syncthreads();
+    const int64_t off0 = row_offset(entry0);
+    // the zero fill is complete everywhere before any gather lands; the Q
+    // loads stay in flight beside the first gather
+    lds_barrier();
     issue_part(Buf<0>{}, Buf<0>{}, off0);
     issue_part(Buf<0>{}, Buf<1>{}, off0);
     issue_part(Buf<0>{}, Buf<2>{}, off0);
     if (w == 0 && n_tiles > 1) issue_idx(Buf<1>{}, 1);
   }
+
+  // decode: a split that ends before the last tile keeps its O in registers
+  // and is stored by the next tile, after that tile's gather is issued, so
+  // the stores drain during a tile instead of inside its first wait
+  int pend_sp = -1;       // split whose partial is still to be stored
+  float pend_inv = 0.0f;  // its normalization (heads 32hh + l32)
+  float pend_lse = 0.0f;
+  auto store_partial = [&](int sp, float inv, float lse_v) {
+    const int h = h0 + 32 * hh + l32;
+    if (h < p.H) {
+      float* po = p.part_out + ((t * p.num_splits + sp) * p.H + h) * (int64_t)D_V + 128 * g + 4 * hi;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *reinterpret_cast<f32x4*>(po + 32 * dt + 8 * q4) = f32x4{O[dt][4 * q4] * inv, O[dt][4 * q4 + 1] * inv,
+                                                                   O[dt][4 * q4 + 2] * inv, O[dt][4 * q4 + 3] * inv};
+      if (g == 0 && hi == 0) p.part_lse[(t * p.num_splits + sp) * p.H + h] = lse_v;
+    }
+  };
 
   // one tile; tile k sits in raw buffer B = k & 1
   auto step = [&](auto buf, int k) {
@@ -284,6 +318,14 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
       issue_part(Buf<1 - B>{}, Buf<0>{}, off_next);
     }
     if (w == 0 && k + 2 < n_tiles) issue_idx(Buf<B>{}, k + 2);
+    if (DECODE && pend_sp >= 0) {
+      store_partial(pend_sp, pend_inv, pend_lse);
+      pend_sp = -1;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) O[dt][i] = 0.0f;
+    }
     // ---- 1. partial S^T (exact dequantized K) for candidates 32c2 + m ----
     f32x16 acc[2];
 #pragma unroll
@@ -439,7 +481,7 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
   // ---- end of a split (decode) or of the list: per-head sum over the four
   // groups, normalize, store; then start over with empty state ----
   float* lsum = maxb;  // [4][64]; free once every wave is past the softmax of the tile
-  auto finish = [&](int sp) {
+  auto finish = [&](int sp, bool defer) {
     {
       const float lt = l_part + __shfl_xor(l_part, 32);
       if (hi == 0) lsum[g * 64 + 32 * hh + l32] = lt;
@@ -451,44 +493,43 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
     const float M = m_run;
     const bool empty = !(Ls > 0.0f);
     const float lse_v = empty ? -INFINITY : (M + __log2f(Ls)) * LN2;
-    if (h < p.H) {
-      if constexpr (DECODE) {
-        const float inv = empty ? 0.0f : 1.0f / Ls;
-        float* po = p.part_out + ((t * p.num_splits + sp) * p.H + h) * (int64_t)D_V + 128 * g + 4 * hi;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4)
-            *reinterpret_cast<f32x4*>(po + 32 * dt + 8 * q4) = f32x4{O[dt][4 * q4] * inv, O[dt][4 * q4 + 1] * inv,
-                                                                     O[dt][4 * q4 + 2] * inv, O[dt][4 * q4 + 3] * inv};
-        if (g == 0 && hi == 0) p.part_lse[(t * p.num_splits + sp) * p.H + h] = lse_v;
-      } else {
-        float factor;
-        if (empty) {
-          factor = 0.0f;
-        } else if (p.sink) {
-          const float s2 = p.sink[h] * LOG2E;
-          const float ms = fmaxf(M, s2);
-          const float a = exp2f(M - ms);
-          factor = a / (Ls * a + exp2f(s2 - ms));
-        } else {
-          factor = 1.0f / Ls;
-        }
-        uint16_t* orow = p.out + t * p.out_st + (int64_t)h * p.out_sh + 128 * g + 4 * hi;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4)
-            *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * q4) =
-                make_uint2(pack_bf16(O[dt][4 * q4] * factor, O[dt][4 * q4 + 1] * factor),
-                           pack_bf16(O[dt][4 * q4 + 2] * factor, O[dt][4 * q4 + 3] * factor));
-        if (g == 0 && hi == 0) p.lse[t * p.lse_st + h] = lse_v;
+    m_run = -INFINITY;
+    l_part = 0.0f;
+    if constexpr (DECODE) {
+      const float inv = empty ? 0.0f : 1.0f / Ls;
+      if (defer) {
+        // stored by the next tile; its first barrier also orders these lsum
+        // reads before the next writes of that buffer
+        pend_sp = sp;
+        pend_inv = inv;
+        pend_lse = lse_v;
+        return;
       }
+      store_partial(sp, inv, lse_v);
+    } else if (h < p.H) {
+      float factor;
+      if (empty) {
+        factor = 0.0f;
+      } else if (p.sink) {
+        const float s2 = p.sink[h] * LOG2E;
+        const float ms = fmaxf(M, s2);
+        const float a = exp2f(M - ms);
+        factor = a / (Ls * a + exp2f(s2 - ms));
+      } else {
+        factor = 1.0f / Ls;
+      }
+      uint16_t* orow = p.out + t * p.out_st + (int64_t)h * p.out_sh + 128 * g + 4 * hi;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * q4) =
+              make_uint2(pack_bf16(O[dt][4 * q4] * factor, O[dt][4 * q4 + 1] * factor),
+                         pack_bf16(O[dt][4 * q4 + 2] * factor, O[dt][4 * q4 + 3] * factor));
+      if (g == 0 && hi == 0) p.lse[t * p.lse_st + h] = lse_v;
     }
     // every wave has read lsum before anyone writes it again
     lds_barrier();
-    m_run = -INFINITY;
-    l_part = 0.0f;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -499,18 +540,18 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
   int sp_next = sp0;  // next split to finish
   for (int k = 0; k < n_tiles; k += 2) {
     step(Buf<0>{}, k);
-    if (DECODE && ((k + 1) % tps == 0 || k + 1 == n_tiles)) finish(sp_next++);
+    if (DECODE && ((k + 1) % tps == 0 || k + 1 == n_tiles)) finish(sp_next++, k + 1 < n_tiles);
     if (k + 1 < n_tiles) {
       step(Buf<1>{}, k + 1);
-      if (DECODE && ((k + 2) % tps == 0 || k + 2 == n_tiles)) finish(sp_next++);
+      if (DECODE && ((k + 2) % tps == 0 || k + 2 == n_tiles)) finish(sp_next++, k + 2 < n_tiles);
     }
   }
   // the rest of the list: prefill's only result, or decode splits left empty
   // by the list length
   if (DECODE) {
-    while (sp_next < sp_end) finish(sp_next++);
+    while (sp_next < sp_end) finish(sp_next++, false);
   } else {
-    finish(0);
+    finish(0, false);
   }
 }
 
