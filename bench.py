@@ -11,6 +11,8 @@ into the cache (smla_quantize_kv) + the prefill over the T tokens
 Also measured in the same run:
 - "decode": the split-KV decode batch -- 64 sequences x 1 query, ctx 16384
   each (656 MiB FP8 pool), H = 64, top-k 2048, 8 splits, decode + combine;
+  beside it the same batch at the split count the library's cost model
+  picks for this device (smla_decode_num_splits);
 - "fewhead": 8192 tokens, 8 native heads read as a view of a 64-head BF16 q
   buffer, ctx 32768 BF16 pool, top-k 640 with per-token lengths and a sink,
   written in place; beside it the same inputs with all 64 heads;
@@ -227,9 +229,6 @@ def main():
         dpool = smla.KVPool.empty(dc.num_blocks, W.FMT_FP8, device=dev)
         smla.quantize_kv(dkv, dslots, dpool)
         del dkv
-        S = dc.num_splits
-        po = torch.empty((dc.T, S, dc.H, D_V), dtype=torch.float32, device=dev)
-        pl = torch.empty((dc.T, S, dc.H), dtype=torch.float32, device=dev)
         dout = torch.empty((dc.T, dc.H, D_V), dtype=torch.bfloat16, device=dev)
         dlse = torch.empty((dc.T, dc.H), dtype=torch.float32, device=dev)
         # rotate over independent index sets so no call finds its rows cache-warm
@@ -243,48 +242,67 @@ def main():
             idx_sets.append(torch.where(didx >= 0, moved, didx).to(torch.int32))
         torch.cuda.synchronize()
         dsteps = max(args.steps, 20)
-
-        def dstep(i, ev=None):
-            ix = idx_sets[i % len(idx_sets)]
-            if ev is not None:
-                ev[0].record(stream)
-            smla.decode(dq, dpool, ix, S, sm_scale=float(dc.sm_scale), part_out=po, part_lse=pl)
-            if ev is not None:
-                ev[1].record(stream)
-            smla.combine(po, pl, out=dout, lse=dlse)
-            if ev is not None:
-                ev[2].record(stream)
-
-        for i in range(args.warmup):
-            dstep(i)
-        devs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(dsteps)]
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        for i in range(dsteps):
-            dstep(i, devs[i])
-        torch.cuda.synchronize()
-        d_elapsed = (time.perf_counter() - t1) * 1e6 / dsteps
-        dec_list = [a.elapsed_time(b) * 1e3 for a, b, _ in devs]
-        comb_list = [b.elapsed_time(c) * 1e3 for _, b, c in devs]
-        dec_us = float(np.mean(dec_list))
-        comb_us = float(np.mean(comb_list))
         drows = dc.gathered_rows()
         dbytes = drows * W.ROW_BYTES[W.FMT_FP8]
+
+        def time_decode(S):
+            po = torch.empty((dc.T, S, dc.H, D_V), dtype=torch.float32, device=dev)
+            pl = torch.empty((dc.T, S, dc.H), dtype=torch.float32, device=dev)
+
+            def dstep(i, ev=None):
+                ix = idx_sets[i % len(idx_sets)]
+                if ev is not None:
+                    ev[0].record(stream)
+                smla.decode(dq, dpool, ix, S, sm_scale=float(dc.sm_scale), part_out=po, part_lse=pl)
+                if ev is not None:
+                    ev[1].record(stream)
+                smla.combine(po, pl, out=dout, lse=dlse)
+                if ev is not None:
+                    ev[2].record(stream)
+
+            for i in range(args.warmup):
+                dstep(i)
+            devs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(dsteps)]
+            torch.cuda.synchronize()
+            t1 = time.perf_counter()
+            for i in range(dsteps):
+                dstep(i, devs[i])
+            torch.cuda.synchronize()
+            d_elapsed = (time.perf_counter() - t1) * 1e6 / dsteps
+            dec_list = [a.elapsed_time(b) * 1e3 for a, b, _ in devs]
+            comb_list = [b.elapsed_time(c) * 1e3 for _, b, c in devs]
+            dec_us = float(np.mean(dec_list))
+            comb_us = float(np.mean(comb_list))
+            return {
+                "num_splits": S,
+                "us_per_call": round(d_elapsed, 3),
+                "decode_kernel_us": round(dec_us, 3),
+                "decode_kernel_us_median_p10_p90": [round(v, 3) for v in pct(dec_list)],
+                "combine_kernel_us": round(comb_us, 3),
+                "combine_kernel_us_median_p10_p90": [round(v, 3) for v in pct(comb_list)],
+                "gathered_kv_GBps_decode_kernel": round(dbytes / (dec_us * 1e-6) / 1e9, 2),
+                "gathered_kv_GBps_end_to_end": round(dbytes / ((dec_us + comb_us) * 1e-6) / 1e9, 2),
+                "hbm_frac_end_to_end": round(dbytes / ((dec_us + comb_us) * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            }
+
+        S = dc.num_splits
         result["decode"] = {
             "workload": f"fp8 split-KV decode {dc.T} seqs x 1 query, ctx {dc.ctx}, H={dc.H}, "
                         f"topk={dc.topk}, splits={S} (decode + combine)",
-            "us_per_call": round(d_elapsed, 3),
-            "decode_kernel_us": round(dec_us, 3),
-            "decode_kernel_us_median_p10_p90": [round(v, 3) for v in pct(dec_list)],
-            "combine_kernel_us": round(comb_us, 3),
-            "combine_kernel_us_median_p10_p90": [round(v, 3) for v in pct(comb_list)],
             "gathered_kv_bytes": dbytes,
-            "gathered_kv_GBps_decode_kernel": round(dbytes / (dec_us * 1e-6) / 1e9, 2),
-            "gathered_kv_GBps_end_to_end": round(dbytes / ((dec_us + comb_us) * 1e-6) / 1e9, 2),
-            "hbm_frac_end_to_end": round(dbytes / ((dec_us + comb_us) * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
         }
-        print(f"[bench] decode {dec_us:.2f} us + combine {comb_us:.2f} us", file=sys.stderr, flush=True)
-        del dpool, po, pl, dq, didx, idx_sets, dout, dlse
+        result["decode"].update(time_decode(S))
+        # the split count the library's cost model picks for this shape on this device
+        Sm = smla.decode_num_splits(dc.T, dc.H, dc.topk, W.FMT_FP8)
+        model = time_decode(Sm) if Sm != S else {k: v for k, v in result["decode"].items()
+                                                if k not in ("workload", "gathered_kv_bytes")}
+        model["predicted_us"] = round(smla.split_model_cost(dc.T, dc.H, dc.topk, W.FMT_FP8, Sm), 2)
+        result["decode"]["model_split_count"] = model
+        d8 = result["decode"]
+        print(f"[bench] decode {d8['decode_kernel_us']:.2f} us + combine {d8['combine_kernel_us']:.2f} us (S={S}); "
+              f"model S={Sm}: {model['decode_kernel_us']:.2f} + {model['combine_kernel_us']:.2f} us",
+              file=sys.stderr, flush=True)
+        del dpool, dq, didx, idx_sets, dout, dlse
         torch.cuda.empty_cache()
 
     # ---------------- few-head BF16 and INT8 prefill ----------------

@@ -160,6 +160,54 @@ smla_status smla_combine(const float* part_out, const float* part_lse, int64_t T
                          int32_t H, const float* sink, void* out, int64_t out_stride_t,
                          int64_t out_stride_h, float* lse, int64_t lse_stride_t, void* stream);
 
+/* Split-count model (FlashInfer PR #4802, description sections "cpb model"
+ * and "Crossover": a closed form over a few per-device constants replaces a
+ * per-shape tuning sweep, and small-T prefill is routed to the split form
+ * when that is predicted at most 0.95x the prefill time).  Predicted time in
+ * microseconds on MI355X of smla_decode + smla_combine with num_splits
+ * splits, or of smla_prefill when num_splits == 0, for T tokens of H heads
+ * with topk list entries in the given format:
+ *   decode  = waves * (a + b * tiles per workgroup + f * splits per workgroup)
+ *             + w * MB of partials;  combine = c0 + c1 * MB;
+ *   prefill = waves * (ap + bp * tiles per token),
+ * with waves = rounds of workgroups over compute_units and constants fitted
+ * per kernel (format, H > 16) by calibrate_splits.py in the package.
+ * compute_units <= 0 means the current device's.  Returns -1 when T < 1,
+ * H outside [1, 128], topk < 1, the format is unknown or num_splits is
+ * outside [0, 64]. */
+double smla_split_model_cost(int64_t T, int32_t H, int32_t topk, int32_t format, int32_t num_splits,
+                             int32_t compute_units);
+
+/* The split count in [1, min(64, ceil(topk / 64))] with the least predicted
+ * decode + combine time (ties go to the smaller count); -1 on the argument
+ * errors of smla_split_model_cost. */
+int32_t smla_decode_num_splits(int64_t T, int32_t H, int32_t topk, int32_t format, int32_t compute_units);
+
+/* 1 when the split form at smla_decode_num_splits is predicted to take at
+ * most 0.95 of the prefill form's time, 0 when not, -1 on argument errors. */
+int32_t smla_use_split_form(int64_t T, int32_t H, int32_t topk, int32_t format, int32_t compute_units);
+
+/* Workspace smla_attention uses on the current device for this shape: the
+ * smla_decode_workspace_size of the chosen split count when the split form
+ * is chosen, else 0.  T >= 0, H in [1, 128], topk >= 1 (SMLA_ERR_SHAPE),
+ * known format (SMLA_ERR_UNSUPPORTED), bytes_out non-NULL (SMLA_ERR_NULL). */
+smla_status smla_attention_workspace_size(int64_t T, int32_t H, int32_t topk, int32_t format, size_t* bytes_out);
+
+/* Prefill-form result (out, lse as smla_prefill defines them) by whichever
+ * form the split-count model predicts faster on the current device: the
+ * prefill form, or smla_decode at smla_decode_num_splits into `workspace`
+ * followed by smla_combine with the sink.  The split form runs only when
+ * it is chosen and workspace (16-byte aligned, caller-owned, its contents
+ * overwritten) holds at least smla_attention_workspace_size bytes; with a
+ * NULL or smaller workspace the prefill form runs.  Both forms compute the
+ * same values up to rounding order.  Arguments and errors as smla_prefill;
+ * a misaligned workspace is SMLA_ERR_STRIDE. */
+smla_status smla_attention(const void* q, int64_t T, int32_t H, int64_t q_stride_t, int64_t q_stride_h,
+                           smla_kv_pool kv, const int32_t* indices, int32_t topk, int64_t idx_stride_t,
+                           const int32_t* topk_length, const float* sink, float sm_scale, void* out,
+                           int64_t out_stride_t, int64_t out_stride_h, float* lse, int64_t lse_stride_t,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
 /* Message describing the last failed call on this thread ("" if none). */
 const char* smla_last_error(void);
 

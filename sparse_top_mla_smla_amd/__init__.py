@@ -57,7 +57,15 @@ def _load():
                                P, i64, P]
     L.smla_decode.argtypes = [P, i64, i32, i64, i64, _Pool, P, i32, i64, P, f32, i32, P, P, P]
     L.smla_combine.argtypes = [P, P, i64, i32, i32, P, P, i64, i64, P, i64, P]
-    for fn in (L.smla_quantize_kv, L.smla_prefill, L.smla_decode, L.smla_combine):
+    L.smla_split_model_cost.argtypes = [i64, i32, i32, i32, i32, i32]
+    L.smla_split_model_cost.restype = ctypes.c_double
+    L.smla_decode_num_splits.argtypes, L.smla_decode_num_splits.restype = [i64, i32, i32, i32, i32], i32
+    L.smla_use_split_form.argtypes, L.smla_use_split_form.restype = [i64, i32, i32, i32, i32], i32
+    L.smla_attention_workspace_size.argtypes = [i64, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
+    L.smla_attention_workspace_size.restype = ctypes.c_int
+    L.smla_attention.argtypes = [P, i64, i32, i64, i64, _Pool, P, i32, i64, P, P, f32, P, i64, i64,
+                                 P, i64, P, ctypes.c_size_t, P]
+    for fn in (L.smla_quantize_kv, L.smla_prefill, L.smla_decode, L.smla_combine, L.smla_attention):
         fn.restype = ctypes.c_int
     _lib = L
     return L
@@ -81,6 +89,31 @@ def decode_workspace_size(T: int, H: int, num_splits: int) -> int:
     """Bytes of decode scratch (part_out then part_lse) for T tokens."""
     n = ctypes.c_size_t(0)
     _check(_load().smla_decode_workspace_size(T, H, num_splits, ctypes.byref(n)), "smla_decode_workspace_size")
+    return int(n.value)
+
+
+def split_model_cost(T: int, H: int, topk: int, fmt: int, num_splits: int, compute_units: int = 0) -> float:
+    """Predicted microseconds of decode + combine at num_splits, or of the
+    prefill form when num_splits == 0 (see smla_split_model_cost); -1 on
+    argument errors."""
+    return float(_load().smla_split_model_cost(T, H, topk, fmt, num_splits, compute_units))
+
+
+def decode_num_splits(T: int, H: int, topk: int, fmt: int, compute_units: int = 0) -> int:
+    """Split count the model picks for smla_decode (-1 on argument errors)."""
+    return int(_load().smla_decode_num_splits(T, H, topk, fmt, compute_units))
+
+
+def use_split_form(T: int, H: int, topk: int, fmt: int, compute_units: int = 0) -> int:
+    """1 when the model routes this shape to the split form, 0 to prefill."""
+    return int(_load().smla_use_split_form(T, H, topk, fmt, compute_units))
+
+
+def attention_workspace_size(T: int, H: int, topk: int, fmt: int) -> int:
+    """Bytes of workspace smla_attention uses for this shape (0: prefill form)."""
+    n = ctypes.c_size_t(0)
+    _check(_load().smla_attention_workspace_size(T, H, topk, fmt, ctypes.byref(n)),
+           "smla_attention_workspace_size")
     return int(n.value)
 
 
@@ -217,4 +250,37 @@ def combine(part_out: torch.Tensor, part_lse: torch.Tensor, sink: Optional[torch
     _check(_load().smla_combine(_ptr(part_out), _ptr(part_lse), T, S, H, _ptr(sink), _ptr(out),
                                 out.stride(0), out.stride(1), _ptr(lse), lse.stride(0),
                                 _stream(stream)), "smla_combine")
+    return out, lse
+
+
+def attention(q: torch.Tensor, pool: KVPool, indices: torch.Tensor, topk: Optional[int] = None,
+              topk_length: Optional[torch.Tensor] = None, sink: Optional[torch.Tensor] = None,
+              sm_scale: float = 1.0 / 24.0, out: Optional[torch.Tensor] = None,
+              lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+              stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Prefill-form result by the form the split-count model picks (see
+    smla_attention).  workspace: a uint8 device tensor of at least
+    attention_workspace_size bytes, or None (then the prefill form runs)."""
+    _need(q, "q", torch.bfloat16)
+    T, H, _ = q.shape
+    topk, ist = _idx_args(indices, topk)
+    if topk_length is not None:
+        _need(topk_length, "topk_length", torch.int32)
+    if sink is not None:
+        _need(sink, "sink", torch.float32)
+    if out is None:
+        out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.bfloat16)
+    _need(lse, "lse", torch.float32)
+    ws_bytes = 0
+    if workspace is not None:
+        if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+            raise SmlaError("workspace must be a contiguous uint8 tensor")
+        ws_bytes = workspace.numel()
+    _check(_load().smla_attention(_ptr(q), T, H, q.stride(0), q.stride(1), pool.c(), _ptr(indices), topk,
+                                  ist, _ptr(topk_length), _ptr(sink), float(sm_scale), _ptr(out),
+                                  out.stride(0), out.stride(1), _ptr(lse), lse.stride(0), _ptr(workspace),
+                                  ws_bytes, _stream(stream)), "smla_attention")
     return out, lse

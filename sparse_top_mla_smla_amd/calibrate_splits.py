@@ -1,0 +1,219 @@
+"""Measure the split-KV decode, the combine and the prefill form over a grid
+of shapes on the current GPU, and fit the constants of the split-count cost
+model in csrc/split_model.cpp.
+
+FlashInfer PR #4802 ("cpb model") chooses its split geometry from a closed
+form over a few hardware constants, fitted once per device from timings over
+an HBM-sized pool with uniform indices, so that the working set is not
+cache-resident.  This script does the same for this library's kernels:
+
+    decode(T, H, topk, S) = waves * (a + b * tiles_per_block + f * splits_per_block)
+                            + w * partial_MB
+    combine(T, H, S)      = c0 + c1 * partial_MB + c2 * T * H / 1000
+    prefill(T, H, topk)   = waves_p * (ap + bp * tiles_per_token)
+
+with a, b, f, ap, bp per kernel class (format x many-head or narrow
+kernel), w and c0..c2 shared, all in microseconds.  waves counts rounds of
+workgroups over the compute units at the kernel's occupancy.
+
+Usage (needs a GPU; writes JSON to stdout or --out):
+    python -m sparse_top_mla_smla_amd.calibrate_splits --out split_model.json
+"""
+import argparse
+import json
+import math
+import sys
+
+import numpy as np
+import torch
+
+import sparse_top_mla_smla_amd as smla
+from sparse_top_mla_smla_amd import workloads as W
+
+POOL_ROWS = 1 << 20  # 16384 blocks: 656 MiB (FP8/INT8) or 1.1 GiB (BF16), beyond the last-level cache
+
+# kernel class -> (format, head counts measured, workgroups per CU per round,
+# heads per block).  The narrow kernel fits two workgroups in a CU's LDS, but
+# two co-resident workgroups share its four SIMDs and each runs about half as
+# fast, so one round still completes about one workgroup per CU: fitted with
+# 2, the model misses the best split count by up to 26%; with 1, by 4%.
+CLASSES = {
+    "fp8_wide": (W.FMT_FP8, (64, 128), 1, 64),
+    "int8_wide": (W.FMT_INT8, (128,), 1, 64),
+    "fp8_narrow": (W.FMT_FP8, (8, 16), 1, 16),
+    "bf16_narrow": (W.FMT_BF16, (8,), 1, 16),
+    "int8_narrow": (W.FMT_INT8, (8,), 1, 16),
+}
+T_GRID = (1, 2, 4, 8, 16, 32, 64, 128, 256)
+TOPK_GRID = (512, 2048)
+S_GRID = (1, 2, 4, 8, 16, 32)
+
+
+def geometry(cls: str, T: int, H: int, topk: int, S: int, cus: int):
+    """(waves, tiles of the longest block, splits per block, partial MB) of
+    a decode launch, following the launchers' grid rules."""
+    _, _, occ, hpb = CLASSES[cls]
+    hb = (H + hpb - 1) // hpb
+    w = smla.split_width(topk, S)
+    spb = 1
+    if cls.endswith("_wide") and cls.startswith("fp8"):
+        spb = max(1, min(S, (T * hb * S) // cus))
+    blocks = T * hb * ((S + spb - 1) // spb)
+    waves = math.ceil(blocks / (cus * occ))
+    tiles = math.ceil(min(spb * w, topk) / 64)
+    mb = T * S * H * (512 * 4 + 4) / 1e6
+    return waves, tiles, spb, mb
+
+
+def prefill_geometry(cls: str, T: int, H: int, topk: int, cus: int):
+    _, _, occ, hpb = CLASSES[cls]
+    hb = (H + hpb - 1) // hpb
+    return math.ceil(T * hb / (cus * occ)), math.ceil(topk / 64)
+
+
+def timed(fn, sets, warmup=3, iters=9):
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    out = []
+    for it in range(warmup + iters):
+        x = sets[it % len(sets)]
+        ev0.record()
+        fn(x)
+        ev1.record()
+        torch.cuda.synchronize()
+        if it >= warmup:
+            out.append(ev0.elapsed_time(ev1) * 1000.0)
+    return float(np.median(out))
+
+
+def measure(cus: int, log):
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1234)
+    pools = {}
+    for fmt in (W.FMT_FP8, W.FMT_INT8, W.FMT_BF16):
+        pool = smla.KVPool.empty(POOL_ROWS // 64, fmt)
+        for r0 in range(0, POOL_ROWS, 1 << 18):
+            kv = torch.randn((1 << 18, 576), generator=gen, device="cuda").to(torch.bfloat16)
+            slots = torch.arange(r0, r0 + (1 << 18), dtype=torch.int32, device="cuda")
+            smla.quantize_kv(kv, slots, pool)
+        pools[fmt] = pool
+    torch.cuda.synchronize()
+    rows = []
+    for cls, (fmt, heads, _, _) in CLASSES.items():
+        for H in heads:
+            for topk in TOPK_GRID:
+                for T in T_GRID:
+                    q = torch.randn((T, H, 576), generator=gen, device="cuda").to(torch.bfloat16)
+                    sets = [torch.randint(0, POOL_ROWS, (T, topk), generator=gen, device="cuda", dtype=torch.int32)
+                            for _ in range(3)]
+                    out = torch.empty((T, H, 512), dtype=torch.bfloat16, device="cuda")
+                    lse = torch.empty((T, H), dtype=torch.float32, device="cuda")
+                    pool = pools[fmt]
+                    tp = timed(lambda x: smla.prefill(q, pool, x, out=out, lse=lse), sets)
+                    rows.append(dict(kind="prefill", cls=cls, T=T, H=H, topk=topk, us=tp))
+                    for S in S_GRID:
+                        if S > topk // 64:
+                            continue
+                        po = torch.empty((T, S, H, 512), dtype=torch.float32, device="cuda")
+                        pl = torch.empty((T, S, H), dtype=torch.float32, device="cuda")
+                        td = timed(lambda x: smla.decode(q, pool, x, S, part_out=po, part_lse=pl), sets)
+                        tc = timed(lambda x: smla.combine(po, pl, out=out, lse=lse), [None])
+                        rows.append(dict(kind="decode", cls=cls, T=T, H=H, topk=topk, S=S, us=td, combine_us=tc))
+                    log(f"{cls} H={H} topk={topk} T={T}: prefill {tp:.1f} us")
+    return rows
+
+
+def fit(rows, cus: int):
+    """Least-squares constants; a negative fitted term is clamped to 0 and
+    the rest refit (the NNLS step of FlashInfer PR #4802's calibration)."""
+    def lsq(X, y):
+        X = np.asarray(X, float)
+        y = np.asarray(y, float)
+        active = list(range(X.shape[1]))
+        coef = np.zeros(X.shape[1])
+        while active:
+            c, *_ = np.linalg.lstsq(X[:, active], y, rcond=None)
+            if (c >= 0).all():
+                coef[active] = c
+                break
+            active.pop(int(np.argmin(c)))
+        return coef
+
+    dec = [r for r in rows if r["kind"] == "decode"]
+    # shared partial-write cost and per-class block constants, fitted jointly
+    classes = list(CLASSES)
+    X, y = [], []
+    for r in dec:
+        waves, tiles, spb, mb = geometry(r["cls"], r["T"], r["H"], r["topk"], r["S"], cus)
+        k = classes.index(r["cls"])
+        row = [0.0] * (3 * len(classes) + 1)
+        row[3 * k + 0] = waves
+        row[3 * k + 1] = waves * tiles
+        row[3 * k + 2] = waves * spb
+        row[-1] = mb
+        X.append(row)
+        y.append(r["us"])
+    c = lsq(X, y)
+    consts = {cls: dict(a=c[3 * k], b=c[3 * k + 1], f=c[3 * k + 2]) for k, cls in enumerate(classes)}
+    w = c[-1]
+    Xc = [[1.0, T * S * H * 2052 / 1e6, T * H / 1000.0] for T, S, H in ((r["T"], r["S"], r["H"]) for r in dec)]
+    cc = lsq(Xc, [r["combine_us"] for r in dec])
+    for cls in classes:
+        pre = [r for r in rows if r["kind"] == "prefill" and r["cls"] == cls]
+        Xp = []
+        for r in pre:
+            waves, tiles = prefill_geometry(cls, r["T"], r["H"], r["topk"], cus)
+            Xp.append([waves, waves * tiles])
+        cp = lsq(Xp, [r["us"] for r in pre])
+        consts[cls].update(ap=cp[0], bp=cp[1])
+    return dict(classes=consts, w_us_per_MB=w, combine=dict(c0=cc[0], c1=cc[1], c2=cc[2]))
+
+
+def predict(model, cls, T, H, topk, S, cus):
+    k = model["classes"][cls]
+    waves, tiles, spb, mb = geometry(cls, T, H, topk, S, cus)
+    dec = waves * (k["a"] + k["b"] * tiles + k["f"] * spb) + model["w_us_per_MB"] * mb
+    cm = model["combine"]
+    com = cm["c0"] + cm["c1"] * T * S * H * 2052 / 1e6 + cm["c2"] * T * H / 1000.0
+    return dec + com
+
+
+def evaluate(model, rows, cus):
+    """Pick error of the model against the measured best split count, per
+    (class, T, H, topk): measured time of the model's pick / measured best."""
+    groups = {}
+    for r in rows:
+        if r["kind"] == "decode":
+            groups.setdefault((r["cls"], r["T"], r["H"], r["topk"]), {})[r["S"]] = r["us"] + r["combine_us"]
+    ratios = []
+    for (cls, T, H, topk), by_s in groups.items():
+        pick = min(by_s, key=lambda S: (predict(model, cls, T, H, topk, S, cus), S))
+        ratios.append(by_s[pick] / min(by_s.values()))
+    return dict(mean=float(np.mean(ratios)), max=float(np.max(ratios)), shapes=len(ratios))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--out", default="", help="write the JSON here instead of stdout")
+    ap.add_argument("--refit", default="", metavar="JSON",
+                    help="fit again from the measurements stored in a JSON this script wrote (no GPU)")
+    args = ap.parse_args()
+    if args.refit:
+        with open(args.refit) as f:
+            old = json.load(f)
+        device, cus, rows = old["device"], old["compute_units"], old["rows"]
+    else:
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        device = torch.cuda.get_device_name(0) or "gpu"
+        rows = measure(cus, lambda s: print(s, file=sys.stderr, flush=True))
+    model = fit(rows, cus)
+    res = dict(device=device, compute_units=cus, model=model, pick_error=evaluate(model, rows, cus), rows=rows)
+    text = json.dumps(res, indent=1)
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(text)
+    else:
+        print(text)
+
+
+if __name__ == "__main__":
+    main()

@@ -249,3 +249,45 @@ smla_status smla_combine(const float* part_out, const float* part_lse, int64_t T
 }
 
 }  // extern "C"
+
+smla_status smla_attention_workspace_size(int64_t T, int32_t H, int32_t topk, int32_t format, size_t* bytes_out) {
+  if (!bytes_out) return fail(SMLA_ERR_NULL, "bytes_out is NULL");
+  if (T < 0 || T > INT32_MAX) return fail(SMLA_ERR_SHAPE, "T = %lld is outside [0, 2^31-1]", (long long)T);
+  if (H < 1 || H > 128) return fail(SMLA_ERR_SHAPE, "H = %d is outside [1, 128]", H);
+  if (topk < 1) return fail(SMLA_ERR_SHAPE, "topk = %d must be >= 1", topk);
+  if (smla_row_bytes(format) < 0) return fail(SMLA_ERR_UNSUPPORTED, "kv format %d is not supported", format);
+  *bytes_out = 0;
+  if (T == 0 || smla_use_split_form(T, H, topk, format, 0) != 1) return ok();
+  return smla_decode_workspace_size(T, H, smla_decode_num_splits(T, H, topk, format, 0), bytes_out);
+}
+
+smla_status smla_attention(const void* q, int64_t T, int32_t H, int64_t q_stride_t, int64_t q_stride_h,
+                           smla_kv_pool kv, const int32_t* indices, int32_t topk, int64_t idx_stride_t,
+                           const int32_t* topk_length, const float* sink, float sm_scale, void* out,
+                           int64_t out_stride_t, int64_t out_stride_h, float* lse, int64_t lse_stride_t,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  // both forms validate the same way before anything is chosen
+  smla_status st = check_attn_common(q, T, H, q_stride_t, q_stride_h, kv, indices, topk, idx_stride_t);
+  if (st != SMLA_OK) return st;
+  if (T == 0) return ok();
+  st = check_out(out, out_stride_t, out_stride_h, H, lse, lse_stride_t);
+  if (st != SMLA_OK) return st;
+  if (!std::isfinite(sm_scale)) return fail(SMLA_ERR_SHAPE, "sm_scale must be finite");
+  if (workspace && !aligned(workspace, 16)) return fail(SMLA_ERR_STRIDE, "workspace is not 16-byte aligned");
+  int32_t S = 0;
+  if (workspace && smla_use_split_form(T, H, topk, kv.format, 0) == 1) {
+    S = smla_decode_num_splits(T, H, topk, kv.format, 0);
+    size_t need = 0;
+    if (smla_decode_workspace_size(T, H, S, &need) != SMLA_OK || need > workspace_bytes) S = 0;
+  }
+  if (S == 0)
+    return smla_prefill(q, T, H, q_stride_t, q_stride_h, kv, indices, topk, idx_stride_t, topk_length, sink,
+                        sm_scale, out, out_stride_t, out_stride_h, lse, lse_stride_t, stream);
+  float* part_out = static_cast<float*>(workspace);
+  float* part_lse = part_out + (size_t)T * (size_t)S * (size_t)H * 512;
+  st = smla_decode(q, T, H, q_stride_t, q_stride_h, kv, indices, topk, idx_stride_t, topk_length, sm_scale, S,
+                   part_out, part_lse, stream);
+  if (st != SMLA_OK) return st;
+  return smla_combine(part_out, part_lse, T, S, H, sink, out, out_stride_t, out_stride_h, lse, lse_stride_t,
+                      stream);
+}

@@ -555,8 +555,8 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
   }
 }
 
-// compute units of the current device, looked up once per device
-static int compute_units() {
+// looked up once per device
+int device_compute_units() {
   static int cached[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
@@ -568,18 +568,19 @@ static int compute_units() {
   return cached[dev];
 }
 
+// One workgroup takes several consecutive splits of a token when there are
+// more (token, split) pairs than compute units: the gather pipeline and Q
+// carry across the split boundary, and the grid fills the chip about once
+// instead of leaving a ragged second round.
+int fp8_splits_per_block(int64_t T, int32_t H, int32_t num_splits, int compute_units) {
+  const int64_t pairs = T * (int64_t)((H + 63) / 64) * num_splits;
+  const int64_t g = pairs / (compute_units > 0 ? compute_units : 1);
+  return (int)(g < 1 ? 1 : (g > num_splits ? num_splits : g));
+}
+
 hipError_t launch_attention_fp8(const AttnParams& p, bool decode, hipStream_t s) {
   AttnParams q = p;
-  q.splits_per_block = 1;
-  if (decode) {
-    // One workgroup takes several consecutive splits of a token when there
-    // are more (token, split) pairs than compute units: the gather pipeline
-    // and Q carry across the split boundary, and the grid fills the chip
-    // about once instead of leaving a ragged second wave.
-    const int64_t pairs = p.T * (int64_t)((p.H + 63) / 64) * p.num_splits;
-    int64_t g = pairs / compute_units();
-    q.splits_per_block = (int)(g < 1 ? 1 : (g > p.num_splits ? p.num_splits : g));
-  }
+  q.splits_per_block = decode ? fp8_splits_per_block(p.T, p.H, p.num_splits, device_compute_units()) : 1;
   dim3 block(f8::NT);
   dim3 grid((unsigned)q.T, (unsigned)((q.H + 63) / 64),
             decode ? (unsigned)((q.num_splits + q.splits_per_block - 1) / q.splits_per_block) : 1u);

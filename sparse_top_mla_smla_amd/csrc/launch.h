@@ -62,4 +62,11 @@ hipError_t launch_attention_wide(const AttnParams& p, int fmt, bool decode, hipS
 hipError_t launch_attention_fp8(const AttnParams& p, bool decode, hipStream_t s);
 hipError_t launch_combine(const CombineParams& p, hipStream_t s);
 
+// compute units of the current device (256 when it cannot be queried)
+int device_compute_units();
+// consecutive decode splits one workgroup of the FP8 many-head kernel runs:
+// about one workgroup per compute unit when (token, split) pairs outnumber
+// the units
+int fp8_splits_per_block(int64_t T, int32_t H, int32_t num_splits, int compute_units);
+
 }  // namespace smla

@@ -1,0 +1,129 @@
+// split_model.cpp -- the decode split count and the choice between the split
+// form (decode + combine) and the prefill form, from a cost model fitted on
+// MI355X.
+//
+// FlashInfer PR #4802 ("cpb model" and "Crossover" in its description)
+// replaces a per-shape tuning sweep with a closed form over a few hardware
+// constants, fitted once per device from timings over an HBM-sized pool,
+// and routes small-T prefill to the split form when that form is predicted
+// at most 0.95x the prefill time.  Here the terms follow this library's
+// launch geometry:
+//   decode  = waves * (a + b * tiles_per_block + f * splits_per_block) + w * MB
+//   combine = c0 + c1 * MB + c2 * T * H / 1000
+//   prefill = waves_p * (ap + bp * tiles_per_token)
+// with MB the partial buffers (T * S * H * 2052 bytes), waves the rounds of
+// workgroups over the compute units (one workgroup per CU per round: the
+// many-head kernels fill a CU's LDS, and two co-resident narrow workgroups
+// share the CU's SIMDs), and a, b, f, ap, bp per kernel class.  The
+// constants were fitted by sparse_top_mla_smla_amd/calibrate_splits.py on
+// one MI355X (256 CUs) over 126 decode shapes; there the pick is on average
+// 0.1% and at most 4.1% slower than the best measured split count.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+
+#include "launch.h"
+#include "smla.h"
+
+namespace smla {
+namespace {
+
+struct KernelClass {
+  double a, b, f;  // decode: per block, per tile of the longest block, per split it finishes (us)
+  double ap, bp;   // prefill: per block, per tile (us)
+  int heads_per_block;
+  bool grouped;    // consecutive splits per workgroup (the FP8 many-head kernel)
+};
+
+// fitted constants (microseconds), MI355X
+constexpr KernelClass kFp8Wide{13.80, 2.873, 3.100, 17.84, 2.890, 64, true};
+constexpr KernelClass kInt8Wide{4.704, 4.939, 4.704, 16.04, 4.851, 64, false};
+constexpr KernelClass kFp8Narrow{3.629, 4.033, 3.629, 16.69, 3.487, 16, false};
+constexpr KernelClass kBf16Narrow{3.683, 4.589, 3.683, 16.42, 4.027, 16, false};
+constexpr KernelClass kInt8Narrow{3.472, 4.271, 3.472, 16.21, 3.742, 16, false};
+constexpr double kWriteUsPerMB = 0.1444;  // decode's partial stores
+constexpr double kComb0 = 11.00, kComb1 = 0.1853, kComb2 = 0.0;
+constexpr double kPartialBytesPerRow = 512 * 4 + 4;
+constexpr double kCrossover = 0.95;  // split form only when at most this fraction of prefill
+
+const KernelClass* kernel_class(int32_t format, int32_t H) {
+  // the dispatch rule of launch_attention
+  switch (format) {
+    case SMLA_KV_FP8_E4M3: return H > 16 ? &kFp8Wide : &kFp8Narrow;
+    case SMLA_KV_INT8: return H > 16 ? &kInt8Wide : &kInt8Narrow;
+    case SMLA_KV_BF16: return &kBf16Narrow;
+    default: return nullptr;
+  }
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+double split_cost(const KernelClass& c, int64_t T, int32_t H, int32_t topk, int32_t S, int cus) {
+  const int64_t hb = ceil_div(H, c.heads_per_block);
+  const int64_t w = smla_split_width(topk, S);
+  const int64_t spb = c.grouped ? fp8_splits_per_block(T, H, S, cus) : 1;
+  const int64_t blocks = T * hb * ceil_div(S, spb);
+  const double waves = (double)ceil_div(blocks, cus);
+  const double tiles = (double)ceil_div(std::min<int64_t>(spb * w, topk), 64);
+  const double mb = (double)T * S * H * kPartialBytesPerRow / 1e6;
+  const double decode = waves * (c.a + c.b * tiles + c.f * (double)spb) + kWriteUsPerMB * mb;
+  const double combine = kComb0 + kComb1 * mb + kComb2 * (double)T * H / 1000.0;
+  return decode + combine;
+}
+
+double prefill_cost(const KernelClass& c, int64_t T, int32_t H, int32_t topk, int cus) {
+  const double waves = (double)ceil_div(T * ceil_div(H, c.heads_per_block), cus);
+  return waves * (c.ap + c.bp * (double)ceil_div(topk, 64));
+}
+
+int max_splits(int32_t topk) { return (int)std::min<int64_t>(64, ceil_div(topk, 64)); }
+
+bool valid(int64_t T, int32_t H, int32_t topk, int32_t format) {
+  return T >= 1 && T <= INT32_MAX && H >= 1 && H <= 128 && topk >= 1 && kernel_class(format, H) != nullptr;
+}
+
+int resolve_cus(int32_t compute_units) { return compute_units > 0 ? compute_units : device_compute_units(); }
+
+int best_splits(const KernelClass& c, int64_t T, int32_t H, int32_t topk, int cus, double* cost) {
+  int best = 1;
+  double best_cost = split_cost(c, T, H, topk, 1, cus);
+  for (int S = 2; S <= max_splits(topk); ++S) {
+    const double v = split_cost(c, T, H, topk, S, cus);
+    if (v < best_cost) {  // ties keep the smaller split count
+      best = S;
+      best_cost = v;
+    }
+  }
+  if (cost) *cost = best_cost;
+  return best;
+}
+
+}  // namespace
+}  // namespace smla
+
+extern "C" {
+
+double smla_split_model_cost(int64_t T, int32_t H, int32_t topk, int32_t format, int32_t num_splits,
+                             int32_t compute_units) {
+  if (!smla::valid(T, H, topk, format) || num_splits < 0 || num_splits > 64) return -1.0;
+  const smla::KernelClass& c = *smla::kernel_class(format, H);
+  const int cus = smla::resolve_cus(compute_units);
+  return num_splits == 0 ? smla::prefill_cost(c, T, H, topk, cus) : smla::split_cost(c, T, H, topk, num_splits, cus);
+}
+
+int32_t smla_decode_num_splits(int64_t T, int32_t H, int32_t topk, int32_t format, int32_t compute_units) {
+  if (!smla::valid(T, H, topk, format)) return -1;
+  return smla::best_splits(*smla::kernel_class(format, H), T, H, topk, smla::resolve_cus(compute_units), nullptr);
+}
+
+int32_t smla_use_split_form(int64_t T, int32_t H, int32_t topk, int32_t format, int32_t compute_units) {
+  if (!smla::valid(T, H, topk, format)) return -1;
+  const smla::KernelClass& c = *smla::kernel_class(format, H);
+  const int cus = smla::resolve_cus(compute_units);
+  double split = 0.0;
+  smla::best_splits(c, T, H, topk, cus, &split);
+  return split <= smla::kCrossover * smla::prefill_cost(c, T, H, topk, cus) ? 1 : 0;
+}
+
+}  // extern "C"

@@ -1,0 +1,127 @@
+"""The split-count model without a GPU: the library's cost equals the
+calibration script's formula with the fitted constants, its picks on the
+committed MI355X measurements are close to the measured best, the pick and
+the routing rule follow from the cost, and the routing entry point validates
+its arguments before anything is chosen or launched."""
+import ctypes
+import json
+import os
+from collections import defaultdict
+
+import pytest
+
+import sparse_top_mla_smla_amd as smla
+from sparse_top_mla_smla_amd import calibrate_splits as C
+from sparse_top_mla_smla_amd import workloads as W
+
+FIT = json.load(open(os.path.join(os.path.dirname(smla.__file__), "split_model_fit.json")))
+CUS = 256
+FAKE = 0x10000
+
+
+def fmt_of(cls):
+    return C.CLASSES[cls][0]
+
+
+def groups():
+    g = defaultdict(dict)
+    for r in FIT["rows"]:
+        if r["kind"] == "decode":
+            g[(r["cls"], r["T"], r["H"], r["topk"])][r["S"]] = r["us"] + r["combine_us"]
+    return g
+
+
+def test_fit_was_taken_on_this_chip_class():
+    assert FIT["compute_units"] == CUS
+    assert len(groups()) == FIT["pick_error"]["shapes"]
+
+
+@pytest.mark.parametrize("cls", sorted(C.CLASSES))
+def test_library_cost_is_the_calibration_formula(cls):
+    model = FIT["model"]
+    for r in FIT["rows"]:
+        if r["cls"] != cls:
+            continue
+        fmt = fmt_of(cls)
+        if r["kind"] == "decode":
+            want = C.predict(model, cls, r["T"], r["H"], r["topk"], r["S"], CUS)
+            got = smla.split_model_cost(r["T"], r["H"], r["topk"], fmt, r["S"], CUS)
+        else:
+            waves, tiles = C.prefill_geometry(cls, r["T"], r["H"], r["topk"], CUS)
+            k = model["classes"][cls]
+            want = waves * (k["ap"] + k["bp"] * tiles)
+            got = smla.split_model_cost(r["T"], r["H"], r["topk"], fmt, 0, CUS)
+        # the library holds the constants to four significant digits
+        assert got == pytest.approx(want, rel=2e-3), (r, got, want)
+
+
+def test_pick_error_on_the_measurements():
+    """Among the measured split counts, the one the library's cost ranks
+    first is on average within 2% and at worst within 10% of the measured
+    best (FlashInfer PR #4802 reports 1.011x mean and 1.061x max for its
+    model)."""
+    ratios = []
+    for (cls, T, H, topk), by_s in groups().items():
+        fmt = fmt_of(cls)
+        pick = min(by_s, key=lambda S: (smla.split_model_cost(T, H, topk, fmt, S, CUS), S))
+        ratios.append(by_s[pick] / min(by_s.values()))
+    assert sum(ratios) / len(ratios) <= 1.02
+    assert max(ratios) <= 1.10
+
+
+@pytest.mark.parametrize("fmt,H", [(W.FMT_FP8, 64), (W.FMT_FP8, 128), (W.FMT_INT8, 128), (W.FMT_FP8, 8),
+                                   (W.FMT_BF16, 8), (W.FMT_BF16, 64), (W.FMT_INT8, 16), (W.FMT_FP8, 20)])
+@pytest.mark.parametrize("T,topk", [(1, 64), (1, 2048), (7, 640), (64, 2048), (300, 512), (4096, 1024)])
+def test_pick_and_route_follow_from_the_cost(fmt, H, T, topk):
+    s_max = min(64, -(-topk // 64))
+    costs = [smla.split_model_cost(T, H, topk, fmt, S, CUS) for S in range(1, s_max + 1)]
+    assert all(c > 0 for c in costs)
+    best = min(range(s_max), key=lambda i: (costs[i], i)) + 1
+    assert smla.decode_num_splits(T, H, topk, fmt, CUS) == best
+    prefill = smla.split_model_cost(T, H, topk, fmt, 0, CUS)
+    assert smla.use_split_form(T, H, topk, fmt, CUS) == int(costs[best - 1] <= 0.95 * prefill)
+
+
+def test_routes_few_tokens_to_the_split_form():
+    # one token over 2048 candidates: one workgroup per token leaves the chip idle
+    assert smla.use_split_form(1, 64, 2048, W.FMT_FP8, CUS) == 1
+    assert smla.decode_num_splits(1, 64, 2048, W.FMT_FP8, CUS) >= 16
+    # the decode batch of 64 sequences: about one workgroup per compute unit
+    assert smla.decode_num_splits(64, 64, 2048, W.FMT_FP8, CUS) == 4
+    # a full prefill batch fills the chip by itself
+    assert smla.use_split_form(1024, 64, 1024, W.FMT_FP8, CUS) == 0
+    # short lists: the split form's fixed costs never pay
+    assert smla.use_split_form(4, 64, 128, W.FMT_FP8, CUS) == 0
+
+
+def test_argument_errors():
+    for args in ((0, 64, 64, 1, 1), (1, 0, 64, 1, 1), (1, 129, 64, 1, 1), (1, 64, 0, 1, 1), (1, 64, 64, 7, 1),
+                 (1, 64, 64, 1, -1), (1, 64, 64, 1, 65)):
+        assert smla.split_model_cost(*args, CUS) == -1.0
+    assert smla.decode_num_splits(1, 64, 0, 1, CUS) == -1
+    assert smla.use_split_form(1, 0, 64, 1, CUS) == -1
+    lib = smla._load()
+    assert lib.smla_attention_workspace_size(1, 64, 64, 1, None) == 1            # NULL bytes_out
+    n = ctypes.c_size_t(99)
+    assert lib.smla_attention_workspace_size(0, 64, 64, 1, ctypes.byref(n)) == 0 and n.value == 0
+    assert lib.smla_attention_workspace_size(1, 0, 64, 1, ctypes.byref(n)) == 2
+    assert lib.smla_attention_workspace_size(1, 64, 0, 1, ctypes.byref(n)) == 2
+    assert lib.smla_attention_workspace_size(1, 64, 64, 9, ctypes.byref(n)) == 4
+
+
+def test_attention_validation_before_launch():
+    lib = smla._load()
+    pool = smla._Pool(FAKE, 4, 64 * 656, 64, W.FMT_FP8)
+
+    def call(q=FAKE, T=2, H=64, ws=None, ws_bytes=0, out=FAKE, lse=FAKE, topk=64):
+        return lib.smla_attention(q, T, H, 64 * 576, 576, pool, FAKE, topk, 64, None, None, ctypes.c_float(1 / 24),
+                                  out, 64 * 512, 512, lse, 64, ws, ws_bytes, None)
+
+    assert call(T=0, q=None, out=None, lse=None) == 0
+    assert call(q=None) == 1
+    assert call(out=None) == 1
+    assert call(H=0) == 2
+    assert call(H=129) == 4
+    assert call(topk=0) == 2
+    assert call(ws=FAKE + 8, ws_bytes=1 << 20) == 3                              # misaligned workspace
+    assert "workspace" in lib.smla_last_error().decode()
