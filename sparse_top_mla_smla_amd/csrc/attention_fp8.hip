@@ -165,44 +165,64 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  const int64_t t = blockIdx.x;
   const int h0 = blockIdx.y * 64;
-  // decode: this workgroup covers splits [sp0, sp_end) as one list, with a
-  // partial result at the end of each split
+  // decode: this workgroup covers splits [sp0, sp_end) of token blockIdx.x
+  // as one list, with a partial result at the end of each split
   const int sp0 = DECODE ? (int)blockIdx.z * p.splits_per_block : 0;
   const int sp_end = DECODE ? min(sp0 + p.splits_per_block, p.num_splits) : 1;
+  const int32_t t_stride = gridDim.x;
 
-  int64_t L = p.topk;
-  if (p.topk_length) {
-    const int64_t v = p.topk_length[t];
-    L = v < 0 ? 0 : (v > p.topk ? p.topk : v);
-  }
-  int64_t j_begin = 0, j_end = p.topk;
-  if (DECODE) {
-    j_begin = (int64_t)sp0 * p.split_w;
-    j_end = (int64_t)sp_end * p.split_w;
-    if (j_end > p.topk) j_end = p.topk;
-  }
-  if (j_end > L) j_end = L;
-  const int n_tiles = j_end > j_begin ? (int)((j_end - j_begin + TC - 1) / TC) : 0;
-
-  // list entry k*64 + lane of this workgroup's range: its index value, and
-  // the byte offset in the pool of its row (-1: masked or not a pool slot)
-  const int32_t* idx_row = p.idx + t * p.idx_st;
-  auto load_entry = [&](int k) -> int32_t {
-    const int64_t j = j_begin + (int64_t)k * TC + lane;
-    return j < j_end ? idx_row[j] : -1;
+  // end of token tt's candidate range: its list length clamped to [0, topk]
+  // (read through the scalar cache: a vector load would make the wait for
+  // it also wait for the gathers in flight)
+  auto list_end = [&](int32_t tt) -> int32_t {
+    if (!p.topk_length) return p.topk;
+    const int32_t v = *(const __attribute__((address_space(4))) int32_t*)(p.topk_length + tt);
+    return v < 0 ? 0 : (v > p.topk ? p.topk : v);
   };
+  // A tile is list positions [j0, j0 + 64) of token t, cut at jend (t < 0:
+  // no tile; T and topk fit in 31 bits).  Prefill: the workgroup takes tokens blockIdx.x,
+  // blockIdx.x + gridDim.x, ... and its tile pipeline (gather one tile
+  // ahead, index list two tiles ahead) runs on across token boundaries, so
+  // no token pays for filling it.  Decode: the tiles of one token's split
+  // range.
+  struct TileRef {
+    int32_t t, j0, jend;
+  };
+  const TileRef none{-1, 0, 0};
+  auto first_tile = [&](int32_t t0) -> TileRef {
+    if (DECODE) {
+      const int64_t jb = (int64_t)sp0 * p.split_w;
+      int64_t je = (int64_t)sp_end * p.split_w;
+      if (je > p.topk) je = p.topk;
+      const int32_t L = list_end(t0);
+      if (je > L) je = L;
+      return je > jb ? TileRef{t0, (int32_t)jb, (int32_t)je} : none;
+    }
+    for (int32_t tt = t0; tt < p.T; tt += t_stride) {
+      const int32_t je = list_end(tt);
+      if (je > 0) return TileRef{tt, 0, je};
+    }
+    return none;
+  };
+  auto advance = [&](const TileRef& r) -> TileRef {
+    if (r.t < 0) return none;
+    if (r.j0 + TC < r.jend) return TileRef{r.t, r.j0 + TC, r.jend};
+    return DECODE ? none : first_tile(r.t + t_stride);
+  };
+
+  // byte offset in the pool of the row of index value x (-1: masked or not
+  // a pool slot)
   auto row_offset = [&](int32_t x) -> int64_t {
     return (x >= 0 && (int64_t)x < p.nslots) ? (int64_t)(x / PAGE) * p.block_stride + (int64_t)(x % PAGE) * RB
                                              : (int64_t)-1;
   };
-  // wave 0 moves the index list entries of tile k into index buffer B
+  // wave 0 moves the index list entries of tile r into index buffer B
   // (entries past the range are not loaded; readers check the range)
-  auto issue_idx = [&](auto buf, int k) {
+  auto issue_idx = [&](auto buf, const TileRef& r) {
     constexpr int B = decltype(buf)::value;
-    const int64_t j = j_begin + (int64_t)k * TC + lane;
-    if (j < j_end) global_to_lds_4(idx_row + j, B ? idx1 : idx0);
+    const int32_t j = r.j0 + lane;
+    if (j < r.jend) global_to_lds_4(p.idx + (int64_t)r.t * p.idx_st + j, B ? idx1 : idx0);
   };
   // wave w moves pieces w, w + 8, ... of all 64 rows of a tile (lane = row)
   // into raw buffer B, in part P (0..2) the pieces of rounds 2P and 2P + 1.
@@ -224,25 +244,15 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
   };
   static_assert(2 * GPARTS == GROUNDS, "three parts of two rounds");
 
-  // the first index entry is loaded before Q, so the first gather waits
-  // only for it
-  // (an unconditional load of an entry inside the range, selected after)
-  int32_t entry0 = -1;
-  if (n_tiles > 0) {
-    const int64_t j = j_begin + lane;
-    const int32_t x = idx_row[j < j_end ? j : j_end - 1];
-    entry0 = j < j_end ? x : -1;
-  }
-
   // Q as the B operand of S^T = K Q^T for head h0 + 32hh + l32.  A K lane
   // reads one 16-byte piece (8g + 2j + hi) that feeds MFMA steps 2j and
   // 2j+1, so qn[2j + b] holds nope columns 128g + 32j + 16hi + 8b + i; qr
   // holds rope columns 16g + 8hi + i.
   bf16x8 qn[8], qr;
-  {
+  auto load_q = [&](int32_t tq) {
     const int h = h0 + 32 * hh + l32;
     const bool hv = h < p.H;
-    const uint16_t* qrow = p.q + t * p.q_st + (int64_t)(hv ? h : 0) * p.q_sh;
+    const uint16_t* qrow = p.q + (int64_t)tq * p.q_st + (int64_t)(hv ? h : 0) * p.q_sh;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -254,7 +264,26 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
       }
     const uint4 v = *reinterpret_cast<const uint4*>(qrow + D_NOPE + 16 * g + 8 * hi);
     qr = __builtin_bit_cast(bf16x8, hv ? v : make_uint4(0, 0, 0, 0));
+  };
+
+  TileRef cur = first_tile((int32_t)blockIdx.x);
+  TileRef nxt = advance(cur);
+  TileRef nn = advance(nxt);
+  // the first tile's index entries (an unconditional load of an entry
+  // inside the range, selected after), then Q: the compiler barrier keeps
+  // the Q loads behind the wait for the entries, so they are in flight
+  // during the zero fill and the first gather instead of delaying its issue
+  int32_t entry0 = -1;
+  if (cur.t >= 0) {
+    const int32_t j = cur.j0 + lane;
+    const int32_t x = p.idx[(int64_t)cur.t * p.idx_st + (j < cur.jend ? j : cur.jend - 1)];
+    entry0 = j < cur.jend ? x : -1;
   }
+  asm volatile("" ::: "memory");
+  if (cur.t >= 0) load_q(cur.t);
+
+  // sink of head h0 + 32hh + l32 in exp2 units (prefill), loaded once
+  float sink2 = 0.0f;
 
   // softmax state for heads 32hh + l32 (identical in the four waves of hh)
   float m_run = -INFINITY;
@@ -266,67 +295,91 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) O[dt][i] = 0.0f;
 
-  if (n_tiles > 0) {
+  // A finished result (a split's partial, or a token's output) whose O is
+  // kept in registers is stored by the next tile, after that tile's gather
+  // is issued, so the stores drain during a tile instead of inside its
+  // first wait.
+  int32_t pend = -1;  // split (decode) or token (prefill) still to be stored
+  float pend_factor = 0.0f, pend_lse = 0.0f;
+  auto store_result = [&](int32_t key, float factor, float lse_v) {
+    const int h = h0 + 32 * hh + l32;
+    if (h >= p.H) return;
+    if constexpr (DECODE) {
+      const int64_t td = blockIdx.x;
+      float* po = p.part_out + ((td * p.num_splits + key) * p.H + h) * (int64_t)D_V + 128 * g + 4 * hi;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *reinterpret_cast<f32x4*>(po + 32 * dt + 8 * q4) =
+              f32x4{O[dt][4 * q4] * factor, O[dt][4 * q4 + 1] * factor, O[dt][4 * q4 + 2] * factor,
+                    O[dt][4 * q4 + 3] * factor};
+      if (g == 0 && hi == 0) p.part_lse[(td * p.num_splits + key) * p.H + h] = lse_v;
+    } else {
+      uint16_t* orow = p.out + (int64_t)key * p.out_st + (int64_t)h * p.out_sh + 128 * g + 4 * hi;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * q4) =
+              make_uint2(pack_bf16(O[dt][4 * q4] * factor, O[dt][4 * q4 + 1] * factor),
+                         pack_bf16(O[dt][4 * q4 + 2] * factor, O[dt][4 * q4 + 3] * factor));
+      if (g == 0 && hi == 0) p.lse[(int64_t)key * p.lse_st + h] = lse_v;
+    }
+  };
+
+  // prefill: the workgroup's tokens with an empty list (O is still zero)
+  if (!DECODE && p.topk_length) {
+    for (int32_t tt = blockIdx.x; tt < p.T; tt += t_stride)
+      if (list_end(tt) == 0) store_result(tt, 0.0f, -INFINITY);
+  }
+
+  if (cur.t >= 0) {
     for (int i = tid; i < TILE / 16; i += NT) {
       reinterpret_cast<uint4*>(raw0)[i] = make_uint4(0, 0, 0, 0);
       reinterpret_cast<uint4*>(raw1)[i] = make_uint4(0, 0, 0, 0);
     }
     const int64_t off0 = row_offset(entry0);
-    // the zero fill is complete everywhere before any gather lands; the Q
-    // loads stay in flight beside the first gather
+    // the zero fill is complete everywhere before any gather lands
     lds_barrier();
     issue_part(Buf<0>{}, Buf<0>{}, off0);
     issue_part(Buf<0>{}, Buf<1>{}, off0);
     issue_part(Buf<0>{}, Buf<2>{}, off0);
-    if (w == 0 && n_tiles > 1) issue_idx(Buf<1>{}, 1);
+    if (w == 0 && nxt.t >= 0) issue_idx(Buf<1>{}, nxt);
+    // the sink, in flight beside the first gather
+    if (!DECODE && p.sink) {
+      const int h = h0 + 32 * hh + l32;
+      sink2 = (h < p.H ? p.sink[h] : 0.0f) * LOG2E;
+    }
   }
 
-  // decode: a split that ends before the last tile keeps its O in registers
-  // and is stored by the next tile, after that tile's gather is issued, so
-  // the stores drain during a tile instead of inside its first wait
-  int pend_sp = -1;       // split whose partial is still to be stored
-  float pend_inv = 0.0f;  // its normalization (heads 32hh + l32)
-  float pend_lse = 0.0f;
-  auto store_partial = [&](int sp, float inv, float lse_v) {
-    const int h = h0 + 32 * hh + l32;
-    if (h < p.H) {
-      float* po = p.part_out + ((t * p.num_splits + sp) * p.H + h) * (int64_t)D_V + 128 * g + 4 * hi;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-          *reinterpret_cast<f32x4*>(po + 32 * dt + 8 * q4) = f32x4{O[dt][4 * q4] * inv, O[dt][4 * q4 + 1] * inv,
-                                                                   O[dt][4 * q4 + 2] * inv, O[dt][4 * q4 + 3] * inv};
-      if (g == 0 && hi == 0) p.part_lse[(t * p.num_splits + sp) * p.H + h] = lse_v;
-    }
-  };
-
-  // one tile; tile k sits in raw buffer B = k & 1
-  auto step = [&](auto buf, int k) {
+  // one tile (cur) in raw buffer B; nxt is gathered into the other buffer
+  // meanwhile, and nn's index list is fetched into index buffer B
+  auto step = [&](auto buf, const TileRef& cur, const TileRef& nxt, const TileRef& nn) {
     constexpr int B = decltype(buf)::value;
     const uint8_t* raw = B ? raw1 : raw0;
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's part of tile k has landed
-    __syncthreads();                // B0: all of tile k is in LDS; tile k-1 is consumed
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's part of the tile has landed
+    __syncthreads();                // B0: all of the tile is in LDS; the one before is consumed
     // gather of the next tile (its index list arrived before B0), then the
     // index list one tile further ahead, read after the next B0
-    const bool more = k + 1 < n_tiles;
+    const bool more = nxt.t >= 0;
     int64_t off_next = -1;
     if (more) {
-      const int64_t j = j_begin + (int64_t)(k + 1) * TC + lane;
-      const int32_t x = j < j_end ? (B ? idx0 : idx1)[lane] : -1;
+      const int32_t j = nxt.j0 + lane;
+      const int32_t x = j < nxt.jend ? (B ? idx0 : idx1)[lane] : -1;
       off_next = row_offset(x);
       issue_part(Buf<1 - B>{}, Buf<0>{}, off_next);
     }
-    if (w == 0 && k + 2 < n_tiles) issue_idx(Buf<B>{}, k + 2);
-    if (DECODE && pend_sp >= 0) {
-      store_partial(pend_sp, pend_inv, pend_lse);
-      pend_sp = -1;
+    if (w == 0 && nn.t >= 0) issue_idx(Buf<B>{}, nn);
+    if (pend >= 0) {
+      store_result(pend, pend_factor, pend_lse);
+      pend = -1;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) O[dt][i] = 0.0f;
     }
-    // ---- 1. partial S^T (exact dequantized K) for candidates 32c2 + m ----
+  // ---- 1. partial S^T (exact dequantized K) for candidates 32c2 + m ----
     f32x16 acc[2];
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2) {
@@ -349,6 +402,8 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
       if (bad) r16 = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
       acc[c2] = mfma_32x32x16(__builtin_bit_cast(bf16x8, r16), qr, acc[c2]);
     }
+    // prefill: Q of the next token, not read again before that token's QK
+    if (!DECODE && more && nxt.t != cur.t) load_q(nxt.t);
     // ---- 2. reduce-scatter: accumulator elements [8hf, 8hf+8) of tile c2
     // are candidates 32c2 + 16hf + 8(i/4) + 4hi + i%4, owned by wave
     // (2c2 + hf, hh) ----
@@ -478,10 +533,11 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
         O[dt] = mfma_32x32x16(cvt8((uint32_t)v8[ks][dt][0], (uint32_t)v8[ks][dt][1], 1.0f),
                               __builtin_bit_cast(bf16x8, pb[ks]), O[dt]);
   };
-  // ---- end of a split (decode) or of the list: per-head sum over the four
-  // groups, normalize, store; then start over with empty state ----
+  // ---- end of a split (decode) or of a token (prefill): per-head sum over
+  // the four groups, normalization; the result is stored now, or by the
+  // next tile when there is one; then start over with empty state ----
   float* lsum = maxb;  // [4][64]; free once every wave is past the softmax of the tile
-  auto finish = [&](int sp, bool defer) {
+  auto finish = [&](int32_t key, bool defer) {
     {
       const float lt = l_part + __shfl_xor(l_part, 32);
       if (hi == 0) lsum[g * 64 + 32 * hh + l32] = lt;
@@ -495,39 +551,25 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
     const float lse_v = empty ? -INFINITY : (M + __log2f(Ls)) * LN2;
     m_run = -INFINITY;
     l_part = 0.0f;
-    if constexpr (DECODE) {
-      const float inv = empty ? 0.0f : 1.0f / Ls;
-      if (defer) {
-        // stored by the next tile; its first barrier also orders these lsum
-        // reads before the next writes of that buffer
-        pend_sp = sp;
-        pend_inv = inv;
-        pend_lse = lse_v;
-        return;
-      }
-      store_partial(sp, inv, lse_v);
-    } else if (h < p.H) {
-      float factor;
-      if (empty) {
-        factor = 0.0f;
-      } else if (p.sink) {
-        const float s2 = p.sink[h] * LOG2E;
-        const float ms = fmaxf(M, s2);
-        const float a = exp2f(M - ms);
-        factor = a / (Ls * a + exp2f(s2 - ms));
-      } else {
-        factor = 1.0f / Ls;
-      }
-      uint16_t* orow = p.out + t * p.out_st + (int64_t)h * p.out_sh + 128 * g + 4 * hi;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-          *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * q4) =
-              make_uint2(pack_bf16(O[dt][4 * q4] * factor, O[dt][4 * q4 + 1] * factor),
-                         pack_bf16(O[dt][4 * q4 + 2] * factor, O[dt][4 * q4 + 3] * factor));
-      if (g == 0 && hi == 0) p.lse[t * p.lse_st + h] = lse_v;
+    float factor;
+    if (empty) {
+      factor = 0.0f;
+    } else if (!DECODE && p.sink) {
+      const float ms = fmaxf(M, sink2);
+      const float a = exp2f(M - ms);
+      factor = a / (Ls * a + exp2f(sink2 - ms));
+    } else {
+      factor = 1.0f / Ls;
     }
+    if (defer) {
+      // the next tile's first barrier also orders these lsum reads before
+      // the next writes of that buffer
+      pend = key;
+      pend_factor = factor;
+      pend_lse = lse_v;
+      return;
+    }
+    store_result(key, factor, lse_v);
     // every wave has read lsum before anyone writes it again
     lds_barrier();
 #pragma unroll
@@ -535,24 +577,35 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) O[dt][i] = 0.0f;
   };
-  // tiles per split; a split ends after its last tile
-  const int tps = DECODE ? p.split_w / TC : 0;
-  int sp_next = sp0;  // next split to finish
-  for (int k = 0; k < n_tiles; k += 2) {
-    step(Buf<0>{}, k);
-    if (DECODE && ((k + 1) % tps == 0 || k + 1 == n_tiles)) finish(sp_next++, k + 1 < n_tiles);
-    if (k + 1 < n_tiles) {
-      step(Buf<1>{}, k + 1);
-      if (DECODE && ((k + 2) % tps == 0 || k + 2 == n_tiles)) finish(sp_next++, k + 2 < n_tiles);
+  int sp_next = sp0;  // decode: next split to finish
+  const int tiles_per_split = DECODE ? p.split_w / TC : 0;
+  int split_tiles_left = tiles_per_split;  // decode: tiles of the current split still to run
+  auto after_tile = [&](const TileRef& c, const TileRef& n) {
+    if constexpr (DECODE) {
+      if (--split_tiles_left == 0 || n.t < 0) {
+        finish(sp_next++, n.t >= 0);
+        split_tiles_left = tiles_per_split;
+      }
+    } else {
+      if (n.t != c.t) finish(c.t, n.t >= 0);
     }
+  };
+  while (cur.t >= 0) {
+    step(Buf<0>{}, cur, nxt, nn);
+    after_tile(cur, nxt);
+    cur = nxt;
+    nxt = nn;
+    nn = advance(nn);
+    if (cur.t < 0) break;
+    step(Buf<1>{}, cur, nxt, nn);
+    after_tile(cur, nxt);
+    cur = nxt;
+    nxt = nn;
+    nn = advance(nn);
   }
-  // the rest of the list: prefill's only result, or decode splits left empty
-  // by the list length
-  if (DECODE) {
+  // decode: splits left empty by the list length
+  if (DECODE)
     while (sp_next < sp_end) finish(sp_next++, false);
-  } else {
-    finish(0, false);
-  }
 }
 
 // looked up once per device
@@ -578,11 +631,21 @@ int fp8_splits_per_block(int64_t T, int32_t H, int32_t num_splits, int compute_u
   return (int)(g < 1 ? 1 : (g > num_splits ? num_splits : g));
 }
 
+// prefill: workgroups per head block; each takes tokens blockIdx.x,
+// blockIdx.x + gridDim.x, ... (one workgroup per compute unit in all)
+int fp8_prefill_blocks(int64_t T, int32_t H, int compute_units) {
+  const int64_t hb = (H + 63) / 64;
+  int64_t per = (compute_units > 0 ? compute_units : 1) / hb;
+  if (per < 1) per = 1;
+  return (int)(T < per ? T : per);
+}
+
 hipError_t launch_attention_fp8(const AttnParams& p, bool decode, hipStream_t s) {
   AttnParams q = p;
-  q.splits_per_block = decode ? fp8_splits_per_block(p.T, p.H, p.num_splits, device_compute_units()) : 1;
+  const int cus = device_compute_units();
+  q.splits_per_block = decode ? fp8_splits_per_block(p.T, p.H, p.num_splits, cus) : 1;
   dim3 block(f8::NT);
-  dim3 grid((unsigned)q.T, (unsigned)((q.H + 63) / 64),
+  dim3 grid(decode ? (unsigned)q.T : (unsigned)fp8_prefill_blocks(q.T, q.H, cus), (unsigned)((q.H + 63) / 64),
             decode ? (unsigned)((q.num_splits + q.splits_per_block - 1) / q.splits_per_block) : 1u);
   if (decode) hipLaunchKernelGGL((attn_fp8_kernel<true>), grid, block, 0, s, q);
   else hipLaunchKernelGGL((attn_fp8_kernel<false>), grid, block, 0, s, q);

@@ -68,5 +68,8 @@ int device_compute_units();
 // about one workgroup per compute unit when (token, split) pairs outnumber
 // the units
 int fp8_splits_per_block(int64_t T, int32_t H, int32_t num_splits, int compute_units);
+// prefill workgroups per head block of the FP8 many-head kernel: each runs
+// tokens blockIdx.x, blockIdx.x + gridDim.x, ... (at most one per compute unit)
+int fp8_prefill_blocks(int64_t T, int32_t H, int compute_units);
 
 }  // namespace smla

@@ -176,3 +176,36 @@ def test_quantize_padded_block_stride():
     a = smla.prefill(d.q, d.pool, d.indices, sm_scale=float(c.sm_scale))
     b = smla.prefill(d2.q, d2.pool, d2.indices, sm_scale=float(c.sm_scale))
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("H,T", [(64, 600), (128, 300)])
+def test_prefill_many_tokens_per_workgroup(H, T):
+    """More tokens than compute units: each workgroup of the many-head FP8
+    kernel runs several tokens in a row, with empty (0 or negative), clamped
+    and short lists among them."""
+    c = W.make_case(f"fp8_persist_h{H}", config_id=290 + H // 64, seed=3, fmt=W.FMT_FP8, T=T, H=H, n_seqs=1,
+                    ctx=1024, topk=96, causal=True, with_topk_length=True, with_sink=True)
+    L = c.topk_length.copy()
+    L[::7] = 0
+    L[3::11] = -3
+    L[5::13] = c.topk + 50
+    c.topk_length = L
+    d = Dev(c)
+    o, l = smla.prefill(d.q, d.pool, d.indices, topk_length=d.topk_length, sink=d.sink, sm_scale=float(c.sm_scale))
+    torch.cuda.synchronize()
+    ob, lf32, of64, _ = oracle.prefill(c.q, oracle_pool(c), c.indices, topk_length=c.topk_length, sink=c.sink,
+                                       sm_scale=c.sm_scale)
+    got_l = l.cpu().numpy()
+    assert np.array_equal(np.isneginf(got_l), np.isneginf(lf32))
+    assert np.isneginf(lf32[L <= 0]).all() and (L <= 0).sum() > 0
+    # Lists of one to three candidates give |out| up to about 4, where one
+    # BF16 ulp (2^-6) exceeds the 1e-2 bar: two correctly rounded results of
+    # values a rounding error apart may land one ulp apart.  So the BF16
+    # output is held to the bar against the oracle's exact result, and to at
+    # most one ulp against the oracle's own rounding.
+    got = bf16_dev_to_f64(o)
+    assert_out_close(got, of64)
+    want_b = f64_of_bits(ob)
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(want_b), 2.0 ** -126))) - 7)
+    assert np.all(np.abs(got - want_b) <= np.maximum(1e-2, ulp))
+    assert_lse_close(got_l, lf32)
