@@ -169,7 +169,7 @@ smla_status smla_combine(const float* part_out, const float* part_lse, int64_t T
  * with topk list entries in the given format:
  *   decode  = waves * (a + b * tiles per workgroup + f * splits per workgroup)
  *             + w * MB of partials;  combine = c0 + c1 * MB;
- *   prefill = waves * (ap + bp * tiles per token),
+ *   prefill = ap0 + waves * (ap + bp * tiles per token),
  * with waves = rounds of workgroups over compute_units and constants fitted
  * per kernel (format, H > 16) by calibrate_splits.py in the package.
  * compute_units <= 0 means the current device's.  Returns -1 when T < 1,

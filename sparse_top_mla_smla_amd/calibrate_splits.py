@@ -10,9 +10,9 @@ cache-resident.  This script does the same for this library's kernels:
     decode(T, H, topk, S) = waves * (a + b * tiles_per_block + f * splits_per_block)
                             + w * partial_MB
     combine(T, H, S)      = c0 + c1 * partial_MB + c2 * T * H / 1000
-    prefill(T, H, topk)   = waves_p * (ap + bp * tiles_per_token)
+    prefill(T, H, topk)   = ap0 + waves_p * (ap + bp * tiles_per_token)
 
-with a, b, f, ap, bp per kernel class (format x many-head or narrow
+with a, b, f, ap0, ap, bp per kernel class (format x many-head or narrow
 kernel), w and c0..c2 shared, all in microseconds.  waves counts rounds of
 workgroups over the compute units at the kernel's occupancy.
 
@@ -45,6 +45,7 @@ CLASSES = {
     "int8_narrow": (W.FMT_INT8, (8,), 1, 16),
 }
 T_GRID = (1, 2, 4, 8, 16, 32, 64, 128, 256)
+T_PREFILL_ONLY = (1024,)  # several tokens per workgroup in the persistent prefill
 TOPK_GRID = (512, 2048)
 S_GRID = (1, 2, 4, 8, 16, 32)
 
@@ -101,7 +102,7 @@ def measure(cus: int, log):
     for cls, (fmt, heads, _, _) in CLASSES.items():
         for H in heads:
             for topk in TOPK_GRID:
-                for T in T_GRID:
+                for T in T_GRID + T_PREFILL_ONLY:
                     q = torch.randn((T, H, 576), generator=gen, device="cuda").to(torch.bfloat16)
                     sets = [torch.randint(0, POOL_ROWS, (T, topk), generator=gen, device="cuda", dtype=torch.int32)
                             for _ in range(3)]
@@ -111,7 +112,7 @@ def measure(cus: int, log):
                     tp = timed(lambda x: smla.prefill(q, pool, x, out=out, lse=lse), sets)
                     rows.append(dict(kind="prefill", cls=cls, T=T, H=H, topk=topk, us=tp))
                     for S in S_GRID:
-                        if S > topk // 64:
+                        if S > topk // 64 or T not in T_GRID:
                             continue
                         po = torch.empty((T, S, H, 512), dtype=torch.float32, device="cuda")
                         pl = torch.empty((T, S, H), dtype=torch.float32, device="cuda")
@@ -162,10 +163,16 @@ def fit(rows, cus: int):
         Xp = []
         for r in pre:
             waves, tiles = prefill_geometry(cls, r["T"], r["H"], r["topk"], cus)
-            Xp.append([waves, waves * tiles])
+            Xp.append([1.0, waves, waves * tiles])
         cp = lsq(Xp, [r["us"] for r in pre])
-        consts[cls].update(ap=cp[0], bp=cp[1])
+        consts[cls].update(ap0=cp[0], ap=cp[1], bp=cp[2])
     return dict(classes=consts, w_us_per_MB=w, combine=dict(c0=cc[0], c1=cc[1], c2=cc[2]))
+
+
+def predict_prefill(model, cls, T, H, topk, cus):
+    k = model["classes"][cls]
+    waves, tiles = prefill_geometry(cls, T, H, topk, cus)
+    return k["ap0"] + waves * (k["ap"] + k["bp"] * tiles)
 
 
 def predict(model, cls, T, H, topk, S, cus):

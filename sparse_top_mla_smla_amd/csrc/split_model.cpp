@@ -10,14 +10,15 @@
 // launch geometry:
 //   decode  = waves * (a + b * tiles_per_block + f * splits_per_block) + w * MB
 //   combine = c0 + c1 * MB + c2 * T * H / 1000
-//   prefill = waves_p * (ap + bp * tiles_per_token)
+//   prefill = ap0 + waves_p * (ap + bp * tiles_per_token)
 // with MB the partial buffers (T * S * H * 2052 bytes), waves the rounds of
 // workgroups over the compute units (one workgroup per CU per round: the
 // many-head kernels fill a CU's LDS, and two co-resident narrow workgroups
-// share the CU's SIMDs), and a, b, f, ap, bp per kernel class.  The
+// share the CU's SIMDs), and a, b, f, ap0, ap, bp per kernel class.  The
 // constants were fitted by sparse_top_mla_smla_amd/calibrate_splits.py on
-// one MI355X (256 CUs) over 126 decode shapes; there the pick is on average
-// 0.1% and at most 4.1% slower than the best measured split count.
+// one MI355X (256 CUs) over 126 decode shapes and their prefill
+// counterparts; there the pick is on average 0.2% and at most 7.7% slower
+// than the best measured split count.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -31,19 +32,19 @@ namespace {
 
 struct KernelClass {
   double a, b, f;  // decode: per block, per tile of the longest block, per split it finishes (us)
-  double ap, bp;   // prefill: per block, per tile (us)
+  double ap0, ap, bp;  // prefill: per launch, per round of blocks, per tile of a round (us)
   int heads_per_block;
   bool grouped;    // consecutive splits per workgroup (the FP8 many-head kernel)
 };
 
 // fitted constants (microseconds), MI355X
-constexpr KernelClass kFp8Wide{13.80, 2.873, 3.100, 17.84, 2.890, 64, true};
-constexpr KernelClass kInt8Wide{4.704, 4.939, 4.704, 16.04, 4.851, 64, false};
-constexpr KernelClass kFp8Narrow{3.629, 4.033, 3.629, 16.69, 3.487, 16, false};
-constexpr KernelClass kBf16Narrow{3.683, 4.589, 3.683, 16.42, 4.027, 16, false};
-constexpr KernelClass kInt8Narrow{3.472, 4.271, 3.472, 16.21, 3.742, 16, false};
-constexpr double kWriteUsPerMB = 0.1444;  // decode's partial stores
-constexpr double kComb0 = 11.00, kComb1 = 0.1853, kComb2 = 0.0;
+constexpr KernelClass kFp8Wide{14.09, 2.993, 1.554, 2.596, 10.08, 3.211, 64, true};
+constexpr KernelClass kInt8Wide{4.027, 4.956, 4.027, 0.0, 14.59, 5.132, 64, false};
+constexpr KernelClass kFp8Narrow{3.509, 4.015, 3.509, 1.068, 13.21, 3.592, 16, false};
+constexpr KernelClass kBf16Narrow{3.608, 4.568, 3.608, 0.0, 14.05, 4.183, 16, false};
+constexpr KernelClass kInt8Narrow{3.363, 4.257, 3.363, 1.179, 12.82, 3.839, 16, false};
+constexpr double kWriteUsPerMB = 0.186;  // decode's partial stores
+constexpr double kComb0 = 10.57, kComb1 = 0.1856, kComb2 = 0.0;
 constexpr double kPartialBytesPerRow = 512 * 4 + 4;
 constexpr double kCrossover = 0.95;  // split form only when at most this fraction of prefill
 
@@ -74,7 +75,7 @@ double split_cost(const KernelClass& c, int64_t T, int32_t H, int32_t topk, int3
 
 double prefill_cost(const KernelClass& c, int64_t T, int32_t H, int32_t topk, int cus) {
   const double waves = (double)ceil_div(T * ceil_div(H, c.heads_per_block), cus);
-  return waves * (c.ap + c.bp * (double)ceil_div(topk, 64));
+  return c.ap0 + waves * (c.ap + c.bp * (double)ceil_div(topk, 64));
 }
 
 int max_splits(int32_t topk) { return (int)std::min<int64_t>(64, ceil_div(topk, 64)); }

@@ -47,9 +47,7 @@ def test_library_cost_is_the_calibration_formula(cls):
             want = C.predict(model, cls, r["T"], r["H"], r["topk"], r["S"], CUS)
             got = smla.split_model_cost(r["T"], r["H"], r["topk"], fmt, r["S"], CUS)
         else:
-            waves, tiles = C.prefill_geometry(cls, r["T"], r["H"], r["topk"], CUS)
-            k = model["classes"][cls]
-            want = waves * (k["ap"] + k["bp"] * tiles)
+            want = C.predict_prefill(model, cls, r["T"], r["H"], r["topk"], CUS)
             got = smla.split_model_cost(r["T"], r["H"], r["topk"], fmt, 0, CUS)
         # the library holds the constants to four significant digits
         assert got == pytest.approx(want, rel=2e-3), (r, got, want)
