@@ -76,16 +76,24 @@ typedef enum {
 } smla_kv_format;
 
 /* A paged latent pool.  Slot s (a flat pool position) lives in block s/64 at
- * row s%64: byte address base + (s/64)*block_stride_bytes + (s%64)*row_bytes.
- * base must be 16-byte aligned; block_stride_bytes a multiple of 16 and at
- * least 64*row_bytes; page_block must be 64 (PR #4802: the kernels are
- * compiled for page block 64 and launchers reject anything else). */
+ * row s%64: byte address base + (s/64)*block_stride_bytes + (s%64)*R, with
+ * R = row_stride_bytes, or the format's row bytes when row_stride_bytes is 0
+ * (dense rows).  A padded row stride describes caches whose rows carry
+ * bytes beyond the format's (PR #4802 review of the binding: rows addressed
+ * by a token-axis stride that may exceed bytes_per_token); with one latent
+ * head per row the NHD and HND block layouts differ only in these two
+ * strides.  base must be 16-byte aligned; R a multiple of 16 and at least
+ * the row bytes; block_stride_bytes a multiple of 16 and at least 64*R;
+ * page_block must be 64 (PR #4802: the kernels are compiled for page block
+ * 64 and launchers reject anything else).  Bytes outside the rows are never
+ * read or written. */
 typedef struct {
   void* base;
   int64_t num_blocks;
   int64_t block_stride_bytes;
   int32_t page_block;
   int32_t format; /* smla_kv_format */
+  int64_t row_stride_bytes; /* 0: dense rows */
 } smla_kv_pool;
 
 /* Bytes of one cache row: 1152 (BF16), 656 (FP8, INT8); -1 for an unknown format. */

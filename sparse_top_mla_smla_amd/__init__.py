@@ -30,7 +30,7 @@ class SmlaError(RuntimeError):
 class _Pool(ctypes.Structure):
     _fields_ = [("base", ctypes.c_void_p), ("num_blocks", ctypes.c_int64),
                 ("block_stride_bytes", ctypes.c_int64), ("page_block", ctypes.c_int32),
-                ("format", ctypes.c_int32)]
+                ("format", ctypes.c_int32), ("row_stride_bytes", ctypes.c_int64)]
 
 
 def library_path() -> str:
@@ -142,18 +142,20 @@ def _need(t: torch.Tensor, name: str, dtype, last_contig: bool = True):
 
 class KVPool:
     """A paged latent pool: a uint8 device tensor [num_blocks, block_stride]
-    (block_stride >= 64 * row_bytes, multiple of 16) in format fmt."""
+    (block_stride >= 64 * row stride, multiple of 16) in format fmt, rows
+    row_stride bytes apart within a block (0: dense rows of row_bytes)."""
 
-    def __init__(self, data: torch.Tensor, fmt: int, page_block: int = 64):
+    def __init__(self, data: torch.Tensor, fmt: int, page_block: int = 64, row_stride: int = 0):
         _need(data, "pool", torch.uint8)
         if data.dim() != 2:
             raise SmlaError("pool must be 2-D [num_blocks, block_stride_bytes]")
-        self.data, self.fmt, self.page_block = data, fmt, page_block
+        self.data, self.fmt, self.page_block, self.row_stride = data, fmt, page_block, row_stride
 
     @classmethod
-    def empty(cls, num_blocks: int, fmt: int, device="cuda", block_stride: int = 0) -> "KVPool":
-        bs = block_stride or 64 * row_bytes(fmt)
-        return cls(torch.zeros((num_blocks, bs), dtype=torch.uint8, device=device), fmt)
+    def empty(cls, num_blocks: int, fmt: int, device="cuda", block_stride: int = 0,
+              row_stride: int = 0) -> "KVPool":
+        bs = block_stride or 64 * (row_stride or row_bytes(fmt))
+        return cls(torch.zeros((num_blocks, bs), dtype=torch.uint8, device=device), fmt, row_stride=row_stride)
 
     @property
     def num_blocks(self) -> int:
@@ -161,7 +163,7 @@ class KVPool:
 
     def c(self) -> _Pool:
         return _Pool(self.data.data_ptr(), self.data.shape[0], self.data.stride(0), self.page_block,
-                     self.fmt)
+                     self.fmt, self.row_stride)
 
 
 def quantize_kv(kv: torch.Tensor, slots: torch.Tensor, pool: KVPool, stream=None) -> None:

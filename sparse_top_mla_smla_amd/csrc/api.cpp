@@ -41,9 +41,12 @@ smla_status check_pool(const smla_kv_pool& kv) {
   if (kv.num_blocks < 1) return fail(SMLA_ERR_SHAPE, "num_blocks %lld must be >= 1", (long long)kv.num_blocks);
   if (kv.num_blocks > (int64_t)(INT32_MAX / 64) + 1)
     return fail(SMLA_ERR_SHAPE, "num_blocks %lld exceeds the int32 slot range", (long long)kv.num_blocks);
-  if (kv.block_stride_bytes < 64LL * rb)
-    return fail(SMLA_ERR_STRIDE, "block_stride_bytes %lld is smaller than 64 rows of %d bytes",
-                (long long)kv.block_stride_bytes, rb);
+  const int64_t rs = kv.row_stride_bytes ? kv.row_stride_bytes : rb;
+  if (rs < rb) return fail(SMLA_ERR_STRIDE, "row_stride_bytes %lld is smaller than the %d-byte row", (long long)rs, rb);
+  if (rs % 16 != 0) return fail(SMLA_ERR_STRIDE, "row_stride_bytes %lld is not a multiple of 16", (long long)rs);
+  if (kv.block_stride_bytes < 64LL * rs)
+    return fail(SMLA_ERR_STRIDE, "block_stride_bytes %lld is smaller than 64 rows of %lld bytes",
+                (long long)kv.block_stride_bytes, (long long)rs);
   if (kv.block_stride_bytes % 16 != 0)
     return fail(SMLA_ERR_STRIDE, "block_stride_bytes %lld is not a multiple of 16", (long long)kv.block_stride_bytes);
   if (!aligned(kv.base, 16)) return fail(SMLA_ERR_STRIDE, "kv pool base is not 16-byte aligned");
@@ -139,7 +142,7 @@ smla_status smla_quantize_kv(const void* kv, int64_t n, int64_t kv_stride, const
   if (!aligned(kv, 16)) return fail(SMLA_ERR_STRIDE, "kv is not 16-byte aligned");
   if (!aligned(slots, 4)) return fail(SMLA_ERR_STRIDE, "slots is not 4-byte aligned");
   if ((n + 3) / 4 > (int64_t)UINT32_MAX) return fail(SMLA_ERR_SHAPE, "n = %lld is too large", (long long)n);
-  smla::QuantParams p;
+  smla::QuantParams p{};
   p.kv = static_cast<const uint16_t*>(kv);
   p.n = n;
   p.kv_stride = kv_stride;
@@ -147,6 +150,7 @@ smla_status smla_quantize_kv(const void* kv, int64_t n, int64_t kv_stride, const
   p.pool = static_cast<uint8_t*>(pool.base);
   p.nslots = pool.num_blocks * 64;
   p.block_stride = pool.block_stride_bytes;
+  p.row_stride = pool.row_stride_bytes ? pool.row_stride_bytes : smla_row_bytes(pool.format);
   return launched(smla::launch_quantize(p, pool.format, static_cast<hipStream_t>(stream)), "quantize");
 }
 
@@ -161,6 +165,7 @@ static void fill_attn(smla::AttnParams& p, const void* q, int64_t T, int32_t H, 
   p.H = H;
   p.pool = static_cast<const uint8_t*>(kv.base);
   p.block_stride = kv.block_stride_bytes;
+  p.row_stride = kv.row_stride_bytes ? kv.row_stride_bytes : smla_row_bytes(kv.format);
   p.nslots = kv.num_blocks * 64;
   p.idx = indices;
   p.idx_st = idx_st;

@@ -121,7 +121,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_kernel(AttnParams p) {
         const int32_t slot = il[row];
         if (slot >= 0) {
           const uint8_t* src = p.pool + (int64_t)(slot / PAGE) * p.block_stride +
-                               (int64_t)(slot % PAGE) * G::BYTES + 16 * ck;
+                               (int64_t)(slot % PAGE) * p.row_stride + 16 * ck;
           v = *reinterpret_cast<const uint4*>(src);
         }
       }

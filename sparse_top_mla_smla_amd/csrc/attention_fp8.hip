@@ -214,7 +214,7 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
   // byte offset in the pool of the row of index value x (-1: masked or not
   // a pool slot)
   auto row_offset = [&](int32_t x) -> int64_t {
-    return (x >= 0 && (int64_t)x < p.nslots) ? (int64_t)(x / PAGE) * p.block_stride + (int64_t)(x % PAGE) * RB
+    return (x >= 0 && (int64_t)x < p.nslots) ? (int64_t)(x / PAGE) * p.block_stride + (int64_t)(x % PAGE) * p.row_stride
                                              : (int64_t)-1;
   };
   // wave 0 moves the index list entries of tile r into index buffer B

@@ -158,7 +158,7 @@ __global__ __launch_bounds__(wide::NT, 1) void attn_wide_kernel(AttnParams p) {
     int64_t v = -1;
     if (j < j_end) {
       const int32_t x = idx_row[j];
-      if (x >= 0 && (int64_t)x < p.nslots) v = (int64_t)(x / PAGE) * p.block_stride + (int64_t)(x % PAGE) * RB;
+      if (x >= 0 && (int64_t)x < p.nslots) v = (int64_t)(x / PAGE) * p.block_stride + (int64_t)(x % PAGE) * p.row_stride;
     }
     return v;
   };

@@ -15,6 +15,7 @@ struct QuantParams {
   uint8_t* pool;
   int64_t nslots;       // num_blocks * 64
   int64_t block_stride; // bytes
+  int64_t row_stride;   // bytes between the rows of a block
 };
 
 struct AttnParams {
@@ -24,6 +25,7 @@ struct AttnParams {
   int32_t H;
   const uint8_t* pool;
   int64_t block_stride; // bytes
+  int64_t row_stride;   // bytes between the rows of a block
   int64_t nslots;
   const int32_t* idx;
   int64_t idx_st;       // elements

@@ -61,7 +61,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantParams p) {
   const int64_t slot = p.slots[row];
   if (slot < 0 || slot >= p.nslots) return;
   const uint16_t* src = p.kv + row * p.kv_stride;
-  uint8_t* dst = p.pool + (slot / PAGE) * p.block_stride + (slot % PAGE) * G::BYTES;
+  uint8_t* dst = p.pool + (slot / PAGE) * p.block_stride + (slot % PAGE) * p.row_stride;
 
   if constexpr (FMT == FMT_BF16) {
     const uint4* s4 = reinterpret_cast<const uint4*>(src);

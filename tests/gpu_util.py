@@ -32,7 +32,7 @@ def bf16_dev_to_f64(t: torch.Tensor) -> np.ndarray:
 class Dev:
     """Device copies of a case's inputs plus a pool filled by smla.quantize_kv."""
 
-    def __init__(self, case: W.Case, block_stride: int = 0, fill: int = 0):
+    def __init__(self, case: W.Case, block_stride: int = 0, fill: int = 0, row_stride: int = 0):
         self.case = case
         self.q_buf = u16_to_bf16_dev(case.q_buf)
         self.q = self.q_buf[:, : case.H]
@@ -43,9 +43,9 @@ class Dev:
         self.topk_length = None if case.topk_length is None else torch.from_numpy(case.topk_length).cuda()
         self.sink = None if case.sink is None else torch.from_numpy(case.sink).cuda()
         rb = W.ROW_BYTES[case.fmt]
-        bs = block_stride or 64 * rb
+        bs = block_stride or 64 * (row_stride or rb)
         self.pool = smla.KVPool(torch.full((case.num_blocks, bs), fill, dtype=torch.uint8, device="cuda"),
-                                case.fmt)
+                                case.fmt, row_stride=row_stride)
         smla.quantize_kv(self.kv, self.slots, self.pool)
 
 

@@ -77,9 +77,10 @@ def test_decode_workspace_size():
     assert lib.smla_decode_workspace_size(1, 8, 1, None) == 1  # SMLA_ERR_NULL
 
 
-def pool(fmt=W.FMT_FP8, num_blocks=4, page_block=64, block_stride=None):
+def pool(fmt=W.FMT_FP8, num_blocks=4, page_block=64, block_stride=None, row_stride=0):
     rb = W.ROW_BYTES.get(fmt, 656)
-    return smla._Pool(FAKE, num_blocks, block_stride if block_stride is not None else 64 * rb, page_block, fmt)
+    bs = block_stride if block_stride is not None else 64 * (row_stride or rb)
+    return smla._Pool(FAKE, num_blocks, bs, page_block, fmt, row_stride)
 
 
 def prefill(lib, T=2, H=64, q=FAKE, pl=None, idx=FAKE, topk=64, q_st=64 * 576, q_sh=576, out=FAKE, lse=FAKE,
@@ -100,6 +101,10 @@ def test_prefill_validation_before_launch():
     assert "page_block 32" in lib.smla_last_error().decode()
     assert prefill(lib, pl=pool(fmt=5)) == 4                                 # unknown format
     assert prefill(lib, pl=pool(block_stride=64 * 656 - 16)) == 3            # block stride below 64 rows
+    assert prefill(lib, pl=pool(row_stride=640)) == 3                        # row stride below the row
+    assert prefill(lib, pl=pool(row_stride=664)) == 3                        # row stride not a multiple of 16
+    assert prefill(lib, pl=pool(row_stride=672, block_stride=64 * 656)) == 3  # block stride below 64 padded rows
+    assert "row_stride" in lib.smla_last_error().decode() or "64 rows" in lib.smla_last_error().decode()
     assert prefill(lib, q=FAKE + 8) == 3                                     # q not 16-byte aligned
     assert prefill(lib, idx_st=32) == 3                                      # index row stride < topk
 

@@ -178,6 +178,37 @@ def test_quantize_padded_block_stride():
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
+@pytest.mark.parametrize("name", ["fp8_h8_ragged", "bf16_h16_sink_len", "int8_h64_len", "fp8_h64_multi_tile",
+                                  "int8_h128_view"])
+def test_padded_rows(name):
+    """Rows padded beyond the format's bytes (and blocks beyond 64 rows):
+    each row's bytes equal the oracle's packed row, the padding is never
+    written, and prefill and decode over the padded pool equal those over
+    the packed pool bit for bit."""
+    c = make(name)
+    rb = W.ROW_BYTES[c.fmt]
+    rs = rb + 48
+    bs = 64 * rs + 80
+    d = Dev(c, block_stride=bs, fill=0xC3, row_stride=rs)
+    torch.cuda.synchronize()
+    got = d.pool.data.cpu().numpy()
+    ref = oracle_pool(c).data  # packed rows
+    for blk in range(c.num_blocks):
+        for r in range(64):
+            assert np.array_equal(got[blk, r * rs:r * rs + rb], ref[blk, r * rb:(r + 1) * rb])
+            assert (got[blk, r * rs + rb:(r + 1) * rs] == 0xC3).all()
+        assert (got[blk, 64 * rs:] == 0xC3).all()
+    dp = Dev(c)
+    a = smla.prefill(d.q, d.pool, d.indices, topk_length=d.topk_length, sink=d.sink, sm_scale=float(c.sm_scale))
+    b = smla.prefill(dp.q, dp.pool, dp.indices, topk_length=dp.topk_length, sink=dp.sink,
+                     sm_scale=float(c.sm_scale))
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    for S in (1, 3):
+        x = smla.decode(d.q, d.pool, d.indices, S, topk_length=d.topk_length, sm_scale=float(c.sm_scale))
+        y = smla.decode(dp.q, dp.pool, dp.indices, S, topk_length=dp.topk_length, sm_scale=float(c.sm_scale))
+        assert torch.equal(x[0], y[0]) and torch.equal(x[1], y[1])
+
+
 @pytest.mark.parametrize("H,T", [(64, 600), (128, 300)])
 def test_prefill_many_tokens_per_workgroup(H, T):
     """More tokens than compute units: each workgroup of the many-head FP8
