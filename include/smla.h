@@ -146,6 +146,36 @@ smla_status smla_prefill(const void* q, int64_t T, int32_t H, int64_t q_stride_t
                          void* out, int64_t out_stride_t, int64_t out_stride_h,
                          float* lse, int64_t lse_stride_t, void* stream);
 
+/* The secondary candidate list of a dual-cache call.  FlashInfer #4802
+ * gives the DSv4 decode a secondary cache with its own strided index rows
+ * (commit message on strided decode indices) and lets DSv3.2-family calls
+ * carry one too (PR description, "Plan layer": dual-cache decode calls had
+ * ignored it); its dual-cache shapes pair a 1024-wide main list with a
+ * 2176-wide secondary list.  Here the two lists form one candidate list:
+ * positions [0, topk) are the main list over the main pool and positions
+ * [topk, topk + extra.topk) the secondary list over extra.kv, each cut at its
+ * own length (extra.topk_length, int32 [T] or NULL), and one softmax runs
+ * over all candidates.  extra.kv has the main pool's format; indices are
+ * int32 [T, >= extra.topk] with row stride idx_stride_t (a narrowed view is
+ * allowed) and index the secondary pool's slots. */
+typedef struct {
+  smla_kv_pool kv;
+  const int32_t* indices;
+  int32_t topk;
+  int64_t idx_stride_t;
+  const int32_t* topk_length;
+} smla_kv_extra;
+
+/* smla_prefill over the main list and a secondary list (extra may be NULL:
+ * then it is smla_prefill).  With a secondary list the main list width topk
+ * must be a multiple of 64 (SMLA_ERR_UNSUPPORTED otherwise), extra.topk >= 1,
+ * and extra.kv must pass the pool checks with the main pool's format. */
+smla_status smla_prefill_dual(const void* q, int64_t T, int32_t H, int64_t q_stride_t, int64_t q_stride_h,
+                              smla_kv_pool kv, const int32_t* indices, int32_t topk, int64_t idx_stride_t,
+                              const int32_t* topk_length, const smla_kv_extra* extra, const float* sink,
+                              float sm_scale, void* out, int64_t out_stride_t, int64_t out_stride_h, float* lse,
+                              int64_t lse_stride_t, void* stream);
+
 /* Decode split form: per split s (smla_split_width) of each token's list,
  * the partial result over that split's candidates, with no sink:
  *   part_lse[t,s,h] = ln sum_{j in split} exp(s_j)   (-inf when empty)
@@ -157,6 +187,14 @@ smla_status smla_decode(const void* q, int64_t T, int32_t H, int64_t q_stride_t,
                         smla_kv_pool kv, const int32_t* indices, int32_t topk, int64_t idx_stride_t,
                         const int32_t* topk_length, float sm_scale, int32_t num_splits,
                         float* part_out, float* part_lse, void* stream);
+
+/* smla_decode over the main list and a secondary list (as smla_prefill_dual):
+ * the splits run over the combined positions [0, topk + extra.topk), with
+ * split width smla_split_width(topk + extra.topk, num_splits). */
+smla_status smla_decode_dual(const void* q, int64_t T, int32_t H, int64_t q_stride_t, int64_t q_stride_h,
+                             smla_kv_pool kv, const int32_t* indices, int32_t topk, int64_t idx_stride_t,
+                             const int32_t* topk_length, const smla_kv_extra* extra, float sm_scale,
+                             int32_t num_splits, float* part_out, float* part_lse, void* stream);
 
 /* Log-sum-exp merge of decode splits (AppMana "decode H6" combine): with
  * M = max_s part_lse, w_s = exp(part_lse_s - M) and W = sum w_s,

@@ -33,6 +33,11 @@ class _Pool(ctypes.Structure):
                 ("format", ctypes.c_int32), ("row_stride_bytes", ctypes.c_int64)]
 
 
+class _Extra(ctypes.Structure):
+    _fields_ = [("kv", _Pool), ("indices", ctypes.c_void_p), ("topk", ctypes.c_int32),
+                ("idx_stride_t", ctypes.c_int64), ("topk_length", ctypes.c_void_p)]
+
+
 def library_path() -> str:
     return _LIB_PATH
 
@@ -65,7 +70,12 @@ def _load():
     L.smla_attention_workspace_size.restype = ctypes.c_int
     L.smla_attention.argtypes = [P, i64, i32, i64, i64, _Pool, P, i32, i64, P, P, f32, P, i64, i64,
                                  P, i64, P, ctypes.c_size_t, P]
-    for fn in (L.smla_quantize_kv, L.smla_prefill, L.smla_decode, L.smla_combine, L.smla_attention):
+    PE = ctypes.POINTER(_Extra)
+    L.smla_prefill_dual.argtypes = [P, i64, i32, i64, i64, _Pool, P, i32, i64, P, PE, P, f32, P, i64, i64,
+                                    P, i64, P]
+    L.smla_decode_dual.argtypes = [P, i64, i32, i64, i64, _Pool, P, i32, i64, P, PE, f32, i32, P, P, P]
+    for fn in (L.smla_quantize_kv, L.smla_prefill, L.smla_decode, L.smla_combine, L.smla_attention,
+               L.smla_prefill_dual, L.smla_decode_dual):
         fn.restype = ctypes.c_int
     _lib = L
     return L
@@ -286,3 +296,65 @@ def attention(q: torch.Tensor, pool: KVPool, indices: torch.Tensor, topk: Option
                                   out.stride(0), out.stride(1), _ptr(lse), lse.stride(0), _ptr(workspace),
                                   ws_bytes, _stream(stream)), "smla_attention")
     return out, lse
+
+
+def _extra(pool: KVPool, indices: torch.Tensor, topk: Optional[int], topk_length: Optional[torch.Tensor]):
+    topk, ist = _idx_args(indices, topk)
+    if topk_length is not None:
+        _need(topk_length, "extra_topk_length", torch.int32)
+    return _Extra(pool.c(), _ptr(indices), topk, ist, _ptr(topk_length))
+
+
+def prefill_dual(q: torch.Tensor, pool: KVPool, indices: torch.Tensor, extra_pool: KVPool,
+                 extra_indices: torch.Tensor, topk: Optional[int] = None, extra_topk: Optional[int] = None,
+                 topk_length: Optional[torch.Tensor] = None, extra_topk_length: Optional[torch.Tensor] = None,
+                 sink: Optional[torch.Tensor] = None, sm_scale: float = 1.0 / 24.0,
+                 out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                 stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Prefill over a main and a secondary candidate list (see smla_prefill_dual)."""
+    _need(q, "q", torch.bfloat16)
+    T, H, _ = q.shape
+    topk, ist = _idx_args(indices, topk)
+    ex = _extra(extra_pool, extra_indices, extra_topk, extra_topk_length)
+    if topk_length is not None:
+        _need(topk_length, "topk_length", torch.int32)
+    if sink is not None:
+        _need(sink, "sink", torch.float32)
+    if out is None:
+        out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.bfloat16)
+    _need(lse, "lse", torch.float32)
+    _check(_load().smla_prefill_dual(_ptr(q), T, H, q.stride(0), q.stride(1), pool.c(), _ptr(indices), topk, ist,
+                                     _ptr(topk_length), ctypes.byref(ex), _ptr(sink), float(sm_scale), _ptr(out),
+                                     out.stride(0), out.stride(1), _ptr(lse), lse.stride(0), _stream(stream)),
+           "smla_prefill_dual")
+    return out, lse
+
+
+def decode_dual(q: torch.Tensor, pool: KVPool, indices: torch.Tensor, extra_pool: KVPool,
+                extra_indices: torch.Tensor, num_splits: int, topk: Optional[int] = None,
+                extra_topk: Optional[int] = None, topk_length: Optional[torch.Tensor] = None,
+                extra_topk_length: Optional[torch.Tensor] = None, sm_scale: float = 1.0 / 24.0,
+                part_out: Optional[torch.Tensor] = None, part_lse: Optional[torch.Tensor] = None,
+                stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Split-KV decode partials over a main and a secondary list (see smla_decode_dual)."""
+    _need(q, "q", torch.bfloat16)
+    T, H, _ = q.shape
+    topk, ist = _idx_args(indices, topk)
+    ex = _extra(extra_pool, extra_indices, extra_topk, extra_topk_length)
+    if topk_length is not None:
+        _need(topk_length, "topk_length", torch.int32)
+    if part_out is None:
+        part_out = torch.empty((T, num_splits, H, 512), dtype=torch.float32, device=q.device)
+    if part_lse is None:
+        part_lse = torch.empty((T, num_splits, H), dtype=torch.float32, device=q.device)
+    _need(part_out, "part_out", torch.float32)
+    _need(part_lse, "part_lse", torch.float32)
+    if not (part_out.is_contiguous() and part_lse.is_contiguous()):
+        raise SmlaError("part_out / part_lse must be contiguous")
+    _check(_load().smla_decode_dual(_ptr(q), T, H, q.stride(0), q.stride(1), pool.c(), _ptr(indices), topk, ist,
+                                    _ptr(topk_length), ctypes.byref(ex), float(sm_scale), num_splits,
+                                    _ptr(part_out), _ptr(part_lse), _stream(stream)), "smla_decode_dual")
+    return part_out, part_lse

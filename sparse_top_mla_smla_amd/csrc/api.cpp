@@ -90,6 +90,27 @@ smla_status check_out(const void* out, int64_t out_st, int64_t out_sh, int32_t H
   return SMLA_OK;
 }
 
+// the secondary list of a dual-cache call (extra != NULL)
+smla_status check_extra(const smla_kv_pool& kv, int32_t topk, const smla_kv_extra* extra) {
+  if (!extra) return SMLA_OK;
+  if (topk % 64 != 0)
+    return fail(SMLA_ERR_UNSUPPORTED, "topk = %d: with a secondary list the main list width must be a multiple of 64",
+                topk);
+  if (extra->topk < 1) return fail(SMLA_ERR_SHAPE, "extra topk = %d must be >= 1", extra->topk);
+  if ((int64_t)topk + extra->topk > INT32_MAX) return fail(SMLA_ERR_SHAPE, "topk + extra topk exceeds 2^31-1");
+  if (!extra->indices) return fail(SMLA_ERR_NULL, "extra indices is NULL");
+  smla_status st = check_pool(extra->kv);
+  if (st != SMLA_OK) return st;
+  if (extra->kv.format != kv.format)
+    return fail(SMLA_ERR_UNSUPPORTED, "extra pool format %d differs from the main pool's %d", extra->kv.format,
+                kv.format);
+  if (extra->idx_stride_t < extra->topk)
+    return fail(SMLA_ERR_STRIDE, "extra idx_stride_t = %lld is smaller than extra topk = %d",
+                (long long)extra->idx_stride_t, extra->topk);
+  if (!aligned(extra->indices, 4)) return fail(SMLA_ERR_STRIDE, "extra indices is not 4-byte aligned");
+  return SMLA_OK;
+}
+
 smla_status launched(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(SMLA_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
   return ok();
@@ -174,20 +195,44 @@ static void fill_attn(smla::AttnParams& p, const void* q, int64_t T, int32_t H, 
   p.scale_log2 = sm_scale * 1.4426950408889634f;
 }
 
+static void fill_extra(smla::AttnParams& p, const smla_kv_extra* extra) {
+  if (!extra) return;
+  p.pool2 = static_cast<const uint8_t*>(extra->kv.base);
+  p.block_stride2 = extra->kv.block_stride_bytes;
+  p.row_stride2 = extra->kv.row_stride_bytes ? extra->kv.row_stride_bytes : smla_row_bytes(extra->kv.format);
+  p.nslots2 = extra->kv.num_blocks * 64;
+  p.idx2 = extra->indices;
+  p.idx_st2 = extra->idx_stride_t;
+  p.topk2 = extra->topk;
+  p.topk_length2 = extra->topk_length;
+}
+
 smla_status smla_prefill(const void* q, int64_t T, int32_t H, int64_t q_stride_t, int64_t q_stride_h,
                          smla_kv_pool kv, const int32_t* indices, int32_t topk, int64_t idx_stride_t,
                          const int32_t* topk_length, const float* sink, float sm_scale, void* out,
                          int64_t out_stride_t, int64_t out_stride_h, float* lse, int64_t lse_stride_t,
                          void* stream) {
+  return smla_prefill_dual(q, T, H, q_stride_t, q_stride_h, kv, indices, topk, idx_stride_t, topk_length, nullptr,
+                           sink, sm_scale, out, out_stride_t, out_stride_h, lse, lse_stride_t, stream);
+}
+
+smla_status smla_prefill_dual(const void* q, int64_t T, int32_t H, int64_t q_stride_t, int64_t q_stride_h,
+                              smla_kv_pool kv, const int32_t* indices, int32_t topk, int64_t idx_stride_t,
+                              const int32_t* topk_length, const smla_kv_extra* extra, const float* sink,
+                              float sm_scale, void* out, int64_t out_stride_t, int64_t out_stride_h, float* lse,
+                              int64_t lse_stride_t, void* stream) {
   smla_status st = check_attn_common(q, T, H, q_stride_t, q_stride_h, kv, indices, topk, idx_stride_t);
   if (st != SMLA_OK) return st;
   if (T == 0) return ok();
+  st = check_extra(kv, topk, extra);
+  if (st != SMLA_OK) return st;
   st = check_out(out, out_stride_t, out_stride_h, H, lse, lse_stride_t);
   if (st != SMLA_OK) return st;
   if (!std::isfinite(sm_scale)) return fail(SMLA_ERR_SHAPE, "sm_scale must be finite");
   if (T == 0) return ok();
   smla::AttnParams p{};
   fill_attn(p, q, T, H, q_stride_t, q_stride_h, kv, indices, topk, idx_stride_t, topk_length, sm_scale);
+  fill_extra(p, extra);
   p.sink = sink;
   p.out = static_cast<uint16_t*>(out);
   p.out_st = out_stride_t;
@@ -201,9 +246,19 @@ smla_status smla_decode(const void* q, int64_t T, int32_t H, int64_t q_stride_t,
                         smla_kv_pool kv, const int32_t* indices, int32_t topk, int64_t idx_stride_t,
                         const int32_t* topk_length, float sm_scale, int32_t num_splits, float* part_out,
                         float* part_lse, void* stream) {
+  return smla_decode_dual(q, T, H, q_stride_t, q_stride_h, kv, indices, topk, idx_stride_t, topk_length, nullptr,
+                          sm_scale, num_splits, part_out, part_lse, stream);
+}
+
+smla_status smla_decode_dual(const void* q, int64_t T, int32_t H, int64_t q_stride_t, int64_t q_stride_h,
+                             smla_kv_pool kv, const int32_t* indices, int32_t topk, int64_t idx_stride_t,
+                             const int32_t* topk_length, const smla_kv_extra* extra, float sm_scale,
+                             int32_t num_splits, float* part_out, float* part_lse, void* stream) {
   smla_status st = check_attn_common(q, T, H, q_stride_t, q_stride_h, kv, indices, topk, idx_stride_t);
   if (st != SMLA_OK) return st;
   if (T == 0) return ok();
+  st = check_extra(kv, topk, extra);
+  if (st != SMLA_OK) return st;
   if (num_splits < 1 || num_splits > 64)
     return fail(SMLA_ERR_UNSUPPORTED, "num_splits = %d is not supported (supported: 1..64)", num_splits);
   if (!part_out) return fail(SMLA_ERR_NULL, "part_out is NULL");
@@ -214,10 +269,11 @@ smla_status smla_decode(const void* q, int64_t T, int32_t H, int64_t q_stride_t,
   if (T == 0) return ok();
   smla::AttnParams p{};
   fill_attn(p, q, T, H, q_stride_t, q_stride_h, kv, indices, topk, idx_stride_t, topk_length, sm_scale);
+  fill_extra(p, extra);
   p.part_out = part_out;
   p.part_lse = part_lse;
   p.num_splits = num_splits;
-  p.split_w = smla_split_width(topk, num_splits);
+  p.split_w = smla_split_width(topk + p.topk2, num_splits);
   p.splits_per_block = 1;
   return launched(smla::launch_attention(p, kv.format, true, static_cast<hipStream_t>(stream)), "decode");
 }

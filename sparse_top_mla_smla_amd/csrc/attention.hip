@@ -26,8 +26,11 @@
 // Each wave keeps its own (max, sum, O) over its candidates; the four
 // states are merged through LDS once at the end (the same log-sum-exp merge
 // the decode combine uses).
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
+#include "lists.h"
 
 namespace smla {
 
@@ -35,30 +38,42 @@ constexpr int TILE_C = 64;     // candidates per tile
 constexpr int NTHREADS = 256;  // 4 waves
 constexpr float LAZY_TAU = 8.0f;
 
-template <int FMT>
+// DUAL: the call has a secondary list, and the index stage holds row
+// addresses (0: no candidate) instead of main-pool slots (-1: none); the
+// single-list kernels keep the narrower stage and its registers.
+template <int FMT, bool DUAL>
 struct Cfg {
   using G = RowGeom<FMT>;
+  using IdxT = typename std::conditional<DUAL, uint64_t, int32_t>::type;
+  static constexpr IdxT NONE = DUAL ? (IdxT)0 : (IdxT)-1;
+  // (a slot stage holds NONE or slots >= 0: testing the sign lets the
+  // compiler form row addresses with shifts)
+  static __device__ __forceinline__ bool present(IdxT e) {
+    if constexpr (DUAL) return e != 0;
+    return e >= 0;
+  }
   static constexpr int LDS_ROW = G::BYTES + 16;                 // padded row stride
   static constexpr int TILE_BYTES = TILE_C * LDS_ROW;
-  static constexpr int IDX_OFF = TILE_BYTES;                    // int32 [3][64]
+  static constexpr int IDX_OFF = TILE_BYTES;                    // IdxT [3][64]
   static constexpr int RED_O_BYTES = 2 * 16 * D_V * 4;          // two waves' O
   static constexpr int RED_ML_OFF = RED_O_BYTES;                // [4 waves][16][2] f32
   static constexpr int LDS_BYTES =
-      (TILE_BYTES + 3 * TILE_C * 4) > (RED_O_BYTES + 4 * 16 * 2 * 4)
-          ? (TILE_BYTES + 3 * TILE_C * 4)
+      (TILE_BYTES + 3 * TILE_C * (int)sizeof(IdxT)) > (RED_O_BYTES + 4 * 16 * 2 * 4)
+          ? (TILE_BYTES + 3 * TILE_C * (int)sizeof(IdxT))
           : (RED_O_BYTES + 4 * 16 * 2 * 4);
   static constexpr int TOTAL_CHUNKS = TILE_C * G::CHUNKS;
   static constexpr int NCH = (TOTAL_CHUNKS + NTHREADS - 1) / NTHREADS;  // staged chunks/thread
 };
 
-template <int FMT, bool DECODE>
+template <int FMT, bool DECODE, bool DUAL>
 __global__ __launch_bounds__(NTHREADS, 1) void attn_kernel(AttnParams p) {
-  using C = Cfg<FMT>;
+  using C = Cfg<FMT, DUAL>;
+  using IdxT = typename C::IdxT;
   using G = RowGeom<FMT>;
   constexpr bool QUANT = FMT != FMT_BF16;
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS_BYTES];
   uint8_t* tile = smem;
-  int32_t* idx_lds = reinterpret_cast<int32_t*>(smem + C::IDX_OFF);
+  IdxT* idx_lds = reinterpret_cast<IdxT*>(smem + C::IDX_OFF);
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -70,19 +85,17 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_kernel(AttnParams p) {
   const int h0 = blockIdx.y * 16;
   const int split = DECODE ? (int)blockIdx.z : 0;
 
-  // candidate range of this workgroup
-  int64_t L = p.topk;
-  if (p.topk_length) {
-    int64_t v = p.topk_length[t];
-    L = v < 0 ? 0 : (v > p.topk ? p.topk : v);
-  }
-  int64_t j_begin = 0, j_end = p.topk;
+  // candidate range of this workgroup over the token's list positions
+  const ListEnds le = list_ends(p, t);
+  const Sources src_lists = sources<DUAL>(p);
+  const int64_t topk_all = (int64_t)p.topk + p.topk2;
+  int64_t j_begin = 0, j_end = topk_all;
   if (DECODE) {
     j_begin = (int64_t)split * p.split_w;
     j_end = j_begin + p.split_w;
-    if (j_end > p.topk) j_end = p.topk;
+    if (j_end > topk_all) j_end = topk_all;
   }
-  if (j_end > L) j_end = L;
+  if (j_end > le.end) j_end = le.end;
   const int n_tiles = j_end > j_begin ? (int)((j_end - j_begin + TILE_C - 1) / TILE_C) : 0;
 
   // Q^T as the B operand of S^T = K Q^T: lane holds Q[h0+lc][32ks + 8lg + i]
@@ -98,31 +111,41 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_kernel(AttnParams p) {
     }
   }
 
-  const int32_t* idx_row = p.idx + t * p.idx_st;
-  auto load_idx = [&](int k) -> int32_t {
+  // index stage entry of list position j_begin + 64k + tid: with a
+  // secondary list the address of its row, else its main-pool slot; NONE
+  // when the position holds no candidate
+  auto load_idx = [&](int k) -> IdxT {
     int64_t j = j_begin + (int64_t)k * TILE_C + tid;
-    int32_t v = -1;
-    if (j < j_end) {
-      int32_t x = idx_row[j];
-      if (x >= 0 && (int64_t)x < p.nslots) v = x;
+    IdxT v = C::NONE;
+    if (j < j_end && in_list<DUAL>(p, le, j)) {
+      const int32_t x = *entry_ptr<DUAL>(src_lists, t, j);
+      if constexpr (DUAL) {
+        v = (uint64_t)row_of<DUAL>(src_lists, j, x);
+      } else {
+        if (x >= 0 && (int64_t)x < p.nslots) v = x;
+      }
     }
     return v;
   };
 
   uint4 stage[C::NCH];
   auto issue_rows = [&](int k) {
-    const int32_t* il = idx_lds + (k % 3) * TILE_C;
+    const IdxT* il = idx_lds + (k % 3) * TILE_C;
 #pragma unroll
     for (int r = 0; r < C::NCH; ++r) {
       const int qc = tid + r * NTHREADS;
       uint4 v = make_uint4(0, 0, 0, 0);
       if (qc < C::TOTAL_CHUNKS) {
         const int row = qc / G::CHUNKS, ck = qc % G::CHUNKS;
-        const int32_t slot = il[row];
-        if (slot >= 0) {
-          const uint8_t* src = p.pool + (int64_t)(slot / PAGE) * p.block_stride +
-                               (int64_t)(slot % PAGE) * p.row_stride + 16 * ck;
-          v = *reinterpret_cast<const uint4*>(src);
+        const IdxT e = il[row];
+        if (C::present(e)) {
+          const uint8_t* src;
+          if constexpr (DUAL) {
+            src = (const uint8_t*)e;
+          } else {
+            src = p.pool + (int64_t)(e / PAGE) * p.block_stride + (int64_t)(e % PAGE) * p.row_stride;
+          }
+          v = *reinterpret_cast<const uint4*>(src + 16 * ck);
         }
       }
       stage[r] = v;
@@ -160,7 +183,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_kernel(AttnParams p) {
 
   for (int k = 0; k < n_tiles; ++k) {
     if (k + 1 < n_tiles) issue_rows(k + 1);
-    int32_t pend = -1;
+    IdxT pend = C::NONE;
     if (k + 2 < n_tiles && tid < TILE_C) pend = load_idx(k + 2);
 
     // ---- S^T for this wave's 16 candidates x 16 heads ----
@@ -189,7 +212,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_kernel(AttnParams p) {
     }
 
     // scores of candidates c = 16*wave + 4lg + i for head lc
-    const int32_t* il = idx_lds + (k % 3) * TILE_C + 16 * wave + 4 * lg;
+    const IdxT* il = idx_lds + (k % 3) * TILE_C + 16 * wave + 4 * lg;
     float s[4];
     f32x4 sc[4];  // sc[i][g]: scale of row (4lg+i), 128-group g
     if constexpr (QUANT) {
@@ -207,7 +230,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_kernel(AttnParams p) {
       } else {
         v = acc[0][i];
       }
-      s[i] = il[i] >= 0 ? v * p.scale_log2 : -INFINITY;
+      s[i] = C::present(il[i]) ? v * p.scale_log2 : -INFINITY;
     }
 
     // ---- online softmax (lazy max) ----
@@ -356,10 +379,13 @@ template <int FMT>
 static hipError_t launch_fmt(const AttnParams& p, bool decode, hipStream_t s) {
   dim3 block(NTHREADS);
   dim3 grid((unsigned)p.T, (unsigned)((p.H + 15) / 16), decode ? (unsigned)p.num_splits : 1u);
-  if (decode)
-    hipLaunchKernelGGL((attn_kernel<FMT, true>), grid, block, 0, s, p);
-  else
-    hipLaunchKernelGGL((attn_kernel<FMT, false>), grid, block, 0, s, p);
+  if (p.topk2 > 0) {
+    if (decode) hipLaunchKernelGGL((attn_kernel<FMT, true, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((attn_kernel<FMT, false, true>), grid, block, 0, s, p);
+  } else {
+    if (decode) hipLaunchKernelGGL((attn_kernel<FMT, true, false>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((attn_kernel<FMT, false, false>), grid, block, 0, s, p);
+  }
   return hipGetLastError();
 }
 

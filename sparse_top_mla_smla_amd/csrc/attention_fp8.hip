@@ -46,6 +46,7 @@
 // to be finite, as the cache writer produces them).
 #include "device_common.h"
 #include "launch.h"
+#include "lists.h"
 
 namespace smla {
 
@@ -142,7 +143,7 @@ struct Buf {
 };
 }  // namespace f8
 
-template <bool DECODE>
+template <bool DECODE, bool DUAL>
 __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
   using namespace f8;
   // Separate LDS objects, and a loop unrolled by two so that every access
@@ -171,76 +172,103 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
   const int sp0 = DECODE ? (int)blockIdx.z * p.splits_per_block : 0;
   const int sp_end = DECODE ? min(sp0 + p.splits_per_block, p.num_splits) : 1;
   const int32_t t_stride = gridDim.x;
+  const Sources src_lists = sources<DUAL>(p);
 
-  // end of token tt's candidate range: its list length clamped to [0, topk]
-  // (read through the scalar cache: a vector load would make the wait for
-  // it also wait for the gathers in flight)
-  auto list_end = [&](int32_t tt) -> int32_t {
-    if (!p.topk_length) return p.topk;
-    const int32_t v = *(const __attribute__((address_space(4))) int32_t*)(p.topk_length + tt);
-    return v < 0 ? 0 : (v > p.topk ? p.topk : v);
+  // token tt's list lengths (read through the scalar cache: a vector load
+  // would make the wait for it also wait for the gathers in flight)
+  auto token_lists = [&](int32_t tt) -> ListEnds {
+    int32_t l1 = p.topk, l2 = 0;
+    if (p.topk_length) l1 = clamp_len(*(const __attribute__((address_space(4))) int32_t*)(p.topk_length + tt), p.topk);
+    if constexpr (DUAL) {
+      l2 = p.topk2;
+      if (p.topk_length2) l2 = clamp_len(*(const __attribute__((address_space(4))) int32_t*)(p.topk_length2 + tt), p.topk2);
+    }
+    return list_ends_of(p, l1, l2);
   };
-  // A tile is list positions [j0, j0 + 64) of token t, cut at jend (t < 0:
-  // no tile; T and topk fit in 31 bits).  Prefill: the workgroup takes tokens blockIdx.x,
+  // A tile is list positions [j0, j0 + 64) of token t, cut at jend, with
+  // the main list's length l1 (positions [l1, topk) hold no candidate; t < 0:
+  // no tile; T and the list widths fit in 31 bits).  Prefill: the workgroup takes tokens blockIdx.x,
   // blockIdx.x + gridDim.x, ... and its tile pipeline (gather one tile
   // ahead, index list two tiles ahead) runs on across token boundaries, so
   // no token pays for filling it.  Decode: the tiles of one token's split
   // range.
   struct TileRef {
-    int32_t t, j0, jend;
+    int32_t t, j0, jend, l1;
   };
-  const TileRef none{-1, 0, 0};
+  // (values are built field by field, never chosen between two objects, so
+  // the references stay in registers)
   auto first_tile = [&](int32_t t0) -> TileRef {
+    TileRef r{-1, 0, 0, 0};
     if (DECODE) {
+      const ListEnds le = token_lists(t0);
       const int64_t jb = (int64_t)sp0 * p.split_w;
       int64_t je = (int64_t)sp_end * p.split_w;
-      if (je > p.topk) je = p.topk;
-      const int32_t L = list_end(t0);
-      if (je > L) je = L;
-      return je > jb ? TileRef{t0, (int32_t)jb, (int32_t)je} : none;
+      const int64_t topk_all = DUAL ? (int64_t)p.topk + p.topk2 : (int64_t)p.topk;
+      if (je > topk_all) je = topk_all;
+      if (je > le.end) je = le.end;
+      if (je > jb) {
+        r.t = t0;
+        r.j0 = (int32_t)jb;
+        r.jend = (int32_t)je;
+        r.l1 = le.l1;
+      }
+      return r;
     }
     for (int32_t tt = t0; tt < p.T; tt += t_stride) {
-      const int32_t je = list_end(tt);
-      if (je > 0) return TileRef{tt, 0, je};
+      const ListEnds le = token_lists(tt);
+      if (le.end > 0) {
+        r.t = tt;
+        r.j0 = (DUAL && le.l1 == 0) ? p.topk : 0;
+        r.jend = le.end;
+        r.l1 = le.l1;
+        break;
+      }
     }
-    return none;
+    return r;
   };
-  auto advance = [&](const TileRef& r) -> TileRef {
-    if (r.t < 0) return none;
-    if (r.j0 + TC < r.jend) return TileRef{r.t, r.j0 + TC, r.jend};
-    return DECODE ? none : first_tile(r.t + t_stride);
+  // Prefill skips the positions between the main list's length and the
+  // secondary list; decode keeps its tiles contiguous, so split ends fall
+  // on tile counts (a skipped range holds no candidate either way).
+  auto advance = [&](TileRef r) -> TileRef {
+    if (r.t < 0) return r;
+    int32_t nj = r.j0 + TC;
+    if (DUAL && !DECODE && nj >= r.l1 && nj < p.topk) nj = p.topk;
+    if (nj < r.jend) {
+      r.j0 = nj;
+      return r;
+    }
+    if (DECODE) {
+      r.t = -1;
+      return r;
+    }
+    return first_tile(r.t + t_stride);
   };
+  // list position j of tile r holds a candidate position
+  auto in_tile = [&](TileRef r, int32_t j) -> bool { return j < r.jend && (!DUAL || j < r.l1 || j >= p.topk); };
 
-  // byte offset in the pool of the row of index value x (-1: masked or not
-  // a pool slot)
-  auto row_offset = [&](int32_t x) -> int64_t {
-    return (x >= 0 && (int64_t)x < p.nslots) ? (int64_t)(x / PAGE) * p.block_stride + (int64_t)(x % PAGE) * p.row_stride
-                                             : (int64_t)-1;
-  };
   // wave 0 moves the index list entries of tile r into index buffer B
-  // (entries past the range are not loaded; readers check the range)
+  // (positions without a candidate are not loaded; readers check them)
   auto issue_idx = [&](auto buf, const TileRef& r) {
     constexpr int B = decltype(buf)::value;
     const int32_t j = r.j0 + lane;
-    if (j < r.jend) global_to_lds_4(p.idx + (int64_t)r.t * p.idx_st + j, B ? idx1 : idx0);
+    if (in_tile(r, j)) global_to_lds_4(entry_ptr<DUAL>(src_lists, r.t, j), B ? idx1 : idx0);
   };
   // wave w moves pieces w, w + 8, ... of all 64 rows of a tile (lane = row)
   // into raw buffer B, in part P (0..2) the pieces of rounds 2P and 2P + 1.
   // Spreading the issue over the tile keeps the address unit's queue short,
   // so no wave stalls long at issue.  Wave 0 records which rows exist.
-  auto issue_part = [&](auto buf, auto part, int64_t off) {
+  auto issue_part = [&](auto buf, auto part, const uint8_t* src) {
     constexpr int B = decltype(buf)::value;
     constexpr int P = decltype(part)::value;
     uint8_t* raw = B ? raw1 : raw0;
-    if (off >= 0) {
-      const uint8_t* src = p.pool + off;
+    if (src) {
 #pragma unroll
       for (int r = 2 * P; r < 2 * P + 2; ++r) {
         const int ck = w + 8 * r;
         if (r + 1 < GROUNDS || ck < CHUNKS) global_to_lds_16(src + 16 * ck, raw + ck * CS);
       }
     }
-    if (P == 0 && w == 0) valid[B * TC + lane] = off >= 0;
+    if (P == 0 && w == 0) valid[B * TC + lane] = src != nullptr;
   };
   static_assert(2 * GPARTS == GROUNDS, "three parts of two rounds");
 
@@ -273,11 +301,11 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
   // inside the range, selected after), then Q: the compiler barrier keeps
   // the Q loads behind the wait for the entries, so they are in flight
   // during the zero fill and the first gather instead of delaying its issue
-  int32_t entry0 = -1;
+  const uint8_t* src0 = nullptr;
   if (cur.t >= 0) {
     const int32_t j = cur.j0 + lane;
-    const int32_t x = p.idx[(int64_t)cur.t * p.idx_st + (j < cur.jend ? j : cur.jend - 1)];
-    entry0 = j < cur.jend ? x : -1;
+    const int32_t x = *entry_ptr<DUAL>(src_lists, cur.t, j < cur.jend ? j : cur.jend - 1);
+    src0 = in_tile(cur, j) ? row_of<DUAL>(src_lists, j, x) : nullptr;
   }
   asm volatile("" ::: "memory");
   if (cur.t >= 0) load_q(cur.t);
@@ -331,7 +359,7 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
   // prefill: the workgroup's tokens with an empty list (O is still zero)
   if (!DECODE && p.topk_length) {
     for (int32_t tt = blockIdx.x; tt < p.T; tt += t_stride)
-      if (list_end(tt) == 0) store_result(tt, 0.0f, -INFINITY);
+      if (token_lists(tt).end == 0) store_result(tt, 0.0f, -INFINITY);
   }
 
   if (cur.t >= 0) {
@@ -339,12 +367,11 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
       reinterpret_cast<uint4*>(raw0)[i] = make_uint4(0, 0, 0, 0);
       reinterpret_cast<uint4*>(raw1)[i] = make_uint4(0, 0, 0, 0);
     }
-    const int64_t off0 = row_offset(entry0);
     // the zero fill is complete everywhere before any gather lands
     lds_barrier();
-    issue_part(Buf<0>{}, Buf<0>{}, off0);
-    issue_part(Buf<0>{}, Buf<1>{}, off0);
-    issue_part(Buf<0>{}, Buf<2>{}, off0);
+    issue_part(Buf<0>{}, Buf<0>{}, src0);
+    issue_part(Buf<0>{}, Buf<1>{}, src0);
+    issue_part(Buf<0>{}, Buf<2>{}, src0);
     if (w == 0 && nxt.t >= 0) issue_idx(Buf<1>{}, nxt);
     // the sink, in flight beside the first gather
     if (!DECODE && p.sink) {
@@ -363,12 +390,11 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
     // gather of the next tile (its index list arrived before B0), then the
     // index list one tile further ahead, read after the next B0
     const bool more = nxt.t >= 0;
-    int64_t off_next = -1;
+    const uint8_t* src_next = nullptr;
     if (more) {
       const int32_t j = nxt.j0 + lane;
-      const int32_t x = j < nxt.jend ? (B ? idx0 : idx1)[lane] : -1;
-      off_next = row_offset(x);
-      issue_part(Buf<1 - B>{}, Buf<0>{}, off_next);
+      src_next = in_tile(nxt, j) ? row_of<DUAL>(src_lists, j, (B ? idx0 : idx1)[lane]) : nullptr;
+      issue_part(Buf<1 - B>{}, Buf<0>{}, src_next);
     }
     if (w == 0 && nn.t >= 0) issue_idx(Buf<B>{}, nn);
     if (pend >= 0) {
@@ -426,7 +452,7 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
         }
       }
     lds_barrier();  // B1: partials visible
-    if (more) issue_part(Buf<1 - B>{}, Buf<1>{}, off_next);
+    if (more) issue_part(Buf<1 - B>{}, Buf<1>{}, src_next);
 
     {
       const f32x4* src = reinterpret_cast<const f32x4*>(recv) + w * 3 * 128 + lane;
@@ -447,7 +473,7 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
       if (hi == 0) maxb[g * 64 + 32 * hh + l32] = mx;
     }
     lds_barrier();  // B2: block maxima visible; every partial has been read
-    if (more) issue_part(Buf<1 - B>{}, Buf<2>{}, off_next);
+    if (more) issue_part(Buf<1 - B>{}, Buf<2>{}, src_next);
 
     float alpha;
     {
@@ -647,8 +673,11 @@ hipError_t launch_attention_fp8(const AttnParams& p, bool decode, hipStream_t s)
   dim3 block(f8::NT);
   dim3 grid(decode ? (unsigned)q.T : (unsigned)fp8_prefill_blocks(q.T, q.H, cus), (unsigned)((q.H + 63) / 64),
             decode ? (unsigned)((q.num_splits + q.splits_per_block - 1) / q.splits_per_block) : 1u);
-  if (decode) hipLaunchKernelGGL((attn_fp8_kernel<true>), grid, block, 0, s, q);
-  else hipLaunchKernelGGL((attn_fp8_kernel<false>), grid, block, 0, s, q);
+  const bool dual = q.topk2 > 0;
+  if (decode && dual) hipLaunchKernelGGL((attn_fp8_kernel<true, true>), grid, block, 0, s, q);
+  else if (decode) hipLaunchKernelGGL((attn_fp8_kernel<true, false>), grid, block, 0, s, q);
+  else if (dual) hipLaunchKernelGGL((attn_fp8_kernel<false, true>), grid, block, 0, s, q);
+  else hipLaunchKernelGGL((attn_fp8_kernel<false, false>), grid, block, 0, s, q);
   return hipGetLastError();
 }
 

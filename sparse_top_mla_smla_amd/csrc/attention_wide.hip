@@ -41,6 +41,7 @@
 // exactly 0.
 #include "device_common.h"
 #include "launch.h"
+#include "lists.h"
 
 namespace smla {
 
@@ -87,7 +88,7 @@ constexpr float TAU = 8.0f;
 // output columns likewise) for head half hh (heads [32hh, 32hh+32)).  Score
 // tile (c2, hh) -- candidates [32c2, +32) x heads [32hh, +32) -- is owned by
 // wave c2 + 6hh (waves 0, 1, 6, 7: one owner per SIMD); waves 2..5 gather.
-template <int FMT, bool DECODE>
+template <int FMT, bool DECODE, bool DUAL>
 __global__ __launch_bounds__(wide::NT, 1) void attn_wide_kernel(AttnParams p) {
   using namespace wide;
   static_assert(FMT == FMT_FP8 || FMT == FMT_INT8, "wide kernel serves quantized caches");
@@ -113,18 +114,16 @@ __global__ __launch_bounds__(wide::NT, 1) void attn_wide_kernel(AttnParams p) {
   const int h0 = blockIdx.y * 64;
   const int split = DECODE ? (int)blockIdx.z : 0;
 
-  int64_t L = p.topk;
-  if (p.topk_length) {
-    const int64_t v = p.topk_length[t];
-    L = v < 0 ? 0 : (v > p.topk ? p.topk : v);
-  }
-  int64_t j_begin = 0, j_end = p.topk;
+  const ListEnds le = list_ends(p, t);
+  const Sources src_lists = sources<DUAL>(p);
+  const int64_t topk_all = (int64_t)p.topk + p.topk2;
+  int64_t j_begin = 0, j_end = topk_all;
   if (DECODE) {
     j_begin = (int64_t)split * p.split_w;
     j_end = j_begin + p.split_w;
-    if (j_end > p.topk) j_end = p.topk;
+    if (j_end > topk_all) j_end = topk_all;
   }
-  if (j_end > L) j_end = L;
+  if (j_end > le.end) j_end = le.end;
   const int n_tiles = j_end > j_begin ? (int)((j_end - j_begin + TC - 1) / TC) : 0;
 
   // Q as the B operand of S^T = K Q^T for head h0 + 32hh + l32.  A K lane
@@ -150,31 +149,25 @@ __global__ __launch_bounds__(wide::NT, 1) void attn_wide_kernel(AttnParams p) {
     }
   }
 
-  const int32_t* idx_row = p.idx + t * p.idx_st;
-  // byte offset in the pool of the row of list entry k*64 + lane of this
-  // workgroup's range, or -1 when the entry is masked or not a pool slot
-  auto row_offset = [&](int k) -> int64_t {
+  // the row of list position j_begin + k*64 + lane of this workgroup's
+  // range, or null when the position holds no candidate
+  auto row_offset = [&](int k) -> const uint8_t* {
     const int64_t j = j_begin + (int64_t)k * TC + lane;
-    int64_t v = -1;
-    if (j < j_end) {
-      const int32_t x = idx_row[j];
-      if (x >= 0 && (int64_t)x < p.nslots) v = (int64_t)(x / PAGE) * p.block_stride + (int64_t)(x % PAGE) * p.row_stride;
-    }
-    return v;
+    if (j >= j_end || !in_list<DUAL>(p, le, j)) return nullptr;
+    return row_of<DUAL>(src_lists, j, *entry_ptr<DUAL>(src_lists, t, j));
   };
   // gather wave nw moves pieces nw, nw + 4, ... of all 64 rows of tile k
   // (lane = row) into raw buffer k&1, and wave 2 records which rows exist
-  auto issue_tile = [&](int k, int64_t off) {
+  auto issue_tile = [&](int k, const uint8_t* src) {
     uint8_t* raw = smem + OFF_RAW + (k & 1) * TILE;
-    if (off >= 0) {
-      const uint8_t* src = p.pool + off;
+    if (src) {
 #pragma unroll
       for (int r = 0; r < GROUNDS; ++r) {
         const int ck = nw + 4 * r;
         if (r + 1 < GROUNDS || ck < CHUNKS) global_to_lds_16(src + 16 * ck, raw + ck * CS);
       }
     }
-    if (nw == 0) valid[(k & 1) * TC + lane] = off >= 0;
+    if (nw == 0) valid[(k & 1) * TC + lane] = src != nullptr;
   };
 
   // running softmax state of an owned score tile (heads 32hh + l32)
@@ -189,7 +182,7 @@ __global__ __launch_bounds__(wide::NT, 1) void attn_wide_kernel(AttnParams p) {
 
   if (n_tiles > 0) {
     for (int i = tid; i < 2 * TILE / 16; i += NT) reinterpret_cast<uint4*>(smem + OFF_RAW)[i] = make_uint4(0, 0, 0, 0);
-    const int64_t off0 = owner ? -1 : row_offset(0);
+    const uint8_t* off0 = owner ? nullptr : row_offset(0);
     __syncthreads();
     if (!owner) issue_tile(0, off0);
   }
@@ -198,7 +191,7 @@ __global__ __launch_bounds__(wide::NT, 1) void attn_wide_kernel(AttnParams p) {
     const uint8_t* raw = smem + OFF_RAW + (k & 1) * TILE;
     __builtin_amdgcn_s_waitcnt(0);  // this wave's part of tile k has landed
     __syncthreads();                // B0: all of tile k is in LDS
-    int64_t pend = -1;
+    const uint8_t* pend = nullptr;
     if (!owner) {
       if (k + 1 < n_tiles) pend = row_offset(k + 1);
       // the gather waves transpose the tile's scales:
@@ -393,8 +386,11 @@ hipError_t launch_attention_wide(const AttnParams& p, int fmt, bool decode, hipS
   dim3 block(wide::NT);
   dim3 grid((unsigned)p.T, (unsigned)((p.H + 63) / 64), decode ? (unsigned)p.num_splits : 1u);
   if (fmt == FMT_INT8) {
-    if (decode) hipLaunchKernelGGL((attn_wide_kernel<FMT_INT8, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((attn_wide_kernel<FMT_INT8, false>), grid, block, 0, s, p);
+    const bool dual = p.topk2 > 0;
+    if (decode && dual) hipLaunchKernelGGL((attn_wide_kernel<FMT_INT8, true, true>), grid, block, 0, s, p);
+    else if (decode) hipLaunchKernelGGL((attn_wide_kernel<FMT_INT8, true, false>), grid, block, 0, s, p);
+    else if (dual) hipLaunchKernelGGL((attn_wide_kernel<FMT_INT8, false, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((attn_wide_kernel<FMT_INT8, false, false>), grid, block, 0, s, p);
   } else {
     return hipErrorInvalidValue;
   }

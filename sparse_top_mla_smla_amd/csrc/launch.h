@@ -44,6 +44,14 @@ struct AttnParams {
   int32_t num_splits;
   int32_t split_w;
   int32_t splits_per_block;  // decode: consecutive splits one workgroup runs (FP8 many-head kernel)
+  // secondary candidate list (list positions [topk, topk + topk2)) over a
+  // second pool of the same format; topk2 = 0: none
+  const uint8_t* pool2;
+  int64_t block_stride2, row_stride2, nslots2;
+  const int32_t* idx2;
+  int64_t idx_st2;
+  int32_t topk2;
+  const int32_t* topk_length2;  // may be null
 };
 
 struct CombineParams {

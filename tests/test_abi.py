@@ -125,3 +125,28 @@ def test_decode_and_combine_validation_before_launch():
     assert dec(T=0, q=None, idx=None, po=None, pls=None) == 0
     assert lib.smla_combine(None, FAKE, 2, 4, 64, None, FAKE, 64 * 512, 512, FAKE, 64, None) == 1
     assert lib.smla_combine(FAKE, FAKE, 0, 4, 64, None, None, 0, 0, None, 0, None) == 0
+
+
+def test_dual_validation_before_launch():
+    lib = smla._load()
+    f = ctypes.c_float(1 / 24)
+
+    def extra(topk=64, idx=FAKE, fmt=W.FMT_FP8, idx_st=64, row_stride=0):
+        return smla._Extra(pool(fmt=fmt, row_stride=row_stride), idx, topk, idx_st, None)
+
+    def call(ex, topk=64, T=2):
+        return lib.smla_prefill_dual(FAKE, T, 64, 64 * 576, 576, pool(), FAKE, topk, 64, None,
+                                     ctypes.byref(ex) if ex is not None else None, None, f, FAKE, 64 * 512, 512,
+                                     FAKE, 64, None)
+
+    assert call(extra(), T=0) == 0
+    assert call(extra(), topk=32) == 4                    # main width not a multiple of 64
+    assert "multiple of 64" in lib.smla_last_error().decode()
+    assert call(extra(topk=0)) == 2
+    assert call(extra(idx=None)) == 1
+    assert call(extra(fmt=W.FMT_INT8)) == 4              # formats differ
+    assert call(extra(idx_st=32)) == 3
+    assert call(extra(row_stride=664)) == 3               # the secondary pool is checked too
+    dec = lib.smla_decode_dual(FAKE, 2, 64, 64 * 576, 576, pool(), FAKE, 64, 64, None, ctypes.byref(extra(topk=0)),
+                               f, 2, FAKE, FAKE, None)
+    assert dec == 2
