@@ -33,10 +33,10 @@ from sparse_top_mla_smla_amd import workloads as W
 POOL_ROWS = 1 << 20  # 16384 blocks: 656 MiB (FP8/INT8) or 1.1 GiB (BF16), beyond the last-level cache
 
 # kernel class -> (format, head counts measured, workgroups per CU per round,
-# heads per block).  The narrow kernel fits two workgroups in a CU's LDS, but
-# two co-resident workgroups share its four SIMDs and each runs about half as
-# fast, so one round still completes about one workgroup per CU: fitted with
-# 2, the model misses the best split count by up to 26%; with 1, by 4%.
+# heads per block).  The narrow kernel's LDS would allow two workgroups per
+# CU, but it holds about 500 registers per lane, so each SIMD runs one of its
+# waves and a CU one workgroup (fitted with 2, the model misses the best
+# split count by up to 26%; with 1, by 4%).
 CLASSES = {
     "fp8_wide": (W.FMT_FP8, (64, 128), 1, 64),
     "int8_wide": (W.FMT_INT8, (128,), 1, 64),

@@ -13,8 +13,8 @@
 //   prefill = ap0 + waves_p * (ap + bp * tiles_per_token)
 // with MB the partial buffers (T * S * H * 2052 bytes), waves the rounds of
 // workgroups over the compute units (one workgroup per CU per round: the
-// many-head kernels fill a CU's LDS, and two co-resident narrow workgroups
-// share the CU's SIMDs), and a, b, f, ap0, ap, bp per kernel class.  The
+// many-head kernels fill a CU's LDS, and the narrow kernel holds about 500
+// registers per lane), and a, b, f, ap0, ap, bp per kernel class.  The
 // constants were fitted by sparse_top_mla_smla_amd/calibrate_splits.py on
 // one MI355X (256 CUs) over 126 decode shapes and their prefill
 // counterparts; there the pick is on average 0.2% and at most 7.7% slower
