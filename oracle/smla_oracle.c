@@ -29,8 +29,9 @@
  * 576-element dequantized latent and V = its first 512 elements; natural-log
  * LSE that excludes the sink; the sink is one extra logit per head (in
  * scaled-score units) that carries no value; an empty candidate set gives
- * out = 0 and lse = -inf; scales are 2^ceil(log2(amax/448)) (FP8) or
- * amax/127 (INT8), amax = 0 giving scale 1; every index outside
+ * out = 0 and lse = -inf; scales are 2^ceil(log2(amax/448)) (FP8),
+ * amax/448 (FP8 with arbitrary scales, the GLM_NSA rows of FlashInfer #4802's
+ * KV layout comment) or amax/127 (INT8), amax = 0 giving scale 1; every index outside
  * [0, num_blocks*64) -- -1 padding included -- contributes nothing.
  *
  * Precision: all attention arithmetic is float64.  The quantizer runs in
@@ -52,7 +53,7 @@
 #define PAGE_BLOCK 64
 #define TILE 128 /* quantization tile width along the nope part */
 
-enum { FMT_BF16 = 0, FMT_FP8 = 1, FMT_INT8 = 2 };
+enum { FMT_BF16 = 0, FMT_FP8 = 1, FMT_INT8 = 2, FMT_FP8_ANY = 3 };
 
 /* ---------------------------------------------------------------------- */
 /* Scalar helpers                                                          */
@@ -129,6 +130,14 @@ float oracle_fp8_scale(float amax) {
   return ldexpf(1.0f, e);
 }
 
+/* Tile scale of FP8 rows with arbitrary scales: amax = 0 -> 1; otherwise
+ * amax / 448 (float32), so the tile's largest magnitude maps to the largest
+ * e4m3 value. */
+float oracle_fp8_any_scale(float amax) {
+  if (amax == 0.0f) return 1.0f;
+  return amax / 448.0f;
+}
+
 /* INT8 tile scale: amax = 0 -> 1; otherwise amax / 127 (float32). */
 float oracle_int8_scale(float amax) {
   if (amax == 0.0f) return 1.0f;
@@ -162,10 +171,12 @@ static void quantize_row(const uint16_t* x, int32_t fmt, uint8_t* row) {
       float v = fabsf(bf16_bits_to_float(x[i]));
       if (v > amax) amax = v;
     }
-    float scale = (fmt == FMT_FP8) ? oracle_fp8_scale(amax) : oracle_int8_scale(amax);
+    float scale = (fmt == FMT_FP8)       ? oracle_fp8_scale(amax)
+                  : (fmt == FMT_FP8_ANY) ? oracle_fp8_any_scale(amax)
+                                         : oracle_int8_scale(amax);
     for (int i = g * TILE; i < (g + 1) * TILE; ++i) {
       float xv = bf16_bits_to_float(x[i]);
-      if (fmt == FMT_FP8)
+      if (fmt == FMT_FP8 || fmt == FMT_FP8_ANY)
         row[i] = oracle_e4m3_encode(xv / scale);
       else
         row[i] = (uint8_t)oracle_int8_encode(xv, scale);
@@ -211,7 +222,7 @@ static void dequant_row(const uint8_t* pool, int64_t block_stride_bytes, int32_t
   float scale[D_NOPE / TILE];
   memcpy(scale, row + D_NOPE, sizeof scale);
   for (int i = 0; i < D_NOPE; ++i) {
-    double c = (fmt == FMT_FP8) ? oracle_e4m3_decode(row[i]) : (double)(int8_t)row[i];
+    double c = (fmt == FMT_FP8 || fmt == FMT_FP8_ANY) ? oracle_e4m3_decode(row[i]) : (double)(int8_t)row[i];
     K[i] = c * (double)scale[i / TILE];
   }
   for (int r = 0; r < D_ROPE; ++r) {

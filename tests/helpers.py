@@ -26,7 +26,7 @@ def np_dequant(pool: oracle.Pool, slots) -> np.ndarray:
     if pool.fmt == W.FMT_BF16:
         return W.bf16_bits_to_f32(rows.copy().view(np.uint16)).astype(np.float64)
     scales = rows[:, 512:528].copy().view(np.float32).astype(np.float64)
-    if pool.fmt == W.FMT_FP8:
+    if pool.fmt in (W.FMT_FP8, W.FMT_FP8_ANY):
         codes = torch.tensor(rows[:, :512].copy()).view(torch.float8_e4m3fn).double().numpy()
     else:
         codes = rows[:, :512].view(np.int8).astype(np.float64)

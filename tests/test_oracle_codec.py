@@ -175,6 +175,41 @@ def test_int8_quantizer_vs_numpy(orc):
     assert np.array_equal(rows[:, 528:656].copy().view(np.uint16), kv[:, 512:])
 
 
+def test_fp8_any_scale_quantizer(orc):
+    """FP8 rows with arbitrary scales: scale = amax/448 in float32 (1 for an
+    all-zero tile), codes = torch's e4m3 encoding of x/scale, the tile's
+    largest magnitude encodes to 448, and the decoded value is within half an
+    e4m3 ulp (times the scale) of x."""
+    def tweak(kv):
+        kv = kv.copy()
+        kv[0, :128] = 0
+        kv[2, 256:384] = W.f32_to_bf16_bits(np.float32(3e4) * np.linspace(-1, 1, 128, dtype=np.float32))
+        kv[3, :128] = W.f32_to_bf16_bits(np.float32(1e-20) * np.arange(128, dtype=np.float32))
+        return kv
+    kv, pool = _pool_for(W.FMT_FP8_ANY, 128, seed=11, tweak=tweak)
+    assert orc.row_bytes(W.FMT_FP8_ANY) == 656
+    rows = pool.data.reshape(-1, 656)[:128]
+    x32 = W.bf16_bits_to_f32(kv)[:, :512].reshape(128, 4, 128)
+    amax = np.abs(x32).max(axis=2).astype(np.float32)
+    scale = np.where(amax == 0, np.float32(1), amax / np.float32(448)).astype(np.float32)
+    got_scale = rows[:, 512:528].copy().view(np.float32)
+    assert np.array_equal(got_scale, scale)
+    assert got_scale[0, 0] == 1.0
+    assert not np.all(np.log2(got_scale[1:]) == np.round(np.log2(got_scale[1:])))  # not powers of two
+    y = (x32 / scale[:, :, None]).astype(np.float32)
+    codes = rows[:, :512].reshape(128, 4, 128)
+    assert np.array_equal(codes.reshape(-1), torch_e4m3_encode(y.reshape(-1)))
+    top = np.abs(x32).argmax(axis=2)
+    nz = amax > 0
+    assert np.all((np.take_along_axis(codes, top[:, :, None], 2)[:, :, 0][nz] & 0x7F) == 0x7E)
+    dec = torch_e4m3_decode(codes.reshape(-1)).reshape(128, 4, 128).astype(np.float64)
+    ay = np.abs(y.astype(np.float64))
+    half_ulp = np.where(ay >= 2.0 ** -6, 2.0 ** (np.floor(np.log2(np.maximum(ay, 2.0 ** -6))) - 4), 2.0 ** -10)
+    s64 = scale.astype(np.float64)[:, :, None]
+    assert np.all(np.abs(dec * s64 - x32) <= s64 * half_ulp * (1 + 1e-6))
+    assert np.array_equal(rows[:, 528:656].copy().view(np.uint16), kv[:, 512:])
+
+
 def test_bf16_row_is_a_copy(orc):
     kv, pool = _pool_for(W.FMT_BF16, 64, seed=7)
     assert np.array_equal(pool.data.reshape(64, 1152).view(np.uint16), kv)
