@@ -68,11 +68,16 @@ typedef enum {
  * positive normal powers of two (smla_quantize_kv writes only those); with
  * H > 16 a loaded row with any other scale makes its token's output NaN.
  * INT8 uses the same layout with int8 codes and any positive FP32 scale.
- * BF16 row = 576 BF16 values (1152 bytes). */
+ * FP8_E4M3_ANY_SCALE is the same row with e4m3 codes and arbitrary positive
+ * FP32 scales: the same PR's layout comment says GLM_NSA rows store
+ * arbitrary scales where DSv3.2 rows store powers of two; its cache writer
+ * takes scale = amax/448, and the attention entry points accept any positive
+ * scale for it.  BF16 row = 576 BF16 values (1152 bytes). */
 typedef enum {
   SMLA_KV_BF16 = 0,
   SMLA_KV_FP8_E4M3 = 1,
-  SMLA_KV_INT8 = 2
+  SMLA_KV_INT8 = 2,
+  SMLA_KV_FP8_E4M3_ANY_SCALE = 3
 } smla_kv_format;
 
 /* A paged latent pool.  Slot s (a flat pool position) lives in block s/64 at
@@ -122,7 +127,8 @@ smla_status smla_decode_workspace_size(int64_t T, int32_t H, int32_t num_splits,
  * FP8: per 128-element tile of the nope part, amax = max |x|; scale = 1 when
  * amax = 0, else the power of two 2^ceil(log2(amax/448)) (the page's
  * "power-of-2 FP32 scales"); codes = e4m3(x / scale), round to nearest even,
- * sign kept.  INT8: scale = amax/127 (1 when amax = 0), codes =
+ * sign kept.  FP8_E4M3_ANY_SCALE: scale = amax/448 (FP32, correctly rounded;
+ * 1 when amax = 0), codes as for FP8.  INT8: scale = amax/127 (1 when amax = 0), codes =
  * clamp(rne(x/scale), -127, 127).  BF16: a copy.  Rope values are copied
  * bit for bit.  Two slots that are equal race (last writer wins). */
 smla_status smla_quantize_kv(const void* kv, int64_t n, int64_t kv_stride, const int32_t* slots,

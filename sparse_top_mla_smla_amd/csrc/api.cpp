@@ -36,7 +36,7 @@ smla_status check_pool(const smla_kv_pool& kv) {
     return fail(SMLA_ERR_UNSUPPORTED, "page_block %d is not supported (supported: 64)", kv.page_block);
   int32_t rb = smla_row_bytes(kv.format);
   if (rb < 0)
-    return fail(SMLA_ERR_UNSUPPORTED, "kv format %d is not supported (supported: 0 = BF16, 1 = FP8_E4M3, 2 = INT8)",
+    return fail(SMLA_ERR_UNSUPPORTED, "kv format %d is not supported (supported: 0 = BF16, 1 = FP8_E4M3, 2 = INT8, 3 = FP8_E4M3_ANY_SCALE)",
                 kv.format);
   if (kv.num_blocks < 1) return fail(SMLA_ERR_SHAPE, "num_blocks %lld must be >= 1", (long long)kv.num_blocks);
   if (kv.num_blocks > (int64_t)(INT32_MAX / 64) + 1)
@@ -125,6 +125,7 @@ int32_t smla_row_bytes(int32_t format) {
     case SMLA_KV_BF16: return 1152;
     case SMLA_KV_FP8_E4M3: return 656;
     case SMLA_KV_INT8: return 656;
+    case SMLA_KV_FP8_E4M3_ANY_SCALE: return 656;
     default: return -1;
   }
 }

@@ -391,11 +391,15 @@ static hipError_t launch_fmt(const AttnParams& p, bool decode, hipStream_t s) {
 
 hipError_t launch_attention(const AttnParams& p, int fmt, bool decode, hipStream_t s) {
   // many heads over a quantized cache: one workgroup per token for 64 heads
+  // (FP8 codes with arbitrary scales run the kernels that fold each row's
+  // scale into its partial scores and probabilities, as for INT8)
   if (fmt == FMT_FP8 && p.H > 16) return launch_attention_fp8(p, decode, s);
   if (fmt == FMT_INT8 && p.H > 16) return launch_attention_wide(p, fmt, decode, s);
+  if (fmt == FMT_FP8_ANY && p.H > 16) return launch_attention_wide(p, FMT_FP8, decode, s);
   switch (fmt) {
     case FMT_BF16: return launch_fmt<FMT_BF16>(p, decode, s);
-    case FMT_FP8: return launch_fmt<FMT_FP8>(p, decode, s);
+    case FMT_FP8:
+    case FMT_FP8_ANY: return launch_fmt<FMT_FP8>(p, decode, s);
     case FMT_INT8: return launch_fmt<FMT_INT8>(p, decode, s);
     default: return hipErrorInvalidValue;
   }

@@ -1,11 +1,12 @@
 // attention_wide.hip -- sparse MLA attention for many heads (H > 16) over
-// the INT8 paged latent cache, prefill form and split-KV decode partials.
+// the INT8 paged latent cache, and over FP8 rows with arbitrary scales
+// (GLM_NSA rows), prefill form and split-KV decode partials.
 //
-// What is computed is stated in include/smla.h.  INT8 rows carry arbitrary
-// FP32 scales (amax/127), so code * scale is not exact in BF16: the codes
-// are converted exactly and the scales are applied to FP32 partial scores
-// and folded into P.  (The FP8 cache, whose scales are powers of two, has
-// its own kernel that dequantizes while converting.)  One workgroup owns
+// What is computed is stated in include/smla.h.  These rows carry arbitrary
+// FP32 scales (amax/127, amax/448), so code * scale is not exact in BF16:
+// the codes are converted exactly and the scales are applied to FP32
+// partial scores and folded into P.  (The FP8 cache with power-of-two
+// scales has its own kernel that dequantizes while converting.)  One workgroup owns
 // one token (and split) for 64 heads, so every selected row is gathered
 // from the pool once per token, not once per head group.
 //
@@ -385,12 +386,17 @@ __global__ __launch_bounds__(wide::NT, 1) void attn_wide_kernel(AttnParams p) {
 hipError_t launch_attention_wide(const AttnParams& p, int fmt, bool decode, hipStream_t s) {
   dim3 block(wide::NT);
   dim3 grid((unsigned)p.T, (unsigned)((p.H + 63) / 64), decode ? (unsigned)p.num_splits : 1u);
+  const bool dual = p.topk2 > 0;
   if (fmt == FMT_INT8) {
-    const bool dual = p.topk2 > 0;
     if (decode && dual) hipLaunchKernelGGL((attn_wide_kernel<FMT_INT8, true, true>), grid, block, 0, s, p);
     else if (decode) hipLaunchKernelGGL((attn_wide_kernel<FMT_INT8, true, false>), grid, block, 0, s, p);
     else if (dual) hipLaunchKernelGGL((attn_wide_kernel<FMT_INT8, false, true>), grid, block, 0, s, p);
     else hipLaunchKernelGGL((attn_wide_kernel<FMT_INT8, false, false>), grid, block, 0, s, p);
+  } else if (fmt == FMT_FP8) {
+    if (decode && dual) hipLaunchKernelGGL((attn_wide_kernel<FMT_FP8, true, true>), grid, block, 0, s, p);
+    else if (decode) hipLaunchKernelGGL((attn_wide_kernel<FMT_FP8, true, false>), grid, block, 0, s, p);
+    else if (dual) hipLaunchKernelGGL((attn_wide_kernel<FMT_FP8, false, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((attn_wide_kernel<FMT_FP8, false, false>), grid, block, 0, s, p);
   } else {
     return hipErrorInvalidValue;
   }

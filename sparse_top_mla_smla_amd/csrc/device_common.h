@@ -23,7 +23,8 @@ constexpr int D_V = 512;
 constexpr int PAGE = 64;
 constexpr int QTILE = 128;  // quantization tile along the nope part
 
-enum : int { FMT_BF16 = 0, FMT_FP8 = 1, FMT_INT8 = 2 };
+// FMT_FP8_ANY: FP8 codes with arbitrary positive per-128 scales (the row of FMT_FP8)
+enum : int { FMT_BF16 = 0, FMT_FP8 = 1, FMT_INT8 = 2, FMT_FP8_ANY = 3 };
 
 template <int FMT>
 struct RowGeom {

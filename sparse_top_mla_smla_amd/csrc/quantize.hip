@@ -86,8 +86,8 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantParams p) {
 
     uint32_t code[8];
     float scale;
-    if constexpr (FMT == FMT_FP8) {
-      scale = fp8_tile_scale(amax);
+    if constexpr (FMT == FMT_FP8 || FMT == FMT_FP8_ANY) {
+      scale = FMT == FMT_FP8 ? fp8_tile_scale(amax) : (amax == 0.0f ? 1.0f : __fdiv_rn(amax, 448.0f));
 #pragma unroll
       for (int i = 0; i < 8; ++i) code[i] = e4m3_from_f32(__fdiv_rn(x[i], scale));
     } else {
@@ -117,6 +117,7 @@ hipError_t launch_quantize(const QuantParams& p, int fmt, hipStream_t s) {
     case FMT_BF16: hipLaunchKernelGGL(quantize_kernel<FMT_BF16>, grid, block, 0, s, p); break;
     case FMT_FP8: hipLaunchKernelGGL(quantize_kernel<FMT_FP8>, grid, block, 0, s, p); break;
     case FMT_INT8: hipLaunchKernelGGL(quantize_kernel<FMT_INT8>, grid, block, 0, s, p); break;
+    case FMT_FP8_ANY: hipLaunchKernelGGL(quantize_kernel<FMT_FP8_ANY>, grid, block, 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -40,6 +40,11 @@ CASES = {
     "int8_h128_view": dict(fmt=W.FMT_INT8, H=128, topk=256, idx_ld=384, T=2, with_sink=True,
                            pad_fill=W.PAD_SENTINEL),
     "fp8_tail_neg": dict(fmt=W.FMT_FP8, H=16, topk=64, tail_neg=9, causal=False, T=4),
+    # FP8 codes with arbitrary scales (GLM_NSA rows): narrow kernel and the
+    # many-head kernel that folds scales
+    "fp8any_h8_len_sink": dict(fmt=W.FMT_FP8_ANY, H=8, topk=200, with_topk_length=True, with_sink=True),
+    "fp8any_h64_multi_tile": dict(fmt=W.FMT_FP8_ANY, H=64, topk=1024, ctx=2048, T=3, with_sink=True),
+    "fp8any_h100_len": dict(fmt=W.FMT_FP8_ANY, H=100, topk=192, T=3, with_topk_length=True),
 }
 
 
@@ -79,7 +84,7 @@ def test_prefill_parity(name):
 
 
 @pytest.mark.parametrize("name", ["bf16_h8_ragged", "fp8_h20_sink", "int8_h64_len", "fp8_h64_multi_tile",
-                                  "bf16_h8_window_len_sink"])
+                                  "bf16_h8_window_len_sink", "fp8any_h8_len_sink", "fp8any_h64_multi_tile"])
 @pytest.mark.parametrize("S", [1, 3, 8])
 def test_decode_split_and_combine_parity(name, S):
     c = make(name)
@@ -135,7 +140,7 @@ def test_c1_tiny_all_forms():
         assert_lse_close(l2.cpu().numpy(), lf32)
 
 
-@pytest.mark.parametrize("fmt", [W.FMT_BF16, W.FMT_FP8, W.FMT_INT8])
+@pytest.mark.parametrize("fmt", [W.FMT_BF16, W.FMT_FP8, W.FMT_INT8, W.FMT_FP8_ANY])
 def test_quantize_bit_exact(fmt):
     c = W.make_case("quant", config_id=230 + fmt, seed=1, fmt=fmt, T=1, H=1, n_seqs=1, ctx=2048, topk=64)
     kv = c.kv.copy()
