@@ -12,7 +12,11 @@ Also measured in the same run:
 - "decode": the split-KV decode batch -- 64 sequences x 1 query, ctx 16384
   each (656 MiB FP8 pool), H = 64, top-k 2048, 8 splits, decode + combine;
   beside it the same batch at the split count the library's cost model
-  picks for this device (smla_decode_num_splits);
+  picks for this device (smla_decode_num_splits), and a dual-cache decode
+  batch (64 sequences, H = 64, a 1024-wide main list over the same pool
+  plus a 2176-wide secondary list over a second 656 MiB pool);
+- "glm_nsa": the metric's prefill over FP8 rows with arbitrary scales
+  (format 3, written from the same latent rows);
 - "fewhead": 8192 tokens, 8 native heads read as a view of a 64-head BF16 q
   buffer, ctx 32768 BF16 pool, top-k 640 with per-token lengths and a sink,
   written in place; beside it the same inputs with all 64 heads;
@@ -210,6 +214,26 @@ def main():
                      "algorithmic_bytes_per_launch": alg_bytes},
         "kernel_source_sha": sha,
     }
+    # the same prefill over FP8 rows with arbitrary scales (GLM_NSA rows)
+    if not args.no_extra:
+        apool = smla.KVPool.empty(case.num_blocks, W.FMT_FP8_ANY, device=dev)
+        smla.quantize_kv(kv, torch.from_numpy(case.slots).to(dev), apool)
+
+        def nsa():
+            smla.prefill(q, apool, idx, sm_scale=float(case.sm_scale), out=out, lse=lse)
+
+        nsa()
+        tn = pct(event_times_us(torch, nsa, 10, stream))
+        result["glm_nsa"] = {
+            "workload": f"fp8 rows with arbitrary per-128 scales (amax/448), prefill T={T} ctx={case.ctx} H={H} "
+                        f"topk={case.topk}",
+            "kernel_us_median_p10_p90": [round(v, 3) for v in tn],
+            "us_per_token": round(tn[0] / T, 5),
+            "gathered_kv_GBps": round(kv_bytes / (tn[0] * 1e-6) / 1e9, 2),
+            "vs_power_of_two_fp8_kernel": round(tn[0] / p_med, 3),
+        }
+        print(f"[bench] glm_nsa prefill {tn[0]:.1f} us", file=sys.stderr, flush=True)
+        del apool
     props = torch.cuda.get_device_properties(dev)
     result["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                         "compute_units": props.multi_processor_count,
@@ -302,6 +326,51 @@ def main():
         print(f"[bench] decode {d8['decode_kernel_us']:.2f} us + combine {d8['combine_kernel_us']:.2f} us (S={S}); "
               f"model S={Sm}: {model['decode_kernel_us']:.2f} + {model['combine_kernel_us']:.2f} us",
               file=sys.stderr, flush=True)
+        # dual cache: the first 1024 entries of each list over this pool, and a
+        # 2176-wide secondary list over a second pool of the same size
+        if not args.no_extra:
+            k1, k2 = 1024, 2176
+            gen = torch.Generator(device=dev)
+            gen.manual_seed(11)
+            xpool = smla.KVPool.empty(dc.num_blocks, W.FMT_FP8, device=dev)
+            nrows = dc.num_blocks * 64
+            for r0 in range(0, nrows, 1 << 18):
+                xkv = torch.randn((1 << 18, D_QK), generator=gen, device=dev).to(torch.bfloat16)
+                smla.quantize_kv(xkv, torch.arange(r0, r0 + (1 << 18), dtype=torch.int32, device=dev), xpool)
+                del xkv
+            xidx = [torch.randint(0, nrows, (dc.T, k2), generator=gen, device=dev, dtype=torch.int32)
+                    for _ in range(3)]
+            mids = [ix[:, :k1] for ix in idx_sets]
+            Sd = smla.decode_num_splits(dc.T, dc.H, k1 + k2, W.FMT_FP8)
+            xpo = torch.empty((dc.T, Sd, dc.H, D_V), dtype=torch.float32, device=dev)
+            xpl = torch.empty((dc.T, Sd, dc.H), dtype=torch.float32, device=dev)
+
+            def dual(i):
+                smla.decode_dual(dq[:, : dc.H], dpool, mids[i % 3], xpool, xidx[i % 3], Sd,
+                                 sm_scale=float(dc.sm_scale), part_out=xpo, part_lse=xpl)
+                smla.combine(xpo, xpl, out=dout, lse=dlse)
+
+            for i in range(3):
+                dual(i)
+            torch.cuda.synchronize()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record(stream)
+            for i in range(dsteps):
+                dual(i)
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            dual_us = ev[0].elapsed_time(ev[1]) * 1e3 / dsteps
+            dual_bytes = dc.T * (k1 + k2) * W.ROW_BYTES[W.FMT_FP8]
+            result["decode"]["dual_cache"] = {
+                "workload": f"fp8 dual-cache decode {dc.T} seqs x 1 query, H={dc.H}, main topk {k1} + secondary "
+                            f"topk {k2} over two {dc.num_blocks * 64 * 656 >> 20} MiB pools, splits={Sd} "
+                            "(decode + combine)",
+                "us_per_call": round(dual_us, 3),
+                "gathered_kv_bytes": dual_bytes,
+                "gathered_kv_GBps": round(dual_bytes / (dual_us * 1e-6) / 1e9, 2),
+            }
+            print(f"[bench] dual-cache decode {dual_us:.1f} us (S={Sd})", file=sys.stderr, flush=True)
+            del xpool, xidx, mids, xpo, xpl
         del dpool, dq, didx, idx_sets, dout, dlse
         torch.cuda.empty_cache()
 
