@@ -24,7 +24,7 @@ _SRC = os.path.join(_HERE, "smla_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-FMT_BF16, FMT_FP8, FMT_INT8, FMT_FP8_ANY = 0, 1, 2, 3
+FMT_BF16, FMT_FP8, FMT_INT8, FMT_FP8_ANY, FMT_FP8_NOPE = 0, 1, 2, 3, 4
 PAGE_BLOCK = 64
 D_QK, D_V = 576, 512
 

@@ -31,7 +31,10 @@
  * scaled-score units) that carries no value; an empty candidate set gives
  * out = 0 and lse = -inf; scales are 2^ceil(log2(amax/448)) (FP8),
  * amax/448 (FP8 with arbitrary scales, the GLM_NSA rows of FlashInfer #4802's
- * KV layout comment) or amax/127 (INT8), amax = 0 giving scale 1; every index outside
+ * KV layout comment) or amax/127 (INT8), amax = 0 giving scale 1.  GLM53_NOPE
+ * rows (the same layout comment) are FP8 rows whose bytes [528, 656) are
+ * reserved padding: they are never written or read, and scores use the 512
+ * nope dimensions only (q rows hold 512 values); every index outside
  * [0, num_blocks*64) -- -1 padding included -- contributes nothing.
  *
  * Precision: all attention arithmetic is float64.  The quantizer runs in
@@ -53,7 +56,10 @@
 #define PAGE_BLOCK 64
 #define TILE 128 /* quantization tile width along the nope part */
 
-enum { FMT_BF16 = 0, FMT_FP8 = 1, FMT_INT8 = 2, FMT_FP8_ANY = 3 };
+enum { FMT_BF16 = 0, FMT_FP8 = 1, FMT_INT8 = 2, FMT_FP8_ANY = 3, FMT_FP8_NOPE = 4 };
+
+/* elements of a query row that enter a score */
+static int q_dims(int32_t fmt) { return fmt == FMT_FP8_NOPE ? D_NOPE : D_QK; }
 
 /* ---------------------------------------------------------------------- */
 /* Scalar helpers                                                          */
@@ -171,19 +177,19 @@ static void quantize_row(const uint16_t* x, int32_t fmt, uint8_t* row) {
       float v = fabsf(bf16_bits_to_float(x[i]));
       if (v > amax) amax = v;
     }
-    float scale = (fmt == FMT_FP8)       ? oracle_fp8_scale(amax)
+    float scale = (fmt == FMT_FP8 || fmt == FMT_FP8_NOPE) ? oracle_fp8_scale(amax)
                   : (fmt == FMT_FP8_ANY) ? oracle_fp8_any_scale(amax)
                                          : oracle_int8_scale(amax);
     for (int i = g * TILE; i < (g + 1) * TILE; ++i) {
       float xv = bf16_bits_to_float(x[i]);
-      if (fmt == FMT_FP8 || fmt == FMT_FP8_ANY)
+      if (fmt != FMT_INT8)
         row[i] = oracle_e4m3_encode(xv / scale);
       else
         row[i] = (uint8_t)oracle_int8_encode(xv, scale);
     }
     memcpy(row + D_NOPE + 4 * g, &scale, 4);
   }
-  memcpy(row + D_NOPE + 4 * (D_NOPE / TILE), x + D_NOPE, 2 * D_ROPE);
+  if (fmt != FMT_FP8_NOPE) memcpy(row + D_NOPE + 4 * (D_NOPE / TILE), x + D_NOPE, 2 * D_ROPE);
 }
 
 /* Write n latent rows (row i at kv + i*kv_stride elements) into the pool at
@@ -222,10 +228,14 @@ static void dequant_row(const uint8_t* pool, int64_t block_stride_bytes, int32_t
   float scale[D_NOPE / TILE];
   memcpy(scale, row + D_NOPE, sizeof scale);
   for (int i = 0; i < D_NOPE; ++i) {
-    double c = (fmt == FMT_FP8 || fmt == FMT_FP8_ANY) ? oracle_e4m3_decode(row[i]) : (double)(int8_t)row[i];
+    double c = (fmt != FMT_INT8) ? oracle_e4m3_decode(row[i]) : (double)(int8_t)row[i];
     K[i] = c * (double)scale[i / TILE];
   }
   for (int r = 0; r < D_ROPE; ++r) {
+    if (fmt == FMT_FP8_NOPE) { /* padding: not part of the row's data */
+      K[D_NOPE + r] = 0.0;
+      continue;
+    }
     uint16_t b;
     memcpy(&b, row + D_NOPE + sizeof scale + 2 * r, 2);
     K[D_NOPE + r] = bf16_bits_to_float(b);
@@ -281,7 +291,7 @@ static void attend(const problem* P, int64_t t, int32_t h, const double* rows, i
                    double* scores, double* m_out, double* l_out, double* acc) {
   const uint16_t* qr = P->q + t * P->q_stride_t + (int64_t)h * P->q_stride_h;
   double q[D_QK];
-  for (int i = 0; i < D_QK; ++i) q[i] = bf16_bits_to_float(qr[i]);
+  for (int i = 0; i < D_QK; ++i) q[i] = i < q_dims(P->fmt) ? bf16_bits_to_float(qr[i]) : 0.0;
   double m = -INFINITY;
   for (int64_t j = 0; j < n; ++j) {
     double dot = 0.0;
@@ -512,7 +522,7 @@ int oracle_probs(const uint16_t* q, int64_t T, int32_t H, int64_t q_stride_t, in
     }
     dequant_row(pool, block_stride_bytes, fmt, idx, K);
     double dot = 0.0;
-    for (int i = 0; i < D_QK; ++i) dot += (double)bf16_bits_to_float(qr[i]) * K[i];
+    for (int i = 0; i < q_dims(fmt); ++i) dot += (double)bf16_bits_to_float(qr[i]) * K[i];
     s[j] = P.sm_scale * dot;
     if (s[j] > m) m = s[j];
   }

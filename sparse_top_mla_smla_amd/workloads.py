@@ -26,9 +26,12 @@ import numpy as np
 
 PAGE_BLOCK = 64
 D_QK, D_V = 576, 512
-FMT_BF16, FMT_FP8, FMT_INT8, FMT_FP8_ANY = 0, 1, 2, 3
-FMT_NAMES = {FMT_BF16: "bf16", FMT_FP8: "fp8_e4m3", FMT_INT8: "int8", FMT_FP8_ANY: "fp8_e4m3_any_scale"}
-ROW_BYTES = {FMT_BF16: 1152, FMT_FP8: 656, FMT_INT8: 656, FMT_FP8_ANY: 656}
+FMT_BF16, FMT_FP8, FMT_INT8, FMT_FP8_ANY, FMT_FP8_NOPE = 0, 1, 2, 3, 4
+FMT_NAMES = {FMT_BF16: "bf16", FMT_FP8: "fp8_e4m3", FMT_INT8: "int8", FMT_FP8_ANY: "fp8_e4m3_any_scale",
+             FMT_FP8_NOPE: "fp8_e4m3_nope"}
+ROW_BYTES = {FMT_BF16: 1152, FMT_FP8: 656, FMT_INT8: 656, FMT_FP8_ANY: 656, FMT_FP8_NOPE: 656}
+# elements of a query row that enter a score (NOPE rows have no rope dimensions)
+Q_DIMS = {FMT_BF16: 576, FMT_FP8: 576, FMT_INT8: 576, FMT_FP8_ANY: 576, FMT_FP8_NOPE: 512}
 SM_SCALE = np.float32(1.0 / 24.0)  # 1/sqrt(576)
 PAD_SENTINEL = 0x7FFFFFFF
 

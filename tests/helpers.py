@@ -26,11 +26,13 @@ def np_dequant(pool: oracle.Pool, slots) -> np.ndarray:
     if pool.fmt == W.FMT_BF16:
         return W.bf16_bits_to_f32(rows.copy().view(np.uint16)).astype(np.float64)
     scales = rows[:, 512:528].copy().view(np.float32).astype(np.float64)
-    if pool.fmt in (W.FMT_FP8, W.FMT_FP8_ANY):
+    if pool.fmt in (W.FMT_FP8, W.FMT_FP8_ANY, W.FMT_FP8_NOPE):
         codes = torch.tensor(rows[:, :512].copy()).view(torch.float8_e4m3fn).double().numpy()
     else:
         codes = rows[:, :512].view(np.int8).astype(np.float64)
     nope = codes * np.repeat(scales, 128, axis=1)
+    if pool.fmt == W.FMT_FP8_NOPE:  # padding, not data: no rope dimensions
+        return np.concatenate([nope, np.zeros((len(rows), 64))], axis=1)
     rope = W.bf16_bits_to_f32(rows[:, 528:656].copy().view(np.uint16)).astype(np.float64)
     return np.concatenate([nope, rope], axis=1)
 

@@ -28,7 +28,7 @@ def case(fmt, seed, **kw):
     return W.make_case("split", config_id=105, seed=seed, fmt=fmt, **base)
 
 
-@pytest.mark.parametrize("fmt", [W.FMT_BF16, W.FMT_FP8, W.FMT_INT8, W.FMT_FP8_ANY])
+@pytest.mark.parametrize("fmt", [W.FMT_BF16, W.FMT_FP8, W.FMT_INT8, W.FMT_FP8_ANY, W.FMT_FP8_NOPE])
 @pytest.mark.parametrize("S", [1, 2, 3, 8, 16, 32])
 def test_combine_of_splits_equals_unsplit(fmt, S):
     c = case(fmt, seed=S + 10 * fmt, with_topk_length=True, with_sink=True)
