@@ -72,12 +72,17 @@ typedef enum {
  * FP32 scales: the same PR's layout comment says GLM_NSA rows store
  * arbitrary scales where DSv3.2 rows store powers of two; its cache writer
  * takes scale = amax/448, and the attention entry points accept any positive
- * scale for it.  BF16 row = 576 BF16 values (1152 bytes). */
+ * scale for it.  FP8_E4M3_NOPE is the FP8 row of GLM53_NOPE (same comment):
+ * bytes [528, 656) are reserved padding, never written, gathered or read;
+ * K and V are the 512 nope values, q rows hold 512 values (q_stride_h >=
+ * 512) and the writer reads 512 values per row (kv_stride >= 512).  BF16
+ * row = 576 BF16 values (1152 bytes). */
 typedef enum {
   SMLA_KV_BF16 = 0,
   SMLA_KV_FP8_E4M3 = 1,
   SMLA_KV_INT8 = 2,
-  SMLA_KV_FP8_E4M3_ANY_SCALE = 3
+  SMLA_KV_FP8_E4M3_ANY_SCALE = 3,
+  SMLA_KV_FP8_E4M3_NOPE = 4
 } smla_kv_format;
 
 /* A paged latent pool.  Slot s (a flat pool position) lives in block s/64 at

@@ -36,7 +36,7 @@ smla_status check_pool(const smla_kv_pool& kv) {
     return fail(SMLA_ERR_UNSUPPORTED, "page_block %d is not supported (supported: 64)", kv.page_block);
   int32_t rb = smla_row_bytes(kv.format);
   if (rb < 0)
-    return fail(SMLA_ERR_UNSUPPORTED, "kv format %d is not supported (supported: 0 = BF16, 1 = FP8_E4M3, 2 = INT8, 3 = FP8_E4M3_ANY_SCALE)",
+    return fail(SMLA_ERR_UNSUPPORTED, "kv format %d is not supported (supported: 0 = BF16, 1 = FP8_E4M3, 2 = INT8, 3 = FP8_E4M3_ANY_SCALE, 4 = FP8_E4M3_NOPE)",
                 kv.format);
   if (kv.num_blocks < 1) return fail(SMLA_ERR_SHAPE, "num_blocks %lld must be >= 1", (long long)kv.num_blocks);
   if (kv.num_blocks > (int64_t)(INT32_MAX / 64) + 1)
@@ -67,8 +67,10 @@ smla_status check_attn_common(const void* q, int64_t T, int32_t H, int64_t q_st,
   smla_status st = check_pool(kv);
   if (st != SMLA_OK) return st;
   if (!aligned(q, 16)) return fail(SMLA_ERR_STRIDE, "q is not 16-byte aligned");
-  if (q_sh < 576 || q_sh % 8 != 0)
-    return fail(SMLA_ERR_STRIDE, "q_stride_h = %lld must be >= 576 and a multiple of 8", (long long)q_sh);
+  const int64_t qd = kv.format == SMLA_KV_FP8_E4M3_NOPE ? 512 : 576;  // values per q row
+  if (q_sh < qd || q_sh % 8 != 0)
+    return fail(SMLA_ERR_STRIDE, "q_stride_h = %lld must be >= %lld and a multiple of 8", (long long)q_sh,
+                (long long)qd);
   if (q_st % 8 != 0 || q_st < 0)
     return fail(SMLA_ERR_STRIDE, "q_stride_t = %lld must be a non-negative multiple of 8", (long long)q_st);
   if (idx_st < topk) return fail(SMLA_ERR_STRIDE, "idx_stride_t = %lld is smaller than topk = %d", (long long)idx_st, topk);
@@ -126,6 +128,7 @@ int32_t smla_row_bytes(int32_t format) {
     case SMLA_KV_FP8_E4M3: return 656;
     case SMLA_KV_INT8: return 656;
     case SMLA_KV_FP8_E4M3_ANY_SCALE: return 656;
+    case SMLA_KV_FP8_E4M3_NOPE: return 656;
     default: return -1;
   }
 }
@@ -159,8 +162,10 @@ smla_status smla_quantize_kv(const void* kv, int64_t n, int64_t kv_stride, const
   if (!slots) return fail(SMLA_ERR_NULL, "slots is NULL");
   smla_status st = check_pool(pool);
   if (st != SMLA_OK) return st;
-  if (kv_stride < 576 || kv_stride % 8 != 0)
-    return fail(SMLA_ERR_STRIDE, "kv_stride = %lld must be >= 576 and a multiple of 8", (long long)kv_stride);
+  const int64_t kd = pool.format == SMLA_KV_FP8_E4M3_NOPE ? 512 : 576;  // values read per latent row
+  if (kv_stride < kd || kv_stride % 8 != 0)
+    return fail(SMLA_ERR_STRIDE, "kv_stride = %lld must be >= %lld and a multiple of 8", (long long)kv_stride,
+                (long long)kd);
   if (!aligned(kv, 16)) return fail(SMLA_ERR_STRIDE, "kv is not 16-byte aligned");
   if (!aligned(slots, 4)) return fail(SMLA_ERR_STRIDE, "slots is not 4-byte aligned");
   if ((n + 3) / 4 > (int64_t)UINT32_MAX) return fail(SMLA_ERR_SHAPE, "n = %lld is too large", (long long)n);
@@ -194,6 +199,7 @@ static void fill_attn(smla::AttnParams& p, const void* q, int64_t T, int32_t H, 
   p.topk = topk;
   p.topk_length = topk_length;
   p.scale_log2 = sm_scale * 1.4426950408889634f;
+  p.nope = kv.format == SMLA_KV_FP8_E4M3_NOPE;
 }
 
 static void fill_extra(smla::AttnParams& p, const smla_kv_extra* extra) {

@@ -71,6 +71,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_kernel(AttnParams p) {
   using IdxT = typename C::IdxT;
   using G = RowGeom<FMT>;
   constexpr bool QUANT = FMT != FMT_BF16;
+  constexpr bool NOPE = FMT == FMT_FP8_NOPE;  // rows without rope dimensions
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS_BYTES];
   uint8_t* tile = smem;
   IdxT* idx_lds = reinterpret_cast<IdxT*>(smem + C::IDX_OFF);
@@ -106,7 +107,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_kernel(AttnParams p) {
     const uint16_t* qrow = p.q + t * p.q_st + (int64_t)(hv ? h : 0) * p.q_sh;
 #pragma unroll
     for (int ks = 0; ks < 18; ++ks) {
-      uint4 v = hv ? *reinterpret_cast<const uint4*>(qrow + 32 * ks + 8 * lg) : make_uint4(0, 0, 0, 0);
+      // (rows without rope dimensions: q rows end at 512, the rope slices are 0)
+      const bool load = hv && (ks < 16 || !NOPE);
+      uint4 v = load ? *reinterpret_cast<const uint4*>(qrow + 32 * ks + 8 * lg) : make_uint4(0, 0, 0, 0);
       qreg[ks] = __builtin_bit_cast(bf16x8, v);
     }
   }
@@ -138,7 +141,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_kernel(AttnParams p) {
       if (qc < C::TOTAL_CHUNKS) {
         const int row = qc / G::CHUNKS, ck = qc % G::CHUNKS;
         const IdxT e = il[row];
-        if (C::present(e)) {
+        // (rows without rope dimensions: their padding is not gathered)
+        if (C::present(e) && !(NOPE && 16 * ck >= G::ROPE_OFF)) {
           const uint8_t* src;
           if constexpr (DUAL) {
             src = (const uint8_t*)e;
@@ -204,8 +208,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_kernel(AttnParams p) {
         acc[0] = mfma_16x16x32(a, qreg[ks], acc[0]);
       }
     }
+    // rope product (rows without rope dimensions have none)
 #pragma unroll
-    for (int ks = 16; ks < 18; ++ks) {
+    for (int ks = 16; ks < 18 && !NOPE; ++ks) {
       const bf16x8 a = __builtin_bit_cast(
           bf16x8, *reinterpret_cast<const uint4*>(rowA + G::ROPE_OFF + 2 * (32 * (ks - 16) + 8 * lg)));
       acc[QUANT ? 4 : 0] = mfma_16x16x32(a, qreg[ks], acc[QUANT ? 4 : 0]);
@@ -393,13 +398,14 @@ hipError_t launch_attention(const AttnParams& p, int fmt, bool decode, hipStream
   // many heads over a quantized cache: one workgroup per token for 64 heads
   // (FP8 codes with arbitrary scales run the kernels that fold each row's
   // scale into its partial scores and probabilities, as for INT8)
-  if (fmt == FMT_FP8 && p.H > 16) return launch_attention_fp8(p, decode, s);
+  if ((fmt == FMT_FP8 || fmt == FMT_FP8_NOPE) && p.H > 16) return launch_attention_fp8(p, decode, s);
   if (fmt == FMT_INT8 && p.H > 16) return launch_attention_wide(p, fmt, decode, s);
   if (fmt == FMT_FP8_ANY && p.H > 16) return launch_attention_wide(p, FMT_FP8, decode, s);
   switch (fmt) {
     case FMT_BF16: return launch_fmt<FMT_BF16>(p, decode, s);
     case FMT_FP8:
     case FMT_FP8_ANY: return launch_fmt<FMT_FP8>(p, decode, s);
+    case FMT_FP8_NOPE: return launch_fmt<FMT_FP8_NOPE>(p, decode, s);
     case FMT_INT8: return launch_fmt<FMT_INT8>(p, decode, s);
     default: return hipErrorInvalidValue;
   }

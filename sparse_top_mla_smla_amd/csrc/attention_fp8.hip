@@ -143,7 +143,9 @@ struct Buf {
 };
 }  // namespace f8
 
-template <bool DECODE, bool DUAL>
+// NOPE: rows without rope dimensions (q rows of 512 values, row padding never
+// gathered or read)
+template <bool DECODE, bool DUAL, bool NOPE>
 __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
   using namespace f8;
   // Separate LDS objects, and a loop unrolled by two so that every access
@@ -265,7 +267,9 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
 #pragma unroll
       for (int r = 2 * P; r < 2 * P + 2; ++r) {
         const int ck = w + 8 * r;
-        if (r + 1 < GROUNDS || ck < CHUNKS) global_to_lds_16(src + 16 * ck, raw + ck * CS);
+        // (rows without rope dimensions: their padding is not gathered)
+        if ((r + 1 < GROUNDS || ck < CHUNKS) && (!NOPE || ck < CK_ROPE))
+          global_to_lds_16(src + 16 * ck, raw + ck * CS);
       }
     }
     if (P == 0 && w == 0) valid[B * TC + lane] = src != nullptr;
@@ -290,8 +294,13 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
         const uint4 v = *reinterpret_cast<const uint4*>(qrow + 128 * g + 32 * j + 16 * hi + 8 * b);
         qn[2 * j + b] = __builtin_bit_cast(bf16x8, hv ? v : make_uint4(0, 0, 0, 0));
       }
-    const uint4 v = *reinterpret_cast<const uint4*>(qrow + D_NOPE + 16 * g + 8 * hi);
-    qr = __builtin_bit_cast(bf16x8, hv ? v : make_uint4(0, 0, 0, 0));
+    // (rows without rope dimensions: q rows end at 512 and the rope slice is 0)
+    if constexpr (NOPE) {
+      qr = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+    } else {
+      const uint4 v = *reinterpret_cast<const uint4*>(qrow + D_NOPE + 16 * g + 8 * hi);
+      qr = __builtin_bit_cast(bf16x8, hv ? v : make_uint4(0, 0, 0, 0));
+    }
   };
 
   TileRef cur = first_tile((int32_t)blockIdx.x);
@@ -424,7 +433,8 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
         acc[c2] = mfma_32x32x16(cvt8(c16.x, c16.y, sc), qn[2 * j], acc[c2]);
         acc[c2] = mfma_32x32x16(cvt8(c16.z, c16.w, sc), qn[2 * j + 1], acc[c2]);
       }
-      uint4 r16 = *reinterpret_cast<const uint4*>(raw + (CK_ROPE + 2 * g + hi) * CS + row * 16);
+      uint4 r16 = make_uint4(0, 0, 0, 0);  // rows without rope dimensions: 0
+      if constexpr (!NOPE) r16 = *reinterpret_cast<const uint4*>(raw + (CK_ROPE + 2 * g + hi) * CS + row * 16);
       if (bad) r16 = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
       acc[c2] = mfma_32x32x16(__builtin_bit_cast(bf16x8, r16), qr, acc[c2]);
     }
@@ -674,10 +684,17 @@ hipError_t launch_attention_fp8(const AttnParams& p, bool decode, hipStream_t s)
   dim3 grid(decode ? (unsigned)q.T : (unsigned)fp8_prefill_blocks(q.T, q.H, cus), (unsigned)((q.H + 63) / 64),
             decode ? (unsigned)((q.num_splits + q.splits_per_block - 1) / q.splits_per_block) : 1u);
   const bool dual = q.topk2 > 0;
-  if (decode && dual) hipLaunchKernelGGL((attn_fp8_kernel<true, true>), grid, block, 0, s, q);
-  else if (decode) hipLaunchKernelGGL((attn_fp8_kernel<true, false>), grid, block, 0, s, q);
-  else if (dual) hipLaunchKernelGGL((attn_fp8_kernel<false, true>), grid, block, 0, s, q);
-  else hipLaunchKernelGGL((attn_fp8_kernel<false, false>), grid, block, 0, s, q);
+  if (q.nope) {
+    if (decode && dual) hipLaunchKernelGGL((attn_fp8_kernel<true, true, true>), grid, block, 0, s, q);
+    else if (decode) hipLaunchKernelGGL((attn_fp8_kernel<true, false, true>), grid, block, 0, s, q);
+    else if (dual) hipLaunchKernelGGL((attn_fp8_kernel<false, true, true>), grid, block, 0, s, q);
+    else hipLaunchKernelGGL((attn_fp8_kernel<false, false, true>), grid, block, 0, s, q);
+  } else {
+    if (decode && dual) hipLaunchKernelGGL((attn_fp8_kernel<true, true, false>), grid, block, 0, s, q);
+    else if (decode) hipLaunchKernelGGL((attn_fp8_kernel<true, false, false>), grid, block, 0, s, q);
+    else if (dual) hipLaunchKernelGGL((attn_fp8_kernel<false, true, false>), grid, block, 0, s, q);
+    else hipLaunchKernelGGL((attn_fp8_kernel<false, false, false>), grid, block, 0, s, q);
+  }
   return hipGetLastError();
 }
 

@@ -24,7 +24,8 @@ constexpr int PAGE = 64;
 constexpr int QTILE = 128;  // quantization tile along the nope part
 
 // FMT_FP8_ANY: FP8 codes with arbitrary positive per-128 scales (the row of FMT_FP8)
-enum : int { FMT_BF16 = 0, FMT_FP8 = 1, FMT_INT8 = 2, FMT_FP8_ANY = 3 };
+// FMT_FP8_NOPE: the FP8 row whose rope bytes are padding (no rope dimensions)
+enum : int { FMT_BF16 = 0, FMT_FP8 = 1, FMT_INT8 = 2, FMT_FP8_ANY = 3, FMT_FP8_NOPE = 4 };
 
 template <int FMT>
 struct RowGeom {
@@ -79,7 +80,7 @@ __device__ __forceinline__ uint2 int8x4_to_bf16x4(uint32_t v) {
 
 template <int FMT>
 __device__ __forceinline__ uint2 codes4_to_bf16x4(uint32_t v) {
-  if constexpr (FMT == FMT_FP8) return fp8x4_to_bf16x4(v);
+  if constexpr (FMT == FMT_FP8 || FMT == FMT_FP8_NOPE) return fp8x4_to_bf16x4(v);
   else return int8x4_to_bf16x4(v);
 }
 

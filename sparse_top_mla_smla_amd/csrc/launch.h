@@ -33,6 +33,8 @@ struct AttnParams {
   const int32_t* topk_length;  // may be null
   const float* sink;           // may be null (prefill only)
   float scale_log2;            // sm_scale * log2(e)
+  int32_t nope;                // rows have no rope dimensions: q rows hold 512 values and row
+                               // bytes [528, 656) are padding, never gathered or read
   // prefill outputs
   uint16_t* out;
   int64_t out_st, out_sh;

@@ -86,8 +86,8 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantParams p) {
 
     uint32_t code[8];
     float scale;
-    if constexpr (FMT == FMT_FP8 || FMT == FMT_FP8_ANY) {
-      scale = FMT == FMT_FP8 ? fp8_tile_scale(amax) : (amax == 0.0f ? 1.0f : __fdiv_rn(amax, 448.0f));
+    if constexpr (FMT == FMT_FP8 || FMT == FMT_FP8_ANY || FMT == FMT_FP8_NOPE) {
+      scale = FMT != FMT_FP8_ANY ? fp8_tile_scale(amax) : (amax == 0.0f ? 1.0f : __fdiv_rn(amax, 448.0f));
 #pragma unroll
       for (int i = 0; i < 8; ++i) code[i] = e4m3_from_f32(__fdiv_rn(x[i], scale));
     } else {
@@ -104,7 +104,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantParams p) {
     packed.y = code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24);
     reinterpret_cast<uint2*>(dst)[lane] = packed;
     if ((lane & 15) == 0) reinterpret_cast<float*>(dst + G::SCALE_OFF)[lane >> 4] = scale;
-    if (lane < 16) {
+    if (FMT != FMT_FP8_NOPE && lane < 16) {  // (NOPE rows: padding, not written)
       const uint2* rs = reinterpret_cast<const uint2*>(src + D_NOPE);
       reinterpret_cast<uint2*>(dst + G::ROPE_OFF)[lane] = rs[lane];
     }
@@ -118,6 +118,7 @@ hipError_t launch_quantize(const QuantParams& p, int fmt, hipStream_t s) {
     case FMT_FP8: hipLaunchKernelGGL(quantize_kernel<FMT_FP8>, grid, block, 0, s, p); break;
     case FMT_INT8: hipLaunchKernelGGL(quantize_kernel<FMT_INT8>, grid, block, 0, s, p); break;
     case FMT_FP8_ANY: hipLaunchKernelGGL(quantize_kernel<FMT_FP8_ANY>, grid, block, 0, s, p); break;
+    case FMT_FP8_NOPE: hipLaunchKernelGGL(quantize_kernel<FMT_FP8_NOPE>, grid, block, 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -51,7 +51,8 @@ constexpr double kCrossover = 0.95;  // split form only when at most this fracti
 const KernelClass* kernel_class(int32_t format, int32_t H) {
   // the dispatch rule of launch_attention
   switch (format) {
-    case SMLA_KV_FP8_E4M3: return H > 16 ? &kFp8Wide : &kFp8Narrow;
+    case SMLA_KV_FP8_E4M3:
+    case SMLA_KV_FP8_E4M3_NOPE: return H > 16 ? &kFp8Wide : &kFp8Narrow;
     case SMLA_KV_INT8: return H > 16 ? &kInt8Wide : &kInt8Narrow;
     // arbitrary-scale FP8 runs the INT8 many-head kernel's FP8 instantiation
     case SMLA_KV_FP8_E4M3_ANY_SCALE: return H > 16 ? &kInt8Wide : &kFp8Narrow;

@@ -140,7 +140,7 @@ def test_c1_tiny_all_forms():
         assert_lse_close(l2.cpu().numpy(), lf32)
 
 
-@pytest.mark.parametrize("fmt", [W.FMT_BF16, W.FMT_FP8, W.FMT_INT8, W.FMT_FP8_ANY])
+@pytest.mark.parametrize("fmt", [W.FMT_BF16, W.FMT_FP8, W.FMT_INT8, W.FMT_FP8_ANY, W.FMT_FP8_NOPE])
 def test_quantize_bit_exact(fmt):
     c = W.make_case("quant", config_id=230 + fmt, seed=1, fmt=fmt, T=1, H=1, n_seqs=1, ctx=2048, topk=64)
     kv = c.kv.copy()
@@ -245,3 +245,30 @@ def test_prefill_many_tokens_per_workgroup(H, T):
     ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(want_b), 2.0 ** -126))) - 7)
     assert np.all(np.abs(got - want_b) <= np.maximum(1e-2, ulp))
     assert_lse_close(got_l, lf32)
+
+
+@pytest.mark.parametrize("H", [8, 64])
+def test_nope_rows(H):
+    """GLM53_NOPE rows: q rows of 512 values (a compact tensor, so a read
+    past 512 would take the next head's values) and row padding filled with
+    NaN bytes (a read of it would poison the result); prefill and decode
+    match the oracle."""
+    c = W.make_case(f"nope_h{H}", config_id=295 + H // 64, seed=4, fmt=W.FMT_FP8_NOPE, T=4, H=H, n_seqs=1,
+                    ctx=1024, topk=320, causal=True, with_topk_length=True, with_sink=True)
+    d = Dev(c, fill=0xFF)
+    q512 = torch.from_numpy(np.ascontiguousarray(c.q[:, :, :512]).view(np.int16)).view(torch.bfloat16).cuda()
+    assert q512.stride(1) == 512
+    o, l = smla.prefill(q512, d.pool, d.indices, topk_length=d.topk_length, sink=d.sink, sm_scale=float(c.sm_scale))
+    torch.cuda.synchronize()
+    pool = oracle_pool(c)
+    ob, lf32, _, _ = oracle.prefill(c.q, pool, c.indices, topk_length=c.topk_length, sink=c.sink,
+                                    sm_scale=c.sm_scale)
+    assert_out_close(bf16_dev_to_f64(o), f64_of_bits(ob))
+    assert_lse_close(l.cpu().numpy(), lf32)
+    po, pl = smla.decode(q512, d.pool, d.indices, 3, topk_length=d.topk_length, sm_scale=float(c.sm_scale))
+    o2, l2 = smla.combine(po, pl, sink=d.sink)
+    torch.cuda.synchronize()
+    rpo, rpl = oracle.decode_split(c.q, pool, c.indices, 3, topk_length=c.topk_length, sm_scale=c.sm_scale)
+    assert_out_close(po.cpu().numpy().astype(np.float64), rpo, "part_out")
+    assert_out_close(bf16_dev_to_f64(o2), f64_of_bits(ob))
+    assert_lse_close(l2.cpu().numpy(), lf32)
