@@ -24,9 +24,8 @@ _SRC = os.path.join(_HERE, "smla_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-FMT_BF16, FMT_FP8, FMT_INT8, FMT_FP8_ANY, FMT_FP8_NOPE = 0, 1, 2, 3, 4
+FMT_BF16, FMT_FP8, FMT_INT8, FMT_FP8_ANY, FMT_FP8_NOPE, FMT_FP8_DOTS3 = 0, 1, 2, 3, 4, 5
 PAGE_BLOCK = 64
-D_QK, D_V = 576, 512
 
 
 def build(force: bool = True) -> str:
@@ -62,6 +61,14 @@ def lib():
         L.oracle_int8_encode.restype = ctypes.c_int8
         L.oracle_row_bytes.argtypes = [i32]
         L.oracle_row_bytes.restype = i32
+        L.oracle_d_k.argtypes = [i32]
+        L.oracle_d_k.restype = i32
+        L.oracle_d_v.argtypes = [i32]
+        L.oracle_d_v.restype = i32
+        L.oracle_e8m0_scale.argtypes = [f32]
+        L.oracle_e8m0_scale.restype = ctypes.c_uint8
+        L.oracle_e8m0_decode.argtypes = [ctypes.c_uint8]
+        L.oracle_e8m0_decode.restype = ctypes.c_double
         L.oracle_split_width.argtypes = [i32, i32]
         L.oracle_split_width.restype = i32
         L.oracle_quantize_kv.argtypes = [P, i64, i64, P, P, i64, i64, i32]
@@ -70,7 +77,7 @@ def lib():
                                      P, i64, i64, P, i64, P, P, P, i64, ctypes.c_int]
         L.oracle_decode_split.argtypes = [P, i64, i32, i64, i64, P, i64, i64, i32, P, i32, i64, P,
                                           f32, i32, P, P, P, i64, ctypes.c_int]
-        L.oracle_combine.argtypes = [P, P, i64, i32, i32, P, P, i64, i64, P, i64, P, P, P, i64]
+        L.oracle_combine.argtypes = [P, P, i64, i32, i32, i32, P, P, i64, i64, P, i64, P, P, P, i64]
         L.oracle_probs.argtypes = [P, i64, i32, i64, i64, P, i64, i64, i32, P, i32, i64, P, P, f32,
                                    i64, i32, P, P]
         for name in ("oracle_quantize_kv", "oracle_prefill", "oracle_decode_split",
@@ -90,6 +97,25 @@ def _elem_strides(a: np.ndarray):
 
 def row_bytes(fmt: int) -> int:
     return int(lib().oracle_row_bytes(fmt))
+
+
+def d_k(fmt: int) -> int:
+    """Elements of a dequantized K row (nope + rope)."""
+    return int(lib().oracle_d_k(fmt))
+
+
+def d_v(fmt: int) -> int:
+    """Elements of a V row (the nope part): 1024 for DOTS3_SWA rows, else 512."""
+    return int(lib().oracle_d_v(fmt))
+
+
+def e8m0_scale(amax: float) -> int:
+    """DOTS3_SWA tile scale byte (see oracle_e8m0_scale)."""
+    return int(lib().oracle_e8m0_scale(amax))
+
+
+def e8m0_decode(b: int) -> float:
+    return float(lib().oracle_e8m0_decode(b))
 
 
 def split_width(topk: int, num_splits: int) -> int:
@@ -134,7 +160,7 @@ class Pool:
 
 def quantize_kv(kv_bf16: np.ndarray, slots: np.ndarray, pool: Pool) -> None:
     """Write latent rows into the pool (FlashInfer PR #4802 review: 656-byte
-    DSv3.2 row layout; see smla_oracle.c).  kv_bf16: uint16 [n, >=576] rows."""
+    DSv3.2 row layout; see smla_oracle.c).  kv_bf16: uint16 [n, >=d_k] rows."""
     assert kv_bf16.dtype == np.uint16 and kv_bf16.strides[1] == 2
     slots = np.ascontiguousarray(slots, dtype=np.int32)
     n = kv_bf16.shape[0]
@@ -144,7 +170,7 @@ def quantize_kv(kv_bf16: np.ndarray, slots: np.ndarray, pool: Pool) -> None:
 
 def dequant_rows(pool: Pool, slots: np.ndarray) -> np.ndarray:
     slots = np.ascontiguousarray(slots, dtype=np.int32)
-    out = np.empty((slots.shape[0], D_QK), dtype=np.float64)
+    out = np.empty((slots.shape[0], d_k(pool.fmt)), dtype=np.float64)
     lib().oracle_dequant_rows(_ptr(pool.data), pool.block_stride, pool.fmt, _ptr(slots),
                               slots.shape[0], _ptr(out))
     return out
@@ -163,10 +189,10 @@ def _check_idx(indices):
 
 def prefill(q, pool: Pool, indices, topk_length=None, sink=None, sm_scale=1.0 / 24.0,
             tokens=None, nthreads: int = 0):
-    """Prefill form (see oracle_prefill).  q: uint16 (bf16 bits) [T,H,576]
+    """Prefill form (see oracle_prefill).  q: uint16 (bf16 bits) [T,H,d_k]
     (any strides, last dim contiguous); indices: int32 [T, >=topk] with
-    last dim contiguous.  Returns (out_bf16 uint16 [T,H,512], lse f32 [T,H],
-    out_f64 [T,H,512], lse_f64 [T,H]); rows of tokens not in `tokens` are
+    last dim contiguous.  Returns (out_bf16 uint16 [T,H,d_v], lse f32 [T,H],
+    out_f64 [T,H,d_v], lse_f64 [T,H]); rows of tokens not in `tokens` are
     left zero."""
     T, H, _ = q.shape
     qst, qsh = _check_q(q)
@@ -174,14 +200,15 @@ def prefill(q, pool: Pool, indices, topk_length=None, sink=None, sm_scale=1.0 / 
     topk = indices.shape[1]
     tl = None if topk_length is None else np.ascontiguousarray(topk_length, dtype=np.int32)
     sk = None if sink is None else np.ascontiguousarray(sink, dtype=np.float32)
-    out = np.zeros((T, H, D_V), dtype=np.uint16)
+    dv = d_v(pool.fmt)
+    out = np.zeros((T, H, dv), dtype=np.uint16)
     lse = np.zeros((T, H), dtype=np.float32)
-    of = np.zeros((T, H, D_V), dtype=np.float64)
+    of = np.zeros((T, H, dv), dtype=np.float64)
     lf = np.zeros((T, H), dtype=np.float64)
     tok = None if tokens is None else np.ascontiguousarray(tokens, dtype=np.int64)
     rc = lib().oracle_prefill(_ptr(q), T, H, qst, qsh, _ptr(pool.data), pool.num_blocks,
                               pool.block_stride, pool.fmt, _ptr(indices), topk, ist, _ptr(tl),
-                              _ptr(sk), float(sm_scale), _ptr(out), H * D_V, D_V, _ptr(lse), H,
+                              _ptr(sk), float(sm_scale), _ptr(out), H * dv, dv, _ptr(lse), H,
                               _ptr(of), _ptr(lf), _ptr(tok), 0 if tok is None else tok.shape[0],
                               nthreads)
     assert rc == 0
@@ -191,13 +218,13 @@ def prefill(q, pool: Pool, indices, topk_length=None, sink=None, sm_scale=1.0 / 
 def decode_split(q, pool: Pool, indices, num_splits: int, topk_length=None, sm_scale=1.0 / 24.0,
                  tokens=None, nthreads: int = 0):
     """Decode split form (see oracle_decode_split).  Returns float64
-    part_out [T,S,H,512] and part_lse [T,S,H]."""
+    part_out [T,S,H,d_v] and part_lse [T,S,H]."""
     T, H, _ = q.shape
     qst, qsh = _check_q(q)
     ist = _check_idx(indices)
     topk = indices.shape[1]
     tl = None if topk_length is None else np.ascontiguousarray(topk_length, dtype=np.int32)
-    po = np.zeros((T, num_splits, H, D_V), dtype=np.float64)
+    po = np.zeros((T, num_splits, H, d_v(pool.fmt)), dtype=np.float64)
     pl = np.zeros((T, num_splits, H), dtype=np.float64)
     tok = None if tokens is None else np.ascontiguousarray(tokens, dtype=np.int64)
     rc = lib().oracle_decode_split(_ptr(q), T, H, qst, qsh, _ptr(pool.data), pool.num_blocks,
@@ -212,16 +239,17 @@ def combine(part_out, part_lse, sink=None, tokens=None):
     """LSE combine (see oracle_combine).  Returns (out_bf16, lse_f32, out_f64, lse_f64)."""
     part_out = np.ascontiguousarray(part_out, dtype=np.float64)
     part_lse = np.ascontiguousarray(part_lse, dtype=np.float64)
-    T, S, H, _ = part_out.shape
+    T, S, H, dv = part_out.shape
     sk = None if sink is None else np.ascontiguousarray(sink, dtype=np.float32)
-    out = np.zeros((T, H, D_V), dtype=np.uint16)
+    out = np.zeros((T, H, dv), dtype=np.uint16)
     lse = np.zeros((T, H), dtype=np.float32)
-    of = np.zeros((T, H, D_V), dtype=np.float64)
+    of = np.zeros((T, H, dv), dtype=np.float64)
     lf = np.zeros((T, H), dtype=np.float64)
     tok = None if tokens is None else np.ascontiguousarray(tokens, dtype=np.int64)
-    lib().oracle_combine(_ptr(part_out), _ptr(part_lse), T, S, H, _ptr(sk), _ptr(out), H * D_V, D_V,
-                         _ptr(lse), H, _ptr(of), _ptr(lf), _ptr(tok),
-                         0 if tok is None else tok.shape[0])
+    rc = lib().oracle_combine(_ptr(part_out), _ptr(part_lse), T, S, H, dv, _ptr(sk), _ptr(out), H * dv,
+                              dv, _ptr(lse), H, _ptr(of), _ptr(lf), _ptr(tok),
+                              0 if tok is None else tok.shape[0])
+    assert rc == 0
     return out, lse, of, lf
 
 

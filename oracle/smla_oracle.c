@@ -37,6 +37,16 @@
  * nope dimensions only (q rows hold 512 values); every index outside
  * [0, num_blocks*64) -- -1 padding included -- contributes nothing.
  *
+ * DOTS3_SWA rows (FlashInfer PR #4802 description: d_qk = 1088, d_v = 1024,
+ * 1160 bytes per token with the scales in a footer): K is 1024 nope values
+ * plus 64 rope values and V the 1024 nope values.  The row is read as
+ * [0,1024) e4m3 codes, [1024,1152) the 64 BF16 rope values, [1152,1160) one
+ * scale byte per 128-element tile.  The byte count leaves one byte per
+ * scale, read as an unsigned power-of-two exponent with bias 127 (the
+ * E8M0 scale of the OCP microscaling formats: 2^(b-127), 255 = NaN).  The
+ * writer takes the same power-of-two scale as the FP8 rows, raised to at
+ * least 2^-126 so that the byte is never 0.
+ *
  * Precision: all attention arithmetic is float64.  The quantizer runs in
  * float32, because float32 arithmetic decides its integer codes and the
  * stored scales are float32.
@@ -49,17 +59,27 @@
 #include <omp.h>
 #endif
 
-#define D_NOPE 512
+#define D_NOPE 512 /* nope values of every row but DOTS3_SWA's */
 #define D_ROPE 64
 #define D_QK 576
-#define D_V 512
+#define D_NOPE_MAX 1024
+#define D_QK_MAX (D_NOPE_MAX + D_ROPE)
+#define D_V_MAX D_NOPE_MAX
 #define PAGE_BLOCK 64
 #define TILE 128 /* quantization tile width along the nope part */
 
-enum { FMT_BF16 = 0, FMT_FP8 = 1, FMT_INT8 = 2, FMT_FP8_ANY = 3, FMT_FP8_NOPE = 4 };
+enum { FMT_BF16 = 0, FMT_FP8 = 1, FMT_INT8 = 2, FMT_FP8_ANY = 3, FMT_FP8_NOPE = 4, FMT_FP8_DOTS3 = 5 };
 
+/* nope values of a row; K holds these plus D_ROPE rope values (zero for
+ * rows without rope dimensions), V is the nope part */
+static int d_nope(int32_t fmt) { return fmt == FMT_FP8_DOTS3 ? D_NOPE_MAX : D_NOPE; }
+static int d_k(int32_t fmt) { return d_nope(fmt) + D_ROPE; }
+static int d_v(int32_t fmt) { return d_nope(fmt); }
 /* elements of a query row that enter a score */
-static int q_dims(int32_t fmt) { return fmt == FMT_FP8_NOPE ? D_NOPE : D_QK; }
+static int q_dims(int32_t fmt) { return fmt == FMT_FP8_NOPE ? D_NOPE : d_k(fmt); }
+
+int32_t oracle_d_k(int32_t fmt) { return d_k(fmt); }
+int32_t oracle_d_v(int32_t fmt) { return d_v(fmt); }
 
 /* ---------------------------------------------------------------------- */
 /* Scalar helpers                                                          */
@@ -157,18 +177,48 @@ int8_t oracle_int8_encode(float x, float scale) {
   return (int8_t)q;
 }
 
+/* DOTS3_SWA tile scale byte: the FP8 power-of-two scale 2^e, e raised to
+ * at least -126, stored as e + 127 (so 1..254). */
+uint8_t oracle_e8m0_scale(float amax) {
+  int e;
+  frexpf(oracle_fp8_scale(amax), &e); /* the scale is 2^(e-1) */
+  e -= 1;
+  if (e < -126) e = -126;
+  return (uint8_t)(e + 127);
+}
+
+/* 2^(b-127); 255 is NaN */
+double oracle_e8m0_decode(uint8_t b) { return b == 255 ? NAN : ldexp(1.0, (int)b - 127); }
+
 int32_t oracle_row_bytes(int32_t fmt) {
-  return fmt == FMT_BF16 ? 2 * D_QK : D_NOPE + 4 * (D_NOPE / TILE) + 2 * D_ROPE;
+  if (fmt == FMT_BF16) return 2 * D_QK;
+  if (fmt == FMT_FP8_DOTS3) return D_NOPE_MAX + 2 * D_ROPE + D_NOPE_MAX / TILE;
+  return D_NOPE + 4 * (D_NOPE / TILE) + 2 * D_ROPE;
 }
 
 /* ---------------------------------------------------------------------- */
 /* Cache writer                                                            */
 /* ---------------------------------------------------------------------- */
 
-/* Quantize one BF16 latent row (576 raw bf16 values) into a pool row. */
+/* Quantize one BF16 latent row (d_k(fmt) raw bf16 values) into a pool row. */
 static void quantize_row(const uint16_t* x, int32_t fmt, uint8_t* row) {
   if (fmt == FMT_BF16) {
     memcpy(row, x, 2 * D_QK);
+    return;
+  }
+  if (fmt == FMT_FP8_DOTS3) {
+    for (int g = 0; g < D_NOPE_MAX / TILE; ++g) {
+      float amax = 0.0f;
+      for (int i = g * TILE; i < (g + 1) * TILE; ++i) {
+        float v = fabsf(bf16_bits_to_float(x[i]));
+        if (v > amax) amax = v;
+      }
+      uint8_t b = oracle_e8m0_scale(amax);
+      float scale = ldexpf(1.0f, (int)b - 127);
+      for (int i = g * TILE; i < (g + 1) * TILE; ++i) row[i] = oracle_e4m3_encode(bf16_bits_to_float(x[i]) / scale);
+      row[D_NOPE_MAX + 2 * D_ROPE + g] = b;
+    }
+    memcpy(row + D_NOPE_MAX, x + D_NOPE_MAX, 2 * D_ROPE);
     return;
   }
   for (int g = 0; g < D_NOPE / TILE; ++g) {
@@ -212,11 +262,21 @@ int oracle_quantize_kv(const uint16_t* kv, int64_t n, int64_t kv_stride, const i
 /* Cache reader                                                            */
 /* ---------------------------------------------------------------------- */
 
-/* Dequantize pool row `slot` into K[576] (V is K[0:512]). */
+/* Dequantize pool row `slot` into K[d_k(fmt)] (V is K[0:d_v(fmt)]). */
 static void dequant_row(const uint8_t* pool, int64_t block_stride_bytes, int32_t fmt,
                         int64_t slot, double* K) {
   int64_t rb = oracle_row_bytes(fmt);
   const uint8_t* row = pool + (slot / PAGE_BLOCK) * block_stride_bytes + (slot % PAGE_BLOCK) * rb;
+  if (fmt == FMT_FP8_DOTS3) {
+    for (int i = 0; i < D_NOPE_MAX; ++i)
+      K[i] = oracle_e4m3_decode(row[i]) * oracle_e8m0_decode(row[D_NOPE_MAX + 2 * D_ROPE + i / TILE]);
+    for (int r = 0; r < D_ROPE; ++r) {
+      uint16_t b;
+      memcpy(&b, row + D_NOPE_MAX + 2 * r, 2);
+      K[D_NOPE_MAX + r] = bf16_bits_to_float(b);
+    }
+    return;
+  }
   if (fmt == FMT_BF16) {
     for (int i = 0; i < D_QK; ++i) {
       uint16_t b;
@@ -243,8 +303,8 @@ static void dequant_row(const uint8_t* pool, int64_t block_stride_bytes, int32_t
 }
 
 void oracle_dequant_rows(const uint8_t* pool, int64_t block_stride_bytes, int32_t fmt,
-                         const int32_t* slots, int64_t n, double* out /* [n][576] */) {
-  for (int64_t i = 0; i < n; ++i) dequant_row(pool, block_stride_bytes, fmt, slots[i], out + i * D_QK);
+                         const int32_t* slots, int64_t n, double* out /* [n][d_k(fmt)] */) {
+  for (int64_t i = 0; i < n; ++i) dequant_row(pool, block_stride_bytes, fmt, slots[i], out + i * d_k(fmt));
 }
 
 /* ---------------------------------------------------------------------- */
@@ -290,21 +350,22 @@ static int64_t candidates(const problem* P, int64_t t, int64_t j0, int64_t j1, i
 static void attend(const problem* P, int64_t t, int32_t h, const double* rows, int64_t n,
                    double* scores, double* m_out, double* l_out, double* acc) {
   const uint16_t* qr = P->q + t * P->q_stride_t + (int64_t)h * P->q_stride_h;
-  double q[D_QK];
-  for (int i = 0; i < D_QK; ++i) q[i] = i < q_dims(P->fmt) ? bf16_bits_to_float(qr[i]) : 0.0;
+  const int dk = d_k(P->fmt), dv = d_v(P->fmt);
+  double q[D_QK_MAX];
+  for (int i = 0; i < dk; ++i) q[i] = i < q_dims(P->fmt) ? bf16_bits_to_float(qr[i]) : 0.0;
   double m = -INFINITY;
   for (int64_t j = 0; j < n; ++j) {
     double dot = 0.0;
-    for (int i = 0; i < D_QK; ++i) dot += q[i] * rows[j * D_QK + i];
+    for (int i = 0; i < dk; ++i) dot += q[i] * rows[j * dk + i];
     scores[j] = P->sm_scale * dot;
     if (scores[j] > m) m = scores[j];
   }
   double l = 0.0;
-  for (int d = 0; d < D_V; ++d) acc[d] = 0.0;
+  for (int d = 0; d < dv; ++d) acc[d] = 0.0;
   for (int64_t j = 0; j < n; ++j) {
     double p = exp(scores[j] - m);
     l += p;
-    for (int d = 0; d < D_V; ++d) acc[d] += p * rows[j * D_QK + d];
+    for (int d = 0; d < dv; ++d) acc[d] += p * rows[j * dk + d];
   }
   *m_out = m;
   *l_out = l;
@@ -326,7 +387,7 @@ static int nthreads_or_default(int nthreads) {
  *   Z = sum_j exp(s_j - m*) + exp(sink_h - m*) (sink term only when a sink
  *   is given); an empty set gives out = 0, lse = -inf.
  * out is rounded to BF16 (ties to even); out_f64 / lse_f64 (optional,
- * dense [T][H][512] / [T][H]) receive the unrounded values. */
+ * dense [T][H][d_v] / [T][H]) receive the unrounded values. */
 int oracle_prefill(const uint16_t* q, int64_t T, int32_t H, int64_t q_stride_t, int64_t q_stride_h,
                    const uint8_t* pool, int64_t num_blocks, int64_t block_stride_bytes, int32_t fmt,
                    const int32_t* indices, int32_t topk, int64_t idx_stride_t,
@@ -337,13 +398,14 @@ int oracle_prefill(const uint16_t* q, int64_t T, int32_t H, int64_t q_stride_t, 
                    const int64_t* token_list, int64_t n_tokens, int nthreads) {
   problem P = {q, T, H, q_stride_t, q_stride_h, pool, num_blocks, block_stride_bytes, fmt,
                indices, topk, idx_stride_t, topk_length, (double)sm_scale};
+  const int dk = d_k(fmt), dv = d_v(fmt);
   int64_t count = token_list ? n_tokens : T;
   int nt = nthreads_or_default(nthreads);
   int failed = 0;
 #pragma omp parallel num_threads(nt)
   {
     int32_t* cand = (int32_t*)malloc(sizeof(int32_t) * (topk > 0 ? topk : 1));
-    double* rows = (double*)malloc(sizeof(double) * D_QK * (topk > 0 ? topk : 1));
+    double* rows = (double*)malloc(sizeof(double) * dk * (topk > 0 ? topk : 1));
     double* scores = (double*)malloc(sizeof(double) * (topk > 0 ? topk : 1));
     if (!cand || !rows || !scores) {
 #pragma omp atomic write
@@ -353,12 +415,12 @@ int oracle_prefill(const uint16_t* q, int64_t T, int32_t H, int64_t q_stride_t, 
       for (int64_t it = 0; it < count; ++it) {
         int64_t t = token_list ? token_list[it] : it;
         int64_t n = candidates(&P, t, 0, topk, cand);
-        for (int64_t j = 0; j < n; ++j) dequant_row(pool, block_stride_bytes, fmt, cand[j], rows + j * D_QK);
+        for (int64_t j = 0; j < n; ++j) dequant_row(pool, block_stride_bytes, fmt, cand[j], rows + j * dk);
         for (int32_t h = 0; h < H; ++h) {
-          double acc[D_V], m = -INFINITY, l = 0.0, res_lse;
-          double o[D_V];
+          double acc[D_V_MAX], m = -INFINITY, l = 0.0, res_lse;
+          double o[D_V_MAX];
           if (n == 0) {
-            for (int d = 0; d < D_V; ++d) o[d] = 0.0;
+            for (int d = 0; d < dv; ++d) o[d] = 0.0;
             res_lse = -INFINITY;
           } else {
             attend(&P, t, h, rows, n, scores, &m, &l, acc);
@@ -367,12 +429,12 @@ int oracle_prefill(const uint16_t* q, int64_t T, int32_t H, int64_t q_stride_t, 
             if (sink && (double)sink[h] > ms) ms = (double)sink[h];
             double a = exp(m - ms); /* rescales exp(s - m) to exp(s - m*) */
             z = l * a + (sink ? exp((double)sink[h] - ms) : 0.0);
-            for (int d = 0; d < D_V; ++d) o[d] = acc[d] * a / z;
+            for (int d = 0; d < dv; ++d) o[d] = acc[d] * a / z;
           }
           uint16_t* orow = out + t * out_stride_t + (int64_t)h * out_stride_h;
-          for (int d = 0; d < D_V; ++d) orow[d] = oracle_double_to_bf16(o[d]);
+          for (int d = 0; d < dv; ++d) orow[d] = oracle_double_to_bf16(o[d]);
           lse[t * lse_stride_t + h] = (float)res_lse;
-          if (out_f64) memcpy(out_f64 + (t * H + h) * D_V, o, sizeof o);
+          if (out_f64) memcpy(out_f64 + (t * H + h) * dv, o, sizeof(double) * dv);
           if (lse_f64) lse_f64[t * H + h] = res_lse;
         }
       }
@@ -399,18 +461,19 @@ int oracle_decode_split(const uint16_t* q, int64_t T, int32_t H, int64_t q_strid
                         int64_t block_stride_bytes, int32_t fmt, const int32_t* indices,
                         int32_t topk, int64_t idx_stride_t, const int32_t* topk_length,
                         float sm_scale, int32_t num_splits,
-                        double* part_out /* [T][S][H][512] */, double* part_lse /* [T][S][H] */,
+                        double* part_out /* [T][S][H][d_v] */, double* part_lse /* [T][S][H] */,
                         const int64_t* token_list, int64_t n_tokens, int nthreads) {
   problem P = {q, T, H, q_stride_t, q_stride_h, pool, num_blocks, block_stride_bytes, fmt,
                indices, topk, idx_stride_t, topk_length, (double)sm_scale};
   int32_t w = oracle_split_width(topk, num_splits);
+  const int dk = d_k(fmt), dv = d_v(fmt);
   int64_t count = token_list ? n_tokens : T;
   int nt = nthreads_or_default(nthreads);
   int failed = 0;
 #pragma omp parallel num_threads(nt)
   {
     int32_t* cand = (int32_t*)malloc(sizeof(int32_t) * (w > 0 ? w : 1));
-    double* rows = (double*)malloc(sizeof(double) * D_QK * (w > 0 ? w : 1));
+    double* rows = (double*)malloc(sizeof(double) * dk * (w > 0 ? w : 1));
     double* scores = (double*)malloc(sizeof(double) * (w > 0 ? w : 1));
     if (!cand || !rows || !scores) {
 #pragma omp atomic write
@@ -423,18 +486,18 @@ int oracle_decode_split(const uint16_t* q, int64_t T, int32_t H, int64_t q_strid
           int64_t j0 = (int64_t)s * w, j1 = j0 + w;
           if (j1 > topk) j1 = topk;
           int64_t n = j0 < j1 ? candidates(&P, t, j0, j1, cand) : 0;
-          for (int64_t j = 0; j < n; ++j) dequant_row(pool, block_stride_bytes, fmt, cand[j], rows + j * D_QK);
+          for (int64_t j = 0; j < n; ++j) dequant_row(pool, block_stride_bytes, fmt, cand[j], rows + j * dk);
           for (int32_t h = 0; h < H; ++h) {
-            double* po = part_out + (((t * num_splits) + s) * H + h) * D_V;
+            double* po = part_out + (((t * num_splits) + s) * H + h) * dv;
             double* pl = part_lse + ((t * num_splits) + s) * H + h;
             if (n == 0) {
-              for (int d = 0; d < D_V; ++d) po[d] = 0.0;
+              for (int d = 0; d < dv; ++d) po[d] = 0.0;
               *pl = -INFINITY;
               continue;
             }
-            double acc[D_V], m, l;
+            double acc[D_V_MAX], m, l;
             attend(&P, t, h, rows, n, scores, &m, &l, acc);
-            for (int d = 0; d < D_V; ++d) po[d] = acc[d] / l;
+            for (int d = 0; d < dv; ++d) po[d] = acc[d] / l;
             *pl = m + log(l);
           }
         }
@@ -450,12 +513,14 @@ int oracle_decode_split(const uint16_t* q, int64_t T, int32_t H, int64_t q_strid
 /* Log-sum-exp merge of decode splits.  M = max_s LSE_s; if M = -inf the
  * result is out = 0, lse = -inf.  Otherwise w_s = exp(LSE_s - M),
  * W = sum w_s, lse = M + ln W, o = sum (w_s / W) O_s; with a sink the output
- * is scaled by 1 / (1 + exp(sink_h - lse)); out = bf16(o). */
+ * is scaled by 1 / (1 + exp(sink_h - lse)); out = bf16(o).  part_out rows
+ * hold dv values (512, or 1024 for DOTS3_SWA). */
 int oracle_combine(const double* part_out, const double* part_lse, int64_t T, int32_t num_splits,
-                   int32_t H, const float* sink, uint16_t* out, int64_t out_stride_t,
+                   int32_t H, int32_t dv, const float* sink, uint16_t* out, int64_t out_stride_t,
                    int64_t out_stride_h, float* lse, int64_t lse_stride_t, double* out_f64,
                    double* lse_f64, const int64_t* token_list, int64_t n_tokens) {
   int64_t count = token_list ? n_tokens : T;
+  if (dv < 1 || dv > D_V_MAX) return -1;
   for (int64_t it = 0; it < count; ++it) {
     int64_t t = token_list ? token_list[it] : it;
     for (int32_t h = 0; h < H; ++h) {
@@ -464,8 +529,8 @@ int oracle_combine(const double* part_out, const double* part_lse, int64_t T, in
         double v = part_lse[((t * num_splits) + s) * H + h];
         if (v > M) M = v;
       }
-      double o[D_V], res;
-      for (int d = 0; d < D_V; ++d) o[d] = 0.0;
+      double o[D_V_MAX], res;
+      for (int d = 0; d < dv; ++d) o[d] = 0.0;
       if (M == -INFINITY) {
         res = -INFINITY;
       } else {
@@ -475,18 +540,18 @@ int oracle_combine(const double* part_out, const double* part_lse, int64_t T, in
         for (int32_t s = 0; s < num_splits; ++s) {
           double ws = exp(part_lse[((t * num_splits) + s) * H + h] - M) / W;
           if (ws == 0.0) continue;
-          const double* po = part_out + (((t * num_splits) + s) * H + h) * D_V;
-          for (int d = 0; d < D_V; ++d) o[d] += ws * po[d];
+          const double* po = part_out + (((t * num_splits) + s) * H + h) * dv;
+          for (int d = 0; d < dv; ++d) o[d] += ws * po[d];
         }
         if (sink) {
           double f = 1.0 / (1.0 + exp((double)sink[h] - res));
-          for (int d = 0; d < D_V; ++d) o[d] *= f;
+          for (int d = 0; d < dv; ++d) o[d] *= f;
         }
       }
       uint16_t* orow = out + t * out_stride_t + (int64_t)h * out_stride_h;
-      for (int d = 0; d < D_V; ++d) orow[d] = oracle_double_to_bf16(o[d]);
+      for (int d = 0; d < dv; ++d) orow[d] = oracle_double_to_bf16(o[d]);
       lse[t * lse_stride_t + h] = (float)res;
-      if (out_f64) memcpy(out_f64 + (t * H + h) * D_V, o, sizeof o);
+      if (out_f64) memcpy(out_f64 + (t * H + h) * dv, o, sizeof(double) * dv);
       if (lse_f64) lse_f64[t * H + h] = res;
     }
   }
@@ -511,7 +576,7 @@ int oracle_probs(const uint16_t* q, int64_t T, int32_t H, int64_t q_stride_t, in
   }
   int64_t nslots = num_blocks * PAGE_BLOCK;
   double m = sink ? (double)sink[h] : -INFINITY;
-  double K[D_QK];
+  double K[D_QK_MAX];
   double* s = (double*)malloc(sizeof(double) * (topk > 0 ? topk : 1));
   if (!s) return -1;
   for (int64_t j = 0; j < topk; ++j) {

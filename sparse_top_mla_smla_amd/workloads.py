@@ -26,13 +26,19 @@ import numpy as np
 
 PAGE_BLOCK = 64
 D_QK, D_V = 576, 512
-FMT_BF16, FMT_FP8, FMT_INT8, FMT_FP8_ANY, FMT_FP8_NOPE = 0, 1, 2, 3, 4
+FMT_BF16, FMT_FP8, FMT_INT8, FMT_FP8_ANY, FMT_FP8_NOPE, FMT_FP8_DOTS3 = 0, 1, 2, 3, 4, 5
 FMT_NAMES = {FMT_BF16: "bf16", FMT_FP8: "fp8_e4m3", FMT_INT8: "int8", FMT_FP8_ANY: "fp8_e4m3_any_scale",
-             FMT_FP8_NOPE: "fp8_e4m3_nope"}
-ROW_BYTES = {FMT_BF16: 1152, FMT_FP8: 656, FMT_INT8: 656, FMT_FP8_ANY: 656, FMT_FP8_NOPE: 656}
+             FMT_FP8_NOPE: "fp8_e4m3_nope", FMT_FP8_DOTS3: "fp8_e4m3_dots3"}
+ROW_BYTES = {FMT_BF16: 1152, FMT_FP8: 656, FMT_INT8: 656, FMT_FP8_ANY: 656, FMT_FP8_NOPE: 656,
+             FMT_FP8_DOTS3: 1160}
 # elements of a query row that enter a score (NOPE rows have no rope dimensions)
-Q_DIMS = {FMT_BF16: 576, FMT_FP8: 576, FMT_INT8: 576, FMT_FP8_ANY: 576, FMT_FP8_NOPE: 512}
+Q_DIMS = {FMT_BF16: 576, FMT_FP8: 576, FMT_INT8: 576, FMT_FP8_ANY: 576, FMT_FP8_NOPE: 512,
+          FMT_FP8_DOTS3: 1088}
+# elements of a latent row (and of the q buffer's rows) and of an output row
+KV_DIMS = {f: (1088 if f == FMT_FP8_DOTS3 else D_QK) for f in FMT_NAMES}
+V_DIMS = {f: (1024 if f == FMT_FP8_DOTS3 else D_V) for f in FMT_NAMES}
 SM_SCALE = np.float32(1.0 / 24.0)  # 1/sqrt(576)
+SM_SCALE_DOTS3 = np.float32(1.0 / np.sqrt(1088.0))
 PAD_SENTINEL = 0x7FFFFFFF
 
 TID_Q, TID_KV, TID_IDX, TID_BT, TID_LEN, TID_SINK = 1, 2, 3, 4, 5, 6
@@ -90,8 +96,8 @@ class Case:
     n_seqs: int
     ctx: int
     topk: int
-    q_buf: np.ndarray            # uint16 [T, Hbuf, 576]; heads [0, H) are used
-    kv: np.ndarray               # uint16 [n_seqs*ctx, 576] latent rows, row = seq*ctx + pos
+    q_buf: np.ndarray            # uint16 [T, Hbuf, KV_DIMS]; heads [0, H) are used
+    kv: np.ndarray               # uint16 [n_seqs*ctx, KV_DIMS] latent rows, row = seq*ctx + pos
     slots: np.ndarray            # int32 [n_seqs*ctx] pool slot of each latent row
     num_blocks: int
     block_table: np.ndarray      # int32 [n_seqs, ctx/64]
@@ -157,8 +163,8 @@ def make_case(name: str, *, config_id: int, seed: int = 0, fmt: int, T: int, H: 
     pos = np.arange(ctx)
     slots = (bt[:, pos // PAGE_BLOCK] * PAGE_BLOCK + (pos % PAGE_BLOCK)[None, :]).astype(np.int32)
     slots = slots.reshape(-1)
-    kv = normal_bf16(rng_for(seed, config_id, TID_KV), (n_seqs * ctx, D_QK))
-    q_buf = normal_bf16(rng_for(seed, config_id, TID_Q), (T, hbuf, D_QK))
+    kv = normal_bf16(rng_for(seed, config_id, TID_KV), (n_seqs * ctx, KV_DIMS[fmt]))
+    q_buf = normal_bf16(rng_for(seed, config_id, TID_Q), (T, hbuf, KV_DIMS[fmt]))
 
     if n_seqs == 1:
         seq_of_token = np.zeros(T, dtype=np.int64)
@@ -197,7 +203,8 @@ def make_case(name: str, *, config_id: int, seed: int = 0, fmt: int, T: int, H: 
         sink = rng_for(seed, config_id, TID_SINK).standard_normal(H, dtype=np.float32)
     return Case(name=name, fmt=fmt, T=T, H=H, n_seqs=n_seqs, ctx=ctx, topk=topk, q_buf=q_buf,
                 kv=kv, slots=slots, num_blocks=num_blocks, block_table=bt, idx_buf=idx_buf,
-                topk_length=topk_length, sink=sink, sm_scale=SM_SCALE, positions=positions,
+                topk_length=topk_length, sink=sink,
+                sm_scale=SM_SCALE_DOTS3 if fmt == FMT_FP8_DOTS3 else SM_SCALE, positions=positions,
                 seq_of_token=seq_of_token, num_splits=num_splits, out_hbuf=out_hbuf)
 
 

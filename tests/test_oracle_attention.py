@@ -16,7 +16,7 @@ from sparse_top_mla_smla_amd import workloads as W
 
 from helpers import dense_attention, np_dequant, oracle_pool, q_f64
 
-FMTS = [W.FMT_BF16, W.FMT_FP8, W.FMT_INT8, W.FMT_FP8_ANY, W.FMT_FP8_NOPE]
+FMTS = [W.FMT_BF16, W.FMT_FP8, W.FMT_INT8, W.FMT_FP8_ANY, W.FMT_FP8_NOPE, W.FMT_FP8_DOTS3]
 
 
 def full_ctx_case(fmt, seed=0, ctx=192, T=3, H=4, with_sink=False):
@@ -35,7 +35,7 @@ def test_dense_brute_force(fmt, with_sink):
     q = q_f64(c)
     for h in range(c.H):
         o_ref, l_ref = dense_attention(q[:, h], K, float(c.sm_scale),
-                                       None if c.sink is None else float(c.sink[h]))
+                                       None if c.sink is None else float(c.sink[h]), dv=W.V_DIMS[fmt])
         assert np.allclose(of[:, h], o_ref, rtol=0, atol=1e-12)
         assert np.allclose(lf[:, h], l_ref, rtol=0, atol=1e-12)
     # BF16 output is the nearest BF16 of the float64 value
@@ -50,9 +50,9 @@ def test_dense_vs_torch_sdpa(fmt):
     pool = oracle_pool(c)
     _, _, of, _ = oracle.prefill(c.q, pool, c.indices, sm_scale=c.sm_scale)
     K = torch.tensor(np_dequant(pool, c.slots))
-    q = torch.tensor(q_f64(c)).permute(1, 0, 2).unsqueeze(0)     # [1,H,T,576]
+    q = torch.tensor(q_f64(c)).permute(1, 0, 2).unsqueeze(0)     # [1,H,T,d_k]
     k = K.unsqueeze(0).unsqueeze(0).expand(1, c.H, -1, -1)
-    v = K[:, :512].unsqueeze(0).unsqueeze(0).expand(1, c.H, -1, -1)
+    v = K[:, :W.V_DIMS[fmt]].unsqueeze(0).unsqueeze(0).expand(1, c.H, -1, -1)
     ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, scale=float(c.sm_scale))
     assert np.allclose(of, ref[0].permute(1, 0, 2).numpy(), rtol=0, atol=1e-12)
 
@@ -72,7 +72,8 @@ def test_sparse_equals_dense_over_selected_rows(fmt):
         sel = c.indices[t][c.indices[t] >= 0]
         K = np_dequant(pool, sel)
         for h in range(c.H):
-            o_ref, l_ref = dense_attention(q[t:t + 1, h], K, float(c.sm_scale), float(c.sink[h]))
+            o_ref, l_ref = dense_attention(q[t:t + 1, h], K, float(c.sm_scale), float(c.sink[h]),
+                                           dv=W.V_DIMS[fmt])
             assert np.allclose(of[t, h], o_ref[0], atol=1e-12, rtol=0)
             assert abs(lf[t, h] - l_ref[0]) < 1e-12
 
@@ -123,6 +124,7 @@ def tiny_pool(fmt, seed=0):
 def test_closed_forms(fmt):
     c, pool = tiny_pool(fmt, seed=fmt)
     q = q_f64(c)
+    dv = W.V_DIMS[fmt]
     K = np_dequant(pool, np.arange(64))
     s = float(c.sm_scale)
     a, b = 7, 42
@@ -132,14 +134,14 @@ def test_closed_forms(fmt):
     _, _, of, lf = oracle.prefill(c.q, pool, idx, sm_scale=c.sm_scale)
     for t in range(2):
         for h in range(3):
-            assert np.allclose(of[t, h], K[a, :512], atol=1e-12, rtol=0)
+            assert np.allclose(of[t, h], K[a, :dv], atol=1e-12, rtol=0)
             assert abs(lf[t, h] - s * q[t, h] @ K[a]) < 1e-12
     # one candidate with a sink: out = V * sigmoid(score - sink)
     _, _, of, _ = oracle.prefill(c.q, pool, idx, sink=c.sink, sm_scale=c.sm_scale)
     for t in range(2):
         for h in range(3):
             z = s * q[t, h] @ K[a] - float(c.sink[h])
-            assert np.allclose(of[t, h], K[a, :512] / (1 + np.exp(-z)), atol=1e-12, rtol=0)
+            assert np.allclose(of[t, h], K[a, :dv] / (1 + np.exp(-z)), atol=1e-12, rtol=0)
     # two candidates: weights sigmoid(s_a - s_b), sigmoid(s_b - s_a)
     idx[:, 5] = b
     _, _, of, lf = oracle.prefill(c.q, pool, idx, sm_scale=c.sm_scale)
@@ -147,7 +149,7 @@ def test_closed_forms(fmt):
         for h in range(3):
             sa, sb = s * q[t, h] @ K[a], s * q[t, h] @ K[b]
             pa = 1 / (1 + np.exp(sb - sa))
-            assert np.allclose(of[t, h], pa * K[a, :512] + (1 - pa) * K[b, :512], atol=1e-12, rtol=0)
+            assert np.allclose(of[t, h], pa * K[a, :dv] + (1 - pa) * K[b, :dv], atol=1e-12, rtol=0)
             assert abs(lf[t, h] - np.logaddexp(sa, sb)) < 1e-12
     # n copies of one slot: out = V, lse = s + ln n
     idx = np.full((2, 8), a, np.int32)
@@ -155,7 +157,7 @@ def test_closed_forms(fmt):
     _, _, of, lf = oracle.prefill(c.q, pool, idx, sm_scale=c.sm_scale)
     for t in range(2):
         for h in range(3):
-            assert np.allclose(of[t, h], K[a, :512], atol=1e-12, rtol=0)
+            assert np.allclose(of[t, h], K[a, :dv], atol=1e-12, rtol=0)
             assert abs(lf[t, h] - (s * q[t, h] @ K[a] + np.log(6))) < 1e-12
 
 
@@ -188,7 +190,7 @@ def test_probabilities_sum_to_one(fmt):
             valid = (np.arange(c.topk) < L) & (c.indices[t] >= 0)
             assert np.all(p[~valid] == 0)
             K = np_dequant(pool, np.where(valid, c.indices[t], 0))
-            assert np.allclose(p @ K[:, :512], of[t, h], atol=1e-12, rtol=0)
+            assert np.allclose(p @ K[:, :W.V_DIMS[fmt]], of[t, h], atol=1e-12, rtol=0)
             # the sink's share equals 1 / (1 + exp(lse - sink))
             assert abs(ps - 1 / (1 + np.exp(lf[t, h] - c.sink[h]))) < 1e-12
 
