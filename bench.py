@@ -21,7 +21,12 @@ Also measured in the same run:
   buffer, ctx 32768 BF16 pool, top-k 640 with per-token lengths and a sink,
   written in place; beside it the same inputs with all 64 heads;
 - "int8": T = 1024, H = 128, ctx 65536 INT8 pool, top-k 2048 as a view of a
-  4096-wide index buffer, with a sink.
+  4096-wide index buffer, with a sink; and in "decode", the decode batch
+  over an INT8 pool at the model's split count;
+- "dots3": DOTS3_SWA rows (1160 bytes, d_qk 1088, d_v 1024) -- prefill at
+  T = 1024, ctx 16384, H = 64 over 513-entry lists (385 causal uniform + a
+  128-position window) with a sink, and decode of 32 sequences x 1 query
+  at 4 splits (decode + combine).
 Kernel times come from HIP events on the launch stream (median, p10, p90).
 
 Prints one JSON line on stdout.
@@ -110,6 +115,90 @@ def load_traffic(sha: str):
     if d.get("kernel_source_sha") != sha:
         return None
     return d.get("hbm_bytes_per_launch")
+
+
+def dots3_lines(torch, smla, W, dev, stream, bf16, args):
+    """DOTS3_SWA prefill and decode (1160-byte rows, d_v 1024)."""
+    out = {}
+    pc = W.dots3_prefill()
+    q = bf16(pc.q_buf)
+    kv = bf16(pc.kv)
+    pool = smla.KVPool.empty(pc.num_blocks, W.FMT_FP8_DOTS3, device=dev)
+    smla.quantize_kv(kv, torch.from_numpy(pc.slots).to(dev), pool)
+    del kv
+    idx = torch.from_numpy(pc.idx_buf).to(dev)
+    sink = torch.from_numpy(pc.sink).to(dev)
+    o = torch.empty((pc.T, pc.H, 1024), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((pc.T, pc.H), dtype=torch.float32, device=dev)
+
+    def pre():
+        smla.prefill(q, pool, idx, sink=sink, sm_scale=float(pc.sm_scale), out=o, lse=lse)
+
+    pre()
+    tp = pct(event_times_us(torch, pre, 10, stream))
+    rows = pc.gathered_rows()
+    nbytes = rows * W.ROW_BYTES[W.FMT_FP8_DOTS3]
+    flops = 2.0 * pc.H * (1088 + 1024) * rows
+    out["prefill"] = {
+        "workload": f"dots3_swa prefill T={pc.T} ctx={pc.ctx} H={pc.H} topk={pc.topk} (385 causal uniform + "
+                    "128-position window), sink",
+        "kernel_us_median_p10_p90": [round(v, 3) for v in tp],
+        "us_per_token": round(tp[0] / pc.T, 5),
+        "gathered_kv_bytes": nbytes,
+        "gathered_kv_GBps": round(nbytes / (tp[0] * 1e-6) / 1e9, 2),
+        "mfma_util": round(flops / (tp[0] * 1e-6) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+    }
+    print(f"[bench] dots3 prefill {tp[0]:.1f} us", file=sys.stderr, flush=True)
+    del q, pool, idx, o, lse
+    torch.cuda.empty_cache()
+
+    dc = W.dots3_decode()
+    q = bf16(dc.q_buf)
+    kv = bf16(dc.kv)
+    pool = smla.KVPool.empty(dc.num_blocks, W.FMT_FP8_DOTS3, device=dev)
+    smla.quantize_kv(kv, torch.from_numpy(dc.slots).to(dev), pool)
+    del kv
+    idx = torch.from_numpy(dc.idx_buf).to(dev)
+    # three index sets (the same positions in freshly permuted blocks), so
+    # that consecutive calls do not find their rows cache-warm
+    rng = np.random.default_rng(9)
+    idx_sets = [idx]
+    for _ in range(2):
+        remap = torch.from_numpy(rng.permutation(dc.num_blocks).astype(np.int32)).to(dev)
+        moved = remap[(idx.clamp(min=0) // 64).long()] * 64 + idx.clamp(min=0) % 64
+        idx_sets.append(torch.where(idx >= 0, moved, idx).to(torch.int32))
+    calls = [0]
+    S = dc.num_splits
+    po = torch.empty((dc.T, S, dc.H, 1024), dtype=torch.float32, device=dev)
+    pl = torch.empty((dc.T, S, dc.H), dtype=torch.float32, device=dev)
+    o = torch.empty((dc.T, dc.H, 1024), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((dc.T, dc.H), dtype=torch.float32, device=dev)
+
+    def dec():
+        calls[0] += 1
+        smla.decode(q, pool, idx_sets[calls[0] % 3], S, sm_scale=float(dc.sm_scale), part_out=po, part_lse=pl)
+
+    def comb():
+        smla.combine(po, pl, out=o, lse=lse)
+
+    dec()
+    comb()
+    td = pct(event_times_us(torch, dec, 20, stream))
+    tc = pct(event_times_us(torch, comb, 20, stream))
+    drows = dc.gathered_rows()
+    dbytes = drows * W.ROW_BYTES[W.FMT_FP8_DOTS3]
+    out["decode"] = {
+        "workload": f"dots3_swa decode {dc.T} seqs x 1 query, ctx {dc.ctx}, H={dc.H}, topk={dc.topk}, splits={S} "
+                    "(decode + combine)",
+        "decode_kernel_us_median_p10_p90": [round(v, 3) for v in td],
+        "combine_kernel_us_median_p10_p90": [round(v, 3) for v in tc],
+        "gathered_kv_bytes": dbytes,
+        "gathered_kv_GBps_end_to_end": round(dbytes / ((td[0] + tc[0]) * 1e-6) / 1e9, 2),
+    }
+    print(f"[bench] dots3 decode {td[0]:.1f} + {tc[0]:.1f} us (S={S})", file=sys.stderr, flush=True)
+    del q, pool, idx, idx_sets, po, pl, o, lse
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -252,6 +341,10 @@ def main():
         didx = torch.from_numpy(dc.idx_buf).to(dev)
         dpool = smla.KVPool.empty(dc.num_blocks, W.FMT_FP8, device=dev)
         smla.quantize_kv(dkv, dslots, dpool)
+        ipool8 = None
+        if not args.no_extra:  # the same rows in an INT8 pool
+            ipool8 = smla.KVPool.empty(dc.num_blocks, W.FMT_INT8, device=dev)
+            smla.quantize_kv(dkv, dslots, ipool8)
         del dkv
         dout = torch.empty((dc.T, dc.H, D_V), dtype=torch.bfloat16, device=dev)
         dlse = torch.empty((dc.T, dc.H), dtype=torch.float32, device=dev)
@@ -269,7 +362,8 @@ def main():
         drows = dc.gathered_rows()
         dbytes = drows * W.ROW_BYTES[W.FMT_FP8]
 
-        def time_decode(S):
+        def time_decode(S, pool=None):
+            pool = pool or dpool
             po = torch.empty((dc.T, S, dc.H, D_V), dtype=torch.float32, device=dev)
             pl = torch.empty((dc.T, S, dc.H), dtype=torch.float32, device=dev)
 
@@ -277,7 +371,7 @@ def main():
                 ix = idx_sets[i % len(idx_sets)]
                 if ev is not None:
                     ev[0].record(stream)
-                smla.decode(dq, dpool, ix, S, sm_scale=float(dc.sm_scale), part_out=po, part_lse=pl)
+                smla.decode(dq, pool, ix, S, sm_scale=float(dc.sm_scale), part_out=po, part_lse=pl)
                 if ev is not None:
                     ev[1].record(stream)
                 smla.combine(po, pl, out=dout, lse=dlse)
@@ -326,6 +420,15 @@ def main():
         print(f"[bench] decode {d8['decode_kernel_us']:.2f} us + combine {d8['combine_kernel_us']:.2f} us (S={S}); "
               f"model S={Sm}: {model['decode_kernel_us']:.2f} + {model['combine_kernel_us']:.2f} us",
               file=sys.stderr, flush=True)
+        if ipool8 is not None:
+            Si = smla.decode_num_splits(dc.T, dc.H, dc.topk, W.FMT_INT8)
+            i8d = time_decode(Si, ipool8)
+            i8d["predicted_us"] = round(smla.split_model_cost(dc.T, dc.H, dc.topk, W.FMT_INT8, Si), 2)
+            i8d["workload"] = f"int8 split-KV decode, the same batch and rows, splits={Si} (the model's count)"
+            result["decode"]["int8"] = i8d
+            print(f"[bench] int8 decode {i8d['decode_kernel_us']:.2f} + {i8d['combine_kernel_us']:.2f} us (S={Si})",
+                  file=sys.stderr, flush=True)
+            del ipool8
         # dual cache: the first 1024 entries of each list over this pool, and a
         # 2176-wide secondary list over a second pool of the same size
         if not args.no_extra:
@@ -448,6 +551,10 @@ def main():
         print(f"[bench] int8 {i_med[0]:.1f} us", file=sys.stderr, flush=True)
         del iq, ipool, iidx, iout, ilse
         torch.cuda.empty_cache()
+
+    # ---------------- DOTS3_SWA rows ----------------
+    if not args.no_extra:
+        result["dots3"] = dots3_lines(torch, smla, W, dev, stream, bf16, args)
 
     if args.calibrate_copy:
         n = args.calibrate_copy << 20

@@ -76,13 +76,25 @@ typedef enum {
  * bytes [528, 656) are reserved padding, never written, gathered or read;
  * K and V are the 512 nope values, q rows hold 512 values (q_stride_h >=
  * 512) and the writer reads 512 values per row (kv_stride >= 512).  BF16
- * row = 576 BF16 values (1152 bytes). */
+ * row = 576 BF16 values (1152 bytes).
+ * FP8_E4M3_DOTS3 is the DOTS3_SWA row (same PR's description: d_qk 1088,
+ * d_v 1024, 1160 bytes per token with the scales in a footer): [0,1024)
+ * e4m3 codes of the 1024 nope values, [1024,1152) 64 BF16 rope values,
+ * [1152,1160) one scale byte per 128-element tile, read as the power of
+ * two 2^(b-127) (b = 255 is NaN); the byte count leaves one byte per scale.
+ * K is the 1024 nope + 64 rope values and V the 1024 nope values: q rows
+ * hold 1088 values, out and decode partial rows 1024, and the writer reads
+ * 1088 values per latent row.  Its writer takes the power-of-two scale of
+ * the FP8 rows, raised to at least 2^-126, so it stores b in [1, 254].
+ * Lists of any width run on it (the page's lists hold at least 513
+ * entries); the dual-list entry points do not accept it. */
 typedef enum {
   SMLA_KV_BF16 = 0,
   SMLA_KV_FP8_E4M3 = 1,
   SMLA_KV_INT8 = 2,
   SMLA_KV_FP8_E4M3_ANY_SCALE = 3,
-  SMLA_KV_FP8_E4M3_NOPE = 4
+  SMLA_KV_FP8_E4M3_NOPE = 4,
+  SMLA_KV_FP8_E4M3_DOTS3 = 5
 } smla_kv_format;
 
 /* A paged latent pool.  Slot s (a flat pool position) lives in block s/64 at
@@ -92,8 +104,9 @@ typedef enum {
  * bytes beyond the format's (PR #4802 review of the binding: rows addressed
  * by a token-axis stride that may exceed bytes_per_token); with one latent
  * head per row the NHD and HND block layouts differ only in these two
- * strides.  base must be 16-byte aligned; R a multiple of 16 and at least
- * the row bytes; block_stride_bytes a multiple of 16 and at least 64*R;
+ * strides.  base must be 16-byte aligned; R a multiple of 16 (of 8 for
+ * FP8_E4M3_DOTS3, whose 1160-byte rows pack 8-byte aligned) and at least
+ * the row bytes; block_stride_bytes a multiple of the same and at least 64*R;
  * page_block must be 64 (PR #4802: the kernels are compiled for page block
  * 64 and launchers reject anything else).  Bytes outside the rows are never
  * read or written. */
@@ -106,8 +119,18 @@ typedef struct {
   int64_t row_stride_bytes; /* 0: dense rows */
 } smla_kv_pool;
 
-/* Bytes of one cache row: 1152 (BF16), 656 (FP8, INT8); -1 for an unknown format. */
+/* Bytes of one cache row: 1152 (BF16), 656 (FP8, INT8 and the other
+ * 656-byte rows), 1160 (FP8_E4M3_DOTS3); -1 for an unknown format. */
 int32_t smla_row_bytes(int32_t format);
+
+/* Values per q row that enter a score, which is also the values per latent
+ * row that smla_quantize_kv reads: 576, 512 (FP8_E4M3_NOPE) or 1088
+ * (FP8_E4M3_DOTS3); -1 for an unknown format. */
+int32_t smla_query_dims(int32_t format);
+
+/* Values per output row (d_v): 1024 for FP8_E4M3_DOTS3, else 512; -1 for an
+ * unknown format. */
+int32_t smla_value_dims(int32_t format);
 
 /* Width of one decode split: 64 * ceil(ceil(topk / num_splits) / 64).  Split
  * s covers list positions [s*w, min((s+1)*w, topk)); trailing splits may be
@@ -116,17 +139,19 @@ int32_t smla_row_bytes(int32_t format);
 int32_t smla_split_width(int32_t topk, int32_t num_splits);
 
 /* Scratch smla_decode needs, for callers that carve it from one buffer:
- * *bytes_out = T*num_splits*H*512*4 (part_out) + T*num_splits*H*4
- * (part_lse).  part_out may start at the buffer and part_lse at byte offset
- * T*num_splits*H*2048, which keeps both 16-byte aligned.  (PR #4802 makes
- * decode scratch caller-owned and sized by the library so that a graph can
- * hold it.)  T >= 0, H in [1, 128], num_splits in [1, 64]; SMLA_ERR_NULL
- * when bytes_out is NULL, SMLA_ERR_SHAPE otherwise out of range. */
-smla_status smla_decode_workspace_size(int64_t T, int32_t H, int32_t num_splits, size_t* bytes_out);
+ * *bytes_out = T*num_splits*H*d_v*4 (part_out) + T*num_splits*H*4
+ * (part_lse), d_v = smla_value_dims of the pool's format.  part_out may
+ * start at the buffer and part_lse at byte offset T*num_splits*H*d_v*4,
+ * which keeps both 16-byte aligned.  (PR #4802 makes decode scratch
+ * caller-owned and sized by the library so that a graph can hold it.)
+ * T >= 0, H in [1, 128], num_splits in [1, 64], d_v 512 or 1024;
+ * SMLA_ERR_NULL when bytes_out is NULL, SMLA_ERR_SHAPE otherwise out of
+ * range. */
+smla_status smla_decode_workspace_size(int64_t T, int32_t H, int32_t num_splits, int32_t d_v, size_t* bytes_out);
 
 /* Write n latent rows into the pool.
- *   kv     BF16 [n, >=576], row i at kv + i*kv_stride (kv_stride >= 576,
- *          multiple of 8, kv 16-byte aligned)
+ *   kv     BF16 [n, >=D], row i at kv + i*kv_stride (kv_stride >= D =
+ *          smla_query_dims(format), multiple of 8, kv 16-byte aligned)
  *   slots  int32 [n]: destination slot of row i; slots outside
  *          [0, num_blocks*64) (-1 included) are skipped.
  * FP8: per 128-element tile of the nope part, amax = max |x|; scale = 1 when
@@ -134,20 +159,22 @@ smla_status smla_decode_workspace_size(int64_t T, int32_t H, int32_t num_splits,
  * "power-of-2 FP32 scales"); codes = e4m3(x / scale), round to nearest even,
  * sign kept.  FP8_E4M3_ANY_SCALE: scale = amax/448 (FP32, correctly rounded;
  * 1 when amax = 0), codes as for FP8.  INT8: scale = amax/127 (1 when amax = 0), codes =
- * clamp(rne(x/scale), -127, 127).  BF16: a copy.  Rope values are copied
- * bit for bit.  Two slots that are equal race (last writer wins). */
+ * clamp(rne(x/scale), -127, 127).  FP8_E4M3_DOTS3: the FP8 rule over its
+ * eight tiles with the scale 2^e raised to at least 2^-126, e + 127 stored
+ * as the tile's scale byte.  BF16: a copy.  Rope values are copied bit for
+ * bit.  Two slots that are equal race (last writer wins). */
 smla_status smla_quantize_kv(const void* kv, int64_t n, int64_t kv_stride, const int32_t* slots,
                              smla_kv_pool pool, void* stream);
 
 /* Prefill form: attention for T query tokens, written straight to out/lse.
- *   q            BF16 [T, H, 576] with strides (q_stride_t, q_stride_h):
+ *   q            BF16 [T, H, D] (D = smla_query_dims(format)) with strides (q_stride_t, q_stride_h):
  *                both multiples of 8, q 16-byte aligned (views such as
  *                q[:, :8] of a wider head buffer are allowed)
  *   indices      int32 [T, >=topk], row stride idx_stride_t >= topk: flat
  *                slot ids (a narrowed view of a wider buffer is allowed)
  *   topk_length  int32 [T] or NULL
  *   sink         FP32 [H] or NULL
- *   out          BF16 [T, H, 512] with strides (out_stride_t, out_stride_h),
+ *   out          BF16 [T, H, d_v] (d_v = smla_value_dims(format)) with strides (out_stride_t, out_stride_h),
  *                multiples of 8, 16-byte aligned; written in place
  *   lse          FP32 [T, H] with row stride lse_stride_t >= H
  * H in [1, 128]. */
@@ -191,7 +218,7 @@ smla_status smla_prefill_dual(const void* q, int64_t T, int32_t H, int64_t q_str
  * the partial result over that split's candidates, with no sink:
  *   part_lse[t,s,h] = ln sum_{j in split} exp(s_j)   (-inf when empty)
  *   part_out[t,s,h,:] = sum exp(s_j) V_j / sum exp(s_j)  (0 when empty)
- * part_out FP32 [T, num_splits, H, 512] and part_lse FP32 [T, num_splits, H]
+ * part_out FP32 [T, num_splits, H, d_v] and part_lse FP32 [T, num_splits, H]
  * are caller-owned, contiguous, 16-byte aligned.  Other arguments as in
  * smla_prefill.  num_splits in [1, 64]. */
 smla_status smla_decode(const void* q, int64_t T, int32_t H, int64_t q_stride_t, int64_t q_stride_h,
@@ -211,10 +238,11 @@ smla_status smla_decode_dual(const void* q, int64_t T, int32_t H, int64_t q_stri
  * M = max_s part_lse, w_s = exp(part_lse_s - M) and W = sum w_s,
  *   lse = M + ln W,  o = sum_s (w_s / W) part_out_s,
  *   and with a sink o *= 1 / (1 + exp(sink_h - lse));  out = bf16(o).
- * All splits empty (M = -inf): out = 0, lse = -inf.  Buffers as in
- * smla_decode / smla_prefill. */
+ * All splits empty (M = -inf): out = 0, lse = -inf.  d_v (512 or 1024) is
+ * the row width of part_out and out (smla_value_dims of the pool that
+ * smla_decode read).  Buffers as in smla_decode / smla_prefill. */
 smla_status smla_combine(const float* part_out, const float* part_lse, int64_t T, int32_t num_splits,
-                         int32_t H, const float* sink, void* out, int64_t out_stride_t,
+                         int32_t H, int32_t d_v, const float* sink, void* out, int64_t out_stride_t,
                          int64_t out_stride_h, float* lse, int64_t lse_stride_t, void* stream);
 
 /* Split-count model (FlashInfer PR #4802, description sections "cpb model"
@@ -230,8 +258,9 @@ smla_status smla_combine(const float* part_out, const float* part_lse, int64_t T
  * with waves = rounds of workgroups over compute_units and constants fitted
  * per kernel (format, H > 16) by calibrate_splits.py in the package.
  * compute_units <= 0 means the current device's.  Returns -1 when T < 1,
- * H outside [1, 128], topk < 1, the format is unknown or num_splits is
- * outside [0, 64]. */
+ * H outside [1, 128], topk < 1, num_splits is outside [0, 64], or the
+ * format is unknown or has no fitted constants (FP8_E4M3_DOTS3: there
+ * smla_attention runs the prefill form). */
 double smla_split_model_cost(int64_t T, int32_t H, int32_t topk, int32_t format, int32_t num_splits,
                              int32_t compute_units);
 

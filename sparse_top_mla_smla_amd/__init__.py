@@ -15,9 +15,10 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["KVPool", "quantize_kv", "prefill", "decode", "combine", "split_width", "row_bytes",
-           "library_path", "SmlaError", "FMT_BF16", "FMT_FP8", "FMT_INT8"]
+           "query_dims", "value_dims", "library_path", "SmlaError", "FMT_BF16", "FMT_FP8", "FMT_INT8",
+           "FMT_FP8_ANY", "FMT_FP8_NOPE", "FMT_FP8_DOTS3"]
 
-FMT_BF16, FMT_FP8, FMT_INT8 = 0, 1, 2
+FMT_BF16, FMT_FP8, FMT_INT8, FMT_FP8_ANY, FMT_FP8_NOPE, FMT_FP8_DOTS3 = 0, 1, 2, 3, 4, 5
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libsmla.so")
 _lib = None
@@ -53,7 +54,9 @@ def _load():
     P, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
     L.smla_row_bytes.argtypes, L.smla_row_bytes.restype = [i32], i32
     L.smla_split_width.argtypes, L.smla_split_width.restype = [i32, i32], i32
-    L.smla_decode_workspace_size.argtypes = [i64, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
+    L.smla_query_dims.argtypes, L.smla_query_dims.restype = [i32], i32
+    L.smla_value_dims.argtypes, L.smla_value_dims.restype = [i32], i32
+    L.smla_decode_workspace_size.argtypes = [i64, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
     L.smla_decode_workspace_size.restype = ctypes.c_int
     L.smla_last_error.argtypes, L.smla_last_error.restype = [], ctypes.c_char_p
     L.smla_version.argtypes, L.smla_version.restype = [], ctypes.c_char_p
@@ -61,7 +64,7 @@ def _load():
     L.smla_prefill.argtypes = [P, i64, i32, i64, i64, _Pool, P, i32, i64, P, P, f32, P, i64, i64,
                                P, i64, P]
     L.smla_decode.argtypes = [P, i64, i32, i64, i64, _Pool, P, i32, i64, P, f32, i32, P, P, P]
-    L.smla_combine.argtypes = [P, P, i64, i32, i32, P, P, i64, i64, P, i64, P]
+    L.smla_combine.argtypes = [P, P, i64, i32, i32, i32, P, P, i64, i64, P, i64, P]
     L.smla_split_model_cost.argtypes = [i64, i32, i32, i32, i32, i32]
     L.smla_split_model_cost.restype = ctypes.c_double
     L.smla_decode_num_splits.argtypes, L.smla_decode_num_splits.restype = [i64, i32, i32, i32, i32], i32
@@ -91,14 +94,24 @@ def row_bytes(fmt: int) -> int:
     return int(_load().smla_row_bytes(fmt))
 
 
+def query_dims(fmt: int) -> int:
+    """Values per q row (and per latent row the writer reads) for a format."""
+    return int(_load().smla_query_dims(fmt))
+
+
+def value_dims(fmt: int) -> int:
+    """Values per output row (d_v) for a format."""
+    return int(_load().smla_value_dims(fmt))
+
+
 def split_width(topk: int, num_splits: int) -> int:
     return int(_load().smla_split_width(topk, num_splits))
 
 
-def decode_workspace_size(T: int, H: int, num_splits: int) -> int:
+def decode_workspace_size(T: int, H: int, num_splits: int, d_v: int = 512) -> int:
     """Bytes of decode scratch (part_out then part_lse) for T tokens."""
     n = ctypes.c_size_t(0)
-    _check(_load().smla_decode_workspace_size(T, H, num_splits, ctypes.byref(n)), "smla_decode_workspace_size")
+    _check(_load().smla_decode_workspace_size(T, H, num_splits, d_v, ctypes.byref(n)), "smla_decode_workspace_size")
     return int(n.value)
 
 
@@ -177,11 +190,11 @@ class KVPool:
 
 
 def quantize_kv(kv: torch.Tensor, slots: torch.Tensor, pool: KVPool, stream=None) -> None:
-    """Write BF16 latent rows kv [n, >=576] into pool slots (see smla_quantize_kv)."""
+    """Write BF16 latent rows kv [n, >=query_dims] into pool slots (see smla_quantize_kv)."""
     _need(kv, "kv", torch.bfloat16)
     _need(slots, "slots", torch.int32)
     n = kv.shape[0]
-    _check(_load().smla_quantize_kv(_ptr(kv), n, kv.stride(0) if n else 576, _ptr(slots), pool.c(),
+    _check(_load().smla_quantize_kv(_ptr(kv), n, kv.stride(0) if n else query_dims(pool.fmt), _ptr(slots), pool.c(),
                                     _stream(stream)), "smla_quantize_kv")
 
 
@@ -195,8 +208,9 @@ def prefill(q: torch.Tensor, pool: KVPool, indices: torch.Tensor, topk: Optional
             topk_length: Optional[torch.Tensor] = None, sink: Optional[torch.Tensor] = None,
             sm_scale: float = 1.0 / 24.0, out: Optional[torch.Tensor] = None,
             lse: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Sparse MLA prefill (see smla_prefill).  q [T,H,576] bf16 (strided views
-    allowed), indices [T, >=topk] int32.  Returns (out [T,H,512] bf16, lse [T,H] f32)."""
+    """Sparse MLA prefill (see smla_prefill).  q [T,H,query_dims] bf16 (strided
+    views allowed), indices [T, >=topk] int32.  Returns (out [T,H,value_dims]
+    bf16, lse [T,H] f32)."""
     _need(q, "q", torch.bfloat16)
     T, H, _ = q.shape
     topk, ist = _idx_args(indices, topk)
@@ -205,7 +219,7 @@ def prefill(q: torch.Tensor, pool: KVPool, indices: torch.Tensor, topk: Optional
     if sink is not None:
         _need(sink, "sink", torch.float32)
     if out is None:
-        out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=q.device)
+        out = torch.empty((T, H, value_dims(pool.fmt)), dtype=torch.bfloat16, device=q.device)
     if lse is None:
         lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
     _need(out, "out", torch.bfloat16)
@@ -222,14 +236,14 @@ def decode(q: torch.Tensor, pool: KVPool, indices: torch.Tensor, num_splits: int
            sm_scale: float = 1.0 / 24.0, part_out: Optional[torch.Tensor] = None,
            part_lse: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Split-KV decode partials (see smla_decode).  Returns part_out
-    [T,S,H,512] f32 and part_lse [T,S,H] f32."""
+    [T,S,H,value_dims] f32 and part_lse [T,S,H] f32."""
     _need(q, "q", torch.bfloat16)
     T, H, _ = q.shape
     topk, ist = _idx_args(indices, topk)
     if topk_length is not None:
         _need(topk_length, "topk_length", torch.int32)
     if part_out is None:
-        part_out = torch.empty((T, num_splits, H, 512), dtype=torch.float32, device=q.device)
+        part_out = torch.empty((T, num_splits, H, value_dims(pool.fmt)), dtype=torch.float32, device=q.device)
     if part_lse is None:
         part_lse = torch.empty((T, num_splits, H), dtype=torch.float32, device=q.device)
     _need(part_out, "part_out", torch.float32)
@@ -250,16 +264,16 @@ def combine(part_out: torch.Tensor, part_lse: torch.Tensor, sink: Optional[torch
     _need(part_lse, "part_lse", torch.float32)
     if not (part_out.is_contiguous() and part_lse.is_contiguous()):
         raise SmlaError("part_out / part_lse must be contiguous")
-    T, S, H, _ = part_out.shape
+    T, S, H, dv = part_out.shape
     if sink is not None:
         _need(sink, "sink", torch.float32)
     if out is None:
-        out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=part_out.device)
+        out = torch.empty((T, H, dv), dtype=torch.bfloat16, device=part_out.device)
     if lse is None:
         lse = torch.empty((T, H), dtype=torch.float32, device=part_out.device)
     _need(out, "out", torch.bfloat16)
     _need(lse, "lse", torch.float32)
-    _check(_load().smla_combine(_ptr(part_out), _ptr(part_lse), T, S, H, _ptr(sink), _ptr(out),
+    _check(_load().smla_combine(_ptr(part_out), _ptr(part_lse), T, S, H, dv, _ptr(sink), _ptr(out),
                                 out.stride(0), out.stride(1), _ptr(lse), lse.stride(0),
                                 _stream(stream)), "smla_combine")
     return out, lse
@@ -281,7 +295,7 @@ def attention(q: torch.Tensor, pool: KVPool, indices: torch.Tensor, topk: Option
     if sink is not None:
         _need(sink, "sink", torch.float32)
     if out is None:
-        out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=q.device)
+        out = torch.empty((T, H, value_dims(pool.fmt)), dtype=torch.bfloat16, device=q.device)
     if lse is None:
         lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
     _need(out, "out", torch.bfloat16)
@@ -321,7 +335,7 @@ def prefill_dual(q: torch.Tensor, pool: KVPool, indices: torch.Tensor, extra_poo
     if sink is not None:
         _need(sink, "sink", torch.float32)
     if out is None:
-        out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=q.device)
+        out = torch.empty((T, H, value_dims(pool.fmt)), dtype=torch.bfloat16, device=q.device)
     if lse is None:
         lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
     _need(out, "out", torch.bfloat16)
@@ -347,7 +361,7 @@ def decode_dual(q: torch.Tensor, pool: KVPool, indices: torch.Tensor, extra_pool
     if topk_length is not None:
         _need(topk_length, "topk_length", torch.int32)
     if part_out is None:
-        part_out = torch.empty((T, num_splits, H, 512), dtype=torch.float32, device=q.device)
+        part_out = torch.empty((T, num_splits, H, value_dims(pool.fmt)), dtype=torch.float32, device=q.device)
     if part_lse is None:
         part_lse = torch.empty((T, num_splits, H), dtype=torch.float32, device=q.device)
     _need(part_out, "part_out", torch.float32)

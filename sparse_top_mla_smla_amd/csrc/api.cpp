@@ -30,25 +30,33 @@ smla_status ok() {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// DOTS3_SWA rows are 1160 bytes: rows and blocks need only 8-byte alignment
+int64_t row_align(int32_t format) { return format == SMLA_KV_FP8_E4M3_DOTS3 ? 8 : 16; }
+
 smla_status check_pool(const smla_kv_pool& kv) {
   if (!kv.base) return fail(SMLA_ERR_NULL, "kv pool base is NULL");
   if (kv.page_block != 64)
     return fail(SMLA_ERR_UNSUPPORTED, "page_block %d is not supported (supported: 64)", kv.page_block);
   int32_t rb = smla_row_bytes(kv.format);
   if (rb < 0)
-    return fail(SMLA_ERR_UNSUPPORTED, "kv format %d is not supported (supported: 0 = BF16, 1 = FP8_E4M3, 2 = INT8, 3 = FP8_E4M3_ANY_SCALE, 4 = FP8_E4M3_NOPE)",
+    return fail(SMLA_ERR_UNSUPPORTED,
+                "kv format %d is not supported (supported: 0 = BF16, 1 = FP8_E4M3, 2 = INT8, 3 = FP8_E4M3_ANY_SCALE, "
+                "4 = FP8_E4M3_NOPE, 5 = FP8_E4M3_DOTS3)",
                 kv.format);
   if (kv.num_blocks < 1) return fail(SMLA_ERR_SHAPE, "num_blocks %lld must be >= 1", (long long)kv.num_blocks);
   if (kv.num_blocks > (int64_t)(INT32_MAX / 64) + 1)
     return fail(SMLA_ERR_SHAPE, "num_blocks %lld exceeds the int32 slot range", (long long)kv.num_blocks);
   const int64_t rs = kv.row_stride_bytes ? kv.row_stride_bytes : rb;
   if (rs < rb) return fail(SMLA_ERR_STRIDE, "row_stride_bytes %lld is smaller than the %d-byte row", (long long)rs, rb);
-  if (rs % 16 != 0) return fail(SMLA_ERR_STRIDE, "row_stride_bytes %lld is not a multiple of 16", (long long)rs);
+  const int64_t ra = row_align(kv.format);
+  if (rs % ra != 0)
+    return fail(SMLA_ERR_STRIDE, "row_stride_bytes %lld is not a multiple of %lld", (long long)rs, (long long)ra);
   if (kv.block_stride_bytes < 64LL * rs)
     return fail(SMLA_ERR_STRIDE, "block_stride_bytes %lld is smaller than 64 rows of %lld bytes",
                 (long long)kv.block_stride_bytes, (long long)rs);
-  if (kv.block_stride_bytes % 16 != 0)
-    return fail(SMLA_ERR_STRIDE, "block_stride_bytes %lld is not a multiple of 16", (long long)kv.block_stride_bytes);
+  if (kv.block_stride_bytes % ra != 0)
+    return fail(SMLA_ERR_STRIDE, "block_stride_bytes %lld is not a multiple of %lld", (long long)kv.block_stride_bytes,
+                (long long)ra);
   if (!aligned(kv.base, 16)) return fail(SMLA_ERR_STRIDE, "kv pool base is not 16-byte aligned");
   return SMLA_OK;
 }
@@ -67,7 +75,7 @@ smla_status check_attn_common(const void* q, int64_t T, int32_t H, int64_t q_st,
   smla_status st = check_pool(kv);
   if (st != SMLA_OK) return st;
   if (!aligned(q, 16)) return fail(SMLA_ERR_STRIDE, "q is not 16-byte aligned");
-  const int64_t qd = kv.format == SMLA_KV_FP8_E4M3_NOPE ? 512 : 576;  // values per q row
+  const int64_t qd = smla_query_dims(kv.format);  // values per q row
   if (q_sh < qd || q_sh % 8 != 0)
     return fail(SMLA_ERR_STRIDE, "q_stride_h = %lld must be >= %lld and a multiple of 8", (long long)q_sh,
                 (long long)qd);
@@ -79,12 +87,12 @@ smla_status check_attn_common(const void* q, int64_t T, int32_t H, int64_t q_st,
 }
 
 smla_status check_out(const void* out, int64_t out_st, int64_t out_sh, int32_t H, const float* lse,
-                      int64_t lse_st) {
+                      int64_t lse_st, int32_t dv) {
   if (!out) return fail(SMLA_ERR_NULL, "out is NULL");
   if (!lse) return fail(SMLA_ERR_NULL, "lse is NULL");
   if (!aligned(out, 16)) return fail(SMLA_ERR_STRIDE, "out is not 16-byte aligned");
-  if (out_sh < 512 || out_sh % 8 != 0)
-    return fail(SMLA_ERR_STRIDE, "out_stride_h = %lld must be >= 512 and a multiple of 8", (long long)out_sh);
+  if (out_sh < dv || out_sh % 8 != 0)
+    return fail(SMLA_ERR_STRIDE, "out_stride_h = %lld must be >= %d and a multiple of 8", (long long)out_sh, dv);
   if (out_st % 8 != 0 || out_st < 0)
     return fail(SMLA_ERR_STRIDE, "out_stride_t = %lld must be a non-negative multiple of 8", (long long)out_st);
   if (lse_st < H) return fail(SMLA_ERR_STRIDE, "lse_stride_t = %lld is smaller than H = %d", (long long)lse_st, H);
@@ -95,6 +103,8 @@ smla_status check_out(const void* out, int64_t out_st, int64_t out_sh, int32_t H
 // the secondary list of a dual-cache call (extra != NULL)
 smla_status check_extra(const smla_kv_pool& kv, int32_t topk, const smla_kv_extra* extra) {
   if (!extra) return SMLA_OK;
+  if (kv.format == SMLA_KV_FP8_E4M3_DOTS3)
+    return fail(SMLA_ERR_UNSUPPORTED, "a secondary list is not supported for FP8_E4M3_DOTS3 pools");
   if (topk % 64 != 0)
     return fail(SMLA_ERR_UNSUPPORTED, "topk = %d: with a secondary list the main list width must be a multiple of 64",
                 topk);
@@ -129,8 +139,26 @@ int32_t smla_row_bytes(int32_t format) {
     case SMLA_KV_INT8: return 656;
     case SMLA_KV_FP8_E4M3_ANY_SCALE: return 656;
     case SMLA_KV_FP8_E4M3_NOPE: return 656;
+    case SMLA_KV_FP8_E4M3_DOTS3: return 1160;
     default: return -1;
   }
+}
+
+int32_t smla_query_dims(int32_t format) {
+  switch (format) {
+    case SMLA_KV_BF16:
+    case SMLA_KV_FP8_E4M3:
+    case SMLA_KV_INT8:
+    case SMLA_KV_FP8_E4M3_ANY_SCALE: return 576;
+    case SMLA_KV_FP8_E4M3_NOPE: return 512;
+    case SMLA_KV_FP8_E4M3_DOTS3: return 1088;
+    default: return -1;
+  }
+}
+
+int32_t smla_value_dims(int32_t format) {
+  if (smla_row_bytes(format) < 0) return -1;
+  return format == SMLA_KV_FP8_E4M3_DOTS3 ? 1024 : 512;
 }
 
 int32_t smla_split_width(int32_t topk, int32_t num_splits) {
@@ -139,20 +167,21 @@ int32_t smla_split_width(int32_t topk, int32_t num_splits) {
   return ((per + 63) / 64) * 64;
 }
 
-smla_status smla_decode_workspace_size(int64_t T, int32_t H, int32_t num_splits, size_t* bytes_out) {
+smla_status smla_decode_workspace_size(int64_t T, int32_t H, int32_t num_splits, int32_t d_v, size_t* bytes_out) {
   if (!bytes_out) return fail(SMLA_ERR_NULL, "bytes_out is NULL");
   if (T < 0) return fail(SMLA_ERR_SHAPE, "T = %lld must be >= 0", (long long)T);
   if (H < 1 || H > 128) return fail(SMLA_ERR_SHAPE, "H = %d is outside [1, 128]", H);
   if (num_splits < 1 || num_splits > 64)
     return fail(SMLA_ERR_SHAPE, "num_splits = %d is outside [1, 64]", num_splits);
+  if (d_v != 512 && d_v != 1024) return fail(SMLA_ERR_SHAPE, "d_v = %d is not 512 or 1024", d_v);
   const size_t rows = (size_t)T * (size_t)num_splits * (size_t)H;
-  *bytes_out = rows * 512 * sizeof(float) + rows * sizeof(float);
+  *bytes_out = rows * (size_t)d_v * sizeof(float) + rows * sizeof(float);
   return ok();
 }
 
 const char* smla_last_error(void) { return g_err; }
 
-const char* smla_version(void) { return "smla 0.1.0 (gfx950)"; }
+const char* smla_version(void) { return "smla 0.2.0 (gfx950)"; }
 
 smla_status smla_quantize_kv(const void* kv, int64_t n, int64_t kv_stride, const int32_t* slots,
                              smla_kv_pool pool, void* stream) {
@@ -162,7 +191,7 @@ smla_status smla_quantize_kv(const void* kv, int64_t n, int64_t kv_stride, const
   if (!slots) return fail(SMLA_ERR_NULL, "slots is NULL");
   smla_status st = check_pool(pool);
   if (st != SMLA_OK) return st;
-  const int64_t kd = pool.format == SMLA_KV_FP8_E4M3_NOPE ? 512 : 576;  // values read per latent row
+  const int64_t kd = smla_query_dims(pool.format);  // values read per latent row
   if (kv_stride < kd || kv_stride % 8 != 0)
     return fail(SMLA_ERR_STRIDE, "kv_stride = %lld must be >= %lld and a multiple of 8", (long long)kv_stride,
                 (long long)kd);
@@ -233,7 +262,7 @@ smla_status smla_prefill_dual(const void* q, int64_t T, int32_t H, int64_t q_str
   if (T == 0) return ok();
   st = check_extra(kv, topk, extra);
   if (st != SMLA_OK) return st;
-  st = check_out(out, out_stride_t, out_stride_h, H, lse, lse_stride_t);
+  st = check_out(out, out_stride_t, out_stride_h, H, lse, lse_stride_t, smla_value_dims(kv.format));
   if (st != SMLA_OK) return st;
   if (!std::isfinite(sm_scale)) return fail(SMLA_ERR_SHAPE, "sm_scale must be finite");
   if (T == 0) return ok();
@@ -286,10 +315,11 @@ smla_status smla_decode_dual(const void* q, int64_t T, int32_t H, int64_t q_stri
 }
 
 smla_status smla_combine(const float* part_out, const float* part_lse, int64_t T, int32_t num_splits,
-                         int32_t H, const float* sink, void* out, int64_t out_stride_t,
+                         int32_t H, int32_t d_v, const float* sink, void* out, int64_t out_stride_t,
                          int64_t out_stride_h, float* lse, int64_t lse_stride_t, void* stream) {
   if (T < 0) return fail(SMLA_ERR_SHAPE, "T = %lld must be >= 0", (long long)T);
   if (T == 0) return ok();  // nothing is read or launched
+  if (d_v != 512 && d_v != 1024) return fail(SMLA_ERR_SHAPE, "d_v = %d is not 512 or 1024", d_v);
   if (H < 1) return fail(SMLA_ERR_SHAPE, "H = %d must be >= 1", H);
   if (H > 128) return fail(SMLA_ERR_UNSUPPORTED, "H = %d is not supported (supported: 1..128)", H);
   if (num_splits < 1 || num_splits > 64)
@@ -297,11 +327,12 @@ smla_status smla_combine(const float* part_out, const float* part_lse, int64_t T
   if (!part_out) return fail(SMLA_ERR_NULL, "part_out is NULL");
   if (!part_lse) return fail(SMLA_ERR_NULL, "part_lse is NULL");
   if (!aligned(part_out, 16)) return fail(SMLA_ERR_STRIDE, "part_out is not 16-byte aligned");
-  smla_status st = check_out(out, out_stride_t, out_stride_h, H, lse, lse_stride_t);
+  smla_status st = check_out(out, out_stride_t, out_stride_h, H, lse, lse_stride_t, d_v);
   if (st != SMLA_OK) return st;
   if (T == 0) return ok();
   if ((T * H + 3) / 4 > (int64_t)UINT32_MAX) return fail(SMLA_ERR_SHAPE, "T*H is too large");
   smla::CombineParams p;
+  p.dv = d_v;
   p.part_out = part_out;
   p.part_lse = part_lse;
   p.T = T;
@@ -326,7 +357,8 @@ smla_status smla_attention_workspace_size(int64_t T, int32_t H, int32_t topk, in
   if (smla_row_bytes(format) < 0) return fail(SMLA_ERR_UNSUPPORTED, "kv format %d is not supported", format);
   *bytes_out = 0;
   if (T == 0 || smla_use_split_form(T, H, topk, format, 0) != 1) return ok();
-  return smla_decode_workspace_size(T, H, smla_decode_num_splits(T, H, topk, format, 0), bytes_out);
+  return smla_decode_workspace_size(T, H, smla_decode_num_splits(T, H, topk, format, 0), smla_value_dims(format),
+                                    bytes_out);
 }
 
 smla_status smla_attention(const void* q, int64_t T, int32_t H, int64_t q_stride_t, int64_t q_stride_h,
@@ -338,7 +370,8 @@ smla_status smla_attention(const void* q, int64_t T, int32_t H, int64_t q_stride
   smla_status st = check_attn_common(q, T, H, q_stride_t, q_stride_h, kv, indices, topk, idx_stride_t);
   if (st != SMLA_OK) return st;
   if (T == 0) return ok();
-  st = check_out(out, out_stride_t, out_stride_h, H, lse, lse_stride_t);
+  const int32_t dv = smla_value_dims(kv.format);
+  st = check_out(out, out_stride_t, out_stride_h, H, lse, lse_stride_t, dv);
   if (st != SMLA_OK) return st;
   if (!std::isfinite(sm_scale)) return fail(SMLA_ERR_SHAPE, "sm_scale must be finite");
   if (workspace && !aligned(workspace, 16)) return fail(SMLA_ERR_STRIDE, "workspace is not 16-byte aligned");
@@ -346,16 +379,16 @@ smla_status smla_attention(const void* q, int64_t T, int32_t H, int64_t q_stride
   if (workspace && smla_use_split_form(T, H, topk, kv.format, 0) == 1) {
     S = smla_decode_num_splits(T, H, topk, kv.format, 0);
     size_t need = 0;
-    if (smla_decode_workspace_size(T, H, S, &need) != SMLA_OK || need > workspace_bytes) S = 0;
+    if (smla_decode_workspace_size(T, H, S, dv, &need) != SMLA_OK || need > workspace_bytes) S = 0;
   }
   if (S == 0)
     return smla_prefill(q, T, H, q_stride_t, q_stride_h, kv, indices, topk, idx_stride_t, topk_length, sink,
                         sm_scale, out, out_stride_t, out_stride_h, lse, lse_stride_t, stream);
   float* part_out = static_cast<float*>(workspace);
-  float* part_lse = part_out + (size_t)T * (size_t)S * (size_t)H * 512;
+  float* part_lse = part_out + (size_t)T * (size_t)S * (size_t)H * (size_t)dv;
   st = smla_decode(q, T, H, q_stride_t, q_stride_h, kv, indices, topk, idx_stride_t, topk_length, sm_scale, S,
                    part_out, part_lse, stream);
   if (st != SMLA_OK) return st;
-  return smla_combine(part_out, part_lse, T, S, H, sink, out, out_stride_t, out_stride_h, lse, lse_stride_t,
+  return smla_combine(part_out, part_lse, T, S, H, dv, sink, out, out_stride_t, out_stride_h, lse, lse_stride_t,
                       stream);
 }

@@ -5,14 +5,16 @@
 // wave is 64 lanes, so one wave merges one (token, head) with split s in
 // lane s (up to 64 splits): a wave max gives M, a wave sum gives
 // W = sum exp(lse_s - M), and each lane then accumulates 8 of the 512
-// output columns over the splits.  The sink (FlashInfer PR #4802 / vLLM
+// output columns over the splits (16 of 1024 for DOTS3_SWA's value width).  The sink (FlashInfer PR #4802 / vLLM
 // PR #57673 attn_sink) scales the merged output by 1 / (1 + exp(sink - lse)).
 #include "device_common.h"
 #include "launch.h"
 
 namespace smla {
 
+template <int DV>
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
+  constexpr int NV = DV / 256;  // f32x4 per lane
   const int lane = threadIdx.x & 63;
   const int64_t pair = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (pair >= p.T * p.H) return;  // whole waves exit together
@@ -26,33 +28,39 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   const bool empty = (M == -INFINITY);
   const float lse_v = empty ? -INFINITY : M + logf(W);
 
-  f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+  f32x4 a[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) a[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   if (!empty) {
     const float invW = 1.0f / W;
     for (int s = 0; s < p.S; ++s) {
       const float ws = __shfl(w, s) * invW;
       if (ws != 0.0f) {
-        const f32x4* src = reinterpret_cast<const f32x4*>(p.part_out + ((t * p.S + s) * p.H + h) * (int64_t)D_V) + 2 * lane;
-        a0 += ws * src[0];
-        a1 += ws * src[1];
+        const f32x4* src = reinterpret_cast<const f32x4*>(p.part_out + ((t * p.S + s) * p.H + h) * (int64_t)DV) + NV * lane;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) a[i] += ws * src[i];
       }
     }
     if (p.sink) {
       const float f = 1.0f / (1.0f + expf(p.sink[h] - lse_v));
-      a0 *= f;
-      a1 *= f;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) a[i] *= f;
     }
   }
-  uint16_t* orow = p.out + t * p.out_st + (int64_t)h * p.out_sh + 8 * lane;
-  *reinterpret_cast<uint4*>(orow) = make_uint4(pack_bf16(a0[0], a0[1]), pack_bf16(a0[2], a0[3]),
-                                               pack_bf16(a1[0], a1[1]), pack_bf16(a1[2], a1[3]));
+  uint16_t* orow = p.out + t * p.out_st + (int64_t)h * p.out_sh + 4 * NV * lane;
+#pragma unroll
+  for (int i = 0; i < NV; i += 2)
+    *reinterpret_cast<uint4*>(orow + 4 * i) = make_uint4(pack_bf16(a[i][0], a[i][1]), pack_bf16(a[i][2], a[i][3]),
+                                                         pack_bf16(a[i + 1][0], a[i + 1][1]),
+                                                         pack_bf16(a[i + 1][2], a[i + 1][3]));
   if (lane == 0) p.lse[t * p.lse_st + h] = lse_v;
 }
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t s) {
   const int64_t pairs = p.T * p.H;
   dim3 grid((unsigned)((pairs + 3) / 4)), block(256);
-  hipLaunchKernelGGL(combine_kernel, grid, block, 0, s, p);
+  if (p.dv == dots3::D_V) hipLaunchKernelGGL(combine_kernel<dots3::D_V>, grid, block, 0, s, p);
+  else hipLaunchKernelGGL(combine_kernel<D_V>, grid, block, 0, s, p);
   return hipGetLastError();
 }
 

@@ -41,7 +41,7 @@ struct AttnParams {
   float* lse;
   int64_t lse_st;
   // decode outputs
-  float* part_out;      // [T, S, H, 512]
+  float* part_out;      // [T, S, H, d_v]
   float* part_lse;      // [T, S, H]
   int32_t num_splits;
   int32_t split_w;
@@ -61,6 +61,7 @@ struct CombineParams {
   const float* part_lse;
   int64_t T;
   int32_t S, H;
+  int32_t dv;           // values per part_out and out row: 512, or 1024 (DOTS3_SWA)
   const float* sink;
   uint16_t* out;
   int64_t out_st, out_sh;
@@ -72,6 +73,7 @@ hipError_t launch_quantize(const QuantParams& p, int fmt, hipStream_t s);
 hipError_t launch_attention(const AttnParams& p, int fmt, bool decode, hipStream_t s);
 hipError_t launch_attention_wide(const AttnParams& p, int fmt, bool decode, hipStream_t s);
 hipError_t launch_attention_fp8(const AttnParams& p, bool decode, hipStream_t s);
+hipError_t launch_attention_dots3(const AttnParams& p, bool decode, hipStream_t s);
 hipError_t launch_combine(const CombineParams& p, hipStream_t s);
 
 // compute units of the current device (256 when it cannot be queried)

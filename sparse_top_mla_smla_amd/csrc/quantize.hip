@@ -37,17 +37,19 @@ __device__ __forceinline__ uint32_t e4m3_from_f32(float y) {
   return sign | code;
 }
 
-// 2^ceil(log2(amax/448)) from the bits of r = amax / 448 (float32, r > 0).
-__device__ __forceinline__ float fp8_tile_scale(float amax) {
-  if (amax == 0.0f) return 1.0f;
+// e with 2^e = 2^ceil(log2(amax/448)), from the bits of r = amax / 448
+// (float32, amax > 0).
+__device__ __forceinline__ int fp8_scale_exponent(float amax) {
   float r = __fdiv_rn(amax, 448.0f);
   uint32_t rb = __builtin_bit_cast(uint32_t, r);
-  int e;
-  if (rb >= 0x00800000u) {
-    e = (int)(rb >> 23) - 127 + ((rb & 0x7FFFFFu) != 0u);
-  } else {  // subnormal r = rb * 2^-149
-    e = (32 - __clz((int)(rb - 1u))) - 149;
-  }
+  if (rb >= 0x00800000u) return (int)(rb >> 23) - 127 + ((rb & 0x7FFFFFu) != 0u);
+  return (32 - __clz((int)(rb - 1u))) - 149;  // subnormal r = rb * 2^-149
+}
+
+// 2^ceil(log2(amax/448)); 1 when amax = 0.
+__device__ __forceinline__ float fp8_tile_scale(float amax) {
+  if (amax == 0.0f) return 1.0f;
+  const int e = fp8_scale_exponent(amax);
   uint32_t sb = (e >= -126) ? (uint32_t)(e + 127) << 23 : 1u << (e + 149);
   return __builtin_bit_cast(float, sb);
 }
@@ -111,6 +113,61 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantParams p) {
   }
 }
 
+// DOTS3_SWA rows: the same power-of-two scale, with its exponent raised to
+// at least -126 and stored as one byte (e + 127) in the row's footer.  One
+// wave per row; lane l owns nope elements [16l, 16l+16), so the 8 lanes of
+// an aligned group cover one 128-element tile.  Rows are 8-byte aligned.
+__global__ __launch_bounds__(256) void quantize_dots3_kernel(QuantParams p) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= p.n) return;
+  const int64_t slot = p.slots[row];
+  if (slot < 0 || slot >= p.nslots) return;
+  const uint16_t* src = p.kv + row * p.kv_stride;
+  uint8_t* dst = p.pool + (slot / PAGE) * p.block_stride + (slot % PAGE) * p.row_stride;
+
+  const uint4* s4 = reinterpret_cast<const uint4*>(src) + 2 * lane;
+  const uint4 r0 = s4[0], r1 = s4[1];
+  const uint32_t w[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+  float x[16];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    x[2 * i] = __builtin_bit_cast(float, w[i] << 16);
+    x[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xFFFF0000u);
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
+#pragma unroll
+  for (int o = 1; o < 8; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+  int e = amax == 0.0f ? 0 : fp8_scale_exponent(amax);
+  e = e < -126 ? -126 : e;
+  const float scale = __builtin_bit_cast(float, (uint32_t)(e + 127) << 23);
+  uint32_t code[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) code[i] = e4m3_from_f32(__fdiv_rn(x[i], scale));
+  uint32_t pk[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    pk[i] = code[4 * i] | (code[4 * i + 1] << 8) | (code[4 * i + 2] << 16) | (code[4 * i + 3] << 24);
+  uint2* d2 = reinterpret_cast<uint2*>(dst) + 2 * lane;
+  d2[0] = make_uint2(pk[0], pk[1]);
+  d2[1] = make_uint2(pk[2], pk[3]);
+  if (lane < 16) {
+    const uint2* rs = reinterpret_cast<const uint2*>(src + dots3::D_NOPE) + lane;  // 4 rope values
+    reinterpret_cast<uint2*>(dst + dots3::ROPE_OFF)[lane] = *rs;
+  }
+  // the eight scale bytes, from the first lane of each tile, in one store
+  const uint32_t b = (uint32_t)(e + 127);
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    lo |= (uint32_t)__shfl((int)b, 8 * g) << (8 * g);
+    hi |= (uint32_t)__shfl((int)b, 8 * (g + 4)) << (8 * g);
+  }
+  if (lane == 0) *reinterpret_cast<uint2*>(dst + dots3::SCALE_OFF) = make_uint2(lo, hi);
+}
+
 hipError_t launch_quantize(const QuantParams& p, int fmt, hipStream_t s) {
   dim3 grid((unsigned)((p.n + 3) / 4)), block(256);
   switch (fmt) {
@@ -119,6 +176,7 @@ hipError_t launch_quantize(const QuantParams& p, int fmt, hipStream_t s) {
     case FMT_INT8: hipLaunchKernelGGL(quantize_kernel<FMT_INT8>, grid, block, 0, s, p); break;
     case FMT_FP8_ANY: hipLaunchKernelGGL(quantize_kernel<FMT_FP8_ANY>, grid, block, 0, s, p); break;
     case FMT_FP8_NOPE: hipLaunchKernelGGL(quantize_kernel<FMT_FP8_NOPE>, grid, block, 0, s, p); break;
+    case FMT_FP8_DOTS3: hipLaunchKernelGGL(quantize_dots3_kernel, grid, block, 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

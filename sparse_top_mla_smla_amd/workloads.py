@@ -253,4 +253,24 @@ def c5_int8(seed: int = 0, T: int = 1024) -> Case:
                      pad_fill=PAD_SENTINEL)
 
 
-NAMED = {"c1": c1_tiny, "c2": c2_decode, "c3": c3_prefill, "c4": c4_fewhead, "c5": c5_int8}
+def dots3_prefill(seed: int = 0, T: int = 1024) -> Case:
+    """DOTS3_SWA rows (FlashInfer PR #4802: d_qk 1088, d_v 1024, 1160-byte
+    rows, lists of at least 513 entries so that the sliding window fits):
+    one sequence of 16384 tokens, T queries at its last positions, H=64,
+    513-entry lists of 385 causal uniform positions plus the 128-position
+    window ending at the query, per-head sink.  (The split of the 513
+    entries between selection and window is not given on the page.)"""
+    return make_case("dots3_prefill", config_id=6, seed=seed, fmt=FMT_FP8_DOTS3, T=T, H=64, n_seqs=1,
+                     ctx=16384, topk=513, window=128, causal=True, with_sink=True)
+
+
+def dots3_decode(seed: int = 0, n_seqs: int = 32) -> Case:
+    """DOTS3_SWA decode: 32 sequences x 1 query at position 16383 (the page
+    quotes a T=32 decode for this model), ctx 16384 each, H=64, 513-entry
+    lists as in dots3_prefill, 4 splits."""
+    return make_case("dots3_decode", config_id=7, seed=seed, fmt=FMT_FP8_DOTS3, T=n_seqs, H=64,
+                     n_seqs=n_seqs, ctx=16384, topk=513, window=128, causal=True, num_splits=4)
+
+
+NAMED = {"c1": c1_tiny, "c2": c2_decode, "c3": c3_prefill, "c4": c4_fewhead, "c5": c5_int8,
+         "dots3_prefill": dots3_prefill, "dots3_decode": dots3_decode}

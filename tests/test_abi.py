@@ -52,8 +52,16 @@ def test_row_bytes_and_version():
     assert smla.row_bytes(W.FMT_BF16) == 1152
     assert smla.row_bytes(W.FMT_FP8) == 656
     assert smla.row_bytes(W.FMT_INT8) == 656
+    assert smla.row_bytes(W.FMT_FP8_DOTS3) == 1160
     assert smla.row_bytes(7) == -1
     assert "gfx950" in smla.version()
+
+
+def test_query_and_value_dims():
+    for f in W.FMT_NAMES:
+        assert smla.query_dims(f) == W.Q_DIMS[f]
+        assert smla.value_dims(f) == W.V_DIMS[f]
+    assert smla.query_dims(9) == -1 and smla.value_dims(9) == -1
 
 
 @pytest.mark.parametrize("topk,S,w", [(2048, 8, 256), (64, 2, 64), (1000, 7, 192), (1, 64, 64), (640, 3, 256)])
@@ -69,12 +77,13 @@ def test_split_width_rejects_bad_arguments():
 def test_decode_workspace_size():
     T, H, S = 64, 64, 8
     assert smla.decode_workspace_size(T, H, S) == T * S * H * 512 * 4 + T * S * H * 4
+    assert smla.decode_workspace_size(T, H, S, 1024) == T * S * H * 1024 * 4 + T * S * H * 4
     assert smla.decode_workspace_size(0, 8, 1) == 0
-    for bad in ((-1, 8, 1), (1, 0, 1), (1, 129, 1), (1, 8, 0), (1, 8, 65)):
+    for bad in ((-1, 8, 1), (1, 0, 1), (1, 129, 1), (1, 8, 0), (1, 8, 65), (1, 8, 1, 576)):
         with pytest.raises(smla.SmlaError):
             smla.decode_workspace_size(*bad)
     lib = smla._load()
-    assert lib.smla_decode_workspace_size(1, 8, 1, None) == 1  # SMLA_ERR_NULL
+    assert lib.smla_decode_workspace_size(1, 8, 1, 512, None) == 1  # SMLA_ERR_NULL
 
 
 def pool(fmt=W.FMT_FP8, num_blocks=4, page_block=64, block_stride=None, row_stride=0):
@@ -99,7 +108,7 @@ def test_prefill_validation_before_launch():
     assert prefill(lib, topk=0) == 2
     assert prefill(lib, pl=pool(page_block=32)) == 4                         # page block must be 64
     assert "page_block 32" in lib.smla_last_error().decode()
-    assert prefill(lib, pl=pool(fmt=5)) == 4                                 # unknown format
+    assert prefill(lib, pl=pool(fmt=6)) == 4                                 # unknown format
     assert prefill(lib, pl=pool(block_stride=64 * 656 - 16)) == 3            # block stride below 64 rows
     assert prefill(lib, pl=pool(row_stride=640)) == 3                        # row stride below the row
     assert prefill(lib, pl=pool(row_stride=664)) == 3                        # row stride not a multiple of 16
@@ -123,8 +132,31 @@ def test_decode_and_combine_validation_before_launch():
     assert dec(S=65) == 4
     assert dec(po=None) == 1
     assert dec(T=0, q=None, idx=None, po=None, pls=None) == 0
-    assert lib.smla_combine(None, FAKE, 2, 4, 64, None, FAKE, 64 * 512, 512, FAKE, 64, None) == 1
-    assert lib.smla_combine(FAKE, FAKE, 0, 4, 64, None, None, 0, 0, None, 0, None) == 0
+    assert lib.smla_combine(None, FAKE, 2, 4, 64, 512, None, FAKE, 64 * 512, 512, FAKE, 64, None) == 1
+    assert lib.smla_combine(FAKE, FAKE, 0, 4, 64, 512, None, None, 0, 0, None, 0, None) == 0
+    assert lib.smla_combine(FAKE, FAKE, 2, 4, 64, 768, None, FAKE, 64 * 1024, 1024, FAKE, 64, None) == 2
+    assert lib.smla_combine(FAKE, FAKE, 2, 4, 64, 1024, None, FAKE, 64 * 512, 512, FAKE, 64, None) == 3
+
+
+def test_dots3_validation_before_launch():
+    lib = smla._load()
+    f = ctypes.c_float(1 / 33)
+    F = W.FMT_FP8_DOTS3
+
+    def call(pl=None, q_sh=1088, out_sh=1024, ex=None):
+        return lib.smla_prefill_dual(FAKE, 2, 16, 16 * q_sh, q_sh, pl or pool(fmt=F), FAKE, 576, 576, None,
+                                     ctypes.byref(ex) if ex is not None else None, None, f, FAKE, 16 * out_sh,
+                                     out_sh, FAKE, 16, None)
+
+    assert call(q_sh=576) == 3                                               # q rows hold 1088 values
+    assert call(out_sh=512) == 3                                             # out rows hold 1024 values
+    assert call(pl=pool(fmt=F, row_stride=1164)) == 3                        # rows 8-byte aligned
+    assert call(pl=pool(fmt=F, block_stride=64 * 1160 + 4)) == 3
+    ex = smla._Extra(pool(fmt=F), FAKE, 64, 64, None)
+    assert call(ex=ex) == 4                                                  # no secondary list
+    assert "DOTS3" in lib.smla_last_error().decode()
+    kv = lib.smla_quantize_kv(FAKE, 4, 576, FAKE, pool(fmt=F), None)
+    assert kv == 3                                                           # writer reads 1088 values
 
 
 def test_dual_validation_before_launch():
