@@ -32,9 +32,15 @@
 //
 // Rows are gathered one tile ahead through registers while the current
 // tile is consumed from LDS: four threads per row, each loading every
-// fourth 8-byte piece (a row is only 8-byte aligned in the pool), so one
-// row address per thread and immediate offsets serve all 37 loads.  Masked
-// rows are zero-filled so they can never inject NaN into PV.
+// fourth 16-byte piece (gfx950 serves 16-byte loads from the 8-byte-aligned
+// rows; the 8-byte tail goes to the row's first thread), so one row address
+// per thread and immediate offsets serve all 19 loads.  Masked rows are
+// zero-filled so they can never inject NaN into PV.
+//
+// Block order: the workgroups of one token's head groups (and of one
+// split) read the same rows, so they are placed on the same XCD (the
+// dispatcher deals consecutive workgroups to the 8 XCDs in turn) and meet
+// in its L2.
 #include "device_common.h"
 #include "launch.h"
 #include "lists.h"
@@ -47,18 +53,21 @@ constexpr int NT = 256;       // 4 waves
 constexpr float LAZY = 8.0f;  // log2 units
 constexpr int KS = dots3::D_QK / 32;        // 34 k-steps of QK (32 nope + 2 rope)
 constexpr int LDS_ROW = 1184;               // 1160 rounded up to 16, + 16 (bank spread)
-constexpr int PIECES = dots3::ROW_BYTES / 8;  // 145 8-byte pieces per row
-constexpr int NCH = (PIECES + 3) / 4;         // 37 staged pieces per thread (4 threads per row)
+constexpr int PIECES = dots3::ROW_BYTES / 16;  // 72 whole 16-byte pieces per row (+ an 8-byte tail)
+constexpr int NCH = PIECES / 4;                // 18 staged pieces per thread (4 threads per row)
+constexpr int NXCD = 8;                        // XCDs of the chip
 // LDS: the tile, Q [16 heads][1088] BF16 (rows padded to 2192 B), P' [8
-// groups][16 heads][64 candidates] BF16 (head rows padded to 144 B), wave
-// maxima / sums [4][16], index stage [3][64]
+// groups][16 heads][64 candidates] BF16 (head rows padded to 144 B), the
+// tile's scales as floats [64][8], wave maxima / sums [4][16], index stage
+// [3][64]
 constexpr int TILE_BYTES = TC * LDS_ROW;
 constexpr int Q_ROW = 2 * dots3::D_QK + 16;
 constexpr int Q_OFF = TILE_BYTES;
 constexpr int P_HEAD = 144;
 constexpr int P_GROUP = 16 * P_HEAD;
 constexpr int P_OFF = Q_OFF + 16 * Q_ROW;
-constexpr int RED_OFF = P_OFF + dots3::NGROUPS * P_GROUP;
+constexpr int SC_OFF = P_OFF + dots3::NGROUPS * P_GROUP;
+constexpr int RED_OFF = SC_OFF + TC * dots3::NGROUPS * 4;
 constexpr int IDX_OFF = RED_OFF + 4 * 16 * 4;
 constexpr int LDS_BYTES = IDX_OFF + 3 * TC * 4;
 
@@ -74,6 +83,7 @@ __global__ __launch_bounds__(NT, 1) void attn_dots3_kernel(AttnParams p) {
   uint8_t* tile = smem;
   uint8_t* qbuf = smem + Q_OFF;
   uint8_t* pbuf = smem + P_OFF;
+  float* sct = reinterpret_cast<float*>(smem + SC_OFF);
   float* red = reinterpret_cast<float*>(smem + RED_OFF);
   int32_t* idx_lds = reinterpret_cast<int32_t*>(smem + IDX_OFF);
 
@@ -83,9 +93,16 @@ __global__ __launch_bounds__(NT, 1) void attn_dots3_kernel(AttnParams p) {
   const int lg = lane >> 4;
   const int lc = lane & 15;
 
-  const int64_t t = blockIdx.x;
-  const int h0 = blockIdx.y * 16;
-  const int split = DECODE ? (int)blockIdx.z : 0;
+  // workgroup x -> (token, head group, split): x = ((tq*S + split)*HG + hg)*8 + xcd, t = 8*tq + xcd
+  const int HG = (p.H + 15) >> 4;
+  const int S = DECODE ? p.num_splits : 1;
+  const int64_t bx = blockIdx.x;
+  const int64_t rest = bx / NXCD;
+  const int hg = (int)(rest % HG);
+  const int split = DECODE ? (int)((rest / HG) % S) : 0;
+  const int64_t t = (rest / HG / S) * NXCD + bx % NXCD;
+  if (t >= p.T) return;  // the last round of tokens may be short (whole workgroup)
+  const int h0 = hg * 16;
 
   const ListEnds le = list_ends(p, t);
   const Sources src_lists = sources<false>(p);
@@ -121,26 +138,40 @@ __global__ __launch_bounds__(NT, 1) void attn_dots3_kernel(AttnParams p) {
     return v;
   };
 
-  // thread tid gathers pieces sub + 4r (r < NCH) of tile row tid / 4
+  // thread tid gathers 16-byte pieces sub + 4r (r < NCH) of tile row
+  // tid / 4, and the row's 8-byte tail when sub == 0
   const int grow = tid >> 2, sub = tid & 3;
-  uint2 stage[NCH];
+  uint4 stage[NCH];
+  uint2 tail;
   auto issue_rows = [&](int k) {
     const int32_t e = idx_lds[(k % 3) * TC + grow];
     if (e >= 0) {
-      const uint2* src = reinterpret_cast<const uint2*>(
-          p.pool + (int64_t)(e / PAGE) * p.block_stride + (int64_t)(e % PAGE) * p.row_stride) + sub;
+      const uint8_t* row = p.pool + (int64_t)(e / PAGE) * p.block_stride + (int64_t)(e % PAGE) * p.row_stride;
 #pragma unroll
-      for (int r = 0; r < NCH; ++r) stage[r] = (r < NCH - 1 || sub == 0) ? src[4 * r] : make_uint2(0, 0);
+      for (int r = 0; r < NCH; ++r) __builtin_memcpy(&stage[r], row + 16 * (sub + 4 * r), 16);
+      tail = make_uint2(0, 0);
+      if (sub == 0) __builtin_memcpy(&tail, row + 16 * PIECES, 8);
     } else {
 #pragma unroll
-      for (int r = 0; r < NCH; ++r) stage[r] = make_uint2(0, 0);
+      for (int r = 0; r < NCH; ++r) stage[r] = make_uint4(0, 0, 0, 0);
+      tail = make_uint2(0, 0);
     }
   };
   auto store_rows = [&]() {
-    uint2* dst = reinterpret_cast<uint2*>(tile + grow * LDS_ROW) + sub;
+    uint8_t* dst = tile + grow * LDS_ROW;
 #pragma unroll
-    for (int r = 0; r < NCH; ++r)
-      if (r < NCH - 1 || sub == 0) dst[4 * r] = stage[r];
+    for (int r = 0; r < NCH; ++r) *reinterpret_cast<uint4*>(dst + 16 * (sub + 4 * r)) = stage[r];
+    if (sub == 0) {  // the tail is the row's eight scale bytes: decode them once for the tile
+      *reinterpret_cast<uint2*>(dst + 16 * PIECES) = tail;
+      f32x4 lo, hi;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        lo[g] = e8m0_to_f32((tail.x >> (8 * g)) & 0xFFu);
+        hi[g] = e8m0_to_f32((tail.y >> (8 * g)) & 0xFFu);
+      }
+      reinterpret_cast<f32x4*>(sct + grow * dots3::NGROUPS)[0] = lo;
+      reinterpret_cast<f32x4*>(sct + grow * dots3::NGROUPS)[1] = hi;
+    }
   };
 
   // running max (log2 units) of head lc, shared by the four waves; this
@@ -194,20 +225,17 @@ __global__ __launch_bounds__(NT, 1) void attn_dots3_kernel(AttnParams p) {
 
     // scores of candidates c = 16*wave + 4lg + i for head lc
     const int32_t* il = idx_lds + (k % 3) * TC + 16 * wave + 4 * lg;
-    // scale bytes of candidates (4lg+i): group g in byte g of sb[i]
-    auto scale_bytes = [&](int i) -> uint2 {
-      return *reinterpret_cast<const uint2*>(tile + (16 * wave + 4 * lg + i) * LDS_ROW + dots3::SCALE_OFF);
-    };
-    auto scale_of = [](uint2 sb, int g) -> float {
-      return e8m0_to_f32(((g < 4 ? sb.x : sb.y) >> (8 * (g & 3))) & 0xFFu);
+    // scales of candidate (4lg+i), groups 0..3 and 4..7
+    auto scales = [&](int i, int half) -> f32x4 {
+      return reinterpret_cast<const f32x4*>(sct + (16 * wave + 4 * lg + i) * dots3::NGROUPS)[half];
     };
     float s[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint2 sb = scale_bytes(i);
+      const f32x4 lo = scales(i, 0), hi = scales(i, 1);
       float v = acc[dots3::NGROUPS][i];
 #pragma unroll
-      for (int g = 0; g < dots3::NGROUPS; ++g) v += scale_of(sb, g) * acc[g][i];
+      for (int g = 0; g < 4; ++g) v += lo[g] * acc[g][i] + hi[g] * acc[g + 4][i];
       s[i] = il[i] >= 0 ? v * p.scale_log2 : -INFINITY;
     }
 
@@ -235,11 +263,12 @@ __global__ __launch_bounds__(NT, 1) void attn_dots3_kernel(AttnParams p) {
       l_part += pr[i];
     }
     // P'_g[h][c] = P[c][h] * scale(c, g), candidates 16*wave + 4lg + (0..3)
-    const uint2 sb0 = scale_bytes(0), sb1 = scale_bytes(1), sb2 = scale_bytes(2), sb3 = scale_bytes(3);
 #pragma unroll
     for (int g = 0; g < dots3::NGROUPS; ++g) {
-      const uint32_t u0 = pack_bf16(pr[0] * scale_of(sb0, g), pr[1] * scale_of(sb1, g));
-      const uint32_t u1 = pack_bf16(pr[2] * scale_of(sb2, g), pr[3] * scale_of(sb3, g));
+      const float s0 = scales(0, g >> 2)[g & 3], s1 = scales(1, g >> 2)[g & 3];
+      const float s2 = scales(2, g >> 2)[g & 3], s3 = scales(3, g >> 2)[g & 3];
+      const uint32_t u0 = pack_bf16(pr[0] * s0, pr[1] * s1);
+      const uint32_t u1 = pack_bf16(pr[2] * s2, pr[3] * s3);
       *reinterpret_cast<uint2*>(pbuf + g * P_GROUP + lc * P_HEAD + 2 * (16 * wave + 4 * lg)) = make_uint2(u0, u1);
     }
     __syncthreads();
@@ -313,8 +342,11 @@ __global__ __launch_bounds__(NT, 1) void attn_dots3_kernel(AttnParams p) {
 }  // namespace
 
 hipError_t launch_attention_dots3(const AttnParams& p, bool decode, hipStream_t s) {
+  const int64_t rounds = (p.T + NXCD - 1) / NXCD;
+  const int64_t blocks = rounds * NXCD * ((p.H + 15) / 16) * (decode ? p.num_splits : 1);
+  if (blocks > (int64_t)UINT32_MAX) return hipErrorInvalidConfiguration;
   dim3 block(NT);
-  dim3 grid((unsigned)p.T, (unsigned)((p.H + 15) / 16), decode ? (unsigned)p.num_splits : 1u);
+  dim3 grid((unsigned)blocks);
   if (decode) hipLaunchKernelGGL((attn_dots3_kernel<true>), grid, block, 0, s, p);
   else hipLaunchKernelGGL((attn_dots3_kernel<false>), grid, block, 0, s, p);
   return hipGetLastError();
