@@ -24,7 +24,7 @@ _SRC = os.path.join(_HERE, "smla_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-FMT_BF16, FMT_FP8, FMT_INT8, FMT_FP8_ANY, FMT_FP8_NOPE, FMT_FP8_DOTS3 = 0, 1, 2, 3, 4, 5
+FMT_BF16, FMT_FP8, FMT_INT8, FMT_FP8_ANY, FMT_FP8_NOPE, FMT_FP8_DOTS3, FMT_FP8_DSV4 = 0, 1, 2, 3, 4, 5, 6
 PAGE_BLOCK = 64
 
 
@@ -105,7 +105,7 @@ def d_k(fmt: int) -> int:
 
 
 def d_v(fmt: int) -> int:
-    """Elements of a V row (the nope part): 1024 for DOTS3_SWA rows, else 512."""
+    """Elements of a V row (K's first d_v values): 1024 for DOTS3_SWA rows, else 512."""
     return int(lib().oracle_d_v(fmt))
 
 

@@ -47,6 +47,14 @@
  * writer takes the same power-of-two scale as the FP8 rows, raised to at
  * least 2^-126 so that the byte is never 0.
  *
+ * DSv4 rows (FlashInfer PR #4802 gives only their size, 584 bytes, and that
+ * the V3.2-family models share d_v = 512): read as 448 nope values and 64
+ * rope values (d_qk = 512, K's first 512 values -- all of them -- are V, the
+ * rule every row follows), [0,448) e4m3 codes, [448,576) the rope values in
+ * BF16, [576,583) one exponent byte per 64-element tile of the nope part
+ * (448 = 7 x 64; 128-element tiles would not divide it), [583] padding that
+ * the writer sets to 0 and no reader uses.  Scale bytes as for DOTS3_SWA.
+ *
  * Precision: all attention arithmetic is float64.  The quantizer runs in
  * float32, because float32 arithmetic decides its integer codes and the
  * stored scales are float32.
@@ -68,13 +76,17 @@
 #define PAGE_BLOCK 64
 #define TILE 128 /* quantization tile width along the nope part */
 
-enum { FMT_BF16 = 0, FMT_FP8 = 1, FMT_INT8 = 2, FMT_FP8_ANY = 3, FMT_FP8_NOPE = 4, FMT_FP8_DOTS3 = 5 };
+enum { FMT_BF16 = 0, FMT_FP8 = 1, FMT_INT8 = 2, FMT_FP8_ANY = 3, FMT_FP8_NOPE = 4, FMT_FP8_DOTS3 = 5,
+       FMT_FP8_DSV4 = 6 };
+
+#define DSV4_NOPE 448
+#define DSV4_TILE 64 /* its quantization tile */
 
 /* nope values of a row; K holds these plus D_ROPE rope values (zero for
- * rows without rope dimensions), V is the nope part */
-static int d_nope(int32_t fmt) { return fmt == FMT_FP8_DOTS3 ? D_NOPE_MAX : D_NOPE; }
+ * rows without rope dimensions); V is K's first d_v values */
+static int d_nope(int32_t fmt) { return fmt == FMT_FP8_DOTS3 ? D_NOPE_MAX : fmt == FMT_FP8_DSV4 ? DSV4_NOPE : D_NOPE; }
 static int d_k(int32_t fmt) { return d_nope(fmt) + D_ROPE; }
-static int d_v(int32_t fmt) { return d_nope(fmt); }
+static int d_v(int32_t fmt) { return fmt == FMT_FP8_DSV4 ? d_k(fmt) : d_nope(fmt); }
 /* elements of a query row that enter a score */
 static int q_dims(int32_t fmt) { return fmt == FMT_FP8_NOPE ? D_NOPE : d_k(fmt); }
 
@@ -193,6 +205,7 @@ double oracle_e8m0_decode(uint8_t b) { return b == 255 ? NAN : ldexp(1.0, (int)b
 int32_t oracle_row_bytes(int32_t fmt) {
   if (fmt == FMT_BF16) return 2 * D_QK;
   if (fmt == FMT_FP8_DOTS3) return D_NOPE_MAX + 2 * D_ROPE + D_NOPE_MAX / TILE;
+  if (fmt == FMT_FP8_DSV4) return DSV4_NOPE + 2 * D_ROPE + DSV4_NOPE / DSV4_TILE + 1;
   return D_NOPE + 4 * (D_NOPE / TILE) + 2 * D_ROPE;
 }
 
@@ -219,6 +232,23 @@ static void quantize_row(const uint16_t* x, int32_t fmt, uint8_t* row) {
       row[D_NOPE_MAX + 2 * D_ROPE + g] = b;
     }
     memcpy(row + D_NOPE_MAX, x + D_NOPE_MAX, 2 * D_ROPE);
+    return;
+  }
+  if (fmt == FMT_FP8_DSV4) {
+    for (int g = 0; g < DSV4_NOPE / DSV4_TILE; ++g) {
+      float amax = 0.0f;
+      for (int i = g * DSV4_TILE; i < (g + 1) * DSV4_TILE; ++i) {
+        float v = fabsf(bf16_bits_to_float(x[i]));
+        if (v > amax) amax = v;
+      }
+      uint8_t b = oracle_e8m0_scale(amax);
+      float scale = ldexpf(1.0f, (int)b - 127);
+      for (int i = g * DSV4_TILE; i < (g + 1) * DSV4_TILE; ++i)
+        row[i] = oracle_e4m3_encode(bf16_bits_to_float(x[i]) / scale);
+      row[DSV4_NOPE + 2 * D_ROPE + g] = b;
+    }
+    row[DSV4_NOPE + 2 * D_ROPE + DSV4_NOPE / DSV4_TILE] = 0; /* padding */
+    memcpy(row + DSV4_NOPE, x + DSV4_NOPE, 2 * D_ROPE);
     return;
   }
   for (int g = 0; g < D_NOPE / TILE; ++g) {
@@ -274,6 +304,16 @@ static void dequant_row(const uint8_t* pool, int64_t block_stride_bytes, int32_t
       uint16_t b;
       memcpy(&b, row + D_NOPE_MAX + 2 * r, 2);
       K[D_NOPE_MAX + r] = bf16_bits_to_float(b);
+    }
+    return;
+  }
+  if (fmt == FMT_FP8_DSV4) {
+    for (int i = 0; i < DSV4_NOPE; ++i)
+      K[i] = oracle_e4m3_decode(row[i]) * oracle_e8m0_decode(row[DSV4_NOPE + 2 * D_ROPE + i / DSV4_TILE]);
+    for (int r = 0; r < D_ROPE; ++r) {
+      uint16_t b;
+      memcpy(&b, row + DSV4_NOPE + 2 * r, 2);
+      K[DSV4_NOPE + r] = bf16_bits_to_float(b);
     }
     return;
   }

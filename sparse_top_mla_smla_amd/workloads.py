@@ -26,19 +26,20 @@ import numpy as np
 
 PAGE_BLOCK = 64
 D_QK, D_V = 576, 512
-FMT_BF16, FMT_FP8, FMT_INT8, FMT_FP8_ANY, FMT_FP8_NOPE, FMT_FP8_DOTS3 = 0, 1, 2, 3, 4, 5
+FMT_BF16, FMT_FP8, FMT_INT8, FMT_FP8_ANY, FMT_FP8_NOPE, FMT_FP8_DOTS3, FMT_FP8_DSV4 = 0, 1, 2, 3, 4, 5, 6
 FMT_NAMES = {FMT_BF16: "bf16", FMT_FP8: "fp8_e4m3", FMT_INT8: "int8", FMT_FP8_ANY: "fp8_e4m3_any_scale",
-             FMT_FP8_NOPE: "fp8_e4m3_nope", FMT_FP8_DOTS3: "fp8_e4m3_dots3"}
+             FMT_FP8_NOPE: "fp8_e4m3_nope", FMT_FP8_DOTS3: "fp8_e4m3_dots3", FMT_FP8_DSV4: "fp8_e4m3_dsv4"}
 ROW_BYTES = {FMT_BF16: 1152, FMT_FP8: 656, FMT_INT8: 656, FMT_FP8_ANY: 656, FMT_FP8_NOPE: 656,
-             FMT_FP8_DOTS3: 1160}
+             FMT_FP8_DOTS3: 1160, FMT_FP8_DSV4: 584}
 # elements of a query row that enter a score (NOPE rows have no rope dimensions)
 Q_DIMS = {FMT_BF16: 576, FMT_FP8: 576, FMT_INT8: 576, FMT_FP8_ANY: 576, FMT_FP8_NOPE: 512,
-          FMT_FP8_DOTS3: 1088}
+          FMT_FP8_DOTS3: 1088, FMT_FP8_DSV4: 512}
 # elements of a latent row (and of the q buffer's rows) and of an output row
-KV_DIMS = {f: (1088 if f == FMT_FP8_DOTS3 else D_QK) for f in FMT_NAMES}
+KV_DIMS = {f: {FMT_FP8_DOTS3: 1088, FMT_FP8_DSV4: 512}.get(f, D_QK) for f in FMT_NAMES}
 V_DIMS = {f: (1024 if f == FMT_FP8_DOTS3 else D_V) for f in FMT_NAMES}
 SM_SCALE = np.float32(1.0 / 24.0)  # 1/sqrt(576)
 SM_SCALE_DOTS3 = np.float32(1.0 / np.sqrt(1088.0))
+SM_SCALE_DSV4 = np.float32(1.0 / np.sqrt(512.0))
 PAD_SENTINEL = 0x7FFFFFFF
 
 TID_Q, TID_KV, TID_IDX, TID_BT, TID_LEN, TID_SINK = 1, 2, 3, 4, 5, 6
@@ -204,7 +205,7 @@ def make_case(name: str, *, config_id: int, seed: int = 0, fmt: int, T: int, H: 
     return Case(name=name, fmt=fmt, T=T, H=H, n_seqs=n_seqs, ctx=ctx, topk=topk, q_buf=q_buf,
                 kv=kv, slots=slots, num_blocks=num_blocks, block_table=bt, idx_buf=idx_buf,
                 topk_length=topk_length, sink=sink,
-                sm_scale=SM_SCALE_DOTS3 if fmt == FMT_FP8_DOTS3 else SM_SCALE, positions=positions,
+                sm_scale={FMT_FP8_DOTS3: SM_SCALE_DOTS3, FMT_FP8_DSV4: SM_SCALE_DSV4}.get(fmt, SM_SCALE), positions=positions,
                 seq_of_token=seq_of_token, num_splits=num_splits, out_hbuf=out_hbuf)
 
 

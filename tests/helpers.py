@@ -32,6 +32,13 @@ def np_dequant(pool: oracle.Pool, slots) -> np.ndarray:
         scales = np.where(e == 255, np.nan, np.ldexp(1.0, e - 127))
         rope = W.bf16_bits_to_f32(rows[:, 1024:1152].copy().view(np.uint16)).astype(np.float64)
         return np.concatenate([codes * np.repeat(scales, 128, axis=1), rope], axis=1)
+    if pool.fmt == W.FMT_FP8_DSV4:
+        # [0,448) e4m3 codes, [448,576) BF16 rope, [576,583) exponent bytes per 64 (bias 127), [583] pad
+        codes = torch.tensor(rows[:, :448].copy()).view(torch.float8_e4m3fn).double().numpy()
+        e = rows[:, 576:583].astype(np.int64)
+        scales = np.where(e == 255, np.nan, np.ldexp(1.0, e - 127))
+        rope = W.bf16_bits_to_f32(rows[:, 448:576].copy().view(np.uint16)).astype(np.float64)
+        return np.concatenate([codes * np.repeat(scales, 64, axis=1), rope], axis=1)
     scales = rows[:, 512:528].copy().view(np.float32).astype(np.float64)
     if pool.fmt in (W.FMT_FP8, W.FMT_FP8_ANY, W.FMT_FP8_NOPE):
         codes = torch.tensor(rows[:, :512].copy()).view(torch.float8_e4m3fn).double().numpy()

@@ -16,7 +16,7 @@ from sparse_top_mla_smla_amd import workloads as W
 
 from helpers import dense_attention, np_dequant, oracle_pool, q_f64
 
-FMTS = [W.FMT_BF16, W.FMT_FP8, W.FMT_INT8, W.FMT_FP8_ANY, W.FMT_FP8_NOPE, W.FMT_FP8_DOTS3]
+FMTS = [W.FMT_BF16, W.FMT_FP8, W.FMT_INT8, W.FMT_FP8_ANY, W.FMT_FP8_NOPE, W.FMT_FP8_DOTS3, W.FMT_FP8_DSV4]
 
 
 def full_ctx_case(fmt, seed=0, ctx=192, T=3, H=4, with_sink=False):
