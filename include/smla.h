@@ -87,14 +87,23 @@ typedef enum {
  * 1088 values per latent row.  Its writer takes the power-of-two scale of
  * the FP8 rows, raised to at least 2^-126, so it stores b in [1, 254].
  * Lists of any width run on it (the page's lists hold at least 513
- * entries); the dual-list entry points do not accept it. */
+ * entries); the dual-list entry points do not accept it.
+ * FP8_E4M3_DSV4 is the DSv4 row, which the same PR gives only as 584 bytes
+ * (and d_v = 512 for the V3.2 family); read as [0,448) e4m3 codes of 448
+ * nope values, [448,576) 64 BF16 rope values, [576,583) one scale byte per
+ * 64-element tile (2^(b-127), as above; 448 = 7 x 64), [583] a pad byte the
+ * writer sets to 0 and no reader uses.  K and V are the same 512 values
+ * (448 nope + 64 rope): q rows hold 512 values, out rows 512, and the
+ * writer reads 512 values per latent row.  Scales as for FP8_E4M3_DOTS3;
+ * the dual-list entry points do not accept it. */
 typedef enum {
   SMLA_KV_BF16 = 0,
   SMLA_KV_FP8_E4M3 = 1,
   SMLA_KV_INT8 = 2,
   SMLA_KV_FP8_E4M3_ANY_SCALE = 3,
   SMLA_KV_FP8_E4M3_NOPE = 4,
-  SMLA_KV_FP8_E4M3_DOTS3 = 5
+  SMLA_KV_FP8_E4M3_DOTS3 = 5,
+  SMLA_KV_FP8_E4M3_DSV4 = 6
 } smla_kv_format;
 
 /* A paged latent pool.  Slot s (a flat pool position) lives in block s/64 at
@@ -105,7 +114,8 @@ typedef enum {
  * by a token-axis stride that may exceed bytes_per_token); with one latent
  * head per row the NHD and HND block layouts differ only in these two
  * strides.  base must be 16-byte aligned; R a multiple of 16 (of 8 for
- * FP8_E4M3_DOTS3, whose 1160-byte rows pack 8-byte aligned) and at least
+ * FP8_E4M3_DOTS3 and FP8_E4M3_DSV4, whose 1160- and 584-byte rows pack
+ * 8-byte aligned) and at least
  * the row bytes; block_stride_bytes a multiple of the same and at least 64*R;
  * page_block must be 64 (PR #4802: the kernels are compiled for page block
  * 64 and launchers reject anything else).  Bytes outside the rows are never
@@ -120,12 +130,13 @@ typedef struct {
 } smla_kv_pool;
 
 /* Bytes of one cache row: 1152 (BF16), 656 (FP8, INT8 and the other
- * 656-byte rows), 1160 (FP8_E4M3_DOTS3); -1 for an unknown format. */
+ * 656-byte rows), 1160 (FP8_E4M3_DOTS3), 584 (FP8_E4M3_DSV4); -1 for an
+ * unknown format. */
 int32_t smla_row_bytes(int32_t format);
 
 /* Values per q row that enter a score, which is also the values per latent
- * row that smla_quantize_kv reads: 576, 512 (FP8_E4M3_NOPE) or 1088
- * (FP8_E4M3_DOTS3); -1 for an unknown format. */
+ * row that smla_quantize_kv reads: 576, 512 (FP8_E4M3_NOPE and
+ * FP8_E4M3_DSV4) or 1088 (FP8_E4M3_DOTS3); -1 for an unknown format. */
 int32_t smla_query_dims(int32_t format);
 
 /* Values per output row (d_v): 1024 for FP8_E4M3_DOTS3, else 512; -1 for an
@@ -159,9 +170,9 @@ smla_status smla_decode_workspace_size(int64_t T, int32_t H, int32_t num_splits,
  * "power-of-2 FP32 scales"); codes = e4m3(x / scale), round to nearest even,
  * sign kept.  FP8_E4M3_ANY_SCALE: scale = amax/448 (FP32, correctly rounded;
  * 1 when amax = 0), codes as for FP8.  INT8: scale = amax/127 (1 when amax = 0), codes =
- * clamp(rne(x/scale), -127, 127).  FP8_E4M3_DOTS3: the FP8 rule over its
- * eight tiles with the scale 2^e raised to at least 2^-126, e + 127 stored
- * as the tile's scale byte.  BF16: a copy.  Rope values are copied bit for
+ * clamp(rne(x/scale), -127, 127).  FP8_E4M3_DOTS3 and FP8_E4M3_DSV4: the
+ * FP8 rule over their 128- or 64-element tiles with the scale 2^e raised
+ * to at least 2^-126, e + 127 stored as the tile's scale byte.  BF16: a copy.  Rope values are copied bit for
  * bit.  Two slots that are equal race (last writer wins). */
 smla_status smla_quantize_kv(const void* kv, int64_t n, int64_t kv_stride, const int32_t* slots,
                              smla_kv_pool pool, void* stream);
@@ -259,8 +270,8 @@ smla_status smla_combine(const float* part_out, const float* part_lse, int64_t T
  * per kernel (format, H > 16) by calibrate_splits.py in the package.
  * compute_units <= 0 means the current device's.  Returns -1 when T < 1,
  * H outside [1, 128], topk < 1, num_splits is outside [0, 64], or the
- * format is unknown or has no fitted constants (FP8_E4M3_DOTS3: there
- * smla_attention runs the prefill form). */
+ * format is unknown or has no fitted constants (FP8_E4M3_DOTS3 and
+ * FP8_E4M3_DSV4: there smla_attention runs the prefill form). */
 double smla_split_model_cost(int64_t T, int32_t H, int32_t topk, int32_t format, int32_t num_splits,
                              int32_t compute_units);
 

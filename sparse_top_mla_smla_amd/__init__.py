@@ -16,9 +16,9 @@ import torch
 
 __all__ = ["KVPool", "quantize_kv", "prefill", "decode", "combine", "split_width", "row_bytes",
            "query_dims", "value_dims", "library_path", "SmlaError", "FMT_BF16", "FMT_FP8", "FMT_INT8",
-           "FMT_FP8_ANY", "FMT_FP8_NOPE", "FMT_FP8_DOTS3"]
+           "FMT_FP8_ANY", "FMT_FP8_NOPE", "FMT_FP8_DOTS3", "FMT_FP8_DSV4"]
 
-FMT_BF16, FMT_FP8, FMT_INT8, FMT_FP8_ANY, FMT_FP8_NOPE, FMT_FP8_DOTS3 = 0, 1, 2, 3, 4, 5
+FMT_BF16, FMT_FP8, FMT_INT8, FMT_FP8_ANY, FMT_FP8_NOPE, FMT_FP8_DOTS3, FMT_FP8_DSV4 = 0, 1, 2, 3, 4, 5, 6
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libsmla.so")
 _lib = None

@@ -30,8 +30,9 @@ smla_status ok() {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// DOTS3_SWA rows are 1160 bytes: rows and blocks need only 8-byte alignment
-int64_t row_align(int32_t format) { return format == SMLA_KV_FP8_E4M3_DOTS3 ? 8 : 16; }
+// rows with exponent-byte scales are 1160 or 584 bytes: rows and blocks need only 8-byte alignment
+bool mx_format(int32_t format) { return format == SMLA_KV_FP8_E4M3_DOTS3 || format == SMLA_KV_FP8_E4M3_DSV4; }
+int64_t row_align(int32_t format) { return mx_format(format) ? 8 : 16; }
 
 smla_status check_pool(const smla_kv_pool& kv) {
   if (!kv.base) return fail(SMLA_ERR_NULL, "kv pool base is NULL");
@@ -41,7 +42,7 @@ smla_status check_pool(const smla_kv_pool& kv) {
   if (rb < 0)
     return fail(SMLA_ERR_UNSUPPORTED,
                 "kv format %d is not supported (supported: 0 = BF16, 1 = FP8_E4M3, 2 = INT8, 3 = FP8_E4M3_ANY_SCALE, "
-                "4 = FP8_E4M3_NOPE, 5 = FP8_E4M3_DOTS3)",
+                "4 = FP8_E4M3_NOPE, 5 = FP8_E4M3_DOTS3, 6 = FP8_E4M3_DSV4)",
                 kv.format);
   if (kv.num_blocks < 1) return fail(SMLA_ERR_SHAPE, "num_blocks %lld must be >= 1", (long long)kv.num_blocks);
   if (kv.num_blocks > (int64_t)(INT32_MAX / 64) + 1)
@@ -103,8 +104,8 @@ smla_status check_out(const void* out, int64_t out_st, int64_t out_sh, int32_t H
 // the secondary list of a dual-cache call (extra != NULL)
 smla_status check_extra(const smla_kv_pool& kv, int32_t topk, const smla_kv_extra* extra) {
   if (!extra) return SMLA_OK;
-  if (kv.format == SMLA_KV_FP8_E4M3_DOTS3)
-    return fail(SMLA_ERR_UNSUPPORTED, "a secondary list is not supported for FP8_E4M3_DOTS3 pools");
+  if (mx_format(kv.format))
+    return fail(SMLA_ERR_UNSUPPORTED, "a secondary list is not supported for FP8_E4M3_DOTS3 / FP8_E4M3_DSV4 pools");
   if (topk % 64 != 0)
     return fail(SMLA_ERR_UNSUPPORTED, "topk = %d: with a secondary list the main list width must be a multiple of 64",
                 topk);
@@ -140,6 +141,7 @@ int32_t smla_row_bytes(int32_t format) {
     case SMLA_KV_FP8_E4M3_ANY_SCALE: return 656;
     case SMLA_KV_FP8_E4M3_NOPE: return 656;
     case SMLA_KV_FP8_E4M3_DOTS3: return 1160;
+    case SMLA_KV_FP8_E4M3_DSV4: return 584;
     default: return -1;
   }
 }
@@ -150,7 +152,8 @@ int32_t smla_query_dims(int32_t format) {
     case SMLA_KV_FP8_E4M3:
     case SMLA_KV_INT8:
     case SMLA_KV_FP8_E4M3_ANY_SCALE: return 576;
-    case SMLA_KV_FP8_E4M3_NOPE: return 512;
+    case SMLA_KV_FP8_E4M3_NOPE:
+    case SMLA_KV_FP8_E4M3_DSV4: return 512;
     case SMLA_KV_FP8_E4M3_DOTS3: return 1088;
     default: return -1;
   }
@@ -158,7 +161,7 @@ int32_t smla_query_dims(int32_t format) {
 
 int32_t smla_value_dims(int32_t format) {
   if (smla_row_bytes(format) < 0) return -1;
-  return format == SMLA_KV_FP8_E4M3_DOTS3 ? 1024 : 512;
+  return format == SMLA_KV_FP8_E4M3_DOTS3 ? 1024 : 512;  // (DSv4: V is the whole 512-value row)
 }
 
 int32_t smla_split_width(int32_t topk, int32_t num_splits) {

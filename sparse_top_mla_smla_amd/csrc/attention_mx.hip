@@ -1,0 +1,406 @@
+// attention_mx.hip -- sparse MLA attention over cache rows whose nope part
+// carries one power-of-two exponent byte per tile (prefill form and
+// split-KV decode partials) for gfx950.  Two row families, from FlashInfer
+// PR #4802:
+//  * DOTS3_SWA (description: d_qk = 1088, d_v = 1024, 1160 bytes per token
+//    with the scales in a footer): 1024 e4m3 codes, 64 BF16 rope values,
+//    eight exponent bytes (128-element tiles); V is the 1024 nope values.
+//    Its lists hold at least 513 entries (a 512-entry selection plus the
+//    sliding window), so tails are ragged.
+//  * DSv4 (584 bytes; d_v = 512 for the V3.2 family): 448 e4m3 codes, 64
+//    BF16 rope values, seven exponent bytes (64-element tiles) and a pad
+//    byte; K and V are the whole 512-value row, so V's last 64 columns are
+//    the BF16 rope values.
+// What is computed is stated in include/smla.h.
+//
+// Work unit: one workgroup (4 waves) per (token, 16-head group, split);
+// tiles of 64 list entries.  The value width (up to 1024 f32 per head) is
+// too wide for one wave to hold the output of all its candidates, so the
+// two products split the work differently:
+//  * QK: wave w owns candidates [16w, 16w+16) of the tile and forms S^T
+//    (v_mfma 16x16x32, K rows as A, Q^T from LDS, where the token's 16 q
+//    rows stay for the whole list: in registers they would take up to 136
+//    of them, more than the gather stage and O leave free).  Codes convert
+//    to BF16 with scale 1 (exact); each scale tile accumulates apart and is
+//    scaled afterwards, and the rope columns (BF16 in the row) add on top.
+//  * The four waves agree on one running max per head through LDS (lazy:
+//    it moves only when exceeded by 2^8, so O is rarely rescaled); each
+//    wave writes its candidates' probabilities times each tile's scale,
+//    P'_g = P * scale(c, g) (and P itself for BF16 value columns), in BF16
+//    to LDS.
+//  * PV: wave w owns value columns [w*DV/4, (w+1)*DV/4) for all 64
+//    candidates: O^T[d][h] += V^T[d][c] P'^T[c][h] (v_mfma 16x16x32); V^T
+//    comes from the raw codes with ds_read_b64_tr_b8 (converted with scale
+//    1) or, for BF16 columns, with ds_read_b64_tr_b16.
+// Because every wave holds a disjoint slice of the value columns under the
+// same running max, the end of the list needs only the per-head sums from
+// the other waves, not a merge of outputs.
+//
+// Rows are gathered one tile ahead through registers while the current
+// tile is consumed from LDS: four threads per row, each loading every
+// fourth 16-byte piece (gfx950 serves 16-byte loads from these 8-byte-
+// aligned rows); the 8-byte tail, which holds the exponent bytes, goes to
+// the row's first thread, which also decodes it once into a float table
+// for the tile.  One row address per thread and immediate offsets serve
+// all the loads.  Masked rows are zero-filled so they can never inject NaN
+// into PV.
+//
+// Block order: the workgroups of one token's head groups (and of one
+// split) read the same rows, so they are placed on the same XCD (the
+// dispatcher deals consecutive workgroups to the 8 XCDs in turn) and meet
+// in its L2.
+#include "device_common.h"
+#include "launch.h"
+#include "lists.h"
+
+namespace smla {
+namespace {
+
+struct Dots3Row {
+  static constexpr int NOPE = 1024, QK = 1088, DV = 1024, ROW = 1160;
+  static constexpr int ROPE_OFF = 1024, SCALE_OFF = 1152, TILE = 128, NG = 8;
+  static constexpr int OCC = 1;  // workgroups per CU the kernel is built for
+};
+struct Dsv4Row {
+  static constexpr int NOPE = 448, QK = 512, DV = 512, ROW = 584;
+  static constexpr int ROPE_OFF = 448, SCALE_OFF = 576, TILE = 64, NG = 7;
+  static constexpr int OCC = 2;
+};
+
+constexpr int TC = 64;        // candidates per tile
+constexpr int NT = 256;       // 4 waves
+constexpr float LAZY = 8.0f;  // log2 units
+constexpr int NXCD = 8;       // XCDs of the chip
+constexpr int P_HEAD = 144;   // bytes of one head's P' row (64 BF16, padded)
+constexpr int P_SLOT = 16 * P_HEAD;
+
+template <class R>
+struct Geo {
+  static constexpr int KS_NOPE = R::NOPE / 32;          // QK k-steps over the nope part
+  static constexpr int KS = R::QK / 32;                 // all QK k-steps (+2 rope)
+  static constexpr int KS_PER_TILE = R::TILE / 32;      // k-steps per scale tile
+  static constexpr bool ROPE_V = R::DV > R::NOPE;       // BF16 value columns (the rope part)
+  static constexpr int SLOTS = R::NG + (ROPE_V ? 1 : 0);  // P' slots: one per scale tile (+ scale 1)
+  static constexpr int WCOLS = R::DV / 4;               // value columns per wave
+  static constexpr int NDT = WCOLS / 16;                // 16-column blocks per wave
+  static constexpr int LDS_ROW = (R::ROW + 15) / 16 * 16 + 16;  // row stride in LDS (bank spread)
+  static constexpr int PIECES = R::ROW / 16;            // whole 16-byte pieces per row (+ 8-byte tail)
+  static constexpr int NCH = PIECES / 4;                // staged pieces per thread (4 threads per row)
+  static constexpr int Q_ROW = 2 * R::QK + 16;
+  // LDS: tile, Q [16][QK] BF16, P' [SLOTS][16 heads][64] BF16, scales [64][8] f32,
+  // wave maxima / sums [4][16], index stage [3][64]
+  static constexpr int TILE_BYTES = TC * LDS_ROW;
+  static constexpr int Q_OFF = TILE_BYTES;
+  static constexpr int P_OFF = Q_OFF + 16 * Q_ROW;
+  static constexpr int SC_OFF = P_OFF + SLOTS * P_SLOT;
+  static constexpr int RED_OFF = SC_OFF + TC * 8 * 4;
+  static constexpr int IDX_OFF = RED_OFF + 4 * 16 * 4;
+  static constexpr int LDS_BYTES = IDX_OFF + 3 * TC * 4;
+  static_assert(R::ROW - 16 * PIECES == 8 && R::SCALE_OFF == 16 * PIECES, "the tail holds the scale bytes");
+  static_assert(PIECES % 4 == 0 && R::NOPE % R::TILE == 0 && R::TILE % 32 == 0 && R::NG <= 8, "row geometry");
+  // a wave's value columns are two scale tiles, 2w and 2w+1 (for DSv4's last
+  // wave: tile 6 and the rope columns, whose P' slot is 7)
+  static_assert(WCOLS == 2 * R::TILE && (!ROPE_V || R::DV - R::NOPE == R::TILE), "value columns per wave");
+};
+
+// scale byte -> 2^(b-127) (0 -> 2^-127, 255 -> NaN; the writer stores 1..254)
+__device__ __forceinline__ float e8m0_to_f32(uint32_t b) {
+  const uint32_t bits = b == 0u ? 0x00400000u : (b == 255u ? 0x7FC00000u : b << 23);
+  return __builtin_bit_cast(float, bits);
+}
+
+template <class R, bool DECODE>
+__global__ __launch_bounds__(NT, R::OCC) void attn_mx_kernel(AttnParams p) {
+  using G = Geo<R>;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[G::LDS_BYTES];
+  uint8_t* tile = smem;
+  uint8_t* qbuf = smem + G::Q_OFF;
+  uint8_t* pbuf = smem + G::P_OFF;
+  float* sct = reinterpret_cast<float*>(smem + G::SC_OFF);
+  float* red = reinterpret_cast<float*>(smem + G::RED_OFF);
+  int32_t* idx_lds = reinterpret_cast<int32_t*>(smem + G::IDX_OFF);
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int lg = lane >> 4;
+  const int lc = lane & 15;
+
+  // workgroup x -> (token, head group, split): x = ((tq*S + split)*HG + hg)*8 + xcd, t = 8*tq + xcd
+  const int HG = (p.H + 15) >> 4;
+  const int S = DECODE ? p.num_splits : 1;
+  const int64_t bx = blockIdx.x;
+  const int64_t rest = bx / NXCD;
+  const int hg = (int)(rest % HG);
+  const int split = DECODE ? (int)((rest / HG) % S) : 0;
+  const int64_t t = (rest / HG / S) * NXCD + bx % NXCD;
+  if (t >= p.T) return;  // the last round of tokens may be short (whole workgroup)
+  const int h0 = hg * 16;
+
+  const ListEnds le = list_ends(p, t);
+  const Sources src_lists = sources<false>(p);
+  int64_t j_begin = 0, j_end = p.topk;
+  if (DECODE) {
+    j_begin = (int64_t)split * p.split_w;
+    j_end = j_begin + p.split_w;
+    if (j_end > p.topk) j_end = p.topk;
+  }
+  if (j_end > le.end) j_end = le.end;
+  const int n_tiles = j_end > j_begin ? (int)((j_end - j_begin + TC - 1) / TC) : 0;
+
+  // the token's q rows of heads h0..h0+15 into LDS (zeros past H); they
+  // are visible after the first barrier below
+  for (int qc = tid; qc < 16 * (R::QK / 8); qc += NT) {
+    const int hl = qc / (R::QK / 8), piece = qc % (R::QK / 8);
+    const int h = h0 + hl;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (h < p.H) v = *reinterpret_cast<const uint4*>(p.q + t * p.q_st + (int64_t)h * p.q_sh + 8 * piece);
+    *reinterpret_cast<uint4*>(qbuf + hl * G::Q_ROW + 16 * piece) = v;
+  }
+  // Q^T as the B operand of S^T = K Q^T: lane reads Q[h0+lc][32ks + 8lg + i]
+  const uint8_t* qB = qbuf + lc * G::Q_ROW + 16 * lg;
+
+  // slot of list position j_begin + 64k + tid, or -1
+  auto load_idx = [&](int k) -> int32_t {
+    const int64_t j = j_begin + (int64_t)k * TC + tid;
+    int32_t v = -1;
+    if (j < j_end && in_list<false>(p, le, j)) {
+      const int32_t x = *entry_ptr<false>(src_lists, t, j);
+      if (x >= 0 && (int64_t)x < p.nslots) v = x;
+    }
+    return v;
+  };
+
+  // thread tid gathers 16-byte pieces sub + 4r (r < NCH) of tile row
+  // tid / 4, and the row's 8-byte tail when sub == 0
+  const int grow = tid >> 2, sub = tid & 3;
+  uint4 stage[G::NCH];
+  uint2 tail;
+  auto issue_rows = [&](int k) {
+    const int32_t e = idx_lds[(k % 3) * TC + grow];
+    if (e >= 0) {
+      const uint8_t* row = p.pool + (int64_t)(e / PAGE) * p.block_stride + (int64_t)(e % PAGE) * p.row_stride;
+#pragma unroll
+      for (int r = 0; r < G::NCH; ++r) __builtin_memcpy(&stage[r], row + 16 * (sub + 4 * r), 16);
+      tail = make_uint2(0, 0);
+      if (sub == 0) __builtin_memcpy(&tail, row + 16 * G::PIECES, 8);
+    } else {
+#pragma unroll
+      for (int r = 0; r < G::NCH; ++r) stage[r] = make_uint4(0, 0, 0, 0);
+      tail = make_uint2(0, 0);
+    }
+  };
+  auto store_rows = [&]() {
+    uint8_t* dst = tile + grow * G::LDS_ROW;
+#pragma unroll
+    for (int r = 0; r < G::NCH; ++r) *reinterpret_cast<uint4*>(dst + 16 * (sub + 4 * r)) = stage[r];
+    if (sub == 0) {  // the tail holds the row's scale bytes: decode them once for the tile
+      *reinterpret_cast<uint2*>(dst + 16 * G::PIECES) = tail;
+      f32x4 lo, hi;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        lo[g] = e8m0_to_f32((tail.x >> (8 * g)) & 0xFFu);
+        hi[g] = e8m0_to_f32((tail.y >> (8 * g)) & 0xFFu);
+      }
+      reinterpret_cast<f32x4*>(sct + grow * 8)[0] = lo;
+      reinterpret_cast<f32x4*>(sct + grow * 8)[1] = hi;
+    }
+  };
+
+  // running max (log2 units) of head lc, shared by the four waves; this
+  // lane's partial sum over its candidates; O^T for columns
+  // WCOLS*wave + 16dt + 4lg + i of head lc
+  float m_run = -INFINITY;
+  float l_part = 0.0f;
+  f32x4 O[G::NDT];
+#pragma unroll
+  for (int i = 0; i < G::NDT; ++i) O[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (n_tiles > 0) {
+    if (tid < TC) {
+      idx_lds[tid] = load_idx(0);
+      if (n_tiles > 1) idx_lds[TC + tid] = load_idx(1);
+    }
+    __syncthreads();
+    issue_rows(0);
+    store_rows();
+    __syncthreads();
+  }
+
+  for (int k = 0; k < n_tiles; ++k) {
+    if (k + 1 < n_tiles) issue_rows(k + 1);
+    int32_t pend = -1;
+    if (k + 2 < n_tiles && tid < TC) pend = load_idx(k + 2);
+
+    // ---- S^T for candidates 16*wave + (0..15) x heads h0 + (0..15) ----
+    const uint8_t* rowA = tile + (16 * wave + lc) * G::LDS_ROW;
+    f32x4 acc[R::NG + 1];
+#pragma unroll
+    for (int g = 0; g <= R::NG; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < G::KS_PER_TILE; ++kk) {
+#pragma unroll
+      for (int g = 0; g < R::NG; ++g) {  // consecutive products go to different tiles
+        const int ks = G::KS_PER_TILE * g + kk;
+        const uint2 c8 = *reinterpret_cast<const uint2*>(rowA + 32 * ks + 8 * lg);
+        const uint2 lo = fp8x4_to_bf16x4(c8.x), hi = fp8x4_to_bf16x4(c8.y);
+        const bf16x8 b = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qB + 64 * ks));
+        acc[g] = mfma_16x16x32(__builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y)), b, acc[g]);
+      }
+    }
+#pragma unroll
+    for (int ks = G::KS_NOPE; ks < G::KS; ++ks) {
+      const bf16x8 a = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const uint4*>(rowA + R::ROPE_OFF + 2 * (32 * (ks - G::KS_NOPE) + 8 * lg)));
+      const bf16x8 b = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qB + 64 * ks));
+      acc[R::NG] = mfma_16x16x32(a, b, acc[R::NG]);
+    }
+
+    // scores of candidates c = 16*wave + 4lg + i for head lc
+    const int32_t* il = idx_lds + (k % 3) * TC + 16 * wave + 4 * lg;
+    // scales of candidate (4lg+i), tiles 0..3 and 4..7
+    auto scales = [&](int i, int half) -> f32x4 {
+      return reinterpret_cast<const f32x4*>(sct + (16 * wave + 4 * lg + i) * 8)[half];
+    };
+    float s[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x4 lo = scales(i, 0), hi = scales(i, 1);
+      float v = acc[R::NG][i];
+#pragma unroll
+      for (int g = 0; g < R::NG; ++g) v += (g < 4 ? lo[g & 3] : hi[g & 3]) * acc[g][i];
+      s[i] = il[i] >= 0 ? v * p.scale_log2 : -INFINITY;
+    }
+
+    // ---- one running max per head across the four waves ----
+    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (lg == 0) red[wave * 16 + lc] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(red[lc], red[16 + lc]), fmaxf(red[32 + lc], red[48 + lc]));
+    // every wave takes the same decision per head, so the waves' column
+    // slices stay under one max; lanes that do not move multiply by 1
+    const bool need = mx > m_run + LAZY;
+    if (__any(need)) {
+      const float alpha = need ? ((m_run == -INFINITY) ? 0.0f : exp2f(m_run - mx)) : 1.0f;
+      m_run = need ? mx : m_run;
+      l_part *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < G::NDT; ++dt) O[dt] *= alpha;
+    }
+    float pr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pr[i] = (s[i] == -INFINITY) ? 0.0f : exp2f(s[i] - m_run);
+      l_part += pr[i];
+    }
+    // P'_g[h][c] = P[c][h] * scale(c, g), candidates 16*wave + 4lg + (0..3);
+    // slot NG (BF16 value columns) holds P itself
+#pragma unroll
+    for (int g = 0; g < G::SLOTS; ++g) {
+      float sg[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sg[i] = g < R::NG ? scales(i, g >> 2)[g & 3] : 1.0f;
+      const uint32_t u0 = pack_bf16(pr[0] * sg[0], pr[1] * sg[1]);
+      const uint32_t u1 = pack_bf16(pr[2] * sg[2], pr[3] * sg[3]);
+      *reinterpret_cast<uint2*>(pbuf + g * P_SLOT + lc * P_HEAD + 2 * (16 * wave + 4 * lg)) = make_uint2(u0, u1);
+    }
+    __syncthreads();
+
+    // ---- O^T += V^T P'^T over value columns [WCOLS*wave, +WCOLS) ----
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      bf16x8 pb[2];  // P' of slots 2w and 2w+1 for candidates 32kc + 8lg + (0..7)
+#pragma unroll
+      for (int gg = 0; gg < 2; ++gg)
+        pb[gg] = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const uint4*>(pbuf + (2 * wave + gg) * P_SLOT + lc * P_HEAD + 2 * (32 * kc + 8 * lg)));
+#pragma unroll
+      for (int dt = 0; dt < G::NDT; ++dt) {
+        const int c0 = G::WCOLS * wave + 16 * dt;  // first column of the block (wave-uniform)
+        bf16x8 a;
+        if (!G::ROPE_V || c0 < R::NOPE) {
+          // tr8: lane lc = 2r + b reads candidate row (32kc + 8lg + r), byte columns c0 + 8b..
+          const i32x2 raw = lds_read_tr8(tile + (32 * kc + 8 * lg + (lc >> 1)) * G::LDS_ROW + c0 + 8 * (lc & 1));
+          const uint2 lo = fp8x4_to_bf16x4((uint32_t)raw[0]), hi = fp8x4_to_bf16x4((uint32_t)raw[1]);
+          a = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        } else {
+          // tr16 (BF16 rope columns): lane lc = 4r + b reads rows (32kc + 8lg + 4half + r), columns 4b..
+          const uint8_t* rb = tile + (32 * kc + 8 * lg + (lc >> 2)) * G::LDS_ROW + R::ROPE_OFF + 2 * (c0 - R::NOPE) + 8 * (lc & 3);
+          const i16x4 r0 = lds_read_tr16(rb), r1 = lds_read_tr16(rb + 4 * G::LDS_ROW);
+          a = __builtin_bit_cast(bf16x8, make_uint4(__builtin_bit_cast(uint2, r0).x, __builtin_bit_cast(uint2, r0).y,
+                                                    __builtin_bit_cast(uint2, r1).x, __builtin_bit_cast(uint2, r1).y));
+        }
+        O[dt] = mfma_16x16x32(a, pb[dt / (G::NDT / 2)], O[dt]);
+      }
+    }
+
+    if (k + 2 < n_tiles && tid < TC) idx_lds[((k + 2) % 3) * TC + tid] = pend;
+    __syncthreads();
+    if (k + 1 < n_tiles) store_rows();
+    __syncthreads();
+  }
+
+  // ---- per-head sums from the four waves ----
+  float l_w = l_part + __shfl_xor(l_part, 16);
+  l_w += __shfl_xor(l_w, 32);
+  if (lg == 0) red[wave * 16 + lc] = l_w;
+  __syncthreads();
+  const float Lsum = (red[lc] + red[16 + lc]) + (red[32 + lc] + red[48 + lc]);
+  const float M = m_run;
+
+  const int h = h0 + lc;
+  if (h >= p.H) return;
+  const bool empty = !(Lsum > 0.0f);
+  const float lse_v = empty ? -INFINITY : (M + __log2f(Lsum)) * LN2;
+  const int col = G::WCOLS * wave + 4 * lg;
+  if constexpr (DECODE) {
+    const float inv = empty ? 0.0f : 1.0f / Lsum;
+    float* po = p.part_out + ((t * p.num_splits + split) * p.H + h) * (int64_t)R::DV + col;
+#pragma unroll
+    for (int dt = 0; dt < G::NDT; ++dt) *reinterpret_cast<f32x4*>(po + 16 * dt) = O[dt] * inv;
+    if (wave == 0 && lg == 0) p.part_lse[(t * p.num_splits + split) * p.H + h] = lse_v;
+  } else {
+    float factor;
+    if (empty) {
+      factor = 0.0f;
+    } else if (p.sink) {
+      const float s2 = p.sink[h] * LOG2E;
+      const float ms = fmaxf(M, s2);
+      const float a = exp2f(M - ms);
+      factor = a / (Lsum * a + exp2f(s2 - ms));
+    } else {
+      factor = 1.0f / Lsum;
+    }
+    uint16_t* orow = p.out + t * p.out_st + (int64_t)h * p.out_sh + col;
+#pragma unroll
+    for (int dt = 0; dt < G::NDT; ++dt) {
+      const f32x4 v = O[dt] * factor;
+      *reinterpret_cast<uint2*>(orow + 16 * dt) = make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
+    }
+    if (wave == 0 && lg == 0) p.lse[t * p.lse_st + h] = lse_v;
+  }
+}
+
+template <class R>
+hipError_t launch_rows(const AttnParams& p, bool decode, hipStream_t s) {
+  const int64_t rounds = (p.T + NXCD - 1) / NXCD;
+  const int64_t blocks = rounds * NXCD * ((p.H + 15) / 16) * (decode ? p.num_splits : 1);
+  if (blocks > (int64_t)UINT32_MAX) return hipErrorInvalidConfiguration;
+  dim3 block(NT);
+  dim3 grid((unsigned)blocks);
+  if (decode) hipLaunchKernelGGL((attn_mx_kernel<R, true>), grid, block, 0, s, p);
+  else hipLaunchKernelGGL((attn_mx_kernel<R, false>), grid, block, 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attention_mx(const AttnParams& p, int fmt, bool decode, hipStream_t s) {
+  if (fmt == FMT_FP8_DOTS3) return launch_rows<Dots3Row>(p, decode, s);
+  if (fmt == FMT_FP8_DSV4) return launch_rows<Dsv4Row>(p, decode, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace smla

@@ -26,8 +26,12 @@ constexpr int QTILE = 128;  // quantization tile along the nope part
 // FMT_FP8_ANY: FP8 codes with arbitrary positive per-128 scales (the row of FMT_FP8)
 // FMT_FP8_NOPE: the FP8 row whose rope bytes are padding (no rope dimensions)
 // FMT_FP8_DOTS3: 1160-byte rows of 1024 e4m3 codes, 64 BF16 rope values and
-//   eight power-of-two exponent bytes (its own kernels, attention_dots3.hip)
-enum : int { FMT_BF16 = 0, FMT_FP8 = 1, FMT_INT8 = 2, FMT_FP8_ANY = 3, FMT_FP8_NOPE = 4, FMT_FP8_DOTS3 = 5 };
+//   eight power-of-two exponent bytes (its own kernels, attention_mx.hip)
+// FMT_FP8_DSV4: 584-byte rows of 448 e4m3 codes, 64 BF16 rope values, seven
+//   exponent bytes and a pad byte (attention_mx.hip)
+enum : int {
+  FMT_BF16 = 0, FMT_FP8 = 1, FMT_INT8 = 2, FMT_FP8_ANY = 3, FMT_FP8_NOPE = 4, FMT_FP8_DOTS3 = 5, FMT_FP8_DSV4 = 6
+};
 
 // DOTS3_SWA row geometry: [0,1024) codes, [1024,1152) rope, [1152,1160) scale bytes
 namespace dots3 {
@@ -39,6 +43,17 @@ constexpr int ROPE_OFF = 1024;
 constexpr int SCALE_OFF = 1152;
 constexpr int NGROUPS = 8;  // 128-element scale tiles
 }  // namespace dots3
+
+// DSv4 row geometry: [0,448) codes, [448,576) rope, [576,583) scale bytes, [583] pad
+namespace dsv4 {
+constexpr int D_NOPE = 448;
+constexpr int D_QK = 512;
+constexpr int D_V = 512;
+constexpr int ROW_BYTES = 584;
+constexpr int ROPE_OFF = 448;
+constexpr int SCALE_OFF = 576;
+constexpr int NGROUPS = 7;  // 64-element scale tiles
+}  // namespace dsv4
 
 template <int FMT>
 struct RowGeom {

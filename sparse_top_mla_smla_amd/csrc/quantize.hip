@@ -113,11 +113,17 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantParams p) {
   }
 }
 
-// DOTS3_SWA rows: the same power-of-two scale, with its exponent raised to
-// at least -126 and stored as one byte (e + 127) in the row's footer.  One
-// wave per row; lane l owns nope elements [16l, 16l+16), so the 8 lanes of
-// an aligned group cover one 128-element tile.  Rows are 8-byte aligned.
-__global__ __launch_bounds__(256) void quantize_dots3_kernel(QuantParams p) {
+// Rows with exponent-byte scales (DOTS3_SWA: 1024 codes in 128-element
+// tiles; DSv4: 448 codes in 64-element tiles): the same power-of-two scale
+// as the FP8 rows, with its exponent raised to at least -126 and stored as
+// one byte (e + 127) in the row's tail; DSv4's pad byte is written as 0.
+// One wave per row; lane l owns nope elements [EPL*l, EPL*l + EPL), so the
+// 8 lanes of an aligned group cover one tile.  Rows are 8-byte aligned.
+template <int NOPE, int EPL, int ROPE_OFF, int SCALE_OFF>
+__global__ __launch_bounds__(256) void quantize_mx_kernel(QuantParams p) {
+  constexpr int LANES = NOPE / EPL;  // lanes holding nope elements
+  constexpr int NG = LANES / 8;      // scale tiles
+  static_assert(NOPE % EPL == 0 && LANES % 8 == 0 && LANES <= 64 && EPL % 8 == 0 && NG <= 8, "row geometry");
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= p.n) return;
@@ -125,47 +131,53 @@ __global__ __launch_bounds__(256) void quantize_dots3_kernel(QuantParams p) {
   if (slot < 0 || slot >= p.nslots) return;
   const uint16_t* src = p.kv + row * p.kv_stride;
   uint8_t* dst = p.pool + (slot / PAGE) * p.block_stride + (slot % PAGE) * p.row_stride;
+  const bool active = lane < LANES;
 
-  const uint4* s4 = reinterpret_cast<const uint4*>(src) + 2 * lane;
-  const uint4 r0 = s4[0], r1 = s4[1];
-  const uint32_t w[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
-  float x[16];
+  float x[EPL];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    x[2 * i] = __builtin_bit_cast(float, w[i] << 16);
-    x[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xFFFF0000u);
+  for (int c = 0; c < EPL / 8; ++c) {
+    const uint4 r = active ? reinterpret_cast<const uint4*>(src + EPL * lane)[c] : make_uint4(0, 0, 0, 0);
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[8 * c + 2 * i] = __builtin_bit_cast(float, w[i] << 16);
+      x[8 * c + 2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xFFFF0000u);
+    }
   }
   float amax = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
+  for (int i = 0; i < EPL; ++i) amax = fmaxf(amax, fabsf(x[i]));
 #pragma unroll
   for (int o = 1; o < 8; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
   int e = amax == 0.0f ? 0 : fp8_scale_exponent(amax);
   e = e < -126 ? -126 : e;
   const float scale = __builtin_bit_cast(float, (uint32_t)(e + 127) << 23);
-  uint32_t code[16];
+  if (active) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) code[i] = e4m3_from_f32(__fdiv_rn(x[i], scale));
-  uint32_t pk[4];
+    for (int c = 0; c < EPL / 8; ++c) {
+      uint32_t code[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    pk[i] = code[4 * i] | (code[4 * i + 1] << 8) | (code[4 * i + 2] << 16) | (code[4 * i + 3] << 24);
-  uint2* d2 = reinterpret_cast<uint2*>(dst) + 2 * lane;
-  d2[0] = make_uint2(pk[0], pk[1]);
-  d2[1] = make_uint2(pk[2], pk[3]);
-  if (lane < 16) {
-    const uint2* rs = reinterpret_cast<const uint2*>(src + dots3::D_NOPE) + lane;  // 4 rope values
-    reinterpret_cast<uint2*>(dst + dots3::ROPE_OFF)[lane] = *rs;
+      for (int i = 0; i < 8; ++i) code[i] = e4m3_from_f32(__fdiv_rn(x[8 * c + i], scale));
+      const uint2 pk = make_uint2(code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24),
+                                  code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24));
+      reinterpret_cast<uint2*>(dst + EPL * lane)[c] = pk;
+    }
   }
-  // the eight scale bytes, from the first lane of each tile, in one store
+  if (lane < 16) {  // 64 rope values, 4 per lane
+    const uint2* rs = reinterpret_cast<const uint2*>(src + NOPE) + lane;
+    reinterpret_cast<uint2*>(dst + ROPE_OFF)[lane] = *rs;
+  }
+  // the scale bytes (and zero padding up to 8 bytes), from the first lane
+  // of each tile, in one store
   const uint32_t b = (uint32_t)(e + 127);
   uint32_t lo = 0, hi = 0;
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
-    lo |= (uint32_t)__shfl((int)b, 8 * g) << (8 * g);
-    hi |= (uint32_t)__shfl((int)b, 8 * (g + 4)) << (8 * g);
+    const uint32_t b0 = (uint32_t)__shfl((int)b, 8 * g), b1 = (uint32_t)__shfl((int)b, 8 * (g + 4));
+    lo |= (g < NG ? b0 : 0u) << (8 * g);
+    hi |= (g + 4 < NG ? b1 : 0u) << (8 * g);
   }
-  if (lane == 0) *reinterpret_cast<uint2*>(dst + dots3::SCALE_OFF) = make_uint2(lo, hi);
+  if (lane == 0) *reinterpret_cast<uint2*>(dst + SCALE_OFF) = make_uint2(lo, hi);
 }
 
 hipError_t launch_quantize(const QuantParams& p, int fmt, hipStream_t s) {
@@ -176,7 +188,12 @@ hipError_t launch_quantize(const QuantParams& p, int fmt, hipStream_t s) {
     case FMT_INT8: hipLaunchKernelGGL(quantize_kernel<FMT_INT8>, grid, block, 0, s, p); break;
     case FMT_FP8_ANY: hipLaunchKernelGGL(quantize_kernel<FMT_FP8_ANY>, grid, block, 0, s, p); break;
     case FMT_FP8_NOPE: hipLaunchKernelGGL(quantize_kernel<FMT_FP8_NOPE>, grid, block, 0, s, p); break;
-    case FMT_FP8_DOTS3: hipLaunchKernelGGL(quantize_dots3_kernel, grid, block, 0, s, p); break;
+    case FMT_FP8_DOTS3:
+      hipLaunchKernelGGL((quantize_mx_kernel<dots3::D_NOPE, 16, dots3::ROPE_OFF, dots3::SCALE_OFF>), grid, block, 0, s, p);
+      break;
+    case FMT_FP8_DSV4:
+      hipLaunchKernelGGL((quantize_mx_kernel<dsv4::D_NOPE, 8, dsv4::ROPE_OFF, dsv4::SCALE_OFF>), grid, block, 0, s, p);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

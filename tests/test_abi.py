@@ -53,6 +53,7 @@ def test_row_bytes_and_version():
     assert smla.row_bytes(W.FMT_FP8) == 656
     assert smla.row_bytes(W.FMT_INT8) == 656
     assert smla.row_bytes(W.FMT_FP8_DOTS3) == 1160
+    assert smla.row_bytes(W.FMT_FP8_DSV4) == 584
     assert smla.row_bytes(7) == -1
     assert "gfx950" in smla.version()
 
@@ -108,7 +109,7 @@ def test_prefill_validation_before_launch():
     assert prefill(lib, topk=0) == 2
     assert prefill(lib, pl=pool(page_block=32)) == 4                         # page block must be 64
     assert "page_block 32" in lib.smla_last_error().decode()
-    assert prefill(lib, pl=pool(fmt=6)) == 4                                 # unknown format
+    assert prefill(lib, pl=pool(fmt=7)) == 4                                 # unknown format
     assert prefill(lib, pl=pool(block_stride=64 * 656 - 16)) == 3            # block stride below 64 rows
     assert prefill(lib, pl=pool(row_stride=640)) == 3                        # row stride below the row
     assert prefill(lib, pl=pool(row_stride=664)) == 3                        # row stride not a multiple of 16

@@ -1,10 +1,13 @@
-"""DOTS3_SWA rows on the GPU (1160-byte rows: 1024 e4m3 codes, 64 BF16
-rope values, eight exponent bytes; d_qk 1088, d_v 1024) against the oracle.
+"""Rows with exponent-byte scales on the GPU against the oracle:
+DOTS3_SWA (1160-byte rows: 1024 e4m3 codes, 64 BF16 rope values, eight
+exponent bytes; d_qk 1088, d_v 1024) and DSv4 (584-byte rows: 448 e4m3
+codes, 64 BF16 rope values, seven exponent bytes and a pad byte; d_qk =
+d_v = 512, so V's last 64 columns are the rope values).
 
 Cases span several 64-entry tiles with ragged tails (the pages' 513-entry
-lists), head counts that are not multiples of the 16-head group, strided q
-and out views, per-token lengths (including empty lists), sinks, padded
-rows, and the split form with its combine at the 1024-value width.
+DOTS3_SWA lists), head counts that are not multiples of the 16-head group,
+strided q and out views, per-token lengths (including empty lists), sinks,
+padded rows, and the split form with its combine at each value width.
 """
 import numpy as np
 import pytest
@@ -18,7 +21,7 @@ from gpu_util import Dev, assert_lse_close, assert_out_close, bf16_dev_to_f64, f
 from helpers import oracle_pool
 
 pytestmark = pytest.mark.gpu
-F = W.FMT_FP8_DOTS3
+D3, V4 = W.FMT_FP8_DOTS3, W.FMT_FP8_DSV4
 
 
 @pytest.fixture(autouse=True)
@@ -27,21 +30,22 @@ def _gpu():
 
 
 CASES = {
-    # name: make_case kwargs (config ids 500+)
+    # name: make_case kwargs (config ids 500+ for DOTS3_SWA, 540+ for DSv4)
     "h16_w513_window_len_sink": dict(H=16, topk=513, ctx=1024, window=128, with_topk_length=True, with_sink=True),
     "h20_view_tailneg": dict(H=20, hbuf=32, topk=640, tail_neg=37, idx_ld=700, pad_fill=W.PAD_SENTINEL),
     "h64_w1024": dict(H=64, topk=1024, ctx=2048, T=3, with_sink=True),
     "h1_w100": dict(H=1, topk=100, causal=False),
     "h8_w513_len": dict(H=8, topk=513, ctx=768, T=7, with_topk_length=True),
 }
+FMTS = [D3, V4]
 
 
-def make(name, **over):
+def make(name, fmt=D3, **over):
     kw = dict(CASES[name])
-    base = dict(fmt=F, T=5, n_seqs=1, ctx=1024, causal=True)
+    base = dict(fmt=fmt, T=5, n_seqs=1, ctx=1024, causal=True)
     base.update(kw)
     base.update(over)
-    cid = 500 + sorted(CASES).index(name)
+    cid = (500 if fmt == D3 else 540) + sorted(CASES).index(name)
     return W.make_case(name, config_id=cid, seed=0, **base)
 
 
@@ -50,11 +54,12 @@ def reference(c):
                           sm_scale=c.sm_scale)
 
 
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("name", sorted(CASES))
-def test_prefill_parity(name):
-    c = make(name)
+def test_prefill_parity(name, fmt):
+    c = make(name, fmt)
     d = Dev(c)
-    out_buf = torch.full((c.T, c.H + 3, 1024), 7.0, dtype=torch.bfloat16, device="cuda")
+    out_buf = torch.full((c.T, c.H + 3, W.V_DIMS[fmt]), 7.0, dtype=torch.bfloat16, device="cuda")
     o, l = smla.prefill(d.q, d.pool, d.indices, topk_length=d.topk_length, sink=d.sink,
                         sm_scale=float(c.sm_scale), out=out_buf[:, :c.H])
     torch.cuda.synchronize()
@@ -64,13 +69,14 @@ def test_prefill_parity(name):
     assert torch.all(out_buf[:, c.H:] == 7.0)          # heads beyond the view untouched
 
 
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("name", ["h16_w513_window_len_sink", "h20_view_tailneg", "h64_w1024"])
 @pytest.mark.parametrize("S", [1, 3, 9])
-def test_decode_split_and_combine_parity(name, S):
-    c = make(name)
+def test_decode_split_and_combine_parity(name, S, fmt):
+    c = make(name, fmt)
     d = Dev(c)
     po, pl = smla.decode(d.q, d.pool, d.indices, S, topk_length=d.topk_length, sm_scale=float(c.sm_scale))
-    assert po.shape == (c.T, S, c.H, 1024)
+    assert po.shape == (c.T, S, c.H, W.V_DIMS[fmt])
     o, l = smla.combine(po, pl, sink=d.sink)
     torch.cuda.synchronize()
     pool = oracle_pool(c)
@@ -86,8 +92,9 @@ def test_decode_split_and_combine_parity(name, S):
     assert_lse_close(l.cpu().numpy(), lf32)
 
 
-def test_empty_lists():
-    c = make("h8_w513_len")
+@pytest.mark.parametrize("fmt", FMTS)
+def test_empty_lists(fmt):
+    c = make("h8_w513_len", fmt)
     L = c.topk_length.copy()
     L[0], L[3], L[5] = 0, -2, 1
     c.topk_length = L
@@ -101,20 +108,23 @@ def test_empty_lists():
     assert_lse_close(got_l, lf32)
 
 
-def test_padded_rows_and_blocks():
-    """Packed 1160-byte rows are 8-byte aligned; padded ones (1168) and
-    padded blocks give each row the oracle's packed bytes, leave the padding
+@pytest.mark.parametrize("fmt", FMTS)
+def test_padded_rows_and_blocks(fmt):
+    """Packed rows are 8-byte aligned; padded ones (8 bytes more) and padded
+    blocks give each row the oracle's packed bytes, leave the padding
     unwritten, and give bit-identical attention."""
-    c = make("h20_view_tailneg")
-    rs, bs = 1168, 64 * 1168 + 40
+    c = make("h20_view_tailneg", fmt)
+    rb = W.ROW_BYTES[fmt]
+    rs = rb + 8
+    bs = 64 * rs + 40
     d = Dev(c, block_stride=bs, fill=0xC3, row_stride=rs)
     torch.cuda.synchronize()
     got = d.pool.data.cpu().numpy()
     ref = oracle_pool(c).data
     for blk in range(c.num_blocks):
         for r in range(64):
-            assert np.array_equal(got[blk, r * rs:r * rs + 1160], ref[blk, r * 1160:(r + 1) * 1160])
-            assert (got[blk, r * rs + 1160:(r + 1) * rs] == 0xC3).all()
+            assert np.array_equal(got[blk, r * rs:r * rs + rb], ref[blk, r * rb:(r + 1) * rb])
+            assert (got[blk, r * rs + rb:(r + 1) * rs] == 0xC3).all()
         assert (got[blk, 64 * rs:] == 0xC3).all()
     dp = Dev(c)
     assert np.array_equal(dp.pool.data.cpu().numpy(), ref)
@@ -126,10 +136,11 @@ def test_padded_rows_and_blocks():
     assert torch.equal(x[0], y[0]) and torch.equal(x[1], y[1])
 
 
-def test_attention_entry_runs_the_prefill_form():
-    c = make("h16_w513_window_len_sink")
+@pytest.mark.parametrize("fmt", FMTS)
+def test_attention_entry_runs_the_prefill_form(fmt):
+    c = make("h16_w513_window_len_sink", fmt)
     d = Dev(c)
-    assert smla.attention_workspace_size(c.T, c.H, c.topk, F) == 0
+    assert smla.attention_workspace_size(c.T, c.H, c.topk, fmt) == 0
     ws = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
     a = smla.attention(d.q, d.pool, d.indices, topk_length=d.topk_length, sink=d.sink,
                        sm_scale=float(c.sm_scale), workspace=ws)

@@ -141,7 +141,7 @@ def test_c1_tiny_all_forms():
 
 
 @pytest.mark.parametrize("fmt", [W.FMT_BF16, W.FMT_FP8, W.FMT_INT8, W.FMT_FP8_ANY, W.FMT_FP8_NOPE,
-                                 W.FMT_FP8_DOTS3])
+                                 W.FMT_FP8_DOTS3, W.FMT_FP8_DSV4])
 def test_quantize_bit_exact(fmt):
     c = W.make_case("quant", config_id=230 + fmt, seed=1, fmt=fmt, T=1, H=1, n_seqs=1, ctx=2048, topk=64)
     kv = c.kv.copy()
