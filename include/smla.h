@@ -87,15 +87,14 @@ typedef enum {
  * 1088 values per latent row.  Its writer takes the power-of-two scale of
  * the FP8 rows, raised to at least 2^-126, so it stores b in [1, 254].
  * Lists of any width run on it (the page's lists hold at least 513
- * entries); the dual-list entry points do not accept it.
+ * entries).
  * FP8_E4M3_DSV4 is the DSv4 row, which the same PR gives only as 584 bytes
  * (and d_v = 512 for the V3.2 family); read as [0,448) e4m3 codes of 448
  * nope values, [448,576) 64 BF16 rope values, [576,583) one scale byte per
  * 64-element tile (2^(b-127), as above; 448 = 7 x 64), [583] a pad byte the
  * writer sets to 0 and no reader uses.  K and V are the same 512 values
  * (448 nope + 64 rope): q rows hold 512 values, out rows 512, and the
- * writer reads 512 values per latent row.  Scales as for FP8_E4M3_DOTS3;
- * the dual-list entry points do not accept it. */
+ * writer reads 512 values per latent row.  Scales as for FP8_E4M3_DOTS3. */
 typedef enum {
   SMLA_KV_BF16 = 0,
   SMLA_KV_FP8_E4M3 = 1,

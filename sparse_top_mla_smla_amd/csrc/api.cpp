@@ -104,8 +104,6 @@ smla_status check_out(const void* out, int64_t out_st, int64_t out_sh, int32_t H
 // the secondary list of a dual-cache call (extra != NULL)
 smla_status check_extra(const smla_kv_pool& kv, int32_t topk, const smla_kv_extra* extra) {
   if (!extra) return SMLA_OK;
-  if (mx_format(kv.format))
-    return fail(SMLA_ERR_UNSUPPORTED, "a secondary list is not supported for FP8_E4M3_DOTS3 / FP8_E4M3_DSV4 pools");
   if (topk % 64 != 0)
     return fail(SMLA_ERR_UNSUPPORTED, "topk = %d: with a secondary list the main list width must be a multiple of 64",
                 topk);

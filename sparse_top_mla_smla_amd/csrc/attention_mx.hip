@@ -45,6 +45,11 @@
 // all the loads.  Masked rows are zero-filled so they can never inject NaN
 // into PV.
 //
+// A secondary list (positions [topk, topk + topk2) over a second pool of
+// the same format) runs in the DUAL instantiation: the index stage holds
+// row addresses in both, so the two lists differ only where an entry is
+// read and its row located.
+//
 // Block order: the workgroups of one token's head groups (and of one
 // split) read the same rows, so they are placed on the same XCD (the
 // dispatcher deals consecutive workgroups to the 8 XCDs in turn) and meet
@@ -88,14 +93,14 @@ struct Geo {
   static constexpr int NCH = PIECES / 4;                // staged pieces per thread (4 threads per row)
   static constexpr int Q_ROW = 2 * R::QK + 16;
   // LDS: tile, Q [16][QK] BF16, P' [SLOTS][16 heads][64] BF16, scales [64][8] f32,
-  // wave maxima / sums [4][16], index stage [3][64]
+  // wave maxima / sums [4][16], index stage [3][64] (row addresses)
   static constexpr int TILE_BYTES = TC * LDS_ROW;
   static constexpr int Q_OFF = TILE_BYTES;
   static constexpr int P_OFF = Q_OFF + 16 * Q_ROW;
   static constexpr int SC_OFF = P_OFF + SLOTS * P_SLOT;
   static constexpr int RED_OFF = SC_OFF + TC * 8 * 4;
   static constexpr int IDX_OFF = RED_OFF + 4 * 16 * 4;
-  static constexpr int LDS_BYTES = IDX_OFF + 3 * TC * 4;
+  static constexpr int LDS_BYTES = IDX_OFF + 3 * TC * 8;
   static_assert(R::ROW - 16 * PIECES == 8 && R::SCALE_OFF == 16 * PIECES, "the tail holds the scale bytes");
   static_assert(PIECES % 4 == 0 && R::NOPE % R::TILE == 0 && R::TILE % 32 == 0 && R::NG <= 8, "row geometry");
   // a wave's value columns are two scale tiles, 2w and 2w+1 (for DSv4's last
@@ -109,7 +114,7 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t b) {
   return __builtin_bit_cast(float, bits);
 }
 
-template <class R, bool DECODE>
+template <class R, bool DECODE, bool DUAL>
 __global__ __launch_bounds__(NT, R::OCC) void attn_mx_kernel(AttnParams p) {
   using G = Geo<R>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[G::LDS_BYTES];
@@ -118,7 +123,7 @@ __global__ __launch_bounds__(NT, R::OCC) void attn_mx_kernel(AttnParams p) {
   uint8_t* pbuf = smem + G::P_OFF;
   float* sct = reinterpret_cast<float*>(smem + G::SC_OFF);
   float* red = reinterpret_cast<float*>(smem + G::RED_OFF);
-  int32_t* idx_lds = reinterpret_cast<int32_t*>(smem + G::IDX_OFF);
+  uint64_t* idx_lds = reinterpret_cast<uint64_t*>(smem + G::IDX_OFF);  // 0: no candidate
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -138,12 +143,13 @@ __global__ __launch_bounds__(NT, R::OCC) void attn_mx_kernel(AttnParams p) {
   const int h0 = hg * 16;
 
   const ListEnds le = list_ends(p, t);
-  const Sources src_lists = sources<false>(p);
-  int64_t j_begin = 0, j_end = p.topk;
+  const Sources src_lists = sources<DUAL>(p);
+  const int64_t topk_all = (int64_t)p.topk + p.topk2;
+  int64_t j_begin = 0, j_end = topk_all;
   if (DECODE) {
     j_begin = (int64_t)split * p.split_w;
     j_end = j_begin + p.split_w;
-    if (j_end > p.topk) j_end = p.topk;
+    if (j_end > topk_all) j_end = topk_all;
   }
   if (j_end > le.end) j_end = le.end;
   const int n_tiles = j_end > j_begin ? (int)((j_end - j_begin + TC - 1) / TC) : 0;
@@ -160,14 +166,11 @@ __global__ __launch_bounds__(NT, R::OCC) void attn_mx_kernel(AttnParams p) {
   // Q^T as the B operand of S^T = K Q^T: lane reads Q[h0+lc][32ks + 8lg + i]
   const uint8_t* qB = qbuf + lc * G::Q_ROW + 16 * lg;
 
-  // slot of list position j_begin + 64k + tid, or -1
-  auto load_idx = [&](int k) -> int32_t {
+  // row address of list position j_begin + 64k + tid, or 0
+  auto load_idx = [&](int k) -> uint64_t {
     const int64_t j = j_begin + (int64_t)k * TC + tid;
-    int32_t v = -1;
-    if (j < j_end && in_list<false>(p, le, j)) {
-      const int32_t x = *entry_ptr<false>(src_lists, t, j);
-      if (x >= 0 && (int64_t)x < p.nslots) v = x;
-    }
+    uint64_t v = 0;
+    if (j < j_end && in_list<DUAL>(p, le, j)) v = (uint64_t)row_of<DUAL>(src_lists, j, *entry_ptr<DUAL>(src_lists, t, j));
     return v;
   };
 
@@ -177,9 +180,8 @@ __global__ __launch_bounds__(NT, R::OCC) void attn_mx_kernel(AttnParams p) {
   uint4 stage[G::NCH];
   uint2 tail;
   auto issue_rows = [&](int k) {
-    const int32_t e = idx_lds[(k % 3) * TC + grow];
-    if (e >= 0) {
-      const uint8_t* row = p.pool + (int64_t)(e / PAGE) * p.block_stride + (int64_t)(e % PAGE) * p.row_stride;
+    const uint8_t* row = (const uint8_t*)idx_lds[(k % 3) * TC + grow];
+    if (row) {
 #pragma unroll
       for (int r = 0; r < G::NCH; ++r) __builtin_memcpy(&stage[r], row + 16 * (sub + 4 * r), 16);
       tail = make_uint2(0, 0);
@@ -229,7 +231,7 @@ __global__ __launch_bounds__(NT, R::OCC) void attn_mx_kernel(AttnParams p) {
 
   for (int k = 0; k < n_tiles; ++k) {
     if (k + 1 < n_tiles) issue_rows(k + 1);
-    int32_t pend = -1;
+    uint64_t pend = 0;
     if (k + 2 < n_tiles && tid < TC) pend = load_idx(k + 2);
 
     // ---- S^T for candidates 16*wave + (0..15) x heads h0 + (0..15) ----
@@ -257,7 +259,7 @@ __global__ __launch_bounds__(NT, R::OCC) void attn_mx_kernel(AttnParams p) {
     }
 
     // scores of candidates c = 16*wave + 4lg + i for head lc
-    const int32_t* il = idx_lds + (k % 3) * TC + 16 * wave + 4 * lg;
+    const uint64_t* il = idx_lds + (k % 3) * TC + 16 * wave + 4 * lg;
     // scales of candidate (4lg+i), tiles 0..3 and 4..7
     auto scales = [&](int i, int half) -> f32x4 {
       return reinterpret_cast<const f32x4*>(sct + (16 * wave + 4 * lg + i) * 8)[half];
@@ -269,7 +271,7 @@ __global__ __launch_bounds__(NT, R::OCC) void attn_mx_kernel(AttnParams p) {
       float v = acc[R::NG][i];
 #pragma unroll
       for (int g = 0; g < R::NG; ++g) v += (g < 4 ? lo[g & 3] : hi[g & 3]) * acc[g][i];
-      s[i] = il[i] >= 0 ? v * p.scale_log2 : -INFINITY;
+      s[i] = il[i] != 0 ? v * p.scale_log2 : -INFINITY;
     }
 
     // ---- one running max per head across the four waves ----
@@ -390,8 +392,13 @@ hipError_t launch_rows(const AttnParams& p, bool decode, hipStream_t s) {
   if (blocks > (int64_t)UINT32_MAX) return hipErrorInvalidConfiguration;
   dim3 block(NT);
   dim3 grid((unsigned)blocks);
-  if (decode) hipLaunchKernelGGL((attn_mx_kernel<R, true>), grid, block, 0, s, p);
-  else hipLaunchKernelGGL((attn_mx_kernel<R, false>), grid, block, 0, s, p);
+  if (p.topk2 > 0) {
+    if (decode) hipLaunchKernelGGL((attn_mx_kernel<R, true, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((attn_mx_kernel<R, false, true>), grid, block, 0, s, p);
+  } else {
+    if (decode) hipLaunchKernelGGL((attn_mx_kernel<R, true, false>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((attn_mx_kernel<R, false, false>), grid, block, 0, s, p);
+  }
   return hipGetLastError();
 }
 

@@ -153,9 +153,9 @@ def test_dots3_validation_before_launch():
     assert call(out_sh=512) == 3                                             # out rows hold 1024 values
     assert call(pl=pool(fmt=F, row_stride=1164)) == 3                        # rows 8-byte aligned
     assert call(pl=pool(fmt=F, block_stride=64 * 1160 + 4)) == 3
-    ex = smla._Extra(pool(fmt=F), FAKE, 64, 64, None)
-    assert call(ex=ex) == 4                                                  # no secondary list
-    assert "DOTS3" in lib.smla_last_error().decode()
+    ex = smla._Extra(pool(fmt=W.FMT_FP8_DSV4), FAKE, 64, 64, None)
+    assert call(ex=ex) == 4                                                  # secondary pool of another format
+    assert "format" in lib.smla_last_error().decode()
     kv = lib.smla_quantize_kv(FAKE, 4, 576, FAKE, pool(fmt=F), None)
     assert kv == 3                                                           # writer reads 1088 values
 

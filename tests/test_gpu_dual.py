@@ -26,6 +26,10 @@ CASES = {
     "int8_h64": (W.FMT_INT8, 64, 64, 130, True, True),
     "fp8_h8": (W.FMT_FP8, 8, 192, 70, True, False),
     "bf16_h16": (W.FMT_BF16, 16, 64, 100, True, True),
+    # rows with exponent-byte scales: DSv4 (the page's dual-cache model) and DOTS3_SWA
+    "dsv4_h64": (W.FMT_FP8_DSV4, 64, 128, 192, True, True),
+    "dsv4_h20_w1024_2176": (W.FMT_FP8_DSV4, 20, 1024, 2176, False, False),
+    "dots3_h16": (W.FMT_FP8_DOTS3, 16, 192, 130, True, True),
 }
 
 
@@ -79,7 +83,7 @@ def dual_args(dm, de):
 @pytest.mark.parametrize("name", sorted(CASES))
 def test_prefill_dual_parity(name):
     main, extra = make(name)
-    dm, de = Dev(main), Dev(extra, row_stride=W.ROW_BYTES[extra.fmt] + 16)  # padded secondary rows
+    dm, de = Dev(main), Dev(extra, row_stride=(W.ROW_BYTES[extra.fmt] + 31) // 16 * 16)  # padded secondary rows
     o, l = smla.prefill_dual(dm.q, dm.pool, dm.indices, sink=dm.sink, **dual_args(dm, de))
     torch.cuda.synchronize()
     ob, lf32, _, _ = reference(main, extra)
@@ -89,7 +93,7 @@ def test_prefill_dual_parity(name):
     assert_lse_close(got_l, lf32)
 
 
-@pytest.mark.parametrize("name", ["fp8_h64", "int8_h64", "fp8_h8", "bf16_h16"])
+@pytest.mark.parametrize("name", ["fp8_h64", "int8_h64", "fp8_h8", "bf16_h16", "dsv4_h64", "dots3_h16"])
 @pytest.mark.parametrize("S", [1, 3, 5])
 def test_decode_dual_parity(name, S):
     main, extra = make(name)
@@ -107,7 +111,7 @@ def test_decode_dual_parity(name, S):
     assert_lse_close(l.cpu().numpy(), lf32)
 
 
-@pytest.mark.parametrize("name", ["fp8_h64", "int8_h64", "fp8_h8", "bf16_h16"])
+@pytest.mark.parametrize("name", ["fp8_h64", "int8_h64", "fp8_h8", "bf16_h16", "dsv4_h64", "dots3_h16"])
 def test_empty_secondary_list_is_the_single_list_call(name):
     """A secondary list cut to length 0 everywhere leaves exactly the
     single-list result, bit for bit."""
@@ -122,7 +126,7 @@ def test_empty_secondary_list_is_the_single_list_call(name):
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
-@pytest.mark.parametrize("name", ["fp8_h64", "int8_h64", "fp8_h8", "bf16_h16"])
+@pytest.mark.parametrize("name", ["fp8_h64", "int8_h64", "fp8_h8", "bf16_h16", "dsv4_h64", "dots3_h16"])
 def test_empty_main_list_is_the_secondary_list_alone(name):
     """A main list cut to length 0 everywhere leaves the secondary list's
     single-list result, bit for bit (the main list's width is a multiple of
