@@ -23,6 +23,9 @@ Also measured in the same run:
 - "int8": T = 1024, H = 128, ctx 65536 INT8 pool, top-k 2048 as a view of a
   4096-wide index buffer, with a sink; and in "decode", the decode batch
   over an INT8 pool at the model's split count;
+- "dsv4": DSv4 584-byte rows -- the metric's prefill from the same latent
+  rows and lists (first 512 values), and the dual-cache decode batch over
+  two DSv4 pools;
 - "dots3": DOTS3_SWA rows (1160 bytes, d_qk 1088, d_v 1024) -- prefill at
   T = 1024, ctx 16384, H = 64 over 513-entry lists (385 causal uniform + a
   128-position window) with a sink, and decode of 32 sequences x 1 query
@@ -323,6 +326,28 @@ def main():
         }
         print(f"[bench] glm_nsa prefill {tn[0]:.1f} us", file=sys.stderr, flush=True)
         del apool
+        # the same rows and lists as DSv4 584-byte rows (the first 512 values of
+        # each latent row and of each q row)
+        v4pool = smla.KVPool.empty(case.num_blocks, W.FMT_FP8_DSV4, device=dev)
+        smla.quantize_kv(kv, torch.from_numpy(case.slots).to(dev), v4pool)
+        v4out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=dev)
+
+        def v4():
+            smla.prefill(q[:, :, :512], v4pool, idx, sm_scale=float(W.SM_SCALE_DSV4), out=v4out, lse=lse)
+
+        v4()
+        t4 = pct(event_times_us(torch, v4, 10, stream))
+        v4_bytes = rows * W.ROW_BYTES[W.FMT_FP8_DSV4]
+        result["dsv4"] = {"prefill": {
+            "workload": f"dsv4 584-byte rows, prefill T={T} ctx={case.ctx} H={H} topk={case.topk} (the metric's "
+                        "lists and latent rows)",
+            "kernel_us_median_p10_p90": [round(v, 3) for v in t4],
+            "us_per_token": round(t4[0] / T, 5),
+            "gathered_kv_bytes": v4_bytes,
+            "gathered_kv_GBps": round(v4_bytes / (t4[0] * 1e-6) / 1e9, 2),
+        }}
+        print(f"[bench] dsv4 prefill {t4[0]:.1f} us", file=sys.stderr, flush=True)
+        del v4pool, v4out
     props = torch.cuda.get_device_properties(dev)
     result["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                         "compute_units": props.multi_processor_count,
@@ -341,10 +366,12 @@ def main():
         didx = torch.from_numpy(dc.idx_buf).to(dev)
         dpool = smla.KVPool.empty(dc.num_blocks, W.FMT_FP8, device=dev)
         smla.quantize_kv(dkv, dslots, dpool)
-        ipool8 = None
-        if not args.no_extra:  # the same rows in an INT8 pool
+        ipool8 = v4main = None
+        if not args.no_extra:  # the same rows in an INT8 pool and in a DSv4 pool
             ipool8 = smla.KVPool.empty(dc.num_blocks, W.FMT_INT8, device=dev)
             smla.quantize_kv(dkv, dslots, ipool8)
+            v4main = smla.KVPool.empty(dc.num_blocks, W.FMT_FP8_DSV4, device=dev)
+            smla.quantize_kv(dkv, dslots, v4main)
         del dkv
         dout = torch.empty((dc.T, dc.H, D_V), dtype=torch.bfloat16, device=dev)
         dlse = torch.empty((dc.T, dc.H), dtype=torch.float32, device=dev)
@@ -473,7 +500,41 @@ def main():
                 "gathered_kv_GBps": round(dual_bytes / (dual_us * 1e-6) / 1e9, 2),
             }
             print(f"[bench] dual-cache decode {dual_us:.1f} us (S={Sd})", file=sys.stderr, flush=True)
-            del xpool, xidx, mids, xpo, xpl
+            del xpool
+            # the same dual-cache decode over DSv4 584-byte rows (the model
+            # the page pairs with the 1024 + 2176 widths)
+            x4pool = smla.KVPool.empty(dc.num_blocks, W.FMT_FP8_DSV4, device=dev)
+            for r0 in range(0, nrows, 1 << 18):
+                xkv = torch.randn((1 << 18, 512), generator=gen, device=dev).to(torch.bfloat16)
+                smla.quantize_kv(xkv, torch.arange(r0, r0 + (1 << 18), dtype=torch.int32, device=dev), x4pool)
+                del xkv
+
+            def dual4(i):
+                smla.decode_dual(dq[:, : dc.H, :512], v4main, mids[i % 3], x4pool, xidx[i % 3], Sd,
+                                 sm_scale=float(W.SM_SCALE_DSV4), part_out=xpo, part_lse=xpl)
+                smla.combine(xpo, xpl, out=dout, lse=dlse)
+
+            for i in range(3):
+                dual4(i)
+            torch.cuda.synchronize()
+            ev[0].record(stream)
+            for i in range(dsteps):
+                dual4(i)
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            dual4_us = ev[0].elapsed_time(ev[1]) * 1e3 / dsteps
+            dual4_bytes = dc.T * (k1 + k2) * W.ROW_BYTES[W.FMT_FP8_DSV4]
+            result.setdefault("dsv4", {})["dual_cache_decode"] = {
+                "workload": f"dsv4 dual-cache decode {dc.T} seqs x 1 query, H={dc.H}, main topk {k1} + secondary "
+                            f"topk {k2} over two {dc.num_blocks * 64 * 584 >> 20} MiB pools, splits={Sd} "
+                            "(decode + combine)",
+                "us_per_call": round(dual4_us, 3),
+                "gathered_kv_bytes": dual4_bytes,
+                "gathered_kv_GBps": round(dual4_bytes / (dual4_us * 1e-6) / 1e9, 2),
+            }
+            print(f"[bench] dsv4 dual-cache decode {dual4_us:.1f} us (S={Sd})", file=sys.stderr, flush=True)
+            del x4pool, xidx, mids, xpo, xpl
+        del v4main
         del dpool, dq, didx, idx_sets, dout, dlse
         torch.cuda.empty_cache()
 
