@@ -263,14 +263,13 @@ smla_status smla_combine(const float* part_out, const float* part_lse, int64_t T
  * splits, or of smla_prefill when num_splits == 0, for T tokens of H heads
  * with topk list entries in the given format:
  *   decode  = waves * (a + b * tiles per workgroup + f * splits per workgroup)
- *             + w * MB of partials;  combine = c0 + c1 * MB;
+ *             + w * MB of partials (T*S*H*(4*d_v + 4) bytes);  combine = c0 + c1 * MB;
  *   prefill = ap0 + waves * (ap + bp * tiles per token),
  * with waves = rounds of workgroups over compute_units and constants fitted
- * per kernel (format, H > 16) by calibrate_splits.py in the package.
+ * per kernel class (format, H > 16) by calibrate_splits.py in the package.
  * compute_units <= 0 means the current device's.  Returns -1 when T < 1,
- * H outside [1, 128], topk < 1, num_splits is outside [0, 64], or the
- * format is unknown or has no fitted constants (FP8_E4M3_DOTS3 and
- * FP8_E4M3_DSV4: there smla_attention runs the prefill form). */
+ * H outside [1, 128], topk < 1, the format is unknown or num_splits is
+ * outside [0, 64]. */
 double smla_split_model_cost(int64_t T, int32_t H, int32_t topk, int32_t format, int32_t num_splits,
                              int32_t compute_units);
 

@@ -18,6 +18,9 @@ workgroups over the compute units at the kernel's occupancy.
 
 Usage (needs a GPU; writes JSON to stdout or --out):
     python -m sparse_top_mla_smla_amd.calibrate_splits --out split_model.json
+    # add classes to a fit, holding its shared constants (w, combine):
+    python -m sparse_top_mla_smla_amd.calibrate_splits --classes dots3_mx,dsv4_mx \
+        --extend split_model_fit.json --out split_model_fit.json
 """
 import argparse
 import json
@@ -30,24 +33,33 @@ import torch
 import sparse_top_mla_smla_amd as smla
 from sparse_top_mla_smla_amd import workloads as W
 
-POOL_ROWS = 1 << 20  # 16384 blocks: 656 MiB (FP8/INT8) or 1.1 GiB (BF16), beyond the last-level cache
+POOL_ROWS = 1 << 20  # 16384 blocks: 584 MiB to 1.2 GiB, beyond the last-level cache
 
 # kernel class -> (format, head counts measured, workgroups per CU per round,
 # heads per block).  The narrow kernel's LDS would allow two workgroups per
 # CU, but it holds about 500 registers per lane, so each SIMD runs one of its
 # waves and a CU one workgroup (fitted with 2, the model misses the best
-# split count by up to 26%; with 1, by 4%).
+# split count by up to 26%; with 1, by 4%).  The exponent-byte kernel
+# (DOTS3_SWA, DSv4 rows) runs 16 heads per workgroup at any H; its DSv4
+# instantiation fits two workgroups per CU.
 CLASSES = {
     "fp8_wide": (W.FMT_FP8, (64, 128), 1, 64),
     "int8_wide": (W.FMT_INT8, (128,), 1, 64),
     "fp8_narrow": (W.FMT_FP8, (8, 16), 1, 16),
     "bf16_narrow": (W.FMT_BF16, (8,), 1, 16),
     "int8_narrow": (W.FMT_INT8, (8,), 1, 16),
+    "dots3_mx": (W.FMT_FP8_DOTS3, (16, 64), 1, 16),
+    "dsv4_mx": (W.FMT_FP8_DSV4, (16, 64), 2, 16),
 }
 T_GRID = (1, 2, 4, 8, 16, 32, 64, 128, 256)
 T_PREFILL_ONLY = (1024,)  # several tokens per workgroup in the persistent prefill
 TOPK_GRID = (512, 2048)
 S_GRID = (1, 2, 4, 8, 16, 32)
+
+
+def partial_mb(cls: str, T: int, S: int, H: int) -> float:
+    """MB of decode partials: T*S*H rows of d_v FP32 values and an LSE."""
+    return T * S * H * (W.V_DIMS[CLASSES[cls][0]] * 4 + 4) / 1e6
 
 
 def geometry(cls: str, T: int, H: int, topk: int, S: int, cus: int):
@@ -62,8 +74,7 @@ def geometry(cls: str, T: int, H: int, topk: int, S: int, cus: int):
     blocks = T * hb * ((S + spb - 1) // spb)
     waves = math.ceil(blocks / (cus * occ))
     tiles = math.ceil(min(spb * w, topk) / 64)
-    mb = T * S * H * (512 * 4 + 4) / 1e6
-    return waves, tiles, spb, mb
+    return waves, tiles, spb, partial_mb(cls, T, S, H)
 
 
 def prefill_geometry(cls: str, T: int, H: int, topk: int, cus: int):
@@ -86,27 +97,30 @@ def timed(fn, sets, warmup=3, iters=9):
     return float(np.median(out))
 
 
-def measure(cus: int, log):
+def measure(cus: int, log, classes=None):
+    classes = list(classes or CLASSES)
     gen = torch.Generator(device="cuda")
     gen.manual_seed(1234)
     pools = {}
-    for fmt in (W.FMT_FP8, W.FMT_INT8, W.FMT_BF16):
+    for fmt in sorted({CLASSES[c][0] for c in classes}):
         pool = smla.KVPool.empty(POOL_ROWS // 64, fmt)
         for r0 in range(0, POOL_ROWS, 1 << 18):
-            kv = torch.randn((1 << 18, 576), generator=gen, device="cuda").to(torch.bfloat16)
+            kv = torch.randn((1 << 18, W.KV_DIMS[fmt]), generator=gen, device="cuda").to(torch.bfloat16)
             slots = torch.arange(r0, r0 + (1 << 18), dtype=torch.int32, device="cuda")
             smla.quantize_kv(kv, slots, pool)
         pools[fmt] = pool
     torch.cuda.synchronize()
     rows = []
-    for cls, (fmt, heads, _, _) in CLASSES.items():
+    for cls in classes:
+        fmt, heads, _, _ = CLASSES[cls]
+        dq, dv = W.KV_DIMS[fmt], W.V_DIMS[fmt]
         for H in heads:
             for topk in TOPK_GRID:
                 for T in T_GRID + T_PREFILL_ONLY:
-                    q = torch.randn((T, H, 576), generator=gen, device="cuda").to(torch.bfloat16)
+                    q = torch.randn((T, H, dq), generator=gen, device="cuda").to(torch.bfloat16)
                     sets = [torch.randint(0, POOL_ROWS, (T, topk), generator=gen, device="cuda", dtype=torch.int32)
                             for _ in range(3)]
-                    out = torch.empty((T, H, 512), dtype=torch.bfloat16, device="cuda")
+                    out = torch.empty((T, H, dv), dtype=torch.bfloat16, device="cuda")
                     lse = torch.empty((T, H), dtype=torch.float32, device="cuda")
                     pool = pools[fmt]
                     tp = timed(lambda x: smla.prefill(q, pool, x, out=out, lse=lse), sets)
@@ -114,7 +128,7 @@ def measure(cus: int, log):
                     for S in S_GRID:
                         if S > topk // 64 or T not in T_GRID:
                             continue
-                        po = torch.empty((T, S, H, 512), dtype=torch.float32, device="cuda")
+                        po = torch.empty((T, S, H, dv), dtype=torch.float32, device="cuda")
                         pl = torch.empty((T, S, H), dtype=torch.float32, device="cuda")
                         td = timed(lambda x: smla.decode(q, pool, x, S, part_out=po, part_lse=pl), sets)
                         tc = timed(lambda x: smla.combine(po, pl, out=out, lse=lse), [None])
@@ -156,7 +170,7 @@ def fit(rows, cus: int):
     c = lsq(X, y)
     consts = {cls: dict(a=c[3 * k], b=c[3 * k + 1], f=c[3 * k + 2]) for k, cls in enumerate(classes)}
     w = c[-1]
-    Xc = [[1.0, T * S * H * 2052 / 1e6, T * H / 1000.0] for T, S, H in ((r["T"], r["S"], r["H"]) for r in dec)]
+    Xc = [[1.0, partial_mb(r["cls"], r["T"], r["S"], r["H"]), r["T"] * r["H"] / 1000.0] for r in dec]
     cc = lsq(Xc, [r["combine_us"] for r in dec])
     for cls in classes:
         pre = [r for r in rows if r["kind"] == "prefill" and r["cls"] == cls]
@@ -167,6 +181,42 @@ def fit(rows, cus: int):
         cp = lsq(Xp, [r["us"] for r in pre])
         consts[cls].update(ap0=cp[0], ap=cp[1], bp=cp[2])
     return dict(classes=consts, w_us_per_MB=w, combine=dict(c0=cc[0], c1=cc[1], c2=cc[2]))
+
+
+def fit_classes(rows, cus: int, base):
+    """Constants of the classes in `rows` with the shared partial-write and
+    combine constants of the fitted model `base` held fixed."""
+    def nnls(X, y):
+        X = np.asarray(X, float)
+        y = np.asarray(y, float)
+        active = list(range(X.shape[1]))
+        coef = np.zeros(X.shape[1])
+        while active:
+            c, *_ = np.linalg.lstsq(X[:, active], y, rcond=None)
+            if (c >= 0).all():
+                coef[active] = c
+                break
+            active.pop(int(np.argmin(c)))
+        return coef
+
+    consts = {}
+    for cls in sorted({r["cls"] for r in rows}):
+        X, y = [], []
+        for r in rows:
+            if r["kind"] == "decode" and r["cls"] == cls:
+                waves, tiles, spb, mb = geometry(cls, r["T"], r["H"], r["topk"], r["S"], cus)
+                X.append([waves, waves * tiles, waves * spb])
+                y.append(r["us"] - base["w_us_per_MB"] * mb)
+        c = nnls(X, y)
+        Xp, yp = [], []
+        for r in rows:
+            if r["kind"] == "prefill" and r["cls"] == cls:
+                waves, tiles = prefill_geometry(cls, r["T"], r["H"], r["topk"], cus)
+                Xp.append([1.0, waves, waves * tiles])
+                yp.append(r["us"])
+        cp = nnls(Xp, yp)
+        consts[cls] = dict(a=c[0], b=c[1], f=c[2], ap0=cp[0], ap=cp[1], bp=cp[2])
+    return consts
 
 
 def predict_prefill(model, cls, T, H, topk, cus):
@@ -180,7 +230,7 @@ def predict(model, cls, T, H, topk, S, cus):
     waves, tiles, spb, mb = geometry(cls, T, H, topk, S, cus)
     dec = waves * (k["a"] + k["b"] * tiles + k["f"] * spb) + model["w_us_per_MB"] * mb
     cm = model["combine"]
-    com = cm["c0"] + cm["c1"] * T * S * H * 2052 / 1e6 + cm["c2"] * T * H / 1000.0
+    com = cm["c0"] + cm["c1"] * partial_mb(cls, T, S, H) + cm["c2"] * T * H / 1000.0
     return dec + com
 
 
@@ -203,7 +253,29 @@ def main():
     ap.add_argument("--out", default="", help="write the JSON here instead of stdout")
     ap.add_argument("--refit", default="", metavar="JSON",
                     help="fit again from the measurements stored in a JSON this script wrote (no GPU)")
+    ap.add_argument("--classes", default="", help="comma-separated kernel classes to measure (default: all)")
+    ap.add_argument("--extend", default="", metavar="JSON",
+                    help="add the measured classes to this fit, holding its shared constants")
     args = ap.parse_args()
+    if args.extend:
+        with open(args.extend) as f:
+            old = json.load(f)
+        cus = old["compute_units"]
+        assert cus == torch.cuda.get_device_properties(0).multi_processor_count
+        classes = [c for c in args.classes.split(",") if c]
+        new_rows = measure(cus, lambda s: print(s, file=sys.stderr, flush=True), classes)
+        model = old["model"]
+        model["classes"].update(fit_classes(new_rows, cus, model))
+        rows = [r for r in old["rows"] if r["cls"] not in classes] + new_rows
+        res = dict(device=old["device"], compute_units=cus, model=model, pick_error=evaluate(model, rows, cus),
+                   rows=rows)
+        text = json.dumps(res, indent=1)
+        if args.out:
+            with open(args.out, "w") as f:
+                f.write(text)
+        else:
+            print(text)
+        return
     if args.refit:
         with open(args.refit) as f:
             old = json.load(f)

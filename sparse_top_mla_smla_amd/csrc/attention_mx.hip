@@ -50,10 +50,10 @@
 // row addresses in both, so the two lists differ only where an entry is
 // read and its row located.
 //
-// Block order: the workgroups of one token's head groups (and of one
-// split) read the same rows, so they are placed on the same XCD (the
-// dispatcher deals consecutive workgroups to the 8 XCDs in turn) and meet
-// in its L2.
+// Block order: the head groups of one (token, split) read the same rows,
+// so they are placed on the same XCD (the dispatcher deals consecutive
+// workgroups to the 8 XCDs in turn) and meet in its L2, while consecutive
+// (token, split) pairs go to different XCDs.
 #include "device_common.h"
 #include "launch.h"
 #include "lists.h"
@@ -131,15 +131,16 @@ __global__ __launch_bounds__(NT, R::OCC) void attn_mx_kernel(AttnParams p) {
   const int lg = lane >> 4;
   const int lc = lane & 15;
 
-  // workgroup x -> (token, head group, split): x = ((tq*S + split)*HG + hg)*8 + xcd, t = 8*tq + xcd
+  // workgroup x -> (pair u = t*S + split, head group): x = ((u / 8)*HG + hg)*8 + u % 8
   const int HG = (p.H + 15) >> 4;
   const int S = DECODE ? p.num_splits : 1;
   const int64_t bx = blockIdx.x;
   const int64_t rest = bx / NXCD;
   const int hg = (int)(rest % HG);
-  const int split = DECODE ? (int)((rest / HG) % S) : 0;
-  const int64_t t = (rest / HG / S) * NXCD + bx % NXCD;
-  if (t >= p.T) return;  // the last round of tokens may be short (whole workgroup)
+  const int64_t u = (rest / HG) * NXCD + bx % NXCD;
+  if (u >= p.T * S) return;  // the last round of pairs may be short (whole workgroup)
+  const int64_t t = u / S;
+  const int split = DECODE ? (int)(u % S) : 0;
   const int h0 = hg * 16;
 
   const ListEnds le = list_ends(p, t);
@@ -387,8 +388,8 @@ __global__ __launch_bounds__(NT, R::OCC) void attn_mx_kernel(AttnParams p) {
 
 template <class R>
 hipError_t launch_rows(const AttnParams& p, bool decode, hipStream_t s) {
-  const int64_t rounds = (p.T + NXCD - 1) / NXCD;
-  const int64_t blocks = rounds * NXCD * ((p.H + 15) / 16) * (decode ? p.num_splits : 1);
+  const int64_t pairs = p.T * (decode ? p.num_splits : 1);
+  const int64_t blocks = (pairs + NXCD - 1) / NXCD * NXCD * ((p.H + 15) / 16);
   if (blocks > (int64_t)UINT32_MAX) return hipErrorInvalidConfiguration;
   dim3 block(NT);
   dim3 grid((unsigned)blocks);

@@ -11,14 +11,15 @@
 //   decode  = waves * (a + b * tiles_per_block + f * splits_per_block) + w * MB
 //   combine = c0 + c1 * MB + c2 * T * H / 1000
 //   prefill = ap0 + waves_p * (ap + bp * tiles_per_token)
-// with MB the partial buffers (T * S * H * 2052 bytes), waves the rounds of
-// workgroups over the compute units (one workgroup per CU per round: the
-// many-head kernels fill a CU's LDS, and the narrow kernel holds about 500
-// registers per lane), and a, b, f, ap0, ap, bp per kernel class.  The
-// constants were fitted by sparse_top_mla_smla_amd/calibrate_splits.py on
-// one MI355X (256 CUs) over 126 decode shapes and their prefill
-// counterparts; there the pick is on average 0.2% and at most 7.7% slower
-// than the best measured split count.
+// with MB the partial buffers (T * S * H * (4 d_v + 4) bytes), waves the
+// rounds of workgroups over the compute units (one workgroup per CU per
+// round: the many-head kernels fill a CU's LDS, and the narrow kernel holds
+// about 500 registers per lane; two for the exponent-byte kernel's DSv4
+// instantiation), and a, b, f, ap0, ap, bp per kernel class.  The constants
+// were fitted by sparse_top_mla_smla_amd/calibrate_splits.py on one MI355X
+// (256 CUs) over 198 decode shapes and their prefill counterparts; there
+// the pick is on average 0.2% and at most 7.7% slower than the best
+// measured split count.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -35,17 +36,19 @@ struct KernelClass {
   double ap0, ap, bp;  // prefill: per launch, per round of blocks, per tile of a round (us)
   int heads_per_block;
   bool grouped;    // consecutive splits per workgroup (the FP8 many-head kernel)
+  int occupancy;   // workgroups per CU in one round
 };
 
 // fitted constants (microseconds), MI355X
-constexpr KernelClass kFp8Wide{14.09, 2.993, 1.554, 2.596, 10.08, 3.211, 64, true};
-constexpr KernelClass kInt8Wide{4.027, 4.956, 4.027, 0.0, 14.59, 5.132, 64, false};
-constexpr KernelClass kFp8Narrow{3.509, 4.015, 3.509, 1.068, 13.21, 3.592, 16, false};
-constexpr KernelClass kBf16Narrow{3.608, 4.568, 3.608, 0.0, 14.05, 4.183, 16, false};
-constexpr KernelClass kInt8Narrow{3.363, 4.257, 3.363, 1.179, 12.82, 3.839, 16, false};
+constexpr KernelClass kFp8Wide{14.09, 2.993, 1.554, 2.596, 10.08, 3.211, 64, true, 1};
+constexpr KernelClass kInt8Wide{4.027, 4.956, 4.027, 0.0, 14.59, 5.132, 64, false, 1};
+constexpr KernelClass kFp8Narrow{3.509, 4.015, 3.509, 1.068, 13.21, 3.592, 16, false, 1};
+constexpr KernelClass kBf16Narrow{3.608, 4.568, 3.608, 0.0, 14.05, 4.183, 16, false, 1};
+constexpr KernelClass kInt8Narrow{3.363, 4.257, 3.363, 1.179, 12.82, 3.839, 16, false, 1};
+constexpr KernelClass kDots3Mx{3.496, 6.141, 3.496, 5.921, 9.735, 5.983, 16, false, 1};
+constexpr KernelClass kDsv4Mx{1.678, 4.843, 1.678, 0.0, 8.484, 4.814, 16, false, 2};
 constexpr double kWriteUsPerMB = 0.186;  // decode's partial stores
 constexpr double kComb0 = 10.57, kComb1 = 0.1856, kComb2 = 0.0;
-constexpr double kPartialBytesPerRow = 512 * 4 + 4;
 constexpr double kCrossover = 0.95;  // split form only when at most this fraction of prefill
 
 const KernelClass* kernel_class(int32_t format, int32_t H) {
@@ -57,27 +60,30 @@ const KernelClass* kernel_class(int32_t format, int32_t H) {
     // arbitrary-scale FP8 runs the INT8 many-head kernel's FP8 instantiation
     case SMLA_KV_FP8_E4M3_ANY_SCALE: return H > 16 ? &kInt8Wide : &kFp8Narrow;
     case SMLA_KV_BF16: return &kBf16Narrow;
+    // rows with exponent-byte scales: their own kernel at any H
+    case SMLA_KV_FP8_E4M3_DOTS3: return &kDots3Mx;
+    case SMLA_KV_FP8_E4M3_DSV4: return &kDsv4Mx;
     default: return nullptr;
   }
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-double split_cost(const KernelClass& c, int64_t T, int32_t H, int32_t topk, int32_t S, int cus) {
+double split_cost(const KernelClass& c, int64_t T, int32_t H, int32_t topk, int32_t S, int cus, int32_t dv) {
   const int64_t hb = ceil_div(H, c.heads_per_block);
   const int64_t w = smla_split_width(topk, S);
   const int64_t spb = c.grouped ? fp8_splits_per_block(T, H, S, cus) : 1;
   const int64_t blocks = T * hb * ceil_div(S, spb);
-  const double waves = (double)ceil_div(blocks, cus);
+  const double waves = (double)ceil_div(blocks, (int64_t)cus * c.occupancy);
   const double tiles = (double)ceil_div(std::min<int64_t>(spb * w, topk), 64);
-  const double mb = (double)T * S * H * kPartialBytesPerRow / 1e6;
+  const double mb = (double)T * S * H * (4.0 * dv + 4.0) / 1e6;
   const double decode = waves * (c.a + c.b * tiles + c.f * (double)spb) + kWriteUsPerMB * mb;
   const double combine = kComb0 + kComb1 * mb + kComb2 * (double)T * H / 1000.0;
   return decode + combine;
 }
 
 double prefill_cost(const KernelClass& c, int64_t T, int32_t H, int32_t topk, int cus) {
-  const double waves = (double)ceil_div(T * ceil_div(H, c.heads_per_block), cus);
+  const double waves = (double)ceil_div(T * ceil_div(H, c.heads_per_block), (int64_t)cus * c.occupancy);
   return c.ap0 + waves * (c.ap + c.bp * (double)ceil_div(topk, 64));
 }
 
@@ -89,11 +95,11 @@ bool valid(int64_t T, int32_t H, int32_t topk, int32_t format) {
 
 int resolve_cus(int32_t compute_units) { return compute_units > 0 ? compute_units : device_compute_units(); }
 
-int best_splits(const KernelClass& c, int64_t T, int32_t H, int32_t topk, int cus, double* cost) {
+int best_splits(const KernelClass& c, int64_t T, int32_t H, int32_t topk, int cus, int32_t dv, double* cost) {
   int best = 1;
-  double best_cost = split_cost(c, T, H, topk, 1, cus);
+  double best_cost = split_cost(c, T, H, topk, 1, cus, dv);
   for (int S = 2; S <= max_splits(topk); ++S) {
-    const double v = split_cost(c, T, H, topk, S, cus);
+    const double v = split_cost(c, T, H, topk, S, cus, dv);
     if (v < best_cost) {  // ties keep the smaller split count
       best = S;
       best_cost = v;
@@ -113,12 +119,14 @@ double smla_split_model_cost(int64_t T, int32_t H, int32_t topk, int32_t format,
   if (!smla::valid(T, H, topk, format) || num_splits < 0 || num_splits > 64) return -1.0;
   const smla::KernelClass& c = *smla::kernel_class(format, H);
   const int cus = smla::resolve_cus(compute_units);
-  return num_splits == 0 ? smla::prefill_cost(c, T, H, topk, cus) : smla::split_cost(c, T, H, topk, num_splits, cus);
+  return num_splits == 0 ? smla::prefill_cost(c, T, H, topk, cus)
+                         : smla::split_cost(c, T, H, topk, num_splits, cus, smla_value_dims(format));
 }
 
 int32_t smla_decode_num_splits(int64_t T, int32_t H, int32_t topk, int32_t format, int32_t compute_units) {
   if (!smla::valid(T, H, topk, format)) return -1;
-  return smla::best_splits(*smla::kernel_class(format, H), T, H, topk, smla::resolve_cus(compute_units), nullptr);
+  return smla::best_splits(*smla::kernel_class(format, H), T, H, topk, smla::resolve_cus(compute_units),
+                           smla_value_dims(format), nullptr);
 }
 
 int32_t smla_use_split_form(int64_t T, int32_t H, int32_t topk, int32_t format, int32_t compute_units) {
@@ -126,7 +134,7 @@ int32_t smla_use_split_form(int64_t T, int32_t H, int32_t topk, int32_t format, 
   const smla::KernelClass& c = *smla::kernel_class(format, H);
   const int cus = smla::resolve_cus(compute_units);
   double split = 0.0;
-  smla::best_splits(c, T, H, topk, cus, &split);
+  smla::best_splits(c, T, H, topk, cus, smla_value_dims(format), &split);
   return split <= smla::kCrossover * smla::prefill_cost(c, T, H, topk, cus) ? 1 : 0;
 }
 

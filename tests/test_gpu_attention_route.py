@@ -23,6 +23,10 @@ CASES = {
     "bf16_h8_t3_w640_len_sink": dict(fmt=W.FMT_BF16, H=8, hbuf=64, T=3, topk=640, ctx=2048, window=128,
                                      with_topk_length=True, with_sink=True, out_hbuf=64),
     "int8_h128_t2_w768_sink": dict(fmt=W.FMT_INT8, H=128, T=2, topk=768, ctx=1024, with_sink=True),
+    # rows with exponent-byte scales (their own kernel and model constants)
+    "dots3_h64_t3_w1024_sink": dict(fmt=W.FMT_FP8_DOTS3, H=64, T=3, topk=1024, ctx=2048, with_sink=True),
+    "dsv4_h20_t2_w2048_len": dict(fmt=W.FMT_FP8_DSV4, H=20, T=2, topk=2048, ctx=4096, with_topk_length=True),
+    "dsv4_h64_t64_w128": dict(fmt=W.FMT_FP8_DSV4, H=64, T=64, topk=128, ctx=512),
 }
 
 
@@ -41,7 +45,7 @@ def run(d, workspace):
     c = d.case
     out = None
     if c.out_hbuf:
-        out = torch.full((c.T, c.out_hbuf, 512), 7.0, dtype=torch.bfloat16, device="cuda")[:, : c.H]
+        out = torch.full((c.T, c.out_hbuf, W.V_DIMS[c.fmt]), 7.0, dtype=torch.bfloat16, device="cuda")[:, : c.H]
     o, l = smla.attention(d.q, d.pool, d.indices, topk_length=d.topk_length, sink=d.sink,
                           sm_scale=float(c.sm_scale), out=out, workspace=workspace)
     torch.cuda.synchronize()
@@ -62,7 +66,7 @@ def test_routed_result_matches_the_oracle(name):
     assert (nbytes > 0) == split
     if split:
         S = smla.decode_num_splits(c.T, c.H, c.topk, c.fmt)
-        assert nbytes == smla.decode_workspace_size(c.T, c.H, S)
+        assert nbytes == smla.decode_workspace_size(c.T, c.H, S, W.V_DIMS[c.fmt])
     ws = torch.full((max(nbytes, 16),), 0xFF, dtype=torch.uint8, device="cuda")  # stale contents
     o, l = run(d, ws)
     ob, lf32, _, _ = oracle.prefill(c.q, oracle_pool(c), c.indices, topk_length=c.topk_length, sink=c.sink,

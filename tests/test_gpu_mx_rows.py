@@ -134,15 +134,3 @@ def test_padded_rows_and_blocks(fmt):
     x = smla.decode(d.q, d.pool, d.indices, 3, sm_scale=float(c.sm_scale))
     y = smla.decode(dp.q, dp.pool, dp.indices, 3, sm_scale=float(c.sm_scale))
     assert torch.equal(x[0], y[0]) and torch.equal(x[1], y[1])
-
-
-@pytest.mark.parametrize("fmt", FMTS)
-def test_attention_entry_runs_the_prefill_form(fmt):
-    c = make("h16_w513_window_len_sink", fmt)
-    d = Dev(c)
-    assert smla.attention_workspace_size(c.T, c.H, c.topk, fmt) == 0
-    ws = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
-    a = smla.attention(d.q, d.pool, d.indices, topk_length=d.topk_length, sink=d.sink,
-                       sm_scale=float(c.sm_scale), workspace=ws)
-    b = smla.prefill(d.q, d.pool, d.indices, topk_length=d.topk_length, sink=d.sink, sm_scale=float(c.sm_scale))
-    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])

@@ -68,7 +68,8 @@ def test_pick_error_on_the_measurements():
 
 
 @pytest.mark.parametrize("fmt,H", [(W.FMT_FP8, 64), (W.FMT_FP8, 128), (W.FMT_INT8, 128), (W.FMT_FP8, 8),
-                                   (W.FMT_BF16, 8), (W.FMT_BF16, 64), (W.FMT_INT8, 16), (W.FMT_FP8, 20)])
+                                   (W.FMT_BF16, 8), (W.FMT_BF16, 64), (W.FMT_INT8, 16), (W.FMT_FP8, 20),
+                                   (W.FMT_FP8_DOTS3, 64), (W.FMT_FP8_DSV4, 16), (W.FMT_FP8_DSV4, 64)])
 @pytest.mark.parametrize("T,topk", [(1, 64), (1, 2048), (7, 640), (64, 2048), (300, 512), (4096, 1024)])
 def test_pick_and_route_follow_from_the_cost(fmt, H, T, topk):
     s_max = min(64, -(-topk // 64))
