@@ -82,7 +82,7 @@ def run_prefill_case(case, out_hbuf=0):
     q_buf, pool, idx_buf, tl, sink = gpu_setup(case)
     q = q_buf[:, : case.H]
     if out_hbuf:
-        out_buf = torch.full((case.T, out_hbuf, 512), 3.0, dtype=torch.bfloat16, device="cuda")
+        out_buf = torch.full((case.T, out_hbuf, W.V_DIMS[case.fmt]), 3.0, dtype=torch.bfloat16, device="cuda")
         out = out_buf[:, : case.H]
     else:
         out_buf, out = None, None
@@ -121,8 +121,19 @@ def test_fullsize_int8_h128():
     run_prefill_case(W.c5_int8())
 
 
-def test_fullsize_decode_fp8():
-    case = W.c2_decode()
+def test_fullsize_prefill_dots3():
+    run_prefill_case(W.dots3_prefill(), out_hbuf=80)
+
+
+def test_fullsize_prefill_dsv4():
+    """DSv4 rows at the metric's shape (T=1024, ctx 16384, H=64, topk 1024)."""
+    run_prefill_case(W.make_case("dsv4_c3", config_id=8, seed=0, fmt=W.FMT_FP8_DSV4, T=1024, H=64, n_seqs=1,
+                                 ctx=16384, topk=1024, causal=True, with_sink=True))
+
+
+@pytest.mark.parametrize("make", [W.c2_decode, W.dots3_decode], ids=["fp8", "dots3"])
+def test_fullsize_decode(make):
+    case = make()
     q_buf, pool, idx_buf, tl, sink = gpu_setup(case)
     S = case.num_splits
     po, pl = smla.decode(q_buf[:, : case.H], pool, idx_buf[:, : case.topk], S, sm_scale=float(case.sm_scale))
@@ -132,6 +143,42 @@ def test_fullsize_decode_fp8():
     ref_pool, slots = oracle_pool_for(case, tokens)
     check_pool_rows(case, pool, ref_pool, slots)
     rpo, rpl = oracle.decode_split(case.q, ref_pool, case.indices, S, sm_scale=case.sm_scale, tokens=tokens)
+    gpl = pl.cpu().numpy()
+    assert np.array_equal(np.isneginf(gpl[tokens]), np.isneginf(rpl[tokens]))
+    assert_lse_close(gpl[tokens], rpl[tokens].astype(np.float32), "part_lse")
+    assert_out_close(po[tokens].cpu().numpy().astype(np.float64), rpo[tokens], "part_out")
+    ob, lf, _, _ = oracle.combine(rpo, rpl, tokens=tokens)
+    assert_out_close(bf16_dev_to_f64(o[tokens]), f64_of_bits(ob[tokens]))
+    assert_lse_close(l[tokens].cpu().numpy(), lf[tokens])
+    assert torch.isfinite(o.float()).all() and torch.isfinite(l).all()
+
+
+def test_fullsize_dual_decode_dsv4():
+    """The dual-cache decode batch over DSv4 rows: 64 sequences x 1 query,
+    H=64, a 1024-wide main list and a 2176-wide secondary list over two
+    pools of 16384-token sequences, 4 splits."""
+    main = W.make_case("dsv4_dual_main", config_id=9, seed=0, fmt=W.FMT_FP8_DSV4, T=64, H=64, n_seqs=64,
+                       ctx=16384, topk=1024, causal=True)
+    extra = W.make_case("dsv4_dual_extra", config_id=10, seed=0, fmt=W.FMT_FP8_DSV4, T=64, H=64, n_seqs=64,
+                        ctx=16384, topk=2176, causal=False)
+    S = 4
+    q_buf, pool, idx_buf, _, _ = gpu_setup(main)
+    _, xpool, xidx_buf, _, _ = gpu_setup(extra)
+    po, pl = smla.decode_dual(q_buf[:, : main.H], pool, idx_buf[:, : main.topk], xpool, xidx_buf[:, : extra.topk], S,
+                              sm_scale=float(main.sm_scale))
+    o, l = smla.combine(po, pl)
+    torch.cuda.synchronize()
+    tokens = sample_tokens(main.T)
+    p1, s1 = oracle_pool_for(main, tokens)
+    p2, s2 = oracle_pool_for(extra, tokens)
+    check_pool_rows(main, pool, p1, s1)
+    check_pool_rows(extra, xpool, p2, s2)
+    # the reference: both pools laid end to end, secondary slots moved past the main pool's
+    n1 = main.num_blocks * 64
+    both = oracle.Pool(np.concatenate([p1.data, p2.data]), main.fmt, p1.block_stride)
+    idx = np.ascontiguousarray(np.concatenate([main.indices, np.where(extra.indices >= 0, extra.indices + n1, -1)],
+                                              axis=1).astype(np.int32))
+    rpo, rpl = oracle.decode_split(main.q, both, idx, S, sm_scale=main.sm_scale, tokens=tokens)
     gpl = pl.cpu().numpy()
     assert np.array_equal(np.isneginf(gpl[tokens]), np.isneginf(rpl[tokens]))
     assert_lse_close(gpl[tokens], rpl[tokens].astype(np.float32), "part_lse")
