@@ -644,6 +644,15 @@ def main():
             "sample": f"{n} of the {T} tokens of the same prefill workload (float64 C oracle, "
                       f"OpenMP over tokens), {cpu_s:.2f} s wall"}
         print(f"[bench] cpu oracle {cpu_s:.2f}s for {n} tokens on {ncores} threads", file=sys.stderr, flush=True)
+        # the tiny BF16 case on one thread (prefill and decode at 1, 2 and 4 splits)
+        c1 = W.c1_tiny()
+        p1 = oracle.Pool(np.zeros((c1.num_blocks, 64 * 1152), np.uint8), W.FMT_BF16, 64 * 1152)
+        oracle.quantize_kv(c1.kv, c1.slots, p1)
+        tc = time.perf_counter()
+        oracle.prefill(c1.q, p1, c1.indices, sm_scale=c1.sm_scale, nthreads=1)
+        for S in (1, 2, 4):
+            oracle.decode_split(c1.q, p1, c1.indices, S, sm_scale=c1.sm_scale, nthreads=1)
+        result["cpu_baseline"]["c1_tiny_single_thread_ms"] = round((time.perf_counter() - tc) * 1e3, 3)
 
     print(json.dumps(result), flush=True)
 
