@@ -386,6 +386,322 @@ __global__ __launch_bounds__(NT, R::OCC) void attn_mx_kernel(AttnParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// DOTS3_SWA rows with more than 16 heads: 32 heads per workgroup.  With
+// 16 heads a workgroup's per-tile chain is paid once per 16 heads, and the
+// 16 q rows (1088 values each) fill LDS; here eight waves share each
+// gathered tile between two 16-head halves hh, and QK is split over the
+// latent instead of over candidates so that Q stays in registers:
+//  * QK: wave (wl, hh) forms partial S^T over nope columns [256wl, +256)
+//    (two scale tiles, scaled after accumulating) plus, for wl < 2, rope
+//    k-step wl, for all 64 candidates of the tile and the 16 heads of hh;
+//    the four partials of each 16-candidate block meet in LDS at the wave
+//    that owns the block (wl), which then runs the softmax of the 16-head
+//    kernel above for its candidates;
+//  * PV is the 16-head kernel's: wave (wl, hh) owns value columns
+//    [256wl, +256) of its 16 heads.
+// LDS: tile 75.8 KB, partial-score exchange 32 KB, P' 36 KB, scales, sums
+// and index stage: 146 KB, one workgroup per CU (two waves per SIMD).
+constexpr int NT32 = 512;  // 8 waves
+
+template <class R, bool DECODE, bool DUAL>
+__global__ __launch_bounds__(NT32, 1) void attn_mx32_kernel(AttnParams p) {
+  using G = Geo<R>;
+  constexpr int KSW = R::NOPE / 4 / 32;      // nope k-steps per wave (8)
+  constexpr int TPW = R::NOPE / 4 / R::TILE;  // scale tiles per wave (2)
+  constexpr int NROPE = G::KS - G::KS_NOPE;   // rope k-steps (2), one per wave wl < NROPE
+  constexpr int PIECES8 = G::PIECES / 8;      // 16-byte pieces per thread (8 threads per row)
+  static_assert(G::ROPE_V == false && TPW == 2 && KSW == 2 * G::KS_PER_TILE && NROPE <= 4 &&
+                    G::PIECES % 8 == 0 && G::WCOLS == 2 * R::TILE,
+                "the DOTS3_SWA geometry");
+  constexpr int XCH_OFF = G::TILE_BYTES;                       // f32x4 [2 hh][4 src][4 blk][64]
+  constexpr int P_OFF2 = XCH_OFF + 2 * 4 * 4 * 64 * 16;
+  constexpr int SC_OFF2 = P_OFF2 + 2 * G::SLOTS * P_SLOT;
+  constexpr int RED_OFF2 = SC_OFF2 + TC * 8 * 4;
+  constexpr int IDX_OFF2 = RED_OFF2 + 2 * 4 * 16 * 4;
+  constexpr int LDS_BYTES2 = IDX_OFF2 + 3 * TC * 8;
+  static_assert(LDS_BYTES2 <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[LDS_BYTES2];
+  uint8_t* tile = smem;
+  f32x4* xch = reinterpret_cast<f32x4*>(smem + XCH_OFF);
+  float* sct = reinterpret_cast<float*>(smem + SC_OFF2);
+  uint64_t* idx_lds = reinterpret_cast<uint64_t*>(smem + IDX_OFF2);
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int wl = wave & 3, hh = wave >> 2;
+  const int lane = tid & 63;
+  const int lg = lane >> 4;
+  const int lc = lane & 15;
+  uint8_t* pbuf = smem + P_OFF2 + hh * G::SLOTS * P_SLOT;
+  float* red = reinterpret_cast<float*>(smem + RED_OFF2) + hh * 64;
+
+  // workgroup x -> (pair u = t*S + split, 32-head group): x = ((u / 8)*HG + hg)*8 + u % 8
+  const int HG = (p.H + 31) >> 5;
+  const int S = DECODE ? p.num_splits : 1;
+  const int64_t bx = blockIdx.x;
+  const int64_t rest = bx / NXCD;
+  const int hg = (int)(rest % HG);
+  const int64_t u = (rest / HG) * NXCD + bx % NXCD;
+  if (u >= p.T * S) return;  // the last round of pairs may be short (whole workgroup)
+  const int64_t t = u / S;
+  const int split = DECODE ? (int)(u % S) : 0;
+  const int h0 = hg * 32 + 16 * hh;  // this wave's 16 heads
+
+  const ListEnds le = list_ends(p, t);
+  const Sources src_lists = sources<DUAL>(p);
+  const int64_t topk_all = (int64_t)p.topk + p.topk2;
+  int64_t j_begin = 0, j_end = topk_all;
+  if (DECODE) {
+    j_begin = (int64_t)split * p.split_w;
+    j_end = j_begin + p.split_w;
+    if (j_end > topk_all) j_end = topk_all;
+  }
+  if (j_end > le.end) j_end = le.end;
+  const int n_tiles = j_end > j_begin ? (int)((j_end - j_begin + TC - 1) / TC) : 0;
+
+  // Q^T slices as B operands: lane holds Q[h0+lc][32ks + 8lg + i] for this
+  // wave's nope k-steps ks = KSW*wl + j and, for wl < NROPE, rope k-step wl
+  bf16x8 qn[KSW], qr;
+  {
+    const int h = h0 + lc;
+    const bool hv = h < p.H;
+    const uint16_t* qrow = p.q + t * p.q_st + (int64_t)(hv ? h : 0) * p.q_sh + 8 * lg;
+#pragma unroll
+    for (int j = 0; j < KSW; ++j) {
+      const uint4 v = *reinterpret_cast<const uint4*>(qrow + 32 * (KSW * wl + j));
+      qn[j] = __builtin_bit_cast(bf16x8, hv ? v : make_uint4(0, 0, 0, 0));
+    }
+    const int rk = wl < NROPE ? wl : 0;
+    const uint4 v = *reinterpret_cast<const uint4*>(qrow + 32 * (G::KS_NOPE + rk));
+    qr = __builtin_bit_cast(bf16x8, (hv && wl < NROPE) ? v : make_uint4(0, 0, 0, 0));
+  }
+
+  auto load_idx = [&](int k) -> uint64_t {
+    const int64_t j = j_begin + (int64_t)k * TC + tid;
+    uint64_t v = 0;
+    if (j < j_end && in_list<DUAL>(p, le, j)) v = (uint64_t)row_of<DUAL>(src_lists, j, *entry_ptr<DUAL>(src_lists, t, j));
+    return v;
+  };
+
+  // thread tid gathers 16-byte pieces sub + 8r (r < PIECES8) of tile row
+  // tid / 8, and the row's 8-byte tail (its scale bytes) when sub == 0
+  const int grow = tid >> 3, sub = tid & 7;
+  uint4 stage[PIECES8];
+  uint2 tail;
+  auto issue_rows = [&](int k) {
+    const uint8_t* row = (const uint8_t*)idx_lds[(k % 3) * TC + grow];
+    if (row) {
+#pragma unroll
+      for (int r = 0; r < PIECES8; ++r) __builtin_memcpy(&stage[r], row + 16 * (sub + 8 * r), 16);
+      tail = make_uint2(0, 0);
+      if (sub == 0) __builtin_memcpy(&tail, row + 16 * G::PIECES, 8);
+    } else {
+#pragma unroll
+      for (int r = 0; r < PIECES8; ++r) stage[r] = make_uint4(0, 0, 0, 0);
+      tail = make_uint2(0, 0);
+    }
+  };
+  auto store_rows = [&]() {
+    uint8_t* dst = tile + grow * G::LDS_ROW;
+#pragma unroll
+    for (int r = 0; r < PIECES8; ++r) *reinterpret_cast<uint4*>(dst + 16 * (sub + 8 * r)) = stage[r];
+    if (sub == 0) {
+      *reinterpret_cast<uint2*>(dst + 16 * G::PIECES) = tail;
+      f32x4 lo, hi;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        lo[g] = e8m0_to_f32((tail.x >> (8 * g)) & 0xFFu);
+        hi[g] = e8m0_to_f32((tail.y >> (8 * g)) & 0xFFu);
+      }
+      reinterpret_cast<f32x4*>(sct + grow * 8)[0] = lo;
+      reinterpret_cast<f32x4*>(sct + grow * 8)[1] = hi;
+    }
+  };
+
+  float m_run = -INFINITY;
+  float l_part = 0.0f;
+  f32x4 O[G::NDT];
+#pragma unroll
+  for (int i = 0; i < G::NDT; ++i) O[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (n_tiles > 0) {
+    if (tid < TC) {
+      idx_lds[tid] = load_idx(0);
+      if (n_tiles > 1) idx_lds[TC + tid] = load_idx(1);
+    }
+    __syncthreads();
+    issue_rows(0);
+    store_rows();
+    __syncthreads();
+  }
+
+  for (int k = 0; k < n_tiles; ++k) {
+    if (k + 1 < n_tiles) issue_rows(k + 1);
+    uint64_t pend = 0;
+    if (k + 2 < n_tiles && tid < TC) pend = load_idx(k + 2);
+
+    // ---- partial S^T over this wave's latent slice, candidate blocks cb ----
+    f32x4 own;  // the block this wave owns (cb == wl), kept in registers
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      const uint8_t* rowA = tile + (16 * cb + lc) * G::LDS_ROW;
+      f32x4 acc[TPW + 1];
+#pragma unroll
+      for (int g = 0; g <= TPW; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < G::KS_PER_TILE; ++kk) {
+#pragma unroll
+        for (int g = 0; g < TPW; ++g) {
+          const int j = G::KS_PER_TILE * g + kk;
+          const uint2 c8 = *reinterpret_cast<const uint2*>(rowA + 32 * (KSW * wl + j) + 8 * lg);
+          const uint2 lo = fp8x4_to_bf16x4(c8.x), hi = fp8x4_to_bf16x4(c8.y);
+          acc[g] = mfma_16x16x32(__builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y)), qn[j], acc[g]);
+        }
+      }
+      if (wl < NROPE) {
+        const bf16x8 a = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const uint4*>(rowA + R::ROPE_OFF + 2 * (32 * wl + 8 * lg)));
+        acc[TPW] = mfma_16x16x32(a, qr, acc[TPW]);
+      }
+      // scale tiles TPW*wl + g of candidates 16cb + 4lg + i
+      f32x4 ps = acc[TPW];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x2 sc = *reinterpret_cast<const f32x2*>(sct + (16 * cb + 4 * lg + i) * 8 + TPW * wl);
+        ps[i] += sc[0] * acc[0][i] + sc[1] * acc[1][i];
+      }
+      if (cb == wl) own = ps;
+      else xch[((hh * 4 + wl) * 4 + cb) * 64 + lane] = ps;
+    }
+    __syncthreads();
+    // scores of candidates c = 16wl + 4lg + i for head lc: the four slices
+    const uint64_t* il = idx_lds + (k % 3) * TC + 16 * wl + 4 * lg;
+    float s[4];
+    {
+      f32x4 sum = own;
+#pragma unroll
+      for (int src = 0; src < 4; ++src)
+        if (src != wl) sum += xch[((hh * 4 + src) * 4 + wl) * 64 + lane];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[i] = il[i] != 0 ? sum[i] * p.scale_log2 : -INFINITY;
+    }
+
+    // ---- one running max per head across the four waves of hh ----
+    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (lg == 0) red[wl * 16 + lc] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(red[lc], red[16 + lc]), fmaxf(red[32 + lc], red[48 + lc]));
+    const bool need = mx > m_run + LAZY;
+    if (__any(need)) {
+      const float alpha = need ? ((m_run == -INFINITY) ? 0.0f : exp2f(m_run - mx)) : 1.0f;
+      m_run = need ? mx : m_run;
+      l_part *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < G::NDT; ++dt) O[dt] *= alpha;
+    }
+    float pr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pr[i] = (s[i] == -INFINITY) ? 0.0f : exp2f(s[i] - m_run);
+      l_part += pr[i];
+    }
+    // P'_g[h][c] = P[c][h] * scale(c, g), candidates 16wl + 4lg + (0..3)
+#pragma unroll
+    for (int g = 0; g < R::NG; ++g) {
+      float sg[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sg[i] = sct[(16 * wl + 4 * lg + i) * 8 + g];
+      const uint32_t u0 = pack_bf16(pr[0] * sg[0], pr[1] * sg[1]);
+      const uint32_t u1 = pack_bf16(pr[2] * sg[2], pr[3] * sg[3]);
+      *reinterpret_cast<uint2*>(pbuf + g * P_SLOT + lc * P_HEAD + 2 * (16 * wl + 4 * lg)) = make_uint2(u0, u1);
+    }
+    __syncthreads();
+
+    // ---- O^T += V^T P'^T over value columns [WCOLS*wl, +WCOLS) ----
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      bf16x8 pb[2];
+#pragma unroll
+      for (int gg = 0; gg < 2; ++gg)
+        pb[gg] = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const uint4*>(pbuf + (2 * wl + gg) * P_SLOT + lc * P_HEAD + 2 * (32 * kc + 8 * lg)));
+#pragma unroll
+      for (int dt = 0; dt < G::NDT; ++dt) {
+        const int c0 = G::WCOLS * wl + 16 * dt;
+        const i32x2 raw = lds_read_tr8(tile + (32 * kc + 8 * lg + (lc >> 1)) * G::LDS_ROW + c0 + 8 * (lc & 1));
+        const uint2 lo = fp8x4_to_bf16x4((uint32_t)raw[0]), hi = fp8x4_to_bf16x4((uint32_t)raw[1]);
+        O[dt] = mfma_16x16x32(__builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y)), pb[dt / (G::NDT / 2)],
+                              O[dt]);
+      }
+    }
+
+    if (k + 2 < n_tiles && tid < TC) idx_lds[((k + 2) % 3) * TC + tid] = pend;
+    __syncthreads();
+    if (k + 1 < n_tiles) store_rows();
+    __syncthreads();
+  }
+
+  // ---- per-head sums from the four waves of hh ----
+  float l_w = l_part + __shfl_xor(l_part, 16);
+  l_w += __shfl_xor(l_w, 32);
+  if (lg == 0) red[wl * 16 + lc] = l_w;
+  __syncthreads();
+  const float Lsum = (red[lc] + red[16 + lc]) + (red[32 + lc] + red[48 + lc]);
+  const float M = m_run;
+
+  const int h = h0 + lc;
+  if (h >= p.H) return;
+  const bool empty = !(Lsum > 0.0f);
+  const float lse_v = empty ? -INFINITY : (M + __log2f(Lsum)) * LN2;
+  const int col = G::WCOLS * wl + 4 * lg;
+  if constexpr (DECODE) {
+    const float inv = empty ? 0.0f : 1.0f / Lsum;
+    float* po = p.part_out + ((t * p.num_splits + split) * p.H + h) * (int64_t)R::DV + col;
+#pragma unroll
+    for (int dt = 0; dt < G::NDT; ++dt) *reinterpret_cast<f32x4*>(po + 16 * dt) = O[dt] * inv;
+    if (wl == 0 && lg == 0) p.part_lse[(t * p.num_splits + split) * p.H + h] = lse_v;
+  } else {
+    float factor;
+    if (empty) {
+      factor = 0.0f;
+    } else if (p.sink) {
+      const float s2 = p.sink[h] * LOG2E;
+      const float ms = fmaxf(M, s2);
+      const float a = exp2f(M - ms);
+      factor = a / (Lsum * a + exp2f(s2 - ms));
+    } else {
+      factor = 1.0f / Lsum;
+    }
+    uint16_t* orow = p.out + t * p.out_st + (int64_t)h * p.out_sh + col;
+#pragma unroll
+    for (int dt = 0; dt < G::NDT; ++dt) {
+      const f32x4 v = O[dt] * factor;
+      *reinterpret_cast<uint2*>(orow + 16 * dt) = make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
+    }
+    if (wl == 0 && lg == 0) p.lse[t * p.lse_st + h] = lse_v;
+  }
+}
+
+template <class R>
+hipError_t launch_rows32(const AttnParams& p, bool decode, hipStream_t s) {
+  const int64_t pairs = p.T * (decode ? p.num_splits : 1);
+  const int64_t blocks = (pairs + NXCD - 1) / NXCD * NXCD * ((p.H + 31) / 32);
+  if (blocks > (int64_t)UINT32_MAX) return hipErrorInvalidConfiguration;
+  dim3 block(NT32);
+  dim3 grid((unsigned)blocks);
+  if (p.topk2 > 0) {
+    if (decode) hipLaunchKernelGGL((attn_mx32_kernel<R, true, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((attn_mx32_kernel<R, false, true>), grid, block, 0, s, p);
+  } else {
+    if (decode) hipLaunchKernelGGL((attn_mx32_kernel<R, true, false>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((attn_mx32_kernel<R, false, false>), grid, block, 0, s, p);
+  }
+  return hipGetLastError();
+}
+
 template <class R>
 hipError_t launch_rows(const AttnParams& p, bool decode, hipStream_t s) {
   const int64_t pairs = p.T * (decode ? p.num_splits : 1);
@@ -406,7 +722,7 @@ hipError_t launch_rows(const AttnParams& p, bool decode, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_attention_mx(const AttnParams& p, int fmt, bool decode, hipStream_t s) {
-  if (fmt == FMT_FP8_DOTS3) return launch_rows<Dots3Row>(p, decode, s);
+  if (fmt == FMT_FP8_DOTS3) return p.H > 16 ? launch_rows32<Dots3Row>(p, decode, s) : launch_rows<Dots3Row>(p, decode, s);
   if (fmt == FMT_FP8_DSV4) return launch_rows<Dsv4Row>(p, decode, s);
   return hipErrorInvalidValue;
 }

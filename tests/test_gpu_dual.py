@@ -30,6 +30,7 @@ CASES = {
     "dsv4_h64": (W.FMT_FP8_DSV4, 64, 128, 192, True, True),
     "dsv4_h20_w1024_2176": (W.FMT_FP8_DSV4, 20, 1024, 2176, False, False),
     "dots3_h16": (W.FMT_FP8_DOTS3, 16, 192, 130, True, True),
+    "dots3_h40": (W.FMT_FP8_DOTS3, 40, 128, 200, True, True),
 }
 
 
@@ -93,7 +94,7 @@ def test_prefill_dual_parity(name):
     assert_lse_close(got_l, lf32)
 
 
-@pytest.mark.parametrize("name", ["fp8_h64", "int8_h64", "fp8_h8", "bf16_h16", "dsv4_h64", "dots3_h16"])
+@pytest.mark.parametrize("name", ["fp8_h64", "int8_h64", "fp8_h8", "bf16_h16", "dsv4_h64", "dots3_h16", "dots3_h40"])
 @pytest.mark.parametrize("S", [1, 3, 5])
 def test_decode_dual_parity(name, S):
     main, extra = make(name)
