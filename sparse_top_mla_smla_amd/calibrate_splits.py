@@ -40,15 +40,17 @@ POOL_ROWS = 1 << 20  # 16384 blocks: 584 MiB to 1.2 GiB, beyond the last-level c
 # CU, but it holds about 500 registers per lane, so each SIMD runs one of its
 # waves and a CU one workgroup (fitted with 2, the model misses the best
 # split count by up to 26%; with 1, by 4%).  The exponent-byte kernel
-# (DOTS3_SWA, DSv4 rows) runs 16 heads per workgroup at any H; its DSv4
-# instantiation fits two workgroups per CU.
+# (DOTS3_SWA, DSv4 rows) runs 16 heads per workgroup (DSv4: at any H, two
+# workgroups per CU); DOTS3_SWA rows with more than 16 heads run its
+# 32-head kernel.
 CLASSES = {
     "fp8_wide": (W.FMT_FP8, (64, 128), 1, 64),
     "int8_wide": (W.FMT_INT8, (128,), 1, 64),
     "fp8_narrow": (W.FMT_FP8, (8, 16), 1, 16),
     "bf16_narrow": (W.FMT_BF16, (8,), 1, 16),
     "int8_narrow": (W.FMT_INT8, (8,), 1, 16),
-    "dots3_mx": (W.FMT_FP8_DOTS3, (16, 64), 1, 16),
+    "dots3_mx": (W.FMT_FP8_DOTS3, (8, 16), 1, 16),
+    "dots3_mx32": (W.FMT_FP8_DOTS3, (32, 64), 1, 32),
     "dsv4_mx": (W.FMT_FP8_DSV4, (16, 64), 2, 16),
 }
 T_GRID = (1, 2, 4, 8, 16, 32, 64, 128, 256)

@@ -17,7 +17,7 @@
 // about 500 registers per lane; two for the exponent-byte kernel's DSv4
 // instantiation), and a, b, f, ap0, ap, bp per kernel class.  The constants
 // were fitted by sparse_top_mla_smla_amd/calibrate_splits.py on one MI355X
-// (256 CUs) over 198 decode shapes and their prefill counterparts; there
+// (256 CUs) over 234 decode shapes and their prefill counterparts; there
 // the pick is on average 0.2% and at most 7.7% slower than the best
 // measured split count.
 #include <hip/hip_runtime.h>
@@ -45,7 +45,8 @@ constexpr KernelClass kInt8Wide{4.027, 4.956, 4.027, 0.0, 14.59, 5.132, 64, fals
 constexpr KernelClass kFp8Narrow{3.509, 4.015, 3.509, 1.068, 13.21, 3.592, 16, false, 1};
 constexpr KernelClass kBf16Narrow{3.608, 4.568, 3.608, 0.0, 14.05, 4.183, 16, false, 1};
 constexpr KernelClass kInt8Narrow{3.363, 4.257, 3.363, 1.179, 12.82, 3.839, 16, false, 1};
-constexpr KernelClass kDots3Mx{3.496, 6.141, 3.496, 5.921, 9.735, 5.983, 16, false, 1};
+constexpr KernelClass kDots3Mx{3.851, 6.568, 3.851, 0.0, 14.10, 6.380, 16, false, 1};
+constexpr KernelClass kDots3Mx32{2.827, 7.815, 2.827, 1.264, 12.92, 7.461, 32, false, 1};
 constexpr KernelClass kDsv4Mx{1.678, 4.843, 1.678, 0.0, 8.484, 4.814, 16, false, 2};
 constexpr double kWriteUsPerMB = 0.186;  // decode's partial stores
 constexpr double kComb0 = 10.57, kComb1 = 0.1856, kComb2 = 0.0;
@@ -61,7 +62,7 @@ const KernelClass* kernel_class(int32_t format, int32_t H) {
     case SMLA_KV_FP8_E4M3_ANY_SCALE: return H > 16 ? &kInt8Wide : &kFp8Narrow;
     case SMLA_KV_BF16: return &kBf16Narrow;
     // rows with exponent-byte scales: their own kernel at any H
-    case SMLA_KV_FP8_E4M3_DOTS3: return &kDots3Mx;
+    case SMLA_KV_FP8_E4M3_DOTS3: return H > 16 ? &kDots3Mx32 : &kDots3Mx;
     case SMLA_KV_FP8_E4M3_DSV4: return &kDsv4Mx;
     default: return nullptr;
   }
