@@ -36,6 +36,8 @@ CASES = {
     "h64_w1024": dict(H=64, topk=1024, ctx=2048, T=3, with_sink=True),
     "h1_w100": dict(H=1, topk=100, causal=False),
     "h8_w513_len": dict(H=8, topk=513, ctx=768, T=7, with_topk_length=True),
+    "h17_w300_sink": dict(H=17, topk=300, T=9, with_sink=True),
+    "h128_w200_len": dict(H=128, topk=200, T=2, with_topk_length=True),
 }
 FMTS = [D3, V4]
 
