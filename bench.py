@@ -208,7 +208,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
-              "(this library has no multi-GPU path; see DESIGN.md for how it would shard)",
+              "(this library has no multi-GPU path: tokens, sequences and heads shard across GPUs with no exchange inside attention)",
               file=sys.stderr)
         sys.exit(2)
 
