@@ -95,8 +95,9 @@ def test_decode_split_and_combine_parity(name, S, fmt):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-def test_empty_lists(fmt):
-    c = make("h8_w513_len", fmt)
+@pytest.mark.parametrize("H", [8, 40])
+def test_empty_lists(fmt, H):
+    c = make("h8_w513_len", fmt, H=H)
     L = c.topk_length.copy()
     L[0], L[3], L[5] = 0, -2, 1
     c.topk_length = L
