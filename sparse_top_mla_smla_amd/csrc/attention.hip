@@ -398,6 +398,8 @@ hipError_t launch_attention(const AttnParams& p, int fmt, bool decode, hipStream
   // many heads over a quantized cache: one workgroup per token for 64 heads
   // (FP8 codes with arbitrary scales run the kernels that fold each row's
   // scale into its partial scores and probabilities, as for INT8)
+  // BF16 rows at any head count: the kernel whose waves split PV over columns
+  if (fmt == FMT_BF16) return launch_attention_bf16(p, decode, s);
   // rows with exponent-byte scales have their own row geometry and widths
   if (fmt == FMT_FP8_DOTS3 || fmt == FMT_FP8_DSV4) return launch_attention_mx(p, fmt, decode, s);
   if ((fmt == FMT_FP8 || fmt == FMT_FP8_NOPE) && p.H > 16) return launch_attention_fp8(p, decode, s);

@@ -1,0 +1,278 @@
+// attention_bf16.hip -- sparse MLA attention over BF16 cache rows (576
+// BF16 values: 512 nope + 64 rope; prefill form and split-KV decode
+// partials) for gfx950, at any head count.
+//
+// What is computed is stated in include/smla.h.  The shapes it serves come
+// from vLLM PR #57673 (Test Result): few native heads (h_q = 8 per rank),
+// d = 512, combined top-k lists of 640 with attn_sink and topk_length, q
+// and out read and written as head views of wider buffers.
+//
+// Work unit: one workgroup (4 waves) per (token, 16-head group, split);
+// tiles of 64 list entries.  The work split follows the exponent-byte
+// kernel (attention_mx.hip): QK over candidates (wave w owns candidates
+// [16w, 16w+16), v_mfma 16x16x32, K rows as A), one running max per head
+// shared by the four waves through LDS, and PV over value columns (wave w
+// owns columns [128w, +128) for all 64 candidates, V^T read with
+// ds_read_b64_tr_b16).  Each wave then holds 32 accumulator registers for
+// O instead of 128, Q stays in registers (72), and the 64-row tile plus the
+// probabilities fit in 79 KB of LDS, so two workgroups share a CU and
+// their per-tile chains overlap.
+//
+// Rows are gathered one tile ahead through registers (four threads per
+// row, 16-byte pieces, one row address per thread and immediate offsets);
+// masked rows are zero-filled so they can never inject NaN into PV.
+// Block order: the head groups of one (token, split) sit on one XCD (the
+// dispatcher deals consecutive workgroups to the 8 XCDs in turn) and meet
+// in its L2.
+#include "device_common.h"
+#include "launch.h"
+#include "lists.h"
+
+namespace smla {
+namespace {
+
+constexpr int TC = 64;        // candidates per tile
+constexpr int NT = 256;       // 4 waves
+constexpr float LAZY = 8.0f;  // log2 units
+constexpr int NXCD = 8;       // XCDs of the chip
+constexpr int ROW = 2 * D_QK;                 // 1152 bytes
+constexpr int LDS_ROW = ROW + 16;             // bank spread
+constexpr int PIECES = ROW / 16;              // 72
+constexpr int NCH = PIECES / 4;               // 18 per thread (4 threads per row)
+constexpr int KS = D_QK / 32;                 // 18 QK k-steps
+constexpr int WCOLS = D_V / 4;                // 128 value columns per wave
+constexpr int NDT = WCOLS / 16;               // 8
+constexpr int P_HEAD = 144;                   // bytes of one head's P row (64 BF16, padded)
+// LDS: tile, P [16 heads][64] BF16, wave maxima / sums [4][16], index stage [3][64] (row addresses)
+constexpr int TILE_BYTES = TC * LDS_ROW;
+constexpr int P_OFF = TILE_BYTES;
+constexpr int RED_OFF = P_OFF + 16 * P_HEAD;
+constexpr int IDX_OFF = RED_OFF + 4 * 16 * 4;
+constexpr int LDS_BYTES = IDX_OFF + 3 * TC * 8;
+static_assert(LDS_BYTES <= 80 * 1024, "two workgroups per CU");
+static_assert(PIECES % 4 == 0, "row pieces");
+
+template <bool DECODE, bool DUAL>
+__global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(AttnParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[LDS_BYTES];
+  uint8_t* tile = smem;
+  uint8_t* pbuf = smem + P_OFF;
+  float* red = reinterpret_cast<float*>(smem + RED_OFF);
+  uint64_t* idx_lds = reinterpret_cast<uint64_t*>(smem + IDX_OFF);  // 0: no candidate
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int lg = lane >> 4;
+  const int lc = lane & 15;
+
+  // workgroup x -> (pair u = t*S + split, head group): x = ((u / 8)*HG + hg)*8 + u % 8
+  const int HG = (p.H + 15) >> 4;
+  const int S = DECODE ? p.num_splits : 1;
+  const int64_t bx = blockIdx.x;
+  const int64_t rest = bx / NXCD;
+  const int hg = (int)(rest % HG);
+  const int64_t u = (rest / HG) * NXCD + bx % NXCD;
+  if (u >= p.T * S) return;  // the last round of pairs may be short (whole workgroup)
+  const int64_t t = u / S;
+  const int split = DECODE ? (int)(u % S) : 0;
+  const int h0 = hg * 16;
+
+  const ListEnds le = list_ends(p, t);
+  const Sources src_lists = sources<DUAL>(p);
+  const int64_t topk_all = (int64_t)p.topk + p.topk2;
+  int64_t j_begin = 0, j_end = topk_all;
+  if (DECODE) {
+    j_begin = (int64_t)split * p.split_w;
+    j_end = j_begin + p.split_w;
+    if (j_end > topk_all) j_end = topk_all;
+  }
+  if (j_end > le.end) j_end = le.end;
+  const int n_tiles = j_end > j_begin ? (int)((j_end - j_begin + TC - 1) / TC) : 0;
+
+  // Q^T as the B operand of S^T = K Q^T: lane holds Q[h0+lc][32ks + 8lg + i]
+  bf16x8 qreg[KS];
+  {
+    const int h = h0 + lc;
+    const bool hv = h < p.H;
+    const uint16_t* qrow = p.q + t * p.q_st + (int64_t)(hv ? h : 0) * p.q_sh + 8 * lg;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint4 v = *reinterpret_cast<const uint4*>(qrow + 32 * ks);
+      qreg[ks] = __builtin_bit_cast(bf16x8, hv ? v : make_uint4(0, 0, 0, 0));
+    }
+  }
+
+  // row address of list position j_begin + 64k + tid, or 0
+  auto load_idx = [&](int k) -> uint64_t {
+    const int64_t j = j_begin + (int64_t)k * TC + tid;
+    uint64_t v = 0;
+    if (j < j_end && in_list<DUAL>(p, le, j)) v = (uint64_t)row_of<DUAL>(src_lists, j, *entry_ptr<DUAL>(src_lists, t, j));
+    return v;
+  };
+
+  // thread tid gathers 16-byte pieces sub + 4r (r < NCH) of tile row tid / 4
+  const int grow = tid >> 2, sub = tid & 3;
+  uint4 stage[NCH];
+  auto issue_rows = [&](int k) {
+    const uint4* row = (const uint4*)idx_lds[(k % 3) * TC + grow];
+    if (row) {
+#pragma unroll
+      for (int r = 0; r < NCH; ++r) stage[r] = row[sub + 4 * r];
+    } else {
+#pragma unroll
+      for (int r = 0; r < NCH; ++r) stage[r] = make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store_rows = [&]() {
+    uint4* dst = reinterpret_cast<uint4*>(tile + grow * LDS_ROW) + sub;
+#pragma unroll
+    for (int r = 0; r < NCH; ++r) dst[4 * r] = stage[r];
+  };
+
+  // running max (log2 units) of head lc, shared by the four waves; this
+  // lane's partial sum over its candidates; O^T for columns
+  // 128*wave + 16dt + 4lg + i of head lc
+  float m_run = -INFINITY;
+  float l_part = 0.0f;
+  f32x4 O[NDT];
+#pragma unroll
+  for (int i = 0; i < NDT; ++i) O[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (n_tiles > 0) {
+    if (tid < TC) {
+      idx_lds[tid] = load_idx(0);
+      if (n_tiles > 1) idx_lds[TC + tid] = load_idx(1);
+    }
+    __syncthreads();
+    issue_rows(0);
+    store_rows();
+    __syncthreads();
+  }
+
+  for (int k = 0; k < n_tiles; ++k) {
+    if (k + 1 < n_tiles) issue_rows(k + 1);
+    uint64_t pend = 0;
+    if (k + 2 < n_tiles && tid < TC) pend = load_idx(k + 2);
+
+    // ---- S^T for candidates 16*wave + (0..15) x heads h0 + (0..15) ----
+    const uint8_t* rowA = tile + (16 * wave + lc) * LDS_ROW + 16 * lg;
+    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {  // two chains
+      const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(rowA + 64 * ks));
+      acc[ks & 1] = mfma_16x16x32(a, qreg[ks], acc[ks & 1]);
+    }
+    const uint64_t* il = idx_lds + (k % 3) * TC + 16 * wave + 4 * lg;
+    float s[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s[i] = il[i] != 0 ? (acc[0][i] + acc[1][i]) * p.scale_log2 : -INFINITY;
+
+    // ---- one running max per head across the four waves ----
+    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (lg == 0) red[wave * 16 + lc] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(red[lc], red[16 + lc]), fmaxf(red[32 + lc], red[48 + lc]));
+    // every wave takes the same decision per head, so the waves' column
+    // slices stay under one max; lanes that do not move multiply by 1
+    const bool need = mx > m_run + LAZY;
+    if (__any(need)) {
+      const float alpha = need ? ((m_run == -INFINITY) ? 0.0f : exp2f(m_run - mx)) : 1.0f;
+      m_run = need ? mx : m_run;
+      l_part *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) O[dt] *= alpha;
+    }
+    float pr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pr[i] = (s[i] == -INFINITY) ? 0.0f : exp2f(s[i] - m_run);
+      l_part += pr[i];
+    }
+    *reinterpret_cast<uint2*>(pbuf + lc * P_HEAD + 2 * (16 * wave + 4 * lg)) =
+        make_uint2(pack_bf16(pr[0], pr[1]), pack_bf16(pr[2], pr[3]));
+    __syncthreads();
+
+    // ---- O^T += V^T P^T over value columns [128*wave, +128) ----
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(pbuf + lc * P_HEAD + 2 * (32 * kc + 8 * lg)));
+      // tr16: lane lc = 4r + b reads rows (32kc + 8lg + 4half + r), columns 4b..4b+3 of the block
+      const uint8_t* rb = tile + (32 * kc + 8 * lg + (lc >> 2)) * LDS_ROW + 2 * WCOLS * wave + 8 * (lc & 3);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const i16x4 r0 = lds_read_tr16(rb + 32 * dt), r1 = lds_read_tr16(rb + 32 * dt + 4 * LDS_ROW);
+        const bf16x8 a = __builtin_bit_cast(bf16x8, make_uint4(__builtin_bit_cast(uint2, r0).x, __builtin_bit_cast(uint2, r0).y,
+                                                               __builtin_bit_cast(uint2, r1).x, __builtin_bit_cast(uint2, r1).y));
+        O[dt] = mfma_16x16x32(a, pb, O[dt]);
+      }
+    }
+
+    if (k + 2 < n_tiles && tid < TC) idx_lds[((k + 2) % 3) * TC + tid] = pend;
+    __syncthreads();
+    if (k + 1 < n_tiles) store_rows();
+    __syncthreads();
+  }
+
+  // ---- per-head sums from the four waves ----
+  float l_w = l_part + __shfl_xor(l_part, 16);
+  l_w += __shfl_xor(l_w, 32);
+  if (lg == 0) red[wave * 16 + lc] = l_w;
+  __syncthreads();
+  const float Lsum = (red[lc] + red[16 + lc]) + (red[32 + lc] + red[48 + lc]);
+  const float M = m_run;
+
+  const int h = h0 + lc;
+  if (h >= p.H) return;
+  const bool empty = !(Lsum > 0.0f);
+  const float lse_v = empty ? -INFINITY : (M + __log2f(Lsum)) * LN2;
+  const int col = WCOLS * wave + 4 * lg;
+  if constexpr (DECODE) {
+    const float inv = empty ? 0.0f : 1.0f / Lsum;
+    float* po = p.part_out + ((t * p.num_splits + split) * p.H + h) * (int64_t)D_V + col;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4*>(po + 16 * dt) = O[dt] * inv;
+    if (wave == 0 && lg == 0) p.part_lse[(t * p.num_splits + split) * p.H + h] = lse_v;
+  } else {
+    float factor;
+    if (empty) {
+      factor = 0.0f;
+    } else if (p.sink) {
+      const float s2 = p.sink[h] * LOG2E;
+      const float ms = fmaxf(M, s2);
+      const float a = exp2f(M - ms);
+      factor = a / (Lsum * a + exp2f(s2 - ms));
+    } else {
+      factor = 1.0f / Lsum;
+    }
+    uint16_t* orow = p.out + t * p.out_st + (int64_t)h * p.out_sh + col;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const f32x4 v = O[dt] * factor;
+      *reinterpret_cast<uint2*>(orow + 16 * dt) = make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
+    }
+    if (wave == 0 && lg == 0) p.lse[t * p.lse_st + h] = lse_v;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attention_bf16(const AttnParams& p, bool decode, hipStream_t s) {
+  const int64_t pairs = p.T * (decode ? p.num_splits : 1);
+  const int64_t blocks = (pairs + NXCD - 1) / NXCD * NXCD * ((p.H + 15) / 16);
+  if (blocks > (int64_t)UINT32_MAX) return hipErrorInvalidConfiguration;
+  dim3 block(NT);
+  dim3 grid((unsigned)blocks);
+  if (p.topk2 > 0) {
+    if (decode) hipLaunchKernelGGL((attn_bf16_kernel<true, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((attn_bf16_kernel<false, true>), grid, block, 0, s, p);
+  } else {
+    if (decode) hipLaunchKernelGGL((attn_bf16_kernel<true, false>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((attn_bf16_kernel<false, false>), grid, block, 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace smla

@@ -74,6 +74,7 @@ hipError_t launch_attention(const AttnParams& p, int fmt, bool decode, hipStream
 hipError_t launch_attention_wide(const AttnParams& p, int fmt, bool decode, hipStream_t s);
 hipError_t launch_attention_fp8(const AttnParams& p, bool decode, hipStream_t s);
 hipError_t launch_attention_mx(const AttnParams& p, int fmt, bool decode, hipStream_t s);
+hipError_t launch_attention_bf16(const AttnParams& p, bool decode, hipStream_t s);
 hipError_t launch_combine(const CombineParams& p, hipStream_t s);
 
 // compute units of the current device (256 when it cannot be queried)
