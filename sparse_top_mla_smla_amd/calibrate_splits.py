@@ -39,7 +39,8 @@ POOL_ROWS = 1 << 20  # 16384 blocks: 584 MiB to 1.2 GiB, beyond the last-level c
 # heads per block).  The narrow kernel's LDS would allow two workgroups per
 # CU, but it holds about 500 registers per lane, so each SIMD runs one of its
 # waves and a CU one workgroup (fitted with 2, the model misses the best
-# split count by up to 26%; with 1, by 4%).  The exponent-byte kernel
+# split count by up to 26%; with 1, by 4%).  BF16 rows run, at every H, the
+# kernel that splits PV over value columns (two workgroups per CU).  The exponent-byte kernel
 # (DOTS3_SWA, DSv4 rows) runs 16 heads per workgroup (DSv4: at any H, two
 # workgroups per CU); DOTS3_SWA rows with more than 16 heads run its
 # 32-head kernel.
@@ -47,7 +48,7 @@ CLASSES = {
     "fp8_wide": (W.FMT_FP8, (64, 128), 1, 64),
     "int8_wide": (W.FMT_INT8, (128,), 1, 64),
     "fp8_narrow": (W.FMT_FP8, (8, 16), 1, 16),
-    "bf16_narrow": (W.FMT_BF16, (8,), 1, 16),
+    "bf16_cols": (W.FMT_BF16, (8, 64), 2, 16),
     "int8_narrow": (W.FMT_INT8, (8,), 1, 16),
     "dots3_mx": (W.FMT_FP8_DOTS3, (8, 16), 1, 16),
     "dots3_mx32": (W.FMT_FP8_DOTS3, (32, 64), 1, 32),
@@ -267,8 +268,10 @@ def main():
         classes = [c for c in args.classes.split(",") if c]
         new_rows = measure(cus, lambda s: print(s, file=sys.stderr, flush=True), classes)
         model = old["model"]
+        # classes no longer in CLASSES (a kernel replaced) leave the fit
+        model["classes"] = {c: v for c, v in model["classes"].items() if c in CLASSES}
         model["classes"].update(fit_classes(new_rows, cus, model))
-        rows = [r for r in old["rows"] if r["cls"] not in classes] + new_rows
+        rows = [r for r in old["rows"] if r["cls"] not in classes and r["cls"] in CLASSES] + new_rows
         res = dict(device=old["device"], compute_units=cus, model=model, pick_error=evaluate(model, rows, cus),
                    rows=rows)
         text = json.dumps(res, indent=1)

@@ -14,12 +14,12 @@
 // with MB the partial buffers (T * S * H * (4 d_v + 4) bytes), waves the
 // rounds of workgroups over the compute units (one workgroup per CU per
 // round: the many-head kernels fill a CU's LDS, and the narrow kernel holds
-// about 500 registers per lane; two for the exponent-byte kernel's DSv4
-// instantiation), and a, b, f, ap0, ap, bp per kernel class.  The constants
-// were fitted by sparse_top_mla_smla_amd/calibrate_splits.py on one MI355X
-// (256 CUs) over 234 decode shapes and their prefill counterparts; there
-// the pick is on average 0.2% and at most 7.7% slower than the best
-// measured split count.
+// about 500 registers per lane; two for the BF16 kernel and the
+// exponent-byte kernel's DSv4 instantiation), and a, b, f, ap0, ap, bp per
+// kernel class.  The constants were fitted by
+// sparse_top_mla_smla_amd/calibrate_splits.py on one MI355X (256 CUs) over
+// 252 decode shapes and their prefill counterparts; there the pick is on
+// average 0.4% and at most 12% slower than the best measured split count.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -43,7 +43,7 @@ struct KernelClass {
 constexpr KernelClass kFp8Wide{14.09, 2.993, 1.554, 2.596, 10.08, 3.211, 64, true, 1};
 constexpr KernelClass kInt8Wide{4.027, 4.956, 4.027, 0.0, 14.59, 5.132, 64, false, 1};
 constexpr KernelClass kFp8Narrow{3.509, 4.015, 3.509, 1.068, 13.21, 3.592, 16, false, 1};
-constexpr KernelClass kBf16Narrow{3.608, 4.568, 3.608, 0.0, 14.05, 4.183, 16, false, 1};
+constexpr KernelClass kBf16Cols{1.982, 3.671, 1.982, 0.0, 10.47, 3.488, 16, false, 2};
 constexpr KernelClass kInt8Narrow{3.363, 4.257, 3.363, 1.179, 12.82, 3.839, 16, false, 1};
 constexpr KernelClass kDots3Mx{3.851, 6.568, 3.851, 0.0, 14.10, 6.380, 16, false, 1};
 constexpr KernelClass kDots3Mx32{2.827, 7.815, 2.827, 1.264, 12.92, 7.461, 32, false, 1};
@@ -60,7 +60,7 @@ const KernelClass* kernel_class(int32_t format, int32_t H) {
     case SMLA_KV_INT8: return H > 16 ? &kInt8Wide : &kInt8Narrow;
     // arbitrary-scale FP8 runs the INT8 many-head kernel's FP8 instantiation
     case SMLA_KV_FP8_E4M3_ANY_SCALE: return H > 16 ? &kInt8Wide : &kFp8Narrow;
-    case SMLA_KV_BF16: return &kBf16Narrow;
+    case SMLA_KV_BF16: return &kBf16Cols;
     // rows with exponent-byte scales: their own kernel at any H
     case SMLA_KV_FP8_E4M3_DOTS3: return H > 16 ? &kDots3Mx32 : &kDots3Mx;
     case SMLA_KV_FP8_E4M3_DSV4: return &kDsv4Mx;
