@@ -97,10 +97,16 @@ def host_cpu_model() -> str:
     return "unknown"
 
 
+# the FP8 many-head kernel's own sources: its file and the headers it includes
+FP8_KERNEL_SOURCES = ("attention_fp8.hip", "device_common.h", "launch.h", "lists.h")
+
+
 def kernel_source_sha() -> str:
+    """Hash of the sources the FP8 prefill kernel is built from; counter
+    figures taken on other sources are not reported."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "sparse_top_mla_smla_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in FP8_KERNEL_SOURCES:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]

@@ -338,7 +338,51 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
   // first wait.
   int32_t pend = -1;  // split (decode) or token (prefill) still to be stored
   float pend_factor = 0.0f, pend_lse = 0.0f;
-  auto store_result = [&](int32_t key, float factor, float lse_v) {
+  // Decode, the workgroup's last split (no gather in flight, every wave past
+  // its last PV, so the raw tile buffers are free): each wave stages its
+  // 32 heads x 128 columns in LDS, 64 columns at a time, and stores whole
+  // 256-byte row pieces of 4 heads per instruction instead of 32-byte
+  // pieces of 32 heads.
+  auto store_partial_staged = [&](int32_t key, float factor) {
+    constexpr int SROW = 68;  // floats per staged head row (64 + 4 pad)
+    static_assert(4 * 32 * SROW * 4 <= TILE, "four waves' staging fits one raw buffer");
+    float* st = reinterpret_cast<float*>(w < 4 ? raw0 : raw1) + (w & 3) * 32 * SROW;
+    const int64_t td = blockIdx.x;
+    float* pbase = p.part_out + ((td * p.num_splits + key) * p.H + h0 + 32 * hh) * (int64_t)D_V + 128 * g;
+    const int rh = lane >> 4;       // head offset of this lane's reads
+    const int rc = 4 * (lane & 15); // column of this lane's reads
+    // (LDS accesses of one wave complete in order, so each read sees the
+    // writes before it, and the next half's writes follow those reads)
+    auto put = [&](const f32x16& o, int d) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *reinterpret_cast<f32x4*>(st + l32 * SROW + 32 * d + 8 * q4 + 4 * hi) =
+            f32x4{o[4 * q4] * factor, o[4 * q4 + 1] * factor, o[4 * q4 + 2] * factor, o[4 * q4 + 3] * factor};
+    };
+    auto drain = [&](int half) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int hl = 4 * i + rh;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(st + hl * SROW + rc);
+        if (h0 + 32 * hh + hl < p.H) *reinterpret_cast<f32x4*>(pbase + (int64_t)hl * D_V + 64 * half + rc) = v;
+      }
+    };
+    put(O[0], 0);
+    put(O[1], 1);
+    drain(0);
+    put(O[2], 0);
+    put(O[3], 1);
+    drain(1);
+  };
+  auto store_result = [&](int32_t key, float factor, float lse_v, bool staged) {
+    if constexpr (DECODE) {
+      if (staged) {
+        store_partial_staged(key, factor);
+        const int h = h0 + 32 * hh + l32;
+        if (g == 0 && hi == 0 && h < p.H) p.part_lse[((int64_t)blockIdx.x * p.num_splits + key) * p.H + h] = lse_v;
+        return;
+      }
+    }
     const int h = h0 + 32 * hh + l32;
     if (h >= p.H) return;
     if constexpr (DECODE) {
@@ -368,7 +412,7 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
   // prefill: the workgroup's tokens with an empty list (O is still zero)
   if (!DECODE && p.topk_length) {
     for (int32_t tt = blockIdx.x; tt < p.T; tt += t_stride)
-      if (token_lists(tt).end == 0) store_result(tt, 0.0f, -INFINITY);
+      if (token_lists(tt).end == 0) store_result(tt, 0.0f, -INFINITY, false);
   }
 
   if (cur.t >= 0) {
@@ -407,7 +451,7 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
     }
     if (w == 0 && nn.t >= 0) issue_idx(Buf<B>{}, nn);
     if (pend >= 0) {
-      store_result(pend, pend_factor, pend_lse);
+      store_result(pend, pend_factor, pend_lse, false);
       pend = -1;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
@@ -605,7 +649,8 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
       pend_lse = lse_v;
       return;
     }
-    store_result(key, factor, lse_v);
+    // (decode without a next tile: nothing is gathered any more)
+    store_result(key, factor, lse_v, DECODE);
     // every wave has read lsum before anyone writes it again
     lds_barrier();
 #pragma unroll
