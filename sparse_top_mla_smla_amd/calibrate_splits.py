@@ -36,7 +36,9 @@ from sparse_top_mla_smla_amd import workloads as W
 POOL_ROWS = 1 << 20  # 16384 blocks: 584 MiB to 1.2 GiB, beyond the last-level cache
 
 # kernel class -> (format, head counts measured, workgroups per CU per round,
-# heads per block).  The narrow kernel's LDS would allow two workgroups per
+# heads per block).  FP8 and INT8 rows with more than 16 heads run the same
+# many-head kernel ("wide": 64 heads per workgroup); the classes differ in
+# the codes' conversion.  The narrow kernel's LDS would allow two workgroups per
 # CU, but it holds about 500 registers per lane, so each SIMD runs one of its
 # waves and a CU one workgroup (fitted with 2, the model misses the best
 # split count by up to 26%; with 1, by 4%).  BF16 rows run, at every H, the
@@ -46,7 +48,7 @@ POOL_ROWS = 1 << 20  # 16384 blocks: 584 MiB to 1.2 GiB, beyond the last-level c
 # 32-head kernel.
 CLASSES = {
     "fp8_wide": (W.FMT_FP8, (64, 128), 1, 64),
-    "int8_wide": (W.FMT_INT8, (128,), 1, 64),
+    "int8_wide": (W.FMT_INT8, (64, 128), 1, 64),
     "fp8_narrow": (W.FMT_FP8, (8, 16), 1, 16),
     "bf16_cols": (W.FMT_BF16, (8, 64), 2, 16),
     "int8_narrow": (W.FMT_INT8, (8,), 1, 16),
@@ -54,6 +56,9 @@ CLASSES = {
     "dots3_mx32": (W.FMT_FP8_DOTS3, (32, 64), 1, 32),
     "dsv4_mx": (W.FMT_FP8_DSV4, (16, 64), 2, 16),
 }
+# classes whose decode workgroups run consecutive splits of a token (the
+# many-head kernel of FP8 and INT8 rows)
+GROUPED = ("fp8_wide", "int8_wide")
 T_GRID = (1, 2, 4, 8, 16, 32, 64, 128, 256)
 T_PREFILL_ONLY = (1024,)  # several tokens per workgroup in the persistent prefill
 TOPK_GRID = (512, 2048)
@@ -72,7 +77,7 @@ def geometry(cls: str, T: int, H: int, topk: int, S: int, cus: int):
     hb = (H + hpb - 1) // hpb
     w = smla.split_width(topk, S)
     spb = 1
-    if cls.endswith("_wide") and cls.startswith("fp8"):
+    if cls in GROUPED:
         spb = max(1, min(S, (T * hb * S) // cus))
     blocks = T * hb * ((S + spb - 1) // spb)
     waves = math.ceil(blocks / (cus * occ))

@@ -395,16 +395,13 @@ static hipError_t launch_fmt(const AttnParams& p, bool decode, hipStream_t s) {
 }
 
 hipError_t launch_attention(const AttnParams& p, int fmt, bool decode, hipStream_t s) {
-  // many heads over a quantized cache: one workgroup per token for 64 heads
-  // (FP8 codes with arbitrary scales run the kernels that fold each row's
-  // scale into its partial scores and probabilities, as for INT8)
   // BF16 rows at any head count: the kernel whose waves split PV over columns
   if (fmt == FMT_BF16) return launch_attention_bf16(p, decode, s);
   // rows with exponent-byte scales have their own row geometry and widths
   if (fmt == FMT_FP8_DOTS3 || fmt == FMT_FP8_DSV4) return launch_attention_mx(p, fmt, decode, s);
-  if ((fmt == FMT_FP8 || fmt == FMT_FP8_NOPE) && p.H > 16) return launch_attention_fp8(p, decode, s);
-  if (fmt == FMT_INT8 && p.H > 16) return launch_attention_wide(p, fmt, decode, s);
-  if (fmt == FMT_FP8_ANY && p.H > 16) return launch_attention_wide(p, FMT_FP8, decode, s);
+  // many heads over a quantized cache (FP8 with any scales, with or without
+  // rope, and INT8): one workgroup per token for 64 heads
+  if (p.H > 16) return launch_attention_fp8(p, fmt, decode, s);
   switch (fmt) {
     case FMT_BF16: return launch_fmt<FMT_BF16>(p, decode, s);
     case FMT_FP8:

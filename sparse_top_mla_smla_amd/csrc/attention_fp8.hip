@@ -1,6 +1,7 @@
 // attention_fp8.hip -- sparse MLA attention for many heads (H > 16) over the
-// FP8 paged latent cache (656-byte rows with power-of-two per-128 scales),
-// prefill form and split-KV decode partials.
+// quantized 656-byte paged latent rows: FP8 with power-of-two per-128 scales
+// (DSv3.2, with or without rope dimensions), FP8 with arbitrary scales
+// (GLM_NSA) and INT8 -- prefill form and split-KV decode partials.
 //
 // What is computed is stated in include/smla.h.  This kernel serves the
 // shapes of the AppMana release note's fused prefill (T=1024, ctx 16384,
@@ -15,6 +16,10 @@
 // is converted, and the nope and rope parts of a score accumulate in one
 // MFMA accumulator.  A valid row whose scale is not a positive power of two
 // turns its token's output into NaN instead of a silently wrong result.
+// Rows with arbitrary scales (FP8 amax/448, INT8 amax/127) convert their
+// codes exactly with scale 1; a latent group's 128 nope columns are exactly
+// one scale tile, so its partial score is multiplied by each candidate's
+// scale of that tile before the rope product is added.
 //
 // All products use v_mfma_f32_32x32x16_bf16.  Eight waves; wave w = g + 4hh
 // works on latent group g (0..3) and head half hh (heads [32hh, 32hh+32)).
@@ -44,6 +49,8 @@
 // buffer or the initial zero fill and contribute nothing, because their
 // probabilities are exactly 0 (this needs the pool's codes and rope values
 // to be finite, as the cache writer produces them).
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 #include "lists.h"
@@ -65,6 +72,18 @@ __device__ __forceinline__ bf16x8 cvt8(uint32_t c0, uint32_t c1, float scale) {
   const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c1, scale, true);
   return __builtin_bit_cast(bf16x8, make_uint4(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
                                                __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d)));
+}
+
+// eight codes of the given row format as BF16: e4m3 times a power-of-two
+// scale (exact), or int8 (exact, |code| <= 127; the scale is applied later)
+template <int CODES>
+__device__ __forceinline__ bf16x8 codes8(uint32_t c0, uint32_t c1, float scale) {
+  if constexpr (CODES == FMT_INT8) {
+    const uint2 lo = int8x4_to_bf16x4(c0), hi = int8x4_to_bf16x4(c1);
+    return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+  } else {
+    return cvt8(c0, c1, scale);
+  }
 }
 
 __device__ __forceinline__ void global_to_lds_16(const void* src, void* lds_wave_base) {
@@ -144,8 +163,12 @@ struct Buf {
 }  // namespace f8
 
 // NOPE: rows without rope dimensions (q rows of 512 values, row padding never
-// gathered or read)
-template <bool DECODE, bool DUAL, bool NOPE>
+// gathered or read).  CODES: FMT_FP8 (power-of-two scales, applied while
+// converting), FMT_FP8_ANY or FMT_INT8 (arbitrary scales: the codes convert
+// exactly with scale 1, each latent group's partial score is multiplied by
+// its candidates' scales before the rope part is added, and P' folds the
+// scales into PV as for FMT_FP8).
+template <bool DECODE, bool DUAL, bool NOPE, int CODES>
 __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
   using namespace f8;
   // Separate LDS objects, and a loop unrolled by two so that every access
@@ -465,17 +488,27 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[c2][i] = 0.0f;
       const int row = 32 * c2 + l32;
-      const float sc = *reinterpret_cast<const float*>(raw + CK_SCALE * CS + row * 16 + 4 * g);
-      // a scale that is not a positive power of two makes this row's rope
-      // operand NaN: the row's scores become NaN for every head (rows that
-      // are not loaded are masked out by selection later)
-      const bool bad = !is_pow2_scale(sc);
+      // power-of-two scales: applied while converting.  A scale that is not
+      // a positive power of two makes this row's rope operand NaN: the row's
+      // scores become NaN for every head (rows that are not loaded are
+      // masked out by selection later)
+      const float sc = CODES == FMT_FP8 ? *reinterpret_cast<const float*>(raw + CK_SCALE * CS + row * 16 + 4 * g) : 1.0f;
+      const bool bad = CODES == FMT_FP8 && !is_pow2_scale(sc);
       const uint8_t* kp = raw + (8 * g + hi) * CS + row * 16;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const uint4 c16 = *reinterpret_cast<const uint4*>(kp + 2 * j * CS);
-        acc[c2] = mfma_32x32x16(cvt8(c16.x, c16.y, sc), qn[2 * j], acc[c2]);
-        acc[c2] = mfma_32x32x16(cvt8(c16.z, c16.w, sc), qn[2 * j + 1], acc[c2]);
+        acc[c2] = mfma_32x32x16(codes8<CODES>(c16.x, c16.y, sc), qn[2 * j], acc[c2]);
+        acc[c2] = mfma_32x32x16(codes8<CODES>(c16.z, c16.w, sc), qn[2 * j + 1], acc[c2]);
+      }
+      if constexpr (CODES != FMT_FP8) {
+        // arbitrary scales: accumulator element 4a + b is candidate
+        // 32c2 + 8a + 4hi + b, whose scale of group g is read here
+        const uint8_t* sp = raw + CK_SCALE * CS + (32 * c2 + 4 * hi) * 16 + 4 * g;
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+          for (int b = 0; b < 4; ++b) acc[c2][4 * a + b] *= *reinterpret_cast<const float*>(sp + (8 * a + b) * 16);
       }
       uint4 r16 = make_uint4(0, 0, 0, 0);  // rows without rope dimensions: 0
       if constexpr (!NOPE) r16 = *reinterpret_cast<const uint4*>(raw + (CK_ROPE + 2 * g + hi) * CS + row * 16);
@@ -610,7 +643,7 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
-        O[dt] = mfma_32x32x16(cvt8((uint32_t)v8[ks][dt][0], (uint32_t)v8[ks][dt][1], 1.0f),
+        O[dt] = mfma_32x32x16(codes8<CODES>((uint32_t)v8[ks][dt][0], (uint32_t)v8[ks][dt][1], 1.0f),
                               __builtin_bit_cast(bf16x8, pb[ks]), O[dt]);
   };
   // ---- end of a split (decode) or of a token (prefill): per-head sum over
@@ -721,7 +754,7 @@ int fp8_prefill_blocks(int64_t T, int32_t H, int compute_units) {
   return (int)(T < per ? T : per);
 }
 
-hipError_t launch_attention_fp8(const AttnParams& p, bool decode, hipStream_t s) {
+hipError_t launch_attention_fp8(const AttnParams& p, int fmt, bool decode, hipStream_t s) {
   AttnParams q = p;
   const int cus = device_compute_units();
   q.splits_per_block = decode ? fp8_splits_per_block(p.T, p.H, p.num_splits, cus) : 1;
@@ -729,17 +762,21 @@ hipError_t launch_attention_fp8(const AttnParams& p, bool decode, hipStream_t s)
   dim3 grid(decode ? (unsigned)q.T : (unsigned)fp8_prefill_blocks(q.T, q.H, cus), (unsigned)((q.H + 63) / 64),
             decode ? (unsigned)((q.num_splits + q.splits_per_block - 1) / q.splits_per_block) : 1u);
   const bool dual = q.topk2 > 0;
-  if (q.nope) {
-    if (decode && dual) hipLaunchKernelGGL((attn_fp8_kernel<true, true, true>), grid, block, 0, s, q);
-    else if (decode) hipLaunchKernelGGL((attn_fp8_kernel<true, false, true>), grid, block, 0, s, q);
-    else if (dual) hipLaunchKernelGGL((attn_fp8_kernel<false, true, true>), grid, block, 0, s, q);
-    else hipLaunchKernelGGL((attn_fp8_kernel<false, false, true>), grid, block, 0, s, q);
-  } else {
-    if (decode && dual) hipLaunchKernelGGL((attn_fp8_kernel<true, true, false>), grid, block, 0, s, q);
-    else if (decode) hipLaunchKernelGGL((attn_fp8_kernel<true, false, false>), grid, block, 0, s, q);
-    else if (dual) hipLaunchKernelGGL((attn_fp8_kernel<false, true, false>), grid, block, 0, s, q);
-    else hipLaunchKernelGGL((attn_fp8_kernel<false, false, false>), grid, block, 0, s, q);
-  }
+  // one instantiation per (row format, form, list count)
+  auto go = [&](auto nope, auto codes) {
+    constexpr bool N = decltype(nope)::value;
+    constexpr int C = decltype(codes)::value;
+    if (decode && dual) hipLaunchKernelGGL((attn_fp8_kernel<true, true, N, C>), grid, block, 0, s, q);
+    else if (decode) hipLaunchKernelGGL((attn_fp8_kernel<true, false, N, C>), grid, block, 0, s, q);
+    else if (dual) hipLaunchKernelGGL((attn_fp8_kernel<false, true, N, C>), grid, block, 0, s, q);
+    else hipLaunchKernelGGL((attn_fp8_kernel<false, false, N, C>), grid, block, 0, s, q);
+  };
+  using yes = std::true_type;
+  using no = std::false_type;
+  if (fmt == FMT_FP8_NOPE) go(yes{}, std::integral_constant<int, FMT_FP8>{});
+  else if (fmt == FMT_FP8_ANY) go(no{}, std::integral_constant<int, FMT_FP8_ANY>{});
+  else if (fmt == FMT_INT8) go(no{}, std::integral_constant<int, FMT_INT8>{});
+  else go(no{}, std::integral_constant<int, FMT_FP8>{});
   return hipGetLastError();
 }
 

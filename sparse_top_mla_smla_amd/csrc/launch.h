@@ -71,8 +71,7 @@ struct CombineParams {
 
 hipError_t launch_quantize(const QuantParams& p, int fmt, hipStream_t s);
 hipError_t launch_attention(const AttnParams& p, int fmt, bool decode, hipStream_t s);
-hipError_t launch_attention_wide(const AttnParams& p, int fmt, bool decode, hipStream_t s);
-hipError_t launch_attention_fp8(const AttnParams& p, bool decode, hipStream_t s);
+hipError_t launch_attention_fp8(const AttnParams& p, int fmt, bool decode, hipStream_t s);
 hipError_t launch_attention_mx(const AttnParams& p, int fmt, bool decode, hipStream_t s);
 hipError_t launch_attention_bf16(const AttnParams& p, bool decode, hipStream_t s);
 hipError_t launch_combine(const CombineParams& p, hipStream_t s);

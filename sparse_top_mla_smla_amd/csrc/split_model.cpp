@@ -18,7 +18,7 @@
 // exponent-byte kernel's DSv4 instantiation), and a, b, f, ap0, ap, bp per
 // kernel class.  The constants were fitted by
 // sparse_top_mla_smla_amd/calibrate_splits.py on one MI355X (256 CUs) over
-// 252 decode shapes and their prefill counterparts; there the pick is on
+// 270 decode shapes and their prefill counterparts; there the pick is on
 // average 0.4% and at most 12% slower than the best measured split count.
 #include <hip/hip_runtime.h>
 
@@ -41,7 +41,7 @@ struct KernelClass {
 
 // fitted constants (microseconds), MI355X
 constexpr KernelClass kFp8Wide{14.09, 2.993, 1.554, 2.596, 10.08, 3.211, 64, true, 1};
-constexpr KernelClass kInt8Wide{4.027, 4.956, 4.027, 0.0, 14.59, 5.132, 64, false, 1};
+constexpr KernelClass kInt8Wide{15.41, 4.063, 0.4882, 6.079, 9.363, 3.945, 64, true, 1};
 constexpr KernelClass kFp8Narrow{3.509, 4.015, 3.509, 1.068, 13.21, 3.592, 16, false, 1};
 constexpr KernelClass kBf16Cols{1.982, 3.671, 1.982, 0.0, 10.47, 3.488, 16, false, 2};
 constexpr KernelClass kInt8Narrow{3.363, 4.257, 3.363, 1.179, 12.82, 3.839, 16, false, 1};
@@ -58,7 +58,8 @@ const KernelClass* kernel_class(int32_t format, int32_t H) {
     case SMLA_KV_FP8_E4M3:
     case SMLA_KV_FP8_E4M3_NOPE: return H > 16 ? &kFp8Wide : &kFp8Narrow;
     case SMLA_KV_INT8: return H > 16 ? &kInt8Wide : &kInt8Narrow;
-    // arbitrary-scale FP8 runs the INT8 many-head kernel's FP8 instantiation
+    // arbitrary-scale FP8 rows convert and scale like INT8 rows in the
+    // many-head kernel (their conversion is cheaper: the INT8 constants bound it)
     case SMLA_KV_FP8_E4M3_ANY_SCALE: return H > 16 ? &kInt8Wide : &kFp8Narrow;
     case SMLA_KV_BF16: return &kBf16Cols;
     // rows with exponent-byte scales: their own kernel at any H
