@@ -436,6 +436,54 @@ def main():
                 "hbm_frac_end_to_end": round(dbytes / ((dec_us + comb_us) * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
             }
 
+        def time_decode_graph(S):
+            """decode + combine captured in one HIP graph per index set
+            (stream capture through torch.cuda.graph) and replayed in turn."""
+            po = torch.empty((dc.T, S, dc.H, D_V), dtype=torch.float32, device=dev)
+            pl = torch.empty((dc.T, S, dc.H), dtype=torch.float32, device=dev)
+            graphs = []
+            side = torch.cuda.Stream()
+            for ix in idx_sets:
+                def run(ix=ix):
+                    smla.decode(dq, dpool, ix, S, sm_scale=float(dc.sm_scale), part_out=po, part_lse=pl)
+                    smla.combine(po, pl, out=dout, lse=dlse)
+
+                side.wait_stream(torch.cuda.current_stream())
+                with torch.cuda.stream(side):
+                    run()
+                torch.cuda.current_stream().wait_stream(side)
+                torch.cuda.synchronize()
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    run()
+                graphs.append(g)
+            for i in range(args.warmup):
+                graphs[i % len(graphs)].replay()
+            torch.cuda.synchronize()
+            t1 = time.perf_counter()
+            for i in range(dsteps):
+                graphs[i % len(graphs)].replay()
+            torch.cuda.synchronize()
+            wall = (time.perf_counter() - t1) * 1e6 / dsteps
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(dsteps)]
+            for i in range(dsteps):
+                evs[i][0].record(stream)
+                graphs[i % len(graphs)].replay()
+                evs[i][1].record(stream)
+            torch.cuda.synchronize()
+            per = [a.elapsed_time(b) * 1e3 for a, b in evs]
+            us = float(np.mean(per))
+            del graphs
+            return {
+                "num_splits": S,
+                "us_per_call": round(wall, 3),
+                "graph_us": round(us, 3),
+                "graph_us_median_p10_p90": [round(v, 3) for v in pct(per)],
+                "gathered_kv_GBps_end_to_end": round(dbytes / (us * 1e-6) / 1e9, 2),
+                "hbm_frac_end_to_end": round(dbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            }
+
         S = dc.num_splits
         result["decode"] = {
             "workload": f"fp8 split-KV decode {dc.T} seqs x 1 query, ctx {dc.ctx}, H={dc.H}, "
@@ -453,6 +501,11 @@ def main():
         print(f"[bench] decode {d8['decode_kernel_us']:.2f} us + combine {d8['combine_kernel_us']:.2f} us (S={S}); "
               f"model S={Sm}: {model['decode_kernel_us']:.2f} + {model['combine_kernel_us']:.2f} us",
               file=sys.stderr, flush=True)
+        gr = time_decode_graph(Sm)
+        gr["workload"] = "the same batch at the model's split count, decode + combine replayed as one HIP graph"
+        result["decode"]["graph"] = gr
+        print(f"[bench] decode + combine as a HIP graph (S={Sm}): {gr['graph_us']:.2f} us, "
+              f"{gr['us_per_call']:.2f} us per call", file=sys.stderr, flush=True)
         if ipool8 is not None:
             Si = smla.decode_num_splits(dc.T, dc.H, dc.topk, W.FMT_INT8)
             i8d = time_decode(Si, ipool8)
