@@ -86,6 +86,14 @@ __device__ __forceinline__ bf16x8 codes8(uint32_t c0, uint32_t c1, float scale) 
   }
 }
 
+// x - bf16(x) and y - bf16(y) as a BF16 pair, given hi = the BF16 pair of
+// (x, y) (x in the low half)
+__device__ __forceinline__ uint32_t bf16_rest(float x, float y, uint32_t hi) {
+  const float xh = __builtin_bit_cast(float, hi << 16);
+  const float yh = __builtin_bit_cast(float, hi & 0xFFFF0000u);
+  return pack_bf16(x - xh, y - yh);
+}
+
 __device__ __forceinline__ void global_to_lds_16(const void* src, void* lds_wave_base) {
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
                                    (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
@@ -154,6 +162,11 @@ constexpr int GPARTS = 3;                    // the pieces are issued in three p
 constexpr int RECV_FLOATS = 8 * 3 * 2 * 64 * 4;  // [8 owners][3 senders][2][64 lanes][4] f32
 constexpr int PS = 72;                       // P' row stride (bf16): [4 groups][64 heads][PS], aliases recv
 static_assert(4 * 64 * PS * 2 <= RECV_FLOATS * 4, "P' must fit in the partial-exchange buffer");
+constexpr int GS = 64 * PS * 2;              // bytes of one P' group slot
+// rows with arbitrary scales keep P' as a BF16 pair (high part and rest),
+// eight slots
+constexpr int RECV_FLOATS_ARB = 8 * GS / 4;
+static_assert(RECV_FLOATS_ARB >= RECV_FLOATS, "the pair buffer holds the partial exchange");
 constexpr float TAU = 8.0f;
 
 template <int V>
@@ -177,7 +190,7 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
   // gather into the other buffer, and does not wait for that gather.
   __shared__ __attribute__((aligned(16))) uint8_t raw0[TILE];
   __shared__ __attribute__((aligned(16))) uint8_t raw1[TILE];
-  __shared__ __attribute__((aligned(16))) float recv[RECV_FLOATS];
+  __shared__ __attribute__((aligned(16))) float recv[CODES == FMT_FP8 ? RECV_FLOATS : RECV_FLOATS_ARB];
   __shared__ __attribute__((aligned(16))) float maxb[4 * 64];   // [4 groups][64 heads]
   __shared__ __attribute__((aligned(16))) int32_t valid[2 * TC];  // [buffer][row]: row was loaded
   __shared__ __attribute__((aligned(16))) int32_t idx0[TC];       // index list of even tiles
@@ -593,7 +606,27 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
         w1[gg] = u32x2{pack_bf16(s1[0] * sc1[0][gg], s1[1] * sc1[1][gg]), pack_bf16(s1[2] * sc1[2][gg], s1[3] * sc1[3][gg])};
       }
       const uint32_t pw = lds_addr(pq + hl * PS + 16 * g + 4 * hi);
-      constexpr int GS = 64 * PS * 2;  // bytes per group
+      if constexpr (CODES != FMT_FP8) {
+        // an arbitrary scale makes P x scale inexact in BF16: the rest goes
+        // to slots 4..7 and PV adds both parts (a power-of-two scale only
+        // shifts the exponent)
+        u32x2 r0[4], r1[4];
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+          r0[gg] = u32x2{bf16_rest(s0[0] * sc0[0][gg], s0[1] * sc0[1][gg], w0[gg][0]),
+                         bf16_rest(s0[2] * sc0[2][gg], s0[3] * sc0[3][gg], w0[gg][1])};
+          r1[gg] = u32x2{bf16_rest(s1[0] * sc1[0][gg], s1[1] * sc1[1][gg], w1[gg][0]),
+                         bf16_rest(s1[2] * sc1[2][gg], s1[3] * sc1[3][gg], w1[gg][1])};
+        }
+        b64_store<4 * GS>(pw, r0[0]);
+        b64_store<4 * GS + 16>(pw, r1[0]);
+        b64_store<5 * GS>(pw, r0[1]);
+        b64_store<5 * GS + 16>(pw, r1[1]);
+        b64_store<6 * GS>(pw, r0[2]);
+        b64_store<6 * GS + 16>(pw, r1[2]);
+        b64_store<7 * GS>(pw, r0[3]);
+        b64_store<7 * GS + 16>(pw, r1[3]);
+      }
       b64_store<0>(pw, w0[0]);
       b64_store<16>(pw, w1[0]);
       b64_store<GS>(pw, w0[1]);
@@ -631,20 +664,30 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
     pb[1] = b128_issue<32>(pa);
     pb[2] = b128_issue<64>(pa);
     pb[3] = b128_issue<96>(pa);
-    // one wait for all twenty reads; the empty statement after it (volatile
-    // statements keep their order) carries the dependency to the rest
+    u32x4 pr[4];  // the rest of P'_g (rows with arbitrary scales only)
+    if constexpr (CODES != FMT_FP8) {
+      pr[0] = b128_issue<4 * GS>(pa);
+      pr[1] = b128_issue<4 * GS + 32>(pa);
+      pr[2] = b128_issue<4 * GS + 64>(pa);
+      pr[3] = b128_issue<4 * GS + 96>(pa);
+    }
+    // one wait for all the reads; the empty statements after it (volatile
+    // statements keep their order) carry the dependency to the rest
     asm volatile("s_waitcnt lgkmcnt(0)"
                  : "+v"(v8[0][0]), "+v"(v8[0][1]), "+v"(v8[0][2]), "+v"(v8[0][3]), "+v"(v8[1][0]), "+v"(v8[1][1]),
                    "+v"(v8[1][2]), "+v"(v8[1][3]), "+v"(pb[0]), "+v"(pb[1]), "+v"(pb[2]), "+v"(pb[3]));
+    if constexpr (CODES != FMT_FP8) asm volatile("" : "+v"(pr[0]), "+v"(pr[1]), "+v"(pr[2]), "+v"(pr[3]));
     asm volatile(""
                  : "+v"(v8[2][0]), "+v"(v8[2][1]), "+v"(v8[2][2]), "+v"(v8[2][3]), "+v"(v8[3][0]), "+v"(v8[3][1]),
                    "+v"(v8[3][2]), "+v"(v8[3][3]));
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-        O[dt] = mfma_32x32x16(codes8<CODES>((uint32_t)v8[ks][dt][0], (uint32_t)v8[ks][dt][1], 1.0f),
-                              __builtin_bit_cast(bf16x8, pb[ks]), O[dt]);
+      for (int dt = 0; dt < 4; ++dt) {
+        const bf16x8 v = codes8<CODES>((uint32_t)v8[ks][dt][0], (uint32_t)v8[ks][dt][1], 1.0f);
+        O[dt] = mfma_32x32x16(v, __builtin_bit_cast(bf16x8, pb[ks]), O[dt]);
+        if constexpr (CODES != FMT_FP8) O[dt] = mfma_32x32x16(v, __builtin_bit_cast(bf16x8, pr[ks]), O[dt]);
+      }
   };
   // ---- end of a split (decode) or of a token (prefill): per-head sum over
   // the four groups, normalization; the result is stored now, or by the
