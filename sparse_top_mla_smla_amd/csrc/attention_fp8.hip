@@ -700,7 +700,6 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
     }
     lds_barrier();
     const int hl = 32 * hh + l32;
-    const int h = h0 + hl;
     const float Ls = (lsum[hl] + lsum[64 + hl]) + (lsum[128 + hl] + lsum[192 + hl]);
     const float M = m_run;
     const bool empty = !(Ls > 0.0f);

@@ -41,7 +41,7 @@ struct KernelClass {
 
 // fitted constants (microseconds), MI355X
 constexpr KernelClass kFp8Wide{14.09, 2.993, 1.554, 2.596, 10.08, 3.211, 64, true, 1};
-constexpr KernelClass kInt8Wide{15.41, 4.063, 0.4882, 6.079, 9.363, 3.945, 64, true, 1};
+constexpr KernelClass kInt8Wide{14.71, 4.805, 0.1746, 2.036, 10.82, 4.751, 64, true, 1};
 constexpr KernelClass kFp8Narrow{3.509, 4.015, 3.509, 1.068, 13.21, 3.592, 16, false, 1};
 constexpr KernelClass kBf16Cols{1.982, 3.671, 1.982, 0.0, 10.47, 3.488, 16, false, 2};
 constexpr KernelClass kInt8Narrow{3.363, 4.257, 3.363, 1.179, 12.82, 3.839, 16, false, 1};
