@@ -606,6 +606,9 @@ def main():
         fkv = bf16(fc.kv)
         fpool = smla.KVPool.empty(fc.num_blocks, W.FMT_BF16, device=dev)
         smla.quantize_kv(fkv, torch.from_numpy(fc.slots).to(dev), fpool)
+        # the same latent rows in an FP8 pool (656-byte rows)
+        f8pool = smla.KVPool.empty(fc.num_blocks, W.FMT_FP8, device=dev)
+        smla.quantize_kv(fkv, torch.from_numpy(fc.slots).to(dev), f8pool)
         del fkv
         fidx = torch.from_numpy(fc.idx_buf).to(dev)[:, : fc.topk]
         ftl = torch.from_numpy(fc.topk_length).to(dev)
@@ -636,7 +639,22 @@ def main():
             "speedup_vs_64_heads": round(pct(t64)[0] / f_med[0], 3),
         }
         print(f"[bench] fewhead {f_med[0]:.1f} us (64 heads: {pct(t64)[0]:.1f} us)", file=sys.stderr, flush=True)
-        del fq, fpool, fidx, ftl, fout, flse
+
+        def few8():
+            smla.prefill(fq[:, :fc.H], f8pool, fidx, topk_length=ftl, sink=fsink64[:fc.H],
+                         sm_scale=float(fc.sm_scale), out=fout[:, :fc.H], lse=flse[:, :fc.H])
+
+        few8()
+        t8f = pct(event_times_us(torch, few8, iters, stream))
+        f8bytes = frows * W.ROW_BYTES[W.FMT_FP8]
+        result["fewhead"]["fp8_rows"] = {
+            "workload": "the same prefill over an FP8 pool written from the same latent rows (656-byte rows)",
+            "kernel_us_median_p10_p90": [round(v, 3) for v in t8f],
+            "gathered_kv_bytes": f8bytes,
+            "gathered_kv_GBps": round(f8bytes / (t8f[0] * 1e-6) / 1e9, 2),
+        }
+        print(f"[bench] fewhead over FP8 rows {t8f[0]:.1f} us", file=sys.stderr, flush=True)
+        del fq, fpool, f8pool, fidx, ftl, fout, flse
         torch.cuda.empty_cache()
         # INT8, 128 heads, narrowed index view
         ic = W.c5_int8()

@@ -396,7 +396,9 @@ static hipError_t launch_fmt(const AttnParams& p, bool decode, hipStream_t s) {
 
 hipError_t launch_attention(const AttnParams& p, int fmt, bool decode, hipStream_t s) {
   // BF16 rows at any head count: the kernel whose waves split PV over columns
-  if (fmt == FMT_BF16) return launch_attention_bf16(p, decode, s);
+  if (fmt == FMT_BF16) return launch_attention_bf16(p, FMT_BF16, decode, s);
+  // FP8 rows with power-of-two scales and few heads: the same kernel
+  if (fmt == FMT_FP8 && p.H <= 16) return launch_attention_bf16(p, FMT_FP8, decode, s);
   // rows with exponent-byte scales have their own row geometry and widths
   if (fmt == FMT_FP8_DOTS3 || fmt == FMT_FP8_DSV4) return launch_attention_mx(p, fmt, decode, s);
   // many heads over a quantized cache (FP8 with any scales, with or without

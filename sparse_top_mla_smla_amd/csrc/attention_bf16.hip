@@ -1,6 +1,7 @@
 // attention_bf16.hip -- sparse MLA attention over BF16 cache rows (576
-// BF16 values: 512 nope + 64 rope; prefill form and split-KV decode
-// partials) for gfx950, at any head count.
+// BF16 values: 512 nope + 64 rope) at any head count, and over FP8 rows with
+// power-of-two scales (656 bytes) with 16 or fewer heads; prefill form and
+// split-KV decode partials, for gfx950.
 //
 // What is computed is stated in include/smla.h.  The shapes it serves come
 // from vLLM PR #57673 (Test Result): few native heads (h_q = 8 per rank),
@@ -18,12 +19,19 @@
 // probabilities fit in 79 KB of LDS, so two workgroups share a CU and
 // their per-tile chains overlap.
 //
+// FP8 rows: QK converts each lane's eight codes with the row's scale of
+// their 128 columns (exact in BF16 for a power of two), PV reads V^T from
+// the codes with ds_read_b64_tr_b8 and converts them with scale 1, and P is
+// written in four versions, P times each wave's column scale.
+//
 // Rows are gathered one tile ahead through registers (four threads per
 // row, 16-byte pieces, one row address per thread and immediate offsets);
 // masked rows are zero-filled so they can never inject NaN into PV.
 // Block order: the head groups of one (token, split) sit on one XCD (the
 // dispatcher deals consecutive workgroups to the 8 XCDs in turn) and meet
 // in its L2.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 #include "lists.h"
@@ -35,26 +43,56 @@ constexpr int TC = 64;        // candidates per tile
 constexpr int NT = 256;       // 4 waves
 constexpr float LAZY = 8.0f;  // log2 units
 constexpr int NXCD = 8;       // XCDs of the chip
-constexpr int ROW = 2 * D_QK;                 // 1152 bytes
-constexpr int LDS_ROW = ROW + 16;             // bank spread
-constexpr int PIECES = ROW / 16;              // 72
-constexpr int NCH = PIECES / 4;               // 18 per thread (4 threads per row)
 constexpr int KS = D_QK / 32;                 // 18 QK k-steps
+constexpr int KS_NOPE = D_NOPE / 32;          // 16 of them over the nope part
 constexpr int WCOLS = D_V / 4;                // 128 value columns per wave
 constexpr int NDT = WCOLS / 16;               // 8
 constexpr int P_HEAD = 144;                   // bytes of one head's P row (64 BF16, padded)
-// LDS: tile, P [16 heads][64] BF16, wave maxima / sums [4][16], index stage [3][64] (row addresses)
-constexpr int TILE_BYTES = TC * LDS_ROW;
-constexpr int P_OFF = TILE_BYTES;
-constexpr int RED_OFF = P_OFF + 16 * P_HEAD;
-constexpr int IDX_OFF = RED_OFF + 4 * 16 * 4;
-constexpr int LDS_BYTES = IDX_OFF + 3 * TC * 8;
-static_assert(LDS_BYTES <= 80 * 1024, "two workgroups per CU");
-static_assert(PIECES % 4 == 0, "row pieces");
 
-template <bool DECODE, bool DUAL>
+// Row geometry.  BF16 rows: 576 BF16 values.  FP8 rows: 512 e4m3 codes, four
+// FP32 power-of-two scales (one per 128 columns), 64 BF16 rope values; P is
+// kept in four versions, P times the scale of each wave's value columns.
+template <int FMT>
+struct Cols {
+  static constexpr int ROW = FMT == FMT_BF16 ? 2 * D_QK : D_NOPE + 16 + 2 * D_ROPE;  // 1152 or 656
+  static constexpr int LDS_ROW = ROW + 16;    // bank spread
+  static constexpr int PIECES = ROW / 16;     // 72 or 41
+  static constexpr int NCH = (PIECES + 3) / 4;  // pieces per thread (4 threads per row)
+  static constexpr int VERSIONS = FMT == FMT_BF16 ? 1 : 4;
+  // LDS: tile, P [versions][16 heads][64] BF16, wave maxima / sums [4][16],
+  // index stage [3][64] (row addresses)
+  static constexpr int TILE_BYTES = TC * LDS_ROW;
+  static constexpr int P_OFF = TILE_BYTES;
+  static constexpr int RED_OFF = P_OFF + VERSIONS * 16 * P_HEAD;
+  static constexpr int IDX_OFF = RED_OFF + 4 * 16 * 4;
+  static constexpr int LDS_BYTES = IDX_OFF + 3 * TC * 8;
+  static_assert(LDS_BYTES <= 80 * 1024, "two workgroups per CU");
+};
+
+// eight e4m3 codes (bytes of c0 then c1, in order) times a power-of-two
+// scale, exactly, as BF16
+__device__ __forceinline__ bf16x8 e4m3x8_scaled(uint32_t c0, uint32_t c1, float scale) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c0, scale, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c0, scale, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c1, scale, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c1, scale, true);
+  return __builtin_bit_cast(bf16x8, make_uint4(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+                                               __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d)));
+}
+
+// a positive, finite, normal power of two
+__device__ __forceinline__ bool pow2_scale(float s) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, s);
+  const uint32_t e = b >> 23;
+  return (b & 0x007FFFFFu) == 0 && e != 0 && e < 255;
+}
+
+template <bool DECODE, bool DUAL, int FMT>
 __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[LDS_BYTES];
+  using G = Cols<FMT>;
+  constexpr int LDS_ROW = G::LDS_ROW, PIECES = G::PIECES, NCH = G::NCH;
+  constexpr int P_OFF = G::P_OFF, RED_OFF = G::RED_OFF, IDX_OFF = G::IDX_OFF;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[G::LDS_BYTES];
   uint8_t* tile = smem;
   uint8_t* pbuf = smem + P_OFF;
   float* red = reinterpret_cast<float*>(smem + RED_OFF);
@@ -118,7 +156,8 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(AttnParams p) {
     const uint4* row = (const uint4*)idx_lds[(k % 3) * TC + grow];
     if (row) {
 #pragma unroll
-      for (int r = 0; r < NCH; ++r) stage[r] = row[sub + 4 * r];
+      for (int r = 0; r < NCH; ++r)
+        if (PIECES % 4 == 0 || sub + 4 * r < PIECES) stage[r] = row[sub + 4 * r];
     } else {
 #pragma unroll
       for (int r = 0; r < NCH; ++r) stage[r] = make_uint4(0, 0, 0, 0);
@@ -127,7 +166,8 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(AttnParams p) {
   auto store_rows = [&]() {
     uint4* dst = reinterpret_cast<uint4*>(tile + grow * LDS_ROW) + sub;
 #pragma unroll
-    for (int r = 0; r < NCH; ++r) dst[4 * r] = stage[r];
+    for (int r = 0; r < NCH; ++r)
+      if (PIECES % 4 == 0 || sub + 4 * r < PIECES) dst[4 * r] = stage[r];
   };
 
   // running max (log2 units) of head lc, shared by the four waves; this
@@ -156,12 +196,32 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(AttnParams p) {
     if (k + 2 < n_tiles && tid < TC) pend = load_idx(k + 2);
 
     // ---- S^T for candidates 16*wave + (0..15) x heads h0 + (0..15) ----
-    const uint8_t* rowA = tile + (16 * wave + lc) * LDS_ROW + 16 * lg;
+    const uint8_t* rowA = tile + (16 * wave + lc) * LDS_ROW;
     f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    if constexpr (FMT == FMT_BF16) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {  // two chains
-      const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(rowA + 64 * ks));
-      acc[ks & 1] = mfma_16x16x32(a, qreg[ks], acc[ks & 1]);
+      for (int ks = 0; ks < KS; ++ks) {  // two chains
+        const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(rowA + 16 * lg + 64 * ks));
+        acc[ks & 1] = mfma_16x16x32(a, qreg[ks], acc[ks & 1]);
+      }
+    } else {
+      // codes times the row's power-of-two scale of their 128 columns, exact
+      // in BF16; a scale that is not a positive power of two makes the row's
+      // rope operand NaN, so the row's scores are NaN for every head (a row
+      // that is not loaded holds zeros and is masked out below)
+      const f32x4 sc = *reinterpret_cast<const f32x4*>(rowA + D_NOPE);
+      const bool bad = !(pow2_scale(sc[0]) && pow2_scale(sc[1]) && pow2_scale(sc[2]) && pow2_scale(sc[3]));
+#pragma unroll
+      for (int ks = 0; ks < KS_NOPE; ++ks) {
+        const uint2 c8 = *reinterpret_cast<const uint2*>(rowA + 32 * ks + 8 * lg);
+        acc[ks & 1] = mfma_16x16x32(e4m3x8_scaled(c8.x, c8.y, sc[ks / 4]), qreg[ks], acc[ks & 1]);
+      }
+#pragma unroll
+      for (int ks = KS_NOPE; ks < KS; ++ks) {
+        uint4 r = *reinterpret_cast<const uint4*>(rowA + D_NOPE + 16 + 64 * (ks - KS_NOPE) + 16 * lg);
+        if (bad) r = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
+        acc[ks & 1] = mfma_16x16x32(__builtin_bit_cast(bf16x8, r), qreg[ks], acc[ks & 1]);
+      }
     }
     const uint64_t* il = idx_lds + (k % 3) * TC + 16 * wave + 4 * lg;
     float s[4];
@@ -191,22 +251,48 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(AttnParams p) {
       pr[i] = (s[i] == -INFINITY) ? 0.0f : exp2f(s[i] - m_run);
       l_part += pr[i];
     }
-    *reinterpret_cast<uint2*>(pbuf + lc * P_HEAD + 2 * (16 * wave + 4 * lg)) =
-        make_uint2(pack_bf16(pr[0], pr[1]), pack_bf16(pr[2], pr[3]));
+    if constexpr (FMT == FMT_BF16) {
+      *reinterpret_cast<uint2*>(pbuf + lc * P_HEAD + 2 * (16 * wave + 4 * lg)) =
+          make_uint2(pack_bf16(pr[0], pr[1]), pack_bf16(pr[2], pr[3]));
+    } else {
+      // version v: P times the scale of value columns [128v, +128), exact
+      // (a power of two), for the wave that owns those columns
+      f32x4 scl[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        scl[i] = *reinterpret_cast<const f32x4*>(tile + (16 * wave + 4 * lg + i) * LDS_ROW + D_NOPE);
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        *reinterpret_cast<uint2*>(pbuf + v * 16 * P_HEAD + lc * P_HEAD + 2 * (16 * wave + 4 * lg)) =
+            make_uint2(pack_bf16(pr[0] * scl[0][v], pr[1] * scl[1][v]), pack_bf16(pr[2] * scl[2][v], pr[3] * scl[3][v]));
+    }
     __syncthreads();
 
     // ---- O^T += V^T P^T over value columns [128*wave, +128) ----
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
-      const bf16x8 pb = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(pbuf + lc * P_HEAD + 2 * (32 * kc + 8 * lg)));
-      // tr16: lane lc = 4r + b reads rows (32kc + 8lg + 4half + r), columns 4b..4b+3 of the block
-      const uint8_t* rb = tile + (32 * kc + 8 * lg + (lc >> 2)) * LDS_ROW + 2 * WCOLS * wave + 8 * (lc & 3);
+      const uint8_t* pv = pbuf + (G::VERSIONS > 1 ? wave : 0) * 16 * P_HEAD;
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(pv + lc * P_HEAD + 2 * (32 * kc + 8 * lg)));
+      if constexpr (FMT == FMT_BF16) {
+        // tr16: lane lc = 4r + b reads rows (32kc + 8lg + 4half + r), columns 4b..4b+3 of the block
+        const uint8_t* rb = tile + (32 * kc + 8 * lg + (lc >> 2)) * LDS_ROW + 2 * WCOLS * wave + 8 * (lc & 3);
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const i16x4 r0 = lds_read_tr16(rb + 32 * dt), r1 = lds_read_tr16(rb + 32 * dt + 4 * LDS_ROW);
-        const bf16x8 a = __builtin_bit_cast(bf16x8, make_uint4(__builtin_bit_cast(uint2, r0).x, __builtin_bit_cast(uint2, r0).y,
-                                                               __builtin_bit_cast(uint2, r1).x, __builtin_bit_cast(uint2, r1).y));
-        O[dt] = mfma_16x16x32(a, pb, O[dt]);
+        for (int dt = 0; dt < NDT; ++dt) {
+          const i16x4 r0 = lds_read_tr16(rb + 32 * dt), r1 = lds_read_tr16(rb + 32 * dt + 4 * LDS_ROW);
+          const bf16x8 a = __builtin_bit_cast(bf16x8, make_uint4(__builtin_bit_cast(uint2, r0).x, __builtin_bit_cast(uint2, r0).y,
+                                                                 __builtin_bit_cast(uint2, r1).x, __builtin_bit_cast(uint2, r1).y));
+          O[dt] = mfma_16x16x32(a, pb, O[dt]);
+        }
+      } else {
+        // tr8: lane lc = 2r + b reads row 32kc + 8lg + r (a candidate), bytes
+        // 8b..8b+7 of a 16-column piece; lane lc receives column lc of the
+        // 8 rows.  The codes convert with scale 1 (the scale is in P).
+        const uint8_t* rb = tile + (32 * kc + 8 * lg + (lc >> 1)) * LDS_ROW + WCOLS * wave + 8 * (lc & 1);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const i32x2 c = lds_read_tr8(rb + 16 * dt);
+          O[dt] = mfma_16x16x32(e4m3x8_scaled((uint32_t)c[0], (uint32_t)c[1], 1.0f), pb, O[dt]);
+        }
       }
     }
 
@@ -259,19 +345,24 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(AttnParams p) {
 
 }  // namespace
 
-hipError_t launch_attention_bf16(const AttnParams& p, bool decode, hipStream_t s) {
+hipError_t launch_attention_bf16(const AttnParams& p, int fmt, bool decode, hipStream_t s) {
   const int64_t pairs = p.T * (decode ? p.num_splits : 1);
   const int64_t blocks = (pairs + NXCD - 1) / NXCD * NXCD * ((p.H + 15) / 16);
   if (blocks > (int64_t)UINT32_MAX) return hipErrorInvalidConfiguration;
   dim3 block(NT);
   dim3 grid((unsigned)blocks);
-  if (p.topk2 > 0) {
-    if (decode) hipLaunchKernelGGL((attn_bf16_kernel<true, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((attn_bf16_kernel<false, true>), grid, block, 0, s, p);
-  } else {
-    if (decode) hipLaunchKernelGGL((attn_bf16_kernel<true, false>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((attn_bf16_kernel<false, false>), grid, block, 0, s, p);
-  }
+  auto go = [&](auto f) {
+    constexpr int F = decltype(f)::value;
+    if (p.topk2 > 0) {
+      if (decode) hipLaunchKernelGGL((attn_bf16_kernel<true, true, F>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((attn_bf16_kernel<false, true, F>), grid, block, 0, s, p);
+    } else {
+      if (decode) hipLaunchKernelGGL((attn_bf16_kernel<true, false, F>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((attn_bf16_kernel<false, false, F>), grid, block, 0, s, p);
+    }
+  };
+  if (fmt == FMT_FP8) go(std::integral_constant<int, FMT_FP8>{});
+  else go(std::integral_constant<int, FMT_BF16>{});
   return hipGetLastError();
 }
 

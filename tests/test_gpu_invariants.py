@@ -147,11 +147,12 @@ def test_constant_column_gives_one_minus_sink_share():
 
 
 
-def test_fp8_non_power_of_two_scale_gives_nan():
-    # FP8 scales must be powers of two; with H > 16 a selected row whose
-    # scale for columns [128, 256) is 3.0 makes its token's output NaN, and
-    # tokens that do not select the row are unchanged
-    c = case(W.FMT_FP8, H=64, topk=256)
+@pytest.mark.parametrize("H", [8, 64])
+def test_fp8_non_power_of_two_scale_gives_nan(H):
+    # FP8 scales must be powers of two; a selected row whose scale for
+    # columns [128, 256) is 3.0 makes its token's output NaN, and tokens that
+    # do not select the row are unchanged (both kernels that serve FP8 rows)
+    c = case(W.FMT_FP8, H=H, topk=256)
     d = Dev(c)
     o1, l1 = pre(d)
     slot = int(c.indices[0, 0])
