@@ -38,23 +38,18 @@ POOL_ROWS = 1 << 20  # 16384 blocks: 584 MiB to 1.2 GiB, beyond the last-level c
 # kernel class -> (format, head counts measured, workgroups per CU per round,
 # heads per block).  FP8 and INT8 rows with more than 16 heads run the same
 # many-head kernel ("wide": 64 heads per workgroup); the classes differ in
-# the codes' conversion.  The narrow kernel's LDS would allow two workgroups per
-# CU, but it holds about 500 registers per lane, so each SIMD runs one of its
-# waves and a CU one workgroup (fitted with 2, the model misses the best
-# split count by up to 26%; with 1, by 4%); it serves few heads of INT8,
-# arbitrary-scale FP8 and rope-less FP8 rows.  BF16 rows at every H, and FP8
-# rows with power-of-two scales and 16 or fewer heads, run the kernel that
-# splits PV over value columns (two workgroups per CU).  The exponent-byte kernel
-# (DOTS3_SWA, DSv4 rows) runs 16 heads per workgroup (DSv4: at any H, two
-# workgroups per CU); DOTS3_SWA rows with more than 16 heads run its
+# the codes' conversion.  With 16 or fewer heads, and for BF16 rows at every
+# H, the kernel that splits PV over value columns runs (two workgroups per
+# CU); arbitrary-scale FP8 rows share the INT8 class.  The exponent-byte
+# kernel (DOTS3_SWA, DSv4 rows) runs 16 heads per workgroup (DSv4: at any H,
+# two workgroups per CU); DOTS3_SWA rows with more than 16 heads run its
 # 32-head kernel.
 CLASSES = {
     "fp8_wide": (W.FMT_FP8, (64, 128), 1, 64),
     "int8_wide": (W.FMT_INT8, (64, 128), 1, 64),
-    "fp8_narrow": (W.FMT_FP8_ANY, (8, 16), 1, 16),
     "fp8_cols": (W.FMT_FP8, (8, 16), 2, 16),
+    "int8_cols": (W.FMT_INT8, (8, 16), 2, 16),
     "bf16_cols": (W.FMT_BF16, (8, 64), 2, 16),
-    "int8_narrow": (W.FMT_INT8, (8,), 1, 16),
     "dots3_mx": (W.FMT_FP8_DOTS3, (8, 16), 1, 16),
     "dots3_mx32": (W.FMT_FP8_DOTS3, (32, 64), 1, 32),
     "dsv4_mx": (W.FMT_FP8_DSV4, (16, 64), 2, 16),

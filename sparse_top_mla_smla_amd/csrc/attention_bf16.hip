@@ -1,7 +1,8 @@
 // attention_bf16.hip -- sparse MLA attention over BF16 cache rows (576
-// BF16 values: 512 nope + 64 rope) at any head count, and over FP8 rows with
-// power-of-two scales (656 bytes) with 16 or fewer heads; prefill form and
-// split-KV decode partials, for gfx950.
+// BF16 values: 512 nope + 64 rope) at any head count, and over the 656-byte
+// quantized rows (FP8 with power-of-two or arbitrary scales, rope-less FP8,
+// INT8) with 16 or fewer heads; prefill form and split-KV decode partials,
+// for gfx950.
 //
 // What is computed is stated in include/smla.h.  The shapes it serves come
 // from vLLM PR #57673 (Test Result): few native heads (h_q = 8 per rank),
@@ -19,10 +20,14 @@
 // probabilities fit in 79 KB of LDS, so two workgroups share a CU and
 // their per-tile chains overlap.
 //
-// FP8 rows: QK converts each lane's eight codes with the row's scale of
-// their 128 columns (exact in BF16 for a power of two), PV reads V^T from
-// the codes with ds_read_b64_tr_b8 and converts them with scale 1, and P is
-// written in four versions, P times each wave's column scale.
+// Quantized rows: PV reads V^T from the codes with ds_read_b64_tr_b8 and
+// converts them with scale 1, and P is written in four versions, P times
+// each wave's column scale.  With power-of-two scales QK converts each
+// lane's codes with the row's scale of their 128 columns (exact in BF16);
+// with arbitrary scales (INT8, GLM_NSA FP8) the codes convert exactly with
+// scale 1, each 128-column group accumulates apart and is scaled per
+// candidate, and each P version is a BF16 pair (the rounded value and the
+// rest) so that the scale's rounding does not reach the output.
 //
 // Rows are gathered one tile ahead through registers (four threads per
 // row, 16-byte pieces, one row address per thread and immediate offsets);
@@ -49,16 +54,21 @@ constexpr int WCOLS = D_V / 4;                // 128 value columns per wave
 constexpr int NDT = WCOLS / 16;               // 8
 constexpr int P_HEAD = 144;                   // bytes of one head's P row (64 BF16, padded)
 
-// Row geometry.  BF16 rows: 576 BF16 values.  FP8 rows: 512 e4m3 codes, four
-// FP32 power-of-two scales (one per 128 columns), 64 BF16 rope values; P is
-// kept in four versions, P times the scale of each wave's value columns.
+// Row geometry.  BF16 rows: 576 BF16 values.  Quantized rows (656 bytes):
+// 512 codes, four FP32 scales (one per 128 columns), 64 BF16 rope values
+// (padding in rope-less rows, never gathered).  P is kept in four versions,
+// P times the scale of each wave's value columns; with arbitrary scales each
+// version is a BF16 pair (the rounded value and the rest), eight slots.
 template <int FMT>
 struct Cols {
+  static constexpr bool QUANT = FMT != FMT_BF16;
+  static constexpr bool POW2 = FMT == FMT_FP8 || FMT == FMT_FP8_NOPE;  // scales applied while converting
+  static constexpr bool ROPE = FMT != FMT_FP8_NOPE;
   static constexpr int ROW = FMT == FMT_BF16 ? 2 * D_QK : D_NOPE + 16 + 2 * D_ROPE;  // 1152 or 656
   static constexpr int LDS_ROW = ROW + 16;    // bank spread
-  static constexpr int PIECES = ROW / 16;     // 72 or 41
+  static constexpr int PIECES = ROPE ? ROW / 16 : (D_NOPE + 16) / 16;  // gathered: 72, 41 or 33
   static constexpr int NCH = (PIECES + 3) / 4;  // pieces per thread (4 threads per row)
-  static constexpr int VERSIONS = FMT == FMT_BF16 ? 1 : 4;
+  static constexpr int VERSIONS = !QUANT ? 1 : POW2 ? 4 : 8;
   // LDS: tile, P [versions][16 heads][64] BF16, wave maxima / sums [4][16],
   // index stage [3][64] (row addresses)
   static constexpr int TILE_BYTES = TC * LDS_ROW;
@@ -78,6 +88,26 @@ __device__ __forceinline__ bf16x8 e4m3x8_scaled(uint32_t c0, uint32_t c1, float 
   const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c1, scale, true);
   return __builtin_bit_cast(bf16x8, make_uint4(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
                                                __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d)));
+}
+
+// x - bf16(x) and y - bf16(y) as a BF16 pair, given hi = the BF16 pair of
+// (x, y) (x in the low half)
+__device__ __forceinline__ uint32_t bf16_pair_rest(float x, float y, uint32_t hi) {
+  const float xh = __builtin_bit_cast(float, hi << 16);
+  const float yh = __builtin_bit_cast(float, hi & 0xFFFF0000u);
+  return pack_bf16(x - xh, y - yh);
+}
+
+// eight codes of a quantized row as BF16 (exact): e4m3 times a power-of-two
+// scale, or int8 (scale applied later)
+template <int FMT>
+__device__ __forceinline__ bf16x8 codes8(uint32_t c0, uint32_t c1, float scale) {
+  if constexpr (FMT == FMT_INT8) {
+    const uint2 lo = int8x4_to_bf16x4(c0), hi = int8x4_to_bf16x4(c1);
+    return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+  } else {
+    return e4m3x8_scaled(c0, c1, scale);
+  }
 }
 
 // a positive, finite, normal power of two
@@ -136,6 +166,11 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(AttnParams p) {
     const uint16_t* qrow = p.q + t * p.q_st + (int64_t)(hv ? h : 0) * p.q_sh + 8 * lg;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
+      // (rope-less rows: q rows hold 512 values and the rope k-steps are 0)
+      if (!G::ROPE && ks >= KS_NOPE) {
+        qreg[ks] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+        continue;
+      }
       const uint4 v = *reinterpret_cast<const uint4*>(qrow + 32 * ks);
       qreg[ks] = __builtin_bit_cast(bf16x8, hv ? v : make_uint4(0, 0, 0, 0));
     }
@@ -204,23 +239,47 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(AttnParams p) {
         const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(rowA + 16 * lg + 64 * ks));
         acc[ks & 1] = mfma_16x16x32(a, qreg[ks], acc[ks & 1]);
       }
-    } else {
+    } else if constexpr (G::POW2) {
       // codes times the row's power-of-two scale of their 128 columns, exact
       // in BF16; a scale that is not a positive power of two makes the row's
-      // rope operand NaN, so the row's scores are NaN for every head (a row
+      // first operand NaN, so the row's scores are NaN for every head (a row
       // that is not loaded holds zeros and is masked out below)
       const f32x4 sc = *reinterpret_cast<const f32x4*>(rowA + D_NOPE);
       const bool bad = !(pow2_scale(sc[0]) && pow2_scale(sc[1]) && pow2_scale(sc[2]) && pow2_scale(sc[3]));
 #pragma unroll
       for (int ks = 0; ks < KS_NOPE; ++ks) {
         const uint2 c8 = *reinterpret_cast<const uint2*>(rowA + 32 * ks + 8 * lg);
-        acc[ks & 1] = mfma_16x16x32(e4m3x8_scaled(c8.x, c8.y, sc[ks / 4]), qreg[ks], acc[ks & 1]);
+        bf16x8 a = e4m3x8_scaled(c8.x, c8.y, sc[ks / 4]);
+        if (ks == 0 && bad) a = __builtin_bit_cast(bf16x8, make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u));
+        acc[ks & 1] = mfma_16x16x32(a, qreg[ks], acc[ks & 1]);
+      }
+      if constexpr (G::ROPE) {
+#pragma unroll
+        for (int ks = KS_NOPE; ks < KS; ++ks) {
+          const uint4 r = *reinterpret_cast<const uint4*>(rowA + D_NOPE + 16 + 64 * (ks - KS_NOPE) + 16 * lg);
+          acc[ks & 1] = mfma_16x16x32(__builtin_bit_cast(bf16x8, r), qreg[ks], acc[ks & 1]);
+        }
+      }
+    } else {
+      // arbitrary scales: the codes convert exactly with scale 1, each
+      // 128-column group accumulates apart, and S = sum_g scale(c, g) N_g +
+      // rope; accumulator element i is candidate 16*wave + 4lg + i
+      f32x4 accg[4] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f},
+                       f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int ks = 0; ks < KS_NOPE; ++ks) {
+        const uint2 c8 = *reinterpret_cast<const uint2*>(rowA + 32 * ks + 8 * lg);
+        accg[ks / 4] = mfma_16x16x32(codes8<FMT>(c8.x, c8.y, 1.0f), qreg[ks], accg[ks / 4]);
       }
 #pragma unroll
       for (int ks = KS_NOPE; ks < KS; ++ks) {
-        uint4 r = *reinterpret_cast<const uint4*>(rowA + D_NOPE + 16 + 64 * (ks - KS_NOPE) + 16 * lg);
-        if (bad) r = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
-        acc[ks & 1] = mfma_16x16x32(__builtin_bit_cast(bf16x8, r), qreg[ks], acc[ks & 1]);
+        const uint4 r = *reinterpret_cast<const uint4*>(rowA + D_NOPE + 16 + 64 * (ks - KS_NOPE) + 16 * lg);
+        acc[1] = mfma_16x16x32(__builtin_bit_cast(bf16x8, r), qreg[ks], acc[1]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x4 sci = *reinterpret_cast<const f32x4*>(tile + (16 * wave + 4 * lg + i) * LDS_ROW + D_NOPE);
+        acc[0][i] = (sci[0] * accg[0][i] + sci[1] * accg[1][i]) + (sci[2] * accg[2][i] + sci[3] * accg[3][i]);
       }
     }
     const uint64_t* il = idx_lds + (k % 3) * TC + 16 * wave + 4 * lg;
@@ -255,23 +314,29 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(AttnParams p) {
       *reinterpret_cast<uint2*>(pbuf + lc * P_HEAD + 2 * (16 * wave + 4 * lg)) =
           make_uint2(pack_bf16(pr[0], pr[1]), pack_bf16(pr[2], pr[3]));
     } else {
-      // version v: P times the scale of value columns [128v, +128), exact
-      // (a power of two), for the wave that owns those columns
+      // version v: P times the scale of value columns [128v, +128) (exact for
+      // a power of two), for the wave that owns those columns; with
+      // arbitrary scales the rest of the rounding goes to version 4 + v
       f32x4 scl[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         scl[i] = *reinterpret_cast<const f32x4*>(tile + (16 * wave + 4 * lg + i) * LDS_ROW + D_NOPE);
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
-        *reinterpret_cast<uint2*>(pbuf + v * 16 * P_HEAD + lc * P_HEAD + 2 * (16 * wave + 4 * lg)) =
-            make_uint2(pack_bf16(pr[0] * scl[0][v], pr[1] * scl[1][v]), pack_bf16(pr[2] * scl[2][v], pr[3] * scl[3][v]));
+      for (int v = 0; v < 4; ++v) {
+        const float x0 = pr[0] * scl[0][v], x1 = pr[1] * scl[1][v], x2 = pr[2] * scl[2][v], x3 = pr[3] * scl[3][v];
+        const uint2 hi = make_uint2(pack_bf16(x0, x1), pack_bf16(x2, x3));
+        *reinterpret_cast<uint2*>(pbuf + v * 16 * P_HEAD + lc * P_HEAD + 2 * (16 * wave + 4 * lg)) = hi;
+        if constexpr (!G::POW2)
+          *reinterpret_cast<uint2*>(pbuf + (4 + v) * 16 * P_HEAD + lc * P_HEAD + 2 * (16 * wave + 4 * lg)) =
+              make_uint2(bf16_pair_rest(x0, x1, hi.x), bf16_pair_rest(x2, x3, hi.y));
+      }
     }
     __syncthreads();
 
     // ---- O^T += V^T P^T over value columns [128*wave, +128) ----
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
-      const uint8_t* pv = pbuf + (G::VERSIONS > 1 ? wave : 0) * 16 * P_HEAD;
+      const uint8_t* pv = pbuf + (G::QUANT ? wave : 0) * 16 * P_HEAD;
       const bf16x8 pb = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(pv + lc * P_HEAD + 2 * (32 * kc + 8 * lg)));
       if constexpr (FMT == FMT_BF16) {
         // tr16: lane lc = 4r + b reads rows (32kc + 8lg + 4half + r), columns 4b..4b+3 of the block
@@ -288,10 +353,15 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(AttnParams p) {
         // 8b..8b+7 of a 16-column piece; lane lc receives column lc of the
         // 8 rows.  The codes convert with scale 1 (the scale is in P).
         const uint8_t* rb = tile + (32 * kc + 8 * lg + (lc >> 1)) * LDS_ROW + WCOLS * wave + 8 * (lc & 1);
+        bf16x8 pl;  // the rest of P' (arbitrary scales)
+        if constexpr (!G::POW2)
+          pl = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(pv + 4 * 16 * P_HEAD + lc * P_HEAD + 2 * (32 * kc + 8 * lg)));
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
           const i32x2 c = lds_read_tr8(rb + 16 * dt);
-          O[dt] = mfma_16x16x32(e4m3x8_scaled((uint32_t)c[0], (uint32_t)c[1], 1.0f), pb, O[dt]);
+          const bf16x8 a = codes8<FMT>((uint32_t)c[0], (uint32_t)c[1], 1.0f);
+          O[dt] = mfma_16x16x32(a, pb, O[dt]);
+          if constexpr (!G::POW2) O[dt] = mfma_16x16x32(a, pl, O[dt]);
         }
       }
     }
@@ -361,8 +431,13 @@ hipError_t launch_attention_bf16(const AttnParams& p, int fmt, bool decode, hipS
       else hipLaunchKernelGGL((attn_bf16_kernel<false, false, F>), grid, block, 0, s, p);
     }
   };
-  if (fmt == FMT_FP8) go(std::integral_constant<int, FMT_FP8>{});
-  else go(std::integral_constant<int, FMT_BF16>{});
+  switch (fmt) {
+    case FMT_FP8: go(std::integral_constant<int, FMT_FP8>{}); break;
+    case FMT_FP8_NOPE: go(std::integral_constant<int, FMT_FP8_NOPE>{}); break;
+    case FMT_FP8_ANY: go(std::integral_constant<int, FMT_FP8_ANY>{}); break;
+    case FMT_INT8: go(std::integral_constant<int, FMT_INT8>{}); break;
+    default: go(std::integral_constant<int, FMT_BF16>{}); break;
+  }
   return hipGetLastError();
 }
 

@@ -74,8 +74,9 @@ hipError_t launch_attention(const AttnParams& p, int fmt, bool decode, hipStream
 hipError_t launch_attention_fp8(const AttnParams& p, int fmt, bool decode, hipStream_t s);
 hipError_t launch_attention_mx(const AttnParams& p, int fmt, bool decode, hipStream_t s);
 // the kernel whose waves split QK over candidates and PV over value columns
-// (two workgroups per CU): BF16 rows at any head count, FP8 rows with
-// power-of-two scales and 16 or fewer heads
+// (two workgroups per CU): BF16 rows at any head count, and the 656-byte
+// quantized rows (FP8 with any scales, with or without rope, INT8) with 16
+// or fewer heads
 hipError_t launch_attention_bf16(const AttnParams& p, int fmt, bool decode, hipStream_t s);
 hipError_t launch_combine(const CombineParams& p, hipStream_t s);
 

@@ -13,14 +13,13 @@
 //   prefill = ap0 + waves_p * (ap + bp * tiles_per_token)
 // with MB the partial buffers (T * S * H * (4 d_v + 4) bytes), waves the
 // rounds of workgroups over the compute units (one workgroup per CU per
-// round: the many-head kernels fill a CU's LDS, and the narrow kernel holds
-// about 500 registers per lane; two for the column-split kernel (BF16
-// rows, and FP8 rows with 16 or fewer heads) and the exponent-byte kernel's
-// DSv4 instantiation), and a, b, f, ap0, ap, bp per
+// round: the many-head kernels fill a CU's LDS; two for the column-split
+// kernel (16 or fewer heads, and BF16 rows at any head count) and the
+// exponent-byte kernel's DSv4 instantiation), and a, b, f, ap0, ap, bp per
 // kernel class.  The constants were fitted by
 // sparse_top_mla_smla_amd/calibrate_splits.py on one MI355X (256 CUs) over
-// 306 decode shapes and their prefill counterparts; there the pick is on
-// average 0.4% and at most 12% slower than the best measured split count.
+// 288 decode shapes and their prefill counterparts; there the pick is on
+// average 0.5% and at most 12% slower than the best measured split count.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -43,10 +42,9 @@ struct KernelClass {
 // fitted constants (microseconds), MI355X
 constexpr KernelClass kFp8Wide{14.09, 2.993, 1.554, 2.596, 10.08, 3.211, 64, true, 1};
 constexpr KernelClass kInt8Wide{14.71, 4.805, 0.1746, 2.036, 10.82, 4.751, 64, true, 1};
-constexpr KernelClass kFp8Narrow{3.509, 4.015, 3.509, 1.068, 13.21, 3.592, 16, false, 1};
 constexpr KernelClass kBf16Cols{1.982, 3.671, 1.982, 0.0, 10.47, 3.488, 16, false, 2};
 constexpr KernelClass kFp8Cols{3.377, 3.673, 3.377, 0.0, 12.60, 3.767, 16, false, 2};
-constexpr KernelClass kInt8Narrow{3.363, 4.257, 3.363, 1.179, 12.82, 3.839, 16, false, 1};
+constexpr KernelClass kInt8Cols{3.249, 4.358, 3.249, 0.0, 11.74, 4.483, 16, false, 2};
 constexpr KernelClass kDots3Mx{3.851, 6.568, 3.851, 0.0, 14.10, 6.380, 16, false, 1};
 constexpr KernelClass kDots3Mx32{2.827, 7.815, 2.827, 1.264, 12.92, 7.461, 32, false, 1};
 constexpr KernelClass kDsv4Mx{1.678, 4.843, 1.678, 0.0, 8.484, 4.814, 16, false, 2};
@@ -57,12 +55,12 @@ constexpr double kCrossover = 0.95;  // split form only when at most this fracti
 const KernelClass* kernel_class(int32_t format, int32_t H) {
   // the dispatch rule of launch_attention
   switch (format) {
-    case SMLA_KV_FP8_E4M3: return H > 16 ? &kFp8Wide : &kFp8Cols;
-    case SMLA_KV_FP8_E4M3_NOPE: return H > 16 ? &kFp8Wide : &kFp8Narrow;
-    case SMLA_KV_INT8: return H > 16 ? &kInt8Wide : &kInt8Narrow;
-    // arbitrary-scale FP8 rows convert and scale like INT8 rows in the
-    // many-head kernel (their conversion is cheaper: the INT8 constants bound it)
-    case SMLA_KV_FP8_E4M3_ANY_SCALE: return H > 16 ? &kInt8Wide : &kFp8Narrow;
+    case SMLA_KV_FP8_E4M3:
+    case SMLA_KV_FP8_E4M3_NOPE: return H > 16 ? &kFp8Wide : &kFp8Cols;
+    case SMLA_KV_INT8: return H > 16 ? &kInt8Wide : &kInt8Cols;
+    // arbitrary-scale FP8 rows convert and scale like INT8 rows (their
+    // conversion is cheaper: the INT8 constants bound it)
+    case SMLA_KV_FP8_E4M3_ANY_SCALE: return H > 16 ? &kInt8Wide : &kInt8Cols;
     case SMLA_KV_BF16: return &kBf16Cols;
     // rows with exponent-byte scales: their own kernel at any H
     case SMLA_KV_FP8_E4M3_DOTS3: return H > 16 ? &kDots3Mx32 : &kDots3Mx;
