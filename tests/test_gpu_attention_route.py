@@ -19,7 +19,7 @@ CASES = {
     "fp8_h64_t4_w1024_sink": dict(fmt=W.FMT_FP8, H=64, T=4, topk=1024, ctx=2048, with_sink=True),
     # the same heads with a short list: the prefill form
     "fp8_h64_t4_w128": dict(fmt=W.FMT_FP8, H=64, T=4, topk=128, ctx=512),
-    # narrow kernel, ragged lengths, sink, strided q/out head views
+    # few heads (the column-split kernel), ragged lengths, sink, strided q/out head views
     "bf16_h8_t3_w640_len_sink": dict(fmt=W.FMT_BF16, H=8, hbuf=64, T=3, topk=640, ctx=2048, window=128,
                                      with_topk_length=True, with_sink=True, out_hbuf=64),
     "int8_h128_t2_w768_sink": dict(fmt=W.FMT_INT8, H=128, T=2, topk=768, ctx=1024, with_sink=True),

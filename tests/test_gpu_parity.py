@@ -40,8 +40,9 @@ CASES = {
     "int8_h128_view": dict(fmt=W.FMT_INT8, H=128, topk=256, idx_ld=384, T=2, with_sink=True,
                            pad_fill=W.PAD_SENTINEL),
     "fp8_tail_neg": dict(fmt=W.FMT_FP8, H=16, topk=64, tail_neg=9, causal=False, T=4),
-    # FP8 codes with arbitrary scales (GLM_NSA rows): narrow kernel and the
-    # many-head kernel that folds scales
+    # FP8 codes with arbitrary scales (GLM_NSA rows): the column-split
+    # kernel (few heads) and the many-head kernel, both scaling partial
+    # scores and P
     "fp8any_h8_len_sink": dict(fmt=W.FMT_FP8_ANY, H=8, topk=200, with_topk_length=True, with_sink=True),
     "fp8any_h64_multi_tile": dict(fmt=W.FMT_FP8_ANY, H=64, topk=1024, ctx=2048, T=3, with_sink=True),
     "fp8any_h100_len": dict(fmt=W.FMT_FP8_ANY, H=100, topk=192, T=3, with_topk_length=True),
