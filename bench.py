@@ -308,7 +308,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,
-                     "kernel": "attn_fp8_kernel<prefill> (smla::attn_fp8_kernel<false, false, false>)",
+                     "kernel": "attn_fp8_kernel<prefill> (smla::attn_fp8_kernel<false, false, false, 1>)",
                      "algorithmic_bytes_per_launch": alg_bytes},
         "kernel_source_sha": sha,
     }
