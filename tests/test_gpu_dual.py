@@ -141,3 +141,35 @@ def test_empty_main_list_is_the_secondary_list_alone(name):
     b = smla.prefill(dm.q, de.pool, de.indices, topk_length=de.topk_length, sink=dm.sink,
                      sm_scale=float(main.sm_scale))
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("fmt,H", [(W.FMT_INT8, 8), (W.FMT_FP8_ANY, 16), (W.FMT_FP8_NOPE, 8)])
+def test_few_head_dual_formats(fmt, H):
+    """Dual-list prefill and decode with 16 or fewer heads over INT8,
+    arbitrary-scale FP8 and rope-less FP8 rows (the column-split kernel's
+    dual instantiations), with lengths, empty lists and padded secondary
+    rows."""
+    cid = 480 + 2 * fmt
+    main = W.make_case(f"dual_few_{fmt}_main", config_id=cid, seed=5, fmt=fmt, T=5, H=H, n_seqs=1, ctx=1024,
+                       topk=192, causal=True, with_topk_length=True, with_sink=True)
+    extra = W.make_case(f"dual_few_{fmt}_extra", config_id=cid + 1, seed=6, fmt=fmt, T=5, H=H, n_seqs=1, ctx=512,
+                        topk=130, causal=False, with_topk_length=True)
+    L1, L2 = main.topk_length.copy(), extra.topk_length.copy()
+    L1[1] = 0
+    L1[3], L2[3] = 0, 0
+    main.topk_length, extra.topk_length = L1, L2
+    dm, de = Dev(main), Dev(extra, row_stride=(W.ROW_BYTES[extra.fmt] + 31) // 16 * 16)
+    o, l = smla.prefill_dual(dm.q, dm.pool, dm.indices, sink=dm.sink, **dual_args(dm, de))
+    torch.cuda.synchronize()
+    ob, lf32, _, _ = reference(main, extra)
+    assert np.array_equal(np.isneginf(l.cpu().numpy()), np.isneginf(lf32))
+    assert_out_close(bf16_dev_to_f64(o), f64_of_bits(ob))
+    assert_lse_close(l.cpu().numpy(), lf32)
+    po, pl = smla.decode_dual(dm.q, dm.pool, dm.indices, num_splits=3, **dual_args(dm, de))
+    o2, l2 = smla.combine(po, pl, sink=dm.sink)
+    torch.cuda.synchronize()
+    rpo, rpl = reference(main, extra, num_splits=3)
+    assert np.array_equal(np.isneginf(pl.cpu().numpy()), np.isneginf(rpl))
+    assert_out_close(po.cpu().numpy().astype(np.float64), rpo, "part_out")
+    assert_out_close(bf16_dev_to_f64(o2), f64_of_bits(ob))
+    assert_lse_close(l2.cpu().numpy(), lf32)
