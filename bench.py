@@ -568,10 +568,15 @@ def main():
                 smla.quantize_kv(xkv, torch.arange(r0, r0 + (1 << 18), dtype=torch.int32, device=dev), x4pool)
                 del xkv
 
+            # the split count the model picks for DSv4 rows at these widths
+            Sd4 = smla.decode_num_splits(dc.T, dc.H, k1 + k2, W.FMT_FP8_DSV4)
+            x4po = torch.empty((dc.T, Sd4, dc.H, D_V), dtype=torch.float32, device=dev)
+            x4pl = torch.empty((dc.T, Sd4, dc.H), dtype=torch.float32, device=dev)
+
             def dual4(i):
-                smla.decode_dual(dq[:, : dc.H, :512], v4main, mids[i % 3], x4pool, xidx[i % 3], Sd,
-                                 sm_scale=float(W.SM_SCALE_DSV4), part_out=xpo, part_lse=xpl)
-                smla.combine(xpo, xpl, out=dout, lse=dlse)
+                smla.decode_dual(dq[:, : dc.H, :512], v4main, mids[i % 3], x4pool, xidx[i % 3], Sd4,
+                                 sm_scale=float(W.SM_SCALE_DSV4), part_out=x4po, part_lse=x4pl)
+                smla.combine(x4po, x4pl, out=dout, lse=dlse)
 
             for i in range(3):
                 dual4(i)
@@ -585,14 +590,14 @@ def main():
             dual4_bytes = dc.T * (k1 + k2) * W.ROW_BYTES[W.FMT_FP8_DSV4]
             result.setdefault("dsv4", {})["dual_cache_decode"] = {
                 "workload": f"dsv4 dual-cache decode {dc.T} seqs x 1 query, H={dc.H}, main topk {k1} + secondary "
-                            f"topk {k2} over two {dc.num_blocks * 64 * 584 >> 20} MiB pools, splits={Sd} "
+                            f"topk {k2} over two {dc.num_blocks * 64 * 584 >> 20} MiB pools, splits={Sd4} "
                             "(decode + combine)",
                 "us_per_call": round(dual4_us, 3),
                 "gathered_kv_bytes": dual4_bytes,
                 "gathered_kv_GBps": round(dual4_bytes / (dual4_us * 1e-6) / 1e9, 2),
             }
-            print(f"[bench] dsv4 dual-cache decode {dual4_us:.1f} us (S={Sd})", file=sys.stderr, flush=True)
-            del x4pool, xidx, mids, xpo, xpl
+            print(f"[bench] dsv4 dual-cache decode {dual4_us:.1f} us (S={Sd4})", file=sys.stderr, flush=True)
+            del x4pool, xidx, mids, xpo, xpl, x4po, x4pl
         del v4main
         del dpool, dq, didx, idx_sets, dout, dlse
         torch.cuda.empty_cache()
