@@ -12,8 +12,8 @@ cache-resident.  This script does the same for this library's kernels:
     combine(T, H, S)      = c0 + c1 * partial_MB + c2 * T * H / 1000
     prefill(T, H, topk)   = ap0 + waves_p * (ap + bp * tiles_per_token)
 
-with a, b, f, ap0, ap, bp per kernel class (format x many-head or narrow
-kernel), w and c0..c2 shared, all in microseconds.  waves counts rounds of
+with a, b, f, ap0, ap, bp per kernel class (row format x kernel: many-head,
+column-split or exponent-byte), w and c0..c2 shared, all in microseconds.  waves counts rounds of
 workgroups over the compute units at the kernel's occupancy.
 
 Usage (needs a GPU; writes JSON to stdout or --out):
