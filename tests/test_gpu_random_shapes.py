@@ -9,7 +9,9 @@ FP8 with arbitrary scales, rope-less FP8, DOTS3_SWA, DSv4), each with:
 - sometimes per-token lengths (one token's list then made empty) and a sink.
 
 Every case runs the prefill form and the split form at a drawn split count
-with its combine; both are compared with the oracle.  The shape is in the
+with its combine; both are compared with the oracle.  A second set of 28
+draws does the same for dual-cache calls (a main list and a secondary list
+over two pools, one softmax over both).  The shape is in the
 test id, so a failure names its case.  Outputs use the BF16 bound with the
 one-grid-step floor above magnitude 2 (a short list returns a dequantized V
 row, whose values can exceed 2).
@@ -98,5 +100,61 @@ def test_random_shape(name, i, kw):
     gpo = po.cpu().numpy().astype(np.float64)
     assert np.all(gpo[np.isneginf(gpl)] == 0), "an empty split's partial is not zero"
     assert_out_close(gpo, rpo, "part_out", ulp_floor=True)
+    assert_out_close(bf16_dev_to_f64(o2), want, "combined out", ulp_floor=True)
+    assert_lse_close(l2.cpu().numpy(), lf32, "combined lse")
+
+
+def _draw_dual():
+    """Dual-cache calls: a main list of 64 to 768 entries (a multiple of 64)
+    and a secondary list of 1 to 1500 entries over its own pool with padded
+    rows, four cases per row format."""
+    rng = np.random.default_rng(20261203)
+    cases = []
+    for i in range(4 * len(FMTS)):
+        fmt = FMTS[i % len(FMTS)]
+        k1 = 64 * int(rng.integers(1, 13))
+        k2 = int(rng.integers(1, 1501))
+        kw = dict(fmt=fmt, H=int(rng.choice(HEADS)), k1=k1, k2=k2, T=int(rng.integers(1, 6)),
+                  lengths=bool(rng.random() < 0.6), sink=bool(rng.random() < 0.5))
+        kw["S"] = int(rng.integers(1, min(16, math.ceil((k1 + k2) / 64)) + 1))
+        name = (f"{i:02d}_fmt{fmt}_h{kw['H']}_k{k1}+{k2}_t{kw['T']}_s{kw['S']}"
+                + ("_len" if kw["lengths"] else "") + ("_sink" if kw["sink"] else ""))
+        cases.append((name, i, kw))
+    return cases
+
+
+DUAL_CASES = _draw_dual()
+
+
+@pytest.mark.parametrize("name,i,kw", DUAL_CASES, ids=[n for n, _, _ in DUAL_CASES])
+def test_random_dual_shape(name, i, kw):
+    from test_gpu_dual import dual_args, reference
+
+    fmt, H, T = kw["fmt"], kw["H"], kw["T"]
+    main = W.make_case(f"random_dual_{i}_main", config_id=800 + 2 * i, seed=4, fmt=fmt, T=T, H=H, n_seqs=1,
+                       ctx=max(1024, 2 * kw["k1"]), topk=kw["k1"], causal=True,
+                       with_topk_length=kw["lengths"], with_sink=kw["sink"])
+    extra = W.make_case(f"random_dual_{i}_extra", config_id=801 + 2 * i, seed=4, fmt=fmt, T=T, H=H, n_seqs=1,
+                        ctx=64 * math.ceil(max(512, 2 * kw["k2"]) / 64), topk=kw["k2"], causal=False,
+                        with_topk_length=kw["lengths"])
+    if kw["lengths"] and T > 1:  # one token with an empty main list, another with an empty secondary list
+        L1, L2 = main.topk_length.copy(), extra.topk_length.copy()
+        L1[i % T] = 0
+        L2[(i + 1) % T] = 0
+        main.topk_length, extra.topk_length = L1, L2
+    dm, de = Dev(main), Dev(extra, row_stride=(W.ROW_BYTES[fmt] + 31) // 16 * 16)
+    o, l = smla.prefill_dual(dm.q, dm.pool, dm.indices, sink=dm.sink, **dual_args(dm, de))
+    po, pl = smla.decode_dual(dm.q, dm.pool, dm.indices, num_splits=kw["S"], **dual_args(dm, de))
+    o2, l2 = smla.combine(po, pl, sink=dm.sink)
+    torch.cuda.synchronize()
+    ob, lf32, _, _ = reference(main, extra)
+    want = f64_of_bits(ob)
+    assert_out_close(bf16_dev_to_f64(o), want, ulp_floor=True)
+    assert_lse_close(l.cpu().numpy(), lf32)
+    rpo, rpl = reference(main, extra, num_splits=kw["S"])
+    gpl = pl.cpu().numpy()
+    assert np.array_equal(np.isneginf(gpl), np.isneginf(rpl)), "empty splits differ"
+    assert_lse_close(gpl, rpl.astype(np.float32), "part_lse")
+    assert_out_close(po.cpu().numpy().astype(np.float64), rpo, "part_out", ulp_floor=True)
     assert_out_close(bf16_dev_to_f64(o2), want, "combined out", ulp_floor=True)
     assert_lse_close(l2.cpu().numpy(), lf32, "combined lse")
