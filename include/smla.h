@@ -165,9 +165,10 @@ smla_status smla_decode_workspace_size(int64_t T, int32_t H, int32_t num_splits,
  *   slots  int32 [n]: destination slot of row i; slots outside
  *          [0, num_blocks*64) (-1 included) are skipped.
  * FP8: per 128-element tile of the nope part, amax = max |x|; scale = 1 when
- * amax = 0, else the power of two 2^ceil(log2(amax/448)) (the page's
- * "power-of-2 FP32 scales"); codes = e4m3(x / scale), round to nearest even,
- * sign kept.  FP8_E4M3_ANY_SCALE: scale = amax/448 (FP32, correctly rounded;
+ * amax = 0, else the power of two 2^max(ceil(log2(amax/448)), -126) (DSv3.2
+ * stores FP32 power-of-two scales; the floor keeps the scale a normal FP32
+ * number, which the attention entry points require); codes = e4m3(x /
+ * scale), round to nearest even, sign kept.  FP8_E4M3_ANY_SCALE: scale = amax/448 (FP32, correctly rounded;
  * 1 when amax = 0), codes as for FP8.  INT8: scale = amax/127 (1 when amax = 0), codes =
  * clamp(rne(x/scale), -127, 127).  FP8_E4M3_DOTS3 and FP8_E4M3_DSV4: the
  * FP8 rule over their 128- or 64-element tiles with the scale 2^e raised

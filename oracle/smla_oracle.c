@@ -158,13 +158,16 @@ uint8_t oracle_e4m3_encode(float y) {
 }
 
 /* FP8 tile scale: amax = 0 -> 1; otherwise the smallest power of two s with
- * amax / s <= 448, found from r = amax / 448 (float32) as 2^ceil(log2 r). */
+ * amax / s <= 448, found from r = amax / 448 (float32) as 2^ceil(log2 r),
+ * and at least 2^-126: the stored scale is a normal float32 power of two
+ * (tiles with amax below 448 * 2^-126 then use codes below 448). */
 float oracle_fp8_scale(float amax) {
   if (amax == 0.0f) return 1.0f;
   float r = amax / 448.0f;
   int k;
   float f = frexpf(r, &k); /* r = f * 2^k, f in [0.5, 1) */
   int e = (f == 0.5f) ? k - 1 : k;
+  if (e < -126) e = -126;
   return ldexpf(1.0f, e);
 }
 

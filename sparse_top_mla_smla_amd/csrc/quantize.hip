@@ -46,12 +46,13 @@ __device__ __forceinline__ int fp8_scale_exponent(float amax) {
   return (32 - __clz((int)(rb - 1u))) - 149;  // subnormal r = rb * 2^-149
 }
 
-// 2^ceil(log2(amax/448)); 1 when amax = 0.
+// 2^max(ceil(log2(amax/448)), -126), a normal float32 power of two; 1 when
+// amax = 0.
 __device__ __forceinline__ float fp8_tile_scale(float amax) {
   if (amax == 0.0f) return 1.0f;
-  const int e = fp8_scale_exponent(amax);
-  uint32_t sb = (e >= -126) ? (uint32_t)(e + 127) << 23 : 1u << (e + 149);
-  return __builtin_bit_cast(float, sb);
+  int e = fp8_scale_exponent(amax);
+  e = e < -126 ? -126 : e;
+  return __builtin_bit_cast(float, (uint32_t)(e + 127) << 23);
 }
 
 template <int FMT>

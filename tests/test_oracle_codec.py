@@ -88,16 +88,24 @@ def test_e4m3_encode_sign_of_zero_and_saturation(orc):
 def test_fp8_scale_pow2_and_range(orc):
     amax = np.abs(all_bf16_in_range(limit=np.inf))
     amax = np.unique(amax[amax > 0])
+    floor = 2.0 ** -126                                # the least normal float32
     for a in amax[:: 7]:
         s = orc.fp8_scale(float(a))
         m, e = np.frexp(s)
-        assert m == 0.5, (a, s)                       # a power of two
+        assert m == 0.5 and s >= floor, (a, s)         # a normal power of two
         r = np.float64(a) / s
-        assert 224.0 < r <= 448.0, (a, s, r)          # smallest such power
+        assert r <= 448.0, (a, s, r)
+        if s > floor:
+            assert r > 224.0, (a, s, r)                # the smallest such power
     assert orc.fp8_scale(0.0) == 1.0
     assert orc.fp8_scale(448.0) == 1.0
     assert orc.fp8_scale(448.0 * 2 ** -7) == 2.0 ** -7
     assert orc.fp8_scale(449.0) == 2.0
+    # tiles whose amax/448 is below the least normal float32 keep scale 2^-126
+    assert orc.fp8_scale(448.0 * floor) == floor
+    assert orc.fp8_scale(448.0 * floor * 1.5) == 2 * floor
+    assert orc.fp8_scale(1e-38) == floor
+    assert orc.fp8_scale(float(np.float32(2.0 ** -140))) == floor
 
 
 def _pool_for(fmt, n_rows, seed=0, tweak=None):
@@ -140,6 +148,7 @@ def test_fp8_quantizer_invariants(orc):
         kv[1, 128:256] = W.f32_to_bf16_bits(np.full(128, -0.0, np.float32))
         kv[2, :128] = W.f32_to_bf16_bits(np.float32(1e-30) * np.arange(128, dtype=np.float32))
         kv[3, 256:384] = W.f32_to_bf16_bits(np.float32(3e4) * np.linspace(-1, 1, 128, dtype=np.float32))
+        kv[4, 384:512] = W.f32_to_bf16_bits(np.float32(1e-38) * np.arange(128, dtype=np.float32))
         return kv
     kv, pool = _pool_for(W.FMT_FP8, 192, seed=3, tweak=tweak)
     rows = pool.data.reshape(-1, 656)[:192]
@@ -151,7 +160,11 @@ def test_fp8_quantizer_invariants(orc):
     y = x / scales[:, :, None]
     assert np.all(np.abs(y) <= 448.0)
     nz = amax > 0
-    assert np.all((amax[nz] / scales[nz] > 224.0) & (amax[nz] / scales[nz] <= 448.0))
+    above = nz & (scales > 2.0 ** -126)
+    assert np.all(amax[nz] / scales[nz] <= 448.0)
+    assert np.all(amax[above] / scales[above] > 224.0)
+    assert scales[4, 3] == 2.0 ** -126                  # amax/448 below the least normal float32
+    assert np.abs(y[4, 3]).max() < 224.0
     assert np.all(scales[~nz] == 1.0)
     # the encoded code is the nearest e4m3 value to y (ties to even): compare with torch
     assert np.array_equal(codes.reshape(-1), torch_e4m3_encode(y.reshape(-1).astype(np.float32)))
