@@ -53,23 +53,42 @@ def f64_of_bits(bits: np.ndarray) -> np.ndarray:
     return W.bf16_bits_to_f32(bits).astype(np.float64)
 
 
-def bf16_ulp(x: np.ndarray) -> np.ndarray:
-    """Spacing of the BF16 grid at |x| (8 significant bits)."""
+def bf16_neighbors(x: np.ndarray):
+    """The two BF16 numbers that bracket each float64 x (equal when x is one)."""
+    x = np.asarray(x, dtype=np.float64)
     mag = np.abs(x)
-    e = np.floor(np.log2(np.where(mag > 0, mag, 1.0)))
-    return np.ldexp(1.0, (e - 7).astype(np.int64))
+    b = (mag.astype(np.float32).view(np.uint32) & np.uint32(0xFFFF0000)).astype(np.int64)
+    cand = np.stack([b - 0x10000, b, b + 0x10000, b + 0x20000])
+    cand = np.clip(cand, 0, 0x7F7F0000).astype(np.uint32)
+    vals = (cand << 0).view(np.float32).astype(np.float64)           # candidate magnitudes
+    below = np.where(vals <= mag, vals, -np.inf).max(axis=0)
+    above = np.where(vals >= mag, vals, np.inf).min(axis=0)
+    sign = np.where(x < 0, -1.0, 1.0)
+    return sign * below, sign * above
 
 
-def assert_out_close(got: np.ndarray, want: np.ndarray, what: str = "out", ulp_floor: bool = False):
-    """max_abs <= 1e-2 and mean_abs <= 1e-3.  ulp_floor: BF16 outputs of
-    magnitude 2 or more sit on a grid coarser than 1e-2 (spacing 2^-6), so
-    there the bound is one grid step of the reference value: two roundings of
-    values that differ in their last bits can land one step apart."""
+def assert_out_close(got: np.ndarray, want: np.ndarray, what: str = "out", bf16: bool = True):
+    """The problem statement's bar, max_abs <= 1e-2 and mean_abs <= 1e-3,
+    against `want`, the oracle's exact (float64, unrounded) value.
+
+    BF16 out (bf16=True): the final rounding counts against the bar.  Where
+    no BF16 number lies within 1e-2 of the exact value (possible only at
+    |x| >= 4, where the grid step is 2^-5), no BF16 result can meet the bar,
+    and there the output must be one of the two BF16 numbers adjacent to the
+    exact value.  FP32 decode partials (bf16=False) take the bar as it is."""
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
     d = np.abs(got - want)
     assert np.all(np.isfinite(got)), f"{what}: non-finite values"
-    lim = np.maximum(OUT_MAX_ABS, bf16_ulp(want)) if ulp_floor else OUT_MAX_ABS
-    excess = d - lim
-    assert excess.max() <= 0, f"{what}: max_abs {d.max():.3e} (worst excess over the bound {excess.max():.3e})"
+    ok = d <= OUT_MAX_ABS
+    if bf16 and not ok.all():
+        lo, hi = bf16_neighbors(want)
+        unreachable = np.minimum(np.abs(lo - want), np.abs(hi - want)) > OUT_MAX_ABS
+        ok |= unreachable & ((got == lo) | (got == hi))
+    if not ok.all():
+        worst = np.unravel_index(np.argmax(np.where(ok, 0.0, d)), d.shape)
+        raise AssertionError(f"{what}: max_abs {d[worst]:.3e} at {worst} (got {got[worst]:.6g}, "
+                             f"exact {want[worst]:.6g}); {int((~ok).sum())} values outside the bar")
     assert d.mean() <= OUT_MEAN_ABS, f"{what}: mean_abs {d.mean():.3e}"
 
 

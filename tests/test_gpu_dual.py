@@ -14,7 +14,7 @@ import oracle
 import sparse_top_mla_smla_amd as smla
 from sparse_top_mla_smla_amd import workloads as W
 
-from gpu_util import Dev, assert_lse_close, assert_out_close, bf16_dev_to_f64, f64_of_bits, need_gpu
+from gpu_util import Dev, assert_lse_close, assert_out_close, bf16_dev_to_f64, need_gpu
 from helpers import oracle_pool
 
 pytestmark = pytest.mark.gpu
@@ -87,10 +87,10 @@ def test_prefill_dual_parity(name):
     dm, de = Dev(main), Dev(extra, row_stride=(W.ROW_BYTES[extra.fmt] + 31) // 16 * 16)  # padded secondary rows
     o, l = smla.prefill_dual(dm.q, dm.pool, dm.indices, sink=dm.sink, **dual_args(dm, de))
     torch.cuda.synchronize()
-    ob, lf32, _, _ = reference(main, extra)
+    _, lf32, of, _ = reference(main, extra)
     got_l = l.cpu().numpy()
     assert np.array_equal(np.isneginf(got_l), np.isneginf(lf32))
-    assert_out_close(bf16_dev_to_f64(o), f64_of_bits(ob))
+    assert_out_close(bf16_dev_to_f64(o), of)
     assert_lse_close(got_l, lf32)
 
 
@@ -106,9 +106,9 @@ def test_decode_dual_parity(name, S):
     gpl = pl.cpu().numpy()
     assert np.array_equal(np.isneginf(gpl), np.isneginf(rpl))
     assert_lse_close(gpl, rpl.astype(np.float32), "part_lse")
-    assert_out_close(po.cpu().numpy().astype(np.float64), rpo, "part_out")
-    ob, lf32, _, _ = reference(main, extra)
-    assert_out_close(bf16_dev_to_f64(o), f64_of_bits(ob))
+    assert_out_close(po.cpu().numpy().astype(np.float64), rpo, "part_out", bf16=False)
+    _, lf32, of, _ = reference(main, extra)
+    assert_out_close(bf16_dev_to_f64(o), of)
     assert_lse_close(l.cpu().numpy(), lf32)
 
 
@@ -161,15 +161,15 @@ def test_few_head_dual_formats(fmt, H):
     dm, de = Dev(main), Dev(extra, row_stride=(W.ROW_BYTES[extra.fmt] + 31) // 16 * 16)
     o, l = smla.prefill_dual(dm.q, dm.pool, dm.indices, sink=dm.sink, **dual_args(dm, de))
     torch.cuda.synchronize()
-    ob, lf32, _, _ = reference(main, extra)
+    _, lf32, of, _ = reference(main, extra)
     assert np.array_equal(np.isneginf(l.cpu().numpy()), np.isneginf(lf32))
-    assert_out_close(bf16_dev_to_f64(o), f64_of_bits(ob))
+    assert_out_close(bf16_dev_to_f64(o), of)
     assert_lse_close(l.cpu().numpy(), lf32)
     po, pl = smla.decode_dual(dm.q, dm.pool, dm.indices, num_splits=3, **dual_args(dm, de))
     o2, l2 = smla.combine(po, pl, sink=dm.sink)
     torch.cuda.synchronize()
     rpo, rpl = reference(main, extra, num_splits=3)
     assert np.array_equal(np.isneginf(pl.cpu().numpy()), np.isneginf(rpl))
-    assert_out_close(po.cpu().numpy().astype(np.float64), rpo, "part_out")
-    assert_out_close(bf16_dev_to_f64(o2), f64_of_bits(ob))
+    assert_out_close(po.cpu().numpy().astype(np.float64), rpo, "part_out", bf16=False)
+    assert_out_close(bf16_dev_to_f64(o2), of)
     assert_lse_close(l2.cpu().numpy(), lf32)

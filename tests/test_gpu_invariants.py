@@ -10,6 +10,7 @@ import sparse_top_mla_smla_amd as smla
 from sparse_top_mla_smla_amd import workloads as W
 
 from gpu_util import Dev, need_gpu
+from helpers import oracle_pool
 
 pytestmark = pytest.mark.gpu
 
@@ -198,3 +199,75 @@ def test_error_codes():
                          W.FMT_FP8)
     with pytest.raises(smla.SmlaError, match="block_stride"):
         smla.prefill(d.q, narrow, d.indices)
+
+
+@pytest.mark.parametrize("fmt", [W.FMT_FP8, W.FMT_INT8])
+def test_nonfinite_row_stays_in_its_token(fmt):
+    """One pool row holds non-finite data (e4m3 NaN codes, or a NaN rope
+    value), and token A's list selects it.  Token B, which the same
+    persistent prefill workgroup runs later (T = 300 > 256 workgroups), has
+    a list of length 2, so position 3 of its first tile holds no candidate:
+    that LDS row must not carry token A's row into B's result.  Every token
+    other than A matches the oracle with finite outputs."""
+    c = W.make_case(f"nan_row_{fmt}", config_id=296 + fmt, seed=6, fmt=fmt, T=300, H=64, n_seqs=1, ctx=1024,
+                    topk=128, causal=False, with_topk_length=True)
+    a, b = 5, 5 + 256
+    bad_slot = int(c.slots[17])
+    idx = c.idx_buf.copy()
+    idx[idx == bad_slot] = -1                  # only A selects the row, at list position 3
+    idx[a, 3] = bad_slot
+    c.idx_buf = idx
+    L = c.topk_length.copy()
+    L[a] = max(int(L[a]), 4)
+    L[b] = 2
+    c.topk_length = L
+    d = Dev(c)
+    raw = d.pool.data.view(-1)
+    off = (bad_slot // 64) * d.pool.data.stride(0) + (bad_slot % 64) * 656
+    if fmt == W.FMT_FP8:
+        raw[off:off + 512] = 0x7F                                   # e4m3 NaN codes
+    else:
+        raw[off + 528:off + 530] = torch.tensor([0xC0, 0x7F], dtype=torch.uint8, device="cuda")  # NaN rope
+    pool = oracle_pool(c)
+    pool.data[:] = d.pool.data.cpu().numpy()
+    o, l = smla.prefill(d.q, d.pool, d.indices, topk_length=d.topk_length, sm_scale=float(c.sm_scale))
+    torch.cuda.synchronize()
+    assert not torch.isfinite(o[a].float()).all()                   # A's own result is poisoned
+    keep = np.array([t for t in range(c.T) if t != a])
+    got = o.float().cpu().numpy().astype(np.float64)[keep]
+    assert np.isfinite(got).all()
+    _, lf32, of, _ = oracle.prefill(c.q, pool, c.indices, topk_length=c.topk_length, sm_scale=c.sm_scale,
+                                    tokens=keep)
+    from gpu_util import assert_lse_close, assert_out_close
+    assert_out_close(got, of[keep])
+    assert_lse_close(l.cpu().numpy()[keep], lf32[keep])
+
+
+def test_binding_rejects_wrong_shapes():
+    """The binding checks the sizes the kernels read and write before any
+    call: a wrong output shape, a list wider than the index rows, fewer
+    lengths than tokens or fewer sinks than heads raise SmlaError."""
+    c = case(W.FMT_FP8, with_sink=True)
+    d = Dev(c)
+    T, H = c.T, c.H
+    bad = [
+        dict(out=torch.empty((T, H + 1, 512), dtype=torch.bfloat16, device="cuda")),
+        dict(lse=torch.empty((T + 1, H), dtype=torch.float32, device="cuda")),
+        dict(topk=c.topk + 1),
+        dict(topk_length=torch.ones(T - 1, dtype=torch.int32, device="cuda")),
+        dict(sink=torch.zeros(H - 1, dtype=torch.float32, device="cuda")),
+    ]
+    for kw in bad:
+        with pytest.raises(smla.SmlaError):
+            smla.prefill(d.q, d.pool, d.indices, sm_scale=float(c.sm_scale), **kw)
+    with pytest.raises(smla.SmlaError):
+        smla.prefill(d.q[:, :, :500], d.pool, d.indices)
+    with pytest.raises(smla.SmlaError):
+        smla.decode(d.q, d.pool, d.indices, 2,
+                    part_out=torch.empty((T, 3, H, 512), dtype=torch.float32, device="cuda"))
+    po, pl = smla.decode(d.q, d.pool, d.indices, 2)
+    with pytest.raises(smla.SmlaError):
+        smla.combine(po, pl[:, :1].contiguous())
+    with pytest.raises(smla.SmlaError):
+        smla.combine(po, pl, out=torch.empty((T, H, 256), dtype=torch.bfloat16, device="cuda"))
+    torch.cuda.synchronize()
