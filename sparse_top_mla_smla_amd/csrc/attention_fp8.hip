@@ -44,11 +44,11 @@
 // waves gather the next tile straight from global memory with
 // global_load_lds_dwordx4, one instruction per piece for all 64 rows
 // (lane = row, landing at base + 16*lane), issued as soon as the tile
-// before it is consumed; the index list runs one tile further ahead.  Rows
-// that are never loaded (masked entries) keep stale rows of the same
-// buffer or the initial zero fill and contribute nothing, because their
-// probabilities are exactly 0 (this needs the pool's codes and rope values
-// to be finite, as the cache writer produces them).
+// before it is consumed; the index list runs one tile further ahead.  List
+// positions without a candidate gather a zero row instead, so every LDS row
+// of a tile belongs to the tile's own list: such a row has probability 0
+// and value 0, and no data of another token's list (a non-finite row
+// included) can reach this token's result.
 #include <type_traits>
 
 #include "device_common.h"
@@ -173,6 +173,10 @@ template <int V>
 struct Buf {
   static constexpr int value = V;
 };
+
+// the row that list positions without a candidate gather (zero-initialized
+// device memory, one copy per device)
+__device__ __attribute__((aligned(16))) uint8_t zero_row[RB];
 }  // namespace f8
 
 // NOPE: rows without rope dimensions (q rows of 512 values, row padding never
@@ -294,19 +298,19 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
   // wave w moves pieces w, w + 8, ... of all 64 rows of a tile (lane = row)
   // into raw buffer B, in part P (0..2) the pieces of rounds 2P and 2P + 1.
   // Spreading the issue over the tile keeps the address unit's queue short,
-  // so no wave stalls long at issue.  Wave 0 records which rows exist.
+  // so no wave stalls long at issue.  A lane without a candidate (src null)
+  // moves the zero row.  Wave 0 records which rows hold candidates.
   auto issue_part = [&](auto buf, auto part, const uint8_t* src) {
     constexpr int B = decltype(buf)::value;
     constexpr int P = decltype(part)::value;
     uint8_t* raw = B ? raw1 : raw0;
-    if (src) {
+    const uint8_t* from = src ? src : zero_row;
 #pragma unroll
-      for (int r = 2 * P; r < 2 * P + 2; ++r) {
-        const int ck = w + 8 * r;
-        // (rows without rope dimensions: their padding is not gathered)
-        if ((r + 1 < GROUNDS || ck < CHUNKS) && (!NOPE || ck < CK_ROPE))
-          global_to_lds_16(src + 16 * ck, raw + ck * CS);
-      }
+    for (int r = 2 * P; r < 2 * P + 2; ++r) {
+      const int ck = w + 8 * r;
+      // (rows without rope dimensions: their padding is not gathered)
+      if ((r + 1 < GROUNDS || ck < CHUNKS) && (!NOPE || ck < CK_ROPE))
+        global_to_lds_16(from + 16 * ck, raw + ck * CS);
     }
     if (P == 0 && w == 0) valid[B * TC + lane] = src != nullptr;
   };
@@ -345,7 +349,7 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
   // the first tile's index entries (an unconditional load of an entry
   // inside the range, selected after), then Q: the compiler barrier keeps
   // the Q loads behind the wait for the entries, so they are in flight
-  // during the zero fill and the first gather instead of delaying its issue
+  // during the first gather instead of delaying its issue
   const uint8_t* src0 = nullptr;
   if (cur.t >= 0) {
     const int32_t j = cur.j0 + lane;
@@ -452,12 +456,6 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
   }
 
   if (cur.t >= 0) {
-    for (int i = tid; i < TILE / 16; i += NT) {
-      reinterpret_cast<uint4*>(raw0)[i] = make_uint4(0, 0, 0, 0);
-      reinterpret_cast<uint4*>(raw1)[i] = make_uint4(0, 0, 0, 0);
-    }
-    // the zero fill is complete everywhere before any gather lands
-    lds_barrier();
     issue_part(Buf<0>{}, Buf<0>{}, src0);
     issue_part(Buf<0>{}, Buf<1>{}, src0);
     issue_part(Buf<0>{}, Buf<2>{}, src0);
