@@ -1,10 +1,11 @@
 """Python binding of libsmla -- sparse MLA attention for AMD MI355X.
 
-A thin ctypes layer over the C ABI in include/smla.h: it only checks dtypes
-and devices, reads pointers and strides off torch tensors, allocates outputs
-when the caller passes none, and calls the library on the current HIP
-stream.  Every step of the computation runs in the HIP kernels of
-libsmla.so; there is no fallback, and a missing library raises.
+A thin ctypes layer over the C ABI in include/smla.h: it only checks dtypes,
+devices and the shapes the kernels read from and write to, reads pointers
+and strides off torch tensors, allocates outputs when the caller passes
+none, and calls the library on the current HIP stream.  Every step of the
+computation runs in the HIP kernels of libsmla.so; there is no fallback, and
+a missing library raises.
 """
 from __future__ import annotations
 
@@ -163,6 +164,33 @@ def _need(t: torch.Tensor, name: str, dtype, last_contig: bool = True):
         raise SmlaError(f"{name}: the last dimension must be contiguous")
 
 
+def _shape(t: torch.Tensor, name: str, shape) -> None:
+    if tuple(t.shape) != tuple(shape):
+        raise SmlaError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _check_common(q: torch.Tensor, pool: "KVPool", indices: torch.Tensor, topk: int,
+                  topk_length: Optional[torch.Tensor], sink: Optional[torch.Tensor]) -> None:
+    """Sizes the kernels read from: q rows, index rows, lengths and sinks."""
+    if q.dim() != 3:
+        raise SmlaError(f"q must be [T, H, D], got {tuple(q.shape)}")
+    T, H, D = q.shape
+    if D < query_dims(pool.fmt):
+        raise SmlaError(f"q rows hold {D} values; this format needs {query_dims(pool.fmt)}")
+    if indices.dim() != 2 or indices.shape[0] < T:
+        raise SmlaError(f"indices must be [>= T, >= topk] = [>= {T}, >= {topk}], got {tuple(indices.shape)}")
+    if topk > indices.shape[1]:
+        raise SmlaError(f"topk {topk} exceeds the index rows' {indices.shape[1]} columns")
+    if topk_length is not None:
+        _need(topk_length, "topk_length", torch.int32)
+        if topk_length.numel() < T:
+            raise SmlaError(f"topk_length holds {topk_length.numel()} entries for {T} tokens")
+    if sink is not None:
+        _need(sink, "sink", torch.float32)
+        if sink.numel() < H:
+            raise SmlaError(f"sink holds {sink.numel()} entries for {H} heads")
+
+
 class KVPool:
     """A paged latent pool: a uint8 device tensor [num_blocks, block_stride]
     (block_stride >= 64 * row stride, multiple of 16) in format fmt, rows
@@ -204,6 +232,39 @@ def _idx_args(indices: torch.Tensor, topk: Optional[int]):
     return topk, indices.stride(0)
 
 
+def _outputs(q: torch.Tensor, pool: KVPool, out: Optional[torch.Tensor], lse: Optional[torch.Tensor]):
+    """out [T, H, d_v] bf16 and lse [T, H] f32 (allocated when not given)."""
+    T, H = q.shape[0], q.shape[1]
+    dv = value_dims(pool.fmt)
+    if out is None:
+        out = torch.empty((T, H, dv), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.bfloat16)
+    _need(lse, "lse", torch.float32)
+    _shape(out, "out", (T, H, dv))
+    _shape(lse, "lse", (T, H))
+    return out, lse
+
+
+def _partials(q: torch.Tensor, pool: KVPool, num_splits: int, part_out: Optional[torch.Tensor],
+              part_lse: Optional[torch.Tensor]):
+    """part_out [T, S, H, d_v] and part_lse [T, S, H], f32, contiguous."""
+    T, H = q.shape[0], q.shape[1]
+    dv = value_dims(pool.fmt)
+    if part_out is None:
+        part_out = torch.empty((T, num_splits, H, dv), dtype=torch.float32, device=q.device)
+    if part_lse is None:
+        part_lse = torch.empty((T, num_splits, H), dtype=torch.float32, device=q.device)
+    _need(part_out, "part_out", torch.float32)
+    _need(part_lse, "part_lse", torch.float32)
+    if not (part_out.is_contiguous() and part_lse.is_contiguous()):
+        raise SmlaError("part_out / part_lse must be contiguous")
+    _shape(part_out, "part_out", (T, num_splits, H, dv))
+    _shape(part_lse, "part_lse", (T, num_splits, H))
+    return part_out, part_lse
+
+
 def prefill(q: torch.Tensor, pool: KVPool, indices: torch.Tensor, topk: Optional[int] = None,
             topk_length: Optional[torch.Tensor] = None, sink: Optional[torch.Tensor] = None,
             sm_scale: float = 1.0 / 24.0, out: Optional[torch.Tensor] = None,
@@ -214,16 +275,8 @@ def prefill(q: torch.Tensor, pool: KVPool, indices: torch.Tensor, topk: Optional
     _need(q, "q", torch.bfloat16)
     T, H, _ = q.shape
     topk, ist = _idx_args(indices, topk)
-    if topk_length is not None:
-        _need(topk_length, "topk_length", torch.int32)
-    if sink is not None:
-        _need(sink, "sink", torch.float32)
-    if out is None:
-        out = torch.empty((T, H, value_dims(pool.fmt)), dtype=torch.bfloat16, device=q.device)
-    if lse is None:
-        lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
-    _need(out, "out", torch.bfloat16)
-    _need(lse, "lse", torch.float32)
+    _check_common(q, pool, indices, topk, topk_length, sink)
+    out, lse = _outputs(q, pool, out, lse)
     _check(_load().smla_prefill(_ptr(q), T, H, q.stride(0), q.stride(1), pool.c(), _ptr(indices), topk,
                                 ist, _ptr(topk_length), _ptr(sink), float(sm_scale), _ptr(out),
                                 out.stride(0), out.stride(1), _ptr(lse), lse.stride(0),
@@ -240,16 +293,8 @@ def decode(q: torch.Tensor, pool: KVPool, indices: torch.Tensor, num_splits: int
     _need(q, "q", torch.bfloat16)
     T, H, _ = q.shape
     topk, ist = _idx_args(indices, topk)
-    if topk_length is not None:
-        _need(topk_length, "topk_length", torch.int32)
-    if part_out is None:
-        part_out = torch.empty((T, num_splits, H, value_dims(pool.fmt)), dtype=torch.float32, device=q.device)
-    if part_lse is None:
-        part_lse = torch.empty((T, num_splits, H), dtype=torch.float32, device=q.device)
-    _need(part_out, "part_out", torch.float32)
-    _need(part_lse, "part_lse", torch.float32)
-    if not (part_out.is_contiguous() and part_lse.is_contiguous()):
-        raise SmlaError("part_out / part_lse must be contiguous")
+    _check_common(q, pool, indices, topk, topk_length, None)
+    part_out, part_lse = _partials(q, pool, num_splits, part_out, part_lse)
     _check(_load().smla_decode(_ptr(q), T, H, q.stride(0), q.stride(1), pool.c(), _ptr(indices), topk,
                                ist, _ptr(topk_length), float(sm_scale), num_splits, _ptr(part_out),
                                _ptr(part_lse), _stream(stream)), "smla_decode")
@@ -264,15 +309,22 @@ def combine(part_out: torch.Tensor, part_lse: torch.Tensor, sink: Optional[torch
     _need(part_lse, "part_lse", torch.float32)
     if not (part_out.is_contiguous() and part_lse.is_contiguous()):
         raise SmlaError("part_out / part_lse must be contiguous")
+    if part_out.dim() != 4:
+        raise SmlaError(f"part_out must be [T, S, H, d_v], got {tuple(part_out.shape)}")
     T, S, H, dv = part_out.shape
+    _shape(part_lse, "part_lse", (T, S, H))
     if sink is not None:
         _need(sink, "sink", torch.float32)
+        if sink.numel() < H:
+            raise SmlaError(f"sink holds {sink.numel()} entries for {H} heads")
     if out is None:
         out = torch.empty((T, H, dv), dtype=torch.bfloat16, device=part_out.device)
     if lse is None:
         lse = torch.empty((T, H), dtype=torch.float32, device=part_out.device)
     _need(out, "out", torch.bfloat16)
     _need(lse, "lse", torch.float32)
+    _shape(out, "out", (T, H, dv))
+    _shape(lse, "lse", (T, H))
     _check(_load().smla_combine(_ptr(part_out), _ptr(part_lse), T, S, H, dv, _ptr(sink), _ptr(out),
                                 out.stride(0), out.stride(1), _ptr(lse), lse.stride(0),
                                 _stream(stream)), "smla_combine")
@@ -290,16 +342,8 @@ def attention(q: torch.Tensor, pool: KVPool, indices: torch.Tensor, topk: Option
     _need(q, "q", torch.bfloat16)
     T, H, _ = q.shape
     topk, ist = _idx_args(indices, topk)
-    if topk_length is not None:
-        _need(topk_length, "topk_length", torch.int32)
-    if sink is not None:
-        _need(sink, "sink", torch.float32)
-    if out is None:
-        out = torch.empty((T, H, value_dims(pool.fmt)), dtype=torch.bfloat16, device=q.device)
-    if lse is None:
-        lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
-    _need(out, "out", torch.bfloat16)
-    _need(lse, "lse", torch.float32)
+    _check_common(q, pool, indices, topk, topk_length, sink)
+    out, lse = _outputs(q, pool, out, lse)
     ws_bytes = 0
     if workspace is not None:
         if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
@@ -312,10 +356,14 @@ def attention(q: torch.Tensor, pool: KVPool, indices: torch.Tensor, topk: Option
     return out, lse
 
 
-def _extra(pool: KVPool, indices: torch.Tensor, topk: Optional[int], topk_length: Optional[torch.Tensor]):
+def _extra(T: int, pool: KVPool, indices: torch.Tensor, topk: Optional[int], topk_length: Optional[torch.Tensor]):
     topk, ist = _idx_args(indices, topk)
+    if indices.dim() != 2 or indices.shape[0] < T or topk > indices.shape[1]:
+        raise SmlaError(f"extra_indices must be [>= {T}, >= {topk}], got {tuple(indices.shape)}")
     if topk_length is not None:
         _need(topk_length, "extra_topk_length", torch.int32)
+        if topk_length.numel() < T:
+            raise SmlaError(f"extra_topk_length holds {topk_length.numel()} entries for {T} tokens")
     return _Extra(pool.c(), _ptr(indices), topk, ist, _ptr(topk_length))
 
 
@@ -329,17 +377,9 @@ def prefill_dual(q: torch.Tensor, pool: KVPool, indices: torch.Tensor, extra_poo
     _need(q, "q", torch.bfloat16)
     T, H, _ = q.shape
     topk, ist = _idx_args(indices, topk)
-    ex = _extra(extra_pool, extra_indices, extra_topk, extra_topk_length)
-    if topk_length is not None:
-        _need(topk_length, "topk_length", torch.int32)
-    if sink is not None:
-        _need(sink, "sink", torch.float32)
-    if out is None:
-        out = torch.empty((T, H, value_dims(pool.fmt)), dtype=torch.bfloat16, device=q.device)
-    if lse is None:
-        lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
-    _need(out, "out", torch.bfloat16)
-    _need(lse, "lse", torch.float32)
+    _check_common(q, pool, indices, topk, topk_length, sink)
+    ex = _extra(T, extra_pool, extra_indices, extra_topk, extra_topk_length)
+    out, lse = _outputs(q, pool, out, lse)
     _check(_load().smla_prefill_dual(_ptr(q), T, H, q.stride(0), q.stride(1), pool.c(), _ptr(indices), topk, ist,
                                      _ptr(topk_length), ctypes.byref(ex), _ptr(sink), float(sm_scale), _ptr(out),
                                      out.stride(0), out.stride(1), _ptr(lse), lse.stride(0), _stream(stream)),
@@ -357,17 +397,9 @@ def decode_dual(q: torch.Tensor, pool: KVPool, indices: torch.Tensor, extra_pool
     _need(q, "q", torch.bfloat16)
     T, H, _ = q.shape
     topk, ist = _idx_args(indices, topk)
-    ex = _extra(extra_pool, extra_indices, extra_topk, extra_topk_length)
-    if topk_length is not None:
-        _need(topk_length, "topk_length", torch.int32)
-    if part_out is None:
-        part_out = torch.empty((T, num_splits, H, value_dims(pool.fmt)), dtype=torch.float32, device=q.device)
-    if part_lse is None:
-        part_lse = torch.empty((T, num_splits, H), dtype=torch.float32, device=q.device)
-    _need(part_out, "part_out", torch.float32)
-    _need(part_lse, "part_lse", torch.float32)
-    if not (part_out.is_contiguous() and part_lse.is_contiguous()):
-        raise SmlaError("part_out / part_lse must be contiguous")
+    _check_common(q, pool, indices, topk, topk_length, None)
+    ex = _extra(T, extra_pool, extra_indices, extra_topk, extra_topk_length)
+    part_out, part_lse = _partials(q, pool, num_splits, part_out, part_lse)
     _check(_load().smla_decode_dual(_ptr(q), T, H, q.stride(0), q.stride(1), pool.c(), _ptr(indices), topk, ist,
                                     _ptr(topk_length), ctypes.byref(ex), float(sm_scale), num_splits,
                                     _ptr(part_out), _ptr(part_lse), _stream(stream)), "smla_decode_dual")
