@@ -62,7 +62,7 @@ def parse():
     ap.add_argument("--width", type=int, default=1024, help="prefill index width (512 or 1024)")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=512)
+    ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample of the prefill tokens (0: all)")
     ap.add_argument("--no-extra", action="store_true", help="skip the few-head and INT8 workloads")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="also run one plain device-to-device copy of MIB MiB (reference for HBM counters)")
@@ -210,6 +210,50 @@ def dots3_lines(torch, smla, W, dev, stream, bf16, args):
     return out
 
 
+def cpu_other_workloads(W, oracle, ncores):
+    """The oracle over the decode batch and the few-head prefill (whole
+    workloads) and a 256-token sample of the INT8 prefill, on `ncores`
+    threads (writing the pools is not timed)."""
+    res = {}
+
+    def pool_of(c):
+        rb = W.ROW_BYTES[c.fmt]
+        p = oracle.Pool(np.zeros((c.num_blocks, 64 * rb), np.uint8), c.fmt, 64 * rb)
+        oracle.quantize_kv(c.kv, c.slots, p)
+        return p
+
+    dc = W.c2_decode()
+    p = pool_of(dc)
+    tc = time.perf_counter()
+    po, pl = oracle.decode_split(dc.q, p, dc.indices, dc.num_splits, sm_scale=dc.sm_scale, nthreads=ncores)
+    oracle.combine(po, pl)
+    dt = time.perf_counter() - tc
+    res["decode"] = {"workload": f"fp8 split-KV decode {dc.T} seqs x 1 query, H={dc.H}, topk={dc.topk}, "
+                                 f"{dc.num_splits} splits + combine (all of it)",
+                     "us_per_call": round(dt * 1e6, 1), "cores": ncores}
+    del p, po, pl, dc
+    fc = W.c4_fewhead()
+    p = pool_of(fc)
+    tc = time.perf_counter()
+    oracle.prefill(fc.q, p, fc.indices, topk_length=fc.topk_length, sink=fc.sink, sm_scale=fc.sm_scale,
+                   nthreads=ncores)
+    dt = time.perf_counter() - tc
+    res["fewhead"] = {"workload": f"bf16 few-head prefill T={fc.T} H={fc.H} topk={fc.topk} (all tokens)",
+                      "us_per_token": round(dt * 1e6 / fc.T, 3), "cores": ncores}
+    del p, fc
+    ic = W.c5_int8()
+    p = pool_of(ic)
+    n = 256  # a bounded sample: the whole workload takes about half a minute on 16 cores
+    tokens = np.linspace(0, ic.T - 1, n).astype(np.int64)
+    tc = time.perf_counter()
+    oracle.prefill(ic.q, p, ic.indices, sink=ic.sink, sm_scale=ic.sm_scale, tokens=tokens, nthreads=ncores)
+    dt = time.perf_counter() - tc
+    res["int8"] = {"workload": f"int8 prefill T={ic.T} H={ic.H} topk={ic.topk} ({n} evenly spaced tokens)",
+                   "us_per_token": round(dt * 1e6 / n, 3), "cores": ncores}
+    print(f"[bench] cpu oracle, other workloads: {json.dumps(res)}", file=sys.stderr, flush=True)
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -305,13 +349,44 @@ def main():
         "prefill_kernel_us_median_p10_p90": [round(p_med, 3), round(p_p10, 3), round(p_p90, 3)],
         "prefill_us_per_token_kernel": round(prefill_ms * 1e3 / T, 5),
         "mfma_util": round(flops / (prefill_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+        # The pool (10.75 MB) is cache-resident, so the gathers are served by
+        # L2/MALL and the dense 64-head x 64-candidate tiles make the kernel
+        # MFMA-bound: achieved = algorithmic FLOP per launch / mean kernel time.
+        "roofline": {"bound": "mfma", "achieved": round(flops / (prefill_ms * 1e-3) / 1e12, 2),
+                     "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(flops / (prefill_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
                      "traffic": traffic,
                      "kernel": "attn_fp8_kernel<prefill> (smla::attn_fp8_kernel<false, false, false, 1>)",
-                     "algorithmic_bytes_per_launch": alg_bytes},
+                     "algorithmic_flop_per_launch": flops,
+                     "algorithmic_bytes_per_launch": alg_bytes,
+                     "hbm_view": {"achieved_GBps": round(achieved, 2), "peak_GBps": HBM_PEAK_GBPS,
+                                  "frac": round(achieved / HBM_PEAK_GBPS, 4)}},
         "kernel_source_sha": sha,
     }
+    # the same prefill at the other index width of the page's measurement
+    other_w = 512 if args.width == 1024 else 1024
+    if not args.no_extra:
+        oc = W.c3_prefill(width=other_w)
+        oidx = torch.from_numpy(oc.idx_buf).to(dev)
+
+        def pre_other():
+            smla.prefill(q, pool, oidx, sm_scale=float(case.sm_scale), out=out, lse=lse)
+
+        pre_other()
+        tw = pct(event_times_us(torch, pre_other, 20, stream))
+        orows = oc.gathered_rows()
+        oflops = 2.0 * H * (D_QK + D_V) * orows
+        result[f"width{other_w}"] = {
+            "workload": f"fp8 prefill T={T} ctx={case.ctx} H={H} topk={other_w} (the same q, pool and causal draw "
+                        "at the other index width)",
+            "kernel_us_median_p10_p90": [round(v, 3) for v in tw],
+            "us_per_token_kernel": round(tw[0] / T, 5),
+            "gathered_kv_bytes": orows * W.ROW_BYTES[W.FMT_FP8],
+            "gathered_kv_GBps": round(orows * W.ROW_BYTES[W.FMT_FP8] / (tw[0] * 1e-6) / 1e9, 2),
+            "mfma_util": round(oflops / (tw[0] * 1e-6) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+        }
+        print(f"[bench] prefill width {other_w}: {tw[0]:.1f} us", file=sys.stderr, flush=True)
+        del oidx
     # the same prefill over FP8 rows with arbitrary scales (GLM_NSA rows)
     if not args.no_extra:
         apool = smla.KVPool.empty(case.num_blocks, W.FMT_FP8_ANY, device=dev)
@@ -504,6 +579,14 @@ def main():
         gr = time_decode_graph(Sm)
         gr["workload"] = "the same batch at the model's split count, decode + combine replayed as one HIP graph"
         result["decode"]["graph"] = gr
+        # decode is bound by HBM: the 656 MiB pool exceeds the caches and the
+        # rows are random.  Gathered-KV bytes per call / graph time per call.
+        dach = dbytes / (gr["graph_us"] * 1e-6) / 1e9
+        result["decode"]["roofline"] = {
+            "bound": "hbm", "achieved": round(dach, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(dach / HBM_PEAK_GBPS, 4), "target_frac": 0.60,
+            "measured_over": f"decode + combine per call, replayed as a HIP graph, {Sm} splits",
+            "algorithmic_bytes_per_call": dbytes}
         print(f"[bench] decode + combine as a HIP graph (S={Sm}): {gr['graph_us']:.2f} us, "
               f"{gr['us_per_call']:.2f} us per call", file=sys.stderr, flush=True)
         if ipool8 is not None:
@@ -715,7 +798,7 @@ def main():
         ncores = min(16, os.cpu_count() or 1)
         pool_h = oracle.Pool(np.zeros((case.num_blocks, 64 * 656), np.uint8), W.FMT_FP8, 64 * 656)
         oracle.quantize_kv(case.kv, case.slots, pool_h)
-        n = min(args.cpu_tokens, T)
+        n = min(args.cpu_tokens, T) if args.cpu_tokens > 0 else T
         tokens = np.linspace(0, T - 1, n).astype(np.int64)
         tc = time.perf_counter()
         oracle.prefill(case.q, pool_h, case.indices, sm_scale=case.sm_scale, tokens=tokens, nthreads=ncores)
@@ -723,8 +806,8 @@ def main():
         result["cpu_baseline"] = {
             "value": round(cpu_s * 1e6 / n, 3), "unit": "us/token", "cores": ncores, "kind": "oracle",
             "host": {"cpu_model": host_cpu_model(), "visible_cpus": os.cpu_count()},
-            "sample": f"{n} of the {T} tokens of the same prefill workload (float64 C oracle, "
-                      f"OpenMP over tokens), {cpu_s:.2f} s wall"}
+            "sample": (f"all {T} tokens" if n == T else f"{n} of the {T} tokens") +
+                      f" of the same prefill workload (float64 C oracle, OpenMP over tokens), {cpu_s:.2f} s wall"}
         print(f"[bench] cpu oracle {cpu_s:.2f}s for {n} tokens on {ncores} threads", file=sys.stderr, flush=True)
         # the tiny BF16 case on one thread (prefill and decode at 1, 2 and 4 splits)
         c1 = W.c1_tiny()
@@ -735,6 +818,9 @@ def main():
         for S in (1, 2, 4):
             oracle.decode_split(c1.q, p1, c1.indices, S, sm_scale=c1.sm_scale, nthreads=1)
         result["cpu_baseline"]["c1_tiny_single_thread_ms"] = round((time.perf_counter() - tc) * 1e3, 3)
+        if not args.no_extra:
+            result["cpu_baseline"]["other_workloads"] = cpu_other_workloads(W, oracle, ncores)
+
 
     print(json.dumps(result), flush=True)
 
