@@ -304,6 +304,29 @@ smla_status smla_attention(const void* q, int64_t T, int32_t H, int64_t q_stride
                            int64_t out_stride_t, int64_t out_stride_h, float* lse, int64_t lse_stride_t,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of the static scratch smla_attention_noalloc uses (64 MiB). */
+#define SMLA_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* smla_attention without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  It computes the same out and lse
+ * with the same kernels; when the split form is chosen, the decode partials
+ * go to a file-scope device array of SMLA_NOALLOC_SCRATCH_BYTES bytes that
+ * each GPU the library runs on holds until the process ends.  The call
+ * allocates nothing (no hipMalloc, no allocating library routine); its
+ * first call on a device looks up that device's copy of the array.  Every
+ * call on one GPU shares the array: calls that overlap on one GPU (e.g. on
+ * two streams) race and must be ordered by the caller.  The array keeps the
+ * last call's partials; each call overwrites all the partials it reads.
+ * Arguments and errors as smla_attention; when the chosen split form needs
+ * more than SMLA_NOALLOC_SCRATCH_BYTES of partials (T*S*H*(4*d_v + 4)
+ * bytes), it returns SMLA_ERR_UNSUPPORTED and launches nothing. */
+smla_status smla_attention_noalloc(const void* q, int64_t T, int32_t H, int64_t q_stride_t, int64_t q_stride_h,
+                                   smla_kv_pool kv, const int32_t* indices, int32_t topk, int64_t idx_stride_t,
+                                   const int32_t* topk_length, const float* sink, float sm_scale, void* out,
+                                   int64_t out_stride_t, int64_t out_stride_h, float* lse, int64_t lse_stride_t,
+                                   void* stream);
+
 /* Message describing the last failed call on this thread ("" if none). */
 const char* smla_last_error(void);
 

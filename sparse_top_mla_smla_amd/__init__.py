@@ -74,12 +74,14 @@ def _load():
     L.smla_attention_workspace_size.restype = ctypes.c_int
     L.smla_attention.argtypes = [P, i64, i32, i64, i64, _Pool, P, i32, i64, P, P, f32, P, i64, i64,
                                  P, i64, P, ctypes.c_size_t, P]
+    L.smla_attention_noalloc.argtypes = [P, i64, i32, i64, i64, _Pool, P, i32, i64, P, P, f32, P, i64, i64,
+                                         P, i64, P]
     PE = ctypes.POINTER(_Extra)
     L.smla_prefill_dual.argtypes = [P, i64, i32, i64, i64, _Pool, P, i32, i64, P, PE, P, f32, P, i64, i64,
                                     P, i64, P]
     L.smla_decode_dual.argtypes = [P, i64, i32, i64, i64, _Pool, P, i32, i64, P, PE, f32, i32, P, P, P]
     for fn in (L.smla_quantize_kv, L.smla_prefill, L.smla_decode, L.smla_combine, L.smla_attention,
-               L.smla_prefill_dual, L.smla_decode_dual):
+               L.smla_attention_noalloc, L.smla_prefill_dual, L.smla_decode_dual):
         fn.restype = ctypes.c_int
     _lib = L
     return L
@@ -353,6 +355,25 @@ def attention(q: torch.Tensor, pool: KVPool, indices: torch.Tensor, topk: Option
                                   ist, _ptr(topk_length), _ptr(sink), float(sm_scale), _ptr(out),
                                   out.stride(0), out.stride(1), _ptr(lse), lse.stride(0), _ptr(workspace),
                                   ws_bytes, _stream(stream)), "smla_attention")
+    return out, lse
+
+
+def attention_noalloc(q: torch.Tensor, pool: KVPool, indices: torch.Tensor, topk: Optional[int] = None,
+                      topk_length: Optional[torch.Tensor] = None, sink: Optional[torch.Tensor] = None,
+                      sm_scale: float = 1.0 / 24.0, out: Optional[torch.Tensor] = None,
+                      lse: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """smla_attention with its decode partials in the library's static
+    device scratch (see smla_attention_noalloc): the library allocates
+    nothing; pass out and lse to allocate nothing here either."""
+    _need(q, "q", torch.bfloat16)
+    T, H, _ = q.shape
+    topk, ist = _idx_args(indices, topk)
+    _check_common(q, pool, indices, topk, topk_length, sink)
+    out, lse = _outputs(q, pool, out, lse)
+    _check(_load().smla_attention_noalloc(_ptr(q), T, H, q.stride(0), q.stride(1), pool.c(), _ptr(indices), topk,
+                                          ist, _ptr(topk_length), _ptr(sink), float(sm_scale), _ptr(out),
+                                          out.stride(0), out.stride(1), _ptr(lse), lse.stride(0), _stream(stream)),
+           "smla_attention_noalloc")
     return out, lse
 
 

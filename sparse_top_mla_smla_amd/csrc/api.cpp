@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "smla.h"
 #include "launch.h"
@@ -386,6 +387,80 @@ smla_status smla_attention(const void* q, int64_t T, int32_t H, int64_t q_stride
     return smla_prefill(q, T, H, q_stride_t, q_stride_h, kv, indices, topk, idx_stride_t, topk_length, sink,
                         sm_scale, out, out_stride_t, out_stride_h, lse, lse_stride_t, stream);
   float* part_out = static_cast<float*>(workspace);
+  float* part_lse = part_out + (size_t)T * (size_t)S * (size_t)H * (size_t)dv;
+  st = smla_decode(q, T, H, q_stride_t, q_stride_h, kv, indices, topk, idx_stride_t, topk_length, sm_scale, S,
+                   part_out, part_lse, stream);
+  if (st != SMLA_OK) return st;
+  return smla_combine(part_out, part_lse, T, S, H, dv, sink, out, out_stride_t, out_stride_h, lse, lse_stride_t,
+                      stream);
+}
+
+// ---------------------------------------------------------------------------
+// smla_attention_noalloc: smla_attention with its decode partials in a
+// file-scope device array instead of a caller's workspace, for callers that
+// cannot allocate.  One copy of the array per device, held until the process
+// ends.  In host code `scratch` names a host-side stand-in, never the device
+// array: its device address comes from hipGetSymbolAddress, once per device
+// (on that device's first call), and only that address reaches the kernels.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[SMLA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {nullptr};
+
+// the device address of the current device's scratch array
+smla_status scratch_of_current_device(void** ptr_out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SMLA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(SMLA_ERR_UNSUPPORTED, "device %d is outside the %d devices the static scratch supports", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(SMLA_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_dev[dev] = ptr;
+  }
+  *ptr_out = g_scratch_dev[dev];
+  return SMLA_OK;
+}
+}  // namespace
+
+smla_status smla_attention_noalloc(const void* q, int64_t T, int32_t H, int64_t q_stride_t, int64_t q_stride_h,
+                                   smla_kv_pool kv, const int32_t* indices, int32_t topk, int64_t idx_stride_t,
+                                   const int32_t* topk_length, const float* sink, float sm_scale, void* out,
+                                   int64_t out_stride_t, int64_t out_stride_h, float* lse, int64_t lse_stride_t,
+                                   void* stream) {
+  smla_status st = check_attn_common(q, T, H, q_stride_t, q_stride_h, kv, indices, topk, idx_stride_t);
+  if (st != SMLA_OK) return st;
+  if (T == 0) return ok();
+  const int32_t dv = smla_value_dims(kv.format);
+  st = check_out(out, out_stride_t, out_stride_h, H, lse, lse_stride_t, dv);
+  if (st != SMLA_OK) return st;
+  if (!std::isfinite(sm_scale)) return fail(SMLA_ERR_SHAPE, "sm_scale must be finite");
+  if (smla_use_split_form(T, H, topk, kv.format, 0) != 1)
+    return smla_prefill(q, T, H, q_stride_t, q_stride_h, kv, indices, topk, idx_stride_t, topk_length, sink,
+                        sm_scale, out, out_stride_t, out_stride_h, lse, lse_stride_t, stream);
+  const int32_t S = smla_decode_num_splits(T, H, topk, kv.format, 0);
+  size_t need = 0;
+  st = smla_decode_workspace_size(T, H, S, dv, &need);
+  if (st != SMLA_OK) return st;
+  if (need > (size_t)SMLA_NOALLOC_SCRATCH_BYTES)
+    return fail(SMLA_ERR_UNSUPPORTED,
+                "the split form chosen for T=%lld, H=%d, topk=%d (%d splits) needs %zu bytes of partials; the static "
+                "scratch holds %zu: call smla_attention with a workspace",
+                (long long)T, H, topk, S, need, (size_t)SMLA_NOALLOC_SCRATCH_BYTES);
+  void* base = nullptr;
+  st = scratch_of_current_device(&base);
+  if (st != SMLA_OK) return st;
+  // every partial and LSE of the T x S x H block is written by the decode
+  // launch (empty splits included), so nothing needs clearing first
+  float* part_out = static_cast<float*>(base);
   float* part_lse = part_out + (size_t)T * (size_t)S * (size_t)H * (size_t)dv;
   st = smla_decode(q, T, H, q_stride_t, q_stride_h, kv, indices, topk, idx_stride_t, topk_length, sm_scale, S,
                    part_out, part_lse, stream);

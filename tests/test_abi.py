@@ -183,3 +183,23 @@ def test_dual_validation_before_launch():
     dec = lib.smla_decode_dual(FAKE, 2, 64, 64 * 576, 576, pool(), FAKE, 64, 64, None, ctypes.byref(extra(topk=0)),
                                f, 2, FAKE, FAKE, None)
     assert dec == 2
+
+
+def test_attention_noalloc_rejects_before_launch():
+    """smla_attention_noalloc: argument errors as smla_attention, and a split
+    form whose partials exceed the static scratch is refused (on the host,
+    before the scratch is looked up or anything is launched)."""
+    lib = smla._load()
+    f = ctypes.c_float(1.0 / 24)
+
+    def call(T=200, H=64, topk=8192, fmt=W.FMT_BF16, q=FAKE, out=FAKE):
+        return lib.smla_attention_noalloc(q, T, H, H * 576, 576, pool(fmt=fmt), FAKE, topk, topk, None, None, f,
+                                          out, H * 512, 512, FAKE, H, None)
+
+    # BF16 rows, T=200, H=64, topk 8192: the split form at 3 splits needs 75 MiB of partials
+    assert smla.use_split_form(200, 64, 8192, W.FMT_BF16, 0) == 1
+    assert call() == 4 and "static scratch" in lib.smla_last_error().decode()
+    assert call(q=None) == 1
+    assert call(out=FAKE + 8) == 3
+    assert call(T=0) == 0
+    assert call(H=129) == 4
