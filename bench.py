@@ -64,6 +64,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample of the prefill tokens (0: all)")
     ap.add_argument("--no-extra", action="store_true", help="skip the few-head and INT8 workloads")
+    ap.add_argument("--only", choices=["int8"], default=None,
+                    help="time only this workload and print its line (for counter passes)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="also run one plain device-to-device copy of MIB MiB (reference for HBM counters)")
     return ap.parse_args()
@@ -84,6 +86,38 @@ def event_times_us(torch, fn, iters, stream):
         b.record(stream)
     torch.cuda.synchronize()
     return [a.elapsed_time(b) * 1e3 for a, b in evs]
+
+
+def gather_ceiling(torch, smla, stream, pool, idx, topk_length, nbytes, expect_rows, iters=10):
+    """The gather probe over the same pool and lists: every selected row moved
+    into LDS as the attention kernels move them, nothing computed.  Its rate
+    is the measured ceiling for gathering these rows."""
+    rows = smla.probe_gather(pool, idx, topk_length=topk_length)
+    torch.cuda.synchronize()
+    moved = int(rows.sum().item())
+    t = pct(event_times_us(torch, lambda: smla.probe_gather(pool, idx, topk_length=topk_length, rows_out=rows),
+                           iters, stream))
+    return {"probe_us_median_p10_p90": [round(v, 3) for v in t], "rows_moved": moved,
+            "rows_match": moved == expect_rows, "GBps": round(nbytes / (t[0] * 1e-6) / 1e9, 2)}
+
+
+def device_section(torch, smla, dev):
+    """Device attributes, the shader clock measured under an MFMA load, and
+    the peaks derived from both beside the spec values."""
+    props = torch.cuda.get_device_properties(dev)
+    a = smla.device_attributes()
+    cus = a["compute_units"]
+    out = smla.probe_clock(cus, 20000).cpu().numpy().astype(np.float64)
+    mhz = float(np.median(out[:, 0] / out[:, 1] * a["wall_clock_khz"] / 1000.0))
+    flop_per_clk = cus * 4 * 1024  # 32x32x16 BF16 MFMA: 32 cycles per SIMD, four SIMDs per CU
+    hbm_attr = a["memory_clock_khz"] * 1e3 * 2 * a["memory_bus_bits"] / 8 / 1e9
+    return {"name": props.name, "arch": getattr(props, "gcnArchName", ""), "compute_units": cus,
+            "memory_GiB": round(props.total_memory / 2**30, 1), "attributes": a,
+            "measured_clock_MHz_under_mfma_load": round(mhz, 1),
+            "bf16_mfma_TFLOPs_at_peak_clock": round(flop_per_clk * a["clock_khz"] * 1e3 / 1e12, 1),
+            "bf16_mfma_TFLOPs_at_measured_clock": round(flop_per_clk * mhz * 1e6 / 1e12, 1),
+            "hbm_GBps_from_attributes": round(hbm_attr, 1),
+            "spec_hbm_GBps": HBM_PEAK_GBPS, "spec_bf16_mfma_TFLOPs": BF16_MFMA_PEAK_TFLOPS}
 
 
 def host_cpu_model() -> str:
@@ -254,6 +288,46 @@ def cpu_other_workloads(W, oracle, ncores):
     return res
 
 
+def int8_line(torch, smla, W, dev, stream, bf16, iters=10):
+    """C5: INT8 prefill, T = 1024, H = 128, ctx 65536, top-k 2048 as a view of
+    a 4096-wide index buffer, with a sink."""
+    result = {}
+    # INT8, 128 heads, narrowed index view
+    ic = W.c5_int8()
+    iq = bf16(ic.q_buf)
+    ikv = bf16(ic.kv)
+    ipool = smla.KVPool.empty(ic.num_blocks, W.FMT_INT8, device=dev)
+    smla.quantize_kv(ikv, torch.from_numpy(ic.slots).to(dev), ipool)
+    del ikv
+    iidx = torch.from_numpy(ic.idx_buf).to(dev)[:, : ic.topk]
+    isink = torch.from_numpy(ic.sink).to(dev)
+    iout = torch.empty((ic.T, ic.H, D_V), dtype=torch.bfloat16, device=dev)
+    ilse = torch.empty((ic.T, ic.H), dtype=torch.float32, device=dev)
+
+    def i8():
+        smla.prefill(iq[:, : ic.H], ipool, iidx, sink=isink, sm_scale=float(ic.sm_scale), out=iout, lse=ilse)
+
+    i8()
+    ti = event_times_us(torch, i8, iters, stream)
+    irows = ic.gathered_rows()
+    ibytes = irows * W.ROW_BYTES[W.FMT_INT8]
+    iflops = 2.0 * ic.H * (D_QK + D_V) * irows
+    i_med = pct(ti)
+    result["int8"] = {
+        "workload": f"int8 prefill T={ic.T} H={ic.H} ctx {ic.ctx} topk {ic.topk} (index view of stride "
+                    f"{ic.idx_buf.shape[1]}), sink",
+        "kernel_us_median_p10_p90": [round(v, 3) for v in i_med],
+        "us_per_token": round(i_med[0] / ic.T, 5),
+        "gathered_kv_bytes": ibytes,
+        "gathered_kv_GBps": round(ibytes / (i_med[0] * 1e-6) / 1e9, 2),
+        "mfma_util": round(iflops / (i_med[0] * 1e-6) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+    }
+    print(f"[bench] int8 {i_med[0]:.1f} us", file=sys.stderr, flush=True)
+    del iq, ipool, iidx, iout, ilse
+    torch.cuda.empty_cache()
+    return result["int8"]
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -275,6 +349,11 @@ def main():
 
     def bf16(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    if args.only == "int8":
+        print(json.dumps({"int8": int8_line(torch, smla, W, dev, torch.cuda.current_stream(), bf16,
+                                            max(args.steps, 1))}), flush=True)
+        return
 
     # ---------------- prefill workload ----------------
     t0 = time.time()
@@ -429,11 +508,10 @@ def main():
         }}
         print(f"[bench] dsv4 prefill {t4[0]:.1f} us", file=sys.stderr, flush=True)
         del v4pool, v4out
-    props = torch.cuda.get_device_properties(dev)
-    result["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
-                        "compute_units": props.multi_processor_count,
-                        "memory_GiB": round(props.total_memory / 2**30, 1),
-                        "spec_hbm_GBps": HBM_PEAK_GBPS, "spec_bf16_mfma_TFLOPs": BF16_MFMA_PEAK_TFLOPS}
+    result["device"] = device_section(torch, smla, dev)
+    # the gather ceiling of the metric workload's lists (cache-resident pool)
+    result["gather_ceiling"] = gather_ceiling(torch, smla, stream, pool, idx, None, kv_bytes, rows)
+    result["gather_ceiling"]["workload"] = "the gather probe over the metric workload's pool and lists"
     print(f"[bench] prefill setup {setup_s:.1f}s, step {ms_per_step:.3f} ms, kernel {prefill_ms:.3f} ms",
           file=sys.stderr, flush=True)
 
@@ -565,6 +643,19 @@ def main():
                         f"topk={dc.topk}, splits={S} (decode + combine)",
             "gathered_kv_bytes": dbytes,
         }
+        # the gather ceiling of these rows from HBM (a fresh index set per call)
+        pc = [0]
+
+        def probe_dec():
+            pc[0] += 1
+            smla.probe_gather(dpool, idx_sets[pc[0] % 3])
+
+        probe_dec()
+        tpd = pct(event_times_us(torch, probe_dec, 12, stream))
+        result["decode"]["gather_ceiling"] = {
+            "workload": "the gather probe over the decode batch's lists (rotating index sets)",
+            "probe_us_median_p10_p90": [round(v, 3) for v in tpd],
+            "GBps": round(dbytes / (tpd[0] * 1e-6) / 1e9, 2)}
         result["decode"].update(time_decode(S))
         # the split count the library's cost model picks for this shape on this device
         Sm = smla.decode_num_splits(dc.T, dc.H, dc.topk, W.FMT_FP8)
@@ -586,7 +677,8 @@ def main():
             "bound": "hbm", "achieved": round(dach, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(dach / HBM_PEAK_GBPS, 4), "target_frac": 0.60,
             "measured_over": f"decode + combine per call, replayed as a HIP graph, {Sm} splits",
-            "algorithmic_bytes_per_call": dbytes}
+            "algorithmic_bytes_per_call": dbytes,
+            "frac_of_measured_gather_ceiling": round(dach / result["decode"]["gather_ceiling"]["GBps"], 4)}
         print(f"[bench] decode + combine as a HIP graph (S={Sm}): {gr['graph_us']:.2f} us, "
               f"{gr['us_per_call']:.2f} us per call", file=sys.stderr, flush=True)
         if ipool8 is not None:
@@ -722,10 +814,15 @@ def main():
             "us_per_token": round(f_med[0] / fc.T, 5),
             "gathered_kv_bytes": fbytes,
             "gathered_kv_GBps": round(fbytes / (f_med[0] * 1e-6) / 1e9, 2),
-            "hbm_frac": round(fbytes / (f_med[0] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
             "same_inputs_all_64_heads_us_median": round(pct(t64)[0], 3),
             "speedup_vs_64_heads": round(pct(t64)[0] / f_med[0], 3),
         }
+        # the pool (36 MiB) is cache-resident: the rate is put against the
+        # measured gather ceiling of the same rows rather than HBM peak
+        fc_ceil = gather_ceiling(torch, smla, stream, fpool, fidx, ftl, fbytes, frows)
+        result["fewhead"]["gather_ceiling"] = fc_ceil
+        result["fewhead"]["frac_of_gather_ceiling"] = round(
+            result["fewhead"]["gathered_kv_GBps"] / fc_ceil["GBps"], 4)
         print(f"[bench] fewhead {f_med[0]:.1f} us (64 heads: {pct(t64)[0]:.1f} us)", file=sys.stderr, flush=True)
 
         def few8():
@@ -744,38 +841,7 @@ def main():
         print(f"[bench] fewhead over FP8 rows {t8f[0]:.1f} us", file=sys.stderr, flush=True)
         del fq, fpool, f8pool, fidx, ftl, fout, flse
         torch.cuda.empty_cache()
-        # INT8, 128 heads, narrowed index view
-        ic = W.c5_int8()
-        iq = bf16(ic.q_buf)
-        ikv = bf16(ic.kv)
-        ipool = smla.KVPool.empty(ic.num_blocks, W.FMT_INT8, device=dev)
-        smla.quantize_kv(ikv, torch.from_numpy(ic.slots).to(dev), ipool)
-        del ikv
-        iidx = torch.from_numpy(ic.idx_buf).to(dev)[:, : ic.topk]
-        isink = torch.from_numpy(ic.sink).to(dev)
-        iout = torch.empty((ic.T, ic.H, D_V), dtype=torch.bfloat16, device=dev)
-        ilse = torch.empty((ic.T, ic.H), dtype=torch.float32, device=dev)
-
-        def i8():
-            smla.prefill(iq[:, : ic.H], ipool, iidx, sink=isink, sm_scale=float(ic.sm_scale), out=iout, lse=ilse)
-
-        i8()
-        ti = event_times_us(torch, i8, iters, stream)
-        irows = ic.gathered_rows()
-        ibytes = irows * W.ROW_BYTES[W.FMT_INT8]
-        iflops = 2.0 * ic.H * (D_QK + D_V) * irows
-        i_med = pct(ti)
-        result["int8"] = {
-            "workload": f"int8 prefill T={ic.T} H={ic.H} ctx {ic.ctx} topk {ic.topk} (index view of stride "
-                        f"{ic.idx_buf.shape[1]}), sink",
-            "kernel_us_median_p10_p90": [round(v, 3) for v in i_med],
-            "us_per_token": round(i_med[0] / ic.T, 5),
-            "gathered_kv_bytes": ibytes,
-            "gathered_kv_GBps": round(ibytes / (i_med[0] * 1e-6) / 1e9, 2),
-            "mfma_util": round(iflops / (i_med[0] * 1e-6) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
-        }
-        print(f"[bench] int8 {i_med[0]:.1f} us", file=sys.stderr, flush=True)
-        del iq, ipool, iidx, iout, ilse
+        result["int8"] = int8_line(torch, smla, W, dev, stream, bf16, iters)
         torch.cuda.empty_cache()
 
     # ---------------- DOTS3_SWA rows ----------------

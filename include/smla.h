@@ -304,6 +304,34 @@ smla_status smla_attention(const void* q, int64_t T, int32_t H, int64_t q_stride
                            int64_t out_stride_t, int64_t out_stride_h, float* lse, int64_t lse_stride_t,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- Measurement aids (not steps of the attention path) ---- */
+
+/* Gather probe: moves every candidate row of each token's list (positions
+ * j < L_t whose index is a slot of the pool, as in smla_prefill) into LDS
+ * the way the attention kernels gather them -- 64 rows per tile, 16-byte
+ * direct-to-LDS pieces -- and computes nothing on them; its time is a
+ * measured ceiling for gathering those rows.  rows_out (uint32 [T], device)
+ * receives the number of rows moved for each token (it is cleared with
+ * hipMemsetAsync first, so the probe is not for graph capture).  Pools of 656- or
+ * 1152-byte rows only (SMLA_ERR_UNSUPPORTED otherwise); other arguments as
+ * in smla_prefill. */
+smla_status smla_probe_gather(smla_kv_pool kv, const int32_t* indices, int64_t T, int32_t topk, int64_t idx_stride_t,
+                              const int32_t* topk_length, uint32_t* rows_out, void* stream);
+
+/* Clock probe: `blocks` workgroups of 4 waves each run `iters` rounds of
+ * four independent BF16 MFMAs and record the shader clock counter and the
+ * constant-rate counter around them; out (uint64 [2*blocks], device)
+ * receives per workgroup {shader cycles, constant-rate ticks}.  With the
+ * constant rate from smla_device_attributes this gives the shader clock
+ * under matrix load. */
+smla_status smla_probe_clock(uint64_t* out, int32_t blocks, int32_t iters, void* stream);
+
+/* Attributes of the current device: attrs[0] compute units, attrs[1] peak
+ * shader clock (kHz), attrs[2] constant-rate counter clock (kHz), attrs[3]
+ * memory clock (kHz), attrs[4] memory bus width (bits).  attrs is host
+ * memory, int32 [5]. */
+smla_status smla_device_attributes(int32_t* attrs);
+
 /* Bytes of the static scratch smla_attention_noalloc uses (64 MiB). */
 #define SMLA_NOALLOC_SCRATCH_BYTES (64u << 20)
 

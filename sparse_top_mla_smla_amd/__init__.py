@@ -76,12 +76,16 @@ def _load():
                                  P, i64, P, ctypes.c_size_t, P]
     L.smla_attention_noalloc.argtypes = [P, i64, i32, i64, i64, _Pool, P, i32, i64, P, P, f32, P, i64, i64,
                                          P, i64, P]
+    L.smla_probe_gather.argtypes = [_Pool, P, i64, i32, i64, P, P, P]
+    L.smla_probe_clock.argtypes = [P, i32, i32, P]
+    L.smla_device_attributes.argtypes = [ctypes.POINTER(ctypes.c_int32)]
     PE = ctypes.POINTER(_Extra)
     L.smla_prefill_dual.argtypes = [P, i64, i32, i64, i64, _Pool, P, i32, i64, P, PE, P, f32, P, i64, i64,
                                     P, i64, P]
     L.smla_decode_dual.argtypes = [P, i64, i32, i64, i64, _Pool, P, i32, i64, P, PE, f32, i32, P, P, P]
     for fn in (L.smla_quantize_kv, L.smla_prefill, L.smla_decode, L.smla_combine, L.smla_attention,
-               L.smla_attention_noalloc, L.smla_prefill_dual, L.smla_decode_dual):
+               L.smla_attention_noalloc, L.smla_prefill_dual, L.smla_decode_dual, L.smla_probe_gather,
+               L.smla_probe_clock, L.smla_device_attributes):
         fn.restype = ctypes.c_int
     _lib = L
     return L
@@ -425,3 +429,49 @@ def decode_dual(q: torch.Tensor, pool: KVPool, indices: torch.Tensor, extra_pool
                                     _ptr(topk_length), ctypes.byref(ex), float(sm_scale), num_splits,
                                     _ptr(part_out), _ptr(part_lse), _stream(stream)), "smla_decode_dual")
     return part_out, part_lse
+
+
+# ---- measurement aids (not steps of the attention path) ----
+
+def probe_gather(pool: KVPool, indices: torch.Tensor, topk: Optional[int] = None,
+                 topk_length: Optional[torch.Tensor] = None, rows_out: Optional[torch.Tensor] = None,
+                 stream=None) -> torch.Tensor:
+    """Moves every candidate row of each token's list into LDS as the
+    attention kernels gather them, computing nothing (see smla_probe_gather);
+    returns the rows moved per token (int32 view of uint32 [T])."""
+    topk, ist = _idx_args(indices, topk)
+    T = indices.shape[0]
+    if topk > indices.shape[1]:
+        raise SmlaError(f"topk {topk} exceeds the index rows' {indices.shape[1]} columns")
+    if topk_length is not None:
+        _need(topk_length, "topk_length", torch.int32)
+        if topk_length.numel() < T:
+            raise SmlaError(f"topk_length holds {topk_length.numel()} entries for {T} tokens")
+    if rows_out is None:
+        rows_out = torch.empty(T, dtype=torch.int32, device=indices.device)
+    _need(rows_out, "rows_out", torch.int32)
+    _shape(rows_out, "rows_out", (T,))
+    _check(_load().smla_probe_gather(pool.c(), _ptr(indices), T, topk, ist, _ptr(topk_length), _ptr(rows_out),
+                                     _stream(stream)), "smla_probe_gather")
+    return rows_out
+
+
+def probe_clock(blocks: int, iters: int, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Shader-clock cycles and constant-rate ticks per workgroup around an
+    MFMA loop (see smla_probe_clock): int64 [blocks, 2] on the device."""
+    if out is None:
+        out = torch.empty((blocks, 2), dtype=torch.int64, device="cuda")
+    _need(out, "out", torch.int64)
+    _shape(out, "out", (blocks, 2))
+    _check(_load().smla_probe_clock(_ptr(out), blocks, iters, _stream(stream)), "smla_probe_clock")
+    return out
+
+
+def device_attributes() -> dict:
+    """Compute units, peak shader clock, constant-rate clock and memory clock
+    (kHz) and memory bus width (bits) of the current device."""
+    a = (ctypes.c_int32 * 5)()
+    _check(_load().smla_device_attributes(a), "smla_device_attributes")
+    return {"compute_units": a[0], "clock_khz": a[1], "wall_clock_khz": a[2], "memory_clock_khz": a[3],
+            "memory_bus_bits": a[4]}
+

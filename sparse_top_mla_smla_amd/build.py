@@ -15,7 +15,7 @@ OUT = os.path.join(HERE, "libsmla.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["api.cpp", "quantize.hip", "attention.hip", "attention_fp8.hip",
-           "attention_mx.hip", "attention_bf16.hip", "combine.hip", "split_model.cpp"]
+           "attention_mx.hip", "attention_bf16.hip", "combine.hip", "split_model.cpp", "probe.hip"]
 # -packed-fp32-ops: keep the compiler from emitting packed FP32 VALU ops.
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-Wall",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -396,6 +396,63 @@ smla_status smla_attention(const void* q, int64_t T, int32_t H, int64_t q_stride
 }
 
 // ---------------------------------------------------------------------------
+// Measurement aids
+// ---------------------------------------------------------------------------
+smla_status smla_probe_gather(smla_kv_pool kv, const int32_t* indices, int64_t T, int32_t topk, int64_t idx_stride_t,
+                              const int32_t* topk_length, uint32_t* rows_out, void* stream) {
+  if (T < 0 || T > INT32_MAX) return fail(SMLA_ERR_SHAPE, "T = %lld must be in [0, 2^31-1]", (long long)T);
+  if (T == 0) return ok();
+  if (topk < 1) return fail(SMLA_ERR_SHAPE, "topk = %d must be >= 1", topk);
+  if (!indices || !rows_out) return fail(SMLA_ERR_NULL, "indices or rows_out is NULL");
+  smla_status st = check_pool(kv);
+  if (st != SMLA_OK) return st;
+  const int32_t rb = smla_row_bytes(kv.format);
+  if (rb != 656 && rb != 1152)
+    return fail(SMLA_ERR_UNSUPPORTED, "the gather probe takes 656- or 1152-byte rows, not %d-byte ones", rb);
+  if (idx_stride_t < topk)
+    return fail(SMLA_ERR_STRIDE, "idx_stride_t = %lld is smaller than topk = %d", (long long)idx_stride_t, topk);
+  smla::GatherProbeParams p;
+  p.pool = static_cast<const uint8_t*>(kv.base);
+  p.block_stride = kv.block_stride_bytes;
+  p.row_stride = kv.row_stride_bytes ? kv.row_stride_bytes : rb;
+  p.nslots = kv.num_blocks * 64;
+  p.idx = indices;
+  p.idx_st = idx_stride_t;
+  p.topk = topk;
+  p.topk_length = topk_length;
+  p.T = T;
+  p.rows_out = rows_out;
+  // rows_out accumulates over the workgroups that share a token
+  hipError_t e = hipMemsetAsync(rows_out, 0, (size_t)T * sizeof(uint32_t), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SMLA_ERR_HIP, "clearing rows_out failed: %s", hipGetErrorString(e));
+  return launched(smla::launch_gather_probe(p, rb / 16, static_cast<hipStream_t>(stream)), "gather probe");
+}
+
+smla_status smla_probe_clock(uint64_t* out, int32_t blocks, int32_t iters, void* stream) {
+  if (!out) return fail(SMLA_ERR_NULL, "out is NULL");
+  if (blocks < 1 || blocks > 65536 || iters < 1)
+    return fail(SMLA_ERR_SHAPE, "blocks = %d must be in [1, 65536] and iters = %d >= 1", blocks, iters);
+  return launched(smla::launch_clock_probe(out, blocks, iters, static_cast<hipStream_t>(stream)), "clock probe");
+}
+
+smla_status smla_device_attributes(int32_t* attrs) {
+  if (!attrs) return fail(SMLA_ERR_NULL, "attrs is NULL");
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SMLA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  const hipDeviceAttribute_t which[5] = {hipDeviceAttributeMultiprocessorCount, hipDeviceAttributeClockRate,
+                                         hipDeviceAttributeWallClockRate, hipDeviceAttributeMemoryClockRate,
+                                         hipDeviceAttributeMemoryBusWidth};
+  for (int i = 0; i < 5; ++i) {
+    int v = 0;
+    e = hipDeviceGetAttribute(&v, which[i], dev);
+    if (e != hipSuccess) return fail(SMLA_ERR_HIP, "hipDeviceGetAttribute(%d) failed: %s", (int)which[i], hipGetErrorString(e));
+    attrs[i] = v;
+  }
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
 // smla_attention_noalloc: smla_attention with its decode partials in a
 // file-scope device array instead of a caller's workspace, for callers that
 // cannot allocate.  One copy of the array per device, held until the process

@@ -69,7 +69,22 @@ struct CombineParams {
   int64_t lse_st;
 };
 
+// the gather probe (a measurement aid): rows of a candidate list moved into
+// LDS with nothing computed on them
+struct GatherProbeParams {
+  const uint8_t* pool;
+  int64_t block_stride, row_stride, nslots;
+  const int32_t* idx;
+  int64_t idx_st;
+  int32_t topk;
+  const int32_t* topk_length;  // may be null
+  int64_t T;
+  uint32_t* rows_out;          // [T]
+};
+
 hipError_t launch_quantize(const QuantParams& p, int fmt, hipStream_t s);
+hipError_t launch_gather_probe(const GatherProbeParams& p, int chunks, hipStream_t s);
+hipError_t launch_clock_probe(uint64_t* out, int blocks, int iters, hipStream_t s);
 hipError_t launch_attention(const AttnParams& p, int fmt, bool decode, hipStream_t s);
 hipError_t launch_attention_fp8(const AttnParams& p, int fmt, bool decode, hipStream_t s);
 hipError_t launch_attention_mx(const AttnParams& p, int fmt, bool decode, hipStream_t s);

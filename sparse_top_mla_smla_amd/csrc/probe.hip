@@ -1,0 +1,121 @@
+// probe.hip -- measurement aids beside the attention path: the gather
+// ceiling of a candidate list, the shader clock under matrix load, and the
+// device attributes the peak figures derive from.  None of them is a step of
+// the attention computation; the benchmark uses them to put its rates
+// against measured ceilings.
+#include "device_common.h"
+#include "launch.h"
+#include "lists.h"
+
+namespace smla {
+
+namespace probe {
+constexpr int NT = 512;  // eight waves, as the many-head attention kernel
+constexpr int TC = 64;   // rows per tile
+
+__device__ __forceinline__ void global_to_lds_16(const void* src, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                   (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
+}  // namespace probe
+
+// Every candidate row of every token's list moved into LDS with 16-byte
+// direct-to-LDS loads, nothing computed on them.  Eight lanes share a row
+// and read 128 contiguous bytes of it per instruction (the most cache-line
+// friendly a 16-byte load can be), so a wave moves 8 rows.  A tile is 64
+// rows; workgroup (x, y) takes tokens x, x + gridDim.x, ..., and of each
+// token tiles y, y + gridDim.y, ..., wave w moving rows [8w, 8w + 8) of a
+// tile.  A wave loads the next tile's index entries before it issues the
+// current tile's pieces, so waiting for those entries never waits for the
+// current gathers: up to two tiles per wave are in flight.  The LDS
+// contents are never read.  rows_out[t] receives the number of candidate
+// rows of token t.
+template <int CHUNKS>
+__global__ __launch_bounds__(probe::NT, 1) void gather_probe_kernel(GatherProbeParams p) {
+  using namespace probe;
+  constexpr int CG = (CHUNKS + 7) / 8;  // groups of eight pieces per row
+  __shared__ __attribute__((aligned(16))) uint8_t buf[8 * 1024];
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int r8 = lane >> 3, c8 = lane & 7;  // the lane's row of the wave's 8, and piece of a group
+  const PoolRef pool{p.pool, p.block_stride, p.row_stride, p.nslots};
+  for (int64_t t = blockIdx.x; t < p.T; t += gridDim.x) {
+    const int32_t L = p.topk_length ? clamp_len(p.topk_length[t], p.topk) : p.topk;
+    const int32_t tiles = (L + TC - 1) / TC;
+    const int32_t* row_idx = p.idx + t * p.idx_st;
+    int32_t k = (int32_t)blockIdx.y;
+    const int32_t r = 8 * w + r8;  // row within a tile
+    uint32_t n = 0;
+    int32_t x = (k < tiles && TC * k + r < L) ? row_idx[TC * k + r] : -1;
+    while (k < tiles) {
+      const int32_t kn = k + (int32_t)gridDim.y;
+      const int32_t xn = (kn < tiles && TC * kn + r < L) ? row_idx[TC * kn + r] : -1;
+      const uint8_t* row = TC * k + r < L ? row_in(pool, x) : nullptr;
+      n += __popcll(__ballot(row != nullptr && c8 == 0));
+      const uint8_t* from = row ? row : p.pool;
+#pragma unroll
+      for (int cg = 0; cg < CG; ++cg) {
+        const int ck = 8 * cg + c8;
+        if (ck < CHUNKS) global_to_lds_16(from + 16 * ck, buf + w * 1024);
+      }
+      x = xn;
+      k = kn;
+    }
+    if (lane == 0 && n) atomicAdd(p.rows_out + t, n);
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // no gather lands after the workgroup ends
+}
+
+hipError_t launch_gather_probe(const GatherProbeParams& p, int chunks, hipStream_t s) {
+  const int cus = device_compute_units();
+  // about two workgroups' worth of tokens and tiles per compute unit
+  const int64_t gx = p.T < 2 * cus ? p.T : 2 * cus;
+  const int64_t gy_want = (2 * cus + gx - 1) / gx;
+  const int64_t max_tiles = (p.topk + probe::TC - 1) / probe::TC;
+  dim3 grid((unsigned)gx, (unsigned)(gy_want < max_tiles ? gy_want : max_tiles)), block(probe::NT);
+  switch (chunks) {
+    case 41: hipLaunchKernelGGL(gather_probe_kernel<41>, grid, block, 0, s, p); break;   // 656-byte rows
+    case 72: hipLaunchKernelGGL(gather_probe_kernel<72>, grid, block, 0, s, p); break;   // 1152-byte rows
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// Each wave of every workgroup runs `iters` dependent rounds of four
+// independent 32x32x16 BF16 MFMAs (the matrix units stay busy) and records
+// the shader clock and the constant-rate clock around them; out receives,
+// per workgroup, {shader cycles, constant-rate ticks}.
+__global__ __launch_bounds__(256) void clock_probe_kernel(uint64_t* out, int iters) {
+  typedef float f32x16 __attribute__((ext_vector_type(16)));
+  f32x16 acc[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[k][i] = 0.0f;
+  const bf16x8 a = __builtin_bit_cast(bf16x8, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
+  __syncthreads();
+  const uint64_t c0 = __builtin_readcyclecounter();
+  const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, a, acc[k], 0, 0, 0);
+  }
+  float keep = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) keep += acc[k][0];
+  __syncthreads();
+  const uint64_t c1 = __builtin_readcyclecounter();
+  const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+  if (threadIdx.x == 0) {
+    out[2 * blockIdx.x] = c1 - c0 + (keep == 12345.0f ? 1u : 0u);
+    out[2 * blockIdx.x + 1] = r1 - r0;
+  }
+}
+
+hipError_t launch_clock_probe(uint64_t* out, int blocks, int iters, hipStream_t s) {
+  hipLaunchKernelGGL(clock_probe_kernel, dim3((unsigned)blocks), dim3(256), 0, s, out, iters);
+  return hipGetLastError();
+}
+
+}  // namespace smla

@@ -203,3 +203,15 @@ def test_attention_noalloc_rejects_before_launch():
     assert call(out=FAKE + 8) == 3
     assert call(T=0) == 0
     assert call(H=129) == 4
+
+
+def test_probe_validation_before_launch():
+    """The measurement aids check their arguments on the host."""
+    lib = smla._load()
+    assert lib.smla_probe_gather(pool(), FAKE, 0, 64, 64, None, FAKE, None) == 0          # T = 0: nothing
+    assert lib.smla_probe_gather(pool(), None, 2, 64, 64, None, FAKE, None) == 1
+    assert lib.smla_probe_gather(pool(), FAKE, 2, 64, 32, None, FAKE, None) == 3          # stride < topk
+    assert lib.smla_probe_gather(pool(fmt=W.FMT_FP8_DSV4), FAKE, 2, 64, 64, None, FAKE, None) == 4
+    assert lib.smla_probe_clock(None, 4, 10, None) == 1
+    assert lib.smla_probe_clock(FAKE, 0, 10, None) == 2
+    assert lib.smla_device_attributes(None) == 1
