@@ -88,15 +88,34 @@ def event_times_us(torch, fn, iters, stream):
     return [a.elapsed_time(b) * 1e3 for a, b in evs]
 
 
-def gather_ceiling(torch, smla, stream, pool, idx, topk_length, nbytes, expect_rows, iters=10):
+def queued_times_us(torch, fn, iters, stream, n=20):
+    """Per-call times (us) of n back-to-back calls of fn(), queued behind a
+    sleep kernel so that the host's enqueue cost never leaves the GPU idle
+    between them (a kernel shorter than that cost is otherwise timed with
+    the gaps); one value per batch."""
+    out = []
+    for _ in range(iters):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(20_000_000)
+        a.record(stream)
+        for _ in range(n):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        out.append(a.elapsed_time(b) * 1e3 / n)
+    return out
+
+
+def gather_ceiling(torch, smla, stream, pool, idx, topk_length, nbytes, expect_rows, iters=5):
     """The gather probe over the same pool and lists: every selected row moved
-    into LDS as the attention kernels move them, nothing computed.  Its rate
-    is the measured ceiling for gathering these rows."""
+    into LDS, nothing computed.  Its rate is the measured ceiling for
+    gathering these rows."""
     rows = smla.probe_gather(pool, idx, topk_length=topk_length)
     torch.cuda.synchronize()
     moved = int(rows.sum().item())
-    t = pct(event_times_us(torch, lambda: smla.probe_gather(pool, idx, topk_length=topk_length, rows_out=rows),
-                           iters, stream))
+    t = pct(queued_times_us(torch, lambda: smla.probe_gather(pool, idx, topk_length=topk_length, rows_out=rows),
+                            iters, stream))
     return {"probe_us_median_p10_p90": [round(v, 3) for v in t], "rows_moved": moved,
             "rows_match": moved == expect_rows, "GBps": round(nbytes / (t[0] * 1e-6) / 1e9, 2)}
 
@@ -651,7 +670,7 @@ def main():
             smla.probe_gather(dpool, idx_sets[pc[0] % 3])
 
         probe_dec()
-        tpd = pct(event_times_us(torch, probe_dec, 12, stream))
+        tpd = pct(queued_times_us(torch, probe_dec, 5, stream))
         result["decode"]["gather_ceiling"] = {
             "workload": "the gather probe over the decode batch's lists (rotating index sets)",
             "probe_us_median_p10_p90": [round(v, 3) for v in tpd],

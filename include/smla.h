@@ -308,11 +308,12 @@ smla_status smla_attention(const void* q, int64_t T, int32_t H, int64_t q_stride
 
 /* Gather probe: moves every candidate row of each token's list (positions
  * j < L_t whose index is a slot of the pool, as in smla_prefill) into LDS
- * the way the attention kernels gather them -- 64 rows per tile, 16-byte
- * direct-to-LDS pieces -- and computes nothing on them; its time is a
- * measured ceiling for gathering those rows.  rows_out (uint32 [T], device)
- * receives the number of rows moved for each token (it is cleared with
- * hipMemsetAsync first, so the probe is not for graph capture).  Pools of 656- or
+ * with 16-byte direct-to-LDS pieces, eight lanes per row, one long-lived
+ * workgroup per compute unit, the index entries of up to eight tiles
+ * loaded before their gathers are issued -- and computes nothing on them;
+ * its time is a measured ceiling for gathering those rows.  rows_out
+ * (uint32 [T], device) receives the number of rows moved for each token
+ * (a kernel on the same stream clears it first).  Pools of 656- or
  * 1152-byte rows only (SMLA_ERR_UNSUPPORTED otherwise); other arguments as
  * in smla_prefill. */
 smla_status smla_probe_gather(smla_kv_pool kv, const int32_t* indices, int64_t T, int32_t topk, int64_t idx_stride_t,

@@ -422,9 +422,6 @@ smla_status smla_probe_gather(smla_kv_pool kv, const int32_t* indices, int64_t T
   p.topk_length = topk_length;
   p.T = T;
   p.rows_out = rows_out;
-  // rows_out accumulates over the workgroups that share a token
-  hipError_t e = hipMemsetAsync(rows_out, 0, (size_t)T * sizeof(uint32_t), static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(SMLA_ERR_HIP, "clearing rows_out failed: %s", hipGetErrorString(e));
   return launched(smla::launch_gather_probe(p, rb / 16, static_cast<hipStream_t>(stream)), "gather probe");
 }
 

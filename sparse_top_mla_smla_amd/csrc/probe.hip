@@ -12,6 +12,7 @@ namespace smla {
 namespace probe {
 constexpr int NT = 512;  // eight waves, as the many-head attention kernel
 constexpr int TC = 64;   // rows per tile
+constexpr int PASS = 8;  // tiles per wave whose gathers are issued together
 
 __device__ __forceinline__ void global_to_lds_16(const void* src, void* lds_wave_base) {
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
@@ -25,11 +26,12 @@ __device__ __forceinline__ void global_to_lds_16(const void* src, void* lds_wave
 // friendly a 16-byte load can be), so a wave moves 8 rows.  A tile is 64
 // rows; workgroup (x, y) takes tokens x, x + gridDim.x, ..., and of each
 // token tiles y, y + gridDim.y, ..., wave w moving rows [8w, 8w + 8) of a
-// tile.  A wave loads the next tile's index entries before it issues the
-// current tile's pieces, so waiting for those entries never waits for the
-// current gathers: up to two tiles per wave are in flight.  The LDS
-// contents are never read.  rows_out[t] receives the number of candidate
-// rows of token t.
+// tile.  A wave takes its tiles in passes of PASS: it loads the index
+// entries of all of them at once and then issues all of their gathers, so
+// one index round trip per pass is all the gathers wait for, and the time
+// measured is that of moving the rows, not of a chain of dependent loads.
+// The LDS contents are never read.  rows_out[t] receives the number of
+// candidate rows of token t.
 template <int CHUNKS>
 __global__ __launch_bounds__(probe::NT, 1) void gather_probe_kernel(GatherProbeParams p) {
   using namespace probe;
@@ -44,34 +46,51 @@ __global__ __launch_bounds__(probe::NT, 1) void gather_probe_kernel(GatherProbeP
     const int32_t L = p.topk_length ? clamp_len(p.topk_length[t], p.topk) : p.topk;
     const int32_t tiles = (L + TC - 1) / TC;
     const int32_t* row_idx = p.idx + t * p.idx_st;
-    int32_t k = (int32_t)blockIdx.y;
     const int32_t r = 8 * w + r8;  // row within a tile
+    const int32_t gy = (int32_t)gridDim.y;
     uint32_t n = 0;
-    int32_t x = (k < tiles && TC * k + r < L) ? row_idx[TC * k + r] : -1;
-    while (k < tiles) {
-      const int32_t kn = k + (int32_t)gridDim.y;
-      const int32_t xn = (kn < tiles && TC * kn + r < L) ? row_idx[TC * kn + r] : -1;
-      const uint8_t* row = TC * k + r < L ? row_in(pool, x) : nullptr;
-      n += __popcll(__ballot(row != nullptr && c8 == 0));
-      const uint8_t* from = row ? row : p.pool;
+    for (int32_t k0 = (int32_t)blockIdx.y; k0 < tiles; k0 += PASS * gy) {
+      int32_t x[PASS];
 #pragma unroll
-      for (int cg = 0; cg < CG; ++cg) {
-        const int ck = 8 * cg + c8;
-        if (ck < CHUNKS) global_to_lds_16(from + 16 * ck, buf + w * 1024);
+      for (int i = 0; i < PASS; ++i) {
+        const int32_t j = TC * (k0 + i * gy) + r;  // list position of the lane's row
+        x[i] = (k0 + i * gy < tiles && j < L) ? row_idx[j] : -1;
       }
-      x = xn;
-      k = kn;
+#pragma unroll
+      for (int i = 0; i < PASS; ++i) {
+        if (k0 + i * gy >= tiles) break;  // wave-uniform
+        const uint8_t* row = TC * (k0 + i * gy) + r < L ? row_in(pool, x[i]) : nullptr;
+        n += __popcll(__ballot(row != nullptr && c8 == 0));
+        const uint8_t* from = row ? row : p.pool;
+#pragma unroll
+        for (int cg = 0; cg < CG; ++cg) {
+          const int ck = 8 * cg + c8;
+          if (ck < CHUNKS) global_to_lds_16(from + 16 * ck, buf + w * 1024);
+        }
+      }
     }
     if (lane == 0 && n) atomicAdd(p.rows_out + t, n);
   }
   __builtin_amdgcn_s_waitcnt(0);  // no gather lands after the workgroup ends
 }
 
+// rows_out accumulates over the workgroups that share a token, so it is
+// cleared first, by a kernel on the same stream (a memset may be served by
+// another engine, whose hand-off costs more than the probe itself)
+__global__ __launch_bounds__(256) void clear_rows_kernel(uint32_t* rows_out, int64_t T) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < T) rows_out[i] = 0;
+}
+
 hipError_t launch_gather_probe(const GatherProbeParams& p, int chunks, hipStream_t s) {
+  if (chunks != 41 && chunks != 72) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(clear_rows_kernel, dim3((unsigned)((p.T + 255) / 256)), dim3(256), 0, s, p.rows_out, p.T);
   const int cus = device_compute_units();
-  // about two workgroups' worth of tokens and tiles per compute unit
-  const int64_t gx = p.T < 2 * cus ? p.T : 2 * cus;
-  const int64_t gy_want = (2 * cus + gx - 1) / gx;
+  // one long-lived workgroup per compute unit: short workgroups cost more
+  // to start and drain than their gathers take (on the 64-token decode
+  // lists, four times as many workgroups take three to four times as long)
+  const int64_t gx = p.T < cus ? p.T : cus;
+  const int64_t gy_want = (cus + gx - 1) / gx;
   const int64_t max_tiles = (p.topk + probe::TC - 1) / probe::TC;
   dim3 grid((unsigned)gx, (unsigned)(gy_want < max_tiles ? gy_want : max_tiles)), block(probe::NT);
   switch (chunks) {
