@@ -64,8 +64,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample of the prefill tokens (0: all)")
     ap.add_argument("--no-extra", action="store_true", help="skip the few-head and INT8 workloads")
-    ap.add_argument("--only", choices=["int8"], default=None,
-                    help="time only this workload and print its line (for counter passes)")
+    ap.add_argument("--only", choices=["int8", "probe"], default=None,
+                    help="int8: time only the INT8 workload and print its line (for counter passes); "
+                         "probe: the gather probe over 1..32 copies of the decode batch's lists")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="also run one plain device-to-device copy of MIB MiB (reference for HBM counters)")
     return ap.parse_args()
@@ -347,6 +348,53 @@ def int8_line(torch, smla, W, dev, stream, bf16, iters=10):
     return result["int8"]
 
 
+def probe_scaling(torch, smla, W, dev, stream, bf16):
+    """The gather probe over the decode batch's HBM-resident pool with 1, 2,
+    4, ..., 32 copies of its lists (each copy with the block ids permuted
+    afresh, so every copy reads other rows), the same lists sorted per token,
+    and runs of consecutive slots: how the gather rate depends on the volume
+    one launch moves."""
+    dc = W.c2_decode()
+    dkv = bf16(dc.kv)
+    dpool = smla.KVPool.empty(dc.num_blocks, W.FMT_FP8, device=dev)
+    smla.quantize_kv(dkv, torch.from_numpy(dc.slots).to(dev), dpool)
+    del dkv
+    didx = torch.from_numpy(dc.idx_buf).to(dev)
+    rng = np.random.default_rng(7)
+
+    def remapped():
+        remap = torch.from_numpy(rng.permutation(dc.num_blocks).astype(np.int32)).to(dev)
+        moved = remap[(didx.clamp(min=0) // 64).long()] * 64 + didx.clamp(min=0) % 64
+        return torch.where(didx >= 0, moved, didx).to(torch.int32)
+
+    copies = [remapped() for _ in range(32)]
+    rb = W.ROW_BYTES[W.FMT_FP8]
+    out = {"workload": f"gather probe over the decode pool ({dc.num_blocks} blocks of 64 rows, "
+                       f"{dc.num_blocks * 64 * rb / 2**20:.0f} MiB), lists of {dc.topk} rows per token",
+           "random": [], "sorted": [], "consecutive": []}
+
+    def run(label, idx):
+        rows = int((idx >= 0).sum().item())
+        smla.probe_gather(dpool, idx)
+        torch.cuda.synchronize()
+        t = pct(queued_times_us(torch, lambda: smla.probe_gather(dpool, idx), 5, stream))
+        out[label].append({"tokens": int(idx.shape[0]), "rows": rows, "us_median_p10_p90": [round(v, 3) for v in t],
+                           "GBps": round(rows * rb / (t[0] * 1e-6) / 1e9, 1)})
+
+    for m in (1, 2, 4, 8, 16, 32):
+        run("random", torch.cat(copies[:m], 0).contiguous())
+    big = torch.iinfo(torch.int32).max
+    for m in (1, 8):
+        srt = torch.cat(copies[:m], 0)
+        srt = torch.where(srt >= 0, srt, big).sort(dim=1).values
+        run("sorted", torch.where(srt == big, -1, srt).to(torch.int32).contiguous())
+    nrows = dc.num_blocks * 64
+    for tok in (64, 512):
+        base = (torch.arange(tok, device=dev, dtype=torch.int64) * dc.topk) % (nrows - dc.topk)
+        run("consecutive", (base[:, None] + torch.arange(dc.topk, device=dev)[None, :]).to(torch.int32).contiguous())
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -372,6 +420,10 @@ def main():
     if args.only == "int8":
         print(json.dumps({"int8": int8_line(torch, smla, W, dev, torch.cuda.current_stream(), bf16,
                                             max(args.steps, 1))}), flush=True)
+        return
+    if args.only == "probe":
+        print(json.dumps({"probe_scaling": probe_scaling(torch, smla, W, dev, torch.cuda.current_stream(), bf16)}),
+              flush=True)
         return
 
     # ---------------- prefill workload ----------------
