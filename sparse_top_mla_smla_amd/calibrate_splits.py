@@ -36,27 +36,28 @@ from sparse_top_mla_smla_amd import workloads as W
 POOL_ROWS = 1 << 20  # 16384 blocks: 584 MiB to 1.2 GiB, beyond the last-level cache
 
 # kernel class -> (format, head counts measured, workgroups per CU per round,
-# heads per block).  FP8 and INT8 rows with more than 16 heads run the same
-# many-head kernel ("wide": 64 heads per workgroup); the classes differ in
-# the codes' conversion.  With 16 or fewer heads, and for BF16 rows at every
-# H, the kernel that splits PV over value columns runs (two workgroups per
-# CU); arbitrary-scale FP8 rows share the INT8 class.  The exponent-byte
-# kernel (DOTS3_SWA, DSv4 rows) runs 16 heads per workgroup (DSv4: at any H,
-# two workgroups per CU); DOTS3_SWA rows with more than 16 heads run its
-# 32-head kernel.
+# heads per block).  FP8, INT8 and DSv4 rows with more than 16 heads run the
+# same many-head kernel ("wide": 64 heads per workgroup); the classes differ
+# in the codes' conversion and the row layout.  With 16 or fewer heads, and
+# for BF16 rows at every H, the kernel that splits PV over value columns
+# runs (two workgroups per CU); arbitrary-scale FP8 rows share the INT8
+# class.  The exponent-byte kernel runs DSv4 rows with 16 or fewer heads
+# (16 heads per workgroup, two workgroups per CU) and DOTS3_SWA rows at any
+# H (16 heads per workgroup, its 32-head kernel above 16 heads).
 CLASSES = {
     "fp8_wide": (W.FMT_FP8, (64, 128), 1, 64),
     "int8_wide": (W.FMT_INT8, (64, 128), 1, 64),
+    "dsv4_wide": (W.FMT_FP8_DSV4, (64, 128), 1, 64),
     "fp8_cols": (W.FMT_FP8, (8, 16), 2, 16),
     "int8_cols": (W.FMT_INT8, (8, 16), 2, 16),
     "bf16_cols": (W.FMT_BF16, (8, 64), 2, 16),
     "dots3_mx": (W.FMT_FP8_DOTS3, (8, 16), 1, 16),
     "dots3_mx32": (W.FMT_FP8_DOTS3, (32, 64), 1, 32),
-    "dsv4_mx": (W.FMT_FP8_DSV4, (16, 64), 2, 16),
+    "dsv4_mx": (W.FMT_FP8_DSV4, (8, 16), 2, 16),
 }
 # classes whose decode workgroups run consecutive splits of a token (the
-# many-head kernel of FP8 and INT8 rows)
-GROUPED = ("fp8_wide", "int8_wide")
+# many-head kernel)
+GROUPED = ("fp8_wide", "int8_wide", "dsv4_wide")
 T_GRID = (1, 2, 4, 8, 16, 32, 64, 128, 256)
 T_PREFILL_ONLY = (1024,)  # several tokens per workgroup in the persistent prefill
 TOPK_GRID = (512, 2048)

@@ -6,18 +6,19 @@
 //    kernel (attention_bf16.hip; one workgroup of 4 waves per (token,
 //    16-head group, split), QK over candidates, PV over value columns, two
 //    workgroups per CU);
-//  * rows with exponent-byte scales (DOTS3_SWA, DSv4): their own kernel
-//    (attention_mx.hip) at any head count;
+//  * DOTS3_SWA rows at any head count, and DSv4 rows with 16 or fewer
+//    heads: the exponent-byte kernel (attention_mx.hip);
 //  * more than 16 heads over 656-byte quantized rows (FP8 with any scales,
-//    with or without rope, and INT8): the many-head kernel
-//    (attention_fp8.hip; one workgroup per token for 64 heads).
+//    with or without rope, and INT8) and over DSv4 rows: the many-head
+//    kernel (attention_fp8.hip; one workgroup per token for 64 heads).
 #include "device_common.h"
 #include "launch.h"
 
 namespace smla {
 
 hipError_t launch_attention(const AttnParams& p, int fmt, bool decode, hipStream_t s) {
-  if (fmt == FMT_FP8_DOTS3 || fmt == FMT_FP8_DSV4) return launch_attention_mx(p, fmt, decode, s);
+  if (fmt == FMT_FP8_DOTS3 || (fmt == FMT_FP8_DSV4 && p.H <= 16)) return launch_attention_mx(p, fmt, decode, s);
+  if (fmt == FMT_FP8_DSV4) return launch_attention_fp8(p, fmt, decode, s);
   if (fmt == FMT_BF16 || p.H <= 16) return launch_attention_bf16(p, fmt, decode, s);
   return launch_attention_fp8(p, fmt, decode, s);
 }

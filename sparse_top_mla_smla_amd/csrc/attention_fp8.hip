@@ -127,6 +127,15 @@ __device__ __forceinline__ i32x2 tr8_issue(uint32_t addr) {
   asm volatile("ds_read_b64_tr_b8 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
   return r;
 }
+// ds_read_b64_tr_b16 likewise: in each 16-lane group, lane 4r + b
+// addresses row r of a 4-row block, BF16 columns 4b..4b+3 of a 16-column
+// block; lane l then holds column l of the 4 rows
+template <int OFF>
+__device__ __forceinline__ i32x2 tr16_issue(uint32_t addr) {
+  i32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // ds_write_b64 through asm, for the same reason; the LDS barrier that
@@ -157,8 +166,20 @@ constexpr int CS = TC * 16;                  // bytes of one piece column (64 ro
 constexpr int TILE = CHUNKS * CS;            // 41,984 bytes per tile
 constexpr int CK_SCALE = D_NOPE / 16;        // piece 32 holds the four scales
 constexpr int CK_ROPE = CK_SCALE + 1;        // pieces 33..40 hold the rope
-constexpr int GROUNDS = (CHUNKS + 7) / 8;    // pieces per wave (6, the last for wave 0 only)
 constexpr int GPARTS = 3;                    // the pieces are issued in three parts per tile
+// DSv4 rows (584 bytes, 8-byte aligned in the pool): pieces 0..27 hold the
+// 448 e4m3 codes (piece p: values 16p..16p+15, scale tile p/4), pieces
+// 28..35 the 64 BF16 rope values (piece 28 + q: values 8q..8q+7), and piece
+// 36 is row bytes 568..583, whose bytes 8..14 are the seven scale bytes.
+namespace v4 {
+constexpr int CHUNKS = 37;
+constexpr int CK_ROPE = 28;
+constexpr int CK_TAIL = 36;
+constexpr int TAIL_FROM = 568;               // row byte where piece 36 starts
+constexpr int TILE = CHUNKS * CS;            // 37,888 bytes per tile
+}  // namespace v4
+template <int CODES>
+constexpr int chunks_of() { return CODES == FMT_FP8_DSV4 ? v4::CHUNKS : CHUNKS; }
 constexpr int RECV_FLOATS = 8 * 3 * 2 * 64 * 4;  // [8 owners][3 senders][2][64 lanes][4] f32
 constexpr int PS = 72;                       // P' row stride (bf16): [4 groups][64 heads][PS], aliases recv
 static_assert(4 * 64 * PS * 2 <= RECV_FLOATS * 4, "P' must fit in the partial-exchange buffer");
@@ -177,6 +198,17 @@ struct Buf {
 // the row that list positions without a candidate gather (zero-initialized
 // device memory, one copy per device)
 __device__ __attribute__((aligned(16))) uint8_t zero_row[RB];
+
+// an exponent byte as the FP32 number 2^(b-127) (0: 2^-127, 255: NaN)
+__device__ __forceinline__ float e8m0_value(uint32_t b) {
+  return __builtin_bit_cast(float, b == 0u ? 0x00400000u : (b == 255u ? 0x7FC00000u : b << 23));
+}
+// the scale v_cvt_scalef32_pk_bf16_fp8 applies for exponent byte b: the
+// instruction reads only the scale's exponent, so byte 0 converts as 2^-126
+// (the writer stores 1..254; a 0 byte only doubles values below 2^-118)
+__device__ __forceinline__ float e8m0_cvt_scale(uint32_t b) {
+  return __builtin_bit_cast(float, (b == 0u ? 1u : b) << 23);
+}
 }  // namespace f8
 
 // NOPE: rows without rope dimensions (q rows of 512 values, row padding never
@@ -184,7 +216,11 @@ __device__ __attribute__((aligned(16))) uint8_t zero_row[RB];
 // converting), FMT_FP8_ANY or FMT_INT8 (arbitrary scales: the codes convert
 // exactly with scale 1, each latent group's partial score is multiplied by
 // its candidates' scales before the rope part is added, and P' folds the
-// scales into PV as for FMT_FP8).
+// scales into PV as for FMT_FP8), or FMT_FP8_DSV4 (the 584-byte rows: 512
+// key and value dimensions, 448 of them e4m3 codes with a power-of-two
+// scale per 64, then 64 BF16 rope values; latent group 3 holds the last
+// 64 codes and the rope, and P' has eight versions, one per scale tile and
+// one for the rope columns).
 template <bool DECODE, bool DUAL, bool NOPE, int CODES>
 __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
   using namespace f8;
@@ -192,10 +228,16 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
   // names its raw buffer at compile time: the compiler then sees that reads
   // of one buffer (and of the other arrays) do not alias the direct-to-LDS
   // gather into the other buffer, and does not wait for that gather.
-  __shared__ __attribute__((aligned(16))) uint8_t raw0[TILE];
-  __shared__ __attribute__((aligned(16))) uint8_t raw1[TILE];
+  constexpr bool DS = CODES == FMT_FP8_DSV4;                          // DSv4 rows
+  constexpr bool ARB = CODES == FMT_FP8_ANY || CODES == FMT_INT8;     // arbitrary scales
+  constexpr int NCK = chunks_of<CODES>();                             // pieces per row
+  constexpr int RAW = NCK * CS;                                       // bytes per raw tile
+  __shared__ __attribute__((aligned(16))) uint8_t raw0[RAW];
+  __shared__ __attribute__((aligned(16))) uint8_t raw1[RAW];
   __shared__ __attribute__((aligned(16))) float recv[CODES == FMT_FP8 ? RECV_FLOATS : RECV_FLOATS_ARB];
   __shared__ __attribute__((aligned(16))) float maxb[4 * 64];   // [4 groups][64 heads]
+  // DSv4: the tile's scales, [scale tile][row] (2^(b-127))
+  __shared__ __attribute__((aligned(16))) float dsc[DS ? 7 * TC : 4];
   __shared__ __attribute__((aligned(16))) int32_t valid[2 * TC];  // [buffer][row]: row was loaded
   __shared__ __attribute__((aligned(16))) int32_t idx0[TC];       // index list of even tiles
   __shared__ __attribute__((aligned(16))) int32_t idx1[TC];       // index list of odd tiles
@@ -308,13 +350,14 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
 #pragma unroll
     for (int r = 2 * P; r < 2 * P + 2; ++r) {
       const int ck = w + 8 * r;
-      // (rows without rope dimensions: their padding is not gathered)
-      if ((r + 1 < GROUNDS || ck < CHUNKS) && (!NOPE || ck < CK_ROPE))
-        global_to_lds_16(from + 16 * ck, raw + ck * CS);
+      // (rows without rope dimensions: their padding is not gathered; the
+      // DSv4 row's last piece starts 8 bytes early, inside the row)
+      if ((8 * r + 7 < NCK || ck < NCK) && (!NOPE || ck < CK_ROPE))
+        global_to_lds_16(from + (DS && ck == v4::CK_TAIL ? v4::TAIL_FROM : 16 * ck), raw + ck * CS);
     }
     if (P == 0 && w == 0) valid[B * TC + lane] = src != nullptr;
   };
-  static_assert(2 * GPARTS == GROUNDS, "three parts of two rounds");
+  static_assert(2 * GPARTS * 8 >= NCK && 2 * (GPARTS - 1) * 8 < NCK, "three parts of two rounds");
 
   // Q as the B operand of S^T = K Q^T for head h0 + 32hh + l32.  A K lane
   // reads one 16-byte piece (8g + 2j + hi) that feeds MFMA steps 2j and
@@ -334,8 +377,10 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
         const uint4 v = *reinterpret_cast<const uint4*>(qrow + 128 * g + 32 * j + 16 * hi + 8 * b);
         qn[2 * j + b] = __builtin_bit_cast(bf16x8, hv ? v : make_uint4(0, 0, 0, 0));
       }
-    // (rows without rope dimensions: q rows end at 512 and the rope slice is 0)
-    if constexpr (NOPE) {
+    // (rows without rope dimensions: q rows end at 512 and the rope slice is
+    // 0; DSv4 q rows end at 512 too, their rope values are columns 448..511
+    // of latent group 3, loaded above)
+    if constexpr (NOPE || DS) {
       qr = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
     } else {
       const uint4 v = *reinterpret_cast<const uint4*>(qrow + D_NOPE + 16 * g + 8 * hi);
@@ -385,7 +430,7 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
   // pieces of 32 heads.
   auto store_partial_staged = [&](int32_t key, float factor) {
     constexpr int SROW = 68;  // floats per staged head row (64 + 4 pad)
-    static_assert(4 * 32 * SROW * 4 <= TILE, "four waves' staging fits one raw buffer");
+    static_assert(4 * 32 * SROW * 4 <= RAW, "four waves' staging fits one raw buffer");
     float* st = reinterpret_cast<float*>(w < 4 ? raw0 : raw1) + (w & 3) * 32 * SROW;
     const int64_t td = blockIdx.x;
     float* pbase = p.part_out + ((td * p.num_splits + key) * p.H + h0 + 32 * hh) * (int64_t)D_V + 128 * g;
@@ -499,32 +544,69 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[c2][i] = 0.0f;
       const int row = 32 * c2 + l32;
-      // power-of-two scales: applied while converting.  A scale that is not
-      // a positive power of two makes this row's rope operand NaN: the row's
-      // scores become NaN for every head (rows that are not loaded are
-      // masked out by selection later)
-      const float sc = CODES == FMT_FP8 ? *reinterpret_cast<const float*>(raw + CK_SCALE * CS + row * 16 + 4 * g) : 1.0f;
-      const bool bad = CODES == FMT_FP8 && !is_pow2_scale(sc);
-      const uint8_t* kp = raw + (8 * g + hi) * CS + row * 16;
+      if constexpr (DS) {
+        // DSv4: this wave's 128 key columns are codes of scale tiles 2g and
+        // 2g + 1 (group 3: the codes of tile 6, then the 64 BF16 rope
+        // values).  The row's scale bytes are bytes 8..14 of piece 36; a
+        // byte 255 (NaN) makes the row's scores NaN for every head, as a bad
+        // scale does for the 656-byte rows.
+        const uint2 tb = *reinterpret_cast<const uint2*>(raw + v4::CK_TAIL * CS + row * 16 + 8);
+        const int t0 = 2 * g, t1 = g < 3 ? 2 * g + 1 : 2 * g;
+        const uint32_t b0 = ((t0 < 4 ? tb.x : tb.y) >> (8 * (t0 & 3))) & 0xFFu;
+        const uint32_t b1 = ((t1 < 4 ? tb.x : tb.y) >> (8 * (t1 & 3))) & 0xFFu;
+        const float s0c = e8m0_cvt_scale(b0), s1c = e8m0_cvt_scale(b1);
+        const bool bad = b0 == 255u || b1 == 255u;
+        // the exact scales, for P' (read after the next barrier): lanes
+        // hi = 0 write tile t0, lanes hi = 1 tile t1 (group 3: tile 6 only)
+        if (g < 3 || hi == 0) dsc[(hi ? t1 : t0) * TC + row] = e8m0_value(hi ? b1 : b0);
+        const uint8_t* kp = raw + (8 * g + hi) * CS + row * 16;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint4 c16 = *reinterpret_cast<const uint4*>(kp + 2 * j * CS);
-        acc[c2] = mfma_32x32x16(codes8<CODES>(c16.x, c16.y, sc), qn[2 * j], acc[c2]);
-        acc[c2] = mfma_32x32x16(codes8<CODES>(c16.z, c16.w, sc), qn[2 * j + 1], acc[c2]);
+        for (int j = 0; j < 4; ++j) {
+          if (g < 3 || j < 2) {
+            // e4m3 codes: key columns 128g + 32j + 16hi + 8b + i, scale tile 2g + j/2
+            const uint4 c16 = *reinterpret_cast<const uint4*>(kp + 2 * j * CS);
+            const float sc = j < 2 ? s0c : s1c;
+            bf16x8 k0 = cvt8(c16.x, c16.y, sc);
+            if (j == 0 && bad) k0 = __builtin_bit_cast(bf16x8, make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u));
+            acc[c2] = mfma_32x32x16(k0, qn[2 * j], acc[c2]);
+            acc[c2] = mfma_32x32x16(cvt8(c16.z, c16.w, sc), qn[2 * j + 1], acc[c2]);
+          } else {
+            // group 3, BF16 rope values 32(j - 2) + 16hi + 8b + i (key
+            // columns 384 + 32j + 16hi + 8b + i) in piece 28 + 4(j - 2) + 2hi + b
+            const uint8_t* rp = raw + (v4::CK_ROPE + 4 * (j - 2) + 2 * hi) * CS + row * 16;
+            acc[c2] = mfma_32x32x16(__builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(rp)), qn[2 * j], acc[c2]);
+            acc[c2] = mfma_32x32x16(__builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(rp + CS)), qn[2 * j + 1],
+                                    acc[c2]);
+          }
+        }
+      } else {
+        // power-of-two scales: applied while converting.  A scale that is
+        // not a positive power of two makes this row's rope operand NaN: the
+        // row's scores become NaN for every head (rows that are not loaded
+        // are masked out by selection later)
+        const float sc = CODES == FMT_FP8 ? *reinterpret_cast<const float*>(raw + CK_SCALE * CS + row * 16 + 4 * g) : 1.0f;
+        const bool bad = CODES == FMT_FP8 && !is_pow2_scale(sc);
+        const uint8_t* kp = raw + (8 * g + hi) * CS + row * 16;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint4 c16 = *reinterpret_cast<const uint4*>(kp + 2 * j * CS);
+          acc[c2] = mfma_32x32x16(codes8<CODES>(c16.x, c16.y, sc), qn[2 * j], acc[c2]);
+          acc[c2] = mfma_32x32x16(codes8<CODES>(c16.z, c16.w, sc), qn[2 * j + 1], acc[c2]);
+        }
+        if constexpr (ARB) {
+          // arbitrary scales: accumulator element 4a + b is candidate
+          // 32c2 + 8a + 4hi + b, whose scale of group g is read here
+          const uint8_t* sp = raw + CK_SCALE * CS + (32 * c2 + 4 * hi) * 16 + 4 * g;
+#pragma unroll
+          for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) acc[c2][4 * a + b] *= *reinterpret_cast<const float*>(sp + (8 * a + b) * 16);
+        }
+        uint4 r16 = make_uint4(0, 0, 0, 0);  // rows without rope dimensions: 0
+        if constexpr (!NOPE) r16 = *reinterpret_cast<const uint4*>(raw + (CK_ROPE + 2 * g + hi) * CS + row * 16);
+        if (bad) r16 = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
+        acc[c2] = mfma_32x32x16(__builtin_bit_cast(bf16x8, r16), qr, acc[c2]);
       }
-      if constexpr (CODES != FMT_FP8) {
-        // arbitrary scales: accumulator element 4a + b is candidate
-        // 32c2 + 8a + 4hi + b, whose scale of group g is read here
-        const uint8_t* sp = raw + CK_SCALE * CS + (32 * c2 + 4 * hi) * 16 + 4 * g;
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-          for (int b = 0; b < 4; ++b) acc[c2][4 * a + b] *= *reinterpret_cast<const float*>(sp + (8 * a + b) * 16);
-      }
-      uint4 r16 = make_uint4(0, 0, 0, 0);  // rows without rope dimensions: 0
-      if constexpr (!NOPE) r16 = *reinterpret_cast<const uint4*>(raw + (CK_ROPE + 2 * g + hi) * CS + row * 16);
-      if (bad) r16 = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
-      acc[c2] = mfma_32x32x16(__builtin_bit_cast(bf16x8, r16), qr, acc[c2]);
     }
     // prefill: Q of the next token, not read again before that token's QK
     if (!DECODE && more && nxt.t != cur.t) load_q(nxt.t);
@@ -588,51 +670,78 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
         psum += s0[r] + s1[r];
       }
       l_part = l_part * alpha + psum;
-      // P'_gg = P x (row scale of column group gg), BF16, for the PV of
-      // every group; the four scales of a row are one 16-byte piece
-      const uint8_t* scp = raw + CK_SCALE * CS + (16 * g + 4 * hi) * 16;
-      f32x4 sc0[4], sc1[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        sc0[r] = *reinterpret_cast<const f32x4*>(scp + r * 16);
-        sc1[r] = *reinterpret_cast<const f32x4*>(scp + (8 + r) * 16);
-      }
-      u32x2 w0[4], w1[4];
-#pragma unroll
-      for (int gg = 0; gg < 4; ++gg) {
-        w0[gg] = u32x2{pack_bf16(s0[0] * sc0[0][gg], s0[1] * sc0[1][gg]), pack_bf16(s0[2] * sc0[2][gg], s0[3] * sc0[3][gg])};
-        w1[gg] = u32x2{pack_bf16(s1[0] * sc1[0][gg], s1[1] * sc1[1][gg]), pack_bf16(s1[2] * sc1[2][gg], s1[3] * sc1[3][gg])};
-      }
       const uint32_t pw = lds_addr(pq + hl * PS + 16 * g + 4 * hi);
-      if constexpr (CODES != FMT_FP8) {
-        // an arbitrary scale makes P x scale inexact in BF16: the rest goes
-        // to slots 4..7 and PV adds both parts (a power-of-two scale only
-        // shifts the exponent)
-        u32x2 r0[4], r1[4];
+      if constexpr (DS) {
+        // DSv4: P'_t = P x (the row's scale of tile t) for the seven scale
+        // tiles, in slots 0..6 (exact: the scales are powers of two), and P
+        // itself in slot 7 for the rope columns
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          u32x2 v0, v1;
+          if (t < 7) {
+            // scales of tile t of candidates 16g + 4hi + r and 16g + 8 + 4hi + r
+            const f32x4 c0 = *reinterpret_cast<const f32x4*>(dsc + t * TC + 16 * g + 4 * hi);
+            const f32x4 c1 = *reinterpret_cast<const f32x4*>(dsc + t * TC + 16 * g + 8 + 4 * hi);
+            v0 = u32x2{pack_bf16(s0[0] * c0[0], s0[1] * c0[1]), pack_bf16(s0[2] * c0[2], s0[3] * c0[3])};
+            v1 = u32x2{pack_bf16(s1[0] * c1[0], s1[1] * c1[1]), pack_bf16(s1[2] * c1[2], s1[3] * c1[3])};
+          } else {
+            v0 = u32x2{pack_bf16(s0[0], s0[1]), pack_bf16(s0[2], s0[3])};
+            v1 = u32x2{pack_bf16(s1[0], s1[1]), pack_bf16(s1[2], s1[3])};
+          }
+#define SMLA_PST(T)                   \
+  if (t == (T)) {                     \
+    b64_store<(T) * GS>(pw, v0);      \
+    b64_store<(T) * GS + 16>(pw, v1); \
+  }
+          SMLA_PST(0) SMLA_PST(1) SMLA_PST(2) SMLA_PST(3) SMLA_PST(4) SMLA_PST(5) SMLA_PST(6) SMLA_PST(7)
+#undef SMLA_PST
+        }
+      } else {
+        // P'_gg = P x (row scale of column group gg), BF16, for the PV of
+        // every group; the four scales of a row are one 16-byte piece
+        const uint8_t* scp = raw + CK_SCALE * CS + (16 * g + 4 * hi) * 16;
+        f32x4 sc0[4], sc1[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          sc0[r] = *reinterpret_cast<const f32x4*>(scp + r * 16);
+          sc1[r] = *reinterpret_cast<const f32x4*>(scp + (8 + r) * 16);
+        }
+        u32x2 w0[4], w1[4];
 #pragma unroll
         for (int gg = 0; gg < 4; ++gg) {
-          r0[gg] = u32x2{bf16_rest(s0[0] * sc0[0][gg], s0[1] * sc0[1][gg], w0[gg][0]),
-                         bf16_rest(s0[2] * sc0[2][gg], s0[3] * sc0[3][gg], w0[gg][1])};
-          r1[gg] = u32x2{bf16_rest(s1[0] * sc1[0][gg], s1[1] * sc1[1][gg], w1[gg][0]),
-                         bf16_rest(s1[2] * sc1[2][gg], s1[3] * sc1[3][gg], w1[gg][1])};
+          w0[gg] = u32x2{pack_bf16(s0[0] * sc0[0][gg], s0[1] * sc0[1][gg]), pack_bf16(s0[2] * sc0[2][gg], s0[3] * sc0[3][gg])};
+          w1[gg] = u32x2{pack_bf16(s1[0] * sc1[0][gg], s1[1] * sc1[1][gg]), pack_bf16(s1[2] * sc1[2][gg], s1[3] * sc1[3][gg])};
         }
-        b64_store<4 * GS>(pw, r0[0]);
-        b64_store<4 * GS + 16>(pw, r1[0]);
-        b64_store<5 * GS>(pw, r0[1]);
-        b64_store<5 * GS + 16>(pw, r1[1]);
-        b64_store<6 * GS>(pw, r0[2]);
-        b64_store<6 * GS + 16>(pw, r1[2]);
-        b64_store<7 * GS>(pw, r0[3]);
-        b64_store<7 * GS + 16>(pw, r1[3]);
+            if constexpr (ARB) {
+          // an arbitrary scale makes P x scale inexact in BF16: the rest goes
+          // to slots 4..7 and PV adds both parts (a power-of-two scale only
+          // shifts the exponent)
+          u32x2 r0[4], r1[4];
+#pragma unroll
+          for (int gg = 0; gg < 4; ++gg) {
+            r0[gg] = u32x2{bf16_rest(s0[0] * sc0[0][gg], s0[1] * sc0[1][gg], w0[gg][0]),
+                           bf16_rest(s0[2] * sc0[2][gg], s0[3] * sc0[3][gg], w0[gg][1])};
+            r1[gg] = u32x2{bf16_rest(s1[0] * sc1[0][gg], s1[1] * sc1[1][gg], w1[gg][0]),
+                           bf16_rest(s1[2] * sc1[2][gg], s1[3] * sc1[3][gg], w1[gg][1])};
+          }
+          b64_store<4 * GS>(pw, r0[0]);
+          b64_store<4 * GS + 16>(pw, r1[0]);
+          b64_store<5 * GS>(pw, r0[1]);
+          b64_store<5 * GS + 16>(pw, r1[1]);
+          b64_store<6 * GS>(pw, r0[2]);
+          b64_store<6 * GS + 16>(pw, r1[2]);
+          b64_store<7 * GS>(pw, r0[3]);
+          b64_store<7 * GS + 16>(pw, r1[3]);
+        }
+        b64_store<0>(pw, w0[0]);
+        b64_store<16>(pw, w1[0]);
+        b64_store<GS>(pw, w0[1]);
+        b64_store<GS + 16>(pw, w1[1]);
+        b64_store<2 * GS>(pw, w0[2]);
+        b64_store<2 * GS + 16>(pw, w1[2]);
+        b64_store<3 * GS>(pw, w0[3]);
+        b64_store<3 * GS + 16>(pw, w1[3]);
       }
-      b64_store<0>(pw, w0[0]);
-      b64_store<16>(pw, w1[0]);
-      b64_store<GS>(pw, w0[1]);
-      b64_store<GS + 16>(pw, w1[1]);
-      b64_store<2 * GS>(pw, w0[2]);
-      b64_store<2 * GS + 16>(pw, w1[2]);
-      b64_store<3 * GS>(pw, w0[3]);
-      b64_store<3 * GS + 16>(pw, w1[3]);
     }
     if (__any(alpha != 1.0f)) {
 #pragma unroll
@@ -647,45 +756,134 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
     const int g16 = (lane >> 4) & 1;
     const int jr = (lane & 15) >> 1;
     const int jb = lane & 1;
-    const uint32_t va = lds_addr(raw + (8 * g + g16) * CS + (8 * hi + jr) * 16 + 8 * jb);
-    i32x2 v8[4][4];  // [ks][dt]: candidates 16ks.., columns 128g + 32dt..
+    if constexpr (DS) {
+      // DSv4: columns 128g + 32dt.. take P' of scale tile 2g + dt/2 (slot
+      // A for dt 0, 1, slot B for dt 2, 3); group 3's columns 448..511 are
+      // the BF16 rope values (slot 7, P itself), read with
+      // ds_read_b64_tr_b16 from pieces 28 + 4(dt - 2) + 2g16 + (b >> 1)
+      const uint32_t va = lds_addr(raw + (8 * g + g16) * CS + (8 * hi + jr) * 16 + 8 * jb);
+      // columns 128g + 0..63 (codes of scale tile 2g, slot A) first; the
+      // reads of the other 64 columns are issued under their MFMAs.  The
+      // transposed reads are inline asm and each batch is waited for right
+      // after it is issued, in the same block (the compiler takes an asm
+      // result as ready at once); the P' rows are plain loads, whose waits
+      // the compiler places itself.
+      const u32x4* pA = reinterpret_cast<const u32x4*>(pq + (2 * g * 64 + 32 * hh + l32) * PS + 8 * hi);
+      const u32x4* pB = reinterpret_cast<const u32x4*>(pq + ((g < 3 ? 2 * g + 1 : 7) * 64 + 32 * hh + l32) * PS + 8 * hi);
+      i32x2 v8[4][2];  // [ks][dt]: candidates 16ks.., columns 128g + 32dt..
 #define SMLA_TR8(ks, dt) v8[ks][dt] = tr8_issue<2 * (dt) * CS + 256 * (ks)>(va)
-    SMLA_TR8(0, 0); SMLA_TR8(0, 1); SMLA_TR8(0, 2); SMLA_TR8(0, 3);
-    SMLA_TR8(1, 0); SMLA_TR8(1, 1); SMLA_TR8(1, 2); SMLA_TR8(1, 3);
-    SMLA_TR8(2, 0); SMLA_TR8(2, 1); SMLA_TR8(2, 2); SMLA_TR8(2, 3);
-    SMLA_TR8(3, 0); SMLA_TR8(3, 1); SMLA_TR8(3, 2); SMLA_TR8(3, 3);
+      SMLA_TR8(0, 0); SMLA_TR8(0, 1); SMLA_TR8(1, 0); SMLA_TR8(1, 1);
+      SMLA_TR8(2, 0); SMLA_TR8(2, 1); SMLA_TR8(3, 0); SMLA_TR8(3, 1);
 #undef SMLA_TR8
-    // P'_g for heads 32hh + l32, candidates 16ks + 8hi + i: the B operands
-    const uint32_t pa = lds_addr(pq + (g * 64 + 32 * hh + l32) * PS + 8 * hi);
-    u32x4 pb[4];
-    pb[0] = b128_issue<0>(pa);
-    pb[1] = b128_issue<32>(pa);
-    pb[2] = b128_issue<64>(pa);
-    pb[3] = b128_issue<96>(pa);
-    u32x4 pr[4];  // the rest of P'_g (rows with arbitrary scales only)
-    if constexpr (CODES != FMT_FP8) {
-      pr[0] = b128_issue<4 * GS>(pa);
-      pr[1] = b128_issue<4 * GS + 32>(pa);
-      pr[2] = b128_issue<4 * GS + 64>(pa);
-      pr[3] = b128_issue<4 * GS + 96>(pa);
-    }
-    // one wait for all the reads; the empty statements after it (volatile
-    // statements keep their order) carry the dependency to the rest
-    asm volatile("s_waitcnt lgkmcnt(0)"
-                 : "+v"(v8[0][0]), "+v"(v8[0][1]), "+v"(v8[0][2]), "+v"(v8[0][3]), "+v"(v8[1][0]), "+v"(v8[1][1]),
-                   "+v"(v8[1][2]), "+v"(v8[1][3]), "+v"(pb[0]), "+v"(pb[1]), "+v"(pb[2]), "+v"(pb[3]));
-    if constexpr (CODES != FMT_FP8) asm volatile("" : "+v"(pr[0]), "+v"(pr[1]), "+v"(pr[2]), "+v"(pr[3]));
-    asm volatile(""
-                 : "+v"(v8[2][0]), "+v"(v8[2][1]), "+v"(v8[2][2]), "+v"(v8[2][3]), "+v"(v8[3][0]), "+v"(v8[3][1]),
-                   "+v"(v8[3][2]), "+v"(v8[3][3]));
+      asm volatile("s_waitcnt lgkmcnt(0)"
+                   : "+v"(v8[0][0]), "+v"(v8[0][1]), "+v"(v8[1][0]), "+v"(v8[1][1]), "+v"(v8[2][0]), "+v"(v8[2][1]),
+                     "+v"(v8[3][0]), "+v"(v8[3][1]));
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+      for (int ks = 0; ks < 4; ++ks) {
+        const u32x4 pb = pA[2 * ks];  // candidates 16ks + 8hi + i
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const bf16x8 v = codes8<CODES>((uint32_t)v8[ks][dt][0], (uint32_t)v8[ks][dt][1], 1.0f);
-        O[dt] = mfma_32x32x16(v, __builtin_bit_cast(bf16x8, pb[ks]), O[dt]);
-        if constexpr (CODES != FMT_FP8) O[dt] = mfma_32x32x16(v, __builtin_bit_cast(bf16x8, pr[ks]), O[dt]);
+        for (int dt = 0; dt < 2; ++dt) {
+          const bf16x8 v = cvt8((uint32_t)v8[ks][dt][0], (uint32_t)v8[ks][dt][1], 1.0f);
+          O[dt] = mfma_32x32x16(v, __builtin_bit_cast(bf16x8, pb), O[dt]);
+        }
       }
+      u32x4 pr[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) pr[ks] = pB[2 * ks];
+      if (g < 3) {
+        // codes of scale tile 2g + 1, two candidate blocks at a time
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+          i32x2 w8[2][2];
+#define SMLA_TR8(KH, k, d) w8[k][d] = tr8_issue<2 * (2 + (d)) * CS + 256 * (2 * (KH) + (k))>(va)
+          if (kh == 0) {
+            SMLA_TR8(0, 0, 0); SMLA_TR8(0, 0, 1); SMLA_TR8(0, 1, 0); SMLA_TR8(0, 1, 1);
+          } else {
+            SMLA_TR8(1, 0, 0); SMLA_TR8(1, 0, 1); SMLA_TR8(1, 1, 0); SMLA_TR8(1, 1, 1);
+          }
+#undef SMLA_TR8
+          asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(w8[0][0]), "+v"(w8[0][1]), "+v"(w8[1][0]), "+v"(w8[1][1]));
+#pragma unroll
+          for (int k = 0; k < 2; ++k)
+#pragma unroll
+            for (int d = 0; d < 2; ++d) {
+              const bf16x8 v = cvt8((uint32_t)w8[k][d][0], (uint32_t)w8[k][d][1], 1.0f);
+              O[2 + d] = mfma_32x32x16(v, __builtin_bit_cast(bf16x8, pr[2 * kh + k]), O[2 + d]);
+            }
+        }
+      } else {
+        // group 3: the BF16 rope columns 448 + 32(dt - 2) + 16g16 + lc, two
+        // candidate blocks at a time
+        const int lc = lane & 15;
+        const uint32_t vb = lds_addr(raw + (v4::CK_ROPE + 2 * g16 + ((lc & 3) >> 1)) * CS + (8 * hi + (lc >> 2)) * 16 +
+                                     8 * (lc & 1));
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+          i32x2 vr[2][2][2];  // [ks - 2kh][dt - 2][rows 0..3 / 4..7]
+#define SMLA_TR16(KH, k, d)                                                    \
+  vr[k][d][0] = tr16_issue<4 * (d) * CS + 256 * (2 * (KH) + (k))>(vb);        \
+  vr[k][d][1] = tr16_issue<4 * (d) * CS + 256 * (2 * (KH) + (k)) + 64>(vb)
+          if (kh == 0) {
+            SMLA_TR16(0, 0, 0); SMLA_TR16(0, 0, 1); SMLA_TR16(0, 1, 0); SMLA_TR16(0, 1, 1);
+          } else {
+            SMLA_TR16(1, 0, 0); SMLA_TR16(1, 0, 1); SMLA_TR16(1, 1, 0); SMLA_TR16(1, 1, 1);
+          }
+#undef SMLA_TR16
+          asm volatile("s_waitcnt lgkmcnt(0)"
+                       : "+v"(vr[0][0][0]), "+v"(vr[0][0][1]), "+v"(vr[0][1][0]), "+v"(vr[0][1][1]), "+v"(vr[1][0][0]),
+                         "+v"(vr[1][0][1]), "+v"(vr[1][1][0]), "+v"(vr[1][1][1]));
+#pragma unroll
+          for (int k = 0; k < 2; ++k)
+#pragma unroll
+            for (int d = 0; d < 2; ++d) {
+              const bf16x8 v = __builtin_bit_cast(
+                  bf16x8, make_uint4((uint32_t)vr[k][d][0][0], (uint32_t)vr[k][d][0][1], (uint32_t)vr[k][d][1][0],
+                                     (uint32_t)vr[k][d][1][1]));
+              O[2 + d] = mfma_32x32x16(v, __builtin_bit_cast(bf16x8, pr[2 * kh + k]), O[2 + d]);
+            }
+        }
+      }
+    } else {
+      const uint32_t va = lds_addr(raw + (8 * g + g16) * CS + (8 * hi + jr) * 16 + 8 * jb);
+      i32x2 v8[4][4];  // [ks][dt]: candidates 16ks.., columns 128g + 32dt..
+#define SMLA_TR8(ks, dt) v8[ks][dt] = tr8_issue<2 * (dt) * CS + 256 * (ks)>(va)
+      SMLA_TR8(0, 0); SMLA_TR8(0, 1); SMLA_TR8(0, 2); SMLA_TR8(0, 3);
+      SMLA_TR8(1, 0); SMLA_TR8(1, 1); SMLA_TR8(1, 2); SMLA_TR8(1, 3);
+      SMLA_TR8(2, 0); SMLA_TR8(2, 1); SMLA_TR8(2, 2); SMLA_TR8(2, 3);
+      SMLA_TR8(3, 0); SMLA_TR8(3, 1); SMLA_TR8(3, 2); SMLA_TR8(3, 3);
+#undef SMLA_TR8
+      // P'_g for heads 32hh + l32, candidates 16ks + 8hi + i: the B operands
+      const uint32_t pa = lds_addr(pq + (g * 64 + 32 * hh + l32) * PS + 8 * hi);
+      u32x4 pb[4];
+      pb[0] = b128_issue<0>(pa);
+      pb[1] = b128_issue<32>(pa);
+      pb[2] = b128_issue<64>(pa);
+      pb[3] = b128_issue<96>(pa);
+      u32x4 pr[4];  // the rest of P'_g (rows with arbitrary scales only)
+      if constexpr (ARB) {
+        pr[0] = b128_issue<4 * GS>(pa);
+        pr[1] = b128_issue<4 * GS + 32>(pa);
+        pr[2] = b128_issue<4 * GS + 64>(pa);
+        pr[3] = b128_issue<4 * GS + 96>(pa);
+      }
+      // one wait for all the reads; the empty statements after it (volatile
+      // statements keep their order) carry the dependency to the rest
+      asm volatile("s_waitcnt lgkmcnt(0)"
+                   : "+v"(v8[0][0]), "+v"(v8[0][1]), "+v"(v8[0][2]), "+v"(v8[0][3]), "+v"(v8[1][0]), "+v"(v8[1][1]),
+                     "+v"(v8[1][2]), "+v"(v8[1][3]), "+v"(pb[0]), "+v"(pb[1]), "+v"(pb[2]), "+v"(pb[3]));
+      if constexpr (ARB) asm volatile("" : "+v"(pr[0]), "+v"(pr[1]), "+v"(pr[2]), "+v"(pr[3]));
+      asm volatile(""
+                   : "+v"(v8[2][0]), "+v"(v8[2][1]), "+v"(v8[2][2]), "+v"(v8[2][3]), "+v"(v8[3][0]), "+v"(v8[3][1]),
+                     "+v"(v8[3][2]), "+v"(v8[3][3]));
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const bf16x8 v = codes8<CODES>((uint32_t)v8[ks][dt][0], (uint32_t)v8[ks][dt][1], 1.0f);
+          O[dt] = mfma_32x32x16(v, __builtin_bit_cast(bf16x8, pb[ks]), O[dt]);
+          if constexpr (ARB) O[dt] = mfma_32x32x16(v, __builtin_bit_cast(bf16x8, pr[ks]), O[dt]);
+        }
+    }
   };
   // ---- end of a split (decode) or of a token (prefill): per-head sum over
   // the four groups, normalization; the result is stored now, or by the
@@ -814,6 +1012,7 @@ hipError_t launch_attention_fp8(const AttnParams& p, int fmt, bool decode, hipSt
   using yes = std::true_type;
   using no = std::false_type;
   if (fmt == FMT_FP8_NOPE) go(yes{}, std::integral_constant<int, FMT_FP8>{});
+  else if (fmt == FMT_FP8_DSV4) go(no{}, std::integral_constant<int, FMT_FP8_DSV4>{});
   else if (fmt == FMT_FP8_ANY) go(no{}, std::integral_constant<int, FMT_FP8_ANY>{});
   else if (fmt == FMT_INT8) go(no{}, std::integral_constant<int, FMT_INT8>{});
   else go(no{}, std::integral_constant<int, FMT_FP8>{});

@@ -18,7 +18,7 @@
 // exponent-byte kernel's DSv4 instantiation), and a, b, f, ap0, ap, bp per
 // kernel class.  The constants were fitted by
 // sparse_top_mla_smla_amd/calibrate_splits.py on one MI355X (256 CUs) over
-// 288 decode shapes and their prefill counterparts; there the pick is on
+// 324 decode shapes and their prefill counterparts; there the pick is on
 // average 0.5% and at most 12% slower than the best measured split count.
 #include <hip/hip_runtime.h>
 
@@ -47,7 +47,8 @@ constexpr KernelClass kFp8Cols{3.377, 3.673, 3.377, 0.0, 12.60, 3.767, 16, false
 constexpr KernelClass kInt8Cols{3.249, 4.358, 3.249, 0.0, 11.74, 4.483, 16, false, 2};
 constexpr KernelClass kDots3Mx{3.851, 6.568, 3.851, 0.0, 14.10, 6.380, 16, false, 1};
 constexpr KernelClass kDots3Mx32{2.827, 7.815, 2.827, 1.264, 12.92, 7.461, 32, false, 1};
-constexpr KernelClass kDsv4Mx{1.678, 4.843, 1.678, 0.0, 8.484, 4.814, 16, false, 2};
+constexpr KernelClass kDsv4Mx{3.134, 4.672, 3.134, 0, 13.51, 4.609, 16, false, 2};
+constexpr KernelClass kDsv4Wide{16.36, 3.857, 0, 9.336, 9.113, 3.969, 64, true, 1};
 constexpr double kWriteUsPerMB = 0.186;  // decode's partial stores
 constexpr double kComb0 = 10.57, kComb1 = 0.1856, kComb2 = 0.0;
 constexpr double kCrossover = 0.95;  // split form only when at most this fraction of prefill
@@ -62,9 +63,10 @@ const KernelClass* kernel_class(int32_t format, int32_t H) {
     // conversion is cheaper: the INT8 constants bound it)
     case SMLA_KV_FP8_E4M3_ANY_SCALE: return H > 16 ? &kInt8Wide : &kInt8Cols;
     case SMLA_KV_BF16: return &kBf16Cols;
-    // rows with exponent-byte scales: their own kernel at any H
+    // DOTS3_SWA rows: the exponent-byte kernels at any H; DSv4 rows: the
+    // exponent-byte kernel up to 16 heads, the many-head kernel above
     case SMLA_KV_FP8_E4M3_DOTS3: return H > 16 ? &kDots3Mx32 : &kDots3Mx;
-    case SMLA_KV_FP8_E4M3_DSV4: return &kDsv4Mx;
+    case SMLA_KV_FP8_E4M3_DSV4: return H > 16 ? &kDsv4Wide : &kDsv4Mx;
     default: return nullptr;
   }
 }
