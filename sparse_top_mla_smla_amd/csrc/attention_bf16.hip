@@ -57,8 +57,10 @@ constexpr int P_HEAD = 144;                   // bytes of one head's P row (64 B
 // Row geometry.  BF16 rows: 576 BF16 values.  Quantized rows (656 bytes):
 // 512 codes, four FP32 scales (one per 128 columns), 64 BF16 rope values
 // (padding in rope-less rows, never gathered).  P is kept in four versions,
-// P times the scale of each wave's value columns; with arbitrary scales each
-// version is a BF16 pair (the rounded value and the rest), eight slots.
+// P times the scale of each wave's value columns: FP16 under a per-tile bias
+// for power-of-two scales (f16_bias), a BF16 pair (the rounded value and the
+// rest, eight slots) for arbitrary scales.  BF16 rows keep P as a BF16 pair
+// too (two slots), so P enters PV with 16 significant bits.
 template <int FMT>
 struct Cols {
   static constexpr bool QUANT = FMT != FMT_BF16;
@@ -68,14 +70,15 @@ struct Cols {
   static constexpr int LDS_ROW = ROW + 16;    // bank spread
   static constexpr int PIECES = ROPE ? ROW / 16 : (D_NOPE + 16) / 16;  // gathered: 72, 41 or 33
   static constexpr int NCH = (PIECES + 3) / 4;  // pieces per thread (4 threads per row)
-  static constexpr int VERSIONS = !QUANT ? 1 : POW2 ? 4 : 8;
+  static constexpr int VERSIONS = !QUANT ? 2 : POW2 ? 4 : 8;
   // LDS: tile, P [versions][16 heads][64] BF16, wave maxima / sums [4][16],
   // index stage [3][64] (row addresses)
   static constexpr int TILE_BYTES = TC * LDS_ROW;
   static constexpr int P_OFF = TILE_BYTES;
   static constexpr int RED_OFF = P_OFF + VERSIONS * 16 * P_HEAD;
   static constexpr int IDX_OFF = RED_OFF + 4 * 16 * 4;
-  static constexpr int LDS_BYTES = IDX_OFF + 3 * TC * 8;
+  static constexpr int EMAX_OFF = IDX_OFF + 3 * TC * 8;  // [4 waves] largest scale exponent of their rows
+  static constexpr int LDS_BYTES = EMAX_OFF + 4 * 4;
   static_assert(LDS_BYTES <= 80 * 1024, "two workgroups per CU");
 };
 
@@ -127,6 +130,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(AttnParams p) {
   uint8_t* pbuf = smem + P_OFF;
   float* red = reinterpret_cast<float*>(smem + RED_OFF);
   uint64_t* idx_lds = reinterpret_cast<uint64_t*>(smem + IDX_OFF);  // 0: no candidate
+  uint32_t* emax = reinterpret_cast<uint32_t*>(smem + G::EMAX_OFF);
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -203,6 +207,17 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(AttnParams p) {
 #pragma unroll
     for (int r = 0; r < NCH; ++r)
       if (PIECES % 4 == 0 || sub + 4 * r < PIECES) dst[4 * r] = stage[r];
+    if constexpr (G::POW2) {
+      // the largest scale exponent of this wave's rows (piece 32, the four
+      // scales, is stage[8] of the row's thread sub == 0), for the FP16 bias
+      static_assert(D_NOPE / 16 == 8 * 4 && NCH > 8, "the scale piece");
+      const uint4 sc = stage[8];
+      const uint32_t e = sub == 0 ? max(max((sc.x >> 23) & 0xFFu, (sc.y >> 23) & 0xFFu),
+                                        max((sc.z >> 23) & 0xFFu, (sc.w >> 23) & 0xFFu))
+                                  : 0u;
+      const uint32_t m = wave_max_u32(e);
+      if (lane == 0) emax[wave] = m;
+    }
   };
 
   // running max (log2 units) of head lc, shared by the four waves; this
@@ -226,6 +241,11 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(AttnParams p) {
   }
 
   for (int k = 0; k < n_tiles; ++k) {
+    // power-of-two rows: PV of this tile in FP16 under the bias of its
+    // largest scale (the waves' maxima are read before the next tile's rows
+    // replace them)
+    F16Bias bias{1.0f, 1.0f};
+    if constexpr (G::POW2) bias = f16_bias(max(max(emax[0], emax[1]), max(emax[2], emax[3])));
     if (k + 1 < n_tiles) issue_rows(k + 1);
     uint64_t pend = 0;
     if (k + 2 < n_tiles && tid < TC) pend = load_idx(k + 2);
@@ -311,12 +331,28 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(AttnParams p) {
       l_part += pr[i];
     }
     if constexpr (FMT == FMT_BF16) {
-      *reinterpret_cast<uint2*>(pbuf + lc * P_HEAD + 2 * (16 * wave + 4 * lg)) =
-          make_uint2(pack_bf16(pr[0], pr[1]), pack_bf16(pr[2], pr[3]));
+      // P as a BF16 pair: the rounded value, then the rest
+      const uint2 hi = make_uint2(pack_bf16(pr[0], pr[1]), pack_bf16(pr[2], pr[3]));
+      *reinterpret_cast<uint2*>(pbuf + lc * P_HEAD + 2 * (16 * wave + 4 * lg)) = hi;
+      *reinterpret_cast<uint2*>(pbuf + 16 * P_HEAD + lc * P_HEAD + 2 * (16 * wave + 4 * lg)) =
+          make_uint2(bf16_pair_rest(pr[0], pr[1], hi.x), bf16_pair_rest(pr[2], pr[3], hi.y));
+    } else if constexpr (G::POW2) {
+      // version v: P x 2^-b x the scale of value columns [128v, +128) in
+      // FP16, for the wave that owns those columns
+      f32x4 scl[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        scl[i] = *reinterpret_cast<const f32x4*>(tile + (16 * wave + 4 * lg + i) * LDS_ROW + D_NOPE);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pr[i] *= bias.p;
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        *reinterpret_cast<uint2*>(pbuf + v * 16 * P_HEAD + lc * P_HEAD + 2 * (16 * wave + 4 * lg)) =
+            make_uint2(pack_f16(pr[0] * scl[0][v], pr[1] * scl[1][v]), pack_f16(pr[2] * scl[2][v], pr[3] * scl[3][v]));
     } else {
-      // version v: P times the scale of value columns [128v, +128) (exact for
-      // a power of two), for the wave that owns those columns; with
-      // arbitrary scales the rest of the rounding goes to version 4 + v
+      // version v: P times the scale of value columns [128v, +128), for the
+      // wave that owns those columns, as a BF16 pair: the rest of the
+      // rounding goes to version 4 + v
       f32x4 scl[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -326,9 +362,8 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(AttnParams p) {
         const float x0 = pr[0] * scl[0][v], x1 = pr[1] * scl[1][v], x2 = pr[2] * scl[2][v], x3 = pr[3] * scl[3][v];
         const uint2 hi = make_uint2(pack_bf16(x0, x1), pack_bf16(x2, x3));
         *reinterpret_cast<uint2*>(pbuf + v * 16 * P_HEAD + lc * P_HEAD + 2 * (16 * wave + 4 * lg)) = hi;
-        if constexpr (!G::POW2)
-          *reinterpret_cast<uint2*>(pbuf + (4 + v) * 16 * P_HEAD + lc * P_HEAD + 2 * (16 * wave + 4 * lg)) =
-              make_uint2(bf16_pair_rest(x0, x1, hi.x), bf16_pair_rest(x2, x3, hi.y));
+        *reinterpret_cast<uint2*>(pbuf + (4 + v) * 16 * P_HEAD + lc * P_HEAD + 2 * (16 * wave + 4 * lg)) =
+            make_uint2(bf16_pair_rest(x0, x1, hi.x), bf16_pair_rest(x2, x3, hi.y));
       }
     }
     __syncthreads();
@@ -337,9 +372,12 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(AttnParams p) {
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
       const uint8_t* pv = pbuf + (G::QUANT ? wave : 0) * 16 * P_HEAD;
-      const bf16x8 pb = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(pv + lc * P_HEAD + 2 * (32 * kc + 8 * lg)));
+      const uint4 pw = *reinterpret_cast<const uint4*>(pv + lc * P_HEAD + 2 * (32 * kc + 8 * lg));
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
       if constexpr (FMT == FMT_BF16) {
         // tr16: lane lc = 4r + b reads rows (32kc + 8lg + 4half + r), columns 4b..4b+3 of the block
+        const bf16x8 pl = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(pbuf + 16 * P_HEAD + lc * P_HEAD +
+                                                                                        2 * (32 * kc + 8 * lg)));
         const uint8_t* rb = tile + (32 * kc + 8 * lg + (lc >> 2)) * LDS_ROW + 2 * WCOLS * wave + 8 * (lc & 3);
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
@@ -347,21 +385,33 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(AttnParams p) {
           const bf16x8 a = __builtin_bit_cast(bf16x8, make_uint4(__builtin_bit_cast(uint2, r0).x, __builtin_bit_cast(uint2, r0).y,
                                                                  __builtin_bit_cast(uint2, r1).x, __builtin_bit_cast(uint2, r1).y));
           O[dt] = mfma_16x16x32(a, pb, O[dt]);
+          O[dt] = mfma_16x16x32(a, pl, O[dt]);
+        }
+      } else if constexpr (G::POW2) {
+        // tr8 as below; the codes convert to FP16 times 2^b (the row scale
+        // and 2^-b are in P')
+        const uint8_t* rb = tile + (32 * kc + 8 * lg + (lc >> 1)) * LDS_ROW + WCOLS * wave + 8 * (lc & 1);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const i32x2 c = lds_read_tr8(rb + 16 * dt);
+          const uint2 lo = fp8x4_to_f16x4((uint32_t)c[0], bias.v), hi = fp8x4_to_f16x4((uint32_t)c[1], bias.v);
+          O[dt] = mfma_16x16x32_f16(__builtin_bit_cast(f16x8, make_uint4(lo.x, lo.y, hi.x, hi.y)),
+                                    __builtin_bit_cast(f16x8, pw), O[dt]);
         }
       } else {
         // tr8: lane lc = 2r + b reads row 32kc + 8lg + r (a candidate), bytes
         // 8b..8b+7 of a 16-column piece; lane lc receives column lc of the
         // 8 rows.  The codes convert with scale 1 (the scale is in P).
         const uint8_t* rb = tile + (32 * kc + 8 * lg + (lc >> 1)) * LDS_ROW + WCOLS * wave + 8 * (lc & 1);
-        bf16x8 pl;  // the rest of P' (arbitrary scales)
-        if constexpr (!G::POW2)
-          pl = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(pv + 4 * 16 * P_HEAD + lc * P_HEAD + 2 * (32 * kc + 8 * lg)));
+        // the rest of P' (arbitrary scales)
+        const bf16x8 pl =
+            __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(pv + 4 * 16 * P_HEAD + lc * P_HEAD + 2 * (32 * kc + 8 * lg)));
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
           const i32x2 c = lds_read_tr8(rb + 16 * dt);
           const bf16x8 a = codes8<FMT>((uint32_t)c[0], (uint32_t)c[1], 1.0f);
           O[dt] = mfma_16x16x32(a, pb, O[dt]);
-          if constexpr (!G::POW2) O[dt] = mfma_16x16x32(a, pl, O[dt]);
+          O[dt] = mfma_16x16x32(a, pl, O[dt]);
         }
       }
     }

@@ -74,6 +74,16 @@ __device__ __forceinline__ bf16x8 cvt8(uint32_t c0, uint32_t c1, float scale) {
                                                __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d)));
 }
 
+__device__ __forceinline__ f32x16 mfma_32x32x16_f16(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// eight e4m3 codes times a power-of-two scale as FP16 (see fp8x4_to_f16x4)
+__device__ __forceinline__ f16x8 cvt8_f16(uint32_t c0, uint32_t c1, float scale) {
+  const uint2 lo = fp8x4_to_f16x4(c0, scale), hi = fp8x4_to_f16x4(c1, scale);
+  return __builtin_bit_cast(f16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+
 // eight codes of the given row format as BF16: e4m3 times a power-of-two
 // scale (exact), or int8 (exact, |code| <= 127; the scale is applied later)
 template <int CODES>
@@ -230,6 +240,7 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
   // gather into the other buffer, and does not wait for that gather.
   constexpr bool DS = CODES == FMT_FP8_DSV4;                          // DSv4 rows
   constexpr bool ARB = CODES == FMT_FP8_ANY || CODES == FMT_INT8;     // arbitrary scales
+  constexpr bool F16 = !ARB;                                          // PV in FP16 (see the tile step)
   constexpr int NCK = chunks_of<CODES>();                             // pieces per row
   constexpr int RAW = NCK * CS;                                       // bytes per raw tile
   __shared__ __attribute__((aligned(16))) uint8_t raw0[RAW];
@@ -529,6 +540,23 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
       issue_part(Buf<1 - B>{}, Buf<0>{}, src_next);
     }
     if (w == 0 && nn.t >= 0) issue_idx(Buf<B>{}, nn);
+    // PV of power-of-two rows runs in FP16 under the tile's bias (f16_bias):
+    // the largest exponent of the 64 rows' scales (DSv4: of their seven
+    // exponent bytes; DSv4's BF16 rope values enter PV as FP16 unbiased)
+    float vscale = 1.0f, pscale = 1.0f;
+    if constexpr (F16) {
+      uint32_t e;
+      if constexpr (DS) {
+        const uint2 tb = *reinterpret_cast<const uint2*>(raw + v4::CK_TAIL * CS + lane * 16 + 8);
+        e = max_byte<7>(tb.x, tb.y);
+      } else {
+        const uint4 sc4 = *reinterpret_cast<const uint4*>(raw + CK_SCALE * CS + lane * 16);
+        e = max(max((sc4.x >> 23) & 0xFFu, (sc4.y >> 23) & 0xFFu), max((sc4.z >> 23) & 0xFFu, (sc4.w >> 23) & 0xFFu));
+      }
+      const F16Bias bias = f16_bias(wave_max_u32(e));
+      vscale = bias.v;
+      pscale = bias.p;
+    }
     if (pend >= 0) {
       store_result(pend, pend_factor, pend_lse, false);
       pend = -1;
@@ -675,6 +703,7 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
         // DSv4: P'_t = P x (the row's scale of tile t) for the seven scale
         // tiles, in slots 0..6 (exact: the scales are powers of two), and P
         // itself in slot 7 for the rope columns
+        const f32x4 s0b = s0 * pscale, s1b = s1 * pscale;  // P x 2^-b
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
           u32x2 v0, v1;
@@ -682,11 +711,11 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
             // scales of tile t of candidates 16g + 4hi + r and 16g + 8 + 4hi + r
             const f32x4 c0 = *reinterpret_cast<const f32x4*>(dsc + t * TC + 16 * g + 4 * hi);
             const f32x4 c1 = *reinterpret_cast<const f32x4*>(dsc + t * TC + 16 * g + 8 + 4 * hi);
-            v0 = u32x2{pack_bf16(s0[0] * c0[0], s0[1] * c0[1]), pack_bf16(s0[2] * c0[2], s0[3] * c0[3])};
-            v1 = u32x2{pack_bf16(s1[0] * c1[0], s1[1] * c1[1]), pack_bf16(s1[2] * c1[2], s1[3] * c1[3])};
+            v0 = u32x2{pack_f16(s0b[0] * c0[0], s0b[1] * c0[1]), pack_f16(s0b[2] * c0[2], s0b[3] * c0[3])};
+            v1 = u32x2{pack_f16(s1b[0] * c1[0], s1b[1] * c1[1]), pack_f16(s1b[2] * c1[2], s1b[3] * c1[3])};
           } else {
-            v0 = u32x2{pack_bf16(s0[0], s0[1]), pack_bf16(s0[2], s0[3])};
-            v1 = u32x2{pack_bf16(s1[0], s1[1]), pack_bf16(s1[2], s1[3])};
+            v0 = u32x2{pack_f16(s0[0], s0[1]), pack_f16(s0[2], s0[3])};
+            v1 = u32x2{pack_f16(s1[0], s1[1]), pack_f16(s1[2], s1[3])};
           }
 #define SMLA_PST(T)                   \
   if (t == (T)) {                     \
@@ -707,10 +736,20 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
           sc1[r] = *reinterpret_cast<const f32x4*>(scp + (8 + r) * 16);
         }
         u32x2 w0[4], w1[4];
+        if constexpr (F16) {
+          s0 *= pscale;
+          s1 *= pscale;
 #pragma unroll
-        for (int gg = 0; gg < 4; ++gg) {
-          w0[gg] = u32x2{pack_bf16(s0[0] * sc0[0][gg], s0[1] * sc0[1][gg]), pack_bf16(s0[2] * sc0[2][gg], s0[3] * sc0[3][gg])};
-          w1[gg] = u32x2{pack_bf16(s1[0] * sc1[0][gg], s1[1] * sc1[1][gg]), pack_bf16(s1[2] * sc1[2][gg], s1[3] * sc1[3][gg])};
+          for (int gg = 0; gg < 4; ++gg) {
+            w0[gg] = u32x2{pack_f16(s0[0] * sc0[0][gg], s0[1] * sc0[1][gg]), pack_f16(s0[2] * sc0[2][gg], s0[3] * sc0[3][gg])};
+            w1[gg] = u32x2{pack_f16(s1[0] * sc1[0][gg], s1[1] * sc1[1][gg]), pack_f16(s1[2] * sc1[2][gg], s1[3] * sc1[3][gg])};
+          }
+        } else {
+#pragma unroll
+          for (int gg = 0; gg < 4; ++gg) {
+            w0[gg] = u32x2{pack_bf16(s0[0] * sc0[0][gg], s0[1] * sc0[1][gg]), pack_bf16(s0[2] * sc0[2][gg], s0[3] * sc0[3][gg])};
+            w1[gg] = u32x2{pack_bf16(s1[0] * sc1[0][gg], s1[1] * sc1[1][gg]), pack_bf16(s1[2] * sc1[2][gg], s1[3] * sc1[3][gg])};
+          }
         }
             if constexpr (ARB) {
           // an arbitrary scale makes P x scale inexact in BF16: the rest goes
@@ -783,8 +822,8 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
         const u32x4 pb = pA[2 * ks];  // candidates 16ks + 8hi + i
 #pragma unroll
         for (int dt = 0; dt < 2; ++dt) {
-          const bf16x8 v = cvt8((uint32_t)v8[ks][dt][0], (uint32_t)v8[ks][dt][1], 1.0f);
-          O[dt] = mfma_32x32x16(v, __builtin_bit_cast(bf16x8, pb), O[dt]);
+          const f16x8 v = cvt8_f16((uint32_t)v8[ks][dt][0], (uint32_t)v8[ks][dt][1], vscale);
+          O[dt] = mfma_32x32x16_f16(v, __builtin_bit_cast(f16x8, pb), O[dt]);
         }
       }
       u32x4 pr[4];
@@ -807,8 +846,8 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
           for (int k = 0; k < 2; ++k)
 #pragma unroll
             for (int d = 0; d < 2; ++d) {
-              const bf16x8 v = cvt8((uint32_t)w8[k][d][0], (uint32_t)w8[k][d][1], 1.0f);
-              O[2 + d] = mfma_32x32x16(v, __builtin_bit_cast(bf16x8, pr[2 * kh + k]), O[2 + d]);
+              const f16x8 v = cvt8_f16((uint32_t)w8[k][d][0], (uint32_t)w8[k][d][1], vscale);
+              O[2 + d] = mfma_32x32x16_f16(v, __builtin_bit_cast(f16x8, pr[2 * kh + k]), O[2 + d]);
             }
         }
       } else {
@@ -836,10 +875,10 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
           for (int k = 0; k < 2; ++k)
 #pragma unroll
             for (int d = 0; d < 2; ++d) {
-              const bf16x8 v = __builtin_bit_cast(
-                  bf16x8, make_uint4((uint32_t)vr[k][d][0][0], (uint32_t)vr[k][d][0][1], (uint32_t)vr[k][d][1][0],
-                                     (uint32_t)vr[k][d][1][1]));
-              O[2 + d] = mfma_32x32x16(v, __builtin_bit_cast(bf16x8, pr[2 * kh + k]), O[2 + d]);
+              const f16x8 v = __builtin_bit_cast(
+                  f16x8, make_uint4(bf16x2_to_f16x2((uint32_t)vr[k][d][0][0]), bf16x2_to_f16x2((uint32_t)vr[k][d][0][1]),
+                                    bf16x2_to_f16x2((uint32_t)vr[k][d][1][0]), bf16x2_to_f16x2((uint32_t)vr[k][d][1][1])));
+              O[2 + d] = mfma_32x32x16_f16(v, __builtin_bit_cast(f16x8, pr[2 * kh + k]), O[2 + d]);
             }
         }
       }
@@ -879,9 +918,14 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
       for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
-          const bf16x8 v = codes8<CODES>((uint32_t)v8[ks][dt][0], (uint32_t)v8[ks][dt][1], 1.0f);
-          O[dt] = mfma_32x32x16(v, __builtin_bit_cast(bf16x8, pb[ks]), O[dt]);
-          if constexpr (ARB) O[dt] = mfma_32x32x16(v, __builtin_bit_cast(bf16x8, pr[ks]), O[dt]);
+          if constexpr (F16) {
+            const f16x8 v = cvt8_f16((uint32_t)v8[ks][dt][0], (uint32_t)v8[ks][dt][1], vscale);
+            O[dt] = mfma_32x32x16_f16(v, __builtin_bit_cast(f16x8, pb[ks]), O[dt]);
+          } else {
+            const bf16x8 v = codes8<CODES>((uint32_t)v8[ks][dt][0], (uint32_t)v8[ks][dt][1], 1.0f);
+            O[dt] = mfma_32x32x16(v, __builtin_bit_cast(bf16x8, pb[ks]), O[dt]);
+            if constexpr (ARB) O[dt] = mfma_32x32x16(v, __builtin_bit_cast(bf16x8, pr[ks]), O[dt]);
+          }
         }
     }
   };

@@ -100,7 +100,8 @@ struct Geo {
   static constexpr int SC_OFF = P_OFF + SLOTS * P_SLOT;
   static constexpr int RED_OFF = SC_OFF + TC * 8 * 4;
   static constexpr int IDX_OFF = RED_OFF + 4 * 16 * 4;
-  static constexpr int LDS_BYTES = IDX_OFF + 3 * TC * 8;
+  static constexpr int EMAX_OFF = IDX_OFF + 3 * TC * 8;  // [4 waves] largest exponent byte of their rows
+  static constexpr int LDS_BYTES = EMAX_OFF + 4 * 4;
   static_assert(R::ROW - 16 * PIECES == 8 && R::SCALE_OFF == 16 * PIECES, "the tail holds the scale bytes");
   static_assert(PIECES % 4 == 0 && R::NOPE % R::TILE == 0 && R::TILE % 32 == 0 && R::NG <= 8, "row geometry");
   // a wave's value columns are two scale tiles, 2w and 2w+1 (for DSv4's last
@@ -124,6 +125,7 @@ __global__ __launch_bounds__(NT, R::OCC) void attn_mx_kernel(AttnParams p) {
   float* sct = reinterpret_cast<float*>(smem + G::SC_OFF);
   float* red = reinterpret_cast<float*>(smem + G::RED_OFF);
   uint64_t* idx_lds = reinterpret_cast<uint64_t*>(smem + G::IDX_OFF);  // 0: no candidate
+  uint32_t* emax = reinterpret_cast<uint32_t*>(smem + G::EMAX_OFF);
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -208,6 +210,9 @@ __global__ __launch_bounds__(NT, R::OCC) void attn_mx_kernel(AttnParams p) {
       reinterpret_cast<f32x4*>(sct + grow * 8)[0] = lo;
       reinterpret_cast<f32x4*>(sct + grow * 8)[1] = hi;
     }
+    // the largest exponent byte of this wave's rows, for the tile's FP16 bias
+    const uint32_t e = wave_max_u32(sub == 0 ? max_byte<R::NG>(tail.x, tail.y) : 0u);
+    if (lane == 0) emax[wave] = e;
   };
 
   // running max (log2 units) of head lc, shared by the four waves; this
@@ -231,6 +236,9 @@ __global__ __launch_bounds__(NT, R::OCC) void attn_mx_kernel(AttnParams p) {
   }
 
   for (int k = 0; k < n_tiles; ++k) {
+    // PV of this tile in FP16 under the bias of its largest scale (the
+    // waves' maxima are read here, before the next tile's rows replace them)
+    const F16Bias bias = f16_bias(max(max(emax[0], emax[1]), max(emax[2], emax[3])));
     if (k + 1 < n_tiles) issue_rows(k + 1);
     uint64_t pend = 0;
     if (k + 2 < n_tiles && tid < TC) pend = load_idx(k + 2);
@@ -298,15 +306,25 @@ __global__ __launch_bounds__(NT, R::OCC) void attn_mx_kernel(AttnParams p) {
       pr[i] = (s[i] == -INFINITY) ? 0.0f : exp2f(s[i] - m_run);
       l_part += pr[i];
     }
-    // P'_g[h][c] = P[c][h] * scale(c, g), candidates 16*wave + 4lg + (0..3);
-    // slot NG (BF16 value columns) holds P itself
+    // P'_g[h][c] = P[c][h] * scale(c, g) * 2^-b in FP16, candidates
+    // 16*wave + 4lg + (0..3); slot NG (the BF16 value columns, unbiased)
+    // holds P itself
+    float prb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) prb[i] = pr[i] * bias.p;
 #pragma unroll
     for (int g = 0; g < G::SLOTS; ++g) {
-      float sg[4];
+      uint32_t u0, u1;
+      if (g < R::NG) {
+        float sg[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sg[i] = g < R::NG ? scales(i, g >> 2)[g & 3] : 1.0f;
-      const uint32_t u0 = pack_bf16(pr[0] * sg[0], pr[1] * sg[1]);
-      const uint32_t u1 = pack_bf16(pr[2] * sg[2], pr[3] * sg[3]);
+        for (int i = 0; i < 4; ++i) sg[i] = scales(i, g >> 2)[g & 3];
+        u0 = pack_f16(prb[0] * sg[0], prb[1] * sg[1]);
+        u1 = pack_f16(prb[2] * sg[2], prb[3] * sg[3]);
+      } else {
+        u0 = pack_f16(pr[0], pr[1]);
+        u1 = pack_f16(pr[2], pr[3]);
+      }
       *reinterpret_cast<uint2*>(pbuf + g * P_SLOT + lc * P_HEAD + 2 * (16 * wave + 4 * lg)) = make_uint2(u0, u1);
     }
     __syncthreads();
@@ -314,28 +332,29 @@ __global__ __launch_bounds__(NT, R::OCC) void attn_mx_kernel(AttnParams p) {
     // ---- O^T += V^T P'^T over value columns [WCOLS*wave, +WCOLS) ----
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
-      bf16x8 pb[2];  // P' of slots 2w and 2w+1 for candidates 32kc + 8lg + (0..7)
+      f16x8 pb[2];  // P' of slots 2w and 2w+1 for candidates 32kc + 8lg + (0..7)
 #pragma unroll
       for (int gg = 0; gg < 2; ++gg)
         pb[gg] = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const uint4*>(pbuf + (2 * wave + gg) * P_SLOT + lc * P_HEAD + 2 * (32 * kc + 8 * lg)));
+            f16x8, *reinterpret_cast<const uint4*>(pbuf + (2 * wave + gg) * P_SLOT + lc * P_HEAD + 2 * (32 * kc + 8 * lg)));
 #pragma unroll
       for (int dt = 0; dt < G::NDT; ++dt) {
         const int c0 = G::WCOLS * wave + 16 * dt;  // first column of the block (wave-uniform)
-        bf16x8 a;
+        f16x8 a;
         if (!G::ROPE_V || c0 < R::NOPE) {
           // tr8: lane lc = 2r + b reads candidate row (32kc + 8lg + r), byte columns c0 + 8b..
           const i32x2 raw = lds_read_tr8(tile + (32 * kc + 8 * lg + (lc >> 1)) * G::LDS_ROW + c0 + 8 * (lc & 1));
-          const uint2 lo = fp8x4_to_bf16x4((uint32_t)raw[0]), hi = fp8x4_to_bf16x4((uint32_t)raw[1]);
-          a = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+          const uint2 lo = fp8x4_to_f16x4((uint32_t)raw[0], bias.v), hi = fp8x4_to_f16x4((uint32_t)raw[1], bias.v);
+          a = __builtin_bit_cast(f16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
         } else {
           // tr16 (BF16 rope columns): lane lc = 4r + b reads rows (32kc + 8lg + 4half + r), columns 4b..
           const uint8_t* rb = tile + (32 * kc + 8 * lg + (lc >> 2)) * G::LDS_ROW + R::ROPE_OFF + 2 * (c0 - R::NOPE) + 8 * (lc & 3);
-          const i16x4 r0 = lds_read_tr16(rb), r1 = lds_read_tr16(rb + 4 * G::LDS_ROW);
-          a = __builtin_bit_cast(bf16x8, make_uint4(__builtin_bit_cast(uint2, r0).x, __builtin_bit_cast(uint2, r0).y,
-                                                    __builtin_bit_cast(uint2, r1).x, __builtin_bit_cast(uint2, r1).y));
+          const uint2 r0 = __builtin_bit_cast(uint2, lds_read_tr16(rb));
+          const uint2 r1 = __builtin_bit_cast(uint2, lds_read_tr16(rb + 4 * G::LDS_ROW));
+          a = __builtin_bit_cast(f16x8, make_uint4(bf16x2_to_f16x2(r0.x), bf16x2_to_f16x2(r0.y), bf16x2_to_f16x2(r1.x),
+                                                   bf16x2_to_f16x2(r1.y)));
         }
-        O[dt] = mfma_16x16x32(a, pb[dt / (G::NDT / 2)], O[dt]);
+        O[dt] = mfma_16x16x32_f16(a, pb[dt / (G::NDT / 2)], O[dt]);
       }
     }
 
@@ -419,13 +438,15 @@ __global__ __launch_bounds__(NT32, 1) void attn_mx32_kernel(AttnParams p) {
   constexpr int SC_OFF2 = P_OFF2 + 2 * G::SLOTS * P_SLOT;
   constexpr int RED_OFF2 = SC_OFF2 + TC * 8 * 4;
   constexpr int IDX_OFF2 = RED_OFF2 + 2 * 4 * 16 * 4;
-  constexpr int LDS_BYTES2 = IDX_OFF2 + 3 * TC * 8;
+  constexpr int EMAX_OFF2 = IDX_OFF2 + 3 * TC * 8;  // [8 waves] largest exponent byte of their rows
+  constexpr int LDS_BYTES2 = EMAX_OFF2 + 8 * 4;
   static_assert(LDS_BYTES2 <= 160 * 1024, "LDS");
   __shared__ __attribute__((aligned(16))) uint8_t smem[LDS_BYTES2];
   uint8_t* tile = smem;
   f32x4* xch = reinterpret_cast<f32x4*>(smem + XCH_OFF);
   float* sct = reinterpret_cast<float*>(smem + SC_OFF2);
   uint64_t* idx_lds = reinterpret_cast<uint64_t*>(smem + IDX_OFF2);
+  uint32_t* emax = reinterpret_cast<uint32_t*>(smem + EMAX_OFF2);
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -517,6 +538,9 @@ __global__ __launch_bounds__(NT32, 1) void attn_mx32_kernel(AttnParams p) {
       reinterpret_cast<f32x4*>(sct + grow * 8)[0] = lo;
       reinterpret_cast<f32x4*>(sct + grow * 8)[1] = hi;
     }
+    // the largest exponent byte of this wave's rows, for the tile's FP16 bias
+    const uint32_t e = wave_max_u32(sub == 0 ? max_byte<R::NG>(tail.x, tail.y) : 0u);
+    if (lane == 0) emax[wave] = e;
   };
 
   float m_run = -INFINITY;
@@ -537,6 +561,9 @@ __global__ __launch_bounds__(NT32, 1) void attn_mx32_kernel(AttnParams p) {
   }
 
   for (int k = 0; k < n_tiles; ++k) {
+    // PV of this tile in FP16 under the bias of its largest scale
+    const F16Bias bias = f16_bias(max(max(max(emax[0], emax[1]), max(emax[2], emax[3])),
+                                      max(max(emax[4], emax[5]), max(emax[6], emax[7]))));
     if (k + 1 < n_tiles) issue_rows(k + 1);
     uint64_t pend = 0;
     if (k + 2 < n_tiles && tid < TC) pend = load_idx(k + 2);
@@ -608,14 +635,16 @@ __global__ __launch_bounds__(NT32, 1) void attn_mx32_kernel(AttnParams p) {
       pr[i] = (s[i] == -INFINITY) ? 0.0f : exp2f(s[i] - m_run);
       l_part += pr[i];
     }
-    // P'_g[h][c] = P[c][h] * scale(c, g), candidates 16wl + 4lg + (0..3)
+    // P'_g[h][c] = P[c][h] * scale(c, g) * 2^-b in FP16, candidates 16wl + 4lg + (0..3)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pr[i] *= bias.p;
 #pragma unroll
     for (int g = 0; g < R::NG; ++g) {
       float sg[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) sg[i] = sct[(16 * wl + 4 * lg + i) * 8 + g];
-      const uint32_t u0 = pack_bf16(pr[0] * sg[0], pr[1] * sg[1]);
-      const uint32_t u1 = pack_bf16(pr[2] * sg[2], pr[3] * sg[3]);
+      const uint32_t u0 = pack_f16(pr[0] * sg[0], pr[1] * sg[1]);
+      const uint32_t u1 = pack_f16(pr[2] * sg[2], pr[3] * sg[3]);
       *reinterpret_cast<uint2*>(pbuf + g * P_SLOT + lc * P_HEAD + 2 * (16 * wl + 4 * lg)) = make_uint2(u0, u1);
     }
     __syncthreads();
@@ -623,18 +652,18 @@ __global__ __launch_bounds__(NT32, 1) void attn_mx32_kernel(AttnParams p) {
     // ---- O^T += V^T P'^T over value columns [WCOLS*wl, +WCOLS) ----
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
-      bf16x8 pb[2];
+      f16x8 pb[2];
 #pragma unroll
       for (int gg = 0; gg < 2; ++gg)
         pb[gg] = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const uint4*>(pbuf + (2 * wl + gg) * P_SLOT + lc * P_HEAD + 2 * (32 * kc + 8 * lg)));
+            f16x8, *reinterpret_cast<const uint4*>(pbuf + (2 * wl + gg) * P_SLOT + lc * P_HEAD + 2 * (32 * kc + 8 * lg)));
 #pragma unroll
       for (int dt = 0; dt < G::NDT; ++dt) {
         const int c0 = G::WCOLS * wl + 16 * dt;
         const i32x2 raw = lds_read_tr8(tile + (32 * kc + 8 * lg + (lc >> 1)) * G::LDS_ROW + c0 + 8 * (lc & 1));
-        const uint2 lo = fp8x4_to_bf16x4((uint32_t)raw[0]), hi = fp8x4_to_bf16x4((uint32_t)raw[1]);
-        O[dt] = mfma_16x16x32(__builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y)), pb[dt / (G::NDT / 2)],
-                              O[dt]);
+        const uint2 lo = fp8x4_to_f16x4((uint32_t)raw[0], bias.v), hi = fp8x4_to_f16x4((uint32_t)raw[1], bias.v);
+        O[dt] = mfma_16x16x32_f16(__builtin_bit_cast(f16x8, make_uint4(lo.x, lo.y, hi.x, hi.y)), pb[dt / (G::NDT / 2)],
+                                  O[dt]);
       }
     }
 

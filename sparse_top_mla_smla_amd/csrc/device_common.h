@@ -70,9 +70,14 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ f32x4 mfma_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_16x16x32_f16(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ f32x4 mfma_16x16x16(i16x4 a, i16x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
@@ -84,6 +89,66 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   v[0] = (__bf16)lo;
   v[1] = (__bf16)hi;
   return __builtin_bit_cast(uint32_t, v);
+}
+
+// two floats -> packed FP16 pair (round to nearest even; subnormals kept)
+__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
+  f16x2 v;
+  v[0] = (_Float16)lo;
+  v[1] = (_Float16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// two BF16 values (x's halves) as an FP16 pair: exact for magnitudes in
+// [2^-14, 65504], rounded to FP16's subnormal grid below
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t x) {
+  return pack_f16(__builtin_bit_cast(float, x << 16), __builtin_bit_cast(float, x & 0xFFFF0000u));
+}
+
+// four e4m3 codes (one dword) times a power-of-two scale as four FP16
+// values: exact, subnormal results included, while 448 x scale stays below
+// 65504 and the smallest code (2^-9) times the scale is at least 2^-24
+__device__ __forceinline__ uint2 fp8x4_to_f16x4(uint32_t v, float scale) {
+  return make_uint2(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v, scale, false)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v, scale, true)));
+}
+
+// PV over e4m3 codes with power-of-two scales runs in FP16: P' = P x scale
+// rounded once to FP16 has 11 significant bits against BF16's 8.  FP16's
+// range is held by a power-of-two bias per tile: with 2^(e-127) the tile's
+// largest scale (e its biased exponent, e.g. an exponent byte), V^T =
+// codes x 2^b and P' = P x scale x 2^-b, b = e - 134 within [-15, 7].  Then
+// P' <= 2^8 x 2^7 (P <= 2^8 under a lazy running max that moves when
+// exceeded by 2^8), and the codes (2^-9 .. 448) times 2^b are exact FP16
+// values; the bias cancels in each product.
+struct F16Bias {
+  float v;  // 2^b, for the codes
+  float p;  // 2^-b, for P'
+};
+__device__ __forceinline__ F16Bias f16_bias(uint32_t e) {
+  const int b = min(max((int)e - 134, -15), 7);
+  return F16Bias{__builtin_bit_cast(float, (uint32_t)(127 + b) << 23), __builtin_bit_cast(float, (uint32_t)(127 - b) << 23)};
+}
+
+// the largest value of v over the 64 lanes, in every lane (DPP within each
+// 16-lane row, then the four row maxima); every lane of the wave must call it
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // lanes i ^ 1
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // lanes i ^ 2
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));  // 7 - i within 8
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));  // 15 - i within 16
+  const uint32_t a = max((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16));
+  const uint32_t b = max((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48));
+  return max(a, b);
+}
+
+// the largest of the low n bytes of the 8-byte word (x, y)
+template <int N>
+__device__ __forceinline__ uint32_t max_byte(uint32_t x, uint32_t y) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < N; ++i) m = max(m, ((i < 4 ? x : y) >> (8 * (i & 3))) & 0xFFu);
+  return m;
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {

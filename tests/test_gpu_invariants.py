@@ -169,6 +169,37 @@ def test_fp8_non_power_of_two_scale_gives_nan(H):
     assert torch.isnan(of[sel]).all()
     assert torch.equal(o2[~sel], o1[~sel]) and torch.equal(l2[~sel], l1[~sel])
 
+@pytest.mark.parametrize("H", [16, 64])
+@pytest.mark.parametrize("byte,nan", [(255, True), (0, False)])
+def test_dsv4_special_scale_bytes(H, byte, nan):
+    """DSv4 scale bytes read as 2^(b-127), 255 as NaN: a selected row whose
+    tile-3 scale byte is 255 makes its tokens' outputs NaN and leaves the
+    other tokens unchanged; a byte 0 (2^-127, which the writer never
+    stores) leaves every output finite and within the bar of the oracle
+    (the exponent-byte kernel at 16 heads, the many-head kernel at 64)."""
+    c = case(W.FMT_FP8_DSV4, H=H, topk=256)
+    d = Dev(c)
+    o1, l1 = pre(d)
+    slot = int(c.indices[0, 0])
+    assert slot >= 0
+    flat = d.pool.data.view(-1)
+    at = (slot // 64) * d.pool.data.stride(0) + (slot % 64) * W.ROW_BYTES[W.FMT_FP8_DSV4] + 576 + 3
+    flat[at] = byte
+    o2, l2 = pre(d)
+    sel = torch.from_numpy((c.indices == slot).any(axis=1)).cuda()
+    assert sel[0]
+    if nan:
+        assert torch.isnan(o2.float()[sel]).all()
+        assert torch.equal(o2[~sel], o1[~sel]) and torch.equal(l2[~sel], l1[~sel])
+    else:
+        pool = oracle_pool(c)
+        pool.data[:] = d.pool.data.cpu().numpy()
+        _, lf32, of, _ = oracle.prefill(c.q, pool, c.indices, sm_scale=c.sm_scale)
+        from gpu_util import assert_lse_close, assert_out_close
+        assert_out_close(o2.float().cpu().numpy().astype(np.float64), of)
+        assert_lse_close(l2.cpu().numpy(), lf32)
+
+
 def test_decode_split_invariance():
     # any split count merges to the prefill result (within tolerance)
     c = case(W.FMT_FP8, H=16, topk=1000, ctx=2048, with_sink=True, with_topk_length=True)
@@ -201,7 +232,7 @@ def test_error_codes():
         smla.prefill(d.q, narrow, d.indices)
 
 
-@pytest.mark.parametrize("fmt", [W.FMT_FP8, W.FMT_INT8])
+@pytest.mark.parametrize("fmt", [W.FMT_FP8, W.FMT_INT8, W.FMT_FP8_DSV4])
 def test_nonfinite_row_stays_in_its_token(fmt):
     """One pool row holds non-finite data (e4m3 NaN codes, or a NaN rope
     value), and token A's list selects it.  Token B, which the same
@@ -223,9 +254,11 @@ def test_nonfinite_row_stays_in_its_token(fmt):
     c.topk_length = L
     d = Dev(c)
     raw = d.pool.data.view(-1)
-    off = (bad_slot // 64) * d.pool.data.stride(0) + (bad_slot % 64) * 656
+    off = (bad_slot // 64) * d.pool.data.stride(0) + (bad_slot % 64) * W.ROW_BYTES[fmt]
     if fmt == W.FMT_FP8:
         raw[off:off + 512] = 0x7F                                   # e4m3 NaN codes
+    elif fmt == W.FMT_FP8_DSV4:
+        raw[off:off + 448] = 0x7F                                   # e4m3 NaN codes
     else:
         raw[off + 528:off + 530] = torch.tensor([0xC0, 0x7F], dtype=torch.uint8, device="cuda")  # NaN rope
     pool = oracle_pool(c)

@@ -1,0 +1,70 @@
+"""Short lists put the precision of P, as it enters PV, straight into the
+output.  With one to four candidates, one or two of them carry nearly all
+the weight, so an error in a weight times |v| shows at full size, and
+outputs of magnitude 2..4 leave only 1e-2 - 2^-8 of the bar once the BF16
+rounding of out has taken its share.  The value rows here are twice the
+unit normal of the other tests (|v| up to about 9): P rounded to BF16 (8
+significant bits) would miss the bar by up to 2^-9 x 9 = 0.018, while P'
+in FP16 (11 bits, for e4m3 codes) or as a BF16 pair (16 bits, for
+arbitrary scales and BF16 rows) keeps every value within it.  At these
+magnitudes the BF16 rounding of out alone averages more than the mean bar
+of 1e-3, so the mean error may exceed that of the oracle's correctly rounded
+output by at most 1e-3.  Every kernel family is covered: the many-head kernel (FP8, rope-less FP8, arbitrary
+scales, INT8, DSv4), the MX kernels (DSv4 and DOTS3_SWA at 16 heads, DOTS3_SWA
+at 64) and the few-head kernel (BF16, FP8, INT8), in the prefill form and,
+for two of them, through split decode and the combine."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_top_mla_smla_amd as smla
+from sparse_top_mla_smla_amd import workloads as W
+
+from gpu_util import Dev, assert_lse_close, assert_out_close, bf16_dev_to_f64, f64_of_bits, need_gpu
+from helpers import oracle_pool
+
+pytestmark = pytest.mark.gpu
+
+CONFIGS = [
+    (W.FMT_FP8, 64), (W.FMT_FP8_NOPE, 64), (W.FMT_FP8_ANY, 64), (W.FMT_INT8, 64), (W.FMT_FP8_DSV4, 64),
+    (W.FMT_FP8_DSV4, 16), (W.FMT_FP8_DOTS3, 16), (W.FMT_FP8_DOTS3, 64),
+    (W.FMT_BF16, 8), (W.FMT_FP8, 8), (W.FMT_INT8, 8),
+]
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def short_list_case(fmt, H):
+    c = W.make_case(f"short_{fmt}_{H}", config_id=400 + 8 * fmt + H // 8, seed=11, fmt=fmt, T=256, H=H, n_seqs=1,
+                    ctx=1024, topk=4, causal=False, with_topk_length=True)
+    c.kv = W.f32_to_bf16_bits(W.bf16_bits_to_f32(c.kv) * 2.0)   # exact: a power of two
+    return c
+
+
+@pytest.mark.parametrize("fmt,H", CONFIGS)
+def test_short_lists_with_large_values_prefill(fmt, H):
+    c = short_list_case(fmt, H)
+    d = Dev(c)
+    o, l = smla.prefill(d.q, d.pool, d.indices, topk_length=d.topk_length, sm_scale=float(c.sm_scale))
+    torch.cuda.synchronize()
+    ob, lf32, of, _ = oracle.prefill(c.q, oracle_pool(c), c.indices, topk_length=c.topk_length, sm_scale=c.sm_scale)
+    assert_out_close(bf16_dev_to_f64(o), of, mean_ref=f64_of_bits(ob))
+    assert_lse_close(l.cpu().numpy(), lf32)
+
+
+@pytest.mark.parametrize("fmt,H", [(W.FMT_FP8, 64), (W.FMT_FP8_DSV4, 64)])
+def test_short_lists_with_large_values_decode(fmt, H):
+    """Two splits of the four-entry lists (two entries each), then the
+    combine: the same bar on the combined BF16 output."""
+    c = short_list_case(fmt, H)
+    d = Dev(c)
+    po, pl = smla.decode(d.q, d.pool, d.indices, 2, topk_length=d.topk_length, sm_scale=float(c.sm_scale))
+    o, l = smla.combine(po, pl)
+    torch.cuda.synchronize()
+    ob, lf32, of, _ = oracle.prefill(c.q, oracle_pool(c), c.indices, topk_length=c.topk_length, sm_scale=c.sm_scale)
+    assert_out_close(bf16_dev_to_f64(o), of, mean_ref=f64_of_bits(ob))
+    assert_lse_close(l.cpu().numpy(), lf32)
