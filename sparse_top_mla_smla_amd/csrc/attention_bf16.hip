@@ -225,6 +225,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(AttnParams p) {
   // 128*wave + 16dt + 4lg + i of head lc
   float m_run = -INFINITY;
   float l_part = 0.0f;
+  int o_k = 0;  // FP16 rows: P, l and O are taken relative to 2^(m_run + o_k) (see f16_bias)
   f32x4 O[NDT];
 #pragma unroll
   for (int i = 0; i < NDT; ++i) O[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -244,7 +245,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(AttnParams p) {
     // power-of-two rows: PV of this tile in FP16 under the bias of its
     // largest scale (the waves' maxima are read before the next tile's rows
     // replace them)
-    F16Bias bias{1.0f, 1.0f};
+    F16Bias bias{1.0f, 1.0f, 0.0f, 0};
     if constexpr (G::POW2) bias = f16_bias(max(max(emax[0], emax[1]), max(emax[2], emax[3])));
     if (k + 1 < n_tiles) issue_rows(k + 1);
     uint64_t pend = 0;
@@ -317,9 +318,11 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(AttnParams p) {
     // every wave takes the same decision per head, so the waves' column
     // slices stay under one max; lanes that do not move multiply by 1
     const bool need = mx > m_run + LAZY;
-    if (__any(need)) {
-      const float alpha = need ? ((m_run == -INFINITY) ? 0.0f : exp2f(m_run - mx)) : 1.0f;
+    const bool shift = G::POW2 && bias.k != o_k;  // this tile's k (scales above 2^14): O and l move with P
+    if (__any(need) || shift) {
+      const float alpha = (need ? ((m_run == -INFINITY) ? 0.0f : exp2f(m_run - mx)) : 1.0f) * exp2i(o_k - bias.k);
       m_run = need ? mx : m_run;
+      o_k = bias.k;
       l_part *= alpha;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) O[dt] *= alpha;
@@ -327,7 +330,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(AttnParams p) {
     float pr[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      pr[i] = (s[i] == -INFINITY) ? 0.0f : exp2f(s[i] - m_run);
+      pr[i] = (s[i] == -INFINITY) ? 0.0f : exp2f(s[i] - (m_run + (float)o_k));
       l_part += pr[i];
     }
     if constexpr (FMT == FMT_BF16) {
@@ -428,7 +431,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(AttnParams p) {
   if (lg == 0) red[wave * 16 + lc] = l_w;
   __syncthreads();
   const float Lsum = (red[lc] + red[16 + lc]) + (red[32 + lc] + red[48 + lc]);
-  const float M = m_run;
+  const float M = m_run + (float)o_k;
 
   const int h = h0 + lc;
   if (h >= p.H) return;

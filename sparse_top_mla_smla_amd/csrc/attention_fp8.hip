@@ -21,7 +21,10 @@
 // one scale tile, so its partial score is multiplied by each candidate's
 // scale of that tile before the rope product is added.
 //
-// All products use v_mfma_f32_32x32x16_bf16.  Eight waves; wave w = g + 4hh
+// QK uses v_mfma_f32_32x32x16_bf16.  PV of power-of-two rows uses
+// v_mfma_f32_32x32x16_f16 (P' in FP16 keeps 11 significant bits of each
+// weight against BF16's 8, at the same rate); rows with arbitrary scales
+// keep BF16 and a pair for P'.  Eight waves; wave w = g + 4hh
 // works on latent group g (0..3) and head half hh (heads [32hh, 32hh+32)).
 // Per 64-candidate tile:
 //  1. QK^T, split over the latent dimension: wave (g, hh) forms the partial
@@ -34,11 +37,13 @@
 //  3. Online softmax on the owned 16 x 32 block in the exp2 domain.  The
 //     four waves of a head half exchange their block maxima, so they all
 //     hold the same running max per head; it moves lazily (only when
-//     exceeded by 2^8), so O is rarely rescaled.  P goes to LDS in FP32.
+//     exceeded by 2^8), so O is rarely rescaled.  P' goes to LDS: FP16
+//     under the tile's exponent bias (f16_bias), or a BF16 pair.
 //  4. PV, split over output columns: wave (g, hh) accumulates O^T for
 //     columns [128g, 128g+128) of its heads.  V^T is read from the raw codes
-//     with ds_read_b64_tr_b8 and converted with scale 1; the row scale of
-//     column group g (a per-candidate factor) is folded into P.
+//     with ds_read_b64_tr_b8 and converted with the tile's bias 2^b (FP16)
+//     or scale 1 (BF16); the row scale of column group g (a per-candidate
+//     factor) is folded into P'.
 // Raw tiles are double-buffered in LDS, chunk-major: 16-byte piece ck
 // (0..40) of tile row r (0..63) sits at byte ck*1024 + r*16.  All eight
 // waves gather the next tile straight from global memory with
@@ -191,7 +196,7 @@ constexpr int TILE = CHUNKS * CS;            // 37,888 bytes per tile
 template <int CODES>
 constexpr int chunks_of() { return CODES == FMT_FP8_DSV4 ? v4::CHUNKS : CHUNKS; }
 constexpr int RECV_FLOATS = 8 * 3 * 2 * 64 * 4;  // [8 owners][3 senders][2][64 lanes][4] f32
-constexpr int PS = 72;                       // P' row stride (bf16): [4 groups][64 heads][PS], aliases recv
+constexpr int PS = 72;                       // P' row stride (16-bit): [4 groups][64 heads][PS], aliases recv
 static_assert(4 * 64 * PS * 2 <= RECV_FLOATS * 4, "P' must fit in the partial-exchange buffer");
 constexpr int GS = 64 * PS * 2;              // bytes of one P' group slot
 // rows with arbitrary scales keep P' as a BF16 pair (high part and rest),
@@ -252,7 +257,7 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) int32_t valid[2 * TC];  // [buffer][row]: row was loaded
   __shared__ __attribute__((aligned(16))) int32_t idx0[TC];       // index list of even tiles
   __shared__ __attribute__((aligned(16))) int32_t idx1[TC];       // index list of odd tiles
-  uint16_t* pq = reinterpret_cast<uint16_t*>(recv);              // P' (bf16), after the reduce
+  uint16_t* pq = reinterpret_cast<uint16_t*>(recv);              // P' (FP16 or BF16), after the reduce
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in SGPRs
@@ -421,6 +426,7 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
   // softmax state for heads 32hh + l32 (identical in the four waves of hh)
   float m_run = -INFINITY;
   float l_part = 0.0f;  // this wave's share: candidates 16g.. of every tile
+  int o_k = 0;          // P, l and O are taken relative to 2^(m_run + o_k) (see f16_bias)
   // O^T accumulators: columns [128g + 32dt, +32) x heads [32hh, +32)
   f32x16 O[4];
 #pragma unroll
@@ -543,7 +549,7 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
     // PV of power-of-two rows runs in FP16 under the tile's bias (f16_bias):
     // the largest exponent of the 64 rows' scales (DSv4: of their seven
     // exponent bytes; DSv4's BF16 rope values enter PV as FP16 unbiased)
-    float vscale = 1.0f, pscale = 1.0f;
+    F16Bias bias{1.0f, 1.0f, 0.0f, 0};
     if constexpr (F16) {
       uint32_t e;
       if constexpr (DS) {
@@ -553,9 +559,7 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
         const uint4 sc4 = *reinterpret_cast<const uint4*>(raw + CK_SCALE * CS + lane * 16);
         e = max(max((sc4.x >> 23) & 0xFFu, (sc4.y >> 23) & 0xFFu), max((sc4.z >> 23) & 0xFFu, (sc4.w >> 23) & 0xFFu));
       }
-      const F16Bias bias = f16_bias(wave_max_u32(e));
-      vscale = bias.v;
-      pscale = bias.p;
+      bias = f16_bias(wave_max_u32(e));
     }
     if (pend >= 0) {
       store_result(pend, pend_factor, pend_lse, false);
@@ -690,20 +694,29 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
       const bool need = mx > m_run + TAU;
       alpha = need ? ((m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run - mx)) : 1.0f;
       m_run = need ? mx : m_run;
+      if constexpr (F16) {
+        // this tile's k (scales above 2^14): O and l move with P
+        alpha *= exp2i(o_k - bias.k);
+        o_k = bias.k;
+      }
+      // P relative to 2^(m_run + k); FP16 P' of 656-byte rows takes P x 2^-b
+      // straight from the exponential
+      constexpr bool FOLD = F16 && !DS;
+      const float mb = m_run + (FOLD ? bias.B : (float)o_k);
       float psum = 0.0f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        s0[r] = (s0[r] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(s0[r] - m_run);
-        s1[r] = (s1[r] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(s1[r] - m_run);
+        s0[r] = (s0[r] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(s0[r] - mb);
+        s1[r] = (s1[r] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(s1[r] - mb);
         psum += s0[r] + s1[r];
       }
-      l_part = l_part * alpha + psum;
+      l_part = l_part * alpha + (FOLD ? psum * bias.v : psum);
       const uint32_t pw = lds_addr(pq + hl * PS + 16 * g + 4 * hi);
       if constexpr (DS) {
-        // DSv4: P'_t = P x (the row's scale of tile t) for the seven scale
-        // tiles, in slots 0..6 (exact: the scales are powers of two), and P
-        // itself in slot 7 for the rope columns
-        const f32x4 s0b = s0 * pscale, s1b = s1 * pscale;  // P x 2^-b
+        // DSv4: P'_t = P x 2^-b x (the row's scale of tile t) in FP16 for
+        // the seven scale tiles, in slots 0..6, and P itself in slot 7 for
+        // the rope columns (which enter PV unbiased)
+        const f32x4 s0b = s0 * bias.p, s1b = s1 * bias.p;  // P x 2^-b
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
           u32x2 v0, v1;
@@ -726,7 +739,7 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
 #undef SMLA_PST
         }
       } else {
-        // P'_gg = P x (row scale of column group gg), BF16, for the PV of
+        // P'_gg = P x (row scale of column group gg) (x 2^-b in FP16), for the PV of
         // every group; the four scales of a row are one 16-byte piece
         const uint8_t* scp = raw + CK_SCALE * CS + (16 * g + 4 * hi) * 16;
         f32x4 sc0[4], sc1[4];
@@ -737,8 +750,6 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
         }
         u32x2 w0[4], w1[4];
         if constexpr (F16) {
-          s0 *= pscale;
-          s1 *= pscale;
 #pragma unroll
           for (int gg = 0; gg < 4; ++gg) {
             w0[gg] = u32x2{pack_f16(s0[0] * sc0[0][gg], s0[1] * sc0[1][gg]), pack_f16(s0[2] * sc0[2][gg], s0[3] * sc0[3][gg])};
@@ -799,7 +810,8 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
       // DSv4: columns 128g + 32dt.. take P' of scale tile 2g + dt/2 (slot
       // A for dt 0, 1, slot B for dt 2, 3); group 3's columns 448..511 are
       // the BF16 rope values (slot 7, P itself), read with
-      // ds_read_b64_tr_b16 from pieces 28 + 4(dt - 2) + 2g16 + (b >> 1)
+      // ds_read_b64_tr_b16 from pieces 28 + 4(dt - 2) + 2g16 + (b >> 1) and
+      // converted to FP16
       const uint32_t va = lds_addr(raw + (8 * g + g16) * CS + (8 * hi + jr) * 16 + 8 * jb);
       // columns 128g + 0..63 (codes of scale tile 2g, slot A) first; the
       // reads of the other 64 columns are issued under their MFMAs.  The
@@ -822,7 +834,7 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
         const u32x4 pb = pA[2 * ks];  // candidates 16ks + 8hi + i
 #pragma unroll
         for (int dt = 0; dt < 2; ++dt) {
-          const f16x8 v = cvt8_f16((uint32_t)v8[ks][dt][0], (uint32_t)v8[ks][dt][1], vscale);
+          const f16x8 v = cvt8_f16((uint32_t)v8[ks][dt][0], (uint32_t)v8[ks][dt][1], bias.v);
           O[dt] = mfma_32x32x16_f16(v, __builtin_bit_cast(f16x8, pb), O[dt]);
         }
       }
@@ -846,7 +858,7 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
           for (int k = 0; k < 2; ++k)
 #pragma unroll
             for (int d = 0; d < 2; ++d) {
-              const f16x8 v = cvt8_f16((uint32_t)w8[k][d][0], (uint32_t)w8[k][d][1], vscale);
+              const f16x8 v = cvt8_f16((uint32_t)w8[k][d][0], (uint32_t)w8[k][d][1], bias.v);
               O[2 + d] = mfma_32x32x16_f16(v, __builtin_bit_cast(f16x8, pr[2 * kh + k]), O[2 + d]);
             }
         }
@@ -919,7 +931,7 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
           if constexpr (F16) {
-            const f16x8 v = cvt8_f16((uint32_t)v8[ks][dt][0], (uint32_t)v8[ks][dt][1], vscale);
+            const f16x8 v = cvt8_f16((uint32_t)v8[ks][dt][0], (uint32_t)v8[ks][dt][1], bias.v);
             O[dt] = mfma_32x32x16_f16(v, __builtin_bit_cast(f16x8, pb[ks]), O[dt]);
           } else {
             const bf16x8 v = codes8<CODES>((uint32_t)v8[ks][dt][0], (uint32_t)v8[ks][dt][1], 1.0f);
@@ -933,7 +945,7 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
   // the four groups, normalization; the result is stored now, or by the
   // next tile when there is one; then start over with empty state ----
   float* lsum = maxb;  // [4][64]; free once every wave is past the softmax of the tile
-  auto finish = [&](int32_t key, bool defer) {
+  auto finish = [&](int32_t key, bool defer) __attribute__((always_inline)) {
     {
       const float lt = l_part + __shfl_xor(l_part, 32);
       if (hi == 0) lsum[g * 64 + 32 * hh + l32] = lt;
@@ -941,7 +953,7 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
     lds_barrier();
     const int hl = 32 * hh + l32;
     const float Ls = (lsum[hl] + lsum[64 + hl]) + (lsum[128 + hl] + lsum[192 + hl]);
-    const float M = m_run;
+    const float M = m_run + (float)o_k;
     const bool empty = !(Ls > 0.0f);
     const float lse_v = empty ? -INFINITY : (M + __log2f(Ls)) * LN2;
     m_run = -INFINITY;

@@ -25,13 +25,15 @@
 //    scaled afterwards, and the rope columns (BF16 in the row) add on top.
 //  * The four waves agree on one running max per head through LDS (lazy:
 //    it moves only when exceeded by 2^8, so O is rarely rescaled); each
-//    wave writes its candidates' probabilities times each tile's scale,
-//    P'_g = P * scale(c, g) (and P itself for BF16 value columns), in BF16
-//    to LDS.
+//    wave writes its candidates' probabilities times each tile's scale
+//    and the tile's FP16 bias, P'_g = P * scale(c, g) * 2^-b (and P itself
+//    for BF16 value columns), in FP16 to LDS (f16_bias: b follows the
+//    tile's largest exponent byte, from the waves' maxima in LDS).
 //  * PV: wave w owns value columns [w*DV/4, (w+1)*DV/4) for all 64
-//    candidates: O^T[d][h] += V^T[d][c] P'^T[c][h] (v_mfma 16x16x32); V^T
-//    comes from the raw codes with ds_read_b64_tr_b8 (converted with scale
-//    1) or, for BF16 columns, with ds_read_b64_tr_b16.
+//    candidates: O^T[d][h] += V^T[d][c] P'^T[c][h] (v_mfma_f32_16x16x32_f16);
+//    V^T comes from the raw codes with ds_read_b64_tr_b8 (converted to FP16
+//    times 2^b) or, for BF16 columns, with ds_read_b64_tr_b16 (converted to
+//    FP16).
 // Because every wave holds a disjoint slice of the value columns under the
 // same running max, the end of the list needs only the per-head sums from
 // the other waves, not a merge of outputs.
@@ -220,6 +222,7 @@ __global__ __launch_bounds__(NT, R::OCC) void attn_mx_kernel(AttnParams p) {
   // WCOLS*wave + 16dt + 4lg + i of head lc
   float m_run = -INFINITY;
   float l_part = 0.0f;
+  int o_k = 0;  // P, l and O are taken relative to 2^(m_run + o_k) (see f16_bias)
   f32x4 O[G::NDT];
 #pragma unroll
   for (int i = 0; i < G::NDT; ++i) O[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -293,9 +296,11 @@ __global__ __launch_bounds__(NT, R::OCC) void attn_mx_kernel(AttnParams p) {
     // every wave takes the same decision per head, so the waves' column
     // slices stay under one max; lanes that do not move multiply by 1
     const bool need = mx > m_run + LAZY;
-    if (__any(need)) {
-      const float alpha = need ? ((m_run == -INFINITY) ? 0.0f : exp2f(m_run - mx)) : 1.0f;
+    const bool shift = bias.k != o_k;  // this tile's k (scales above 2^14): O and l move with P
+    if (__any(need) || shift) {
+      const float alpha = (need ? ((m_run == -INFINITY) ? 0.0f : exp2f(m_run - mx)) : 1.0f) * exp2i(o_k - bias.k);
       m_run = need ? mx : m_run;
+      o_k = bias.k;
       l_part *= alpha;
 #pragma unroll
       for (int dt = 0; dt < G::NDT; ++dt) O[dt] *= alpha;
@@ -303,7 +308,7 @@ __global__ __launch_bounds__(NT, R::OCC) void attn_mx_kernel(AttnParams p) {
     float pr[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      pr[i] = (s[i] == -INFINITY) ? 0.0f : exp2f(s[i] - m_run);
+      pr[i] = (s[i] == -INFINITY) ? 0.0f : exp2f(s[i] - (m_run + (float)o_k));
       l_part += pr[i];
     }
     // P'_g[h][c] = P[c][h] * scale(c, g) * 2^-b in FP16, candidates
@@ -370,7 +375,7 @@ __global__ __launch_bounds__(NT, R::OCC) void attn_mx_kernel(AttnParams p) {
   if (lg == 0) red[wave * 16 + lc] = l_w;
   __syncthreads();
   const float Lsum = (red[lc] + red[16 + lc]) + (red[32 + lc] + red[48 + lc]);
-  const float M = m_run;
+  const float M = m_run + (float)o_k;
 
   const int h = h0 + lc;
   if (h >= p.H) return;
@@ -545,6 +550,7 @@ __global__ __launch_bounds__(NT32, 1) void attn_mx32_kernel(AttnParams p) {
 
   float m_run = -INFINITY;
   float l_part = 0.0f;
+  int o_k = 0;  // P, l and O are taken relative to 2^(m_run + o_k) (see f16_bias)
   f32x4 O[G::NDT];
 #pragma unroll
   for (int i = 0; i < G::NDT; ++i) O[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -622,9 +628,11 @@ __global__ __launch_bounds__(NT32, 1) void attn_mx32_kernel(AttnParams p) {
     __syncthreads();
     mx = fmaxf(fmaxf(red[lc], red[16 + lc]), fmaxf(red[32 + lc], red[48 + lc]));
     const bool need = mx > m_run + LAZY;
-    if (__any(need)) {
-      const float alpha = need ? ((m_run == -INFINITY) ? 0.0f : exp2f(m_run - mx)) : 1.0f;
+    const bool shift = bias.k != o_k;  // this tile's k (scales above 2^14): O and l move with P
+    if (__any(need) || shift) {
+      const float alpha = (need ? ((m_run == -INFINITY) ? 0.0f : exp2f(m_run - mx)) : 1.0f) * exp2i(o_k - bias.k);
       m_run = need ? mx : m_run;
+      o_k = bias.k;
       l_part *= alpha;
 #pragma unroll
       for (int dt = 0; dt < G::NDT; ++dt) O[dt] *= alpha;
@@ -632,7 +640,7 @@ __global__ __launch_bounds__(NT32, 1) void attn_mx32_kernel(AttnParams p) {
     float pr[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      pr[i] = (s[i] == -INFINITY) ? 0.0f : exp2f(s[i] - m_run);
+      pr[i] = (s[i] == -INFINITY) ? 0.0f : exp2f(s[i] - (m_run + (float)o_k));
       l_part += pr[i];
     }
     // P'_g[h][c] = P[c][h] * scale(c, g) * 2^-b in FP16, candidates 16wl + 4lg + (0..3)
@@ -679,7 +687,7 @@ __global__ __launch_bounds__(NT32, 1) void attn_mx32_kernel(AttnParams p) {
   if (lg == 0) red[wl * 16 + lc] = l_w;
   __syncthreads();
   const float Lsum = (red[lc] + red[16 + lc]) + (red[32 + lc] + red[48 + lc]);
-  const float M = m_run;
+  const float M = m_run + (float)o_k;
 
   const int h = h0 + lc;
   if (h >= p.H) return;

@@ -116,18 +116,29 @@ __device__ __forceinline__ uint2 fp8x4_to_f16x4(uint32_t v, float scale) {
 // PV over e4m3 codes with power-of-two scales runs in FP16: P' = P x scale
 // rounded once to FP16 has 11 significant bits against BF16's 8.  FP16's
 // range is held by a power-of-two bias per tile: with 2^(e-127) the tile's
-// largest scale (e its biased exponent, e.g. an exponent byte), V^T =
-// codes x 2^b and P' = P x scale x 2^-b, b = e - 134 within [-15, 7].  Then
-// P' <= 2^8 x 2^7 (P <= 2^8 under a lazy running max that moves when
-// exceeded by 2^8), and the codes (2^-9 .. 448) times 2^b are exact FP16
-// values; the bias cancels in each product.
+// largest scale (e its biased exponent, e.g. an exponent byte), P' = P x
+// scale x 2^-B with B = e - 134 (at least -15), so P' <= 2^8 x 2^7 (P <=
+// 2^8 under a lazy running max that moves when exceeded by 2^8), and V^T =
+// codes x 2^b with b = min(B, 7), so the codes (2^-9 .. 448) times 2^b are
+// exact FP16 values.  The rest of 2^-B, 2^-k with k = B - b, is nonzero
+// only for a largest scale above 2^14 (values beyond 7.3e6): the kernels
+// take P relative to 2^(running max + k), which moves P, O and the row sum
+// into units of 2^-k together, like a move of the running max (exactly: by
+// a power of two), and add k back to the max for the LSE.  P' = P x scale
+// x 2^-b then stays below 2^15 in every case.
 struct F16Bias {
   float v;  // 2^b, for the codes
   float p;  // 2^-b, for P'
+  float B;  // b + k
+  int k;    // 0 unless the largest scale exceeds 2^14
 };
+__device__ __forceinline__ float exp2i(int n) {  // 2^n for -126 <= n <= 127
+  return __builtin_bit_cast(float, (uint32_t)(127 + n) << 23);
+}
 __device__ __forceinline__ F16Bias f16_bias(uint32_t e) {
-  const int b = min(max((int)e - 134, -15), 7);
-  return F16Bias{__builtin_bit_cast(float, (uint32_t)(127 + b) << 23), __builtin_bit_cast(float, (uint32_t)(127 - b) << 23)};
+  const int B = max((int)e - 134, -15);
+  const int b = min(B, 7);
+  return F16Bias{exp2i(b), exp2i(-b), (float)B, B - b};
 }
 
 // the largest value of v over the 64 lanes, in every lane (DPP within each

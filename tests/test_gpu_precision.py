@@ -68,3 +68,41 @@ def test_short_lists_with_large_values_decode(fmt, H):
     ob, lf32, of, _ = oracle.prefill(c.q, oracle_pool(c), c.indices, topk_length=c.topk_length, sm_scale=c.sm_scale)
     assert_out_close(bf16_dev_to_f64(o), of, mean_ref=f64_of_bits(ob))
     assert_lse_close(l.cpu().numpy(), lf32)
+
+
+NOPE_DIMS = {W.FMT_FP8: 512, W.FMT_FP8_NOPE: 512, W.FMT_FP8_DSV4: 448, W.FMT_FP8_DOTS3: 1024}
+
+
+@pytest.mark.parametrize("fmt,H", [(W.FMT_FP8, 64), (W.FMT_FP8, 8), (W.FMT_FP8_NOPE, 64), (W.FMT_FP8_DSV4, 64),
+                                   (W.FMT_FP8_DSV4, 16), (W.FMT_FP8_DOTS3, 16), (W.FMT_FP8_DOTS3, 64)])
+def test_scales_above_2_14(fmt, H):
+    """The nope part of every cache row times 2^24 and of every q row times
+    2^-24 leaves each score unchanged and makes the scales 2^24 times larger
+    (above 2^14, where the FP16 bias runs out and the kernels keep O's code
+    columns in units of 2^-k).  The exact result is then the unscaled case's
+    with its nope value columns times 2^24: the outputs scaled back by 2^-24
+    (exact in BF16 and FP32) meet the bar against the oracle of the unscaled
+    case, in the prefill form and in the decode partials."""
+    c = W.make_case(f"bigscale_{fmt}_{H}", config_id=460 + 8 * fmt + H // 8, seed=12, fmt=fmt, T=96, H=H, n_seqs=1,
+                    ctx=1024, topk=200, causal=True, with_topk_length=True)
+    n = NOPE_DIMS[fmt]
+    pool = oracle_pool(c)
+    ob, lf32, of, _ = oracle.prefill(c.q, pool, c.indices, topk_length=c.topk_length, sm_scale=c.sm_scale)
+    rpo, rpl = oracle.decode_split(c.q, pool, c.indices, 3, topk_length=c.topk_length, sm_scale=c.sm_scale)
+    kv = W.bf16_bits_to_f32(c.kv)
+    kv[:, :n] *= 2.0 ** 24
+    q = W.bf16_bits_to_f32(c.q_buf)
+    q[:, :, :n] *= 2.0 ** -24
+    c.kv, c.q_buf = W.f32_to_bf16_bits(kv), W.f32_to_bf16_bits(q)
+    d = Dev(c)
+    o, l = smla.prefill(d.q, d.pool, d.indices, topk_length=d.topk_length, sm_scale=float(c.sm_scale))
+    po, pl = smla.decode(d.q, d.pool, d.indices, 3, topk_length=d.topk_length, sm_scale=float(c.sm_scale))
+    torch.cuda.synchronize()
+    down = torch.ones(o.shape[-1], dtype=torch.float64)
+    down[:n] = 2.0 ** -24
+    got = o.double().cpu() * down
+    assert torch.isfinite(got).all()
+    assert_out_close(got.numpy(), of, mean_ref=f64_of_bits(ob))
+    assert_lse_close(l.cpu().numpy(), lf32)
+    assert_out_close((po.double().cpu() * down).numpy(), rpo, what="part_out", bf16=False)
+    assert_lse_close(pl.cpu().numpy(), rpl, what="part_lse")

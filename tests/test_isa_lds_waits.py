@@ -10,7 +10,9 @@ kernel's instructions in order, tracking the LDS reads in flight: LDS
 operations complete in order, so after `s_waitcnt lgkmcnt(k)` at most the k
 most recent LDS operations can still be pending.  No instruction may read or
 write a register that a pending LDS read still has to fill.  The walk
-follows the instruction order, not the branches.  No GPU is needed.
+follows the instruction order, not the branches; after an unconditional
+branch the next instruction is not reached from the one before it, so the
+walk starts over there with nothing pending.  No GPU is needed.
 """
 import os
 import re
@@ -91,6 +93,9 @@ def hazards(ins):
                     found.append(line)
                 lds.append((False, set()))
             continue
+        if op in ("s_branch", "s_setpc_b64", "s_endpgm"):
+            lds = []
+            continue
         if op.startswith("s_"):
             continue
         if _vregs(line[len(op):]) & pending:
@@ -107,6 +112,11 @@ def test_hazard_walk_finds_a_copy_before_the_wait():
     bad = ["ds_read_b128 v[4:7], v171", "ds_read_b128 v[8:11], v171 offset:16", "s_waitcnt lgkmcnt(1)",
            "v_mov_b32_e32 v2, v9"]
     assert hazards(bad) == ["v_mov_b32_e32 v2, v9"]
+    # the block after an unconditional branch is reached from elsewhere
+    jump = ["ds_read_b128 v[4:7], v171", "s_branch .LBB0_7", "ds_read_b128 v[8:11], v5", "s_waitcnt lgkmcnt(0)"]
+    assert hazards(jump) == []
+    fall = ["ds_read_b128 v[4:7], v171", "s_cbranch_scc1 .LBB0_7", "ds_read_b128 v[8:11], v5"]
+    assert hazards(fall) == ["ds_read_b128 v[8:11], v5"]
 
 
 @pytest.mark.skipif(not shutil.which(HIPCC) and not os.path.exists(HIPCC), reason="hipcc not found")
