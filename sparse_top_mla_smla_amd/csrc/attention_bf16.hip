@@ -57,10 +57,9 @@ constexpr int P_HEAD = 144;                   // bytes of one head's P row (64 B
 // Row geometry.  BF16 rows: 576 BF16 values.  Quantized rows (656 bytes):
 // 512 codes, four FP32 scales (one per 128 columns), 64 BF16 rope values
 // (padding in rope-less rows, never gathered).  P is kept in four versions,
-// P times the scale of each wave's value columns: FP16 under a per-tile bias
-// for power-of-two scales (f16_bias), a BF16 pair (the rounded value and the
-// rest, eight slots) for arbitrary scales.  BF16 rows keep P as a BF16 pair
-// too (two slots), so P enters PV with 16 significant bits.
+// P times the scale of each wave's value columns, in FP16 under a per-tile
+// bias (f16_bias).  BF16 rows keep P as a BF16 pair (the rounded value and
+// the rest, two slots), so P enters PV with 16 significant bits.
 template <int FMT>
 struct Cols {
   static constexpr bool QUANT = FMT != FMT_BF16;
@@ -70,7 +69,7 @@ struct Cols {
   static constexpr int LDS_ROW = ROW + 16;    // bank spread
   static constexpr int PIECES = ROPE ? ROW / 16 : (D_NOPE + 16) / 16;  // gathered: 72, 41 or 33
   static constexpr int NCH = (PIECES + 3) / 4;  // pieces per thread (4 threads per row)
-  static constexpr int VERSIONS = !QUANT ? 2 : POW2 ? 4 : 8;
+  static constexpr int VERSIONS = !QUANT ? 2 : 4;
   // LDS: tile, P [versions][16 heads][64] BF16, wave maxima / sums [4][16],
   // index stage [3][64] (row addresses)
   static constexpr int TILE_BYTES = TC * LDS_ROW;
@@ -207,7 +206,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(AttnParams p) {
 #pragma unroll
     for (int r = 0; r < NCH; ++r)
       if (PIECES % 4 == 0 || sub + 4 * r < PIECES) dst[4 * r] = stage[r];
-    if constexpr (G::POW2) {
+    if constexpr (G::QUANT) {
       // the largest scale exponent of this wave's rows (piece 32, the four
       // scales, is stage[8] of the row's thread sub == 0), for the FP16 bias
       static_assert(D_NOPE / 16 == 8 * 4 && NCH > 8, "the scale piece");
@@ -246,7 +245,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(AttnParams p) {
     // largest scale (the waves' maxima are read before the next tile's rows
     // replace them)
     F16Bias bias{1.0f, 1.0f, 0.0f, 0};
-    if constexpr (G::POW2) bias = f16_bias(max(max(emax[0], emax[1]), max(emax[2], emax[3])));
+    if constexpr (G::QUANT) bias = f16_bias(max(max(emax[0], emax[1]), max(emax[2], emax[3])), FMT == FMT_INT8 ? 5 : 7);
     if (k + 1 < n_tiles) issue_rows(k + 1);
     uint64_t pend = 0;
     if (k + 2 < n_tiles && tid < TC) pend = load_idx(k + 2);
@@ -318,7 +317,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(AttnParams p) {
     // every wave takes the same decision per head, so the waves' column
     // slices stay under one max; lanes that do not move multiply by 1
     const bool need = mx > m_run + LAZY;
-    const bool shift = G::POW2 && bias.k != o_k;  // this tile's k (scales above 2^14): O and l move with P
+    const bool shift = G::QUANT && bias.k != o_k;  // this tile's k (scales above 2^14): O and l move with P
     if (__any(need) || shift) {
       const float alpha = (need ? ((m_run == -INFINITY) ? 0.0f : exp2f(m_run - mx)) : 1.0f) * exp2i(o_k - bias.k);
       m_run = need ? mx : m_run;
@@ -339,7 +338,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(AttnParams p) {
       *reinterpret_cast<uint2*>(pbuf + lc * P_HEAD + 2 * (16 * wave + 4 * lg)) = hi;
       *reinterpret_cast<uint2*>(pbuf + 16 * P_HEAD + lc * P_HEAD + 2 * (16 * wave + 4 * lg)) =
           make_uint2(bf16_pair_rest(pr[0], pr[1], hi.x), bf16_pair_rest(pr[2], pr[3], hi.y));
-    } else if constexpr (G::POW2) {
+    } else {
       // version v: P x 2^-b x the scale of value columns [128v, +128) in
       // FP16, for the wave that owns those columns
       f32x4 scl[4];
@@ -352,22 +351,6 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(AttnParams p) {
       for (int v = 0; v < 4; ++v)
         *reinterpret_cast<uint2*>(pbuf + v * 16 * P_HEAD + lc * P_HEAD + 2 * (16 * wave + 4 * lg)) =
             make_uint2(pack_f16(pr[0] * scl[0][v], pr[1] * scl[1][v]), pack_f16(pr[2] * scl[2][v], pr[3] * scl[3][v]));
-    } else {
-      // version v: P times the scale of value columns [128v, +128), for the
-      // wave that owns those columns, as a BF16 pair: the rest of the
-      // rounding goes to version 4 + v
-      f32x4 scl[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        scl[i] = *reinterpret_cast<const f32x4*>(tile + (16 * wave + 4 * lg + i) * LDS_ROW + D_NOPE);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float x0 = pr[0] * scl[0][v], x1 = pr[1] * scl[1][v], x2 = pr[2] * scl[2][v], x3 = pr[3] * scl[3][v];
-        const uint2 hi = make_uint2(pack_bf16(x0, x1), pack_bf16(x2, x3));
-        *reinterpret_cast<uint2*>(pbuf + v * 16 * P_HEAD + lc * P_HEAD + 2 * (16 * wave + 4 * lg)) = hi;
-        *reinterpret_cast<uint2*>(pbuf + (4 + v) * 16 * P_HEAD + lc * P_HEAD + 2 * (16 * wave + 4 * lg)) =
-            make_uint2(bf16_pair_rest(x0, x1, hi.x), bf16_pair_rest(x2, x3, hi.y));
-      }
     }
     __syncthreads();
 
@@ -390,31 +373,27 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(AttnParams p) {
           O[dt] = mfma_16x16x32(a, pb, O[dt]);
           O[dt] = mfma_16x16x32(a, pl, O[dt]);
         }
-      } else if constexpr (G::POW2) {
-        // tr8 as below; the codes convert to FP16 times 2^b (the row scale
-        // and 2^-b are in P')
-        const uint8_t* rb = tile + (32 * kc + 8 * lg + (lc >> 1)) * LDS_ROW + WCOLS * wave + 8 * (lc & 1);
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          const i32x2 c = lds_read_tr8(rb + 16 * dt);
-          const uint2 lo = fp8x4_to_f16x4((uint32_t)c[0], bias.v), hi = fp8x4_to_f16x4((uint32_t)c[1], bias.v);
-          O[dt] = mfma_16x16x32_f16(__builtin_bit_cast(f16x8, make_uint4(lo.x, lo.y, hi.x, hi.y)),
-                                    __builtin_bit_cast(f16x8, pw), O[dt]);
-        }
       } else {
         // tr8: lane lc = 2r + b reads row 32kc + 8lg + r (a candidate), bytes
         // 8b..8b+7 of a 16-column piece; lane lc receives column lc of the
-        // 8 rows.  The codes convert with scale 1 (the scale is in P).
+        // 8 rows.  The codes convert to FP16 times 2^b (the row scale and
+        // 2^-b are in P').
         const uint8_t* rb = tile + (32 * kc + 8 * lg + (lc >> 1)) * LDS_ROW + WCOLS * wave + 8 * (lc & 1);
-        // the rest of P' (arbitrary scales)
-        const bf16x8 pl =
-            __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(pv + 4 * 16 * P_HEAD + lc * P_HEAD + 2 * (32 * kc + 8 * lg)));
+        const f16x2 sb = {(_Float16)bias.v, (_Float16)bias.v};
+        const f16x2 ob = {(_Float16)(-1152.0f * bias.v), (_Float16)(-1152.0f * bias.v)};
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
           const i32x2 c = lds_read_tr8(rb + 16 * dt);
-          const bf16x8 a = codes8<FMT>((uint32_t)c[0], (uint32_t)c[1], 1.0f);
-          O[dt] = mfma_16x16x32(a, pb, O[dt]);
-          O[dt] = mfma_16x16x32(a, pl, O[dt]);
+          uint2 lo, hi;
+          if constexpr (FMT == FMT_INT8) {
+            lo = int8x4_to_f16x4((uint32_t)c[0], sb, ob);
+            hi = int8x4_to_f16x4((uint32_t)c[1], sb, ob);
+          } else {
+            lo = fp8x4_to_f16x4((uint32_t)c[0], bias.v);
+            hi = fp8x4_to_f16x4((uint32_t)c[1], bias.v);
+          }
+          O[dt] = mfma_16x16x32_f16(__builtin_bit_cast(f16x8, make_uint4(lo.x, lo.y, hi.x, hi.y)),
+                                    __builtin_bit_cast(f16x8, pw), O[dt]);
         }
       }
     }

@@ -21,10 +21,10 @@
 // one scale tile, so its partial score is multiplied by each candidate's
 // scale of that tile before the rope product is added.
 //
-// QK uses v_mfma_f32_32x32x16_bf16.  PV of power-of-two rows uses
-// v_mfma_f32_32x32x16_f16 (P' in FP16 keeps 11 significant bits of each
-// weight against BF16's 8, at the same rate); rows with arbitrary scales
-// keep BF16 and a pair for P'.  Eight waves; wave w = g + 4hh
+// QK uses v_mfma_f32_32x32x16_bf16, PV v_mfma_f32_32x32x16_f16 (P' in FP16
+// keeps 11 significant bits of each weight against BF16's 8, at the same
+// rate; the codes convert exactly to FP16 under the tile's bias).  Eight
+// waves; wave w = g + 4hh
 // works on latent group g (0..3) and head half hh (heads [32hh, 32hh+32)).
 // Per 64-candidate tile:
 //  1. QK^T, split over the latent dimension: wave (g, hh) forms the partial
@@ -37,13 +37,13 @@
 //  3. Online softmax on the owned 16 x 32 block in the exp2 domain.  The
 //     four waves of a head half exchange their block maxima, so they all
 //     hold the same running max per head; it moves lazily (only when
-//     exceeded by 2^8), so O is rarely rescaled.  P' goes to LDS: FP16
-//     under the tile's exponent bias (f16_bias), or a BF16 pair.
+//     exceeded by 2^8), so O is rarely rescaled.  P' goes to LDS in FP16
+//     under the tile's exponent bias (f16_bias).
 //  4. PV, split over output columns: wave (g, hh) accumulates O^T for
 //     columns [128g, 128g+128) of its heads.  V^T is read from the raw codes
-//     with ds_read_b64_tr_b8 and converted with the tile's bias 2^b (FP16)
-//     or scale 1 (BF16); the row scale of column group g (a per-candidate
-//     factor) is folded into P'.
+//     with ds_read_b64_tr_b8 and converted to FP16 times the tile's bias 2^b;
+//     the row scale of column group g (a per-candidate factor) is folded
+//     into P'.
 // Raw tiles are double-buffered in LDS, chunk-major: 16-byte piece ck
 // (0..40) of tile row r (0..63) sits at byte ck*1024 + r*16.  All eight
 // waves gather the next tile straight from global memory with
@@ -99,14 +99,6 @@ __device__ __forceinline__ bf16x8 codes8(uint32_t c0, uint32_t c1, float scale) 
   } else {
     return cvt8(c0, c1, scale);
   }
-}
-
-// x - bf16(x) and y - bf16(y) as a BF16 pair, given hi = the BF16 pair of
-// (x, y) (x in the low half)
-__device__ __forceinline__ uint32_t bf16_rest(float x, float y, uint32_t hi) {
-  const float xh = __builtin_bit_cast(float, hi << 16);
-  const float yh = __builtin_bit_cast(float, hi & 0xFFFF0000u);
-  return pack_bf16(x - xh, y - yh);
 }
 
 __device__ __forceinline__ void global_to_lds_16(const void* src, void* lds_wave_base) {
@@ -199,10 +191,9 @@ constexpr int RECV_FLOATS = 8 * 3 * 2 * 64 * 4;  // [8 owners][3 senders][2][64 
 constexpr int PS = 72;                       // P' row stride (16-bit): [4 groups][64 heads][PS], aliases recv
 static_assert(4 * 64 * PS * 2 <= RECV_FLOATS * 4, "P' must fit in the partial-exchange buffer");
 constexpr int GS = 64 * PS * 2;              // bytes of one P' group slot
-// rows with arbitrary scales keep P' as a BF16 pair (high part and rest),
-// eight slots
-constexpr int RECV_FLOATS_ARB = 8 * GS / 4;
-static_assert(RECV_FLOATS_ARB >= RECV_FLOATS, "the pair buffer holds the partial exchange");
+// DSv4 rows keep eight P' versions (seven scale tiles and the rope columns)
+constexpr int RECV_FLOATS_8 = 8 * GS / 4;
+static_assert(RECV_FLOATS_8 >= RECV_FLOATS, "the eight-slot buffer holds the partial exchange");
 constexpr float TAU = 8.0f;
 
 template <int V>
@@ -245,19 +236,18 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
   // gather into the other buffer, and does not wait for that gather.
   constexpr bool DS = CODES == FMT_FP8_DSV4;                          // DSv4 rows
   constexpr bool ARB = CODES == FMT_FP8_ANY || CODES == FMT_INT8;     // arbitrary scales
-  constexpr bool F16 = !ARB;                                          // PV in FP16 (see the tile step)
   constexpr int NCK = chunks_of<CODES>();                             // pieces per row
   constexpr int RAW = NCK * CS;                                       // bytes per raw tile
   __shared__ __attribute__((aligned(16))) uint8_t raw0[RAW];
   __shared__ __attribute__((aligned(16))) uint8_t raw1[RAW];
-  __shared__ __attribute__((aligned(16))) float recv[CODES == FMT_FP8 ? RECV_FLOATS : RECV_FLOATS_ARB];
+  __shared__ __attribute__((aligned(16))) float recv[DS ? RECV_FLOATS_8 : RECV_FLOATS];
   __shared__ __attribute__((aligned(16))) float maxb[4 * 64];   // [4 groups][64 heads]
   // DSv4: the tile's scales, [scale tile][row] (2^(b-127))
   __shared__ __attribute__((aligned(16))) float dsc[DS ? 7 * TC : 4];
   __shared__ __attribute__((aligned(16))) int32_t valid[2 * TC];  // [buffer][row]: row was loaded
   __shared__ __attribute__((aligned(16))) int32_t idx0[TC];       // index list of even tiles
   __shared__ __attribute__((aligned(16))) int32_t idx1[TC];       // index list of odd tiles
-  uint16_t* pq = reinterpret_cast<uint16_t*>(recv);              // P' (FP16 or BF16), after the reduce
+  uint16_t* pq = reinterpret_cast<uint16_t*>(recv);              // P' (FP16), after the reduce
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in SGPRs
@@ -546,11 +536,11 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
       issue_part(Buf<1 - B>{}, Buf<0>{}, src_next);
     }
     if (w == 0 && nn.t >= 0) issue_idx(Buf<B>{}, nn);
-    // PV of power-of-two rows runs in FP16 under the tile's bias (f16_bias):
-    // the largest exponent of the 64 rows' scales (DSv4: of their seven
-    // exponent bytes; DSv4's BF16 rope values enter PV as FP16 unbiased)
-    F16Bias bias{1.0f, 1.0f, 0.0f, 0};
-    if constexpr (F16) {
+    // PV runs in FP16 under the tile's bias (f16_bias): the largest exponent
+    // of the 64 rows' scales (DSv4: of their seven exponent bytes; DSv4's
+    // BF16 rope values enter PV as FP16 unbiased)
+    F16Bias bias;
+    {
       uint32_t e;
       if constexpr (DS) {
         const uint2 tb = *reinterpret_cast<const uint2*>(raw + v4::CK_TAIL * CS + lane * 16 + 8);
@@ -559,7 +549,7 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
         const uint4 sc4 = *reinterpret_cast<const uint4*>(raw + CK_SCALE * CS + lane * 16);
         e = max(max((sc4.x >> 23) & 0xFFu, (sc4.y >> 23) & 0xFFu), max((sc4.z >> 23) & 0xFFu, (sc4.w >> 23) & 0xFFu));
       }
-      bias = f16_bias(wave_max_u32(e));
+      bias = f16_bias(wave_max_u32(e), CODES == FMT_INT8 ? 5 : 7);
     }
     if (pend >= 0) {
       store_result(pend, pend_factor, pend_lse, false);
@@ -694,14 +684,12 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
       const bool need = mx > m_run + TAU;
       alpha = need ? ((m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run - mx)) : 1.0f;
       m_run = need ? mx : m_run;
-      if constexpr (F16) {
-        // this tile's k (scales above 2^14): O and l move with P
-        alpha *= exp2i(o_k - bias.k);
-        o_k = bias.k;
-      }
-      // P relative to 2^(m_run + k); FP16 P' of 656-byte rows takes P x 2^-b
+      // this tile's k (scales of 2^14 and above): O and l move with P
+      alpha *= exp2i(o_k - bias.k);
+      o_k = bias.k;
+      // P relative to 2^(m_run + k); P' of the 656-byte rows takes P x 2^-b
       // straight from the exponential
-      constexpr bool FOLD = F16 && !DS;
+      constexpr bool FOLD = !DS;
       const float mb = m_run + (FOLD ? bias.B : (float)o_k);
       float psum = 0.0f;
 #pragma unroll
@@ -749,39 +737,10 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
           sc1[r] = *reinterpret_cast<const f32x4*>(scp + (8 + r) * 16);
         }
         u32x2 w0[4], w1[4];
-        if constexpr (F16) {
 #pragma unroll
-          for (int gg = 0; gg < 4; ++gg) {
-            w0[gg] = u32x2{pack_f16(s0[0] * sc0[0][gg], s0[1] * sc0[1][gg]), pack_f16(s0[2] * sc0[2][gg], s0[3] * sc0[3][gg])};
-            w1[gg] = u32x2{pack_f16(s1[0] * sc1[0][gg], s1[1] * sc1[1][gg]), pack_f16(s1[2] * sc1[2][gg], s1[3] * sc1[3][gg])};
-          }
-        } else {
-#pragma unroll
-          for (int gg = 0; gg < 4; ++gg) {
-            w0[gg] = u32x2{pack_bf16(s0[0] * sc0[0][gg], s0[1] * sc0[1][gg]), pack_bf16(s0[2] * sc0[2][gg], s0[3] * sc0[3][gg])};
-            w1[gg] = u32x2{pack_bf16(s1[0] * sc1[0][gg], s1[1] * sc1[1][gg]), pack_bf16(s1[2] * sc1[2][gg], s1[3] * sc1[3][gg])};
-          }
-        }
-            if constexpr (ARB) {
-          // an arbitrary scale makes P x scale inexact in BF16: the rest goes
-          // to slots 4..7 and PV adds both parts (a power-of-two scale only
-          // shifts the exponent)
-          u32x2 r0[4], r1[4];
-#pragma unroll
-          for (int gg = 0; gg < 4; ++gg) {
-            r0[gg] = u32x2{bf16_rest(s0[0] * sc0[0][gg], s0[1] * sc0[1][gg], w0[gg][0]),
-                           bf16_rest(s0[2] * sc0[2][gg], s0[3] * sc0[3][gg], w0[gg][1])};
-            r1[gg] = u32x2{bf16_rest(s1[0] * sc1[0][gg], s1[1] * sc1[1][gg], w1[gg][0]),
-                           bf16_rest(s1[2] * sc1[2][gg], s1[3] * sc1[3][gg], w1[gg][1])};
-          }
-          b64_store<4 * GS>(pw, r0[0]);
-          b64_store<4 * GS + 16>(pw, r1[0]);
-          b64_store<5 * GS>(pw, r0[1]);
-          b64_store<5 * GS + 16>(pw, r1[1]);
-          b64_store<6 * GS>(pw, r0[2]);
-          b64_store<6 * GS + 16>(pw, r1[2]);
-          b64_store<7 * GS>(pw, r0[3]);
-          b64_store<7 * GS + 16>(pw, r1[3]);
+        for (int gg = 0; gg < 4; ++gg) {
+          w0[gg] = u32x2{pack_f16(s0[0] * sc0[0][gg], s0[1] * sc0[1][gg]), pack_f16(s0[2] * sc0[2][gg], s0[3] * sc0[3][gg])};
+          w1[gg] = u32x2{pack_f16(s1[0] * sc1[0][gg], s1[1] * sc1[1][gg]), pack_f16(s1[2] * sc1[2][gg], s1[3] * sc1[3][gg])};
         }
         b64_store<0>(pw, w0[0]);
         b64_store<16>(pw, w1[0]);
@@ -910,34 +869,30 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
       pb[1] = b128_issue<32>(pa);
       pb[2] = b128_issue<64>(pa);
       pb[3] = b128_issue<96>(pa);
-      u32x4 pr[4];  // the rest of P'_g (rows with arbitrary scales only)
-      if constexpr (ARB) {
-        pr[0] = b128_issue<4 * GS>(pa);
-        pr[1] = b128_issue<4 * GS + 32>(pa);
-        pr[2] = b128_issue<4 * GS + 64>(pa);
-        pr[3] = b128_issue<4 * GS + 96>(pa);
-      }
       // one wait for all the reads; the empty statements after it (volatile
       // statements keep their order) carry the dependency to the rest
       asm volatile("s_waitcnt lgkmcnt(0)"
                    : "+v"(v8[0][0]), "+v"(v8[0][1]), "+v"(v8[0][2]), "+v"(v8[0][3]), "+v"(v8[1][0]), "+v"(v8[1][1]),
                      "+v"(v8[1][2]), "+v"(v8[1][3]), "+v"(pb[0]), "+v"(pb[1]), "+v"(pb[2]), "+v"(pb[3]));
-      if constexpr (ARB) asm volatile("" : "+v"(pr[0]), "+v"(pr[1]), "+v"(pr[2]), "+v"(pr[3]));
       asm volatile(""
                    : "+v"(v8[2][0]), "+v"(v8[2][1]), "+v"(v8[2][2]), "+v"(v8[2][3]), "+v"(v8[3][0]), "+v"(v8[3][1]),
                      "+v"(v8[3][2]), "+v"(v8[3][3]));
+      // int8 codes: 2^b and -1152 x 2^b for int8x4_to_f16x4
+      const f16x2 sb = {(_Float16)bias.v, (_Float16)bias.v};
+      const f16x2 ob = {(_Float16)(-1152.0f * bias.v), (_Float16)(-1152.0f * bias.v)};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
-          if constexpr (F16) {
-            const f16x8 v = cvt8_f16((uint32_t)v8[ks][dt][0], (uint32_t)v8[ks][dt][1], bias.v);
-            O[dt] = mfma_32x32x16_f16(v, __builtin_bit_cast(f16x8, pb[ks]), O[dt]);
+          f16x8 v;
+          if constexpr (CODES == FMT_INT8) {
+            const uint2 lo = int8x4_to_f16x4((uint32_t)v8[ks][dt][0], sb, ob);
+            const uint2 hi = int8x4_to_f16x4((uint32_t)v8[ks][dt][1], sb, ob);
+            v = __builtin_bit_cast(f16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
           } else {
-            const bf16x8 v = codes8<CODES>((uint32_t)v8[ks][dt][0], (uint32_t)v8[ks][dt][1], 1.0f);
-            O[dt] = mfma_32x32x16(v, __builtin_bit_cast(bf16x8, pb[ks]), O[dt]);
-            if constexpr (ARB) O[dt] = mfma_32x32x16(v, __builtin_bit_cast(bf16x8, pr[ks]), O[dt]);
+            v = cvt8_f16((uint32_t)v8[ks][dt][0], (uint32_t)v8[ks][dt][1], bias.v);
           }
+          O[dt] = mfma_32x32x16_f16(v, __builtin_bit_cast(f16x8, pb[ks]), O[dt]);
         }
     }
   };

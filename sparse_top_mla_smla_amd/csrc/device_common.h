@@ -113,32 +113,47 @@ __device__ __forceinline__ uint2 fp8x4_to_f16x4(uint32_t v, float scale) {
                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v, scale, true)));
 }
 
-// PV over e4m3 codes with power-of-two scales runs in FP16: P' = P x scale
-// rounded once to FP16 has 11 significant bits against BF16's 8.  FP16's
-// range is held by a power-of-two bias per tile: with 2^(e-127) the tile's
-// largest scale (e its biased exponent, e.g. an exponent byte), P' = P x
-// scale x 2^-B with B = e - 134 (at least -15), so P' <= 2^8 x 2^7 (P <=
-// 2^8 under a lazy running max that moves when exceeded by 2^8), and V^T =
-// codes x 2^b with b = min(B, 7), so the codes (2^-9 .. 448) times 2^b are
-// exact FP16 values.  The rest of 2^-B, 2^-k with k = B - b, is nonzero
-// only for a largest scale above 2^14 (values beyond 7.3e6): the kernels
-// take P relative to 2^(running max + k), which moves P, O and the row sum
-// into units of 2^-k together, like a move of the running max (exactly: by
-// a power of two), and add k back to the max for the LSE.  P' = P x scale
-// x 2^-b then stays below 2^15 in every case.
+// PV over quantized codes runs in FP16: P' = P x scale rounded once to FP16
+// has 11 significant bits against BF16's 8.  FP16's range is held by a
+// power-of-two bias per tile: with e the largest biased exponent of the
+// tile's scales (so every scale is below 2^(e-126); an exponent byte is the
+// scale's biased exponent), P' = P x scale x 2^-B with B = e - 133 (at
+// least -15), so P' < 2^8 x 2^7 (P <= 2^8 under a lazy running max that
+// moves when exceeded by 2^8), and V^T = codes x 2^b with b = min(B, bmax),
+// so the codes times 2^b are exact FP16 values (e4m3 codes, 2^-9 .. 448:
+// bmax = 7; int8 codes, whose conversion also needs -1152 x 2^b in FP16:
+// bmax = 5).  The rest of 2^-B, 2^-k with k = B - b, is nonzero only for
+// scales of 2^14 (int8: 2^11) and above (values beyond 7.3e6): the
+// kernels take P relative to 2^(running max + k), which moves P, O and the
+// row sum into units of 2^-k together, like a move of the running max
+// (exactly: by a power of two), and add k back to the max for the LSE.
+// P' = P x scale x 2^-b then stays below 2^15 in every case.
 struct F16Bias {
   float v;  // 2^b, for the codes
   float p;  // 2^-b, for P'
   float B;  // b + k
-  int k;    // 0 unless the largest scale exceeds 2^14
+  int k;    // 0 below scales of 2^14 (int8: 2^11)
 };
 __device__ __forceinline__ float exp2i(int n) {  // 2^n for -126 <= n <= 127
   return __builtin_bit_cast(float, (uint32_t)(127 + n) << 23);
 }
-__device__ __forceinline__ F16Bias f16_bias(uint32_t e) {
-  const int B = max((int)e - 134, -15);
-  const int b = min(B, 7);
+__device__ __forceinline__ F16Bias f16_bias(uint32_t e, int bmax = 7) {
+  const int B = max((int)e - 133, -15);
+  const int b = min(B, bmax);
   return F16Bias{exp2i(b), exp2i(-b), (float)B, B - b};
+}
+
+// four int8 codes (one dword) times 2^b as four FP16 values, exactly: the
+// biased byte x + 128 placed in the mantissa of 1024 gives 1024 + x + 128,
+// and one fused multiply-add per pair gives (1024 + x + 128 - 1152) x 2^b
+// (sb: 2^b in both halves, ob: -1152 x 2^b in both halves)
+__device__ __forceinline__ uint2 int8x4_to_f16x4(uint32_t v, f16x2 sb, f16x2 ob) {
+  const uint32_t u = v ^ 0x80808080u;
+  const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);  // halves 0x64u0, 0x64u1
+  const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);  // halves 0x64u2, 0x64u3
+  const f16x2 a = __builtin_elementwise_fma(__builtin_bit_cast(f16x2, lo), sb, ob);
+  const f16x2 b = __builtin_elementwise_fma(__builtin_bit_cast(f16x2, hi), sb, ob);
+  return make_uint2(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b));
 }
 
 // the largest value of v over the 64 lanes, in every lane (DPP within each
