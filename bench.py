@@ -489,7 +489,7 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": round(us_per_token / PAGE_A5000_US_PER_TOKEN, 6) if args.width == 1024 else None,
-        "dtype": "fp8_e4m3 cache / bf16 mfma / f32 softmax",
+        "dtype": "fp8_e4m3 cache / bf16 QK mfma, f16 PV mfma / f32 softmax",
         "data": "synthetic (seeded N(0,1) latent and q, uniform causal top-k over a shuffled paged pool)",
         "config": {"workload": f"fp8 sparse-MLA prefill T={T} ctx={case.ctx} H={H} topk={case.topk} "
                                f"page_block=64 (cache write of the batch's {T} rows + prefill)",
