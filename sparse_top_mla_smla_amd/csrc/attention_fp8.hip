@@ -536,21 +536,10 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
       issue_part(Buf<1 - B>{}, Buf<0>{}, src_next);
     }
     if (w == 0 && nn.t >= 0) issue_idx(Buf<B>{}, nn);
-    // PV runs in FP16 under the tile's bias (f16_bias): the largest exponent
-    // of the 64 rows' scales (DSv4: of their seven exponent bytes; DSv4's
-    // BF16 rope values enter PV as FP16 unbiased)
+    // PV runs in FP16 under the tile's bias (f16_bias), taken after B1: the
+    // largest exponent of the 64 rows' scales (DSv4: of their seven exponent
+    // bytes; DSv4's BF16 rope values enter PV as FP16 unbiased)
     F16Bias bias;
-    {
-      uint32_t e;
-      if constexpr (DS) {
-        const uint2 tb = *reinterpret_cast<const uint2*>(raw + v4::CK_TAIL * CS + lane * 16 + 8);
-        e = max_byte<7>(tb.x, tb.y);
-      } else {
-        const uint4 sc4 = *reinterpret_cast<const uint4*>(raw + CK_SCALE * CS + lane * 16);
-        e = max(max((sc4.x >> 23) & 0xFFu, (sc4.y >> 23) & 0xFFu), max((sc4.z >> 23) & 0xFFu, (sc4.w >> 23) & 0xFFu));
-      }
-      bias = f16_bias(wave_max_u32(e), CODES == FMT_INT8 ? 5 : 7);
-    }
     if (pend >= 0) {
       store_result(pend, pend_factor, pend_lse, false);
       pend = -1;
@@ -657,30 +646,65 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
     if (more) issue_part(Buf<1 - B>{}, Buf<1>{}, src_next);
 
     {
+      // all the reads first, then one wait
       const f32x4* src = reinterpret_cast<const f32x4*>(recv) + w * 3 * 128 + lane;
+      f32x4 part[3][2];
 #pragma unroll
       for (int slot = 0; slot < 3; ++slot) {
-        s0 += src[slot * 128];
-        s1 += src[slot * 128 + 64];
+        part[slot][0] = src[slot * 128];
+        part[slot][1] = src[slot * 128 + 64];
       }
       const int32_t* vl = valid + B * TC + 16 * g + 4 * hi;
+      const int4 va = *reinterpret_cast<const int4*>(vl), vb = *reinterpret_cast<const int4*>(vl + 8);
+      // row lane's scales (DSv4: exponent bytes), for the tile's FP16 bias
+      const uint4 sc4 = DS ? make_uint4(0, 0, 0, 0) : *reinterpret_cast<const uint4*>(raw + CK_SCALE * CS + lane * 16);
+      const uint2 tb = DS ? *reinterpret_cast<const uint2*>(raw + v4::CK_TAIL * CS + lane * 16 + 8) : make_uint2(0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      bias = f16_bias(wave_max_u32(DS ? max_byte<7>(tb.x, tb.y)
+                                      : max(max((sc4.x >> 23) & 0xFFu, (sc4.y >> 23) & 0xFFu),
+                                            max((sc4.z >> 23) & 0xFFu, (sc4.w >> 23) & 0xFFu))),
+                      CODES == FMT_INT8 ? 5 : 7);
+#pragma unroll
+      for (int slot = 0; slot < 3; ++slot) {
+        s0 += part[slot][0];
+        s1 += part[slot][1];
+      }
+      const int v0[4] = {va.x, va.y, va.z, va.w}, v1[4] = {vb.x, vb.y, vb.z, vb.w};
       float mx = -INFINITY;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        s0[r] = vl[r] ? s0[r] * p.scale_log2 : -INFINITY;
-        s1[r] = vl[8 + r] ? s1[r] * p.scale_log2 : -INFINITY;
+        s0[r] = v0[r] ? s0[r] * p.scale_log2 : -INFINITY;
+        s1[r] = v1[r] ? s1[r] * p.scale_log2 : -INFINITY;
         mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      {
+        // the other half of the wave: v_permlane32_swap gives the low half's
+        // values in one result and the high half's in the other, in all lanes
+        const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, mx), __builtin_bit_cast(uint32_t, mx), false, false);
+        mx = fmaxf(__builtin_bit_cast(float, sw[0]), __builtin_bit_cast(float, sw[1]));
+      }
       if (hi == 0) maxb[g * 64 + 32 * hh + l32] = mx;
     }
     lds_barrier();  // B2: block maxima visible; every partial has been read
     if (more) issue_part(Buf<1 - B>{}, Buf<2>{}, src_next);
 
     float alpha;
+    // 656-byte rows: the row scales for P' are read now, behind the block
+    // maxima, so that their latency passes under the softmax
+    f32x4 sc0[4], sc1[4];
     {
       const int hl = 32 * hh + l32;
-      const float mx = fmaxf(fmaxf(maxb[hl], maxb[64 + hl]), fmaxf(maxb[128 + hl], maxb[192 + hl]));
+      const float m0 = maxb[hl], m1 = maxb[64 + hl], m2 = maxb[128 + hl], m3 = maxb[192 + hl];
+      if constexpr (!DS) {
+        const uint8_t* scp = raw + CK_SCALE * CS + (16 * g + 4 * hi) * 16;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          sc0[r] = *reinterpret_cast<const f32x4*>(scp + r * 16);
+          sc1[r] = *reinterpret_cast<const f32x4*>(scp + (8 + r) * 16);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      const float mx = fmaxf(fmaxf(m0, m1), fmaxf(m2, m3));
       const bool need = mx > m_run + TAU;
       alpha = need ? ((m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run - mx)) : 1.0f;
       m_run = need ? mx : m_run;
@@ -729,13 +753,6 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
       } else {
         // P'_gg = P x (row scale of column group gg) (x 2^-b in FP16), for the PV of
         // every group; the four scales of a row are one 16-byte piece
-        const uint8_t* scp = raw + CK_SCALE * CS + (16 * g + 4 * hi) * 16;
-        f32x4 sc0[4], sc1[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          sc0[r] = *reinterpret_cast<const f32x4*>(scp + r * 16);
-          sc1[r] = *reinterpret_cast<const f32x4*>(scp + (8 + r) * 16);
-        }
         u32x2 w0[4], w1[4];
 #pragma unroll
         for (int gg = 0; gg < 4; ++gg) {

@@ -10,6 +10,10 @@
 //  * ds_read_b64_tr_b8: lane 2r+b supplies row r, byte columns 8b..8b+7 of
 //    an 8x16 byte block and receives byte column (lane%16) of rows 0..7.
 //  * v_cvt_pk_f32_fp8 decodes OCP E4M3 exactly.
+//  * v_permlane32_swap_b32 (vdst, vsrc): vdst's lanes 32..63 and vsrc's
+//    lanes 0..31 trade places.
+//  * v_cvt_scalef32_pk_f16_fp8, v_cvt_pk_f16_f32 and the FP16 MFMAs keep
+//    FP16 subnormals.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
