@@ -184,6 +184,7 @@ constexpr int CK_ROPE = 28;
 constexpr int CK_TAIL = 36;
 constexpr int TAIL_FROM = 568;               // row byte where piece 36 starts
 constexpr int TILE = CHUNKS * CS;            // 37,888 bytes per tile
+static_assert(CK_TAIL - CK_ROPE == NT / 64, "one rope piece per wave for the FP16 conversion");
 }  // namespace v4
 template <int CODES>
 constexpr int chunks_of() { return CODES == FMT_FP8_DSV4 ? v4::CHUNKS : CHUNKS; }
@@ -659,11 +660,18 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
       // row lane's scales (DSv4: exponent bytes), for the tile's FP16 bias
       const uint4 sc4 = DS ? make_uint4(0, 0, 0, 0) : *reinterpret_cast<const uint4*>(raw + CK_SCALE * CS + lane * 16);
       const uint2 tb = DS ? *reinterpret_cast<const uint2*>(raw + v4::CK_TAIL * CS + lane * 16 + 8) : make_uint2(0, 0);
+      // DSv4: wave w's piece of the BF16 rope values (piece 28 + w), which QK
+      // has read as K by now, goes back as FP16 for PV
+      uint8_t* rope = (B ? raw1 : raw0) + (v4::CK_ROPE + w) * CS + lane * 16;
+      const uint4 r16 = DS ? *reinterpret_cast<const uint4*>(rope) : make_uint4(0, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
       bias = f16_bias(wave_max_u32(DS ? max_byte<7>(tb.x, tb.y)
                                       : max(max((sc4.x >> 23) & 0xFFu, (sc4.y >> 23) & 0xFFu),
                                             max((sc4.z >> 23) & 0xFFu, (sc4.w >> 23) & 0xFFu))),
                       CODES == FMT_INT8 ? 5 : 7);
+      if constexpr (DS)
+        *reinterpret_cast<uint4*>(rope) = make_uint4(bf16x2_to_f16x2(r16.x), bf16x2_to_f16x2(r16.y),
+                                                     bf16x2_to_f16x2(r16.z), bf16x2_to_f16x2(r16.w));
 #pragma unroll
       for (int slot = 0; slot < 3; ++slot) {
         s0 += part[slot][0];
@@ -769,25 +777,34 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
         b64_store<3 * GS + 16>(pw, w1[3]);
       }
     }
+    // ---- 4. O^T += V^T P'^T over columns [128g, 128g + 128), heads 32hh.. ----
+    // ds_read_b64_tr_b8: in each 16-lane group, lane 2r + b addresses row r
+    // of an 8-row block, bytes 8b..8b+7 of a 16-column piece.  656-byte
+    // rows: all sixteen V^T operands of the tile are read before B3 (they
+    // need only the tile), and B3's wait completes them.
+    const int g16 = (lane >> 4) & 1;
+    const int jr = (lane & 15) >> 1;
+    const int jb = lane & 1;
+    i32x2 v8[4][4];  // [ks][dt]: candidates 16ks.., columns 128g + 32dt..
+    if constexpr (!DS) {
+      const uint32_t va = lds_addr(raw + (8 * g + g16) * CS + (8 * hi + jr) * 16 + 8 * jb);
+#define SMLA_TR8(ks, dt) v8[ks][dt] = tr8_issue<2 * (dt) * CS + 256 * (ks)>(va)
+      SMLA_TR8(0, 0); SMLA_TR8(0, 1); SMLA_TR8(0, 2); SMLA_TR8(0, 3);
+      SMLA_TR8(1, 0); SMLA_TR8(1, 1); SMLA_TR8(1, 2); SMLA_TR8(1, 3);
+      SMLA_TR8(2, 0); SMLA_TR8(2, 1); SMLA_TR8(2, 2); SMLA_TR8(2, 3);
+      SMLA_TR8(3, 0); SMLA_TR8(3, 1); SMLA_TR8(3, 2); SMLA_TR8(3, 3);
+#undef SMLA_TR8
+    }
     if (__any(alpha != 1.0f)) {
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) O[dt] *= alpha;
     }
     lds_barrier();  // B3: P visible
-
-    // ---- 4. O^T += V^T P'^T over columns [128g, 128g + 128), heads 32hh.. ----
-    // ds_read_b64_tr_b8: in each 16-lane group, lane 2r + b addresses row r
-    // of an 8-row block, bytes 8b..8b+7 of a 16-column piece.  All sixteen
-    // V^T operands of the tile are read first.
-    const int g16 = (lane >> 4) & 1;
-    const int jr = (lane & 15) >> 1;
-    const int jb = lane & 1;
     if constexpr (DS) {
       // DSv4: columns 128g + 32dt.. take P' of scale tile 2g + dt/2 (slot
       // A for dt 0, 1, slot B for dt 2, 3); group 3's columns 448..511 are
-      // the BF16 rope values (slot 7, P itself), read with
-      // ds_read_b64_tr_b16 from pieces 28 + 4(dt - 2) + 2g16 + (b >> 1) and
-      // converted to FP16
+      // the rope values (slot 7, P itself; FP16 since the exchange phase),
+      // read with ds_read_b64_tr_b16 from pieces 28 + 4(dt - 2) + 2g16 + (b >> 1)
       const uint32_t va = lds_addr(raw + (8 * g + g16) * CS + (8 * hi + jr) * 16 + 8 * jb);
       // columns 128g + 0..63 (codes of scale tile 2g, slot A) first; the
       // reads of the other 64 columns are issued under their MFMAs.  The
@@ -839,8 +856,8 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
             }
         }
       } else {
-        // group 3: the BF16 rope columns 448 + 32(dt - 2) + 16g16 + lc, two
-        // candidate blocks at a time
+        // group 3: the rope columns 448 + 32(dt - 2) + 16g16 + lc (FP16 by
+        // now), two candidate blocks at a time
         const int lc = lane & 15;
         const uint32_t vb = lds_addr(raw + (v4::CK_ROPE + 2 * g16 + ((lc & 3) >> 1)) * CS + (8 * hi + (lc >> 2)) * 16 +
                                      8 * (lc & 1));
@@ -864,21 +881,13 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
 #pragma unroll
             for (int d = 0; d < 2; ++d) {
               const f16x8 v = __builtin_bit_cast(
-                  f16x8, make_uint4(bf16x2_to_f16x2((uint32_t)vr[k][d][0][0]), bf16x2_to_f16x2((uint32_t)vr[k][d][0][1]),
-                                    bf16x2_to_f16x2((uint32_t)vr[k][d][1][0]), bf16x2_to_f16x2((uint32_t)vr[k][d][1][1])));
+                  f16x8, make_uint4((uint32_t)vr[k][d][0][0], (uint32_t)vr[k][d][0][1], (uint32_t)vr[k][d][1][0],
+                                    (uint32_t)vr[k][d][1][1]));
               O[2 + d] = mfma_32x32x16_f16(v, __builtin_bit_cast(f16x8, pr[2 * kh + k]), O[2 + d]);
             }
         }
       }
     } else {
-      const uint32_t va = lds_addr(raw + (8 * g + g16) * CS + (8 * hi + jr) * 16 + 8 * jb);
-      i32x2 v8[4][4];  // [ks][dt]: candidates 16ks.., columns 128g + 32dt..
-#define SMLA_TR8(ks, dt) v8[ks][dt] = tr8_issue<2 * (dt) * CS + 256 * (ks)>(va)
-      SMLA_TR8(0, 0); SMLA_TR8(0, 1); SMLA_TR8(0, 2); SMLA_TR8(0, 3);
-      SMLA_TR8(1, 0); SMLA_TR8(1, 1); SMLA_TR8(1, 2); SMLA_TR8(1, 3);
-      SMLA_TR8(2, 0); SMLA_TR8(2, 1); SMLA_TR8(2, 2); SMLA_TR8(2, 3);
-      SMLA_TR8(3, 0); SMLA_TR8(3, 1); SMLA_TR8(3, 2); SMLA_TR8(3, 3);
-#undef SMLA_TR8
       // P'_g for heads 32hh + l32, candidates 16ks + 8hi + i: the B operands
       const uint32_t pa = lds_addr(pq + (g * 64 + 32 * hh + l32) * PS + 8 * hi);
       u32x4 pb[4];
