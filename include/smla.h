@@ -25,6 +25,13 @@
  *   candidate set gives out = 0 and lse = -inf.  out is BF16 (round to
  *   nearest even), lse FP32.
  *
+ * Arithmetic: the scores accumulate in FP32 from the BF16 q and the exactly
+ * dequantized K; the probabilities enter the value product as P x scale
+ * rounded once to FP16 (11 significant bits) for quantized rows, under a
+ * per-tile power-of-two bias that keeps FP16's range for any scale, and as
+ * a BF16 pair (16 bits) for BF16 rows.  DSv4 rope values enter the value
+ * product as FP16 and must lie within +-65504.
+ *
  * Conventions for every entry point:
  *  - All data pointers are DEVICE pointers; `stream` is a hipStream_t (NULL
  *    = the default stream).  Work is enqueued asynchronously on `stream`.
