@@ -202,9 +202,22 @@ struct Buf {
   static constexpr int value = V;
 };
 
-// the row that list positions without a candidate gather (zero-initialized
-// device memory, one copy per device)
-__device__ __attribute__((aligned(16))) uint8_t zero_row[RB];
+// the rows that list positions without a candidate gather (one copy per
+// device): zero codes and rope values; the 656-byte rows' four scales are
+// 2^-126, a positive power of two (so the row's scores are 0, not NaN) and
+// no larger than any real row's scale (so it never raises a tile's FP16
+// bias).  The DSv4 rows' scale bytes are 0.
+struct ZeroRow {
+  uint32_t w[RB / 4];
+};
+constexpr ZeroRow make_zero_row(bool scales) {
+  ZeroRow r{};
+  if (scales)
+    for (int i = 0; i < 4; ++i) r.w[D_NOPE / 4 + i] = 0x00800000u;
+  return r;
+}
+__device__ __attribute__((aligned(16))) ZeroRow zero_row_656 = make_zero_row(true);
+__device__ __attribute__((aligned(16))) ZeroRow zero_row_584 = make_zero_row(false);
 
 // an exponent byte as the FP32 number 2^(b-127) (0: 2^-127, 255: NaN)
 __device__ __forceinline__ float e8m0_value(uint32_t b) {
@@ -245,7 +258,8 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) float maxb[4 * 64];   // [4 groups][64 heads]
   // DSv4: the tile's scales, [scale tile][row] (2^(b-127))
   __shared__ __attribute__((aligned(16))) float dsc[DS ? 7 * TC : 4];
-  __shared__ __attribute__((aligned(16))) int32_t valid[2 * TC];  // [buffer][row]: row was loaded
+  // [buffer][row]: 0 for a row that holds a candidate, -inf for a position without one
+  __shared__ __attribute__((aligned(16))) float rowbias[2 * TC];
   __shared__ __attribute__((aligned(16))) int32_t idx0[TC];       // index list of even tiles
   __shared__ __attribute__((aligned(16))) int32_t idx1[TC];       // index list of odd tiles
   uint16_t* pq = reinterpret_cast<uint16_t*>(recv);              // P' (FP16), after the reduce
@@ -353,7 +367,7 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
     constexpr int B = decltype(buf)::value;
     constexpr int P = decltype(part)::value;
     uint8_t* raw = B ? raw1 : raw0;
-    const uint8_t* from = src ? src : zero_row;
+    const uint8_t* from = src ? src : reinterpret_cast<const uint8_t*>(DS ? zero_row_584.w : zero_row_656.w);
 #pragma unroll
     for (int r = 2 * P; r < 2 * P + 2; ++r) {
       const int ck = w + 8 * r;
@@ -362,7 +376,7 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
       if ((8 * r + 7 < NCK || ck < NCK) && (!NOPE || ck < CK_ROPE))
         global_to_lds_16(from + (DS && ck == v4::CK_TAIL ? v4::TAIL_FROM : 16 * ck), raw + ck * CS);
     }
-    if (P == 0 && w == 0) valid[B * TC + lane] = src != nullptr;
+    if (P == 0 && w == 0) rowbias[B * TC + lane] = src ? 0.0f : -INFINITY;
   };
   static_assert(2 * GPARTS * 8 >= NCK && 2 * (GPARTS - 1) * 8 < NCK, "three parts of two rounds");
 
@@ -655,8 +669,8 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
         part[slot][0] = src[slot * 128];
         part[slot][1] = src[slot * 128 + 64];
       }
-      const int32_t* vl = valid + B * TC + 16 * g + 4 * hi;
-      const int4 va = *reinterpret_cast<const int4*>(vl), vb = *reinterpret_cast<const int4*>(vl + 8);
+      const float* vl = rowbias + B * TC + 16 * g + 4 * hi;
+      const f32x4 va = *reinterpret_cast<const f32x4*>(vl), vb = *reinterpret_cast<const f32x4*>(vl + 8);
       // row lane's scales (DSv4: exponent bytes), for the tile's FP16 bias
       const uint4 sc4 = DS ? make_uint4(0, 0, 0, 0) : *reinterpret_cast<const uint4*>(raw + CK_SCALE * CS + lane * 16);
       const uint2 tb = DS ? *reinterpret_cast<const uint2*>(raw + v4::CK_TAIL * CS + lane * 16 + 8) : make_uint2(0, 0);
@@ -677,12 +691,13 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
         s0 += part[slot][0];
         s1 += part[slot][1];
       }
-      const int v0[4] = {va.x, va.y, va.z, va.w}, v1[4] = {vb.x, vb.y, vb.z, vb.w};
+      // positions without a candidate hold the zero row, whose score is 0:
+      // adding -inf masks them
       float mx = -INFINITY;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        s0[r] = v0[r] ? s0[r] * p.scale_log2 : -INFINITY;
-        s1[r] = v1[r] ? s1[r] * p.scale_log2 : -INFINITY;
+        s0[r] = fmaf(s0[r], p.scale_log2, va[r]);
+        s1[r] = fmaf(s1[r], p.scale_log2, vb[r]);
         mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
       }
       {
@@ -722,12 +737,14 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
       // P relative to 2^(m_run + k); P' of the 656-byte rows takes P x 2^-b
       // straight from the exponential
       constexpr bool FOLD = !DS;
-      const float mb = m_run + (FOLD ? bias.B : (float)o_k);
+      // (a head whose scores are all -inf so far has m_run = -inf; the
+      // finite floor keeps -inf - mb at -inf, whose exponential is 0)
+      const float mb = fmaxf(m_run + (FOLD ? bias.B : (float)o_k), -__FLT_MAX__);
       float psum = 0.0f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        s0[r] = (s0[r] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(s0[r] - mb);
-        s1[r] = (s1[r] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(s1[r] - mb);
+        s0[r] = __builtin_amdgcn_exp2f(s0[r] - mb);
+        s1[r] = __builtin_amdgcn_exp2f(s1[r] - mb);
         psum += s0[r] + s1[r];
       }
       l_part = l_part * alpha + (FOLD ? psum * bias.v : psum);
