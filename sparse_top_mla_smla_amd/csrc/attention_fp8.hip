@@ -703,8 +703,12 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
       {
         // the other half of the wave: v_permlane32_swap gives the low half's
         // values in one result and the high half's in the other, in all lanes
+        // (both results are copied out before they are reinterpreted: a bit
+        // cast applied to the second element of the builtin's result in place
+        // is compiled as a cast of the first)
         const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, mx), __builtin_bit_cast(uint32_t, mx), false, false);
-        mx = fmaxf(__builtin_bit_cast(float, sw[0]), __builtin_bit_cast(float, sw[1]));
+        const uint32_t lo = sw[0], hi2 = sw[1];
+        mx = fmaxf(__builtin_bit_cast(float, lo), __builtin_bit_cast(float, hi2));
       }
       if (hi == 0) maxb[g * 64 + 32 * hh + l32] = mx;
     }

@@ -106,3 +106,44 @@ def test_scales_above_2_14(fmt, H):
     assert_lse_close(l.cpu().numpy(), lf32)
     assert_out_close((po.double().cpu() * down).numpy(), rpo, what="part_out", bf16=False)
     assert_lse_close(pl.cpu().numpy(), rpl, what="part_lse")
+
+
+@pytest.mark.parametrize("fmt,H", [(W.FMT_FP8, 64), (W.FMT_FP8_NOPE, 64), (W.FMT_FP8_ANY, 64), (W.FMT_INT8, 64),
+                                   (W.FMT_FP8_DSV4, 64), (W.FMT_FP8_DSV4, 16), (W.FMT_FP8, 8)])
+def test_dominant_candidate_at_every_tile_position(fmt, H):
+    """One list entry per token scores about 40 nats above all others: the
+    q rows share a direction u (u + 0.5 x the unit normal q) and that entry's
+    cache row is a multiple of u.  Token t's dominant entry sits at list
+    position t mod 128, so across the tokens it takes every position of both
+    64-candidate tiles (each token has a sequence of its own, so no other
+    token's dominant row enters its list).  The softmax's running maximum must
+    come from all candidates of a tile: a maximum that missed the dominant
+    entry would leave its probability at about 2^58 relative to the others,
+    beyond FP16 and every rescaling, and the output would not be finite.
+    Prefill, and decode over two splits with the combine, against the
+    oracle."""
+    T = 128
+    c = W.make_case(f"dominant_{fmt}_{H}", config_id=530 + 8 * fmt + H // 8, seed=14, fmt=fmt, T=T, H=H, n_seqs=T,
+                    ctx=256, topk=128, causal=False)
+    dims = c.kv.shape[1]
+    rng = np.random.default_rng(1400 + fmt)
+    u = rng.standard_normal(dims) * 2.5
+    q = W.bf16_bits_to_f32(c.q_buf).astype(np.float64)
+    c.q_buf = W.f32_to_bf16_bits((u[None, None, :] + 0.5 * q).astype(np.float32))
+    alpha = 40.0 / (float(c.sm_scale) * float(u @ u))
+    kv = W.bf16_bits_to_f32(c.kv)
+    row_of_slot = np.empty(c.slots.shape[0], dtype=np.int64)
+    row_of_slot[c.slots] = np.arange(c.slots.shape[0])
+    for t in range(T):
+        kv[row_of_slot[c.idx_buf[t, t % 128]]] = (alpha * u).astype(np.float32)
+    c.kv = W.f32_to_bf16_bits(kv)
+    d = Dev(c)
+    o, l = smla.prefill(d.q, d.pool, d.indices, sm_scale=float(c.sm_scale))
+    po, pl = smla.decode(d.q, d.pool, d.indices, 2, sm_scale=float(c.sm_scale))
+    oc, lc = smla.combine(po, pl)
+    torch.cuda.synchronize()
+    ob, lf32, of, _ = oracle.prefill(c.q, oracle_pool(c), c.indices, sm_scale=c.sm_scale)
+    assert_out_close(bf16_dev_to_f64(o), of, mean_ref=f64_of_bits(ob))
+    assert_lse_close(l.cpu().numpy(), lf32)
+    assert_out_close(bf16_dev_to_f64(oc), of, what="combined out", mean_ref=f64_of_bits(ob))
+    assert_lse_close(lc.cpu().numpy(), lf32, what="combined lse")
