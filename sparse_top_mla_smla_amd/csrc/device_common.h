@@ -11,7 +11,10 @@
 //    an 8x16 byte block and receives byte column (lane%16) of rows 0..7.
 //  * v_cvt_pk_f32_fp8 decodes OCP E4M3 exactly.
 //  * v_permlane32_swap_b32 (vdst, vsrc): vdst's lanes 32..63 and vsrc's
-//    lanes 0..31 trade places.
+//    lanes 0..31 trade places.  The builtin returns both registers; with
+//    this compiler, __builtin_bit_cast applied in place to the second
+//    element of that result yields the first, so copy both elements to
+//    scalars before any cast.
 //  * v_cvt_scalef32_pk_f16_fp8, v_cvt_pk_f16_f32 and the FP16 MFMAs keep
 //    FP16 subnormals.
 #pragma once
