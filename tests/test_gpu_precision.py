@@ -109,7 +109,8 @@ def test_scales_above_2_14(fmt, H):
 
 
 @pytest.mark.parametrize("fmt,H", [(W.FMT_FP8, 64), (W.FMT_FP8_NOPE, 64), (W.FMT_FP8_ANY, 64), (W.FMT_INT8, 64),
-                                   (W.FMT_FP8_DSV4, 64), (W.FMT_FP8_DSV4, 16), (W.FMT_FP8, 8)])
+                                   (W.FMT_FP8_DSV4, 64), (W.FMT_FP8_DSV4, 16), (W.FMT_FP8_DOTS3, 16),
+                                   (W.FMT_FP8_DOTS3, 64), (W.FMT_FP8, 8), (W.FMT_BF16, 8), (W.FMT_INT8, 8)])
 def test_dominant_candidate_at_every_tile_position(fmt, H):
     """One list entry per token scores about 40 nats above all others: the
     q rows share a direction u (u + 0.5 x the unit normal q) and that entry's
