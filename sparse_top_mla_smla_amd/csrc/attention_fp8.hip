@@ -551,7 +551,7 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
       issue_part(Buf<1 - B>{}, Buf<0>{}, src_next);
     }
     if (w == 0 && nn.t >= 0) issue_idx(Buf<B>{}, nn);
-    // PV runs in FP16 under the tile's bias (f16_bias), taken after B1: the
+    // PV runs in FP16 under the tile's bias (f16_bias), taken after QK: the
     // largest exponent of the 64 rows' scales (DSv4: of their seven exponent
     // bytes; DSv4's BF16 rope values enter PV as FP16 unbiased)
     F16Bias bias;
@@ -634,6 +634,16 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
         acc[c2] = mfma_32x32x16(__builtin_bit_cast(bf16x8, r16), qr, acc[c2]);
       }
     }
+    // the tile's FP16 bias from row lane's scales (DSv4: exponent bytes),
+    // formed while the QK MFMAs finish
+    {
+      const uint4 sc4 = DS ? make_uint4(0, 0, 0, 0) : *reinterpret_cast<const uint4*>(raw + CK_SCALE * CS + lane * 16);
+      const uint2 tb = DS ? *reinterpret_cast<const uint2*>(raw + v4::CK_TAIL * CS + lane * 16 + 8) : make_uint2(0, 0);
+      bias = f16_bias(wave_max_u32(DS ? max_byte<7>(tb.x, tb.y)
+                                      : max(max((sc4.x >> 23) & 0xFFu, (sc4.y >> 23) & 0xFFu),
+                                            max((sc4.z >> 23) & 0xFFu, (sc4.w >> 23) & 0xFFu))),
+                      CODES == FMT_INT8 ? 5 : 7);
+    }
     // prefill: Q of the next token, not read again before that token's QK
     if (!DECODE && more && nxt.t != cur.t) load_q(nxt.t);
     // ---- 2. reduce-scatter: accumulator elements [8hf, 8hf+8) of tile c2
@@ -671,18 +681,11 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
       }
       const float* vl = rowbias + B * TC + 16 * g + 4 * hi;
       const f32x4 va = *reinterpret_cast<const f32x4*>(vl), vb = *reinterpret_cast<const f32x4*>(vl + 8);
-      // row lane's scales (DSv4: exponent bytes), for the tile's FP16 bias
-      const uint4 sc4 = DS ? make_uint4(0, 0, 0, 0) : *reinterpret_cast<const uint4*>(raw + CK_SCALE * CS + lane * 16);
-      const uint2 tb = DS ? *reinterpret_cast<const uint2*>(raw + v4::CK_TAIL * CS + lane * 16 + 8) : make_uint2(0, 0);
       // DSv4: wave w's piece of the BF16 rope values (piece 28 + w), which QK
       // has read as K by now, goes back as FP16 for PV
       uint8_t* rope = (B ? raw1 : raw0) + (v4::CK_ROPE + w) * CS + lane * 16;
       const uint4 r16 = DS ? *reinterpret_cast<const uint4*>(rope) : make_uint4(0, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
-      bias = f16_bias(wave_max_u32(DS ? max_byte<7>(tb.x, tb.y)
-                                      : max(max((sc4.x >> 23) & 0xFFu, (sc4.y >> 23) & 0xFFu),
-                                            max((sc4.z >> 23) & 0xFFu, (sc4.w >> 23) & 0xFFu))),
-                      CODES == FMT_INT8 ? 5 : 7);
       if constexpr (DS)
         *reinterpret_cast<uint4*>(rope) = make_uint4(bf16x2_to_f16x2(r16.x), bf16x2_to_f16x2(r16.y),
                                                      bf16x2_to_f16x2(r16.z), bf16x2_to_f16x2(r16.w));
