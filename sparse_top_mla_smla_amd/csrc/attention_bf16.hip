@@ -326,10 +326,12 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(AttnParams p) {
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) O[dt] *= alpha;
     }
+    // (the finite floor keeps -inf scores at probability 0 while every score of a head is -inf)
+    const float mb = fmaxf(m_run + (float)o_k, -__FLT_MAX__);
     float pr[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      pr[i] = (s[i] == -INFINITY) ? 0.0f : exp2f(s[i] - (m_run + (float)o_k));
+      pr[i] = __builtin_amdgcn_exp2f(s[i] - mb);
       l_part += pr[i];
     }
     if constexpr (FMT == FMT_BF16) {

@@ -305,10 +305,12 @@ __global__ __launch_bounds__(NT, R::OCC) void attn_mx_kernel(AttnParams p) {
 #pragma unroll
       for (int dt = 0; dt < G::NDT; ++dt) O[dt] *= alpha;
     }
+    // (the finite floor keeps -inf scores at probability 0 while every score of a head is -inf)
+    const float mb = fmaxf(m_run + (float)o_k, -__FLT_MAX__);
     float pr[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      pr[i] = (s[i] == -INFINITY) ? 0.0f : exp2f(s[i] - (m_run + (float)o_k));
+      pr[i] = __builtin_amdgcn_exp2f(s[i] - mb);
       l_part += pr[i];
     }
     // P'_g[h][c] = P[c][h] * scale(c, g) * 2^-b in FP16, candidates
@@ -637,10 +639,12 @@ __global__ __launch_bounds__(NT32, 1) void attn_mx32_kernel(AttnParams p) {
 #pragma unroll
       for (int dt = 0; dt < G::NDT; ++dt) O[dt] *= alpha;
     }
+    // (the finite floor keeps -inf scores at probability 0 while every score of a head is -inf)
+    const float mb = fmaxf(m_run + (float)o_k, -__FLT_MAX__);
     float pr[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      pr[i] = (s[i] == -INFINITY) ? 0.0f : exp2f(s[i] - (m_run + (float)o_k));
+      pr[i] = __builtin_amdgcn_exp2f(s[i] - mb);
       l_part += pr[i];
     }
     // P'_g[h][c] = P[c][h] * scale(c, g) * 2^-b in FP16, candidates 16wl + 4lg + (0..3)
