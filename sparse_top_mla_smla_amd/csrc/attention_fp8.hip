@@ -804,20 +804,20 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
     // ---- 4. O^T += V^T P'^T over columns [128g, 128g + 128), heads 32hh.. ----
     // ds_read_b64_tr_b8: in each 16-lane group, lane 2r + b addresses row r
     // of an 8-row block, bytes 8b..8b+7 of a 16-column piece.  656-byte
-    // rows: all sixteen V^T operands of the tile are read before B3 (they
-    // need only the tile), and B3's wait completes them.
+    // rows: the V^T operands of candidate blocks 0..2 are read before B3
+    // (they need only the tile), and B3's wait completes them; block 3's are
+    // read in PV once the first three blocks' MFMAs are issued, so that less
+    // LDS traffic falls into the interval every wave waits on at B3.
     const int g16 = (lane >> 4) & 1;
     const int jr = (lane & 15) >> 1;
     const int jb = lane & 1;
     i32x2 v8[4][4];  // [ks][dt]: candidates 16ks.., columns 128g + 32dt..
+    const uint32_t vta = lds_addr(raw + (8 * g + g16) * CS + (8 * hi + jr) * 16 + 8 * jb);
+#define SMLA_VT8(ks, dt) v8[ks][dt] = tr8_issue<2 * (dt) * CS + 256 * (ks)>(vta)
     if constexpr (!DS) {
-      const uint32_t va = lds_addr(raw + (8 * g + g16) * CS + (8 * hi + jr) * 16 + 8 * jb);
-#define SMLA_TR8(ks, dt) v8[ks][dt] = tr8_issue<2 * (dt) * CS + 256 * (ks)>(va)
-      SMLA_TR8(0, 0); SMLA_TR8(0, 1); SMLA_TR8(0, 2); SMLA_TR8(0, 3);
-      SMLA_TR8(1, 0); SMLA_TR8(1, 1); SMLA_TR8(1, 2); SMLA_TR8(1, 3);
-      SMLA_TR8(2, 0); SMLA_TR8(2, 1); SMLA_TR8(2, 2); SMLA_TR8(2, 3);
-      SMLA_TR8(3, 0); SMLA_TR8(3, 1); SMLA_TR8(3, 2); SMLA_TR8(3, 3);
-#undef SMLA_TR8
+      SMLA_VT8(0, 0); SMLA_VT8(0, 1); SMLA_VT8(0, 2); SMLA_VT8(0, 3);
+      SMLA_VT8(1, 0); SMLA_VT8(1, 1); SMLA_VT8(1, 2); SMLA_VT8(1, 3);
+      SMLA_VT8(2, 0); SMLA_VT8(2, 1); SMLA_VT8(2, 2); SMLA_VT8(2, 3);
     }
     if (__any(alpha != 1.0f)) {
 #pragma unroll
@@ -919,19 +919,23 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
       pb[1] = b128_issue<32>(pa);
       pb[2] = b128_issue<64>(pa);
       pb[3] = b128_issue<96>(pa);
-      // one wait for all the reads; the empty statements after it (volatile
-      // statements keep their order) carry the dependency to the rest
+      // one wait for all the reads so far
       asm volatile("s_waitcnt lgkmcnt(0)"
                    : "+v"(v8[0][0]), "+v"(v8[0][1]), "+v"(v8[0][2]), "+v"(v8[0][3]), "+v"(v8[1][0]), "+v"(v8[1][1]),
-                     "+v"(v8[1][2]), "+v"(v8[1][3]), "+v"(pb[0]), "+v"(pb[1]), "+v"(pb[2]), "+v"(pb[3]));
-      asm volatile(""
-                   : "+v"(v8[2][0]), "+v"(v8[2][1]), "+v"(v8[2][2]), "+v"(v8[2][3]), "+v"(v8[3][0]), "+v"(v8[3][1]),
-                     "+v"(v8[3][2]), "+v"(v8[3][3]));
+                     "+v"(v8[1][2]), "+v"(v8[1][3]), "+v"(v8[2][0]), "+v"(v8[2][1]), "+v"(v8[2][2]), "+v"(v8[2][3]),
+                     "+v"(pb[0]), "+v"(pb[1]), "+v"(pb[2]), "+v"(pb[3]));
       // int8 codes: 2^b and -1152 x 2^b for int8x4_to_f16x4
       const f16x2 sb = {(_Float16)bias.v, (_Float16)bias.v};
       const f16x2 ob = {(_Float16)(-1152.0f * bias.v), (_Float16)(-1152.0f * bias.v)};
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
+      for (int ks = 0; ks < 4; ++ks) {
+        if (ks == 3) {
+          // block 3's V^T, read while the MFMAs of blocks 0..2 run (the
+          // compiler barrier keeps those MFMAs ahead of the reads and wait)
+          __builtin_amdgcn_sched_barrier(0);
+          SMLA_VT8(3, 0); SMLA_VT8(3, 1); SMLA_VT8(3, 2); SMLA_VT8(3, 3);
+          asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(v8[3][0]), "+v"(v8[3][1]), "+v"(v8[3][2]), "+v"(v8[3][3]));
+        }
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
           f16x8 v;
@@ -944,7 +948,9 @@ __global__ __launch_bounds__(f8::NT, 1) void attn_fp8_kernel(AttnParams p) {
           }
           O[dt] = mfma_32x32x16_f16(v, __builtin_bit_cast(f16x8, pb[ks]), O[dt]);
         }
+      }
     }
+#undef SMLA_VT8
   };
   // ---- end of a split (decode) or of a token (prefill): per-head sum over
   // the four groups, normalization; the result is stored now, or by the
