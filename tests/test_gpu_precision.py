@@ -148,3 +148,41 @@ def test_dominant_candidate_at_every_tile_position(fmt, H):
     assert_lse_close(l.cpu().numpy(), lf32)
     assert_out_close(bf16_dev_to_f64(oc), of, what="combined out", mean_ref=f64_of_bits(ob))
     assert_lse_close(lc.cpu().numpy(), lf32, what="combined lse")
+
+
+@pytest.mark.parametrize("fmt,H", [(W.FMT_FP8, 64), (W.FMT_FP8_ANY, 64), (W.FMT_FP8_DSV4, 64), (W.FMT_FP8_DSV4, 16),
+                                   (W.FMT_FP8_DOTS3, 64), (W.FMT_FP8, 8), (W.FMT_BF16, 8)])
+def test_maximum_rising_in_every_tile(fmt, H):
+    """Every 64-entry block of each token's list scores about 12 nats above
+    the block before it (the cache row of list entry j is (1 + j // 64) x a
+    multiple of the q rows' common direction u, plus the unit normal row),
+    so the running maximum moves past its lazy threshold in every tile and
+    O and l are rescaled each time; the per-entry normal parts keep the
+    probabilities within a block uneven.  Prefill, and decode over three
+    splits with the combine, against the oracle."""
+    T = 64
+    c = W.make_case(f"rising_{fmt}_{H}", config_id=620 + 8 * fmt + H // 8, seed=15, fmt=fmt, T=T, H=H, n_seqs=T,
+                    ctx=256, topk=256, causal=False)
+    dims = c.kv.shape[1]
+    rng = np.random.default_rng(1500 + fmt)
+    u = rng.standard_normal(dims) * 2.5
+    q = W.bf16_bits_to_f32(c.q_buf).astype(np.float64)
+    c.q_buf = W.f32_to_bf16_bits((u[None, None, :] + 0.5 * q).astype(np.float32))
+    step = 12.0 / (float(c.sm_scale) * float(u @ u))
+    kv = W.bf16_bits_to_f32(c.kv).astype(np.float64)
+    row_of_slot = np.empty(c.slots.shape[0], dtype=np.int64)
+    row_of_slot[c.slots] = np.arange(c.slots.shape[0])
+    for t in range(T):
+        rows = row_of_slot[c.idx_buf[t, :256]]
+        kv[rows] += ((1 + np.arange(256) // 64) * step)[:, None] * u[None, :]
+    c.kv = W.f32_to_bf16_bits(kv.astype(np.float32))
+    d = Dev(c)
+    o, l = smla.prefill(d.q, d.pool, d.indices, sm_scale=float(c.sm_scale))
+    po, pl = smla.decode(d.q, d.pool, d.indices, 3, sm_scale=float(c.sm_scale))
+    oc, lc = smla.combine(po, pl)
+    torch.cuda.synchronize()
+    ob, lf32, of, _ = oracle.prefill(c.q, oracle_pool(c), c.indices, sm_scale=c.sm_scale)
+    assert_out_close(bf16_dev_to_f64(o), of, mean_ref=f64_of_bits(ob))
+    assert_lse_close(l.cpu().numpy(), lf32)
+    assert_out_close(bf16_dev_to_f64(oc), of, what="combined out", mean_ref=f64_of_bits(ob))
+    assert_lse_close(lc.cpu().numpy(), lf32, what="combined lse")
