@@ -186,3 +186,42 @@ def test_maximum_rising_in_every_tile(fmt, H):
     assert_lse_close(l.cpu().numpy(), lf32)
     assert_out_close(bf16_dev_to_f64(oc), of, what="combined out", mean_ref=f64_of_bits(ob))
     assert_lse_close(lc.cpu().numpy(), lf32, what="combined lse")
+
+
+@pytest.mark.parametrize("fmt,H", [(W.FMT_FP8, 64), (W.FMT_INT8, 64), (W.FMT_FP8_DSV4, 64), (W.FMT_FP8_DSV4, 16),
+                                   (W.FMT_FP8_DOTS3, 64), (W.FMT_FP8, 8)])
+def test_each_head_its_own_dominant_candidate(fmt, H):
+    """Head h of token t has a direction u_h of its own (q = u_h + 0.5 x
+    the unit normal q) and its dominant list entry at position
+    (7h + 3t) mod 128, whose cache row is a multiple of u_h scoring about
+    40 nats above the others for that head (about 2 nats for the other
+    heads).  Each head's running maximum must come from its own entries:
+    the heads of one workgroup take their maxima at different tile
+    positions and in different tiles.  Prefill and two-split decode with
+    the combine, against the oracle."""
+    T = 128
+    c = W.make_case(f"headdom_{fmt}_{H}", config_id=680 + 8 * fmt + H // 8, seed=16, fmt=fmt, T=T, H=H, n_seqs=T,
+                    ctx=256, topk=128, causal=False)
+    dims = c.kv.shape[1]
+    rng = np.random.default_rng(1600 + fmt)
+    u = rng.standard_normal((H, dims)) * 2.5
+    q = W.bf16_bits_to_f32(c.q_buf).astype(np.float64)
+    c.q_buf = W.f32_to_bf16_bits((u[None, :, :] + 0.5 * q).astype(np.float32))
+    kv = W.bf16_bits_to_f32(c.kv).astype(np.float64)
+    row_of_slot = np.empty(c.slots.shape[0], dtype=np.int64)
+    row_of_slot[c.slots] = np.arange(c.slots.shape[0])
+    for t in range(T):
+        for h in range(H):
+            alpha = 40.0 / (float(c.sm_scale) * float(u[h] @ u[h]))
+            kv[row_of_slot[c.idx_buf[t, (7 * h + 3 * t) % 128]]] = alpha * u[h]
+    c.kv = W.f32_to_bf16_bits(kv.astype(np.float32))
+    d = Dev(c)
+    o, l = smla.prefill(d.q, d.pool, d.indices, sm_scale=float(c.sm_scale))
+    po, pl = smla.decode(d.q, d.pool, d.indices, 2, sm_scale=float(c.sm_scale))
+    oc, lc = smla.combine(po, pl)
+    torch.cuda.synchronize()
+    ob, lf32, of, _ = oracle.prefill(c.q, oracle_pool(c), c.indices, sm_scale=c.sm_scale)
+    assert_out_close(bf16_dev_to_f64(o), of, mean_ref=f64_of_bits(ob))
+    assert_lse_close(l.cpu().numpy(), lf32)
+    assert_out_close(bf16_dev_to_f64(oc), of, what="combined out", mean_ref=f64_of_bits(ob))
+    assert_lse_close(lc.cpu().numpy(), lf32, what="combined lse")
