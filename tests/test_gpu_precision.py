@@ -200,7 +200,7 @@ def test_each_head_its_own_dominant_candidate(fmt, H):
     positions and in different tiles.  Prefill and two-split decode with
     the combine, against the oracle."""
     T = 128
-    c = W.make_case(f"headdom_{fmt}_{H}", config_id=680 + 8 * fmt + H // 8, seed=16, fmt=fmt, T=T, H=H, n_seqs=T,
+    c = W.make_case(f"headdom_{fmt}_{H}", config_id=900 + 8 * fmt + H // 8, seed=16, fmt=fmt, T=T, H=H, n_seqs=T,
                     ctx=256, topk=128, causal=False)
     dims = c.kv.shape[1]
     rng = np.random.default_rng(1600 + fmt)
