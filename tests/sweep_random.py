@@ -3,6 +3,7 @@ by pytest):
 
     python tests/sweep_random.py SECONDS SEED          # small shapes, every format
     python tests/sweep_random.py SECONDS SEED large    # 260-700 tokens, many-head formats
+    python tests/sweep_random.py SECONDS SEED dual     # dual-cache calls (main + secondary list)
 
 Shapes are drawn as in test_gpu_random_shapes.py (head counts on either side
 of every kernel's head group, list widths with ragged tails, per-token
@@ -10,7 +11,9 @@ lengths, sinks, split counts), with sharper score distributions than the
 committed tests: q is scaled by 2^-2..2^3, and in half the cases each token
 gets one list entry whose cache row lies along a random direction that one
 head's q shares, about 30 nats above the rest for that head.  The large
-form sends several tokens through each persistent prefill workgroup.  Every
+form sends several tokens through each persistent prefill workgroup; the
+dual form draws a main list (a multiple of 64 entries) and a secondary list
+over a second pool with padded rows, one softmax over both.  Every
 case runs the prefill and the split decode with the combine, held to the
 output bar against the oracle; the script prints each case and any failure
 and runs until SECONDS have passed."""
@@ -86,13 +89,52 @@ def run_case(c, S):
     assert_lse_close(l2.cpu().numpy(), lf32, "combined lse")
 
 
+def run_dual_case(rng, n):
+    from test_gpu_dual import dual_args, reference
+
+    fmt = FMTS[n % len(FMTS)]
+    k1, k2 = 64 * int(rng.integers(1, 13)), int(rng.integers(1, 1501))
+    H, T = int(rng.choice(HEADS)), int(rng.integers(1, 5))
+    lengths, sink = bool(rng.random() < 0.6), bool(rng.random() < 0.5)
+    S = int(rng.integers(1, min(16, math.ceil((k1 + k2) / 64)) + 1))
+    qscale, dominant = float(2.0 ** rng.uniform(-2, 3)), bool(rng.random() < 0.5)
+    name = (f"{n:05d} dual fmt{fmt} H{H} k{k1}+{k2} T{T} S{S} q*{qscale:.2f} dominant{int(dominant)}"
+            f" len{int(lengths)} sink{int(sink)}")
+    seed = int(rng.integers(0, 1 << 30))
+    main = W.make_case(f"sweep_dual_{n}_main", config_id=4000 + 2 * n, seed=seed, fmt=fmt, T=T, H=H, n_seqs=1,
+                       ctx=max(1024, 2 * k1), topk=k1, causal=True, with_topk_length=lengths, with_sink=sink)
+    extra = W.make_case(f"sweep_dual_{n}_extra", config_id=4001 + 2 * n, seed=seed, fmt=fmt, T=T, H=H, n_seqs=1,
+                        ctx=64 * math.ceil(max(512, 2 * k2) / 64), topk=k2, causal=False, with_topk_length=lengths)
+    sharpen(main, rng, qscale, dominant)
+    dm, de = Dev(main), Dev(extra, row_stride=(W.ROW_BYTES[fmt] + 31) // 16 * 16)
+    o, l = smla.prefill_dual(dm.q, dm.pool, dm.indices, sink=dm.sink, **dual_args(dm, de))
+    po, pl = smla.decode_dual(dm.q, dm.pool, dm.indices, num_splits=S, **dual_args(dm, de))
+    o2, l2 = smla.combine(po, pl, sink=dm.sink)
+    torch.cuda.synchronize()
+    ob, lf32, of, _ = reference(main, extra)
+    assert_out_close(bf16_dev_to_f64(o), of, mean_ref=f64_of_bits(ob))
+    assert_lse_close(l.cpu().numpy(), lf32)
+    assert_out_close(bf16_dev_to_f64(o2), of, "combined out", mean_ref=f64_of_bits(ob))
+    assert_lse_close(l2.cpu().numpy(), lf32, "combined lse")
+    return name
+
+
 def main():
     seconds, seed = float(sys.argv[1]), int(sys.argv[2])
     large = len(sys.argv) > 3 and sys.argv[3] == "large"
+    dual = len(sys.argv) > 3 and sys.argv[3] == "dual"
     rng = np.random.default_rng(seed)
     t_end = time.time() + seconds
     n = fails = 0
     while time.time() < t_end:
+        if dual:
+            try:
+                print("ok  ", run_dual_case(rng, n), flush=True)
+            except AssertionError as e:
+                fails += 1
+                print("FAIL", f"{n:05d} dual", str(e)[:300], flush=True)
+            n += 1
+            continue
         kw, S, qscale, dominant = draw(rng, n, large)
         name = (f"{n:05d} fmt{kw['fmt']} H{kw['H']} k{kw['topk']} T{kw['T']} S{S} q*{qscale:.2f} dominant{int(dominant)}"
                 f" len{int(kw['with_topk_length'])} sink{int(kw['with_sink'])}")
